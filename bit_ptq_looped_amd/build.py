@@ -1,0 +1,72 @@
+"""Build libloopq.so (HIP for gfx950) in-tree with hipcc.
+
+    python -m bit_ptq_looped_amd.build
+
+Compiles every ``csrc/*.hip`` to an object under ``_build/`` and links the
+shared library next to this file.  Always recompiles (the build check expects
+a fresh compile on every call).
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libloopq.so")
+ARCH = os.environ.get("LOOPQ_OFFLOAD_ARCH", "gfx950")
+
+COMMON = [
+    "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
+    "-ffp-contract=off",                      # no implicit FMA: the quantizer's arithmetic is exact as written
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    f"-I{os.path.join(ROOT, 'include')}",
+]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src: str, hipcc: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [hipcc, *COMMON, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    noise = "is not a recognized feature for this target"
+    warn = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l and l.strip())
+    if warn:
+        print(warn, file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    hipcc = _hipcc()
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, hipcc), srcs))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

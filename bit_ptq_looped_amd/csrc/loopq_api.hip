@@ -1,0 +1,337 @@
+// C ABI of libloopq (declared in include/loopq.h): host-side validation,
+// workspace planning and kernel dispatch on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/loopq.h"
+#include "loopq_internal.h"
+
+using namespace loopq;
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? LOOPQ_OK : LOOPQ_ERR_HIP; }
+
+// internal activation buffers for `rows` quantized rows of width K
+struct ActBuffers {
+  int8_t* codes;
+  float* scales;
+  int ld;
+};
+
+size_t act_bytes(int64_t rows, int64_t K) {
+  const int64_t mp = padded_rows(rows);
+  return align256((size_t)(mp * K)) + align256((size_t)((K / 32) * mp * 4));
+}
+
+ActBuffers carve(void* ws, int64_t rows, int64_t K) {
+  ActBuffers b;
+  const int64_t mp = padded_rows(rows);
+  b.codes = reinterpret_cast<int8_t*>(ws);
+  b.scales = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)(mp * K)));
+  b.ld = (int)mp;
+  return b;
+}
+
+int32_t check_weights(int K, int N, int gw) {
+  if (K <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (K % 32 != 0) return LOOPQ_ERR_UNSUPPORTED;
+  if (gw != 32 && gw != 128) return LOOPQ_ERR_UNSUPPORTED;
+  return LOOPQ_OK;
+}
+
+int32_t check_transform(int K, const float* P1, int n1, const float* P2, int n2) {
+  if ((P1 == nullptr) != (P2 == nullptr)) return LOOPQ_ERR_INVALID_ARG;
+  if (P1 == nullptr) return LOOPQ_OK;
+  if (n1 <= 0 || n2 <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if ((int64_t)n1 * n2 != K) return LOOPQ_ERR_UNSUPPORTED;
+  if (n1 % 4 || n2 % 4 || n1 > 128 || n2 > 128) return LOOPQ_ERR_UNSUPPORTED;
+  if (!aligned(P1, 4) || !aligned(P2, 4)) return LOOPQ_ERR_ALIGNMENT;
+  if (!quant_plan_fits(K, n1, n2)) return LOOPQ_ERR_UNSUPPORTED;  // LDS of the fused kernel
+  return LOOPQ_OK;
+}
+
+int32_t check_act(const void* x, int dtype, int M, int K, int bits_a) {
+  if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (K % 32 != 0) return LOOPQ_ERR_UNSUPPORTED;
+  if (dtype != LOOPQ_F32 && dtype != LOOPQ_BF16) return LOOPQ_ERR_UNSUPPORTED;
+  if (bits_a != 4 && bits_a != 8) return LOOPQ_ERR_UNSUPPORTED;
+  if (M > 0 && x == nullptr) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(x, dtype == LOOPQ_F32 ? 16 : 8)) return LOOPQ_ERR_ALIGNMENT;
+  return LOOPQ_OK;
+}
+
+bool clip_ok(float c) { return isfinite(c) && c > 0.0f; }
+
+QuantArgs make_quant_args(const void* x, int dtype, int rows, int K, const float* P1, int n1,
+                          const float* P2, int n2, int bits_a) {
+  QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.rows = rows;
+  a.K = K;
+  a.bf16 = dtype == LOOPQ_BF16;
+  a.P1 = P1;
+  a.P2 = P2;
+  a.n1 = n1;
+  a.n2 = n2;
+  a.rows_per_clip = rows > 0 ? rows : 1;
+  a.qmax = bits_a == 4 ? 7 : 127;
+  return a;
+}
+
+// quantize `rows` rows into the internal layout, then run the GEMM
+int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const float* P1, int n1,
+                    const float* P2, int n2, const ClipTable& clips, int rows_per_clip, int bits_a,
+                    const void* w_codes, const void* w_scales, int gw, float* y, void* ws,
+                    hipStream_t s) {
+  ActBuffers b = carve(ws, rows, K);
+  QuantArgs a = make_quant_args(x, dtype, rows, K, P1, n1, P2, n2, bits_a);
+  a.clips = clips;
+  a.rows_per_clip = rows_per_clip;
+  a.codes = b.codes;
+  a.codes_tiled = 1;
+  a.scales = b.scales;
+  a.scales_gm = 1;
+  a.scales_ld = b.ld;
+  hipError_t e = launch_quant_act(a, s);
+  if (e != hipSuccess) return LOOPQ_ERR_HIP;
+  e = launch_gemm(b.codes, b.scales, b.ld, rows, K, N, reinterpret_cast<const uint8_t*>(w_codes),
+                  reinterpret_cast<const __half*>(w_scales), gw, y, nullptr, 0, s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t loopq_abi_version(void) { return LOOPQ_ABI_VERSION; }
+
+const char* loopq_status_string(int32_t status) {
+  switch (status) {
+    case LOOPQ_OK: return "ok";
+    case LOOPQ_ERR_INVALID_ARG: return "invalid argument";
+    case LOOPQ_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case LOOPQ_ERR_ALIGNMENT: return "misaligned pointer";
+    case LOOPQ_ERR_RANGE: return "weight step overflows fp16";
+    case LOOPQ_ERR_HIP: return "HIP runtime error";
+    case LOOPQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case LOOPQ_ERR_SINGULAR: return "singular transform factor";
+    default: return "unknown status";
+  }
+}
+
+int32_t loopq_packed_weight_bytes(int32_t K, int32_t N, int32_t group_w, size_t* codes_bytes,
+                                  size_t* scales_bytes) {
+  int32_t st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  if (!codes_bytes || !scales_bytes) return LOOPQ_ERR_INVALID_ARG;
+  *codes_bytes = (size_t)padded_cols(N) * (size_t)K / 2;
+  *scales_bytes = (size_t)padded_cols(N) * (size_t)weight_groups(K, group_w) * 2;
+  return LOOPQ_OK;
+}
+
+int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32_t N,
+                              int32_t bits_a, size_t* bytes) {
+  (void)bits_a;
+  if (!bytes) return LOOPQ_ERR_INVALID_ARG;
+  switch (op) {
+    case LOOPQ_OP_LINEAR:
+      if (M < 0 || K <= 0 || K % 32) return M < 0 || K <= 0 ? LOOPQ_ERR_INVALID_ARG : LOOPQ_ERR_UNSUPPORTED;
+      *bytes = act_bytes(M, K);
+      return LOOPQ_OK;
+    case LOOPQ_OP_LOOPED_FORWARD:
+      if (T <= 0 || M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (T > LOOPQ_MAX_LOOPS || K % 32) return LOOPQ_ERR_UNSUPPORTED;
+      *bytes = act_bytes((int64_t)T * M, K);
+      return LOOPQ_OK;
+    case LOOPQ_OP_FOLD:
+      if (M <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (M > 128 || N > 128) return LOOPQ_ERR_UNSUPPORTED;
+      *bytes = align256((size_t)(128 * 256 + M * M + N * N) * 8);
+      return LOOPQ_OK;
+    default:
+      return LOOPQ_ERR_INVALID_ARG;
+  }
+}
+
+int32_t loopq_fold_weights(const float* w, int32_t K, int32_t N, const float* P1, int32_t n1,
+                           const float* P2, int32_t n2, float* w_folded, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!w || !w_folded || !P1 || !P2) return LOOPQ_ERR_INVALID_ARG;
+  if (K <= 0 || N <= 0 || n1 <= 0 || n2 <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if ((int64_t)n1 * n2 != K || n1 > 128 || n2 > 128) return LOOPQ_ERR_UNSUPPORTED;
+  if ((int64_t)K * 16 > 160 * 1024) return LOOPQ_ERR_UNSUPPORTED;  // fold kernel LDS
+  if (!aligned(w, 4) || !aligned(w_folded, 4) || !aligned(P1, 4) || !aligned(P2, 4))
+    return LOOPQ_ERR_ALIGNMENT;
+  size_t need = 0;
+  loopq_workspace_bytes(LOOPQ_OP_FOLD, 0, n1, K, n2, 0, &need);
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = reset_status(s);
+  if (e == hipSuccess) e = launch_fold(w, K, N, P1, n1, P2, n2, w_folded, workspace, s);
+  int flags = 0;
+  if (e == hipSuccess) e = read_status(&flags, s);
+  if (e != hipSuccess) return LOOPQ_ERR_HIP;
+  return (flags & 2) ? LOOPQ_ERR_SINGULAR : LOOPQ_OK;
+}
+
+int32_t loopq_pack_weights(const float* w_folded, int32_t K, int32_t N, int32_t group_w,
+                           void* w_codes, void* w_scales, void* stream) {
+  int32_t st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  if (!w_folded || !w_codes || !w_scales) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(w_folded, 4) || !aligned(w_codes, 16) || !aligned(w_scales, 16))
+    return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = reset_status(s);
+  if (e == hipSuccess)
+    e = launch_pack_weights(w_folded, K, N, group_w, reinterpret_cast<uint8_t*>(w_codes),
+                            reinterpret_cast<__half*>(w_scales), s);
+  int flags = 0;
+  if (e == hipSuccess) e = read_status(&flags, s);
+  if (e != hipSuccess) return LOOPQ_ERR_HIP;
+  return (flags & 1) ? LOOPQ_ERR_RANGE : LOOPQ_OK;
+}
+
+int32_t loopq_quant_act(const void* x, int32_t dtype, int32_t M, int32_t K, const float* P1,
+                        int32_t n1, const float* P2, int32_t n2, float clip, int32_t bits_a,
+                        int8_t* codes, float* scales, float* xt_out, void* stream) {
+  int32_t st = check_act(x, dtype, M, K, bits_a);
+  if (st != LOOPQ_OK) return st;
+  st = check_transform(K, P1, n1, P2, n2);
+  if (st != LOOPQ_OK) return st;
+  if (!clip_ok(clip)) return LOOPQ_ERR_INVALID_ARG;
+  if (M == 0) return LOOPQ_OK;
+  if (!codes || !scales) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(xt_out, 16)) return LOOPQ_ERR_ALIGNMENT;
+  QuantArgs a = make_quant_args(x, dtype, M, K, P1, n1, P2, n2, bits_a);
+  a.clips.c[0] = clip;
+  a.codes = codes;
+  a.scales = scales;
+  a.xt_out = xt_out;
+  return hip_status(launch_quant_act(a, as_stream(stream)));
+}
+
+int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
+                             int32_t N, const float* P1, int32_t n1, const float* P2, int32_t n2,
+                             const float* clips_host, int32_t bits_a, const void* w_codes,
+                             const void* w_scales, int32_t group_w, float* y, int32_t schedule,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (T <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (T > LOOPQ_MAX_LOOPS) return LOOPQ_ERR_UNSUPPORTED;
+  if ((int64_t)T * M > (int64_t)1 << 30) return LOOPQ_ERR_UNSUPPORTED;
+  int32_t st = check_act(x, dtype, M, K, bits_a);
+  if (st != LOOPQ_OK) return st;
+  st = check_transform(K, P1, n1, P2, n2);
+  if (st != LOOPQ_OK) return st;
+  st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  if (!clips_host) return LOOPQ_ERR_INVALID_ARG;
+  ClipTable clips;
+  memset(&clips, 0, sizeof(clips));
+  for (int t = 0; t < T; ++t) {
+    if (!clip_ok(clips_host[t])) return LOOPQ_ERR_INVALID_ARG;
+    clips.c[t] = clips_host[t];
+  }
+  if (schedule < LOOPQ_SCHED_AUTO || schedule > LOOPQ_SCHED_WEIGHT_STATIONARY)
+    return LOOPQ_ERR_INVALID_ARG;
+  if (M == 0) return LOOPQ_OK;
+  if (!w_codes || !w_scales || !y) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(y, 4)) return LOOPQ_ERR_ALIGNMENT;
+  size_t need = 0;
+  loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, bits_a, &need);
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
+  if (schedule == LOOPQ_SCHED_LOOP_SEQUENTIAL) {
+    for (int t = 0; t < T; ++t) {
+      ClipTable one;
+      memset(&one, 0, sizeof(one));
+      one.c[0] = clips.c[t];
+      const void* xt = reinterpret_cast<const char*>(x) + (size_t)t * M * K * esz;
+      st = linear_core(xt, dtype, M, K, N, P1, n1, P2, n2, one, M, bits_a, w_codes, w_scales,
+                       group_w, y + (size_t)t * M * N, workspace, s);
+      if (st != LOOPQ_OK) return st;
+    }
+    return LOOPQ_OK;
+  }
+  return linear_core(x, dtype, T * M, K, N, P1, n1, P2, n2, clips, M, bits_a, w_codes, w_scales,
+                     group_w, y, workspace, s);
+}
+
+int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,
+                          const float* P1, int32_t n1, const float* P2, int32_t n2, float clip,
+                          int32_t bits_a, const void* w_codes, const void* w_scales,
+                          int32_t group_w, float* y, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return loopq_looped_forward(x, dtype, 1, M, K, N, P1, n1, P2, n2, &clip, bits_a, w_codes,
+                              w_scales, group_w, y, LOOPQ_SCHED_WEIGHT_STATIONARY, workspace,
+                              workspace_bytes, stream);
+}
+
+int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M, int32_t K,
+                         int32_t N, const void* w_codes, const void* w_scales, int32_t group_w,
+                         float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  if (M < 0) return LOOPQ_ERR_INVALID_ARG;
+  if (M == 0) return LOOPQ_OK;
+  if (!a_codes || !a_scales || !w_codes || !w_scales || !y) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(a_codes, 4) || !aligned(a_scales, 4) || !aligned(w_codes, 16) ||
+      !aligned(w_scales, 16) || !aligned(y, 4))
+    return LOOPQ_ERR_ALIGNMENT;
+  const size_t need = act_bytes(M, K);
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  ActBuffers b = carve(workspace, M, K);
+  hipError_t e = launch_tile_codes(a_codes, a_scales, M, K, b.codes, b.scales, b.ld, s);
+  if (e == hipSuccess)
+    e = launch_gemm(b.codes, b.scales, b.ld, M, K, N, reinterpret_cast<const uint8_t*>(w_codes),
+                    reinterpret_cast<const __half*>(w_scales), group_w, y, nullptr, 0, s);
+  return hip_status(e);
+}
+
+int32_t loopq_export_weights(const void* w_codes, const void* w_scales, int32_t K, int32_t N,
+                             int32_t group_w, int8_t* codes, uint16_t* scales, void* stream) {
+  int32_t st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  if (!w_codes || !w_scales || !codes || !scales) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(scales, 2))
+    return LOOPQ_ERR_ALIGNMENT;
+  return hip_status(launch_export_weights(reinterpret_cast<const uint8_t*>(w_codes),
+                                          reinterpret_cast<const __half*>(w_scales), K, N,
+                                          group_w, codes, scales, as_stream(stream)));
+}
+
+int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
+                         const void* w_codes, int32_t* dots, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (M < 0 || K <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (K % 32) return LOOPQ_ERR_UNSUPPORTED;
+  if (M == 0) return LOOPQ_OK;
+  if (!a_codes || !w_codes || !dots) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(a_codes, 4) || !aligned(w_codes, 16) || !aligned(dots, 4))
+    return LOOPQ_ERR_ALIGNMENT;
+  const size_t need = act_bytes(M, K);
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  ActBuffers b = carve(workspace, M, K);
+  hipError_t e = launch_tile_codes(a_codes, nullptr, M, K, b.codes, nullptr, b.ld, s);
+  if (e == hipSuccess)
+    e = launch_gemm(b.codes, nullptr, b.ld, M, K, N, reinterpret_cast<const uint8_t*>(w_codes),
+                    nullptr, 32, nullptr, dots, 1, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,223 @@
+"""Python binding of libloopq (the C ABI in include/loopq.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their device pointers and the current HIP stream to
+the C function of the same name, and raises :class:`LoopQError` on a non-zero
+status.  There is no fallback: if the library is missing or fails to load,
+:func:`load` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libloopq.so")
+
+LOOPQ_ABI_VERSION = 1
+LOOPQ_OK = 0
+LOOPQ_ERR_INVALID_ARG = -1
+LOOPQ_ERR_UNSUPPORTED = -2
+LOOPQ_ERR_ALIGNMENT = -3
+LOOPQ_ERR_RANGE = -4
+LOOPQ_ERR_HIP = -5
+LOOPQ_ERR_WORKSPACE = -6
+LOOPQ_ERR_SINGULAR = -7
+
+LOOPQ_F32, LOOPQ_BF16 = 0, 1
+LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
+LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD = 1, 2, 3
+
+# every entry point of include/loopq.h with its ctypes signature
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_ZP = ctypes.POINTER(ctypes.c_size_t)
+SIGNATURES = {
+    "loopq_abi_version": ([], _I),
+    "loopq_status_string": ([_I], ctypes.c_char_p),
+    "loopq_packed_weight_bytes": ([_I, _I, _I, _ZP, _ZP], _I),
+    "loopq_workspace_bytes": ([_I, _I, _I, _I, _I, _I, _ZP], _I),
+    "loopq_fold_weights": ([_P, _I, _I, _P, _I, _P, _I, _P, _P, _Z, _P], _I),
+    "loopq_pack_weights": ([_P, _I, _I, _I, _P, _P, _P], _I),
+    "loopq_quant_act": ([_P, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _P, _P], _I),
+    "loopq_w4a4_linear": ([_P, _I, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
+    "loopq_looped_forward": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _I,
+                              _P, _Z, _P], _I),
+    "loopq_gemm_codes": ([_P, _P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
+    "loopq_export_weights": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
+    "loopq_group_dots": ([_P, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+}
+
+_lib = None
+
+
+class LoopQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = load().loopq_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def load(path: Optional[str] = None):
+    """Load the shared library once; raise if it is missing or mismatched."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m bit_ptq_looped_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if lib.loopq_abi_version() != LOOPQ_ABI_VERSION:
+        raise RuntimeError("libloopq ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != LOOPQ_OK:
+        raise LoopQError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(x) -> int:
+    import torch
+    if x.dtype == torch.float32:
+        return LOOPQ_F32
+    if x.dtype == torch.bfloat16:
+        return LOOPQ_BF16
+    raise ValueError(f"activations must be float32 or bfloat16, got {x.dtype}")
+
+
+def _factor_args(P1, P2):
+    if P1 is None and P2 is None:
+        return None, 0, None, 0
+    return _ptr(P1), int(P1.shape[0]), _ptr(P2), int(P2.shape[0])
+
+
+# ----------------------------------------------------------------- host-only calls
+
+def loopq_abi_version() -> int:
+    return load().loopq_abi_version()
+
+
+def loopq_status_string(status: int) -> str:
+    return load().loopq_status_string(status).decode()
+
+
+def loopq_packed_weight_bytes(K: int, N: int, group_w: int):
+    c, s = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().loopq_packed_weight_bytes(K, N, group_w, ctypes.byref(c), ctypes.byref(s)),
+           "loopq_packed_weight_bytes")
+    return c.value, s.value
+
+
+def loopq_workspace_bytes(op: int, T: int, M: int, K: int, N: int, bits_a: int) -> int:
+    b = ctypes.c_size_t()
+    _check(load().loopq_workspace_bytes(op, T, M, K, N, bits_a, ctypes.byref(b)), "loopq_workspace_bytes")
+    return b.value
+
+
+# ----------------------------------------------------------------- device calls
+
+def loopq_fold_weights(w, P1, P2, w_folded, workspace, stream=None):
+    N, K = w.shape
+    _check(load().loopq_fold_weights(_ptr(w), K, N, _ptr(P1), int(P1.shape[0]), _ptr(P2),
+                                     int(P2.shape[0]), _ptr(w_folded), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+           "loopq_fold_weights")
+
+
+def loopq_pack_weights(w_folded, group_w: int, w_codes, w_scales, stream=None):
+    N, K = w_folded.shape
+    _check(load().loopq_pack_weights(_ptr(w_folded), K, N, group_w, _ptr(w_codes), _ptr(w_scales),
+                                     _stream(stream)), "loopq_pack_weights")
+
+
+def loopq_quant_act(x, P1, P2, clip: float, bits_a: int, codes, scales, xt_out=None, stream=None):
+    M, K = x.shape
+    p1, n1, p2, n2 = _factor_args(P1, P2)
+    _check(load().loopq_quant_act(_ptr(x), _dtype_code(x), M, K, p1, n1, p2, n2, float(clip), bits_a,
+                                  _ptr(codes), _ptr(scales), _ptr(xt_out), _stream(stream)),
+           "loopq_quant_act")
+
+
+def loopq_w4a4_linear(x, P1, P2, clip: float, bits_a: int, w_codes, w_scales, group_w: int, N: int,
+                      y, workspace, stream=None):
+    M, K = x.shape
+    p1, n1, p2, n2 = _factor_args(P1, P2)
+    _check(load().loopq_w4a4_linear(_ptr(x), _dtype_code(x), M, K, N, p1, n1, p2, n2, float(clip),
+                                    bits_a, _ptr(w_codes), _ptr(w_scales), group_w, _ptr(y),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "loopq_w4a4_linear")
+
+
+def loopq_looped_forward(x, P1, P2, clips: Sequence[float], bits_a: int, w_codes, w_scales,
+                         group_w: int, N: int, y, schedule: int, workspace, stream=None):
+    T, M, K = x.shape
+    p1, n1, p2, n2 = _factor_args(P1, P2)
+    c = (ctypes.c_float * T)(*[float(v) for v in clips])
+    _check(load().loopq_looped_forward(_ptr(x), _dtype_code(x), T, M, K, N, p1, n1, p2, n2,
+                                       ctypes.cast(c, ctypes.c_void_p), bits_a, _ptr(w_codes),
+                                       _ptr(w_scales), group_w, _ptr(y), schedule, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)),
+           "loopq_looped_forward")
+
+
+def loopq_gemm_codes(a_codes, a_scales, w_codes, w_scales, group_w: int, N: int, y, workspace,
+                     stream=None):
+    M, K = a_codes.shape
+    _check(load().loopq_gemm_codes(_ptr(a_codes), _ptr(a_scales), M, K, N, _ptr(w_codes),
+                                   _ptr(w_scales), group_w, _ptr(y), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "loopq_gemm_codes")
+
+
+def loopq_export_weights(w_codes, w_scales, K: int, N: int, group_w: int, codes, scales, stream=None):
+    _check(load().loopq_export_weights(_ptr(w_codes), _ptr(w_scales), K, N, group_w, _ptr(codes),
+                                       _ptr(scales), _stream(stream)), "loopq_export_weights")
+
+
+def loopq_group_dots(a_codes, w_codes, N: int, dots, workspace, stream=None):
+    M, K = a_codes.shape
+    _check(load().loopq_group_dots(_ptr(a_codes), M, K, N, _ptr(w_codes), _ptr(dots), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "loopq_group_dots")
+
+
+# ----------------------------------------------------------------- buffer helpers
+
+def empty_packed_weights(K: int, N: int, group_w: int, device="cuda"):
+    """Uninitialized device buffers sized for loopq_pack_weights."""
+    import torch
+    cb, sb = loopq_packed_weight_bytes(K, N, group_w)
+    return (torch.empty(cb, dtype=torch.uint8, device=device),
+            torch.empty(sb, dtype=torch.uint8, device=device))
+
+
+def empty_workspace(op: int, T: int, M: int, K: int, N: int, bits_a: int, device="cuda"):
+    import torch
+    n = loopq_workspace_bytes(op, T, M, K, N, bits_a)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

@@ -1,0 +1,196 @@
+/*
+ * loopq.h -- C ABI of the looped W4A4 / W4A8 group-quantized linear layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are the pages' titles and the passage used):
+ *   - "paper_specification.yaml" of the LoopQ reproduction, lq1_quantization:
+ *     Eq.(4) Q_a(x; c) = c * clip(round(x / c), q_min, q_max); symmetric
+ *     round-to-nearest; 4-bit weights with 4- or 8-bit activations; group-wise
+ *     weights and activations with group size 32.
+ *   - the same file, loopq_components: a shared quantized backbone with an
+ *     invertible transform folded into the activation and weight sides; LAS
+ *     replaces the shared activation clip with one clip per module and loop.
+ *   - implementation_status lq2 (clips multiply dynamic token/group absmax
+ *     steps) and lq3 (a shared Kronecker transform, exact no-quant
+ *     inverse-transpose weight folding).
+ *   - "LoopQ 4-bit quantization of Ouro-1.4B -- raw artifacts", "The arms":
+ *     random orthogonal Kronecker transforms; Ouro-1.4B runs 24 layers 4 times
+ *     per token with the same weights.
+ *   - "Quantizing Looped Transformers: Feedback Exposure and Calibration
+ *     Blindness", Figure 3 and Table 6: grouped INT4 weights with g = 128.
+ *
+ * Readings where the pages are silent: codes are symmetric in
+ * [-(2^(b-1)-1), 2^(b-1)-1]; ties round to even; the step of a group is
+ * fl32(c * fl32(absmax / qmax)) (weights: fl16(fl32(absmax / 7)), codes use
+ * the fp16 step); division is correctly rounded; an all-zero group has step 0
+ * and codes 0; groups run along K over the flat row-major index; the
+ * transform is x~ = x (P1 kron P2) = vec_r(P1^T X P2), formed in fp64 and
+ * rounded once to fp32.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless the name ends in _host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns without waiting, except
+ *     where a call says it synchronizes.
+ *   - The caller owns every buffer.  Compute calls allocate nothing; scratch
+ *     memory comes in through `workspace` (size from loopq_workspace_bytes).
+ *   - Arguments are validated on the host before any HIP call; a failed
+ *     check returns a negative loopq_status and enqueues nothing.  The
+ *     library is fail-closed: an unsupported shape is an error, never a
+ *     slower fallback.  A device fault surfaces at the caller's next
+ *     synchronization.
+ *   - Calls on different streams may run concurrently; they share no
+ *     mutable library state except the status word of the synchronizing
+ *     offline calls (pack, fold), which must not overlap on one device.
+ *   - Matrices are row-major.  x is [M][K] (one token per row), weights are
+ *     stored one output column per row, [N][K]; y is [M][N] fp32.
+ */
+#ifndef LOOPQ_H
+#define LOOPQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOOPQ_ABI_VERSION 1
+#define LOOPQ_GROUP_A 32   /* activation group size (lq1_quantization) */
+#define LOOPQ_MAX_LOOPS 64 /* largest T accepted by loopq_looped_forward */
+
+typedef enum {
+  LOOPQ_OK = 0,
+  LOOPQ_ERR_INVALID_ARG = -1, /* null pointer, size <= 0, clip <= 0 or not finite */
+  LOOPQ_ERR_UNSUPPORTED = -2, /* K % 32 != 0, n1*n2 != K, n1 or n2 not a multiple of 4
+                                 or above 128, bits not 4/8, group_w not 32/128, T > 64 */
+  LOOPQ_ERR_ALIGNMENT = -3,   /* a pointer breaks the alignment a call states */
+  LOOPQ_ERR_RANGE = -4,       /* a weight step overflows fp16 */
+  LOOPQ_ERR_HIP = -5,         /* the HIP runtime reported an error */
+  LOOPQ_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required */
+  LOOPQ_ERR_SINGULAR = -7     /* a transform factor is not invertible (fold) */
+} loopq_status;
+
+typedef enum { LOOPQ_F32 = 0, LOOPQ_BF16 = 1 } loopq_dtype;
+
+typedef enum {
+  LOOPQ_SCHED_AUTO = 0,
+  LOOPQ_SCHED_LOOP_SEQUENTIAL = 1, /* per t: quantize x_t, then the GEMM */
+  LOOPQ_SCHED_WEIGHT_STATIONARY = 2 /* quantize all T*M rows, one pass over the weights */
+} loopq_schedule;
+
+typedef enum {
+  LOOPQ_OP_LINEAR = 1,
+  LOOPQ_OP_LOOPED_FORWARD = 2,
+  LOOPQ_OP_FOLD = 3
+} loopq_op;
+
+/* ABI version of the loaded library (LOOPQ_ABI_VERSION it was built with). */
+int32_t loopq_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* loopq_status_string(int32_t status);
+
+/* Bytes of the packed weight codes and steps for a K x N weight with weight
+ * group size group_w (32 or 128).  Host only, touches no GPU.  Codes take
+ * ceil(N/32)*32 * K/2 bytes; steps ceil(N/32)*32 * ceil(K/group_w) fp16. */
+int32_t loopq_packed_weight_bytes(int32_t K, int32_t N, int32_t group_w,
+                                  size_t* codes_bytes_host, size_t* scales_bytes_host);
+
+/* Workspace bytes an op needs (host only).  LINEAR: T ignored.
+ * LOOPED_FORWARD: T loops.  FOLD: pass n1 as M and n2 as N; T, K and bits_a
+ * are ignored.  The size is a multiple of 256. */
+int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32_t N,
+                              int32_t bits_a, size_t* bytes_host);
+
+/* a0 -- fold the transform into the weights (offline).
+ * Page: paper_specification.yaml, loopq_components.shared_transformed_backbone
+ * and implementation_status lq3 ("exact no-quant inverse-transpose weight
+ * folding").  w [N][K] fp32 holds one output column per row; for each row
+ * w_folded[n] = vec_r(P1^-1 * reshape(w[n], n1, n2) * P2^-T), computed in
+ * fp64 with the factors inverted on the GPU (Gauss-Jordan, partial pivoting)
+ * and rounded once to fp32.  P1 is n1 x n1 and P2 is n2 x n2 fp32, n1*n2 = K,
+ * n1, n2 <= 128.  Needs loopq_workspace_bytes(LOOPQ_OP_FOLD, 0, n1, K, n2, 0, ...).
+ * Synchronizes `stream`; returns LOOPQ_ERR_SINGULAR for a singular factor. */
+int32_t loopq_fold_weights(const float* w, int32_t K, int32_t N,
+                           const float* P1, int32_t n1, const float* P2, int32_t n2,
+                           float* w_folded, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* a1 -- INT4 weight packing (offline).
+ * Page: Eq.(4) with clip 1 (lq1_quantization), group-wise W4; g = 128 from
+ * "Quantizing Looped Transformers", Figure 3.  For output column n and K-group
+ * j of size group_w (the last group may be short): s = fl16(fl32(absmax / 7)),
+ * q = clamp(rint(fl32(w / s)), -7, 7), 0 when s == 0.
+ * w_folded [N][K] fp32 (K % 32 == 0).  w_codes and w_scales receive an opaque,
+ * kernel-tiled layout (sizes from loopq_packed_weight_bytes, 16-byte aligned);
+ * loopq_export_weights recovers canonical codes and steps.
+ * Synchronizes `stream`; returns LOOPQ_ERR_RANGE if a step overflows fp16. */
+int32_t loopq_pack_weights(const float* w_folded, int32_t K, int32_t N, int32_t group_w,
+                           void* w_codes, void* w_scales, void* stream);
+
+/* a2-a4 -- transform + dynamic group absmax + LAS clip + RTN of activations.
+ * Page: Eq.(4) (lq1_quantization); LAS (loopq_components.las, lq2); the
+ * Kronecker transform (lq3).  x [M][K] in `dtype` (fp32 or bf16, 4-byte
+ * aligned); P1 [n1][n1], P2 [n2][n2] fp32 or both NULL for no transform.
+ * For row m and group j of 32: s = fl32(clip * fl32(absmax / qmax)),
+ * codes[m][k] = clamp(rint(fl32(x~ / s)), -qmax, qmax) (0 when s == 0),
+ * scales[m][j] = s; qmax = 7 (bits_a 4) or 127 (bits_a 8).
+ * codes int8 [M][K]; scales fp32 [M][K/32]; xt_out (nullable) receives x~
+ * [M][K] fp32, the values that were quantized. */
+int32_t loopq_quant_act(const void* x, int32_t dtype, int32_t M, int32_t K,
+                        const float* P1, int32_t n1, const float* P2, int32_t n2,
+                        float clip, int32_t bits_a,
+                        int8_t* codes, float* scales, float* xt_out, void* stream);
+
+/* a2-a5 -- one quantized linear: quant_act, then the integer GEMM with the
+ * per-group rescale y[m][n] = sum_j s_a[m][j] * s_w[n][32j/group_w] * d[m][n][j],
+ * d the exact int32 dot of group j.  bits_a 4 is W4A4, 8 is W4A8.
+ * w_codes/w_scales from loopq_pack_weights with the same K, N, group_w.
+ * y [M][N] fp32.  Workspace: loopq_workspace_bytes(LOOPQ_OP_LINEAR, ...). */
+int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,
+                          const float* P1, int32_t n1, const float* P2, int32_t n2,
+                          float clip, int32_t bits_a,
+                          const void* w_codes, const void* w_scales, int32_t group_w,
+                          float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* a6 -- the loop: the same packed weights applied at every loop t with the
+ * loop's own clip.  Page: "LoopQ 4-bit quantization of Ouro-1.4B" (24 layers
+ * run 4 times per token); LAS, one clip per module and loop.
+ * x [T][M][K], y [T][M][N]; clips_host [T] (host memory, read before return).
+ * schedule: a loopq_schedule.  LOOP_SEQUENTIAL quantizes and multiplies loop
+ * by loop; WEIGHT_STATIONARY quantizes all T*M rows, then streams the weights
+ * once for all loops; AUTO picks WEIGHT_STATIONARY.  Both give bitwise equal y.
+ * Workspace: loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, ...). */
+int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
+                             int32_t K, int32_t N,
+                             const float* P1, int32_t n1, const float* P2, int32_t n2,
+                             const float* clips_host, int32_t bits_a,
+                             const void* w_codes, const void* w_scales, int32_t group_w,
+                             float* y, int32_t schedule,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* a5 alone -- the GEMM on activation codes and steps already formed.
+ * a_codes int8 [M][K], a_scales fp32 [M][K/32] (the layouts loopq_quant_act
+ * writes); same weights and output as loopq_w4a4_linear. */
+int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M, int32_t K,
+                         int32_t N, const void* w_codes, const void* w_scales, int32_t group_w,
+                         float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Test export: canonical weight codes int8 [N][K] and steps fp16 [N][ceil(K/group_w)]
+ * (raw binary16 bits) from the packed layout. */
+int32_t loopq_export_weights(const void* w_codes, const void* w_scales, int32_t K, int32_t N,
+                             int32_t group_w, int8_t* codes, uint16_t* scales, void* stream);
+
+/* Test export: the exact int32 per-group dots d[m][n][j] = sum_{k in group j}
+ * a_codes[m][k] * w[n][k], computed by the GEMM's own MFMA path, [M][N][K/32].
+ * a_codes int8 [M][K]; workspace as for loopq_workspace_bytes(LOOPQ_OP_LINEAR). */
+int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
+                         const void* w_codes, int32_t* dots, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOPQ_H */

@@ -1,0 +1,137 @@
+"""The C ABI library loads without a GPU, exports every symbol include/loopq.h
+declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_ptq_looped_amd import loopq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loopq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int32_t|const char\*)\s+(loopq_\w+)\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(loopq.LIB_PATH):
+        from bit_ptq_looped_amd import build
+        build.build(verbose=False)
+    return loopq.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in loopq.SIGNATURES, n
+    assert set(loopq.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert loopq.loopq_abi_version() == loopq.LOOPQ_ABI_VERSION
+    for st in range(0, -8, -1):
+        assert loopq.loopq_status_string(st) != "unknown status"
+    assert loopq.loopq_status_string(-99) == "unknown status"
+
+
+def test_packed_sizes(lib):
+    cb, sb = loopq.loopq_packed_weight_bytes(2048, 5632, 32)
+    assert cb == 5632 * 2048 // 2 and sb == 5632 * 64 * 2
+    cb, sb = loopq.loopq_packed_weight_bytes(10560, 5280, 128)
+    assert cb == 5280 * 10560 // 2 and sb == 5280 * 83 * 2  # 82 full groups + a tail of 64
+    cb, sb = loopq.loopq_packed_weight_bytes(64, 40, 32)  # ragged N padded to 64 columns
+    assert cb == 64 * 64 // 2 and sb == 64 * 2 * 2
+    with pytest.raises(loopq.LoopQError) as e:
+        loopq.loopq_packed_weight_bytes(33, 8, 32)
+    assert e.value.status == loopq.LOOPQ_ERR_UNSUPPORTED
+    with pytest.raises(loopq.LoopQError) as e:
+        loopq.loopq_packed_weight_bytes(64, 8, 64)
+    assert e.value.status == loopq.LOOPQ_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes(lib):
+    ws = loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LINEAR, 1, 1024, 2048, 2048, 4)
+    assert ws >= 1024 * 2048 + 1024 * 64 * 4 and ws % 256 == 0
+    wl = loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LOOPED_FORWARD, 4, 1024, 2048, 2048, 4)
+    assert wl >= 4 * 1024 * 2048
+    with pytest.raises(loopq.LoopQError) as e:
+        loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LOOPED_FORWARD, 65, 1, 32, 32, 4)
+    assert e.value.status == loopq.LOOPQ_ERR_UNSUPPORTED
+
+
+def _raw(lib, name, *args):
+    return getattr(lib, name)(*args)
+
+
+FAKE = 1 << 20  # a non-null, aligned address; never dereferenced because validation fails first
+
+
+@pytest.mark.parametrize("K,n1,n2,bits,clip,want", [
+    (33, 0, 0, 4, 1.0, loopq.LOOPQ_ERR_UNSUPPORTED),      # K % 32
+    (256, 16, 8, 4, 1.0, loopq.LOOPQ_ERR_UNSUPPORTED),    # n1 * n2 != K
+    (240, 16, 15, 4, 1.0, loopq.LOOPQ_ERR_UNSUPPORTED),   # n2 % 4 (K % 32 != 0 first: 240 ok)
+    (256, 16, 16, 5, 1.0, loopq.LOOPQ_ERR_UNSUPPORTED),   # bits
+    (256, 16, 16, 4, 0.0, loopq.LOOPQ_ERR_INVALID_ARG),   # clip <= 0
+    (256, 16, 16, 4, float("nan"), loopq.LOOPQ_ERR_INVALID_ARG),
+    (256, 16, 16, 4, float("inf"), loopq.LOOPQ_ERR_INVALID_ARG),
+    (16384, 128, 128, 4, 1.0, loopq.LOOPQ_ERR_UNSUPPORTED),  # transform does not fit LDS
+])
+def test_quant_act_rejects_on_host(lib, K, n1, n2, bits, clip, want):
+    p1 = FAKE if n1 else None
+    p2 = FAKE if n2 else None
+    st = _raw(lib, "loopq_quant_act", FAKE, loopq.LOOPQ_F32, 4, K, p1, n1, p2, n2, clip, bits,
+              FAKE, FAKE, None, None)
+    assert st == want
+
+
+def test_quant_act_other_rejections(lib):
+    # one factor without the other
+    assert _raw(lib, "loopq_quant_act", FAKE, 0, 4, 256, FAKE, 16, None, 0, 1.0, 4, FAKE, FAKE,
+                None, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    # bad dtype
+    assert _raw(lib, "loopq_quant_act", FAKE, 7, 4, 256, None, 0, None, 0, 1.0, 4, FAKE, FAKE,
+                None, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    # misaligned input (fp32 needs 16 bytes)
+    assert _raw(lib, "loopq_quant_act", FAKE + 4, 0, 4, 256, None, 0, None, 0, 1.0, 4, FAKE, FAKE,
+                None, None) == loopq.LOOPQ_ERR_ALIGNMENT
+    # null outputs
+    assert _raw(lib, "loopq_quant_act", FAKE, 0, 4, 256, None, 0, None, 0, 1.0, 4, None, FAKE,
+                None, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    # M == 0 is an empty no-op (nothing is touched)
+    assert _raw(lib, "loopq_quant_act", None, 0, 0, 256, None, 0, None, 0, 1.0, 4, None, None,
+                None, None) == loopq.LOOPQ_OK
+    # negative M
+    assert _raw(lib, "loopq_quant_act", FAKE, 0, -1, 256, None, 0, None, 0, 1.0, 4, FAKE, FAKE,
+                None, None) == loopq.LOOPQ_ERR_INVALID_ARG
+
+
+def test_looped_forward_rejects_on_host(lib):
+    clips = (ctypes.c_float * 2)(1.0, 0.5)
+    bad = (ctypes.c_float * 2)(1.0, -0.5)
+    args = lambda T, c, gw=32, sched=0, ws=1 << 30: (FAKE, 0, T, 4, 256, 128, None, 0, None, 0,
+                                                      ctypes.cast(c, ctypes.c_void_p), 4, FAKE, FAKE,
+                                                      gw, FAKE, sched, FAKE, ws, None)
+    assert _raw(lib, "loopq_looped_forward", *args(0, clips)) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert _raw(lib, "loopq_looped_forward", *args(65, clips)) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert _raw(lib, "loopq_looped_forward", *args(2, bad)) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert _raw(lib, "loopq_looped_forward", *args(2, clips, gw=64)) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert _raw(lib, "loopq_looped_forward", *args(2, clips, sched=3)) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert _raw(lib, "loopq_looped_forward", *args(2, clips, ws=16)) == loopq.LOOPQ_ERR_WORKSPACE
+
+
+def test_pack_and_fold_reject_on_host(lib):
+    assert _raw(lib, "loopq_pack_weights", FAKE, 48, 8, 32, FAKE, FAKE, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert _raw(lib, "loopq_pack_weights", FAKE, 64, 8, 32, FAKE + 8, FAKE, None) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert _raw(lib, "loopq_pack_weights", None, 64, 8, 32, FAKE, FAKE, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert _raw(lib, "loopq_fold_weights", FAKE, 256, 8, FAKE, 16, FAKE, 8, FAKE, FAKE, 1 << 30,
+                None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert _raw(lib, "loopq_fold_weights", FAKE, 256, 8, FAKE, 16, FAKE, 16, FAKE, FAKE, 16,
+                None) == loopq.LOOPQ_ERR_WORKSPACE

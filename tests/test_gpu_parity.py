@@ -1,0 +1,316 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: weight codes and fp16 steps, activation codes and fp32 steps, and the
+int32 group dots are bit-exact; fp32 outputs satisfy
+max|y - y_oracle| / max|y_oracle| <= 1e-4.  Inputs come from the seeded
+generators only; no oracle input is taken from the GPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_ptq_looped_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 1e-4
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def pack(lq, w32, gw):
+    N, K = w32.shape
+    codes, scales = lq.empty_packed_weights(K, N, gw)
+    lq.loopq_pack_weights(dev(w32), gw, codes, scales)
+    return codes, scales
+
+
+def export(lq, codes, scales, K, N, gw):
+    c = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    s = torch.empty((N, math.ceil(K / gw)), dtype=torch.int16, device="cuda")
+    lq.loopq_export_weights(codes, scales, K, N, gw, c, s)
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), s.cpu().numpy().view(np.float16)
+
+
+def rel_err(y, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(np.asarray(y, dtype=np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def special_weights(N, K, key):
+    w = synth.gaussian((N, K), key, scale=0.02)
+    w[0, :32] = 0.0                          # an all-zero group
+    if N > 1:
+        w[1, 5] = 0.3                        # an outlier inside a group
+    return w
+
+
+# ------------------------------------------------------------------------ weights
+
+@pytest.mark.parametrize("K,N,gw", [(256, 128, 32), (2048, 40, 32), (96, 33, 32), (160, 64, 128),
+                                    (320, 72, 128), (10560, 8, 128)])
+def test_pack_matches_oracle(lq, K, N, gw):
+    say(f"pack K={K} N={N} gw={gw}")
+    w = special_weights(N, K, K + N + gw)
+    codes, scales = pack(lq, w, gw)
+    gc, gs = export(lq, codes, scales, K, N, gw)
+    oc, os_ = oracle.quant_weights(w, gw)
+    np.testing.assert_array_equal(gc, oc)
+    np.testing.assert_array_equal(gs.view(np.uint16), os_.view(np.uint16))
+
+
+def test_pack_rejects_fp16_overflow(lq):
+    w = np.zeros((4, 64), dtype=np.float32)
+    w[2, 40] = 7 * 65520.0
+    with pytest.raises(lq.LoopQError) as e:
+        pack(lq, w, 32)
+    assert e.value.status == lq.LOOPQ_ERR_RANGE
+
+
+# ------------------------------------------------------------------------ activations
+
+def _quant_gpu(lq, xdev, P1, P2, clip, bits, with_xt=False):
+    M, K = xdev.shape
+    codes = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    scales = torch.empty((M, K // 32), dtype=torch.float32, device="cuda")
+    xt = torch.empty((M, K), dtype=torch.float32, device="cuda") if with_xt else None
+    lq.loopq_quant_act(xdev, None if P1 is None else dev(P1), None if P2 is None else dev(P2),
+                       clip, bits, codes, scales, xt)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy(), (xt.cpu().numpy() if with_xt else None)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,K", [(1, 32), (7, 256), (33, 2048), (5, 5632)])
+def test_quant_plain_matches_oracle(lq, dtype, bits, M, K):
+    say(f"quant plain {dtype} A{bits} M={M} K={K}")
+    x = synth.with_outliers(synth.gaussian((M, K), M, K, bits), max(1, K // 100), 20.0, K, M)
+    x[0, :32] = 0.0  # zero group
+    clip = float(synth.uniform((1,), 0.6, 1.0, M, K)[0])
+    if dtype == "bf16":
+        bits16, x32 = synth.round_to_bf16(x)
+        xd = bf16_dev(bits16)
+    else:
+        x32, xd = x, dev(x)
+    gc, gs, _ = _quant_gpu(lq, xd, None, None, clip, bits)
+    oc, os_ = oracle.quant_act(x32, clip, bits)
+    np.testing.assert_array_equal(gs, os_)
+    np.testing.assert_array_equal(gc, oc)
+
+
+@pytest.mark.parametrize("n1,n2", [(16, 16), (32, 64), (64, 88), (40, 64), (64, 108), (4, 8)])
+@pytest.mark.parametrize("dtype,bits", [("f32", 4), ("bf16", 4), ("bf16", 8)])
+def test_quant_transform_matches_oracle(lq, n1, n2, dtype, bits):
+    K = n1 * n2
+    M = 5
+    say(f"quant transform n1={n1} n2={n2} {dtype} A{bits}")
+    rng = synth.seeded_rng(synth.TEST, 100, n1, n2)
+    P1 = synth.haar_orthogonal(n1, rng)
+    P2 = synth.haar_orthogonal(n2, rng)
+    x = synth.with_outliers(synth.gaussian((M, K), 101, n1, n2), max(1, K // 100), 20.0, 102, n1)
+    if dtype == "bf16":
+        bits16, x32 = synth.round_to_bf16(x)
+        xd = bf16_dev(bits16)
+    else:
+        x32, xd = x, dev(x)
+    clip = 0.83
+    gc, gs, gxt = _quant_gpu(lq, xd, P1, P2, clip, bits, with_xt=True)
+    xt32 = oracle.transformed_f32(x32, P1, P2)
+    # the transform is fp64 then one rounding: identical to the oracle's fl32(fp64)
+    diff_ulps = np.abs(gxt.view(np.int32).astype(np.int64) - xt32.view(np.int32).astype(np.int64))
+    assert diff_ulps.max() <= 1
+    assert np.count_nonzero(diff_ulps) <= 2, np.count_nonzero(diff_ulps)
+    oc, os_ = oracle.quant_act(xt32, clip, bits)
+    if np.count_nonzero(diff_ulps) == 0:
+        np.testing.assert_array_equal(gs, os_)
+        np.testing.assert_array_equal(gc, oc)
+    else:  # a one-ulp rounding-boundary case: only its own group may differ
+        bad_groups = np.unique(np.nonzero(diff_ulps)[1] // 32)
+        keep = np.ones(K // 32, dtype=bool)
+        keep[bad_groups] = False
+        np.testing.assert_array_equal(gs[:, keep], os_[:, keep])
+
+
+def test_quant_zero_rows_and_tiny_clip(lq):
+    x = synth.gaussian((3, 256), 103)
+    x[1] = 0.0
+    gc, gs, _ = _quant_gpu(lq, dev(x), None, None, 1e-30, 4)
+    oc, os_ = oracle.quant_act(x, 1e-30, 4)
+    np.testing.assert_array_equal(gs, os_)
+    np.testing.assert_array_equal(gc, oc)
+    assert np.all(gs[1] == 0) and np.all(gc[1] == 0)
+
+
+# ------------------------------------------------------------------------ GEMM
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,K,N,gw", [(16, 256, 128, 32), (37, 512, 200, 32), (130, 2048, 96, 32),
+                                      (5, 160, 64, 128), (64, 10560, 64, 128)])
+def test_group_dots_bit_exact(lq, bits, M, K, N, gw):
+    say(f"group dots A{bits} M={M} K={K} N={N} gw={gw}")
+    qmax = oracle.qmax_for_bits(bits)
+    qa = synth.seeded_rng(synth.TEST, 110, M, K, bits).integers(-qmax, qmax + 1, size=(M, K)).astype(np.int8)
+    w = synth.gaussian((N, K), 111, N, K, scale=0.02)
+    codes, _scales = pack(lq, w, gw)
+    qw, _ = oracle.quant_weights(w, gw)
+    dots = torch.empty((M, N, K // 32), dtype=torch.int32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR, 1, M, K, N, bits)
+    lq.loopq_group_dots(dev(qa), codes, N, dots, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dots.cpu().numpy().astype(np.int64), oracle.group_dots(qa, qw))
+
+
+@pytest.mark.parametrize("M,K,N,gw", [(16, 256, 128, 32), (200, 1024, 300, 32), (3, 320, 40, 128)])
+def test_gemm_codes_matches_oracle(lq, M, K, N, gw):
+    say(f"gemm codes M={M} K={K} N={N} gw={gw}")
+    rng = synth.seeded_rng(synth.TEST, 120, M, K, N)
+    qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    sa = rng.uniform(0.01, 2.0, size=(M, K // 32)).astype(np.float32)
+    sa[0, 0] = 0.0
+    w = synth.gaussian((N, K), 121, M, K, scale=0.02)
+    codes, scales = pack(lq, w, gw)
+    qw, sw = oracle.quant_weights(w, gw)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR, 1, M, K, N, 4)
+    lq.loopq_gemm_codes(dev(qa), dev(sa), codes, scales, gw, N, y, ws)
+    torch.cuda.synchronize()
+    ref = oracle.rescale_dots(sa, oracle.group_dots(qa, qw), sw, gw)
+    assert rel_err(y.cpu().numpy(), ref) <= Y_TOL
+
+
+# ------------------------------------------------------------------------ end to end
+
+def _tiny_gpu_and_oracle(lq, schedule):
+    wl = synth.tiny_workload()
+    lin = wl.linears[0]
+    P1, P2 = synth.factors_for(wl, "x", lin.K)
+    W = synth.weights_for(wl, lin)
+    xs, _ = synth.activations_for(wl, "x", lin.K)
+    clips = synth.clips_for(wl, "x")
+    # GPU: fold -> pack -> looped forward, all on the device
+    wf = torch.empty((lin.N, lin.K), dtype=torch.float32, device="cuda")
+    fws = lq.empty_workspace(lq.LOOPQ_OP_FOLD, 0, 16, lin.K, 16, 0)
+    lq.loopq_fold_weights(dev(W), dev(P1), dev(P2), wf, fws)
+    codes, scales = lq.empty_packed_weights(lin.K, lin.N, 32)
+    lq.loopq_pack_weights(wf, 32, codes, scales)
+    y = torch.empty((wl.T, wl.M, lin.N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, wl.T, wl.M, lin.K, lin.N, 4)
+    lq.loopq_looped_forward(dev(xs), dev(P1), dev(P2), clips, 4, codes, scales, 32, lin.N, y,
+                            schedule, ws)
+    torch.cuda.synchronize()
+    # oracle: its own fold, weight quantization and loop
+    wt = oracle.fold_weights(W, P1, P2).astype(np.float32)
+    qw, sw = oracle.quant_weights(wt, 32)
+    ref = oracle.looped_forward(xs, P1, P2, clips, 4, qw, sw, 32)
+    return y.cpu().numpy(), ref, (codes, scales, qw, sw, lin)
+
+
+@pytest.mark.parametrize("schedule", [1, 2])
+def test_tiny_looped_end_to_end(lq, schedule):
+    say(f"tiny looped schedule={schedule}")
+    y, ref, (codes, scales, qw, sw, lin) = _tiny_gpu_and_oracle(lq, schedule)
+    gc, gs = export(lq, codes, scales, lin.K, lin.N, 32)
+    np.testing.assert_array_equal(gc, qw)
+    np.testing.assert_array_equal(gs.view(np.uint16), sw.view(np.uint16))
+    assert rel_err(y, ref) <= Y_TOL
+    for t in range(ref.shape[0]):
+        assert rel_err(y[t], ref[t]) <= Y_TOL
+
+
+def test_schedules_bitwise_equal_and_deterministic(lq):
+    y1, _, _ = _tiny_gpu_and_oracle(lq, 1)
+    y2, _, _ = _tiny_gpu_and_oracle(lq, 2)
+    y3, _, _ = _tiny_gpu_and_oracle(lq, 2)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    assert np.array_equal(y2.view(np.uint32), y3.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M", [1, 3, 33])
+def test_linear_small_shapes(lq, bits, M):
+    K, N = 512, 96
+    say(f"linear A{bits} M={M}")
+    rng = synth.seeded_rng(synth.TEST, 130, M, bits)
+    P1 = synth.haar_orthogonal(16, rng)
+    P2 = synth.haar_orthogonal(32, rng)
+    x = synth.with_outliers(synth.gaussian((M, K), 131, M), 3, 15.0, 132, M)
+    w = synth.gaussian((N, K), 133, scale=0.02)
+    codes, scales = pack(lq, w, 32)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR, 1, M, K, N, bits)
+    lq.loopq_w4a4_linear(dev(x), dev(P1), dev(P2), 0.9, bits, codes, scales, 32, N, y, ws)
+    torch.cuda.synchronize()
+    qw, sw = oracle.quant_weights(w, 32)
+    ref, _, _ = oracle.linear(x, P1, P2, 0.9, bits, qw, sw, 32)
+    assert rel_err(y.cpu().numpy(), ref) <= Y_TOL
+
+
+def test_empty_input_is_a_no_op(lq):
+    K, N = 256, 64
+    w = synth.gaussian((N, K), 134, scale=0.02)
+    codes, scales = pack(lq, w, 32)
+    y = torch.full((1, 0, N), 7.0, device="cuda")
+    x = torch.empty((1, 0, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    lq.loopq_looped_forward(x, None, None, [1.0], 4, codes, scales, 32, N, y, 0, ws)
+    torch.cuda.synchronize()
+
+
+def test_zero_input_gives_zero_output(lq):
+    K, N, M = 256, 64, 4
+    w = synth.gaussian((N, K), 135, scale=0.02)
+    codes, scales = pack(lq, w, 32)
+    y = torch.full((M, N), 7.0, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR, 1, M, K, N, 4)
+    lq.loopq_w4a4_linear(torch.zeros((M, K), device="cuda"), None, None, 1.0, 4, codes, scales, 32,
+                         N, y, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
+# ------------------------------------------------------------------------ fold
+
+@pytest.mark.parametrize("n1,n2,N", [(16, 16, 128), (32, 64, 48), (64, 88, 6), (64, 108, 4)])
+def test_fold_matches_oracle(lq, n1, n2, N):
+    K = n1 * n2
+    say(f"fold n1={n1} n2={n2} N={N}")
+    rng = synth.seeded_rng(synth.TEST, 140, n1, n2)
+    P1 = synth.haar_orthogonal(n1, rng)
+    P2 = synth.haar_orthogonal(n2, rng)
+    W = synth.gaussian((N, K), 141, N, scale=0.02)
+    out = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_FOLD, 0, n1, K, n2, 0)
+    lq.loopq_fold_weights(dev(W), dev(P1), dev(P2), out, ws)
+    ref = oracle.fold_weights(W, P1, P2).astype(np.float32)
+    got = out.cpu().numpy()
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+    assert np.count_nonzero(ulps) <= max(2, K * N // 10000)
+
+
+def test_fold_rejects_singular_factor(lq):
+    P1 = np.eye(4, dtype=np.float32)
+    P1[3] = P1[2]
+    P2 = np.eye(8, dtype=np.float32)
+    W = synth.gaussian((4, 32), 142, scale=0.02)
+    out = torch.empty((4, 32), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_FOLD, 0, 4, 32, 8, 0)
+    with pytest.raises(lq.LoopQError) as e:
+        lq.loopq_fold_weights(dev(W), dev(P1), dev(P2), out, ws)
+    assert e.value.status == lq.LOOPQ_ERR_SINGULAR
