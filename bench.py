@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of the looped W4A4 group-quantized linear on one MI355X.
+
+One step = one looped forward of an Ouro-1.4B-like block over T loops: for
+each quantized input (qkv_in feeding the fused q/k/v weight, o_in, up_in,
+down_in) the fused Kronecker transform + group RTN quantizer and the integer
+GEMM with per-group rescale, with the same packed INT4 weights at every loop
+and one LAS clip per input and loop.  Inputs (bf16 activations, packed
+weights, factors) are resident in HBM before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Prints one JSON line.  ``value`` is algorithmic GEMM ops (2*M*N*K summed over
+the step's linears and loops) per second of wall time, in TOPS.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "looped W4A4 linear TOPS & GB/s per loop-step, % of INT8-MFMA/HBM roofline"
+INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--M", type=int, default=1024)
+    p.add_argument("--T", type=int, default=4)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
+    p.add_argument("--profile-steps", type=int, default=0,
+                   help="only run this many steps of the W4A4 step (for rocprofv3), no JSON")
+    return p.parse_args()
+
+
+class Module:
+    """One quantized input and the (fused) weight that reads it."""
+
+    def __init__(self, act, K, N, P1, P2, clips, x, codes, scales):
+        self.act, self.K, self.N = act, K, N
+        self.P1, self.P2, self.clips = P1, P2, clips
+        self.x, self.codes, self.scales = x, codes, scales
+        self.y = None
+        self.ws = None
+
+
+def build_modules(lq, synth, wl, torch):
+    """Group the block's linears by quantized input (q, k, v share qkv_in and
+    are packed as one weight of N = 3 * hidden), draw inputs, pack weights."""
+    groups = {}
+    for lin in wl.linears:
+        groups.setdefault(lin.act, []).append(lin)
+    mods = []
+    for act, lins in groups.items():
+        K = lins[0].K
+        W = __import__("numpy").concatenate([synth.weights_for(wl, lin) for lin in lins], axis=0)
+        N = W.shape[0]
+        codes, scales = lq.empty_packed_weights(K, N, wl.group_w)
+        lq.loopq_pack_weights(torch.from_numpy(W).cuda(), wl.group_w, codes, scales)
+        P1, P2 = synth.factors_for(wl, act, K)
+        bits, _ = synth.activations_for(wl, act, K)
+        x = torch.from_numpy(bits.view(__import__("numpy").int16)).cuda().view(torch.bfloat16)
+        mods.append(Module(act, K, N, torch.from_numpy(P1).cuda(), torch.from_numpy(P2).cuda(),
+                           [float(c) for c in synth.clips_for(wl, act)], x, codes, scales))
+    return mods
+
+
+def alg_ops(mods, T, M):
+    return sum(2.0 * T * M * m.N * m.K for m in mods)
+
+
+def alg_bytes_per_loop_step(mods, M, group_w):
+    """Packed weights + fp16 steps + bf16 activations in + fp32 y out, once per loop-step."""
+    b = 0.0
+    for m in mods:
+        b += m.N * m.K / 2 + 2 * m.N * (m.K // group_w)
+        b += 2 * M * m.K + 4 * M * m.N
+    return b
+
+
+def run_steps(lq, mods, bits, schedule, steps):
+    for _ in range(steps):
+        for m in mods:
+            lq.loopq_looped_forward(m.x, m.P1, m.P2, m.clips, bits, m.codes, m.scales, 32, m.N, m.y,
+                                    schedule, m.ws)
+
+
+def timed(lq, torch, mods, bits, schedule, steps, warmup, hooks=False):
+    run_steps(lq, mods, bits, schedule, warmup)
+    torch.cuda.synchronize()
+    lq.loopq_timing_reset()
+    if hooks:
+        lq.loopq_timing_enable(True)
+    t0 = time.perf_counter()
+    run_steps(lq, mods, bits, schedule, steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lq.loopq_timing_enable(False)
+    per_kernel = lq.loopq_timing_read(3)
+    return (t1 - t0) / steps, per_kernel
+
+
+def cpu_baseline(wl, mods_meta, rows_hint):
+    """The oracle, untuned, on a bounded sample: `rows` token rows of loop 0
+    of every quantized input (transform + Eq.(4) RTN + integer group dots +
+    rescale), timed on the host; reported as TOPS of the same algorithmic ops."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+    from bit_ptq_looped_amd import synth
+
+    rows = rows_hint or 128
+    prepared = []
+    for act, K, lins in mods_meta:
+        W = np.concatenate([synth.weights_for(wl, lin) for lin in lins], axis=0)
+        qw, sw = oracle.quant_weights(W, wl.group_w)       # offline step, not timed
+        P1, P2 = synth.factors_for(wl, act, K)
+        _, x32 = synth.activations_for(wl, act, K, rows=rows)
+        clip = float(synth.clips_for(wl, act)[0])
+        prepared.append((x32[0], P1, P2, clip, qw, sw))
+    import contextlib
+    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        t0 = time.perf_counter()
+        for x, P1, P2, clip, qw, sw in prepared:
+            oracle.linear(x, P1, P2, clip, wl.bits_a, qw, sw, wl.group_w)
+        dt = time.perf_counter() - t0
+    ops = sum(2.0 * rows * x.shape[1] * qw.shape[0] for x, _, _, _, qw, _ in prepared)
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} token rows of loop 0 of each quantized input (qkv, o, up, down) at full "
+                      f"K and N; {dt:.1f} s on the host, BLAS limited to 1 thread; weight "
+                      f"quantization and input drawing not timed",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this path runs on one GPU; multi-GPU sharding is described, not built "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from bit_ptq_looped_amd import loopq as lq
+    from bit_ptq_looped_amd import synth
+
+    lq.load()
+    torch.cuda.set_device(0)
+    wl = synth.ouro_block_workload(bits_a=4, M=args.M, T=args.T)
+    mods = build_modules(lq, synth, wl, torch)
+    T, M = wl.T, wl.M
+    for m in mods:
+        m.y = torch.empty((T, M, m.N), dtype=torch.float32, device="cuda")
+        m.ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, m.K, m.N, 8)
+    torch.cuda.synchronize()
+
+    if args.profile_steps:
+        run_steps(lq, mods, 4, lq.LOOPQ_SCHED_AUTO, args.profile_steps)
+        torch.cuda.synchronize()
+        print(f"profiled {args.profile_steps} steps", flush=True)
+        return
+
+    ops = alg_ops(mods, T, M)
+    s_ws, kern = timed(lq, torch, mods, 4, lq.LOOPQ_SCHED_AUTO, args.steps, args.warmup, hooks=True)
+    s_ws_nohook, _ = timed(lq, torch, mods, 4, lq.LOOPQ_SCHED_AUTO, args.steps, args.warmup)
+    s_seq, _ = timed(lq, torch, mods, 4, lq.LOOPQ_SCHED_LOOP_SEQUENTIAL, args.steps, args.warmup)
+    s_a8, kern_a8 = timed(lq, torch, mods, 8, lq.LOOPQ_SCHED_AUTO, args.steps, args.warmup, hooks=True)
+
+    gemm_ms, gemm_n = kern[lq.LOOPQ_KERNEL_GEMM]
+    quant_ms, quant_n = kern[lq.LOOPQ_KERNEL_QUANT_TRANSFORM]
+    gemm_ops_total = ops * args.steps
+    achieved = gemm_ops_total / (gemm_ms * 1e-3) / 1e12
+    bytes_ls = alg_bytes_per_loop_step(mods, M, wl.group_w)
+
+    out = {
+        "metric": METRIC,
+        "value": ops / s_ws / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": s_ws * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "M": M, "T": T, "hidden": 2048, "intermediate": 5632,
+            "linears": "q|k|v fused (2048->6144), o 2048->2048, up 2048->5632, down 5632->2048",
+            "bits": "W4A4", "group_a": 32, "group_w": 32,
+            "factors": "(32,64) for K=2048, (64,88) for K=5632",
+            "schedule": "weight-stationary (all T loops per launch)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": INT8_PEAK_TOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / INT8_PEAK_TOPS,
+            "traffic": None,
+            "kernel": "gemm_kernel<0> (integer GEMM + per-group rescale)",
+            "launches": gemm_n,
+            "avg_launch_ms": gemm_ms / max(gemm_n, 1),
+        },
+        "ms_per_loop_step": s_ws * 1e3 / T,
+        "tops_per_loop_step": ops / T / (s_ws / T) / 1e12,
+        "gbps_per_loop_step": bytes_ls / (s_ws / T) / 1e9,
+        "frac_int8_peak": ops / s_ws / 1e12 / INT8_PEAK_TOPS,
+        "frac_hbm_peak": bytes_ls / (s_ws / T) / 1e9 / HBM_PEAK_GBS,
+        "kernels_ms_per_step": {"quant_transform": quant_ms / args.steps, "gemm": gemm_ms / args.steps},
+        "ms_per_step_without_hooks": s_ws_nohook * 1e3,
+        "loop_sequential": {"ms_per_step": s_seq * 1e3, "value": ops / s_seq / 1e12},
+        "w4a8": {"ms_per_step": s_a8 * 1e3, "value": ops / s_a8 / 1e12,
+                 "gemm_ms_per_step": kern_a8[lq.LOOPQ_KERNEL_GEMM][0] / args.steps},
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        groups = {}
+        for lin in wl.linears:
+            groups.setdefault(lin.act, []).append(lin)
+        meta = [(act, lins[0].K, lins) for act, lins in groups.items()]
+        cb = cpu_baseline(wl, meta, args.cpu_rows)
+        out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

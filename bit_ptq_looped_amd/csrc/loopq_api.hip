@@ -3,6 +3,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "../../include/loopq.h"
 #include "loopq_internal.h"
 
@@ -17,6 +20,60 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? LOOPQ_OK : LOOPQ_ERR_HIP; }
+
+// ---------------------------------------------------------------------------
+// Timing hooks: while enabled, each hot-path launch is bracketed by two HIP
+// events recorded on its own stream; loopq_timing_read sums their elapsed
+// times per kernel id.  Events are pooled and reused after a read or reset.
+// ---------------------------------------------------------------------------
+constexpr int kTimingKernels = 4;  // LOOPQ_KERNEL_* ids
+struct TimingRec {
+  int kid;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRec> g_timing_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct TimingScope {
+  bool on = false;
+  TimingRec rec{};
+  hipStream_t s;
+  TimingScope(int kid, hipStream_t stream) : s(stream) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (!g_timing_on) return;
+    rec.kid = kid;
+    rec.start = pooled_event();
+    rec.stop = pooled_event();
+    if (!rec.start || !rec.stop) return;
+    on = hipEventRecord(rec.start, s) == hipSuccess;
+  }
+  ~TimingScope() {
+    if (!on) return;
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (hipEventRecord(rec.stop, s) == hipSuccess) g_timing_recs.push_back(rec);
+  }
+};
+
+void recycle_locked() {
+  for (auto& r : g_timing_recs) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_timing_recs.clear();
+}
 
 // internal activation buffers for `rows` quantized rows of width K
 struct ActBuffers {
@@ -100,10 +157,17 @@ int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const floa
   a.scales = b.scales;
   a.scales_gm = 1;
   a.scales_ld = b.ld;
-  hipError_t e = launch_quant_act(a, s);
+  hipError_t e;
+  {
+    TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, s);
+    e = launch_quant_act(a, s);
+  }
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
-  e = launch_gemm(b.codes, b.scales, b.ld, rows, K, N, reinterpret_cast<const uint8_t*>(w_codes),
-                  reinterpret_cast<const __half*>(w_scales), gw, y, nullptr, 0, s);
+  {
+    TimingScope ts(LOOPQ_KERNEL_GEMM, s);
+    e = launch_gemm(b.codes, b.scales, b.ld, rows, K, N, reinterpret_cast<const uint8_t*>(w_codes),
+                    reinterpret_cast<const __half*>(w_scales), gw, y, nullptr, 0, s);
+  }
   return hip_status(e);
 }
 
@@ -332,6 +396,41 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
     e = launch_gemm(b.codes, nullptr, b.ld, M, K, N, reinterpret_cast<const uint8_t*>(w_codes),
                     nullptr, 32, nullptr, dots, 1, s);
   return hip_status(e);
+}
+
+int32_t loopq_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_on = on != 0;
+  return LOOPQ_OK;
+}
+
+int32_t loopq_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (auto& r : g_timing_recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return LOOPQ_ERR_HIP;
+  }
+  recycle_locked();
+  return LOOPQ_OK;
+}
+
+int32_t loopq_timing_read(int32_t n, double* ms_host, int64_t* launches_host) {
+  if (n <= 0 || !ms_host || !launches_host) return LOOPQ_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (int k = 0; k < n; ++k) {
+    ms_host[k] = 0.0;
+    launches_host[k] = 0;
+  }
+  for (auto& r : g_timing_recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return LOOPQ_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return LOOPQ_ERR_HIP;
+    if (r.kid < n) {
+      ms_host[r.kid] += ms;
+      launches_host[r.kid] += 1;
+    }
+  }
+  recycle_locked();
+  return LOOPQ_OK;
 }
 
 }  // extern "C"

@@ -29,6 +29,7 @@ LOOPQ_ERR_SINGULAR = -7
 LOOPQ_F32, LOOPQ_BF16 = 0, 1
 LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
 LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD = 1, 2, 3
+LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM = 0, 1, 2
 
 # every entry point of include/loopq.h with its ctypes signature
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -47,6 +48,9 @@ SIGNATURES = {
     "loopq_gemm_codes": ([_P, _P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
     "loopq_export_weights": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "loopq_group_dots": ([_P, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "loopq_timing_enable": ([_I], _I),
+    "loopq_timing_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
+    "loopq_timing_reset": ([], _I),
 }
 
 _lib = None
@@ -205,6 +209,22 @@ def loopq_group_dots(a_codes, w_codes, N: int, dots, workspace, stream=None):
     _check(load().loopq_group_dots(_ptr(a_codes), M, K, N, _ptr(w_codes), _ptr(dots), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)),
            "loopq_group_dots")
+
+
+def loopq_timing_enable(on: bool) -> None:
+    _check(load().loopq_timing_enable(1 if on else 0), "loopq_timing_enable")
+
+
+def loopq_timing_reset() -> None:
+    _check(load().loopq_timing_reset(), "loopq_timing_reset")
+
+
+def loopq_timing_read(n: int = 3):
+    """Per kernel id: (total milliseconds, launches) since the last read."""
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(load().loopq_timing_read(n, ms, cnt), "loopq_timing_read")
+    return [(ms[k], cnt[k]) for k in range(n)]
 
 
 # ----------------------------------------------------------------- buffer helpers

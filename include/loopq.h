@@ -189,6 +189,26 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
                          const void* w_codes, int32_t* dots, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Measurement hooks (tracing).  While enabled, every hot-path kernel launch is
+ * bracketed by a pair of HIP events recorded on the launch's own stream, so
+ * kernel durations can be read without a profiler.  Kernel ids: */
+typedef enum {
+  LOOPQ_KERNEL_QUANT_TRANSFORM = 0, /* fused transform + quantizer */
+  LOOPQ_KERNEL_QUANT_PLAIN = 1,     /* quantizer without transform */
+  LOOPQ_KERNEL_GEMM = 2             /* integer GEMM + rescale */
+} loopq_kernel_id;
+
+/* Turn the hooks on (1) or off (0).  Host only; cheap. */
+int32_t loopq_timing_enable(int32_t on);
+
+/* Sum, per kernel id k < n, the elapsed milliseconds and the number of
+ * launches recorded since the last read or reset, into ms_host[k] and
+ * launches_host[k]; then forget the records.  Waits for the recorded events. */
+int32_t loopq_timing_read(int32_t n, double* ms_host, int64_t* launches_host);
+
+/* Forget all records (waits for outstanding events). */
+int32_t loopq_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

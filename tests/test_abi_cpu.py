@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
         assert n in loopq.SIGNATURES, n
