@@ -29,6 +29,11 @@ COMMON = [
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# per-file code generation options
+EXTRA = {
+    # keep MFMA results in VGPRs: the rescale reads every element with VALU ops
+    "gemm_w4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _hipcc() -> str:
@@ -40,7 +45,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, hipcc: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON, "-c", src, "-o", obj]
+    cmd = [hipcc, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -17,8 +17,9 @@
 // Tiling: 256 threads = 4 waves in a 2x2 arrangement, 128x128 outputs per
 // work-group, 64x64 (2x2 MFMA tiles) per wave.  Operands stream from global
 // memory in the tiled layouts of loopq_internal.h (each wave load is one
-// contiguous 1 KB / 512 B block); the next group is prefetched while the
-// current one is multiplied and folded.
+// contiguous 1 KB / 512 B block); the loop is unrolled twice so the next
+// group's loads are in flight while the current one is multiplied and folded,
+// with no register copies between stages.
 #include "loopq_internal.h"
 
 namespace loopq {
@@ -49,56 +50,60 @@ __device__ __forceinline__ v4i unpack_w(uint2 p) {
   return r;
 }
 
+// Operands of one K-group, as loaded (raw: nothing is converted until used,
+// so a prefetch never forces a wait).
 struct Stage {
-  v4i a[2];
-  uint2 b[2];
-  float4 sa[2][4];
-  float sw[2];
+  uint2 w[2];        // packed nibbles: MFMA operand A, the wave's two 32-column tiles
+  v4i x[2];          // activation codes: MFMA operand B, the wave's two 32-row tiles
+  float sa[2];       // activation step of the lane's row, per row tile
+  uint4 sw[2][2];    // the lane's 16 fp16 weight steps per column tile
 };
 
+// The wave computes 32x32 tiles of y^T: result element e of lane l belongs to
+// row m = l % 32 of the activation tile and column n = 8 (e / 4) + 4 (l / 32)
+// + e % 4 of the weight tile.  One activation step per lane and tile; the
+// 16 weight steps of the lane are stored contiguously (see the step layout in
+// loopq_internal.h) and enter the rescale as fp16 operands of v_fma_mix.
 template <int MODE>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int h = lane >> 5;    // K-half of the operands; row group of the result
-  const int c = lane & 31;    // column of the result
+  const int h = lane >> 5;
+  const int c = lane & 31;
   const int m_base = blockIdx.y * 128 + (wave >> 1) * 64;
   const int n_base = blockIdx.x * 128 + (wave & 1) * 64;
+  if (m_base >= g.M || n_base >= g.N) return;
   const int Ga = g.K >> 5;
   const int Gw = ((g.K >> 5) + (1 << g.gshift) - 1) >> g.gshift;
-  bool mv[2], nv[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    mv[t] = (m_base + 32 * t) < g.M;
-    nv[t] = (n_base + 32 * t) < g.N;
-  }
-  if (!mv[0] || !nv[0]) return;  // the second tile is only valid if the first is
+  const int mlast = ((g.M + 31) >> 5) - 1;
+  const int nlast = ((g.N + 31) >> 5) - 1;
 
-  const int8_t* a_ptr[2];
+  // Tiles past the matrix edge re-read the last valid block (always in
+  // bounds); their results are dropped at the store.
+  const int8_t* x_ptr[2];
   const uint8_t* w_ptr[2];
-  const __half* sw_ptr[2];
+  const float* sa_ptr[2];
+  const uint4* sw_ptr[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int mb = (m_base >> 5) + t;
-    const int nb = (n_base >> 5) + t;
-    a_ptr[t] = g.a + (int64_t)mb * Ga * 1024 + lane * 16;
+    const int mb = min((m_base >> 5) + t, mlast);
+    const int nb = min((n_base >> 5) + t, nlast);
+    x_ptr[t] = g.a + (int64_t)mb * Ga * 1024 + lane * 16;
     w_ptr[t] = g.w + (int64_t)nb * Ga * kBlockBytes + lane * 8;
-    sw_ptr[t] = g.sw + (int64_t)nb * Gw * 32 + c;
+    sa_ptr[t] = g.sa + mb * 32 + c;
+    sw_ptr[t] = reinterpret_cast<const uint4*>(g.sw) + (int64_t)nb * Gw * 4 + 2 * h;
   }
 
   auto load = [&](int j, Stage& s) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      if (mv[t]) s.a[t] = *reinterpret_cast<const v4i*>(a_ptr[t] + (int64_t)j * 1024);
-      else s.a[t] = v4i{0, 0, 0, 0};
-      if (nv[t]) s.b[t] = *reinterpret_cast<const uint2*>(w_ptr[t] + (int64_t)j * kBlockBytes);
-      else s.b[t] = uint2{0x88888888u, 0x88888888u};
+      s.x[t] = *reinterpret_cast<const v4i*>(x_ptr[t] + (int64_t)j * 1024);
+      s.w[t] = *reinterpret_cast<const uint2*>(w_ptr[t] + (int64_t)j * kBlockBytes);
       if (MODE == 0) {
-        const float* sap = g.sa + (int64_t)j * g.ld_sa + m_base + 32 * t + 4 * h;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          s.sa[t][q] = mv[t] ? *reinterpret_cast<const float4*>(sap + 8 * q) : float4{0, 0, 0, 0};
-        s.sw[t] = nv[t] ? __half2float(sw_ptr[t][(int64_t)(j >> g.gshift) * 32]) : 0.0f;
+        s.sa[t] = sa_ptr[t][(int64_t)j * g.ld_sa];
+        const uint4* p = sw_ptr[t] + (int64_t)(j >> g.gshift) * 4;
+        s.sw[t][0] = p[0];
+        s.sw[t][1] = p[1];
       }
     }
   };
@@ -111,65 +116,78 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[t][u][e] = 0.0f;
 
-  Stage cur, nxt;
-  load(0, cur);
-  for (int j = 0; j < Ga; ++j) {
-    if (j + 1 < Ga) load(j + 1, nxt);
-    const v4i b0 = unpack_w(cur.b[0]);
-    const v4i b1 = unpack_w(cur.b[1]);
-    v16i d[2][2];
+  auto compute = [&](const Stage& s, int j) {
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    d[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[0], b0, zero, 0, 0, 0);
-    d[0][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[0], b1, zero, 0, 0, 0);
-    d[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[1], b0, zero, 0, 0, 0);
-    d[1][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[1], b1, zero, 0, 0, 0);
-    if (MODE == 0) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int u = 0; u < 2; ++u) {
+      const v4i wu = unpack_w(s.w[u]);
+      const uint32_t swr[8] = {s.sw[u][0].x, s.sw[u][0].y, s.sw[u][0].z, s.sw[u][0].w,
+                               s.sw[u][1].x, s.sw[u][1].y, s.sw[u][1].z, s.sw[u][1].w};
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 sa4 = cur.sa[t][q];
-            const float sv[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int e = 4 * q + r;
-              const float coef = sv[r] * cur.sw[u];
-              acc[t][u][e] = __builtin_fmaf((float)d[t][u][e], coef, acc[t][u][e]);
-            }
-          }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (!mv[t] || !nv[u]) continue;
-          const int col = n_base + 32 * u + c;
-          if (col >= g.N) continue;
+      for (int t = 0; t < 2; ++t) {
+        const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(wu, s.x[t], zero, 0, 0, 0);
+        if (MODE == 0) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int row = m_base + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (row < g.M) g.dots[((int64_t)row * g.N + col) * Ga + j] = d[t][u][e];
+            const uint32_t pair = swr[e >> 1];
+            const __half hw = __ushort_as_half((unsigned short)((e & 1) ? (pair >> 16) : (pair & 0xffffu)));
+            const float coef = __builtin_fmaf(__half2float(hw), s.sa[t], 0.0f);
+            acc[t][u][e] = __builtin_fmaf((float)d[e], coef, acc[t][u][e]);
+          }
+        } else {
+          const int row = m_base + 32 * t + c;
+          if (row < g.M) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int col = n_base + 32 * u + 8 * (e >> 2) + 4 * h + (e & 3);
+              if (col < g.N) g.dots[((int64_t)row * g.N + col) * Ga + j] = d[e];
+            }
           }
         }
+      }
     }
-    if (j + 1 < Ga) cur = nxt;
+  };
+
+  // Two stages, two groups in flight: a stage is reloaded only after its
+  // group has been folded (the scheduling barriers keep the compiler from
+  // hoisting the reload above the fold, which would need register copies).
+  // Loads past the last group re-read it (in bounds, unused), so the loop
+  // body is one basic block the barriers can order.
+  Stage s0, s1;
+  load(0, s0);
+  load(min(1, Ga - 1), s1);
+  int j = 0;
+  for (; j + 1 < Ga; j += 2) {
+    compute(s0, j);
+    __builtin_amdgcn_sched_barrier(0);
+    load(min(j + 2, Ga - 1), s0);
+    compute(s1, j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(min(j + 3, Ga - 1), s1);
   }
+  if (j < Ga) compute(s0, j);
 
   if (MODE == 0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      const int row = m_base + 32 * t + c;
+      if (row >= g.M) continue;
+      float* yr = g.y + (int64_t)row * g.N;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int col = n_base + 32 * u + c;
-        if (!mv[t] || col >= g.N) continue;
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = m_base + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (row < g.M) g.y[(int64_t)row * g.N + col] = acc[t][u][e];
+        for (int q = 0; q < 4; ++q) {
+          const int col = n_base + 32 * u + 8 * q + 4 * h;
+          if (col + 3 < g.N && (g.N & 3) == 0) {
+            *reinterpret_cast<float4*>(yr + col) =
+                float4{acc[t][u][4 * q], acc[t][u][4 * q + 1], acc[t][u][4 * q + 2], acc[t][u][4 * q + 3]};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (col + r < g.N) yr[col + r] = acc[t][u][4 * q + r];
+          }
         }
-      }
+    }
   }
 }
 

@@ -26,7 +26,6 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? LOOPQ_OK : LOOPQ_ERR
 // events recorded on its own stream; loopq_timing_read sums their elapsed
 // times per kernel id.  Events are pooled and reused after a read or reset.
 // ---------------------------------------------------------------------------
-constexpr int kTimingKernels = 4;  // LOOPQ_KERNEL_* ids
 struct TimingRec {
   int kid;
   hipEvent_t start, stop;

@@ -21,7 +21,10 @@ namespace loopq {
 // contiguous bytes; lane l gets column l % 32 and K-half l / 32, which is the
 // B-operand layout of V_MFMA_I32_32X32X32_I8.
 //
-// Steps: fp16, [ceil(N/32)][G_w][32] (column block, weight group, column).
+// Steps: fp16, [ceil(N/32)][G_w][32] (column block, weight group, slot);
+// column c of a block sits in slot step_slot(c) = ((c >> 2) & 1) * 16 +
+// (c >> 3) * 4 + (c & 3), so the 16 columns 8q + 4h + r (q, r in 0..3) that
+// one half-wave holds in a 32x32 MFMA result are 32 contiguous bytes.
 // Columns past N (padding to a multiple of 32) hold code 0 and step 0.
 // ---------------------------------------------------------------------------
 constexpr int kColBlock = 32;
@@ -29,6 +32,7 @@ constexpr int kChunkK = 32;
 constexpr int kBlockBytes = 512;
 
 inline int64_t padded_cols(int64_t N) { return (N + 31) / 32 * 32; }
+__host__ __device__ inline int step_slot(int c) { return ((c >> 2) & 1) * 16 + (c >> 3) * 4 + (c & 3); }
 inline int64_t weight_groups(int64_t K, int64_t gw) { return (K + gw - 1) / gw; }
 
 // ---------------------------------------------------------------------------

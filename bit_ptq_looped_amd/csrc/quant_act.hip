@@ -24,6 +24,11 @@ namespace {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
+// v if mask is all ones, +0 if it is zero (bitwise, so no branch is formed)
+__device__ __forceinline__ float masked(float v, uint32_t mask) {
+  return __uint_as_float(__float_as_uint(v) & mask);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -109,34 +114,149 @@ __global__ __launch_bounds__(256) void quant_plain_kernel(QuantArgs a) {
   }
 }
 
-// Transform + quantize.  Dynamic LDS: P1 [n1][sp1] f32 at 0, P2 [n2][sp2] f32
-// at off_p2, X [R*n1][sx] f32 at off_x (reused for x~, flat [R][K]), T
-// [R*n1][st] f64 at off_t.
+// Stage 1 of the transform for NI work items of one wave (items wave and
+// wave + 4): T[ii][rt] accumulates X_r * P2 over the 4-deep steps of b.
+template <int NRT, int N1, int N2, int NI>
+__device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, const float* sX,
+                                       int wave, int njt, int li, int lk, v4d (&T)[2][NRT]) {
+  const int n1 = N1 > 0 ? N1 : a.n1;
+  const int n2 = N2 > 0 ? N2 : a.n2;
+  const float* pb[NI];
+  const float* xa[NI][NRT];
+  uint32_t mj[NI], mrow[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) mrow[rt] = (rt * 16 + li < n1) ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int item = wave + 4 * ii;
+    const int r = item / njt;
+    const int j = (item - r * njt) * 16 + li;
+    mj[ii] = j < n2 ? 0xffffffffu : 0u;
+    pb[ii] = sP2 + (j < n2 ? j : 0);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) xa[ii][rt] = sX + (r * n1 + min(rt * 16 + li, n1 - 1)) * a.sx;
+  }
+  auto step = [&](int s) {
+    const int b = 4 * s + lk;
+    double bv[NI];
+    double av[NI][NRT];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      // addresses are clamped in bounds: load unconditionally, then zero the
+      // lanes outside the matrix with an integer mask (no branch)
+      bv[ii] = (double)masked(pb[ii][b * a.sp2], mj[ii]);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) av[ii][rt] = (double)masked(xa[ii][rt][b], mrow[rt]);
+    }
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+        T[ii][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ii][rt], bv[ii], T[ii][rt], 0, 0, 0);
+  };
+  if constexpr (N2 > 0) {  // fully unrolled: the accumulators stay in place
+#pragma unroll
+    for (int s = 0; s < N2 / 4; ++s) step(s);
+  } else {
+    for (int s = 0; s < (n2 >> 2); ++s) step(s);
+  }
+}
+
+// Stage 2 for the same items: x~[:, tile] = P1^T * T, B operands straight
+// from the stage-1 results (element e of tile rt is step s = 4 rt + e);
+// writes fp32 x~ into the flat rows of the X region.
+template <int NRT, int N1, int N2, int NI>
+__device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, float* sX, int wave,
+                                       int njt, int li, int lk, const v4d (&T)[2][NRT]) {
+  const int n1 = N1 > 0 ? N1 : a.n1;
+  const int n2 = N2 > 0 ? N2 : a.n2;
+  const int K = n1 * n2;
+  v4d o[NI][NRT];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) o[ii][it] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int s = 4 * rt + e;
+      if (s < (n1 >> 2)) {
+        const float* pa = sP1 + (4 * s + lk) * a.sp1;
+        double av[NRT];
+#pragma unroll
+        for (int it = 0; it < NRT; ++it) {
+          const int i = it * 16 + li;
+          av[it] = (double)masked(pa[min(i, n1 - 1)], i < n1 ? 0xffffffffu : 0u);
+        }
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+          for (int it = 0; it < NRT; ++it)
+            o[ii][it] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[it], T[ii][rt][e], o[ii][it], 0, 0, 0);
+      }
+    }
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int item = wave + 4 * ii;
+    const int r = item / njt;
+    const int j = (item - r * njt) * 16 + li;
+    if (j < n2) {
+      float* xr = sX + r * K + j;
+#pragma unroll
+      for (int it = 0; it < NRT; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int io = it * 16 + 4 * e + lk;  // result element e of lane l: row 4e + l/16
+          if (io < n1) xr[io * n2] = (float)o[ii][it][e];  // one rounding to fp32 (RNE)
+        }
+    }
+  }
+}
+
+// Transform + quantize, NRT = ceil(n1 / 16) row tiles.  N1, N2 > 0 fix the
+// factor sizes at compile time (the k-loops then unroll fully, which keeps the
+// fp64 accumulators in place); N1 = N2 = 0 takes them from the arguments.
+//
+// Dynamic LDS: P1 [n1][sp1] f32 at 0, P2 [n2][sp2] f32 at off_p2, and
+// X [R*n1][sx] f32 at off_x; after stage 1 the same region holds x~ as flat
+// fp32 rows [R][K].
+//
+// Work item = (row r of the chunk, 16-column tile jt of the n1 x n2 grid).
+// Stage 1 computes T[:, jt] = X_r * P2[:, jt] as NRT independent 16x16
+// accumulators (the reduction over b runs in 4-deep MFMA steps).  In the
+// result, lane l holds T[16 rt + 4 e + l/16][16 jt + l%16] in element e of
+// tile rt, which is exactly the B operand stage 2 needs from lane l at step
+// s = 4 rt + e (rows a = 4 s + l/16), so T stays in registers.  Stage 2 then
+// forms x~[:, jt] = P1^T * T with NRT accumulators over the i tiles.
+template <int NRT, int N1, int N2>
 __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   float* sP1 = reinterpret_cast<float*>(lds);
   float* sP2 = reinterpret_cast<float*>(lds + a.off_p2);
   float* sX = reinterpret_cast<float*>(lds + a.off_x);
-  double* sT = reinterpret_cast<double*>(lds + a.off_t);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n1 = a.n1, n2 = a.n2, K = a.K;
+  const int n1 = N1 > 0 ? N1 : a.n1;
+  const int n2 = N2 > 0 ? N2 : a.n2;
+  const int K = n1 * n2;
   const int R = a.R;
   const float qmaxf = (float)a.qmax;
+  const int njt = (n2 + 15) >> 4;
 
   for (int idx = tid; idx < n1 * n1; idx += 256) sP1[(idx / n1) * a.sp1 + idx % n1] = a.P1[idx];
   for (int idx = tid; idx < n2 * n2; idx += 256) sP2[(idx / n2) * a.sp2 + idx % n2] = a.P2[idx];
 
-  const int li = lane & 15;  // row (A) / column (B, D) within a 16x16 tile
-  const int lk = lane >> 4;  // k within a 4-deep step; D rows lk, lk+4, lk+8, lk+12
+  const int li = lane & 15;  // row of A / column of B and of the result
+  const int lk = lane >> 4;  // k within a 4-deep step; result rows lk + 4 e
   const int nchunks = (a.rows + R - 1) / R;
 
   for (int chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
     const int row0 = chunk * R;
     const int rows = min(R, a.rows - row0);
-    __syncthreads();  // previous chunk done with sX / sT (and P staged on the first pass)
+    __syncthreads();  // previous chunk done with the x~ rows (and P staged on the first pass)
 
     // ---- load X rows (4 consecutive b per thread-step; n2 % 4 == 0)
     const int nq = rows * K / 4;
@@ -162,70 +282,26 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
     }
     __syncthreads();
 
-    // ---- stage 1: T[(r,a)][j] = sum_b X[(r,a)][b] * P2[b][j]
-    {
-      const int flat_rows = rows * n1;
-      const int nrt = (flat_rows + 15) >> 4;
-      const int njt = (n2 + 15) >> 4;
-      const int nsteps = n2 >> 2;
-      for (int tile = wave; tile < nrt * njt; tile += 4) {
-        const int rt = tile / njt, jt = tile - (tile / njt) * njt;
-        const int ra = rt * 16 + li;
-        const int j = jt * 16 + li;
-        const bool va = ra < flat_rows;
-        const bool vj = j < n2;
-        const float* xa = sX + (va ? ra : 0) * a.sx;
-        const float* pb = sP2 + (vj ? j : 0);
-        v4d acc = {0.0, 0.0, 0.0, 0.0};
-        for (int s = 0; s < nsteps; ++s) {
-          const int b = 4 * s + lk;
-          const double av = va ? (double)xa[b] : 0.0;
-          const double bv = vj ? (double)pb[b * a.sp2] : 0.0;
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
-        }
-        if (vj) {
+    // ---- stage 1 for the wave's items (at most two: the plan keeps R * njt <= 8);
+    // both items run in one loop so 2 * NRT accumulator chains interleave
+    const int items = rows * njt;
+    const int nmine = (wave < items) + (wave + 4 < items);
+    v4d T[2][NRT];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int ro = rt * 16 + 4 * e + lk;  // D element e of lane l: row 4e + l/16
-            if (ro < flat_rows) sT[ro * a.st + j] = acc[e];
-          }
-        }
-      }
-    }
-    __syncthreads();
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) T[ii][rt] = v4d{0.0, 0.0, 0.0, 0.0};
+    if (nmine == 2)
+      stage1<NRT, N1, N2, 2>(a, sP2, sX, wave, njt, li, lk, T);
+    else if (nmine == 1)
+      stage1<NRT, N1, N2, 1>(a, sP2, sX, wave, njt, li, lk, T);
+    __syncthreads();  // every X read is done; x~ may now overwrite the region
 
-    // ---- stage 2: x~[r][i][j] = sum_a P1[a][i] * T[(r,a)][j]  -> fp32, flat in sX
-    {
-      const int nit = (n1 + 15) >> 4;
-      const int njt = (n2 + 15) >> 4;
-      const int per_row = nit * njt;
-      const int nsteps = n1 >> 2;
-      for (int tile = wave; tile < rows * per_row; tile += 4) {
-        const int r = tile / per_row;
-        const int rem = tile - r * per_row;
-        const int it = rem / njt, jt = rem - (rem / njt) * njt;
-        const int i = it * 16 + li;
-        const int j = jt * 16 + li;
-        const bool vi = i < n1;
-        const bool vj = j < n2;
-        const float* pa = sP1 + (vi ? i : 0);
-        const double* tb = sT + (int64_t)(r * n1) * a.st + (vj ? j : 0);
-        v4d acc = {0.0, 0.0, 0.0, 0.0};
-        for (int s = 0; s < nsteps; ++s) {
-          const int aa = 4 * s + lk;
-          const double av = vi ? (double)pa[aa * a.sp1] : 0.0;
-          const double bv = vj ? tb[aa * a.st] : 0.0;
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
-        }
-        if (vj) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int io = it * 16 + 4 * e + lk;
-            if (io < n1) sX[r * K + io * n2 + j] = (float)acc[e];  // RNE to fp32
-          }
-        }
-      }
-    }
+    // ---- stage 2: x~[i][j] = sum_a P1[a][i] T[a][j], rounded once to fp32
+    if (nmine == 2)
+      stage2<NRT, N1, N2, 2>(a, sP1, sX, wave, njt, li, lk, T);
+    else if (nmine == 1)
+      stage2<NRT, N1, N2, 1>(a, sP1, sX, wave, njt, li, lk, T);
     __syncthreads();
 
     // ---- quantize groups of the flat transformed rows
@@ -263,34 +339,46 @@ int x_bytes_for(int R, int n1, int sx, int K) {
   return (xb + 15) / 16 * 16;
 }
 
-// LDS plan of the fused transform kernel: strides chosen so the MFMA operand
-// reads of 16 lanes fall on distinct banks, then as many rows per chunk as fit
-// two work-groups per CU (at most 16).  Returns false if one row does not fit.
+// LDS plan of the fused transform kernel: P1 and P2 with strides that put the
+// 16 lanes of an MFMA operand read on distinct banks, and R rows of X with a
+// stride of 2 mod 32 (the same region later holds the flat x~ rows).  R is
+// the largest row count whose R * ceil(n2/16) work items fit two per wave.
+// The bank padding of P1/P2 is dropped if that lets two work-groups share a
+// CU.  Returns false if one row does not fit.
 bool plan_quant(QuantArgs& a) {
   const int budget = 160 * 1024;
-  a.sp1 = a.n1 <= 16 ? 16 : stride_mod(a.n1, 32, 16);
-  a.sp2 = a.n2 <= 16 ? 16 : stride_mod(a.n2, 32, 16);
-  a.sx = stride_mod(a.n2, 32, 2);
-  a.st = stride_mod(a.n2, 16, 8);
-  auto need = [&](int R) {
-    const int p2 = (a.n1 * a.sp1 * 4 + 15) / 16 * 16;
-    const int pt = (p2 + a.n2 * a.sp2 * 4 + 15) / 16 * 16;
-    return pt + x_bytes_for(R, a.n1, a.sx, a.K) + R * a.n1 * a.st * 8;
+  const int njt = (a.n2 + 15) / 16;
+  int R = 8 / njt;
+  if (R < 1) return false;  // n2 > 128 is rejected earlier
+  if (R > 16) R = 16;
+  auto lds_for = [&](int sp1, int sp2, int sx, int r) {
+    const int p2 = (a.n1 * sp1 * 4 + 15) / 16 * 16;
+    const int px = (p2 + a.n2 * sp2 * 4 + 15) / 16 * 16;
+    return px + x_bytes_for(r, a.n1, sx, a.K);
   };
-  if (need(1) > budget) {  // drop the bank padding
-    a.sp1 = a.n1;
-    a.sp2 = a.n2;
-    a.sx = a.n2;
-    a.st = a.n2;
+  int sp1 = a.n1 <= 16 ? 16 : stride_mod(a.n1, 32, 16);
+  int sp2 = a.n2 <= 16 ? 16 : stride_mod(a.n2, 32, 16);
+  int sx = stride_mod(a.n2, 32, 2);
+  if (lds_for(sp1, sp2, sx, R) > 80 * 1024 && lds_for(a.n1, a.n2, sx, R) <= 80 * 1024) {
+    sp1 = a.n1;
+    sp2 = a.n2;
   }
-  if (need(1) > budget) return false;
-  int R = 1;
-  while (R < 16 && need(R + 1) <= 80 * 1024) ++R;
+  while (R > 1 && lds_for(sp1, sp2, sx, R) > budget) --R;
+  if (lds_for(sp1, sp2, sx, R) > budget) {
+    sp1 = a.n1;
+    sp2 = a.n2;
+    sx = a.n2;
+  }
+  if (lds_for(sp1, sp2, sx, R) > budget) return false;
+  a.sp1 = sp1;
+  a.sp2 = sp2;
+  a.sx = sx;
+  a.st = 0;
   a.R = R;
-  a.off_p2 = (a.n1 * a.sp1 * 4 + 15) / 16 * 16;
-  a.off_x = (a.off_p2 + a.n2 * a.sp2 * 4 + 15) / 16 * 16;
-  a.off_t = a.off_x + x_bytes_for(R, a.n1, a.sx, a.K);
-  a.lds_bytes = a.off_t + R * a.n1 * a.st * 8;
+  a.off_p2 = (a.n1 * sp1 * 4 + 15) / 16 * 16;
+  a.off_x = (a.off_p2 + a.n2 * sp2 * 4 + 15) / 16 * 16;
+  a.off_t = 0;
+  a.lds_bytes = a.off_x + x_bytes_for(R, a.n1, sx, a.K);
   return true;
 }
 
@@ -314,8 +402,33 @@ hipError_t launch_quant_act(QuantArgs a, hipStream_t s) {
     return hipGetLastError();
   }
   if (!plan_quant(a)) return hipErrorInvalidConfiguration;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(quant_xform_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);
+  const void* fn = nullptr;
+#define LOOPQ_SHAPE(n1_, n2_)                                                          \
+  if (a.n1 == n1_ && a.n2 == n2_)                                                     \
+    fn = reinterpret_cast<const void*>(quant_xform_kernel<(n1_ + 15) / 16, n1_, n2_>);
+  // factor shapes of the Kronecker transforms in use (K = 256, 2048, 5632,
+  // 2560, 6912, and a 32-wide test shape)
+  LOOPQ_SHAPE(16, 16)
+  LOOPQ_SHAPE(32, 64)
+  LOOPQ_SHAPE(64, 88)
+  LOOPQ_SHAPE(40, 64)
+  LOOPQ_SHAPE(64, 108)
+  LOOPQ_SHAPE(4, 8)
+#undef LOOPQ_SHAPE
+  if (fn == nullptr) {
+    switch ((a.n1 + 15) / 16) {
+      case 1: fn = reinterpret_cast<const void*>(quant_xform_kernel<1, 0, 0>); break;
+      case 2: fn = reinterpret_cast<const void*>(quant_xform_kernel<2, 0, 0>); break;
+      case 3: fn = reinterpret_cast<const void*>(quant_xform_kernel<3, 0, 0>); break;
+      case 4: fn = reinterpret_cast<const void*>(quant_xform_kernel<4, 0, 0>); break;
+      case 5: fn = reinterpret_cast<const void*>(quant_xform_kernel<5, 0, 0>); break;
+      case 6: fn = reinterpret_cast<const void*>(quant_xform_kernel<6, 0, 0>); break;
+      case 7: fn = reinterpret_cast<const void*>(quant_xform_kernel<7, 0, 0>); break;
+      case 8: fn = reinterpret_cast<const void*>(quant_xform_kernel<8, 0, 0>); break;
+      default: return hipErrorInvalidConfiguration;
+    }
+  }
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);
   if (e != hipSuccess) return e;
   const int nchunks = (a.rows + a.R - 1) / a.R;
   int dev = 0, ncu = 256;
@@ -325,7 +438,9 @@ hipError_t launch_quant_act(QuantArgs a, hipStream_t s) {
   const int per_cu = a.lds_bytes <= 80 * 1024 ? 2 : 1;
   int blocks = ncu * per_cu;
   if (blocks > nchunks) blocks = nchunks;
-  hipLaunchKernelGGL(quant_xform_kernel, dim3(blocks), dim3(256), a.lds_bytes, s, a);
+  void* args[] = {&a};
+  e = hipLaunchKernel(fn, dim3(blocks), dim3(256), args, a.lds_bytes, s);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

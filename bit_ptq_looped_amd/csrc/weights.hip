@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ w, 
   const float sdiv = __half2float(s16);
   if (__builtin_isinf(sdiv)) atomicOr(&g_loopq_status, 1);
   const int nb = n >> 5, c = n & 31;
-  scales[((int64_t)nb * Gw + jw) * 32 + c] = s16;
+  scales[((int64_t)nb * Gw + jw) * 32 + step_slot(c)] = s16;
 
   const int Kc = K >> 5;
   for (int kc = k0 >> 5; kc < (k1 >> 5); ++kc) {
@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256) void export_kernel(const uint8_t* __restrict__
     }
   if ((kc * 32) % gw == 0) {
     const int jw = kc * 32 / gw;
-    out_scales[(int64_t)n * Gw + jw] = __half_as_ushort(scales[((int64_t)nb * Gw + jw) * 32 + c]);
+    out_scales[(int64_t)n * Gw + jw] =
+        __half_as_ushort(scales[((int64_t)nb * Gw + jw) * 32 + step_slot(c)]);
   }
 }
 
