@@ -27,6 +27,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 
 struct GemmArgs {
   const int8_t* a;   // tiled codes
@@ -55,8 +56,8 @@ __device__ __forceinline__ v4i unpack_w(uint2 p) {
 struct Stage {
   uint2 w[2];        // packed nibbles: MFMA operand A, the wave's two 32-column tiles
   v4i x[2];          // activation codes: MFMA operand B, the wave's two 32-row tiles
-  float sa[2];       // activation step of the lane's row, per row tile
-  uint4 sw[2][2];    // the lane's 16 fp16 weight steps per column tile
+  float sa[2];       // activation steps of row l % 32 of row tiles h and 1 - h
+  uint32_t sw;       // raw fp16 weight step of column l % 32 of column tile h
 };
 
 // The wave computes 32x32 tiles of y^T: result element e of lane l belongs to
@@ -82,29 +83,31 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   // bounds); their results are dropped at the store.
   const int8_t* x_ptr[2];
   const uint8_t* w_ptr[2];
-  const float* sa_ptr[2];
-  const uint4* sw_ptr[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int mb = min((m_base >> 5) + t, mlast);
     const int nb = min((n_base >> 5) + t, nlast);
     x_ptr[t] = g.a + (int64_t)mb * Ga * 1024 + lane * 16;
     w_ptr[t] = g.w + (int64_t)nb * Ga * kBlockBytes + lane * 8;
-    sa_ptr[t] = g.sa + mb * 32 + c;
-    sw_ptr[t] = reinterpret_cast<const uint4*>(g.sw) + (int64_t)nb * Gw * 4 + 2 * h;
   }
+  // steps feeding the outer-product MFMAs: lane l supplies the weight step of
+  // column l % 32 of column tile h, and the activation steps of row l % 32 of
+  // row tiles h and 1 - h
+  const float* sa_ptr0 = g.sa + min((m_base >> 5) + h, mlast) * 32 + c;
+  const float* sa_ptr1 = g.sa + min((m_base >> 5) + 1 - h, mlast) * 32 + c;
+  const unsigned short* sw_ptr = reinterpret_cast<const unsigned short*>(g.sw) +
+                                 (int64_t)min((n_base >> 5) + h, nlast) * Gw * 32 + step_slot(c);
 
   auto load = [&](int j, Stage& s) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s.x[t] = *reinterpret_cast<const v4i*>(x_ptr[t] + (int64_t)j * 1024);
       s.w[t] = *reinterpret_cast<const uint2*>(w_ptr[t] + (int64_t)j * kBlockBytes);
-      if (MODE == 0) {
-        s.sa[t] = sa_ptr[t][(int64_t)j * g.ld_sa];
-        const uint4* p = sw_ptr[t] + (int64_t)(j >> g.gshift) * 4;
-        s.sw[t][0] = p[0];
-        s.sw[t][1] = p[1];
-      }
+    }
+    if (MODE == 0) {
+      s.sa[0] = sa_ptr0[(int64_t)j * g.ld_sa];
+      s.sa[1] = sa_ptr1[(int64_t)j * g.ld_sa];
+      s.sw = sw_ptr[(int64_t)(j >> g.gshift) * 32];
     }
   };
 
@@ -116,41 +119,53 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[t][u][e] = 0.0f;
 
-  auto compute = [&](const Stage& s, int j) {
+  auto mfma = [&](const Stage& s, const v4i& wu, int t) {
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(wu, s.x[t], zero, 0, 0, 0);
+  };
+  // fold one 32x32 result tile: convert the int32 group dots, FMA with the
+  // step-product tile
+  auto fold = [&](const v16i& d, const v32f& cf, int half, int t, int u, int j) {
+    if (MODE == 0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const v4i wu = unpack_w(s.w[u]);
-      const uint32_t swr[8] = {s.sw[u][0].x, s.sw[u][0].y, s.sw[u][0].z, s.sw[u][0].w,
-                               s.sw[u][1].x, s.sw[u][1].y, s.sw[u][1].z, s.sw[u][1].w};
+      for (int e = 0; e < 16; ++e)
+        acc[t][u][e] = __builtin_fmaf((float)d[e], cf[16 * half + e], acc[t][u][e]);
+    } else {
+      const int row = m_base + 32 * t + c;
+      if (row < g.M) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(wu, s.x[t], zero, 0, 0, 0);
-        if (MODE == 0) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const uint32_t pair = swr[e >> 1];
-            const __half hw = __ushort_as_half((unsigned short)((e & 1) ? (pair >> 16) : (pair & 0xffffu)));
-            const float coef = __builtin_fmaf(__half2float(hw), s.sa[t], 0.0f);
-            acc[t][u][e] = __builtin_fmaf((float)d[e], coef, acc[t][u][e]);
-          }
-        } else {
-          const int row = m_base + 32 * t + c;
-          if (row < g.M) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int col = n_base + 32 * u + 8 * (e >> 2) + 4 * h + (e & 3);
-              if (col < g.N) g.dots[((int64_t)row * g.N + col) * Ga + j] = d[e];
-            }
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int col = n_base + 32 * u + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (col < g.N) g.dots[((int64_t)row * g.N + col) * Ga + j] = d[e];
         }
       }
     }
   };
+  // Step products s_w[n] * s_a[m] of the four result tiles come from two
+  // V_MFMA_F32_32X32X1_2B_F32 outer products (block b from lanes 32b..32b+31,
+  // same element layout as the GEMM tiles): cA = (t0,u0) | (t1,u1),
+  // cB = (t1,u0) | (t0,u1).  The MFMA of the next tile is issued before the
+  // current tile is folded.
+  auto compute = [&](const Stage& s, int j) {
+    v32f cA = {}, cB = {};
+    if (MODE == 0) {
+      const v32f z = {};
+      const float swf = __half2float(__ushort_as_half((unsigned short)s.sw));
+      cA = __builtin_amdgcn_mfma_f32_32x32x1f32(swf, s.sa[0], z, 0, 0, 0);
+      cB = __builtin_amdgcn_mfma_f32_32x32x1f32(swf, s.sa[1], z, 0, 0, 0);
+    }
+    const v4i w0 = unpack_w(s.w[0]);
+    const v4i w1 = unpack_w(s.w[1]);
+    const v16i d00 = mfma(s, w0, 0);
+    const v16i d01 = mfma(s, w1, 0);
+    fold(d00, cA, 0, 0, 0, j);
+    const v16i d10 = mfma(s, w0, 1);
+    fold(d01, cB, 1, 0, 1, j);
+    const v16i d11 = mfma(s, w1, 1);
+    fold(d10, cB, 0, 1, 0, j);
+    fold(d11, cA, 1, 1, 1, j);
+  };
 
-  // Two stages, two groups in flight: a stage is reloaded only after its
-  // group has been folded (the scheduling barriers keep the compiler from
-  // hoisting the reload above the fold, which would need register copies).
   // Loads past the last group re-read it (in bounds, unused), so the loop
   // body is one basic block the barriers can order.
   Stage s0, s1;
@@ -161,9 +176,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     compute(s0, j);
     __builtin_amdgcn_sched_barrier(0);
     load(min(j + 2, Ga - 1), s0);
+    __builtin_amdgcn_sched_barrier(0);
     compute(s1, j + 1);
     __builtin_amdgcn_sched_barrier(0);
     load(min(j + 3, Ga - 1), s1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (j < Ga) compute(s0, j);
 
@@ -193,18 +210,28 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 
 __global__ __launch_bounds__(256) void tile_codes_kernel(const int8_t* __restrict__ canon,
                                                          const float* __restrict__ canon_scales,
-                                                         int M, int K, int8_t* __restrict__ tiled,
-                                                         float* __restrict__ gm_scales, int ld) {
+                                                         int M, int K, void* __restrict__ tiled,
+                                                         int fmt, float* __restrict__ gm_scales,
+                                                         int ld) {
   const int Ga = K >> 5;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 4-byte run
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 4-code run
   const int64_t runs = (int64_t)M * (K >> 2);
   if (idx >= runs) return;
   const int row = (int)(idx / (K >> 2));
   const int k0 = (int)(idx - (int64_t)row * (K >> 2)) * 4;
   const uint32_t v = *reinterpret_cast<const uint32_t*>(canon + (int64_t)row * K + k0);
   const int j = k0 >> 5, kk = k0 & 31;
-  *reinterpret_cast<uint32_t*>(tiled + ((int64_t)(row >> 5) * Ga + j) * 1024 + (kk >> 4) * 512 +
-                               (row & 31) * 16 + (kk & 15)) = v;
+  if (fmt == kCodesTiledBf16) {
+    uint32_t b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = __float_as_uint((float)(int8_t)(v >> (8 * i))) >> 16;
+    char* base = reinterpret_cast<char*>(tiled);
+    *reinterpret_cast<uint2*>(base + ((int64_t)(row >> 5) * Ga + j) * 2048 + (kk >> 4) * 1024 +
+                              (row & 31) * 32 + (kk & 15) * 2) = uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+  } else {
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(tiled) + ((int64_t)(row >> 5) * Ga + j) * 1024 +
+                                 (kk >> 4) * 512 + (row & 31) * 16 + (kk & 15)) = v;
+  }
   if (kk == 0 && gm_scales) gm_scales[(int64_t)j * ld + row] = canon_scales[(int64_t)row * Ga + j];
 }
 
@@ -235,11 +262,11 @@ hipError_t launch_gemm(const int8_t* a_tiled, const float* a_scales_gm, int ld_s
 }
 
 hipError_t launch_tile_codes(const int8_t* canon_codes, const float* canon_scales, int M, int K,
-                             int8_t* tiled_codes, float* gm_scales, int ld, hipStream_t s) {
+                             void* tiled_codes, int fmt, float* gm_scales, int ld, hipStream_t s) {
   const int64_t runs = (int64_t)M * (K / 4);
   if (runs == 0) return hipSuccess;
   hipLaunchKernelGGL(tile_codes_kernel, dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, s,
-                     canon_codes, canon_scales, M, K, tiled_codes, gm_scales, ld);
+                     canon_codes, canon_scales, M, K, tiled_codes, fmt, gm_scales, ld);
   return hipGetLastError();
 }
 

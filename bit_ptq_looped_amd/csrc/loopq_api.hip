@@ -1,6 +1,7 @@
 // C ABI of libloopq (declared in include/loopq.h): host-side validation,
 // workspace planning and kernel dispatch on the caller's stream.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -74,25 +75,113 @@ void recycle_locked() {
   g_timing_recs.clear();
 }
 
-// internal activation buffers for `rows` quantized rows of width K
+// Which GEMM the hot path uses: the INT8 kernel (default) or the bf16-operand
+// kernel (LOOPQ_GEMM=bf16, kept for comparison; same results).
+bool use_bf16_gemm() {
+  static const bool v = [] {
+    const char* e = getenv("LOOPQ_GEMM");
+    return e != nullptr && strcmp(e, "bf16") == 0;
+  }();
+  return v;
+}
+
+// Internal buffers of the quantize -> GEMM path, carved from the caller's
+// workspace for `chunks` chunks of `rows` rows each:
+//   codes  : chunks * padded(rows) rows in the tiled layout (2 bytes/code
+//            reserved so either GEMM's format fits)
+//   scales : fp32 group-major, chunks * padded(rows) columns
+//   wexp   : weights expanded to bf16 operands (bf16 GEMM only)
+// The same region also holds all chunks * rows rows as one contiguous tiled
+// matrix (padded(chunks * rows) <= chunks * padded(rows)).
 struct ActBuffers {
-  int8_t* codes;
+  void* codes;
   float* scales;
+  uint16_t* wexp;
   int ld;
 };
 
-size_t act_bytes(int64_t rows, int64_t K) {
-  const int64_t mp = padded_rows(rows);
-  return align256((size_t)(mp * K)) + align256((size_t)((K / 32) * mp * 4));
+size_t codes_region(int64_t chunks, int64_t rows, int64_t K) {
+  return align256((size_t)(chunks * padded_rows(rows) * K * 2));
+}
+size_t scales_region(int64_t chunks, int64_t rows, int64_t K) {
+  return align256((size_t)((K / 32) * chunks * padded_rows(rows) * 4));
+}
+size_t act_bytes(int64_t chunks, int64_t rows, int64_t K, int64_t N) {
+  size_t b = codes_region(chunks, rows, K) + scales_region(chunks, rows, K);
+  if (use_bf16_gemm()) b += align256((size_t)(padded_cols(N) * K * 2));
+  return b;
 }
 
-ActBuffers carve(void* ws, int64_t rows, int64_t K) {
+// buffers of chunk c (rows rows each), or with all_rows > 0 the whole
+// all_rows-row matrix starting at the region's base
+ActBuffers carve(void* ws, int64_t chunks, int64_t rows, int64_t K, int64_t c, int64_t all_rows) {
   ActBuffers b;
+  char* base = reinterpret_cast<char*>(ws);
   const int64_t mp = padded_rows(rows);
-  b.codes = reinterpret_cast<int8_t*>(ws);
-  b.scales = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)(mp * K)));
-  b.ld = (int)mp;
+  float* scales0 = reinterpret_cast<float*>(base + codes_region(chunks, rows, K));
+  b.wexp = reinterpret_cast<uint16_t*>(base + codes_region(chunks, rows, K) +
+                                       scales_region(chunks, rows, K));
+  if (all_rows > 0) {
+    b.codes = base;
+    b.scales = scales0;
+    b.ld = (int)padded_rows(all_rows);
+  } else {
+    b.codes = base + (size_t)c * mp * K * 2;
+    b.scales = scales0 + (size_t)c * (K / 32) * mp;
+    b.ld = (int)mp;
+  }
   return b;
+}
+
+// GEMM stage on codes already in the internal layout of the selected kernel
+hipError_t run_gemm(const ActBuffers& b, int rows, int K, int N, const void* w_codes,
+                    const void* w_scales, int gw, float* y, int32_t* dots, int mode,
+                    hipStream_t s) {
+  const uint8_t* wc = reinterpret_cast<const uint8_t*>(w_codes);
+  const __half* wsc = reinterpret_cast<const __half*>(w_scales);
+  if (!use_bf16_gemm())
+    return launch_gemm(reinterpret_cast<const int8_t*>(b.codes), b.scales, b.ld, rows, K, N, wc,
+                       wsc, gw, y, dots, mode, s);
+  hipError_t e = launch_expand_weights_bf16(wc, K, N, b.wexp, s);
+  if (e != hipSuccess) return e;
+  return launch_gemm_bf16(reinterpret_cast<const uint16_t*>(b.codes), b.scales, b.ld, rows, K, N,
+                          b.wexp, wsc, gw, y, dots, mode, s);
+}
+
+int code_format() { return use_bf16_gemm() ? kCodesTiledBf16 : kCodesTiledI8; }
+
+// ---------------------------------------------------------------------------
+// Auxiliary stream (one per device, default priority) and events for the
+// pipelined loop-sequential schedule: the quantizer of loop t + 1 runs on the
+// auxiliary stream while the GEMM of loop t runs on the caller's stream.
+// Enqueueing is serialized by a mutex; the caller's stream waits for every
+// auxiliary launch it depends on, so stream order is preserved for the caller.
+// ---------------------------------------------------------------------------
+std::mutex g_pipe_mu;
+struct DevicePipe {
+  hipStream_t aux = nullptr;
+  std::vector<hipEvent_t> events;
+};
+DevicePipe g_pipes[64];
+
+hipError_t device_pipe(DevicePipe** out, int nevents) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  DevicePipe& p = g_pipes[dev];
+  if (!p.aux) {
+    e = hipStreamCreateWithFlags(&p.aux, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+  }
+  while ((int)p.events.size() < nevents) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    p.events.push_back(ev);
+  }
+  *out = &p;
+  return hipSuccess;
 }
 
 int32_t check_weights(int K, int N, int gw) {
@@ -142,20 +231,29 @@ QuantArgs make_quant_args(const void* x, int dtype, int rows, int K, const float
   return a;
 }
 
-// quantize `rows` rows into the internal layout, then run the GEMM
-int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const float* P1, int n1,
-                    const float* P2, int n2, const ClipTable& clips, int rows_per_clip, int bits_a,
-                    const void* w_codes, const void* w_scales, int gw, float* y, void* ws,
-                    hipStream_t s) {
-  ActBuffers b = carve(ws, rows, K);
+QuantArgs internal_quant_args(const void* x, int dtype, int rows, int K, const float* P1, int n1,
+                              const float* P2, int n2, const ClipTable& clips, int rows_per_clip,
+                              int bits_a, const ActBuffers& b) {
   QuantArgs a = make_quant_args(x, dtype, rows, K, P1, n1, P2, n2, bits_a);
   a.clips = clips;
   a.rows_per_clip = rows_per_clip;
-  a.codes = b.codes;
-  a.codes_tiled = 1;
+  a.codes = reinterpret_cast<int8_t*>(b.codes);
+  a.codes_fmt = code_format();
   a.scales = b.scales;
   a.scales_gm = 1;
   a.scales_ld = b.ld;
+  return a;
+}
+
+// weight-stationary: quantize all `rows` rows, then one GEMM pass over the
+// weights for all of them
+int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const float* P1, int n1,
+                    const float* P2, int n2, const ClipTable& clips, int rows_per_clip, int bits_a,
+                    const void* w_codes, const void* w_scales, int gw, float* y, void* ws,
+                    int64_t ws_chunks, int64_t ws_rows, hipStream_t s) {
+  ActBuffers b = carve(ws, ws_chunks, ws_rows, K, 0, rows);
+  QuantArgs a = internal_quant_args(x, dtype, rows, K, P1, n1, P2, n2, clips, rows_per_clip,
+                                    bits_a, b);
   hipError_t e;
   {
     TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, s);
@@ -164,10 +262,51 @@ int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const floa
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   {
     TimingScope ts(LOOPQ_KERNEL_GEMM, s);
-    e = launch_gemm(b.codes, b.scales, b.ld, rows, K, N, reinterpret_cast<const uint8_t*>(w_codes),
-                    reinterpret_cast<const __half*>(w_scales), gw, y, nullptr, 0, s);
+    e = run_gemm(b, rows, K, N, w_codes, w_scales, gw, y, nullptr, 0, s);
   }
   return hip_status(e);
+}
+
+// loop-sequential, pipelined: loop t's rows are quantized on the auxiliary
+// stream and multiplied on the caller's stream as soon as they are ready, so
+// the quantizer of loop t + 1 overlaps the GEMM of loop t
+int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, const float* P1,
+                         int n1, const float* P2, int n2, const ClipTable& clips, int bits_a,
+                         const void* w_codes, const void* w_scales, int gw, float* y, void* ws,
+                         hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_pipe_mu);
+  DevicePipe* p = nullptr;
+  if (device_pipe(&p, T + 1) != hipSuccess) return LOOPQ_ERR_HIP;
+  const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
+  hipEvent_t start = p->events[T];
+  if (hipEventRecord(start, s) != hipSuccess) return LOOPQ_ERR_HIP;
+  if (hipStreamWaitEvent(p->aux, start, 0) != hipSuccess) return LOOPQ_ERR_HIP;
+  for (int t = 0; t < T; ++t) {
+    ClipTable one;
+    memset(&one, 0, sizeof(one));
+    one.c[0] = clips.c[t];
+    ActBuffers b = carve(ws, T, M, K, t, 0);
+    const void* xt = reinterpret_cast<const char*>(x) + (size_t)t * M * K * esz;
+    QuantArgs a = internal_quant_args(xt, dtype, M, K, P1, n1, P2, n2, one, M, bits_a, b);
+    hipError_t e;
+    {
+      TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, p->aux);
+      e = launch_quant_act(a, p->aux);
+    }
+    if (e != hipSuccess) return LOOPQ_ERR_HIP;
+    if (hipEventRecord(p->events[t], p->aux) != hipSuccess) return LOOPQ_ERR_HIP;
+  }
+  for (int t = 0; t < T; ++t) {
+    if (hipStreamWaitEvent(s, p->events[t], 0) != hipSuccess) return LOOPQ_ERR_HIP;
+    ActBuffers b = carve(ws, T, M, K, t, 0);
+    hipError_t e;
+    {
+      TimingScope ts(LOOPQ_KERNEL_GEMM, s);
+      e = run_gemm(b, M, K, N, w_codes, w_scales, gw, y + (size_t)t * M * N, nullptr, 0, s);
+    }
+    if (e != hipSuccess) return LOOPQ_ERR_HIP;
+  }
+  return LOOPQ_OK;
 }
 
 }  // namespace
@@ -207,12 +346,14 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
   switch (op) {
     case LOOPQ_OP_LINEAR:
       if (M < 0 || K <= 0 || K % 32) return M < 0 || K <= 0 ? LOOPQ_ERR_INVALID_ARG : LOOPQ_ERR_UNSUPPORTED;
-      *bytes = act_bytes(M, K);
+      if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
+      *bytes = act_bytes(1, M, K, N);
       return LOOPQ_OK;
     case LOOPQ_OP_LOOPED_FORWARD:
       if (T <= 0 || M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (T > LOOPQ_MAX_LOOPS || K % 32) return LOOPQ_ERR_UNSUPPORTED;
-      *bytes = act_bytes((int64_t)T * M, K);
+      if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
+      *bytes = act_bytes(T, M, K, N);
       return LOOPQ_OK;
     case LOOPQ_OP_FOLD:
       if (M <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
@@ -314,21 +455,11 @@ int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
-  const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
-  if (schedule == LOOPQ_SCHED_LOOP_SEQUENTIAL) {
-    for (int t = 0; t < T; ++t) {
-      ClipTable one;
-      memset(&one, 0, sizeof(one));
-      one.c[0] = clips.c[t];
-      const void* xt = reinterpret_cast<const char*>(x) + (size_t)t * M * K * esz;
-      st = linear_core(xt, dtype, M, K, N, P1, n1, P2, n2, one, M, bits_a, w_codes, w_scales,
-                       group_w, y + (size_t)t * M * N, workspace, s);
-      if (st != LOOPQ_OK) return st;
-    }
-    return LOOPQ_OK;
-  }
+  if (schedule == LOOPQ_SCHED_LOOP_SEQUENTIAL && T > 1)
+    return looped_pipelined(x, dtype, T, M, K, N, P1, n1, P2, n2, clips, bits_a, w_codes, w_scales,
+                            group_w, y, workspace, s);
   return linear_core(x, dtype, T * M, K, N, P1, n1, P2, n2, clips, M, bits_a, w_codes, w_scales,
-                     group_w, y, workspace, s);
+                     group_w, y, workspace, T, M, s);
 }
 
 int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,
@@ -352,15 +483,13 @@ int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M
   if (!aligned(a_codes, 4) || !aligned(a_scales, 4) || !aligned(w_codes, 16) ||
       !aligned(w_scales, 16) || !aligned(y, 4))
     return LOOPQ_ERR_ALIGNMENT;
-  const size_t need = act_bytes(M, K);
+  const size_t need = act_bytes(1, M, K, N);
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
-  ActBuffers b = carve(workspace, M, K);
-  hipError_t e = launch_tile_codes(a_codes, a_scales, M, K, b.codes, b.scales, b.ld, s);
-  if (e == hipSuccess)
-    e = launch_gemm(b.codes, b.scales, b.ld, M, K, N, reinterpret_cast<const uint8_t*>(w_codes),
-                    reinterpret_cast<const __half*>(w_scales), group_w, y, nullptr, 0, s);
+  ActBuffers b = carve(workspace, 1, M, K, 0, M);
+  hipError_t e = launch_tile_codes(a_codes, a_scales, M, K, b.codes, code_format(), b.scales, b.ld, s);
+  if (e == hipSuccess) e = run_gemm(b, M, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s);
   return hip_status(e);
 }
 
@@ -385,15 +514,13 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
   if (!a_codes || !w_codes || !dots) return LOOPQ_ERR_INVALID_ARG;
   if (!aligned(a_codes, 4) || !aligned(w_codes, 16) || !aligned(dots, 4))
     return LOOPQ_ERR_ALIGNMENT;
-  const size_t need = act_bytes(M, K);
+  const size_t need = act_bytes(1, M, K, N);
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
-  ActBuffers b = carve(workspace, M, K);
-  hipError_t e = launch_tile_codes(a_codes, nullptr, M, K, b.codes, nullptr, b.ld, s);
-  if (e == hipSuccess)
-    e = launch_gemm(b.codes, nullptr, b.ld, M, K, N, reinterpret_cast<const uint8_t*>(w_codes),
-                    nullptr, 32, nullptr, dots, 1, s);
+  ActBuffers b = carve(workspace, 1, M, K, 0, M);
+  hipError_t e = launch_tile_codes(a_codes, nullptr, M, K, b.codes, code_format(), nullptr, b.ld, s);
+  if (e == hipSuccess) e = run_gemm(b, M, K, N, w_codes, nullptr, 32, nullptr, dots, 1, s);
   return hip_status(e);
 }
 

@@ -44,7 +44,15 @@ inline int64_t weight_groups(int64_t K, int64_t gw) { return (K + gw - 1) / gw; 
 // loads 16 contiguous bytes = the A operand of V_MFMA_I32_32X32X32_I8 for
 // row l % 32, K-half l / 32.
 // Steps: fp32 group-major [K/32][ld] with ld >= padded rows.
+//
+// bf16 variant (operands of V_MFMA_F32_32X32X16_BF16): the same blocks at
+// 2048 bytes each; row r, K-half h and element i (0..15) sit at
+// h * 1024 + r * 32 + 2 i, so lane l loads 32 contiguous bytes (row l % 32,
+// K-half l / 32) and feeds elements 0..7 and 8..15 to two MFMAs.  Codes are
+// small integers, exact in bf16.  Expanded weights use the identical layout
+// with output columns in place of rows.
 // ---------------------------------------------------------------------------
+enum CodeFormat { kCodesCanonical = 0, kCodesTiledI8 = 1, kCodesTiledBf16 = 2 };
 inline int64_t padded_rows(int64_t M) { return (M + 31) / 32 * 32; }
 
 struct ClipTable {
@@ -62,8 +70,8 @@ struct QuantArgs {
   int rows_per_clip; // row r uses clips.c[r / rows_per_clip]
   ClipTable clips;
   int qmax;
-  int8_t* codes;     // canonical [rows][K] or the tiled GEMM layout
-  int codes_tiled;
+  int8_t* codes;     // canonical [rows][K] or a tiled GEMM layout
+  int codes_fmt;     // CodeFormat
   float* scales;     // row-major [rows][K/32] or group-major [K/32][scales_ld]
   int scales_gm;
   int scales_ld;
@@ -88,7 +96,17 @@ hipError_t launch_fold(const float* w, int K, int N, const float* P1, int n1, co
                        int n2, float* out, void* ws, hipStream_t s);
 
 hipError_t launch_tile_codes(const int8_t* canon_codes, const float* canon_scales, int M, int K,
-                             int8_t* tiled_codes, float* gm_scales, int ld, hipStream_t s);
+                             void* tiled_codes, int fmt, float* gm_scales, int ld, hipStream_t s);
+
+// packed nibbles -> bf16 weight operands in the tiled bf16 layout
+hipError_t launch_expand_weights_bf16(const uint8_t* w_codes, int K, int N, uint16_t* out,
+                                      hipStream_t s);
+
+// bf16-operand GEMM (codes and expanded weights in the bf16 tiled layout);
+// same modes as launch_gemm
+hipError_t launch_gemm_bf16(const uint16_t* a_tiled, const float* a_scales_gm, int ld_sa, int M,
+                            int K, int N, const uint16_t* w_bf16, const __half* w_scales, int gw,
+                            float* y, int32_t* dots, int mode, hipStream_t s);
 
 // GEMM over the internal activation layout.  mode 0: y = rescaled sum;
 // mode 1: write int32 per-group dots [M][N][K/32].

@@ -33,25 +33,58 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// bf16 bit pattern of a small integer code (exact)
+__device__ __forceinline__ uint32_t bf16_of_code(int8_t q) {
+  return __float_as_uint((float)q) >> 16;
+}
+
+// max over the 8 consecutive lanes of a group: quad swaps 1 and 2, then the
+// half-row mirror pairs each lane with one of the other quad (DPP, no LDS)
+__device__ __forceinline__ float group8_max(float v) {
+  int b = __float_as_int(v);
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x141, 0xF, 0xF, false))));
+  return __int_as_float(b);
+}
+
 // Quantize 4 consecutive elements of one 32-group whose 8 lanes are
 // consecutive in the wave (lane % 8 = position of the 4-element run).
 // Returns the 4 codes packed as int8 bytes; writes the step to *step.
+//
+// Codes are clamp(rint(fl32(x / s)), -qmax, qmax).  The quotient is formed as
+// p = fl32(x * r) with r = fl32(1 / s) (both correctly rounded): |p - x/s| and
+// |fl32(x/s) - x/s| are each below 2^-23 |x/s|, so below the clamp (|x/s| <
+// qmax + 1 <= 128) p and fl32(x/s) differ by less than 2^-15, and rint gives
+// the same integer unless p lies within 2^-14 of a half-integer.  Those runs,
+// and any run whose r is not finite (s below 2^-128), are redone with the
+// correctly rounded division.  Above the clamp both sides saturate alike.
 __device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf, float* step) {
   float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+  amax = group8_max(amax);
   const float base = amax / qmaxf;  // correctly rounded fp32 division
   const float s = clip * base;      // one fp32 product
   *step = s;
+  if (!(s > 0.0f)) return 0u;
+  const float r = 1.0f / s;         // correctly rounded
+  const float e[4] = {v.x, v.y, v.z, v.w};
   uint32_t packed = 0u;
-  if (s > 0.0f) {
-    float e[4] = {v.x, v.y, v.z, v.w};
+  bool exact = !(r < 3.0e38f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = e[i] * r;
+    const float rq = __builtin_rintf(p);
+    exact |= (fabsf(p) < qmaxf + 1.0f) && (fabsf(p - rq) > 0.5f - 6.103515625e-05f);
+    const float q = fminf(fmaxf(rq, -qmaxf), qmaxf);
+    packed |= (uint32_t)((int)q & 0xff) << (8 * i);
+  }
+  if (exact) {  // rare: near a rounding boundary, or s tiny
+    packed = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float r = __builtin_rintf(e[i] / s);  // ties to even
-      r = fminf(fmaxf(r, -qmaxf), qmaxf);
-      packed |= (uint32_t)((int)r & 0xff) << (8 * i);
+      float q = __builtin_rintf(e[i] / s);  // ties to even
+      q = fminf(fmaxf(q, -qmaxf), qmaxf);
+      packed |= (uint32_t)((int)q & 0xff) << (8 * i);
     }
   }
   return packed;
@@ -64,7 +97,15 @@ __device__ __forceinline__ void store_run(const QuantArgs& a, int row, int k0, u
   const int K = a.K;
   const int Ga = K >> 5;
   const int j = k0 >> 5;
-  if (a.codes_tiled) {
+  if (a.codes_fmt == kCodesTiledBf16) {
+    // 4 codes -> 4 bf16 (exact: small integers)
+    const int kk = k0 & 31;
+    const int64_t off = ((int64_t)(row >> 5) * Ga + j) * 2048 + (kk >> 4) * 1024 + (row & 31) * 32 +
+                        (kk & 15) * 2;
+    uint32_t w01 = bf16_of_code((int8_t)(packed & 0xff)) | (bf16_of_code((int8_t)((packed >> 8) & 0xff)) << 16);
+    uint32_t w23 = bf16_of_code((int8_t)((packed >> 16) & 0xff)) | (bf16_of_code((int8_t)(packed >> 24)) << 16);
+    *reinterpret_cast<uint2*>(a.codes + off) = uint2{w01, w23};
+  } else if (a.codes_fmt == kCodesTiledI8) {
     const int kk = k0 & 31;
     const int64_t off = ((int64_t)(row >> 5) * Ga + j) * 1024 + (kk >> 4) * 512 + (row & 31) * 16 +
                         (kk & 15);
@@ -435,7 +476,10 @@ hipError_t launch_quant_act(QuantArgs a, hipStream_t s) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     ncu = 256;
-  const int per_cu = a.lds_bytes <= 80 * 1024 ? 2 : 1;
+  int per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, a.lds_bytes) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
   int blocks = ncu * per_cu;
   if (blocks > nchunks) blocks = nchunks;
   void* args[] = {&a};

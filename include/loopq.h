@@ -41,7 +41,10 @@
  *     synchronization.
  *   - Calls on different streams may run concurrently; they share no
  *     mutable library state except the status word of the synchronizing
- *     offline calls (pack, fold), which must not overlap on one device.
+ *     offline calls (pack, fold), which must not overlap on one device, and
+ *     the auxiliary stream of the pipelined loop-sequential schedule, whose
+ *     enqueueing is serialized (its work can then queue behind another
+ *     call's).
  *   - Matrices are row-major.  x is [M][K] (one token per row), weights are
  *     stored one output column per row, [N][K]; y is [M][N] fp32.
  */
@@ -159,7 +162,11 @@ int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, in
  * run 4 times per token); LAS, one clip per module and loop.
  * x [T][M][K], y [T][M][N]; clips_host [T] (host memory, read before return).
  * schedule: a loopq_schedule.  LOOP_SEQUENTIAL quantizes and multiplies loop
- * by loop; WEIGHT_STATIONARY quantizes all T*M rows, then streams the weights
+ * by loop, pipelined: the quantizer of loop t + 1 runs on an auxiliary stream
+ * the library keeps per device (default priority) while the GEMM of loop t
+ * runs on `stream`; `stream` waits for the auxiliary work through events, so
+ * the call keeps stream order for the caller (and can be captured into a HIP
+ * graph).  WEIGHT_STATIONARY quantizes all T*M rows, then streams the weights
  * once for all loops; AUTO picks WEIGHT_STATIONARY.  Both give bitwise equal y.
  * Workspace: loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, ...). */
 int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
