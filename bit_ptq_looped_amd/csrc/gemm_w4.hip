@@ -65,10 +65,17 @@ struct Stage {
 // + e % 4 of the weight tile.  One activation step per lane and tile; the
 // 16 weight steps of the lane are stored contiguously (see the step layout in
 // loopq_internal.h) and enter the rescale as fp16 operands of v_fma_mix.
+// raw buffer resource over [p, p + bytes): stride 0, gfx9 data format word;
+// loads at or past `bytes` return 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // the wave index is uniform; say so, so that tile bases live in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int c = lane & 31;
   const int m_base = blockIdx.y * 128 + (wave >> 1) * 64;
@@ -79,35 +86,41 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int mlast = ((g.M + 31) >> 5) - 1;
   const int nlast = ((g.N + 31) >> 5) - 1;
 
-  // Tiles past the matrix edge re-read the last valid block (always in
-  // bounds); their results are dropped at the store.
-  const int8_t* x_ptr[2];
-  const uint8_t* w_ptr[2];
+  // Every operand load is a buffer load: a wave-uniform resource (tile start,
+  // scalar registers), a per-lane byte offset fixed along K, and the group
+  // offset as the scalar offset, so the K loop does no vector address
+  // arithmetic.  Tiles past the matrix edge re-read the last valid block
+  // (always in bounds); their results are dropped at the store.
+  __amdgpu_buffer_rsrc_t x_rs[2], w_rs[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int mb = min((m_base >> 5) + t, mlast);
     const int nb = min((n_base >> 5) + t, nlast);
-    x_ptr[t] = g.a + (int64_t)mb * Ga * 1024 + lane * 16;
-    w_ptr[t] = g.w + (int64_t)nb * Ga * kBlockBytes + lane * 8;
+    x_rs[t] = make_rsrc(reinterpret_cast<const char*>(g.a) + (int64_t)mb * Ga * 1024, (uint32_t)Ga * 1024u);
+    w_rs[t] = make_rsrc(g.w + (int64_t)nb * Ga * kBlockBytes, (uint32_t)Ga * kBlockBytes);
   }
+  const int x_off = lane * 16;
+  const int w_off = lane * 8;
   // steps feeding the outer-product MFMAs: lane l supplies the weight step of
   // column l % 32 of column tile h, and the activation steps of row l % 32 of
   // row tiles h and 1 - h
-  const float* sa_ptr0 = g.sa + min((m_base >> 5) + h, mlast) * 32 + c;
-  const float* sa_ptr1 = g.sa + min((m_base >> 5) + 1 - h, mlast) * 32 + c;
-  const unsigned short* sw_ptr = reinterpret_cast<const unsigned short*>(g.sw) +
-                                 (int64_t)min((n_base >> 5) + h, nlast) * Gw * 32 + step_slot(c);
+  const __amdgpu_buffer_rsrc_t sa_rs = make_rsrc(g.sa, (uint32_t)g.ld_sa * (uint32_t)Ga * 4u);
+  const __amdgpu_buffer_rsrc_t sw_rs = make_rsrc(g.sw, (uint32_t)(nlast + 1) * (uint32_t)Gw * 64u);
+  const int sa_off0 = (min((m_base >> 5) + h, mlast) * 32 + c) * 4;
+  const int sa_off1 = (min((m_base >> 5) + 1 - h, mlast) * 32 + c) * 4;
+  const int sw_off = (min((n_base >> 5) + h, nlast) * Gw * 32 + step_slot(c)) * 2;
 
   auto load = [&](int j, Stage& s) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      s.x[t] = *reinterpret_cast<const v4i*>(x_ptr[t] + (int64_t)j * 1024);
-      s.w[t] = *reinterpret_cast<const uint2*>(w_ptr[t] + (int64_t)j * kBlockBytes);
+      s.x[t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(x_rs[t], x_off, j * 1024, 0));
+      s.w[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(w_rs[t], w_off, j * kBlockBytes, 0));
     }
     if (MODE == 0) {
-      s.sa[0] = sa_ptr0[(int64_t)j * g.ld_sa];
-      s.sa[1] = sa_ptr1[(int64_t)j * g.ld_sa];
-      s.sw = sw_ptr[(int64_t)(j >> g.gshift) * 32];
+      const int so = j * g.ld_sa * 4;
+      s.sa[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sa_rs, sa_off0, so, 0));
+      s.sa[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sa_rs, sa_off1, so, 0));
+      s.sw = __builtin_amdgcn_raw_buffer_load_b16(sw_rs, sw_off, (j >> g.gshift) * 64, 0);
     }
   };
 
@@ -119,17 +132,26 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[t][u][e] = 0.0f;
 
+  // In the rescale the integer MFMA starts from the bit pattern of
+  // kMagic = 1.5 * 2^23 instead of 0: for |d| < 2^22 the int32 result
+  // kMagicBits + d is the fp32 number kMagic + d exactly, so one exact fp32
+  // subtraction recovers d as a float (cheaper than an int-to-float convert).
+  // The dots-only form starts from 0.
+  constexpr int kMagicBits = 0x4B400000;
+  constexpr float kMagic = 12582912.0f;
+  const int cinit = MODE == 0 ? kMagicBits : 0;
+  const v16i c0 = {cinit, cinit, cinit, cinit, cinit, cinit, cinit, cinit,
+                   cinit, cinit, cinit, cinit, cinit, cinit, cinit, cinit};
   auto mfma = [&](const Stage& s, const v4i& wu, int t) {
-    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_i32_32x32x32_i8(wu, s.x[t], zero, 0, 0, 0);
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(wu, s.x[t], c0, 0, 0, 0);
   };
-  // fold one 32x32 result tile: convert the int32 group dots, FMA with the
-  // step-product tile
+  // fold one 32x32 result tile: recover the group dots as floats, FMA with
+  // the step-product tile
   auto fold = [&](const v16i& d, const v32f& cf, int half, int t, int u, int j) {
     if (MODE == 0) {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        acc[t][u][e] = __builtin_fmaf((float)d[e], cf[16 * half + e], acc[t][u][e]);
+        acc[t][u][e] = __builtin_fmaf(__int_as_float(d[e]) - kMagic, cf[16 * half + e], acc[t][u][e]);
     } else {
       const int row = m_base + 32 * t + c;
       if (row < g.M) {

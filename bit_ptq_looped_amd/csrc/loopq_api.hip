@@ -212,6 +212,16 @@ int32_t check_act(const void* x, int dtype, int M, int K, int bits_a) {
   return LOOPQ_OK;
 }
 
+// The GEMM addresses its operands with 32-bit buffer offsets: the step table
+// of the activations (rows x K/32 fp32) and of the weights must stay below 2 GiB.
+int32_t check_gemm_extent(int64_t rows, int K, int N, int gw) {
+  const int64_t ga = K / 32;
+  const int64_t gwn = (K + gw - 1) / gw;
+  if (rows * ga * 4 >= ((int64_t)1 << 31)) return LOOPQ_ERR_UNSUPPORTED;
+  if (padded_cols(N) * gwn * 2 >= ((int64_t)1 << 31)) return LOOPQ_ERR_UNSUPPORTED;
+  return LOOPQ_OK;
+}
+
 bool clip_ok(float c) { return isfinite(c) && c > 0.0f; }
 
 QuantArgs make_quant_args(const void* x, int dtype, int rows, int K, const float* P1, int n1,
@@ -434,9 +444,11 @@ int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
   if ((int64_t)T * M > (int64_t)1 << 30) return LOOPQ_ERR_UNSUPPORTED;
   int32_t st = check_act(x, dtype, M, K, bits_a);
   if (st != LOOPQ_OK) return st;
-  st = check_transform(K, P1, n1, P2, n2);
-  if (st != LOOPQ_OK) return st;
   st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  st = check_gemm_extent((int64_t)T * padded_rows(M), K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  st = check_transform(K, P1, n1, P2, n2);
   if (st != LOOPQ_OK) return st;
   if (!clips_host) return LOOPQ_ERR_INVALID_ARG;
   ClipTable clips;
@@ -479,6 +491,8 @@ int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M
   if (st != LOOPQ_OK) return st;
   if (M < 0) return LOOPQ_ERR_INVALID_ARG;
   if (M == 0) return LOOPQ_OK;
+  st = check_gemm_extent(padded_rows(M), K, N, group_w);
+  if (st != LOOPQ_OK) return st;
   if (!a_codes || !a_scales || !w_codes || !w_scales || !y) return LOOPQ_ERR_INVALID_ARG;
   if (!aligned(a_codes, 4) || !aligned(a_scales, 4) || !aligned(w_codes, 16) ||
       !aligned(w_scales, 16) || !aligned(y, 4))
@@ -511,6 +525,7 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
   if (M < 0 || K <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
   if (K % 32) return LOOPQ_ERR_UNSUPPORTED;
   if (M == 0) return LOOPQ_OK;
+  if (check_gemm_extent(padded_rows(M), K, N, 32) != LOOPQ_OK) return LOOPQ_ERR_UNSUPPORTED;
   if (!a_codes || !w_codes || !dots) return LOOPQ_ERR_INVALID_ARG;
   if (!aligned(a_codes, 4) || !aligned(w_codes, 16) || !aligned(dots, 4))
     return LOOPQ_ERR_ALIGNMENT;

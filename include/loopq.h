@@ -66,7 +66,9 @@ typedef enum {
   LOOPQ_OK = 0,
   LOOPQ_ERR_INVALID_ARG = -1, /* null pointer, size <= 0, clip <= 0 or not finite */
   LOOPQ_ERR_UNSUPPORTED = -2, /* K % 32 != 0, n1*n2 != K, n1 or n2 not a multiple of 4
-                                 or above 128, bits not 4/8, group_w not 32/128, T > 64 */
+                                 or above 128, bits not 4/8, group_w not 32/128, T > 64,
+                                 or a GEMM whose activation steps (rows x K/32 x 4 B) or
+                                 weight steps (padded N x groups x 2 B) reach 2 GiB */
   LOOPQ_ERR_ALIGNMENT = -3,   /* a pointer breaks the alignment a call states */
   LOOPQ_ERR_RANGE = -4,       /* a weight step overflows fp16 */
   LOOPQ_ERR_HIP = -5,         /* the HIP runtime reported an error */
