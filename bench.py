@@ -40,6 +40,9 @@ def parse():
                    help="only run this many steps of the W4A4 step (for rocprofv3), no JSON")
     p.add_argument("--profile-schedule", type=int, default=0,
                    help="schedule used by --profile-steps (0 auto, 1 loop-sequential, 2 weight-stationary)")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="with --profile-steps: first run one device-to-device copy of this many MiB "
+                        "(a plain copy kernel of known size that calibrates HBM byte counters)")
     return p.parse_args()
 
 
@@ -73,6 +76,33 @@ def build_modules(lq, synth, wl, torch):
         mods.append(Module(act, K, N, torch.from_numpy(P1).cuda(), torch.from_numpy(P2).cuda(),
                            [float(c) for c in synth.clips_for(wl, act)], x, codes, scales))
     return mods
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "hbm_traffic_ouro_block_M1024_T4.md")
+
+
+def gemm_source_sha256():
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in ("bit_ptq_looped_amd/csrc/gemm_w4.hip", "bit_ptq_looped_amd/csrc/loopq_internal.h"):
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None when the GEMM source changed since it was taken."""
+    try:
+        fields = dict(line.split(": ", 1) for line in open(TRAFFIC_FILE).read().splitlines()
+                      if line.startswith("gemm_"))
+    except OSError:
+        return None
+    if fields.get("gemm_source_sha256") != gemm_source_sha256():
+        return None
+    return float(fields["gemm_traffic_bytes_per_launch"])
 
 
 def alg_ops(mods, T, M):
@@ -169,6 +199,14 @@ def main():
     torch.cuda.synchronize()
 
     if args.profile_steps:
+        if args.copy_mib:
+            src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            print(f"copied {args.copy_mib} MiB", flush=True)
+            del src, dst
         run_steps(lq, mods, 4, args.profile_schedule, args.profile_steps)
         torch.cuda.synchronize()
         print(f"profiled {args.profile_steps} steps", flush=True)
@@ -213,7 +251,8 @@ def main():
             "peak": INT8_PEAK_TOPS,
             "unit": "TFLOP/s",
             "frac": achieved / INT8_PEAK_TOPS,
-            "traffic": None,
+            "traffic": measured_traffic(),
+            "traffic_unit": "HBM bytes per GEMM launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": "gemm_kernel<0> (integer GEMM + per-group rescale)",
             "launches": gemm_n,
             "avg_launch_ms": gemm_ms / max(gemm_n, 1),

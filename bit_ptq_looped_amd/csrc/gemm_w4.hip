@@ -78,8 +78,24 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int c = lane & 31;
-  const int m_base = blockIdx.y * 128 + (wave >> 1) * 64;
-  const int n_base = blockIdx.x * 128 + (wave & 1) * 64;
+  // Work-group -> 128x128 output tile.  Consecutive work-groups land on the
+  // 8 XCDs in turn and each XCD has its own L2, so first give every XCD one
+  // contiguous range of tile numbers, then walk tiles in groups of 8 row
+  // panels, down the rows of a group before moving one column panel on: an
+  // XCD's range is then a compact block of row and column panels whose
+  // operands its L2 reads about once.
+  const int Mp = (g.M + 127) >> 7;
+  const int Np = (g.N + 127) >> 7;
+  const int total = Mp * Np;
+  const int xcd = blockIdx.x & 7;
+  const int q = xcd * (total >> 3) + min(xcd, total & 7) + (blockIdx.x >> 3);
+  const int grp = q / (8 * Np);
+  const int gm = min(Mp - grp * 8, 8);
+  const int r = q - grp * 8 * Np;
+  const int mt = grp * 8 + r % gm;
+  const int nt = r / gm;
+  const int m_base = mt * 128 + (wave >> 1) * 64;
+  const int n_base = nt * 128 + (wave & 1) * 64;
   if (m_base >= g.M || n_base >= g.N) return;
   const int Ga = g.K >> 5;
   const int Gw = ((g.K >> 5) + (1 << g.gshift) - 1) >> g.gshift;
@@ -275,7 +291,7 @@ hipError_t launch_gemm(const int8_t* a_tiled, const float* a_scales_gm, int ld_s
   g.gshift = gw == 128 ? 2 : 0;
   g.y = y;
   g.dots = dots;
-  dim3 grid((N + 127) / 128, (M + 127) / 128);
+  dim3 grid(((N + 127) / 128) * ((M + 127) / 128));
   if (mode == 0)
     hipLaunchKernelGGL(gemm_kernel<0>, grid, dim3(256), 0, s, g);
   else

@@ -123,7 +123,7 @@ __device__ __forceinline__ void store_run(const QuantArgs& a, int row, int k0, u
 }
 
 // No transform: quantize x directly.  One wave covers 8 groups (256 elements)
-// per step; the grid strides over all rows * K / 256 wave-steps.
+// per step; each wave takes a contiguous range of the rows * K / 256 steps.
 __global__ __launch_bounds__(256) void quant_plain_kernel(QuantArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -131,7 +131,12 @@ __global__ __launch_bounds__(256) void quant_plain_kernel(QuantArgs a) {
   const int K = a.K;
   const int64_t total = (int64_t)a.rows * K;  // K % 32 == 0, so total % 256 may be 0 or 128.. handled per lane
   const float qmaxf = (float)a.qmax;
-  for (int64_t base = (int64_t)wave * 256; base < total; base += (int64_t)nwaves * 256) {
+  // each wave takes one contiguous range of 256-element steps, so the lines
+  // of the tiled code layout are completed by one wave (one L2)
+  const int64_t nsteps = (total + 255) / 256;
+  const int64_t per_wave = (nsteps + nwaves - 1) / nwaves;
+  const int64_t step_end = min(nsteps, ((int64_t)wave + 1) * per_wave);
+  for (int64_t base = (int64_t)wave * per_wave * 256; base < step_end * 256; base += 256) {
     const int64_t e0 = base + lane * 4;
     // a lane group of 8 covers one 32-group; groups never straddle rows (K % 32 == 0)
     const bool valid = e0 < total;
@@ -294,7 +299,14 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const int lk = lane >> 4;  // k within a 4-deep step; result rows lk + 4 e
   const int nchunks = (a.rows + R - 1) / R;
 
-  for (int chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
+  // Each pass of the grid covers gridDim.x consecutive chunks.  Work-groups
+  // land on the 8 XCDs in turn; slot numbering gives each XCD one run of
+  // consecutive chunks per pass, so the rows sharing a 128-byte line of the
+  // tiled code layout are written at about the same time into one L2.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int slot = xcd * (G >> 3) + min(xcd, G & 7) + (int)(blockIdx.x >> 3);
+  for (int chunk = slot; chunk < nchunks; chunk += G) {
     const int row0 = chunk * R;
     const int rows = min(R, a.rows - row0);
     __syncthreads();  // previous chunk done with the x~ rows (and P staged on the first pass)
