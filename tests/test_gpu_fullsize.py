@@ -1,0 +1,169 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times: loopq_looped_forward with the default (weight-stationary) schedule over
+all T*M rows of one quantized input, checked on sampled outputs the oracle
+computes row by row.
+
+* Packed weights: the exported codes and fp16 steps of the whole matrix are
+  bit-exact against the oracle's weight quantization.
+* y: sampled (loop, row) pairs, all N columns, max|y - y_oracle| /
+  max|y_oracle| <= 1e-4 over the sampled rows.
+* Quantizer: loopq_quant_act over all T*M rows (clip of loop 0) with the x~
+  dump; on sampled rows the dump is within one fp32 ulp of the oracle's
+  fp64-then-rounded transform, and codes and steps are bit-exact against the
+  oracle applied to the dump (equal to the oracle's own x~ wherever no ulp
+  differs).
+
+Inputs are the seeded generators' full tensors, except for the Huginn-like
+recurrence, whose host-side generation at 65,536 rows x K = 17,920 takes about
+a minute per input: there a 256-row seeded block of the same recurrence is
+repeated along M on the device.  Rows are independent in this computation, so
+the launch is still the full-size one, and samples from several repeats check
+every tile position against the same oracle rows.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_ptq_looped_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 1e-4
+HUGINN_BLOCK_ROWS = 256
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def groups_by_input(wl):
+    g = {}
+    for lin in wl.linears:
+        g.setdefault(lin.act, []).append(lin)
+    return g
+
+
+def sample_rows(M, block=None):
+    rows = sorted({0, 1, 31, 32, M // 2 + 5, M - 33, M - 1})
+    if block:
+        rows = sorted(set(rows) | {block - 1, block + 3, 3 * block + 17})
+    return [r for r in rows if 0 <= r < M]
+
+
+def sample_loops(T):
+    return sorted({0, 1, T // 2, T - 1})
+
+
+def run_case(lq, wl, act, tile_rows=None):
+    lins = groups_by_input(wl)[act]
+    K = lins[0].K
+    gw = wl.group_w
+    W = np.concatenate([synth.weights_for(wl, lin) for lin in lins], axis=0)
+    N = W.shape[0]
+    P1, P2 = synth.factors_for(wl, act, K)
+    clips = synth.clips_for(wl, act)
+    T, M = wl.T, wl.M
+    say(f"{wl.name}: input {act} K={K} N={N} T={T} M={M} bits_a={wl.bits_a} g_w={gw}")
+
+    # weights: GPU pack of the whole matrix vs the oracle's quantization
+    codes, scales = lq.empty_packed_weights(K, N, gw)
+    lq.loopq_pack_weights(dev(W), gw, codes, scales)
+    qw, sw = oracle.quant_weights(W, gw)
+    gc = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    gs = torch.empty((N, math.ceil(K / gw)), dtype=torch.int16, device="cuda")
+    lq.loopq_export_weights(codes, scales, K, N, gw, gc, gs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gc.cpu().numpy(), qw)
+    np.testing.assert_array_equal(gs.cpu().numpy().view(np.uint16), sw.view(np.uint16))
+    del gc, gs
+
+    # activations [T][M][K] on the device (bf16), and the oracle's fp32 rows
+    if tile_rows:
+        bits, x32 = synth.activations_for(wl, act, K, rows=tile_rows)
+        x = bf16_dev(bits).repeat(1, M // tile_rows, 1).contiguous()
+        src = lambda t, m: x32[t, m % tile_rows]
+    else:
+        bits, x32 = synth.activations_for(wl, act, K)
+        x = bf16_dev(bits)
+        src = lambda t, m: x32[t, m]
+    del bits
+
+    y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, wl.bits_a)
+    tP1 = dev(P1) if P1 is not None else None
+    tP2 = dev(P2) if P2 is not None else None
+    lq.loopq_looped_forward(x, tP1, tP2, clips, wl.bits_a, codes, scales, gw, N, y,
+                            lq.LOOPQ_SCHED_AUTO, ws)
+    torch.cuda.synchronize()
+    del ws
+
+    ts = sample_loops(T)
+    ms = sample_rows(M, tile_rows)
+    idx_t = torch.tensor(ts, device="cuda")
+    idx_m = torch.tensor(ms, device="cuda")
+    ys = y.index_select(0, idx_t).index_select(1, idx_m).cpu().numpy()  # [len(ts)][len(ms)][N]
+    del y
+    ref = np.empty(ys.shape, dtype=np.float64)
+    for a, t in enumerate(ts):
+        xr = np.stack([src(t, m) for m in ms])
+        ref[a], _, _ = oracle.linear(xr, P1, P2, float(clips[t]), wl.bits_a, qw, sw, gw)
+    err = float(np.max(np.abs(ys - ref)) / np.max(np.abs(ref)))
+    say(f"  y: {len(ts)} loops x {len(ms)} rows x {N} columns, rel err {err:.3e}")
+    assert err <= Y_TOL
+
+    # quantizer over all T*M rows (loop-0 clip) with the x~ dump, sampled
+    rows_all = T * M
+    xf = x.view(rows_all, K)
+    qc = torch.empty((rows_all, K), dtype=torch.int8, device="cuda")
+    qs = torch.empty((rows_all, K // 32), dtype=torch.float32, device="cuda")
+    xt = torch.empty((rows_all, K), dtype=torch.float32, device="cuda") if P1 is not None else None
+    lq.loopq_quant_act(xf, tP1, tP2, float(clips[0]), wl.bits_a, qc, qs, xt)
+    torch.cuda.synchronize()
+    flat = [t * M + m for t in ts for m in ms]
+    fi = torch.tensor(flat, device="cuda")
+    gcodes = qc.index_select(0, fi).cpu().numpy()
+    gsteps = qs.index_select(0, fi).cpu().numpy()
+    xr = np.stack([src(t, m) for t in ts for m in ms])
+    if xt is None:
+        dump = xr.astype(np.float32)
+    else:
+        dump = xt.index_select(0, fi).cpu().numpy()
+        want = oracle.transformed_f32(xr, P1, P2)
+        ulps = np.abs(dump.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        say(f"  x~: {ulps.size} elements, {np.count_nonzero(ulps)} differ by one ulp")
+        assert ulps.max() <= 1
+        assert np.count_nonzero(ulps) <= max(4, ulps.size // 100000)
+    qa, sa = oracle.quant_act(dump, float(clips[0]), wl.bits_a)
+    np.testing.assert_array_equal(gcodes, qa)
+    np.testing.assert_array_equal(gsteps.view(np.uint32), sa.view(np.uint32))
+
+
+OURO_INPUTS = ["qkv_in", "o_in", "up_in", "down_in"]
+
+
+@pytest.mark.parametrize("bits_a", [4, 8])
+@pytest.mark.parametrize("act", OURO_INPUTS)
+def test_fullsize_ouro_block(lq, act, bits_a):
+    run_case(lq, synth.ouro_block_workload(bits_a=bits_a), act)
+
+
+@pytest.mark.parametrize("act", ["adapter_in", "core_in", "proj_in"])
+def test_fullsize_huginn(lq, act):
+    run_case(lq, synth.huginn_workload(), act, tile_rows=HUGINN_BLOCK_ROWS)
+
+
+@pytest.mark.parametrize("act", OURO_INPUTS)
+def test_fullsize_large_prefill(lq, act):
+    run_case(lq, synth.large_prefill_workload(T=4), act)
