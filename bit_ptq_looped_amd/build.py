@@ -33,6 +33,7 @@ COMMON = [
 EXTRA = {
     # keep MFMA results in VGPRs: the rescale reads every element with VALU ops
     "gemm_w4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm_f6.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

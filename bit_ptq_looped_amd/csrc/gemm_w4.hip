@@ -10,9 +10,12 @@
 //
 // One V_MFMA_I32_32X32X32_I8 covers exactly one 32-wide K-group of a 32x32
 // output tile, so its int32 result is the group dot d for 32x32 (m, n)
-// pairs; the accumulator is not carried across groups.  The result is
-// converted to fp32 and folded into an fp32 accumulator with the product of
-// the two steps.  INT4 weight nibbles are unpacked to int8 in registers.
+// pairs; the accumulator is not carried across groups.  The MFMA starts from
+// the bit pattern of 1.5 * 2^23, so its int32 result reads as the fp32 number
+// 1.5 * 2^23 + d and one exact subtraction gives d as a float; it is folded
+// into an fp32 accumulator with the product of the two steps.  INT4 weight
+// nibbles are unpacked to int8 in registers.  This kernel serves W4A8 (and
+// W4A4 on request); gemm_f6.hip is the W4A4 kernel.
 //
 // Tiling: 256 threads = 4 waves in a 2x2 arrangement, 128x128 outputs per
 // work-group, 64x64 (2x2 MFMA tiles) per wave.  Operands stream from global
@@ -20,26 +23,10 @@
 // contiguous 1 KB / 512 B block); the loop is unrolled twice so the next
 // group's loads are in flight while the current one is multiplied and folded,
 // with no register copies between stages.
-#include "loopq_internal.h"
+#include "gemm_tile.h"
 
 namespace loopq {
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v32f __attribute__((ext_vector_type(32)));
-
-struct GemmArgs {
-  const int8_t* a;   // tiled codes
-  const float* sa;   // group-major steps [Ga][ld_sa]
-  int ld_sa;
-  int M, K, N;
-  const uint8_t* w;  // packed nibbles
-  const __half* sw;  // packed steps [Npad/32][Gw][32]
-  int gshift;        // log2(group_w / 32)
-  float* y;          // [M][N]
-  int32_t* dots;     // [M][N][Ga] (mode 1)
-};
 
 // 8 biased nibbles (q + 8) per dword -> 16 int8 codes, in K order
 __device__ __forceinline__ v4i unpack_w(uint2 p) {
@@ -60,17 +47,6 @@ struct Stage {
   uint32_t sw;       // raw fp16 weight step of column l % 32 of column tile h
 };
 
-// The wave computes 32x32 tiles of y^T: result element e of lane l belongs to
-// row m = l % 32 of the activation tile and column n = 8 (e / 4) + 4 (l / 32)
-// + e % 4 of the weight tile.  One activation step per lane and tile; the
-// 16 weight steps of the lane are stored contiguously (see the step layout in
-// loopq_internal.h) and enter the rescale as fp16 operands of v_fma_mix.
-// raw buffer resource over [p, p + bytes): stride 0, gfx9 data format word;
-// loads at or past `bytes` return 0
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
@@ -78,24 +54,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int c = lane & 31;
-  // Work-group -> 128x128 output tile.  Consecutive work-groups land on the
-  // 8 XCDs in turn and each XCD has its own L2, so first give every XCD one
-  // contiguous range of tile numbers, then walk tiles in groups of 8 row
-  // panels, down the rows of a group before moving one column panel on: an
-  // XCD's range is then a compact block of row and column panels whose
-  // operands its L2 reads about once.
-  const int Mp = (g.M + 127) >> 7;
-  const int Np = (g.N + 127) >> 7;
-  const int total = Mp * Np;
-  const int xcd = blockIdx.x & 7;
-  const int q = xcd * (total >> 3) + min(xcd, total & 7) + (blockIdx.x >> 3);
-  const int grp = q / (8 * Np);
-  const int gm = min(Mp - grp * 8, 8);
-  const int r = q - grp * 8 * Np;
-  const int mt = grp * 8 + r % gm;
-  const int nt = r / gm;
-  const int m_base = mt * 128 + (wave >> 1) * 64;
-  const int n_base = nt * 128 + (wave & 1) * 64;
+  int m_base, n_base;
+  map_tile(g, wave, &m_base, &n_base);
   if (m_base >= g.M || n_base >= g.N) return;
   const int Ga = g.K >> 5;
   const int Gw = ((g.K >> 5) + (1 << g.gshift) - 1) >> g.gshift;
@@ -113,7 +73,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     const int mb = min((m_base >> 5) + t, mlast);
     const int nb = min((n_base >> 5) + t, nlast);
     x_rs[t] = make_rsrc(reinterpret_cast<const char*>(g.a) + (int64_t)mb * Ga * 1024, (uint32_t)Ga * 1024u);
-    w_rs[t] = make_rsrc(g.w + (int64_t)nb * Ga * kBlockBytes, (uint32_t)Ga * kBlockBytes);
+    w_rs[t] = make_rsrc(reinterpret_cast<const uint8_t*>(g.w) + (int64_t)nb * Ga * kBlockBytes,
+                        (uint32_t)Ga * kBlockBytes);
   }
   const int x_off = lane * 16;
   const int w_off = lane * 8;
@@ -222,28 +183,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   }
   if (j < Ga) compute(s0, j);
 
-  if (MODE == 0) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = m_base + 32 * t + c;
-      if (row >= g.M) continue;
-      float* yr = g.y + (int64_t)row * g.N;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n_base + 32 * u + 8 * q + 4 * h;
-          if (col + 3 < g.N && (g.N & 3) == 0) {
-            *reinterpret_cast<float4*>(yr + col) =
-                float4{acc[t][u][4 * q], acc[t][u][4 * q + 1], acc[t][u][4 * q + 2], acc[t][u][4 * q + 3]};
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (col + r < g.N) yr[col + r] = acc[t][u][4 * q + r];
-          }
-        }
-    }
-  }
+  if (MODE == 0) store_y(g, acc, m_base, n_base, h, c);
 }
 
 __global__ __launch_bounds__(256) void tile_codes_kernel(const int8_t* __restrict__ canon,
@@ -259,13 +199,10 @@ __global__ __launch_bounds__(256) void tile_codes_kernel(const int8_t* __restric
   const int k0 = (int)(idx - (int64_t)row * (K >> 2)) * 4;
   const uint32_t v = *reinterpret_cast<const uint32_t*>(canon + (int64_t)row * K + k0);
   const int j = k0 >> 5, kk = k0 & 31;
-  if (fmt == kCodesTiledBf16) {
-    uint32_t b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = __float_as_uint((float)(int8_t)(v >> (8 * i))) >> 16;
-    char* base = reinterpret_cast<char*>(tiled);
-    *reinterpret_cast<uint2*>(base + ((int64_t)(row >> 5) * Ga + j) * 2048 + (kk >> 4) * 1024 +
-                              (row & 31) * 32 + (kk & 15) * 2) = uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+  if (fmt == kCodesTiledF6) {
+    // runs idx .. idx + 3 (an aligned quad of lanes) are the 16 codes of one
+    // half-group: runs is a multiple of 8 and K of 32, so quads stay whole
+    store_f6_run(tiled, (int)group_pairs(K), row, k0, e2m3_of_codes4(v));
   } else {
     *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(tiled) + ((int64_t)(row >> 5) * Ga + j) * 1024 +
                                  (kk >> 4) * 512 + (row & 31) * 16 + (kk & 15)) = v;

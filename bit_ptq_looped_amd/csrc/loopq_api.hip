@@ -75,41 +75,49 @@ void recycle_locked() {
   g_timing_recs.clear();
 }
 
-// Which GEMM the hot path uses: the INT8 kernel (default) or the bf16-operand
-// kernel (LOOPQ_GEMM=bf16, kept for comparison; same results).
-bool use_bf16_gemm() {
+// Which GEMM the hot path uses: W4A4 runs on the fp6-operand kernel and W4A8
+// on the INT8 kernel.  LOOPQ_GEMM=int8 sends W4A4 to the INT8 kernel too
+// (same results; kept for comparison).
+bool force_int8_gemm() {
   static const bool v = [] {
     const char* e = getenv("LOOPQ_GEMM");
-    return e != nullptr && strcmp(e, "bf16") == 0;
+    return e != nullptr && strcmp(e, "int8") == 0;
   }();
   return v;
 }
 
+int code_format(int bits_a) { return bits_a == 4 && !force_int8_gemm() ? kCodesTiledF6 : kCodesTiledI8; }
+
 // Internal buffers of the quantize -> GEMM path, carved from the caller's
 // workspace for `chunks` chunks of `rows` rows each:
-//   codes  : chunks * padded(rows) rows in the tiled layout (2 bytes/code
-//            reserved so either GEMM's format fits)
+//   codes  : chunks * padded(rows) rows in the tiled layout, row_bytes(K)
+//            per row (enough for either tiled format)
 //   scales : fp32 group-major, chunks * padded(rows) columns
-//   wexp   : weights expanded to bf16 operands (bf16 GEMM only)
+//   wexp   : weights expanded to fp6 operands (W4A4 kernel only)
 // The same region also holds all chunks * rows rows as one contiguous tiled
 // matrix (padded(chunks * rows) <= chunks * padded(rows)).
 struct ActBuffers {
   void* codes;
   float* scales;
-  uint16_t* wexp;
+  void* wexp;
   int ld;
 };
 
+int64_t row_bytes(int64_t K) {
+  const int64_t f6 = group_pairs(K) * (kF6BlockBytes / 32);
+  return K > f6 ? K : f6;
+}
 size_t codes_region(int64_t chunks, int64_t rows, int64_t K) {
-  return align256((size_t)(chunks * padded_rows(rows) * K * 2));
+  return align256((size_t)(chunks * padded_rows(rows) * row_bytes(K)));
 }
 size_t scales_region(int64_t chunks, int64_t rows, int64_t K) {
   return align256((size_t)((K / 32) * chunks * padded_rows(rows) * 4));
 }
-size_t act_bytes(int64_t chunks, int64_t rows, int64_t K, int64_t N) {
-  size_t b = codes_region(chunks, rows, K) + scales_region(chunks, rows, K);
-  if (use_bf16_gemm()) b += align256((size_t)(padded_cols(N) * K * 2));
-  return b;
+size_t wexp_region(int64_t K, int64_t N, int fmt) {
+  return fmt == kCodesTiledF6 ? align256((size_t)(padded_cols(N) / 32 * group_pairs(K) * kF6BlockBytes)) : 0;
+}
+size_t act_bytes(int64_t chunks, int64_t rows, int64_t K, int64_t N, int fmt) {
+  return codes_region(chunks, rows, K) + scales_region(chunks, rows, K) + wexp_region(K, N, fmt);
 }
 
 // buffers of chunk c (rows rows each), or with all_rows > 0 the whole
@@ -119,36 +127,35 @@ ActBuffers carve(void* ws, int64_t chunks, int64_t rows, int64_t K, int64_t c, i
   char* base = reinterpret_cast<char*>(ws);
   const int64_t mp = padded_rows(rows);
   float* scales0 = reinterpret_cast<float*>(base + codes_region(chunks, rows, K));
-  b.wexp = reinterpret_cast<uint16_t*>(base + codes_region(chunks, rows, K) +
-                                       scales_region(chunks, rows, K));
+  b.wexp = base + codes_region(chunks, rows, K) + scales_region(chunks, rows, K);
   if (all_rows > 0) {
     b.codes = base;
     b.scales = scales0;
     b.ld = (int)padded_rows(all_rows);
   } else {
-    b.codes = base + (size_t)c * mp * K * 2;
+    b.codes = base + (size_t)c * mp * row_bytes(K);
     b.scales = scales0 + (size_t)c * (K / 32) * mp;
     b.ld = (int)mp;
   }
   return b;
 }
 
-// GEMM stage on codes already in the internal layout of the selected kernel
-hipError_t run_gemm(const ActBuffers& b, int rows, int K, int N, const void* w_codes,
-                    const void* w_scales, int gw, float* y, int32_t* dots, int mode,
-                    hipStream_t s) {
-  const uint8_t* wc = reinterpret_cast<const uint8_t*>(w_codes);
-  const __half* wsc = reinterpret_cast<const __half*>(w_scales);
-  if (!use_bf16_gemm())
-    return launch_gemm(reinterpret_cast<const int8_t*>(b.codes), b.scales, b.ld, rows, K, N, wc,
-                       wsc, gw, y, dots, mode, s);
-  hipError_t e = launch_expand_weights_bf16(wc, K, N, b.wexp, s);
-  if (e != hipSuccess) return e;
-  return launch_gemm_bf16(reinterpret_cast<const uint16_t*>(b.codes), b.scales, b.ld, rows, K, N,
-                          b.wexp, wsc, gw, y, dots, mode, s);
+// the W4A4 kernel's weight operands, once per call (before its GEMMs, on the
+// same stream)
+hipError_t prepare_weights(const ActBuffers& b, int fmt, const void* w_codes, int K, int N, hipStream_t s) {
+  if (fmt != kCodesTiledF6) return hipSuccess;
+  return launch_expand_weights_f6(reinterpret_cast<const uint8_t*>(w_codes), K, N, b.wexp, s);
 }
 
-int code_format() { return use_bf16_gemm() ? kCodesTiledBf16 : kCodesTiledI8; }
+// GEMM stage on codes already in the internal layout `fmt`
+hipError_t run_gemm(const ActBuffers& b, int fmt, int rows, int K, int N, const void* w_codes,
+                    const void* w_scales, int gw, float* y, int32_t* dots, int mode, hipStream_t s) {
+  const __half* wsc = reinterpret_cast<const __half*>(w_scales);
+  if (fmt == kCodesTiledF6)
+    return launch_gemm_f6(b.codes, b.scales, b.ld, rows, K, N, b.wexp, wsc, gw, y, dots, mode, s);
+  return launch_gemm(reinterpret_cast<const int8_t*>(b.codes), b.scales, b.ld, rows, K, N,
+                     reinterpret_cast<const uint8_t*>(w_codes), wsc, gw, y, dots, mode, s);
+}
 
 // ---------------------------------------------------------------------------
 // Auxiliary stream (one per device, default priority) and events for the
@@ -248,7 +255,7 @@ QuantArgs internal_quant_args(const void* x, int dtype, int rows, int K, const f
   a.clips = clips;
   a.rows_per_clip = rows_per_clip;
   a.codes = reinterpret_cast<int8_t*>(b.codes);
-  a.codes_fmt = code_format();
+  a.codes_fmt = code_format(bits_a);
   a.scales = b.scales;
   a.scales_gm = 1;
   a.scales_ld = b.ld;
@@ -264,7 +271,9 @@ int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const floa
   ActBuffers b = carve(ws, ws_chunks, ws_rows, K, 0, rows);
   QuantArgs a = internal_quant_args(x, dtype, rows, K, P1, n1, P2, n2, clips, rows_per_clip,
                                     bits_a, b);
-  hipError_t e;
+  const int fmt = code_format(bits_a);
+  hipError_t e = prepare_weights(b, fmt, w_codes, K, N, s);
+  if (e != hipSuccess) return LOOPQ_ERR_HIP;
   {
     TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, s);
     e = launch_quant_act(a, s);
@@ -272,7 +281,7 @@ int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const floa
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   {
     TimingScope ts(LOOPQ_KERNEL_GEMM, s);
-    e = run_gemm(b, rows, K, N, w_codes, w_scales, gw, y, nullptr, 0, s);
+    e = run_gemm(b, fmt, rows, K, N, w_codes, w_scales, gw, y, nullptr, 0, s);
   }
   return hip_status(e);
 }
@@ -287,6 +296,9 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
   std::lock_guard<std::mutex> lk(g_pipe_mu);
   DevicePipe* p = nullptr;
   if (device_pipe(&p, T + 1) != hipSuccess) return LOOPQ_ERR_HIP;
+  const int fmt = code_format(bits_a);
+  if (prepare_weights(carve(ws, T, M, K, 0, 0), fmt, w_codes, K, N, s) != hipSuccess)
+    return LOOPQ_ERR_HIP;
   const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
   hipEvent_t start = p->events[T];
   if (hipEventRecord(start, s) != hipSuccess) return LOOPQ_ERR_HIP;
@@ -312,7 +324,7 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
     hipError_t e;
     {
       TimingScope ts(LOOPQ_KERNEL_GEMM, s);
-      e = run_gemm(b, M, K, N, w_codes, w_scales, gw, y + (size_t)t * M * N, nullptr, 0, s);
+      e = run_gemm(b, fmt, M, K, N, w_codes, w_scales, gw, y + (size_t)t * M * N, nullptr, 0, s);
     }
     if (e != hipSuccess) return LOOPQ_ERR_HIP;
   }
@@ -351,19 +363,20 @@ int32_t loopq_packed_weight_bytes(int32_t K, int32_t N, int32_t group_w, size_t*
 
 int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32_t N,
                               int32_t bits_a, size_t* bytes) {
-  (void)bits_a;
   if (!bytes) return LOOPQ_ERR_INVALID_ARG;
+  if ((op == LOOPQ_OP_LINEAR || op == LOOPQ_OP_LOOPED_FORWARD) && bits_a != 4 && bits_a != 8)
+    return LOOPQ_ERR_UNSUPPORTED;
   switch (op) {
     case LOOPQ_OP_LINEAR:
       if (M < 0 || K <= 0 || K % 32) return M < 0 || K <= 0 ? LOOPQ_ERR_INVALID_ARG : LOOPQ_ERR_UNSUPPORTED;
       if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
-      *bytes = act_bytes(1, M, K, N);
+      *bytes = act_bytes(1, M, K, N, code_format(bits_a));
       return LOOPQ_OK;
     case LOOPQ_OP_LOOPED_FORWARD:
       if (T <= 0 || M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (T > LOOPQ_MAX_LOOPS || K % 32) return LOOPQ_ERR_UNSUPPORTED;
       if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
-      *bytes = act_bytes(T, M, K, N);
+      *bytes = act_bytes(T, M, K, N, code_format(bits_a));
       return LOOPQ_OK;
     case LOOPQ_OP_FOLD:
       if (M <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
@@ -486,9 +499,11 @@ int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, in
 
 int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M, int32_t K,
                          int32_t N, const void* w_codes, const void* w_scales, int32_t group_w,
-                         float* y, void* workspace, size_t workspace_bytes, void* stream) {
+                         int32_t bits_a, float* y, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   int32_t st = check_weights(K, N, group_w);
   if (st != LOOPQ_OK) return st;
+  if (bits_a != 4 && bits_a != 8) return LOOPQ_ERR_UNSUPPORTED;
   if (M < 0) return LOOPQ_ERR_INVALID_ARG;
   if (M == 0) return LOOPQ_OK;
   st = check_gemm_extent(padded_rows(M), K, N, group_w);
@@ -497,13 +512,15 @@ int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M
   if (!aligned(a_codes, 4) || !aligned(a_scales, 4) || !aligned(w_codes, 16) ||
       !aligned(w_scales, 16) || !aligned(y, 4))
     return LOOPQ_ERR_ALIGNMENT;
-  const size_t need = act_bytes(1, M, K, N);
+  const int fmt = code_format(bits_a);
+  const size_t need = act_bytes(1, M, K, N, fmt);
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
   ActBuffers b = carve(workspace, 1, M, K, 0, M);
-  hipError_t e = launch_tile_codes(a_codes, a_scales, M, K, b.codes, code_format(), b.scales, b.ld, s);
-  if (e == hipSuccess) e = run_gemm(b, M, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s);
+  hipError_t e = launch_tile_codes(a_codes, a_scales, M, K, b.codes, fmt, b.scales, b.ld, s);
+  if (e == hipSuccess) e = prepare_weights(b, fmt, w_codes, K, N, s);
+  if (e == hipSuccess) e = run_gemm(b, fmt, M, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s);
   return hip_status(e);
 }
 
@@ -519,23 +536,26 @@ int32_t loopq_export_weights(const void* w_codes, const void* w_scales, int32_t 
                                           group_w, codes, scales, as_stream(stream)));
 }
 
-int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
+int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N, int32_t bits_a,
                          const void* w_codes, int32_t* dots, void* workspace,
                          size_t workspace_bytes, void* stream) {
   if (M < 0 || K <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
   if (K % 32) return LOOPQ_ERR_UNSUPPORTED;
+  if (bits_a != 4 && bits_a != 8) return LOOPQ_ERR_UNSUPPORTED;
   if (M == 0) return LOOPQ_OK;
   if (check_gemm_extent(padded_rows(M), K, N, 32) != LOOPQ_OK) return LOOPQ_ERR_UNSUPPORTED;
   if (!a_codes || !w_codes || !dots) return LOOPQ_ERR_INVALID_ARG;
   if (!aligned(a_codes, 4) || !aligned(w_codes, 16) || !aligned(dots, 4))
     return LOOPQ_ERR_ALIGNMENT;
-  const size_t need = act_bytes(1, M, K, N);
+  const int fmt = code_format(bits_a);
+  const size_t need = act_bytes(1, M, K, N, fmt);
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
   ActBuffers b = carve(workspace, 1, M, K, 0, M);
-  hipError_t e = launch_tile_codes(a_codes, nullptr, M, K, b.codes, code_format(), nullptr, b.ld, s);
-  if (e == hipSuccess) e = run_gemm(b, M, K, N, w_codes, nullptr, 32, nullptr, dots, 1, s);
+  hipError_t e = launch_tile_codes(a_codes, nullptr, M, K, b.codes, fmt, nullptr, b.ld, s);
+  if (e == hipSuccess) e = prepare_weights(b, fmt, w_codes, K, N, s);
+  if (e == hipSuccess) e = run_gemm(b, fmt, M, K, N, w_codes, nullptr, 32, nullptr, dots, 1, s);
   return hip_status(e);
 }
 

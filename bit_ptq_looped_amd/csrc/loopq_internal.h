@@ -45,14 +45,55 @@ inline int64_t weight_groups(int64_t K, int64_t gw) { return (K + gw - 1) / gw; 
 // row l % 32, K-half l / 32.
 // Steps: fp32 group-major [K/32][ld] with ld >= padded rows.
 //
-// bf16 variant (operands of V_MFMA_F32_32X32X16_BF16): the same blocks at
-// 2048 bytes each; row r, K-half h and element i (0..15) sit at
-// h * 1024 + r * 32 + 2 i, so lane l loads 32 contiguous bytes (row l % 32,
-// K-half l / 32) and feeds elements 0..7 and 8..15 to two MFMAs.  Codes are
-// small integers, exact in bf16.  Expanded weights use the identical layout
-// with output columns in place of rows.
+// fp6 variant, W4A4 only (operands of V_MFMA_SCALE_F32_32X32X64_F8F6F4 in
+// the e2m3 format, which holds the codes -7..7 exactly): block (mb, p) of 32
+// rows x one pair of groups (2p, 2p + 1) starts at byte (mb * Gp + p) * 1536,
+// Gp = ceil(Ga / 2); lane slot l = row % 32 + 32 * (group % 2) holds that
+// row's 32 codes of the group in 24 bytes at l * 24, code i at bits 6i..6i+5
+// (little endian).  A wave's 24-byte-per-lane load of a block is the MFMA
+// operand whose K-halves are the two groups.  Expanded weights use the same
+// layout with output columns in place of rows.  With Ga odd the second half
+// of the last pair is never multiplied by anything but zero; it may hold any
+// bits (every e2m3 pattern is finite).
 // ---------------------------------------------------------------------------
-enum CodeFormat { kCodesCanonical = 0, kCodesTiledI8 = 1, kCodesTiledBf16 = 2 };
+enum CodeFormat { kCodesCanonical = 0, kCodesTiledI8 = 1, kCodesTiledF6 = 2 };
+constexpr int kF6BlockBytes = 1536;
+__host__ __device__ inline int64_t group_pairs(int64_t K) { return (K / 32 + 1) / 2; }
+
+// e2m3 patterns of four codes in [-7, 7] given one per byte (two's
+// complement; only the low nibble of each byte is read), packed as 4 x 6
+// bits.  Nibbles 0..7 are the codes 0..7; nibbles 9..15 are -7..-1.  Two byte
+// lookups (v_perm) by the low 3 bits, then a per-byte select on bit 3.
+__device__ __forceinline__ uint32_t e2m3_of_codes4(uint32_t codes) {
+  const uint32_t n = codes & 0x0F0F0F0Fu;
+  const uint32_t sel = n & 0x07070707u;
+  // v_perm picks byte s of {first operand : second operand}, bytes 0..3 from
+  // the second.  Codes 0..7: 00 08 10 14 18 1A 1C 1E.
+  const uint32_t pos = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, sel);
+  // nibble 8 + i is the code i - 8: i = 1..7 -> -7..-1 (i = 0 does not occur)
+  const uint32_t neg = __builtin_amdgcn_perm(0x28303438u, 0x3A3C3E00u, sel);
+  const uint32_t b3 = (n >> 3) & 0x01010101u;
+  const uint32_t mask = (b3 << 8) - b3;  // 0xFF in the bytes whose code is negative
+  const uint32_t f = (neg & mask) | (pos & ~mask);
+  return (f & 0x3Fu) | ((f >> 2) & 0xFC0u) | ((f >> 4) & 0x3F000u) | ((f >> 6) & 0xFC0000u);
+}
+
+// Store the 24 bits of one 4-code run of row `row`, starting at K index k0,
+// into the fp6 tiled layout.  Must be called by all four lanes of an aligned
+// quad of lanes holding the four consecutive runs of one 16-code half-group
+// (lane % 4 == run position): each of three lanes stores one dword of the
+// quad's 12 bytes, taking the next lane's bits through a DPP quad permute.
+__device__ __forceinline__ void store_f6_run(void* tiled, int Gp, int row, int k0, uint32_t bits24) {
+  const int i = (k0 >> 2) & 3;
+  // quad_perm(1, 2, 3, 3): lane i reads lane i + 1
+  const uint32_t nxt = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits24, 0xF9, 0xF, 0xF, false);
+  if (i == 3) return;
+  const uint32_t dw = (bits24 >> (8 * i)) | (nxt << (24 - 8 * i));
+  const int j = k0 >> 5;
+  const int64_t off = ((int64_t)(row >> 5) * Gp + (j >> 1)) * kF6BlockBytes +
+                      ((row & 31) + 32 * (j & 1)) * 24 + ((k0 & 31) >> 4) * 12 + 4 * i;
+  *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(tiled) + off) = dw;
+}
 inline int64_t padded_rows(int64_t M) { return (M + 31) / 32 * 32; }
 
 struct ClipTable {
@@ -98,15 +139,15 @@ hipError_t launch_fold(const float* w, int K, int N, const float* P1, int n1, co
 hipError_t launch_tile_codes(const int8_t* canon_codes, const float* canon_scales, int M, int K,
                              void* tiled_codes, int fmt, float* gm_scales, int ld, hipStream_t s);
 
-// packed nibbles -> bf16 weight operands in the tiled bf16 layout
-hipError_t launch_expand_weights_bf16(const uint8_t* w_codes, int K, int N, uint16_t* out,
-                                      hipStream_t s);
+// packed nibbles -> fp6 weight operands in the fp6 tiled layout
+// (padded_cols(N) / 32 * group_pairs(K) blocks of kF6BlockBytes)
+hipError_t launch_expand_weights_f6(const uint8_t* w_codes, int K, int N, void* out, hipStream_t s);
 
-// bf16-operand GEMM (codes and expanded weights in the bf16 tiled layout);
-// same modes as launch_gemm
-hipError_t launch_gemm_bf16(const uint16_t* a_tiled, const float* a_scales_gm, int ld_sa, int M,
-                            int K, int N, const uint16_t* w_bf16, const __half* w_scales, int gw,
-                            float* y, int32_t* dots, int mode, hipStream_t s);
+// fp6-operand GEMM (W4A4: codes and expanded weights in the fp6 tiled
+// layout); same modes as launch_gemm
+hipError_t launch_gemm_f6(const void* a_tiled, const float* a_scales_gm, int ld_sa, int M, int K,
+                          int N, const void* w_f6, const __half* w_scales, int gw, float* y,
+                          int32_t* dots, int mode, hipStream_t s);
 
 // GEMM over the internal activation layout.  mode 0: y = rescaled sum;
 // mode 1: write int32 per-group dots [M][N][K/32].

@@ -33,11 +33,6 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// bf16 bit pattern of a small integer code (exact)
-__device__ __forceinline__ uint32_t bf16_of_code(int8_t q) {
-  return __float_as_uint((float)q) >> 16;
-}
-
 // max over the 8 consecutive lanes of a group: quad swaps 1 and 2, then the
 // half-row mirror pairs each lane with one of the other quad (DPP, no LDS)
 __device__ __forceinline__ float group8_max(float v) {
@@ -97,14 +92,10 @@ __device__ __forceinline__ void store_run(const QuantArgs& a, int row, int k0, u
   const int K = a.K;
   const int Ga = K >> 5;
   const int j = k0 >> 5;
-  if (a.codes_fmt == kCodesTiledBf16) {
-    // 4 codes -> 4 bf16 (exact: small integers)
-    const int kk = k0 & 31;
-    const int64_t off = ((int64_t)(row >> 5) * Ga + j) * 2048 + (kk >> 4) * 1024 + (row & 31) * 32 +
-                        (kk & 15) * 2;
-    uint32_t w01 = bf16_of_code((int8_t)(packed & 0xff)) | (bf16_of_code((int8_t)((packed >> 8) & 0xff)) << 16);
-    uint32_t w23 = bf16_of_code((int8_t)((packed >> 16) & 0xff)) | (bf16_of_code((int8_t)(packed >> 24)) << 16);
-    *reinterpret_cast<uint2*>(a.codes + off) = uint2{w01, w23};
+  if (a.codes_fmt == kCodesTiledF6) {
+    // the 8 lanes of the group are consecutive and aligned, so its two
+    // half-groups are whole quads of lanes
+    store_f6_run(a.codes, (Ga + 1) >> 1, row, k0, e2m3_of_codes4(packed));
   } else if (a.codes_fmt == kCodesTiledI8) {
     const int kk = k0 & 31;
     const int64_t off = ((int64_t)(row >> 5) * Ga + j) * 1024 + (kk >> 4) * 512 + (row & 31) * 16 +

@@ -16,7 +16,7 @@ from typing import Optional, Sequence
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libloopq.so")
 
-LOOPQ_ABI_VERSION = 1
+LOOPQ_ABI_VERSION = 2
 LOOPQ_OK = 0
 LOOPQ_ERR_INVALID_ARG = -1
 LOOPQ_ERR_UNSUPPORTED = -2
@@ -45,9 +45,9 @@ SIGNATURES = {
     "loopq_w4a4_linear": ([_P, _I, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
     "loopq_looped_forward": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _I,
                               _P, _Z, _P], _I),
-    "loopq_gemm_codes": ([_P, _P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
+    "loopq_gemm_codes": ([_P, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _Z, _P], _I),
     "loopq_export_weights": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
-    "loopq_group_dots": ([_P, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "loopq_group_dots": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "loopq_timing_enable": ([_I], _I),
     "loopq_timing_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
     "loopq_timing_reset": ([], _I),
@@ -191,10 +191,10 @@ def loopq_looped_forward(x, P1, P2, clips: Sequence[float], bits_a: int, w_codes
 
 
 def loopq_gemm_codes(a_codes, a_scales, w_codes, w_scales, group_w: int, N: int, y, workspace,
-                     stream=None):
+                     bits_a: int = 4, stream=None):
     M, K = a_codes.shape
     _check(load().loopq_gemm_codes(_ptr(a_codes), _ptr(a_scales), M, K, N, _ptr(w_codes),
-                                   _ptr(w_scales), group_w, _ptr(y), _ptr(workspace),
+                                   _ptr(w_scales), group_w, bits_a, _ptr(y), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)),
            "loopq_gemm_codes")
 
@@ -204,9 +204,9 @@ def loopq_export_weights(w_codes, w_scales, K: int, N: int, group_w: int, codes,
                                        _ptr(scales), _stream(stream)), "loopq_export_weights")
 
 
-def loopq_group_dots(a_codes, w_codes, N: int, dots, workspace, stream=None):
+def loopq_group_dots(a_codes, w_codes, N: int, dots, workspace, bits_a: int = 4, stream=None):
     M, K = a_codes.shape
-    _check(load().loopq_group_dots(_ptr(a_codes), M, K, N, _ptr(w_codes), _ptr(dots), _ptr(workspace),
+    _check(load().loopq_group_dots(_ptr(a_codes), M, K, N, bits_a, _ptr(w_codes), _ptr(dots), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)),
            "loopq_group_dots")
 

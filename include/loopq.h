@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define LOOPQ_ABI_VERSION 1
+#define LOOPQ_ABI_VERSION 2
 #define LOOPQ_GROUP_A 32   /* activation group size (lq1_quantization) */
 #define LOOPQ_MAX_LOOPS 64 /* largest T accepted by loopq_looped_forward */
 
@@ -181,10 +181,13 @@ int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
 
 /* a5 alone -- the GEMM on activation codes and steps already formed.
  * a_codes int8 [M][K], a_scales fp32 [M][K/32] (the layouts loopq_quant_act
- * writes); same weights and output as loopq_w4a4_linear. */
+ * writes); same weights and output as loopq_w4a4_linear.  bits_a selects
+ * the kernel as in the linear: 4 (every code must lie in [-7, 7]; codes
+ * outside give unspecified results) or 8 ([-127, 127]). */
 int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M, int32_t K,
                          int32_t N, const void* w_codes, const void* w_scales, int32_t group_w,
-                         float* y, void* workspace, size_t workspace_bytes, void* stream);
+                         int32_t bits_a, float* y, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Test export: canonical weight codes int8 [N][K] and steps fp16 [N][ceil(K/group_w)]
  * (raw binary16 bits) from the packed layout. */
@@ -192,9 +195,11 @@ int32_t loopq_export_weights(const void* w_codes, const void* w_scales, int32_t 
                              int32_t group_w, int8_t* codes, uint16_t* scales, void* stream);
 
 /* Test export: the exact int32 per-group dots d[m][n][j] = sum_{k in group j}
- * a_codes[m][k] * w[n][k], computed by the GEMM's own MFMA path, [M][N][K/32].
- * a_codes int8 [M][K]; workspace as for loopq_workspace_bytes(LOOPQ_OP_LINEAR). */
-int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
+ * a_codes[m][k] * w[n][k], computed by the MFMA path of the bits_a kernel
+ * (4: fp6 operands, codes in [-7, 7]; 8: INT8 operands), [M][N][K/32].
+ * a_codes int8 [M][K]; workspace as for loopq_workspace_bytes(LOOPQ_OP_LINEAR,
+ * 1, M, K, N, bits_a). */
+int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N, int32_t bits_a,
                          const void* w_codes, int32_t* dots, void* workspace,
                          size_t workspace_bytes, void* stream);
 

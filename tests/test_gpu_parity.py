@@ -161,7 +161,8 @@ def test_quant_zero_rows_and_tiny_clip(lq):
 
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("M,K,N,gw", [(16, 256, 128, 32), (37, 512, 200, 32), (130, 2048, 96, 32),
-                                      (5, 160, 64, 128), (64, 10560, 64, 128)])
+                                      (5, 160, 64, 128), (64, 10560, 64, 128), (9, 96, 40, 32),
+                                      (3, 32, 33, 32)])
 def test_group_dots_bit_exact(lq, bits, M, K, N, gw):
     say(f"group dots A{bits} M={M} K={K} N={N} gw={gw}")
     qmax = oracle.qmax_for_bits(bits)
@@ -171,24 +172,27 @@ def test_group_dots_bit_exact(lq, bits, M, K, N, gw):
     qw, _ = oracle.quant_weights(w, gw)
     dots = torch.empty((M, N, K // 32), dtype=torch.int32, device="cuda")
     ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR, 1, M, K, N, bits)
-    lq.loopq_group_dots(dev(qa), codes, N, dots, ws)
+    lq.loopq_group_dots(dev(qa), codes, N, dots, ws, bits_a=bits)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(dots.cpu().numpy().astype(np.int64), oracle.group_dots(qa, qw))
 
 
-@pytest.mark.parametrize("M,K,N,gw", [(16, 256, 128, 32), (200, 1024, 300, 32), (3, 320, 40, 128)])
-def test_gemm_codes_matches_oracle(lq, M, K, N, gw):
-    say(f"gemm codes M={M} K={K} N={N} gw={gw}")
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,K,N,gw", [(16, 256, 128, 32), (200, 1024, 300, 32), (3, 320, 40, 128),
+                                      (33, 96, 72, 32)])
+def test_gemm_codes_matches_oracle(lq, bits, M, K, N, gw):
+    say(f"gemm codes A{bits} M={M} K={K} N={N} gw={gw}")
     rng = synth.seeded_rng(synth.TEST, 120, M, K, N)
-    qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qmax = oracle.qmax_for_bits(bits)
+    qa = rng.integers(-qmax, qmax + 1, size=(M, K)).astype(np.int8)
     sa = rng.uniform(0.01, 2.0, size=(M, K // 32)).astype(np.float32)
     sa[0, 0] = 0.0
     w = synth.gaussian((N, K), 121, M, K, scale=0.02)
     codes, scales = pack(lq, w, gw)
     qw, sw = oracle.quant_weights(w, gw)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR, 1, M, K, N, 4)
-    lq.loopq_gemm_codes(dev(qa), dev(sa), codes, scales, gw, N, y, ws)
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR, 1, M, K, N, bits)
+    lq.loopq_gemm_codes(dev(qa), dev(sa), codes, scales, gw, N, y, ws, bits_a=bits)
     torch.cuda.synchronize()
     ref = oracle.rescale_dots(sa, oracle.group_dots(qa, qw), sw, gw)
     assert rel_err(y.cpu().numpy(), ref) <= Y_TOL
