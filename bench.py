@@ -86,7 +86,8 @@ def gemm_source_sha256():
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("bit_ptq_looped_amd/csrc/gemm_w4.hip", "bit_ptq_looped_amd/csrc/loopq_internal.h"):
+    for f in ("bit_ptq_looped_amd/csrc/gemm_f6.hip", "bit_ptq_looped_amd/csrc/gemm_tile.h",
+              "bit_ptq_looped_amd/csrc/loopq_internal.h"):
         with open(os.path.join(root, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
