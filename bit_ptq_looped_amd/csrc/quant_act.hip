@@ -19,6 +19,8 @@
 // group, 4 elements per lane, absmax reduced across the 8 lanes.
 #include "loopq_internal.h"
 
+#include <type_traits>
+
 namespace loopq {
 namespace {
 
@@ -151,11 +153,26 @@ __global__ __launch_bounds__(256) void quant_plain_kernel(QuantArgs a) {
   }
 }
 
-// Stage 1 of the transform for NI work items of one wave (items wave and
-// wave + 4): T[ii][rt] accumulates X_r * P2 over the 4-deep steps of b.
-template <int NRT, int N1, int N2, int NI>
+// LDS strides (elements) of P1, P2 and the X rows: P rows padded to 16 mod
+// 32 and X rows to 2 mod 32 so the 16 lanes of an MFMA operand read fall on
+// distinct banks.  For compile-time factor shapes the kernel uses these
+// constants (every LDS offset then folds into the instruction); the host plan
+// uses the same values for those shapes.
+constexpr int stride_to(int n, int rem) { return n + ((rem - n) % 32 + 32) % 32; }
+constexpr int p_stride(int n) { return n <= 16 ? 16 : stride_to(n, 16); }
+constexpr int x_stride(int n2) { return stride_to(n2, 2); }
+template <int N1, int N2>
+struct XStrides {
+  static constexpr int sp1 = N1 > 0 ? p_stride(N1) : 0;
+  static constexpr int sp2 = N2 > 0 ? p_stride(N2) : 0;
+  static constexpr int sx = N2 > 0 ? x_stride(N2) : 0;
+};
+
+// Stage 1 of the transform for NI work items of one wave (items wave,
+// wave + 4, ...): T[ii][rt] accumulates X_r * P2 over the 4-deep steps of b.
+template <int NRT, int N1, int N2, int NI, int NIM>
 __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, const float* sX,
-                                       int wave, int njt, int li, int lk, v4d (&T)[2][NRT]) {
+                                       int wave, int njt, int li, int lk, v4d (&T)[NIM][NRT]) {
   const int n1 = N1 > 0 ? N1 : a.n1;
   const int n2 = N2 > 0 ? N2 : a.n2;
   const float* pb[NI];
@@ -171,7 +188,8 @@ __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, con
     mj[ii] = j < n2 ? 0xffffffffu : 0u;
     pb[ii] = sP2 + (j < n2 ? j : 0);
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) xa[ii][rt] = sX + (r * n1 + min(rt * 16 + li, n1 - 1)) * a.sx;
+    for (int rt = 0; rt < NRT; ++rt)
+      xa[ii][rt] = sX + (r * n1 + min(rt * 16 + li, n1 - 1)) * (N2 > 0 ? XStrides<N1, N2>::sx : a.sx);
   }
   auto step = [&](int s) {
     const int b = 4 * s + lk;
@@ -181,7 +199,7 @@ __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, con
     for (int ii = 0; ii < NI; ++ii) {
       // addresses are clamped in bounds: load unconditionally, then zero the
       // lanes outside the matrix with an integer mask (no branch)
-      bv[ii] = (double)masked(pb[ii][b * a.sp2], mj[ii]);
+      bv[ii] = (double)masked(pb[ii][b * (N2 > 0 ? XStrides<N1, N2>::sp2 : a.sp2)], mj[ii]);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) av[ii][rt] = (double)masked(xa[ii][rt][b], mrow[rt]);
     }
@@ -202,9 +220,9 @@ __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, con
 // Stage 2 for the same items: x~[:, tile] = P1^T * T, B operands straight
 // from the stage-1 results (element e of tile rt is step s = 4 rt + e);
 // writes fp32 x~ into the flat rows of the X region.
-template <int NRT, int N1, int N2, int NI>
+template <int NRT, int N1, int N2, int NI, int NIM>
 __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, float* sX, int wave,
-                                       int njt, int li, int lk, const v4d (&T)[2][NRT]) {
+                                       int njt, int li, int lk, const v4d (&T)[NIM][NRT]) {
   const int n1 = N1 > 0 ? N1 : a.n1;
   const int n2 = N2 > 0 ? N2 : a.n2;
   const int K = n1 * n2;
@@ -219,7 +237,7 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
     for (int e = 0; e < 4; ++e) {
       const int s = 4 * rt + e;
       if (s < (n1 >> 2)) {
-        const float* pa = sP1 + (4 * s + lk) * a.sp1;
+        const float* pa = sP1 + (4 * s + lk) * (N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1);
         double av[NRT];
 #pragma unroll
         for (int it = 0; it < NRT; ++it) {
@@ -254,19 +272,23 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
 // Transform + quantize, NRT = ceil(n1 / 16) row tiles.  N1, N2 > 0 fix the
 // factor sizes at compile time (the k-loops then unroll fully, which keeps the
 // fp64 accumulators in place); N1 = N2 = 0 takes them from the arguments.
+// RS > 0 fixes the rows per chunk (the host plan uses the same value) and
+// enables the prefetch of the next chunk's X into registers; BF is the input
+// type when RS > 0 (1 bf16, 0 fp32).  NIM bounds the work items per wave.
 //
 // Dynamic LDS: P1 [n1][sp1] f32 at 0, P2 [n2][sp2] f32 at off_p2, and
 // X [R*n1][sx] f32 at off_x; after stage 1 the same region holds x~ as flat
 // fp32 rows [R][K].
 //
-// Work item = (row r of the chunk, 16-column tile jt of the n1 x n2 grid).
-// Stage 1 computes T[:, jt] = X_r * P2[:, jt] as NRT independent 16x16
-// accumulators (the reduction over b runs in 4-deep MFMA steps).  In the
-// result, lane l holds T[16 rt + 4 e + l/16][16 jt + l%16] in element e of
-// tile rt, which is exactly the B operand stage 2 needs from lane l at step
-// s = 4 rt + e (rows a = 4 s + l/16), so T stays in registers.  Stage 2 then
-// forms x~[:, jt] = P1^T * T with NRT accumulators over the i tiles.
-template <int NRT, int N1, int N2>
+// Work item = (row r of the chunk, 16-column tile jt of the n1 x n2 grid);
+// item i belongs to wave i % 4.  Stage 1 computes T[:, jt] = X_r * P2[:, jt]
+// as NRT independent 16x16 accumulators (the reduction over b runs in 4-deep
+// MFMA steps).  In the result, lane l holds T[16 rt + 4 e + l/16][16 jt +
+// l%16] in element e of tile rt, which is exactly the B operand stage 2 needs
+// from lane l at step s = 4 rt + e (rows a = 4 s + l/16), so T stays in
+// registers.  Stage 2 then forms x~[:, jt] = P1^T * T with NRT accumulators
+// over the i tiles.
+template <int NRT, int N1, int N2, int RS, int NIM, int BF>
 __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   float* sP1 = reinterpret_cast<float*>(lds);
@@ -279,16 +301,69 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const int n1 = N1 > 0 ? N1 : a.n1;
   const int n2 = N2 > 0 ? N2 : a.n2;
   const int K = n1 * n2;
-  const int R = a.R;
+  const int R = RS > 0 ? RS : a.R;
+  const bool bf16 = RS > 0 ? BF == 1 : a.bf16 != 0;
   const float qmaxf = (float)a.qmax;
   const int njt = (n2 + 15) >> 4;
 
-  for (int idx = tid; idx < n1 * n1; idx += 256) sP1[(idx / n1) * a.sp1 + idx % n1] = a.P1[idx];
-  for (int idx = tid; idx < n2 * n2; idx += 256) sP2[(idx / n2) * a.sp2 + idx % n2] = a.P2[idx];
+  const int sp1 = N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1;
+  const int sp2 = N2 > 0 ? XStrides<N1, N2>::sp2 : a.sp2;
+  const int sx = N2 > 0 ? XStrides<N1, N2>::sx : a.sx;
+  for (int idx = tid; idx < n1 * n1; idx += 256) sP1[(idx / n1) * sp1 + idx % n1] = a.P1[idx];
+  for (int idx = tid; idx < n2 * n2; idx += 256) sP2[(idx / n2) * sp2 + idx % n2] = a.P2[idx];
 
   const int li = lane & 15;  // row of A / column of B and of the result
   const int lk = lane >> 4;  // k within a 4-deep step; result rows lk + 4 e
   const int nchunks = (a.rows + R - 1) / R;
+
+  // X of a chunk: 4 consecutive b per thread-step (n2 % 4 == 0), element q
+  // of the chunk's rows*K/4 runs
+  auto x_src = [&](int row0, int q) -> int64_t { return (int64_t)row0 * K + (int64_t)q * 4; };
+  auto x_dst = [&](int q) -> float* {
+    const int e = q * 4;
+    const int r = e / K;
+    const int k = e - r * K;
+    return sX + (r * n1 + k / n2) * sx + k % n2;
+  };
+  auto put = [&](float* dst, const float4& v) {
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+  };
+  auto widen = [&](const uint2& u) {
+    return float4{bf16_bits_to_float(u.x & 0xffffu), bf16_bits_to_float(u.x >> 16),
+                  bf16_bits_to_float(u.y & 0xffffu), bf16_bits_to_float(u.y >> 16)};
+  };
+  // prefetch buffer for the next chunk's X (compile-time chunk shapes only)
+  constexpr int PF = RS > 0 ? (RS * N1 * N2 / 4 + 255) / 256 : 1;
+  typedef typename std::conditional<BF == 1, uint2, float4>::type raw_t;
+  raw_t pre[PF];
+  auto fetch = [&](int chunk) {
+    const int row0 = chunk * R;
+    const int nq = min(R, a.rows - row0) * K / 4;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int q = tid + 256 * i;
+      if (q < nq) {
+        if constexpr (BF == 1)
+          pre[i] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + x_src(row0, q));
+        else
+          pre[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + x_src(row0, q));
+      }
+    }
+  };
+  auto stash = [&](int chunk) {
+    const int row0 = chunk * R;
+    const int nq = min(R, a.rows - row0) * K / 4;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int q = tid + 256 * i;
+      if (q < nq) {
+        if constexpr (BF == 1)
+          put(x_dst(q), widen(pre[i]));
+        else
+          put(x_dst(q), pre[i]);
+      }
+    }
+  };
 
   // Each pass of the grid covers gridDim.x consecutive chunks.  Work-groups
   // land on the 8 XCDs in turn; slot numbering gives each XCD one run of
@@ -297,55 +372,61 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int slot = xcd * (G >> 3) + min(xcd, G & 7) + (int)(blockIdx.x >> 3);
+  if (RS > 0 && slot < nchunks) fetch(slot);
   for (int chunk = slot; chunk < nchunks; chunk += G) {
     const int row0 = chunk * R;
     const int rows = min(R, a.rows - row0);
     __syncthreads();  // previous chunk done with the x~ rows (and P staged on the first pass)
 
-    // ---- load X rows (4 consecutive b per thread-step; n2 % 4 == 0)
-    const int nq = rows * K / 4;
-    for (int q = tid; q < nq; q += 256) {
-      const int e = q * 4;
-      const int r = e / K;
-      const int k = e - r * K;
-      const int ra = r * n1 + k / n2;
-      const int b = k % n2;
-      const int64_t g = (int64_t)(row0 + r) * K + k;
-      float4 v;
-      if (a.bf16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + g);
-        v.x = bf16_bits_to_float(u.x & 0xffffu);
-        v.y = bf16_bits_to_float(u.x >> 16);
-        v.z = bf16_bits_to_float(u.y & 0xffffu);
-        v.w = bf16_bits_to_float(u.y >> 16);
-      } else {
-        v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + g);
+    // ---- X rows into LDS: from the prefetch registers, or loaded here
+    if constexpr (RS > 0) {
+      stash(chunk);
+    } else {
+      const int nq = rows * K / 4;
+      for (int q = tid; q < nq; q += 256) {
+        const int64_t g = x_src(row0, q);
+        float4 v;
+        if (bf16)
+          v = widen(*reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + g));
+        else
+          v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + g);
+        put(x_dst(q), v);
       }
-      float* dst = sX + ra * a.sx + b;
-      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
     }
     __syncthreads();
+    // the next chunk's X is in flight during both MFMA stages
+    if constexpr (RS > 0) {
+      if (chunk + G < nchunks) fetch(chunk + G);
+    }
 
-    // ---- stage 1 for the wave's items (at most two: the plan keeps R * njt <= 8);
-    // both items run in one loop so 2 * NRT accumulator chains interleave
+    // ---- stage 1 for the wave's items; all of them run in one loop so
+    // NI * NRT accumulator chains interleave
     const int items = rows * njt;
-    const int nmine = (wave < items) + (wave + 4 < items);
-    v4d T[2][NRT];
+    int nmine = 0;
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int ii = 0; ii < NIM; ++ii) nmine += (wave + 4 * ii < items) ? 1 : 0;
+    v4d T[NIM][NRT];
+#pragma unroll
+    for (int ii = 0; ii < NIM; ++ii)
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) T[ii][rt] = v4d{0.0, 0.0, 0.0, 0.0};
-    if (nmine == 2)
-      stage1<NRT, N1, N2, 2>(a, sP2, sX, wave, njt, li, lk, T);
-    else if (nmine == 1)
-      stage1<NRT, N1, N2, 1>(a, sP2, sX, wave, njt, li, lk, T);
+    switch (nmine) {
+      case 4: if constexpr (NIM >= 4) stage1<NRT, N1, N2, 4, NIM>(a, sP2, sX, wave, njt, li, lk, T); break;
+      case 3: if constexpr (NIM >= 3) stage1<NRT, N1, N2, 3, NIM>(a, sP2, sX, wave, njt, li, lk, T); break;
+      case 2: if constexpr (NIM >= 2) stage1<NRT, N1, N2, 2, NIM>(a, sP2, sX, wave, njt, li, lk, T); break;
+      case 1: stage1<NRT, N1, N2, 1, NIM>(a, sP2, sX, wave, njt, li, lk, T); break;
+      default: break;
+    }
     __syncthreads();  // every X read is done; x~ may now overwrite the region
 
     // ---- stage 2: x~[i][j] = sum_a P1[a][i] T[a][j], rounded once to fp32
-    if (nmine == 2)
-      stage2<NRT, N1, N2, 2>(a, sP1, sX, wave, njt, li, lk, T);
-    else if (nmine == 1)
-      stage2<NRT, N1, N2, 1>(a, sP1, sX, wave, njt, li, lk, T);
+    switch (nmine) {
+      case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM>(a, sP1, sX, wave, njt, li, lk, T); break;
+      case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM>(a, sP1, sX, wave, njt, li, lk, T); break;
+      case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM>(a, sP1, sX, wave, njt, li, lk, T); break;
+      case 1: stage2<NRT, N1, N2, 1, NIM>(a, sP1, sX, wave, njt, li, lk, T); break;
+      default: break;
+    }
     __syncthreads();
 
     // ---- quantize groups of the flat transformed rows
@@ -371,49 +452,74 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
 
 namespace {
 
-int stride_mod(int n, int mod, int rem) {
-  int s = n;
-  while (s % mod != rem) ++s;
-  return s;
-}
-
 int x_bytes_for(int R, int n1, int sx, int K) {
   int xb = R * n1 * sx * 4;
   if (xb < R * K * 4) xb = R * K * 4;
   return (xb + 15) / 16 * 16;
 }
 
+// Factor shapes of the Kronecker transforms in use (K = 256, 2048, 5632,
+// 2560, 6912, and a 32-wide test shape), each with its rows per chunk and the
+// most work items a wave then takes.  Chunk sizes make rows * ceil(n2 / 16)
+// items a multiple of the 4 waves where that fits (3 items per wave for
+// (64, 88) at 2 rows; (64, 108) has 7 per row and stays at one row).
+#define LOOPQ_SHAPES(X) \
+  X(16, 16, 16, 4)      \
+  X(32, 64, 4, 4)       \
+  X(64, 88, 2, 3)       \
+  X(40, 64, 3, 3)       \
+  X(64, 108, 1, 2)      \
+  X(4, 8, 16, 4)
+
 // LDS plan of the fused transform kernel: P1 and P2 with strides that put the
 // 16 lanes of an MFMA operand read on distinct banks, and R rows of X with a
 // stride of 2 mod 32 (the same region later holds the flat x~ rows).  R is
-// the largest row count whose R * ceil(n2/16) work items fit two per wave.
-// The bank padding of P1/P2 is dropped if that lets two work-groups share a
-// CU.  Returns false if one row does not fit.
+// the shape's chunk size above, else the largest row count whose
+// R * ceil(n2/16) work items fit two per wave.  The bank padding of P1/P2 is
+// dropped if that lets two work-groups share a CU.  Returns false if one row
+// does not fit.
 bool plan_quant(QuantArgs& a) {
   const int budget = 160 * 1024;
   const int njt = (a.n2 + 15) / 16;
-  int R = 8 / njt;
-  if (R < 1) return false;  // n2 > 128 is rejected earlier
-  if (R > 16) R = 16;
+  int R = 0, nim = 2;
+#define LOOPQ_PLAN_SHAPE(n1_, n2_, rs_, nim_) \
+  if (a.n1 == n1_ && a.n2 == n2_) {           \
+    R = rs_;                                  \
+    nim = nim_;                               \
+  }
+  LOOPQ_SHAPES(LOOPQ_PLAN_SHAPE)
+#undef LOOPQ_PLAN_SHAPE
+  const bool fixed = R > 0;
+  if (!fixed) {
+    R = 8 / njt;
+    if (R < 1) return false;  // n2 > 128 is rejected earlier
+    if (R > 16) R = 16;
+  }
+  if (R * njt > 4 * nim) return false;  // every work item must have a wave slot
   auto lds_for = [&](int sp1, int sp2, int sx, int r) {
     const int p2 = (a.n1 * sp1 * 4 + 15) / 16 * 16;
     const int px = (p2 + a.n2 * sp2 * 4 + 15) / 16 * 16;
     return px + x_bytes_for(r, a.n1, sx, a.K);
   };
-  int sp1 = a.n1 <= 16 ? 16 : stride_mod(a.n1, 32, 16);
-  int sp2 = a.n2 <= 16 ? 16 : stride_mod(a.n2, 32, 16);
-  int sx = stride_mod(a.n2, 32, 2);
-  if (lds_for(sp1, sp2, sx, R) > 80 * 1024 && lds_for(a.n1, a.n2, sx, R) <= 80 * 1024) {
-    sp1 = a.n1;
-    sp2 = a.n2;
+  int sp1 = p_stride(a.n1);
+  int sp2 = p_stride(a.n2);
+  int sx = x_stride(a.n2);
+  if (fixed) {
+    // compile-time shapes: the kernel has these strides built in
+    if (lds_for(sp1, sp2, sx, R) > budget) return false;
+  } else {
+    if (lds_for(sp1, sp2, sx, R) > 80 * 1024 && lds_for(a.n1, a.n2, sx, R) <= 80 * 1024) {
+      sp1 = a.n1;
+      sp2 = a.n2;
+    }
+    while (R > 1 && lds_for(sp1, sp2, sx, R) > budget) --R;
+    if (lds_for(sp1, sp2, sx, R) > budget) {
+      sp1 = a.n1;
+      sp2 = a.n2;
+      sx = a.n2;
+    }
+    if (lds_for(sp1, sp2, sx, R) > budget) return false;
   }
-  while (R > 1 && lds_for(sp1, sp2, sx, R) > budget) --R;
-  if (lds_for(sp1, sp2, sx, R) > budget) {
-    sp1 = a.n1;
-    sp2 = a.n2;
-    sx = a.n2;
-  }
-  if (lds_for(sp1, sp2, sx, R) > budget) return false;
   a.sp1 = sp1;
   a.sp2 = sp2;
   a.sx = sx;
@@ -447,28 +553,22 @@ hipError_t launch_quant_act(QuantArgs a, hipStream_t s) {
   }
   if (!plan_quant(a)) return hipErrorInvalidConfiguration;
   const void* fn = nullptr;
-#define LOOPQ_SHAPE(n1_, n2_)                                                          \
-  if (a.n1 == n1_ && a.n2 == n2_)                                                     \
-    fn = reinterpret_cast<const void*>(quant_xform_kernel<(n1_ + 15) / 16, n1_, n2_>);
-  // factor shapes of the Kronecker transforms in use (K = 256, 2048, 5632,
-  // 2560, 6912, and a 32-wide test shape)
-  LOOPQ_SHAPE(16, 16)
-  LOOPQ_SHAPE(32, 64)
-  LOOPQ_SHAPE(64, 88)
-  LOOPQ_SHAPE(40, 64)
-  LOOPQ_SHAPE(64, 108)
-  LOOPQ_SHAPE(4, 8)
-#undef LOOPQ_SHAPE
+#define LOOPQ_KERNEL_SHAPE(n1_, n2_, rs_, nim_)                                                     \
+  if (a.n1 == n1_ && a.n2 == n2_)                                                                   \
+    fn = a.bf16 ? reinterpret_cast<const void*>(quant_xform_kernel<(n1_ + 15) / 16, n1_, n2_, rs_, nim_, 1>) \
+                : reinterpret_cast<const void*>(quant_xform_kernel<(n1_ + 15) / 16, n1_, n2_, rs_, nim_, 0>);
+  LOOPQ_SHAPES(LOOPQ_KERNEL_SHAPE)
+#undef LOOPQ_KERNEL_SHAPE
   if (fn == nullptr) {
     switch ((a.n1 + 15) / 16) {
-      case 1: fn = reinterpret_cast<const void*>(quant_xform_kernel<1, 0, 0>); break;
-      case 2: fn = reinterpret_cast<const void*>(quant_xform_kernel<2, 0, 0>); break;
-      case 3: fn = reinterpret_cast<const void*>(quant_xform_kernel<3, 0, 0>); break;
-      case 4: fn = reinterpret_cast<const void*>(quant_xform_kernel<4, 0, 0>); break;
-      case 5: fn = reinterpret_cast<const void*>(quant_xform_kernel<5, 0, 0>); break;
-      case 6: fn = reinterpret_cast<const void*>(quant_xform_kernel<6, 0, 0>); break;
-      case 7: fn = reinterpret_cast<const void*>(quant_xform_kernel<7, 0, 0>); break;
-      case 8: fn = reinterpret_cast<const void*>(quant_xform_kernel<8, 0, 0>); break;
+      case 1: fn = reinterpret_cast<const void*>(quant_xform_kernel<1, 0, 0, 0, 2, 0>); break;
+      case 2: fn = reinterpret_cast<const void*>(quant_xform_kernel<2, 0, 0, 0, 2, 0>); break;
+      case 3: fn = reinterpret_cast<const void*>(quant_xform_kernel<3, 0, 0, 0, 2, 0>); break;
+      case 4: fn = reinterpret_cast<const void*>(quant_xform_kernel<4, 0, 0, 0, 2, 0>); break;
+      case 5: fn = reinterpret_cast<const void*>(quant_xform_kernel<5, 0, 0, 0, 2, 0>); break;
+      case 6: fn = reinterpret_cast<const void*>(quant_xform_kernel<6, 0, 0, 0, 2, 0>); break;
+      case 7: fn = reinterpret_cast<const void*>(quant_xform_kernel<7, 0, 0, 0, 2, 0>); break;
+      case 8: fn = reinterpret_cast<const void*>(quant_xform_kernel<8, 0, 0, 0, 2, 0>); break;
       default: return hipErrorInvalidConfiguration;
     }
   }
