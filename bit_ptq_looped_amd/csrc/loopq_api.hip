@@ -271,8 +271,13 @@ int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const floa
   ActBuffers b = carve(ws, ws_chunks, ws_rows, K, 0, rows);
   QuantArgs a = internal_quant_args(x, dtype, rows, K, P1, n1, P2, n2, clips, rows_per_clip,
                                     bits_a, b);
+  const bool small = rows <= kGemvMaxRows;  // decode: the small-row kernel on canonical codes
+  if (small) {
+    a.codes_fmt = kCodesCanonical;
+    a.scales_gm = 0;
+  }
   const int fmt = code_format(bits_a);
-  hipError_t e = prepare_weights(b, fmt, w_codes, K, N, s);
+  hipError_t e = small ? hipSuccess : prepare_weights(b, fmt, w_codes, K, N, s);
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   {
     TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, s);
@@ -281,7 +286,10 @@ int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const floa
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   {
     TimingScope ts(LOOPQ_KERNEL_GEMM, s);
-    e = run_gemm(b, fmt, rows, K, N, w_codes, w_scales, gw, y, nullptr, 0, s);
+    e = small ? launch_gemv(reinterpret_cast<const int8_t*>(b.codes), b.scales, rows, K, N,
+                            reinterpret_cast<const uint8_t*>(w_codes),
+                            reinterpret_cast<const __half*>(w_scales), gw, y, nullptr, 0, s)
+              : run_gemm(b, fmt, rows, K, N, w_codes, w_scales, gw, y, nullptr, 0, s);
   }
   return hip_status(e);
 }
@@ -297,7 +305,8 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
   DevicePipe* p = nullptr;
   if (device_pipe(&p, T + 1) != hipSuccess) return LOOPQ_ERR_HIP;
   const int fmt = code_format(bits_a);
-  if (prepare_weights(carve(ws, T, M, K, 0, 0), fmt, w_codes, K, N, s) != hipSuccess)
+  const bool small = M <= kGemvMaxRows;  // decode: the small-row kernel on canonical codes
+  if (!small && prepare_weights(carve(ws, T, M, K, 0, 0), fmt, w_codes, K, N, s) != hipSuccess)
     return LOOPQ_ERR_HIP;
   const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
   hipEvent_t start = p->events[T];
@@ -310,6 +319,10 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
     ActBuffers b = carve(ws, T, M, K, t, 0);
     const void* xt = reinterpret_cast<const char*>(x) + (size_t)t * M * K * esz;
     QuantArgs a = internal_quant_args(xt, dtype, M, K, P1, n1, P2, n2, one, M, bits_a, b);
+    if (small) {
+      a.codes_fmt = kCodesCanonical;
+      a.scales_gm = 0;
+    }
     hipError_t e;
     {
       TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, p->aux);
@@ -324,7 +337,11 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
     hipError_t e;
     {
       TimingScope ts(LOOPQ_KERNEL_GEMM, s);
-      e = run_gemm(b, fmt, M, K, N, w_codes, w_scales, gw, y + (size_t)t * M * N, nullptr, 0, s);
+      float* yt = y + (size_t)t * M * N;
+      e = small ? launch_gemv(reinterpret_cast<const int8_t*>(b.codes), b.scales, M, K, N,
+                              reinterpret_cast<const uint8_t*>(w_codes),
+                              reinterpret_cast<const __half*>(w_scales), gw, yt, nullptr, 0, s)
+                : run_gemm(b, fmt, M, K, N, w_codes, w_scales, gw, yt, nullptr, 0, s);
     }
     if (e != hipSuccess) return LOOPQ_ERR_HIP;
   }
@@ -517,6 +534,9 @@ int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
+  if (M <= kGemvMaxRows)  // decode: the small-row kernel reads the canonical codes directly
+    return hip_status(launch_gemv(a_codes, a_scales, M, K, N, reinterpret_cast<const uint8_t*>(w_codes),
+                                  reinterpret_cast<const __half*>(w_scales), group_w, y, nullptr, 0, s));
   ActBuffers b = carve(workspace, 1, M, K, 0, M);
   hipError_t e = launch_tile_codes(a_codes, a_scales, M, K, b.codes, fmt, b.scales, b.ld, s);
   if (e == hipSuccess) e = prepare_weights(b, fmt, w_codes, K, N, s);
@@ -552,6 +572,9 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
+  if (M <= kGemvMaxRows)  // the kernel the forward uses for this many rows
+    return hip_status(launch_gemv(a_codes, nullptr, M, K, N, reinterpret_cast<const uint8_t*>(w_codes),
+                                  nullptr, 32, nullptr, dots, 1, s));
   ActBuffers b = carve(workspace, 1, M, K, 0, M);
   hipError_t e = launch_tile_codes(a_codes, nullptr, M, K, b.codes, fmt, nullptr, b.ld, s);
   if (e == hipSuccess) e = prepare_weights(b, fmt, w_codes, K, N, s);

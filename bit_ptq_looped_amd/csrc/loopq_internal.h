@@ -155,6 +155,14 @@ hipError_t launch_gemm(const int8_t* a_tiled, const float* a_scales_gm, int ld_s
                        int N, const uint8_t* w_codes, const __half* w_scales, int gw, float* y,
                        int32_t* dots, int mode, hipStream_t s);
 
+// Small-row (decode) GEMM: rows <= kGemvMaxRows token rows, canonical int8
+// codes [R][K] with row-major steps [R][K/32], packed weights read directly.
+// mode 0: y [R][N]; mode 1: int32 group dots [R][N][K/32].
+constexpr int kGemvMaxRows = 16;
+hipError_t launch_gemv(const int8_t* a_canon, const float* a_scales, int R, int K, int N,
+                       const uint8_t* w_codes, const __half* w_scales, int gw, float* y,
+                       int32_t* dots, int mode, hipStream_t s);
+
 // status word shared by the synchronizing offline calls
 hipError_t reset_status(hipStream_t s);
 hipError_t read_status(int* host_status, hipStream_t s);

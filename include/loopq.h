@@ -169,7 +169,12 @@ int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, in
  * runs on `stream`; `stream` waits for the auxiliary work through events, so
  * the call keeps stream order for the caller (and can be captured into a HIP
  * graph).  WEIGHT_STATIONARY quantizes all T*M rows, then streams the weights
- * once for all loops; AUTO picks WEIGHT_STATIONARY.  Both give bitwise equal y.
+ * once for all loops; AUTO picks WEIGHT_STATIONARY.  A launch of at most 16
+ * rows (T*M, or M per loop) takes the small-row (decode) kernel, which reads
+ * the packed weights directly and forms the group dots on the VALU; larger
+ * ones take the MFMA GEMM.  Codes and steps are the same either way; y is
+ * deterministic and equal between schedules up to fp32 summation order
+ * (bitwise when both launch the same kernel).
  * Workspace: loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, ...). */
 int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
                              int32_t K, int32_t N,
@@ -183,7 +188,8 @@ int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
  * a_codes int8 [M][K], a_scales fp32 [M][K/32] (the layouts loopq_quant_act
  * writes); same weights and output as loopq_w4a4_linear.  bits_a selects
  * the kernel as in the linear: 4 (every code must lie in [-7, 7]; codes
- * outside give unspecified results) or 8 ([-127, 127]). */
+ * outside give unspecified results) or 8 ([-127, 127]); M <= 16 takes the
+ * small-row kernel. */
 int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M, int32_t K,
                          int32_t N, const void* w_codes, const void* w_scales, int32_t group_w,
                          int32_t bits_a, float* y, void* workspace, size_t workspace_bytes,
@@ -196,7 +202,8 @@ int32_t loopq_export_weights(const void* w_codes, const void* w_scales, int32_t 
 
 /* Test export: the exact int32 per-group dots d[m][n][j] = sum_{k in group j}
  * a_codes[m][k] * w[n][k], computed by the MFMA path of the bits_a kernel
- * (4: fp6 operands, codes in [-7, 7]; 8: INT8 operands), [M][N][K/32].
+ * (4: fp6 operands, codes in [-7, 7]; 8: INT8 operands; M <= 16: the
+ * small-row kernel's VALU dots, as the forward uses), [M][N][K/32].
  * a_codes int8 [M][K]; workspace as for loopq_workspace_bytes(LOOPQ_OP_LINEAR,
  * 1, M, K, N, bits_a). */
 int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N, int32_t bits_a,

@@ -237,11 +237,16 @@ def test_tiny_looped_end_to_end(lq, schedule):
         assert rel_err(y[t], ref[t]) <= Y_TOL
 
 
-def test_schedules_bitwise_equal_and_deterministic(lq):
+def test_schedules_agree_and_are_deterministic(lq):
+    # tiny workload, M = 16, T = 4: the loop-sequential schedule launches 16
+    # rows per loop (small-row kernel), the weight-stationary one 64 rows
+    # (MFMA GEMM); same codes, y equal up to fp32 summation order
     y1, _, _ = _tiny_gpu_and_oracle(lq, 1)
+    y1b, _, _ = _tiny_gpu_and_oracle(lq, 1)
     y2, _, _ = _tiny_gpu_and_oracle(lq, 2)
     y3, _, _ = _tiny_gpu_and_oracle(lq, 2)
-    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    assert rel_err(y1, y2) <= 1e-6
+    assert np.array_equal(y1.view(np.uint32), y1b.view(np.uint32))
     assert np.array_equal(y2.view(np.uint32), y3.view(np.uint32))
 
 
@@ -318,3 +323,29 @@ def test_fold_rejects_singular_factor(lq):
     with pytest.raises(lq.LoopQError) as e:
         lq.loopq_fold_weights(dev(W), dev(P1), dev(P2), out, ws)
     assert e.value.status == lq.LOOPQ_ERR_SINGULAR
+
+
+# ------------------------------------------------------------------------ decode (few rows)
+
+@pytest.mark.parametrize("schedule", [1, 2])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("act,K,N", [("up_in", 2048, 96), ("down_in", 5632, 72)])
+def test_decode_shapes(lq, act, K, N, M, bits, schedule):
+    """Decode-sized calls (at most 16 rows per launch take the small-row
+    kernel) at the block's factor shapes, against the oracle loop."""
+    say(f"decode {act} K={K} N={N} M={M} A{bits} schedule={schedule}")
+    wl = synth.ouro_block_workload(bits_a=bits, M=M, T=4)
+    P1, P2 = synth.factors_for(wl, act, K)
+    clips = synth.clips_for(wl, act)
+    bits16, x32 = synth.activations_for(wl, act, K)
+    w = synth.gaussian((N, K), 150, K, N, scale=0.02)
+    codes, scales = pack(lq, w, 32)
+    y = torch.empty((wl.T, M, N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, wl.T, M, K, N, bits)
+    lq.loopq_looped_forward(bf16_dev(bits16), dev(P1), dev(P2), clips, bits, codes, scales, 32, N, y,
+                            schedule, ws)
+    torch.cuda.synchronize()
+    qw, sw = oracle.quant_weights(w, 32)
+    ref = oracle.looped_forward(x32, P1, P2, clips, bits, qw, sw, 32)
+    assert rel_err(y.cpu().numpy(), ref) <= Y_TOL
