@@ -40,6 +40,10 @@ def parse():
                    help="only run this many steps of the W4A4 step (for rocprofv3), no JSON")
     p.add_argument("--profile-schedule", type=int, default=0,
                    help="schedule used by --profile-steps (0 auto, 1 loop-sequential, 2 weight-stationary)")
+    p.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    p.add_argument("--decode-steps", type=int, default=20)
+    p.add_argument("--profile-decode", type=int, default=0,
+                   help="only run this many decode loop-steps at M=1 (for rocprofv3), no JSON")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="with --profile-steps: first run one device-to-device copy of this many MiB "
                         "(a plain copy kernel of known size that calibrates HBM byte counters)")
@@ -141,6 +145,148 @@ def timed(lq, torch, mods, bits, schedule, steps, warmup, hooks=False):
     return (t1 - t0) / steps, per_kernel
 
 
+DECODE_LAYERS = 24
+
+
+def build_decode(lq, synth, torch, M, T, layers=DECODE_LAYERS):
+    """The Ouro-like block at decode size: per quantized input, one loop's
+    M rows (bf16), the input's factors and clips, and packed weights for
+    `layers` distinct layers.  Layer 0 packs the seeded weights; deeper layers
+    get seeded random packed bytes and fp16 steps drawn on the device (kernel
+    time does not depend on the values; parity runs on layer 0 shapes)."""
+    import numpy as np
+    wl = synth.ouro_block_workload(bits_a=4, M=M, T=T)
+    groups = {}
+    for lin in wl.linears:
+        groups.setdefault(lin.act, []).append(lin)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260)
+    mods = []
+    for act, lins in groups.items():
+        K = lins[0].K
+        W = np.concatenate([synth.weights_for(wl, lin) for lin in lins], axis=0)
+        N = W.shape[0]
+        P1, P2 = synth.factors_for(wl, act, K)
+        bits, _ = synth.activations_for(wl, act, K)
+        x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)  # [T][M][K]
+        weights = []
+        for layer in range(layers):
+            codes, scales = lq.empty_packed_weights(K, N, wl.group_w)
+            if layer == 0:
+                lq.loopq_pack_weights(torch.from_numpy(W).cuda(), wl.group_w, codes, scales)
+            else:
+                codes.copy_(torch.randint(0, 256, codes.shape, dtype=torch.uint8, device="cuda", generator=gen))
+                steps = (torch.rand(scales.numel() // 2, device="cuda", generator=gen) * 0.01 + 0.001)
+                scales.copy_(steps.to(torch.float16).view(torch.uint8))
+            weights.append((codes, scales))
+        m = Module(act, K, N, torch.from_numpy(P1).cuda(), torch.from_numpy(P2).cuda(),
+                   [float(c) for c in synth.clips_for(wl, act)], x, None, None)
+        m.weights = weights
+        m.y1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        m.yT = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+        m.ws1 = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, 1, M, K, N, 4)
+        m.wsT = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, 4)
+        mods.append(m)
+    return wl, mods
+
+
+def decode_loop_step(lq, mods, t):
+    """One loop-step of the decode stack: every layer's quantized inputs
+    (loop t's rows, loop t's clips) through that layer's weights."""
+    for layer in range(DECODE_LAYERS):
+        for m in mods:
+            codes, scales = m.weights[layer]
+            lq.loopq_looped_forward(m.x[t:t + 1], m.P1, m.P2, [m.clips[t]], 4, codes, scales, 32, m.N,
+                                    m.y1, lq.LOOPQ_SCHED_WEIGHT_STATIONARY, m.ws1)
+
+
+def decode_bench(lq, synth, torch, M, T, steps):
+    wl, mods = build_decode(lq, synth, torch, M, T)
+    per_layer_bytes = sum(m.N * m.K / 2 + 2 * m.N * (m.K // 32) for m in mods)
+    act_bytes = sum(2 * M * m.K + 4 * M * m.N for m in mods)
+    step_bytes = DECODE_LAYERS * (per_layer_bytes + act_bytes)
+    for t in range(2):
+        decode_loop_step(lq, mods, t % T)
+    torch.cuda.synchronize()
+    lq.loopq_timing_reset()
+    lq.loopq_timing_enable(True)
+    for i in range(steps):
+        decode_loop_step(lq, mods, i % T)
+    torch.cuda.synchronize()
+    lq.loopq_timing_enable(False)
+    kern = lq.loopq_timing_read(3)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        decode_loop_step(lq, mods, i % T)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    gemv_ms = kern[lq.LOOPQ_KERNEL_GEMM][0] / steps
+    quant_ms = kern[lq.LOOPQ_KERNEL_QUANT_TRANSFORM][0] / steps
+    # the same loop-steps replayed from a captured graph (launch gaps only):
+    # loops 0..T-1 once each per replay; outputs checked against eager runs
+    eager_ref = []
+    for t in range(T):
+        decode_loop_step(lq, mods, t)
+    torch.cuda.synchronize()
+    eager_ref = [m.y1.clone() for m in mods]
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for t in range(T):
+                decode_loop_step(lq, mods, t)
+    torch.cuda.current_stream().wait_stream(cap)
+    graph_ok = True
+    for _ in range(3):
+        for m in mods:
+            m.y1.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        graph_ok &= all(torch.equal(m.y1, r) for m, r in zip(mods, eager_ref))
+        decode_loop_step(lq, mods, 0)  # eager work between replays
+        torch.cuda.synchronize()
+    reps_g = max(1, steps // T)
+    t0 = time.perf_counter()
+    for _ in range(reps_g):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_wall = (time.perf_counter() - t0) / (reps_g * T)
+    del graph
+    # reuse run: layer 0 looped T times in one weight-stationary call per input
+    for m in mods:
+        codes, scales = m.weights[0]
+        lq.loopq_looped_forward(m.x, m.P1, m.P2, m.clips, 4, codes, scales, 32, m.N, m.yT,
+                                lq.LOOPQ_SCHED_WEIGHT_STATIONARY, m.wsT)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 50
+    for _ in range(reps):
+        for m in mods:
+            codes, scales = m.weights[0]
+            lq.loopq_looped_forward(m.x, m.P1, m.P2, m.clips, 4, codes, scales, 32, m.N, m.yT,
+                                    lq.LOOPQ_SCHED_WEIGHT_STATIONARY, m.wsT)
+    torch.cuda.synchronize()
+    reuse = (time.perf_counter() - t0) / reps
+    return {
+        "M": M, "layers": DECODE_LAYERS, "loops": T,
+        "ms_per_loop_step": wall * 1e3,
+        "gbps_per_loop_step": step_bytes / wall / 1e9,
+        "frac_hbm_peak": step_bytes / wall / 1e9 / HBM_PEAK_GBS,
+        "kernel_ms_per_loop_step": {"quant_transform": quant_ms, "gemv": gemv_ms},
+        "gemv_gbps": DECODE_LAYERS * per_layer_bytes / (gemv_ms * 1e-3) / 1e9,
+        "gemv_frac_hbm_peak": DECODE_LAYERS * per_layer_bytes / (gemv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "launches_per_loop_step": 2 * DECODE_LAYERS * len(mods),
+        "bytes_per_loop_step": step_bytes,
+        "graph_ms_per_loop_step": graph_wall * 1e3,
+        "graph_gbps_per_loop_step": step_bytes / graph_wall / 1e9,
+        "graph_frac_hbm_peak": step_bytes / graph_wall / 1e9 / HBM_PEAK_GBS,
+        "graph_replays_match_eager": bool(graph_ok),
+        "reuse_one_layer_T_loops_ms": reuse * 1e3,
+        "reuse_weight_bytes_per_loop": per_layer_bytes / T,
+    }
+
+
 def cpu_baseline(wl, mods_meta, rows_hint):
     """The oracle, untuned, on a bounded sample: `rows` token rows of loop 0
     of every quantized input (transform + Eq.(4) RTN + integer group dots +
@@ -201,6 +347,14 @@ def main():
         m.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
+    if args.profile_decode:
+        _, dmods = build_decode(lq, synth, torch, 1, 4)
+        torch.cuda.synchronize()
+        for i in range(args.profile_decode):
+            decode_loop_step(lq, dmods, i % 4)
+        torch.cuda.synchronize()
+        print(f"profiled {args.profile_decode} decode loop-steps", flush=True)
+        return
     if args.profile_steps:
         if args.copy_mib:
             src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -272,6 +426,10 @@ def main():
                  "gemm_ms_per_step": kern_a8[lq.LOOPQ_KERNEL_GEMM][0] / args.steps},
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.no_decode:
+        del mods
+        torch.cuda.empty_cache()
+        out["decode"] = [decode_bench(lq, synth, torch, Md, 4, args.decode_steps) for Md in (1, 4, 16)]
     if not args.no_cpu_baseline:
         groups = {}
         for lin in wl.linears:

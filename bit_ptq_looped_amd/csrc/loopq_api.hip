@@ -93,6 +93,7 @@ int code_format(int bits_a) { return bits_a == 4 && !force_int8_gemm() ? kCodesT
 //   codes  : chunks * padded(rows) rows in the tiled layout, row_bytes(K)
 //            per row (enough for either tiled format)
 //   scales : fp32 group-major, chunks * padded(rows) columns
+//   xt     : fp32 x~ rows of the few-row transform (launches of <= 16 rows)
 //   wexp   : weights expanded to fp6 operands (W4A4 kernel only)
 // The same region also holds all chunks * rows rows as one contiguous tiled
 // matrix (padded(chunks * rows) <= chunks * padded(rows)).
@@ -100,6 +101,7 @@ struct ActBuffers {
   void* codes;
   float* scales;
   void* wexp;
+  float* xt;  // x~ rows of the few-row transform
   int ld;
 };
 
@@ -116,8 +118,15 @@ size_t scales_region(int64_t chunks, int64_t rows, int64_t K) {
 size_t wexp_region(int64_t K, int64_t N, int fmt) {
   return fmt == kCodesTiledF6 ? align256((size_t)(padded_cols(N) / 32 * group_pairs(K) * kF6BlockBytes)) : 0;
 }
+// x~ rows of the few-row transform: a launch of at most kGemvMaxRows rows
+size_t xt_region(int64_t chunks, int64_t rows, int64_t K) {
+  if (rows > kGemvMaxRows) return 0;
+  const int64_t r = chunks * rows < kGemvMaxRows ? chunks * rows : kGemvMaxRows;
+  return align256((size_t)(r * K * 4));
+}
 size_t act_bytes(int64_t chunks, int64_t rows, int64_t K, int64_t N, int fmt) {
-  return codes_region(chunks, rows, K) + scales_region(chunks, rows, K) + wexp_region(K, N, fmt);
+  return codes_region(chunks, rows, K) + scales_region(chunks, rows, K) + wexp_region(K, N, fmt) +
+         xt_region(chunks, rows, K);
 }
 
 // buffers of chunk c (rows rows each), or with all_rows > 0 the whole
@@ -127,7 +136,9 @@ ActBuffers carve(void* ws, int64_t chunks, int64_t rows, int64_t K, int64_t c, i
   char* base = reinterpret_cast<char*>(ws);
   const int64_t mp = padded_rows(rows);
   float* scales0 = reinterpret_cast<float*>(base + codes_region(chunks, rows, K));
-  b.wexp = base + codes_region(chunks, rows, K) + scales_region(chunks, rows, K);
+  // regions: codes | scales | x~ rows (few-row path) | expanded weights
+  b.xt = reinterpret_cast<float*>(base + codes_region(chunks, rows, K) + scales_region(chunks, rows, K));
+  b.wexp = reinterpret_cast<char*>(b.xt) + xt_region(chunks, rows, K);
   if (all_rows > 0) {
     b.codes = base;
     b.scales = scales0;
@@ -281,7 +292,7 @@ int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const floa
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   {
     TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, s);
-    e = launch_quant_act(a, s);
+    e = small ? launch_quant_act_few(a, b.xt, s) : launch_quant_act(a, s);
   }
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   {
@@ -326,7 +337,7 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
     hipError_t e;
     {
       TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, p->aux);
-      e = launch_quant_act(a, p->aux);
+      e = small ? launch_quant_act_few(a, b.xt, p->aux) : launch_quant_act(a, p->aux);
     }
     if (e != hipSuccess) return LOOPQ_ERR_HIP;
     if (hipEventRecord(p->events[t], p->aux) != hipSuccess) return LOOPQ_ERR_HIP;

@@ -128,6 +128,11 @@ struct QuantArgs {
 hipError_t launch_quant_act(QuantArgs a, hipStream_t s);
 // true if the fused transform kernel's LDS plan fits one work-group
 bool quant_plan_fits(int K, int n1, int n2);
+// Few rows (decode): with a transform of one of the compile-time factor
+// shapes, one work-group per (row, 16-column tile) forms x~ into xt_buf
+// ([rows][K] fp32, bitwise the chunked kernel's x~) and a second launch
+// quantizes it; otherwise the same as launch_quant_act.
+hipError_t launch_quant_act_few(QuantArgs a, float* xt_buf, hipStream_t s);
 
 hipError_t launch_pack_weights(const float* w, int K, int N, int gw, uint8_t* codes,
                                __half* scales, hipStream_t s);

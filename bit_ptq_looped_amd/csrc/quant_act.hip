@@ -448,6 +448,101 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   }
 }
 
+// Few-row form of the transform (decode: a handful of rows).  One
+// work-group per work item (row r, 16-column tile jt): wave w computes the
+// stage-1 tile T[16w .. 16w + 15][tile jt] with the full reduction over b,
+// stores it in LDS, and after a barrier computes the stage-2 tile x~[16w ..
+// 16w + 15][tile jt] with the full reduction over a.  Operands and MFMA order
+// are those of the chunked kernel, so x~ is bitwise the same; it is written
+// rounded to fp32 to `xt` ([rows][K]) and quantized by a second launch.
+// LDS: P1 [n1][sp1] f32, the P2 columns of the tile [n2][16] f32, the row of
+// X [n1][sx] f32 and T [n1][16] f64.
+template <int NRT, int N1, int N2>
+__global__ __launch_bounds__(256) void xform_items_kernel(QuantArgs a, float* __restrict__ xt) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int n1 = N1, n2 = N2, K = N1 * N2;
+  constexpr int sp1 = XStrides<N1, N2>::sp1, sx = XStrides<N1, N2>::sx;
+  constexpr int njt = (N2 + 15) / 16;
+  constexpr int off_p2 = (n1 * sp1 * 4 + 15) / 16 * 16;
+  constexpr int off_x = off_p2 + n2 * 16 * 4;
+  constexpr int off_t = (off_x + n1 * sx * 4 + 15) / 16 * 16;
+  float* sP1 = reinterpret_cast<float*>(lds);
+  float* sP2 = reinterpret_cast<float*>(lds + off_p2);
+  float* sX = reinterpret_cast<float*>(lds + off_x);
+  double* sT = reinterpret_cast<double*>(lds + off_t);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 15;
+  const int lk = lane >> 4;
+  const int r = blockIdx.x / njt;
+  const int jt = blockIdx.x - r * njt;
+
+  for (int idx = tid; idx < n1 * n1; idx += 256) sP1[(idx / n1) * sp1 + idx % n1] = a.P1[idx];
+  for (int idx = tid; idx < n2 * 16; idx += 256) {
+    const int b = idx >> 4, j = jt * 16 + (idx & 15);
+    sP2[idx] = j < n2 ? a.P2[b * n2 + j] : 0.0f;
+  }
+  for (int q = tid; q < K / 4; q += 256) {
+    const int k = q * 4;
+    const int64_t gi = (int64_t)r * K + k;
+    float4 v;
+    if (a.bf16) {
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + gi);
+      v = float4{bf16_bits_to_float(u.x & 0xffffu), bf16_bits_to_float(u.x >> 16),
+                 bf16_bits_to_float(u.y & 0xffffu), bf16_bits_to_float(u.y >> 16)};
+    } else {
+      v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + gi);
+    }
+    float* dst = sX + (k / n2) * sx + k % n2;
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+  }
+  __syncthreads();
+
+  // stage 1: T[rt] = X_r * P2[:, tile], steps of b in order (as the chunked kernel)
+  for (int rt = wave; rt < NRT; rt += 4) {
+    v4d T = {0.0, 0.0, 0.0, 0.0};
+    const float* xa = sX + min(rt * 16 + li, n1 - 1) * sx;
+    const uint32_t mrow = (rt * 16 + li < n1) ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int st = 0; st < N2 / 4; ++st) {
+      const int b = 4 * st + lk;
+      const double av = (double)masked(xa[b], mrow);
+      const double bv = (double)sP2[b * 16 + li];  // zero past n2
+      T = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, T, 0, 0, 0);
+    }
+    // result element e of lane l: row 16 rt + 4 e + l / 16, column l % 16
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = rt * 16 + 4 * e + lk;
+      if (row < n1) sT[row * 16 + li] = T[e];
+    }
+  }
+  __syncthreads();
+
+  // stage 2: x~[it][tile] = sum_a P1[a][it] T[a][tile], steps of a in order
+  for (int it = wave; it < NRT; it += 4) {
+    v4d o = {0.0, 0.0, 0.0, 0.0};
+    const int i = it * 16 + li;
+    const uint32_t mi = i < n1 ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int st = 0; st < N1 / 4; ++st) {
+      const double av = (double)masked(sP1[(4 * st + lk) * sp1 + min(i, n1 - 1)], mi);
+      const double bv = sT[(4 * st + lk) * 16 + li];
+      o = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, o, 0, 0, 0);
+    }
+    const int j = jt * 16 + li;
+    if (j < n2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int io = it * 16 + 4 * e + lk;
+        if (io < n1) xt[(int64_t)r * K + io * n2 + j] = (float)o[e];  // one rounding to fp32
+      }
+    }
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -540,6 +635,45 @@ bool quant_plan_fits(int K, int n1, int n2) {
   a.n1 = n1;
   a.n2 = n2;
   return plan_quant(a);
+}
+
+bool xform_items_supported(int n1, int n2) {
+#define LOOPQ_ITEM_SHAPE(n1_, n2_, rs_, nim_) \
+  if (n1 == n1_ && n2 == n2_) return true;
+  LOOPQ_SHAPES(LOOPQ_ITEM_SHAPE)
+#undef LOOPQ_ITEM_SHAPE
+  return false;
+}
+
+hipError_t launch_quant_act_few(QuantArgs a, float* xt_buf, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.P1 != nullptr && xform_items_supported(a.n1, a.n2)) {
+    const void* fn = nullptr;
+    int lds = 0;
+#define LOOPQ_ITEM_KERNEL(n1_, n2_, rs_, nim_)                                                      \
+    if (a.n1 == n1_ && a.n2 == n2_) {                                                               \
+      fn = reinterpret_cast<const void*>(xform_items_kernel<(n1_ + 15) / 16, n1_, n2_>);           \
+      constexpr int sp1 = XStrides<n1_, n2_>::sp1, sx = XStrides<n1_, n2_>::sx;                    \
+      constexpr int off_x = (n1_ * sp1 * 4 + 15) / 16 * 16 + n2_ * 16 * 4;                         \
+      lds = (off_x + n1_ * sx * 4 + 15) / 16 * 16 + n1_ * 16 * 8;                                 \
+    }
+    LOOPQ_SHAPES(LOOPQ_ITEM_KERNEL)
+#undef LOOPQ_ITEM_KERNEL
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    const int items = a.rows * ((a.n2 + 15) / 16);
+    void* args[] = {&a, &xt_buf};
+    e = hipLaunchKernel(fn, dim3(items), dim3(256), args, lds, s);
+    if (e != hipSuccess) return e;
+    // then quantize the transformed rows as plain fp32 input
+    QuantArgs q = a;
+    q.x = xt_buf;
+    q.bf16 = 0;
+    q.P1 = q.P2 = nullptr;
+    q.n1 = q.n2 = 0;
+    return launch_quant_act(q, s);
+  }
+  return launch_quant_act(a, s);
 }
 
 hipError_t launch_quant_act(QuantArgs a, hipStream_t s) {
