@@ -90,8 +90,7 @@ def gemm_source_sha256():
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("bit_ptq_looped_amd/csrc/gemm_f6.hip", "bit_ptq_looped_amd/csrc/gemm_tile.h",
-              "bit_ptq_looped_amd/csrc/loopq_internal.h"):
+    for f in ("bit_ptq_looped_amd/csrc/gemm_f6.hip", "bit_ptq_looped_amd/csrc/gemm_tile.h"):
         with open(os.path.join(root, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -299,7 +298,7 @@ def cpu_baseline(wl, mods_meta, rows_hint):
     import oracle
     from bit_ptq_looped_amd import synth
 
-    rows = rows_hint or 128
+    rows = rows_hint or 256
     prepared = []
     for act, K, lins in mods_meta:
         W = np.concatenate([synth.weights_for(wl, lin) for lin in lins], axis=0)
