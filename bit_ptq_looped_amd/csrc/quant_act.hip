@@ -49,33 +49,41 @@ __device__ __forceinline__ float group8_max(float v) {
 // consecutive in the wave (lane % 8 = position of the 4-element run).
 // Returns the 4 codes packed as int8 bytes; writes the step to *step.
 //
-// Codes are clamp(rint(fl32(x / s)), -qmax, qmax).  The quotient is formed as
-// p = fl32(x * r) with r = fl32(1 / s) (both correctly rounded): |p - x/s| and
-// |fl32(x/s) - x/s| are each below 2^-23 |x/s|, so below the clamp (|x/s| <
-// qmax + 1 <= 128) p and fl32(x/s) differ by less than 2^-15, and rint gives
-// the same integer unless p lies within 2^-14 of a half-integer.  Those runs,
-// and any run whose r is not finite (s below 2^-128), are redone with the
+// The step: base = fl32(absmax / qmax) is formed as q0 = fl32(absmax * rq)
+// with rq = fl32(1 / qmax), then one FMA correction q0 + (absmax - q0 qmax) rq;
+// for qmax = 7 and 127 this equals the correctly rounded quotient for every
+// finite non-negative fp32 absmax (checked exhaustively over all of them).
+// s = fl32(c * base).
+//
+// The codes: clamp(rint(fl32(x / s)), -qmax, qmax).  The quotient is formed
+// as p = fl32(x * r) with r the hardware reciprocal of s (within 1 ulp):
+// |p - x/s| < 3 * 2^-24 |x/s| and |fl32(x/s) - x/s| <= 2^-24 |x/s|, so below
+// the clamp (|x/s| < qmax + 1 <= 128) p and fl32(x/s) differ by less than
+// 2^-14, and rint gives the same integer unless p lies within 2^-14 of a
+// half-integer.  Those runs, and any run whose r is not a positive finite
+// normal-range value (s outside about [2^-126, 2^126]), are redone with the
 // correctly rounded division.  Above the clamp both sides saturate alike.
-__device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf, float* step) {
+__device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf, float rq, float* step) {
   float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   amax = group8_max(amax);
-  const float base = amax / qmaxf;  // correctly rounded fp32 division
+  const float q0 = amax * rq;
+  const float base = __builtin_fmaf(__builtin_fmaf(-q0, qmaxf, amax), rq, q0);  // = fl32(amax / qmax)
   const float s = clip * base;      // one fp32 product
   *step = s;
   if (!(s > 0.0f)) return 0u;
-  const float r = 1.0f / s;         // correctly rounded
+  const float r = __builtin_amdgcn_rcpf(s);
   const float e[4] = {v.x, v.y, v.z, v.w};
   uint32_t packed = 0u;
-  bool exact = !(r < 3.0e38f);
+  bool exact = !(r > 1.0e-37f && r < 1.0e37f);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float p = e[i] * r;
-    const float rq = __builtin_rintf(p);
-    exact |= (fabsf(p) < qmaxf + 1.0f) && (fabsf(p - rq) > 0.5f - 6.103515625e-05f);
-    const float q = fminf(fmaxf(rq, -qmaxf), qmaxf);
+    const float rq_ = __builtin_rintf(p);
+    exact |= (fabsf(p) < qmaxf + 1.0f) && (fabsf(p - rq_) > 0.5f - 6.103515625e-05f);
+    const float q = fminf(fmaxf(rq_, -qmaxf), qmaxf);
     packed |= (uint32_t)((int)q & 0xff) << (8 * i);
   }
-  if (exact) {  // rare: near a rounding boundary, or s tiny
+  if (exact) {  // rare: near a rounding boundary, or s extreme
     packed = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -124,6 +132,7 @@ __global__ __launch_bounds__(256) void quant_plain_kernel(QuantArgs a) {
   const int K = a.K;
   const int64_t total = (int64_t)a.rows * K;  // K % 32 == 0, so total % 256 may be 0 or 128.. handled per lane
   const float qmaxf = (float)a.qmax;
+  const float rqmax = 1.0f / qmaxf;
   // each wave takes one contiguous range of 256-element steps, so the lines
   // of the tiled code layout are completed by one wave (one L2)
   const int64_t nsteps = (total + 255) / 256;
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(256) void quant_plain_kernel(QuantArgs a) {
     }
     const float clip = a.clips.c[row / a.rows_per_clip];
     float s;
-    const uint32_t packed = quantize4(v, clip, qmaxf, &s);
+    const uint32_t packed = quantize4(v, clip, qmaxf, rqmax, &s);
     if (valid) store_run(a, row, k0, packed, s, (lane & 7) == 0, v);
   }
 }
@@ -304,6 +313,7 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const int R = RS > 0 ? RS : a.R;
   const bool bf16 = RS > 0 ? BF == 1 : a.bf16 != 0;
   const float qmaxf = (float)a.qmax;
+  const float rqmax = 1.0f / qmaxf;
   const int njt = (n2 + 15) >> 4;
 
   const int sp1 = N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1;
@@ -442,7 +452,7 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
       const int row = row0 + r;
       const float clip = a.clips.c[row / a.rows_per_clip];
       float s;
-      const uint32_t packed = quantize4(v, clip, qmaxf, &s);
+      const uint32_t packed = quantize4(v, clip, qmaxf, rqmax, &s);
       if (valid) store_run(a, row, k0, packed, s, (lane & 7) == 0, v);
     }
   }
