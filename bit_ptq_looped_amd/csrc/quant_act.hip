@@ -200,17 +200,32 @@ __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, con
     for (int rt = 0; rt < NRT; ++rt)
       xa[ii][rt] = sX + (r * n1 + min(rt * 16 + li, n1 - 1)) * (N2 > 0 ? XStrides<N1, N2>::sx : a.sx);
   }
-  auto step = [&](int s) {
+  // raw (fp32) operands of one 4-deep step; the compile-time form reads the
+  // next step's operands before converting and multiplying the current
+  // one, so the LDS latency hides behind the MFMAs
+  struct Raw {
+    float b[NI];
+    float a[NI][NRT];
+  };
+  auto fetch = [&](int s, Raw& o) {
     const int b = 4 * s + lk;
-    double bv[NI];
-    double av[NI][NRT];
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
       // addresses are clamped in bounds: load unconditionally, then zero the
       // lanes outside the matrix with an integer mask (no branch)
-      bv[ii] = (double)masked(pb[ii][b * (N2 > 0 ? XStrides<N1, N2>::sp2 : a.sp2)], mj[ii]);
+      o.b[ii] = masked(pb[ii][b * (N2 > 0 ? XStrides<N1, N2>::sp2 : a.sp2)], mj[ii]);
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) av[ii][rt] = (double)masked(xa[ii][rt][b], mrow[rt]);
+      for (int rt = 0; rt < NRT; ++rt) o.a[ii][rt] = masked(xa[ii][rt][b], mrow[rt]);
+    }
+  };
+  auto mma = [&](const Raw& o) {
+    double bv[NI];
+    double av[NI][NRT];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      bv[ii] = (double)o.b[ii];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) av[ii][rt] = (double)o.a[ii][rt];
     }
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii)
@@ -219,10 +234,20 @@ __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, con
         T[ii][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ii][rt], bv[ii], T[ii][rt], 0, 0, 0);
   };
   if constexpr (N2 > 0) {  // fully unrolled: the accumulators stay in place
+    Raw buf[2];
+    fetch(0, buf[0]);
 #pragma unroll
-    for (int s = 0; s < N2 / 4; ++s) step(s);
+    for (int s = 0; s < N2 / 4; ++s) {
+      if (s + 1 < N2 / 4) fetch(s + 1, buf[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(buf[s & 1]);
+    }
   } else {
-    for (int s = 0; s < (n2 >> 2); ++s) step(s);
+    for (int s = 0; s < (n2 >> 2); ++s) {
+      Raw o;
+      fetch(s, o);
+      mma(o);
+    }
   }
 }
 
@@ -240,26 +265,45 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
   for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
     for (int it = 0; it < NRT; ++it) o[ii][it] = v4d{0.0, 0.0, 0.0, 0.0};
+  // step s = 4 rt + e reduces over rows a = 4 s + l/16; as in stage 1 the
+  // compile-time form reads the next step's P1 operands before multiplying
+  auto fetch = [&](int s, float (&o2)[NRT]) {
+    const float* pa = sP1 + (4 * s + lk) * (N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1);
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
+    for (int it = 0; it < NRT; ++it) {
+      const int i = it * 16 + li;
+      o2[it] = masked(pa[min(i, n1 - 1)], i < n1 ? 0xffffffffu : 0u);
+    }
+  };
+  auto mma = [&](int s, const float (&raw)[NRT]) {
+    double av[NRT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int s = 4 * rt + e;
+    for (int it = 0; it < NRT; ++it) av[it] = (double)raw[it];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+      for (int it = 0; it < NRT; ++it)
+        o[ii][it] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[it], T[ii][s >> 2][s & 3], o[ii][it], 0, 0, 0);
+  };
+  if constexpr (N1 > 0) {
+    float buf[2][NRT];
+    fetch(0, buf[0]);
+#pragma unroll
+    for (int s = 0; s < N1 / 4; ++s) {
+      if (s + 1 < N1 / 4) fetch(s + 1, buf[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(s, buf[s & 1]);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4 * NRT; ++s) {
       if (s < (n1 >> 2)) {
-        const float* pa = sP1 + (4 * s + lk) * (N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1);
-        double av[NRT];
-#pragma unroll
-        for (int it = 0; it < NRT; ++it) {
-          const int i = it * 16 + li;
-          av[it] = (double)masked(pa[min(i, n1 - 1)], i < n1 ? 0xffffffffu : 0u);
-        }
-#pragma unroll
-        for (int ii = 0; ii < NI; ++ii)
-#pragma unroll
-          for (int it = 0; it < NRT; ++it)
-            o[ii][it] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[it], T[ii][rt][e], o[ii][it], 0, 0, 0);
+        float raw[NRT];
+        fetch(s, raw);
+        mma(s, raw);
       }
     }
+  }
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
     const int item = wave + 4 * ii;
