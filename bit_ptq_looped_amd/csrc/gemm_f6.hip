@@ -16,7 +16,9 @@
 // weight operand with one half of its lanes zeroed gives one group's dots,
 // already as exact fp32, so the fold needs no conversion: one FMA per output
 // and group, with the step products s_a * s_w from fp32 outer-product MFMAs
-// as in the INT8 kernel.  Scales of the instruction are fixed at 2^0.
+// as in the INT8 kernel.  The zeroing is done by the instruction's own E8M0
+// block scales (2^-127 on the weight lanes of the other group), so the
+// operands go in as loaded.
 //
 // Tiling, operand orientation, tile order and output store are those of the
 // INT8 kernel (gemm_tile.h).  The K loop runs over group pairs with two
@@ -41,11 +43,21 @@ struct F6Stage {
   uint32_t sw[2];  // raw fp16 weight step per group of the pair
 };
 
-__device__ __forceinline__ v8i f6_operand(const v4i& a, const uint2& b, bool keep) {
-  // e2m3 operands use the first six registers; lanes that do not carry the
-  // group being multiplied supply zeros
-  return v8i{keep ? a[0] : 0, keep ? a[1] : 0, keep ? a[2] : 0, keep ? a[3] : 0,
-             keep ? (int)b.x : 0, keep ? (int)b.y : 0, 0, 0};
+// e2m3 operands use the first six registers of the operand tuple
+__device__ __forceinline__ v8i f6_operand(const v4i& a, const uint2& b) {
+  return v8i{a[0], a[1], a[2], a[3], (int)b.x, (int)b.y, 0, 0};
+}
+
+// A 32x32 result tile gives lane l the 16 elements e at rows
+// 8 (e / 4) + 4 (l / 32) + e % 4 of column l % 32.  coef_row(i) is the row of
+// the next element (e + 1 mod 16) of the lane holding row i.  The coefficient
+// MFMA is fed the weight step of row coef_row(i) in place of row i, so its
+// element e is the coefficient of result element e + 1.  The fold then pairs
+// result register e + 1 with coefficient register e: as both tuples are
+// aligned, the two sit at opposite register parity, and the FMA never reads
+// all three operands from one parity (which costs about 1.7x its issue time).
+__device__ __forceinline__ int coef_row(int i) {
+  return (i & 3) < 3 ? i + 1 : ((((i >> 3) + 1) & 3) << 3) | (i & 4);
 }
 
 template <int MODE>
@@ -81,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t sw_rs = make_rsrc(g.sw, MODE == 0 ? (uint32_t)(nlast + 1) * (uint32_t)Gw * 64u : 0u);
   const int sa_off0 = (min((m_base >> 5) + h, mlast) * 32 + c) * 4;
   const int sa_off1 = (min((m_base >> 5) + 1 - h, mlast) * 32 + c) * 4;
-  const int sw_off = (min((n_base >> 5) + h, nlast) * Gw * 32 + step_slot(c)) * 2;
+  const int sw_off = (min((n_base >> 5) + h, nlast) * Gw * 32 + step_slot(coef_row(c))) * 2;
 
   auto load = [&](int p, F6Stage& s) {
     const int po = p * kF6BlockBytes;
@@ -112,15 +124,22 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[t][u][e] = 0.0f;
 
-  auto mfma = [&](const v8i& w, const v8i& x) {
+  // Block scales of the weight operand (E8M0, one per lane = one output
+  // column and K-half): 2^0 on the half that carries the group being
+  // multiplied, 2^-127 on the other.  The other group's dot then adds at most
+  // 1568 * 2^-127 < 2^-116, which leaves a nonzero integer dot unchanged in
+  // fp32 and truncates to 0 where the dot is 0.
+  const int wscale[2] = {h == 0 ? 127 : 0, h == 1 ? 127 : 0};
+  auto mfma = [&](const v8i& w, const v8i& x, int q) {
     const v16f z = {};
-    // formats: 2 = e2m3 for both operands; scales 127 = 2^0
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, z, 2, 2, 0, 127, 0, 127);
+    // formats: 2 = e2m3 for both operands; activation scale 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, z, 2, 2, 0, wscale[q], 0, 127);
   };
   auto fold = [&](const v16f& d, const v32f& cf, int half, int t, int u, int j) {
     if (MODE == 0) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[t][u][e] = __builtin_fmaf(d[e], cf[16 * half + e], acc[t][u][e]);
+      for (int e = 0; e < 16; ++e)
+        acc[t][u][e] = __builtin_fmaf(d[e], cf[16 * half + ((e + 15) & 15)], acc[t][u][e]);
     } else {
       const int row = m_base + 32 * t + c;
       if (row < g.M) {
@@ -141,20 +160,19 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
       cA = __builtin_amdgcn_mfma_f32_32x32x1f32(swf, s.sa[q][0], z, 0, 0, 0);  // (t0,u0) | (t1,u1)
       cB = __builtin_amdgcn_mfma_f32_32x32x1f32(swf, s.sa[q][1], z, 0, 0, 0);  // (t1,u0) | (t0,u1)
     }
-    const bool keep = h == q;
-    const v8i w0 = f6_operand(s.wa[0], s.wc[0], keep);
-    const v8i w1 = f6_operand(s.wa[1], s.wc[1], keep);
-    const v16f d00 = mfma(w0, x[0]);
-    const v16f d01 = mfma(w1, x[0]);
+    const v8i w0 = f6_operand(s.wa[0], s.wc[0]);
+    const v8i w1 = f6_operand(s.wa[1], s.wc[1]);
+    const v16f d00 = mfma(w0, x[0], q);
+    const v16f d01 = mfma(w1, x[0], q);
     fold(d00, cA, 0, 0, 0, j);
-    const v16f d10 = mfma(w0, x[1]);
+    const v16f d10 = mfma(w0, x[1], q);
     fold(d01, cB, 1, 0, 1, j);
-    const v16f d11 = mfma(w1, x[1]);
+    const v16f d11 = mfma(w1, x[1], q);
     fold(d10, cB, 0, 1, 0, j);
     fold(d11, cA, 1, 1, 1, j);
   };
   auto compute = [&](const F6Stage& s, int p) {
-    const v8i x[2] = {f6_operand(s.xa[0], s.xc[0], true), f6_operand(s.xa[1], s.xc[1], true)};
+    const v8i x[2] = {f6_operand(s.xa[0], s.xc[0]), f6_operand(s.xa[1], s.xc[1])};
     group(s, x, 0, 2 * p);
     if (2 * p + 1 < Ga) group(s, x, 1, 2 * p + 1);  // wave-uniform
   };

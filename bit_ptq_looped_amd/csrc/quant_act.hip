@@ -58,11 +58,13 @@ __device__ __forceinline__ float group8_max(float v) {
 // The codes: clamp(rint(fl32(x / s)), -qmax, qmax).  The quotient is formed
 // as p = fl32(x * r) with r the hardware reciprocal of s (within 1 ulp):
 // |p - x/s| < 3 * 2^-24 |x/s| and |fl32(x/s) - x/s| <= 2^-24 |x/s|, so below
-// the clamp (|x/s| < qmax + 1 <= 128) p and fl32(x/s) differ by less than
-// 2^-14, and rint gives the same integer unless p lies within 2^-14 of a
-// half-integer.  Those runs, and any run whose r is not a positive finite
-// normal-range value (s outside about [2^-126, 2^126]), are redone with the
-// correctly rounded division.  Above the clamp both sides saturate alike.
+// the clamp (|x/s| < 128) p and fl32(x/s) differ by less than 2^-15.  The
+// distance d = |x * r - rint(p)| is taken with one FMA (within 2^-17 of
+// |p - rint(p)|); if d <= 0.5 - 2^-14 then fl32(x/s) lies within
+// 0.5 - 3 * 2^-17 of rint(p) and rounds to the same integer.  Runs with a
+// larger d, and any run whose r is not a positive finite normal-range value
+// (s outside about [2^-126, 2^126]), are redone with the correctly rounded
+// division.  Above the clamp both sides saturate alike.
 __device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf, float rq, float* step) {
   float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   amax = group8_max(amax);
@@ -79,8 +81,9 @@ __device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf,
   for (int i = 0; i < 4; ++i) {
     const float p = e[i] * r;
     const float rq_ = __builtin_rintf(p);
-    exact |= (fabsf(p) < qmaxf + 1.0f) && (fabsf(p - rq_) > 0.5f - 6.103515625e-05f);
-    const float q = fminf(fmaxf(rq_, -qmaxf), qmaxf);
+    // runs above the clamp may take the exact path too; both sides clamp
+    exact |= fabsf(__builtin_fmaf(e[i], r, -rq_)) > 0.5f - 6.103515625e-05f;
+    const float q = __builtin_amdgcn_fmed3f(rq_, -qmaxf, qmaxf);
     packed |= (uint32_t)((int)q & 0xff) << (8 * i);
   }
   if (exact) {  // rare: near a rounding boundary, or s extreme
@@ -95,18 +98,19 @@ __device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf,
   return packed;
 }
 
-// Store the codes of one 4-element run and, for the first lane of the group,
-// the step.  k0 is the first K index of the run (a multiple of 4).
-__device__ __forceinline__ void store_run(const QuantArgs& a, int row, int k0, uint32_t packed,
-                                          float s, bool first, const float4& xt) {
-  const int K = a.K;
+// Store the codes of one 4-element run in code format FMT and, for the first
+// lane of the group, the step.  k0 is the first K index of the run (a
+// multiple of 4).
+template <int FMT>
+__device__ __forceinline__ void store_run_f(const QuantArgs& a, int K, int row, int k0,
+                                            uint32_t packed, float s, bool first, const float4& xt) {
   const int Ga = K >> 5;
   const int j = k0 >> 5;
-  if (a.codes_fmt == kCodesTiledF6) {
+  if (FMT == kCodesTiledF6) {
     // the 8 lanes of the group are consecutive and aligned, so its two
     // half-groups are whole quads of lanes
     store_f6_run(a.codes, (Ga + 1) >> 1, row, k0, e2m3_of_codes4(packed));
-  } else if (a.codes_fmt == kCodesTiledI8) {
+  } else if (FMT == kCodesTiledI8) {
     const int kk = k0 & 31;
     const int64_t off = ((int64_t)(row >> 5) * Ga + j) * 1024 + (kk >> 4) * 512 + (row & 31) * 16 +
                         (kk & 15);
@@ -121,6 +125,16 @@ __device__ __forceinline__ void store_run(const QuantArgs& a, int row, int k0, u
       a.scales[(int64_t)row * Ga + j] = s;
   }
   if (a.xt_out) *reinterpret_cast<float4*>(a.xt_out + (int64_t)row * K + k0) = xt;
+}
+
+__device__ __forceinline__ void store_run(const QuantArgs& a, int row, int k0, uint32_t packed,
+                                          float s, bool first, const float4& xt) {
+  if (a.codes_fmt == kCodesTiledF6)
+    store_run_f<kCodesTiledF6>(a, a.K, row, k0, packed, s, first, xt);
+  else if (a.codes_fmt == kCodesTiledI8)
+    store_run_f<kCodesTiledI8>(a, a.K, row, k0, packed, s, first, xt);
+  else
+    store_run_f<kCodesCanonical>(a, a.K, row, k0, packed, s, first, xt);
 }
 
 // No transform: quantize x directly.  One wave covers 8 groups (256 elements)
@@ -177,61 +191,74 @@ struct XStrides {
   static constexpr int sx = N2 > 0 ? x_stride(N2) : 0;
 };
 
-// Stage 1 of the transform for NI work items of one wave (items wave,
-// wave + 4, ...): T[ii][rt] accumulates X_r * P2 over the 4-deep steps of b.
-template <int NRT, int N1, int N2, int NI, int NIM>
+// Work item of slot ii of a wave.  SR (shared row): a wave's NIM slots are
+// consecutive items, all in one row of the chunk (the row's column-tile count
+// is a multiple of NIM), so the stage-1 X operand is read once for all of
+// them; otherwise the items are dealt to the 4 waves in turn.
+template <bool SR, int NIM>
+__device__ __forceinline__ int item_of(int wave, int ii) {
+  return SR ? wave * NIM + ii : wave + 4 * ii;
+}
+
+// Stage 1 of the transform for NI work items of one wave: T[ii][rt]
+// accumulates X_r * P2 over the 4-deep steps of b.
+template <int NRT, int N1, int N2, int NI, int NIM, bool SR>
 __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, const float* sX,
                                        int wave, int njt, int li, int lk, v4d (&T)[NIM][NRT]) {
   const int n1 = N1 > 0 ? N1 : a.n1;
   const int n2 = N2 > 0 ? N2 : a.n2;
+  constexpr int NA = SR ? 1 : NI;  // distinct X rows among the items
   const float* pb[NI];
-  const float* xa[NI][NRT];
+  const float* xa[NA][NRT];
   uint32_t mj[NI], mrow[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) mrow[rt] = (rt * 16 + li < n1) ? 0xffffffffu : 0u;
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
-    const int item = wave + 4 * ii;
+    const int item = item_of<SR, NIM>(wave, ii);
     const int r = item / njt;
     const int j = (item - r * njt) * 16 + li;
     mj[ii] = j < n2 ? 0xffffffffu : 0u;
     pb[ii] = sP2 + (j < n2 ? j : 0);
+    if (ii < NA) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-      xa[ii][rt] = sX + (r * n1 + min(rt * 16 + li, n1 - 1)) * (N2 > 0 ? XStrides<N1, N2>::sx : a.sx);
+      for (int rt = 0; rt < NRT; ++rt)
+        xa[ii][rt] = sX + (r * n1 + min(rt * 16 + li, n1 - 1)) * (N2 > 0 ? XStrides<N1, N2>::sx : a.sx);
+    }
   }
   // raw (fp32) operands of one 4-deep step; the compile-time form reads the
   // next step's operands before converting and multiplying the current
   // one, so the LDS latency hides behind the MFMAs
   struct Raw {
     float b[NI];
-    float a[NI][NRT];
+    float a[NA][NRT];
   };
   auto fetch = [&](int s, Raw& o) {
     const int b = 4 * s + lk;
+    // addresses are clamped in bounds: load unconditionally, then zero the
+    // lanes outside the matrix with an integer mask (no branch)
 #pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-      // addresses are clamped in bounds: load unconditionally, then zero the
-      // lanes outside the matrix with an integer mask (no branch)
+    for (int ii = 0; ii < NI; ++ii)
       o.b[ii] = masked(pb[ii][b * (N2 > 0 ? XStrides<N1, N2>::sp2 : a.sp2)], mj[ii]);
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) o.a[ii][rt] = masked(xa[ii][rt][b], mrow[rt]);
-    }
+    for (int ia = 0; ia < NA; ++ia)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) o.a[ia][rt] = masked(xa[ia][rt][b], mrow[rt]);
   };
   auto mma = [&](const Raw& o) {
     double bv[NI];
-    double av[NI][NRT];
+    double av[NA][NRT];
 #pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-      bv[ii] = (double)o.b[ii];
+    for (int ii = 0; ii < NI; ++ii) bv[ii] = (double)o.b[ii];
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) av[ii][rt] = (double)o.a[ii][rt];
-    }
+    for (int ia = 0; ia < NA; ++ia)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) av[ia][rt] = (double)o.a[ia][rt];
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
-        T[ii][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ii][rt], bv[ii], T[ii][rt], 0, 0, 0);
+        T[ii][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[SR ? 0 : ii][rt], bv[ii], T[ii][rt], 0, 0, 0);
   };
   if constexpr (N2 > 0) {  // fully unrolled: the accumulators stay in place
     Raw buf[2];
@@ -254,7 +281,7 @@ __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, con
 // Stage 2 for the same items: x~[:, tile] = P1^T * T, B operands straight
 // from the stage-1 results (element e of tile rt is step s = 4 rt + e);
 // writes fp32 x~ into the flat rows of the X region.
-template <int NRT, int N1, int N2, int NI, int NIM>
+template <int NRT, int N1, int N2, int NI, int NIM, bool SR>
 __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, float* sX, int wave,
                                        int njt, int li, int lk, const v4d (&T)[NIM][NRT]) {
   const int n1 = N1 > 0 ? N1 : a.n1;
@@ -306,7 +333,7 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
   }
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
-    const int item = wave + 4 * ii;
+    const int item = item_of<SR, NIM>(wave, ii);
     const int r = item / njt;
     const int j = (item - r * njt) * 16 + li;
     if (j < n2) {
@@ -322,6 +349,42 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
   }
 }
 
+// Quantize the flat transformed rows [rows][K] of a chunk held in LDS at sX
+// (chunk row r is global row row0 + r).  Lane r of the wave holds the clip of
+// chunk row r in cl (rows <= 64); a run takes it with one LDS permute, read a
+// step ahead together with the run's four elements.
+template <int FMT>
+__device__ __forceinline__ void quant_chunk(const QuantArgs& a, const float* sX, int row0, int rows,
+                                            int K, int wave, int lane, float cl, float qmaxf,
+                                            float rqmax) {
+  const int nruns = rows * K / 4;  // multiple of 8
+  int q0 = wave * 64;
+  if (q0 >= nruns) return;
+  auto load = [&](int qb, float4& v, float& c) {
+    const int q = qb + lane;
+    const int qc = q < nruns ? q : qb;
+    v = *reinterpret_cast<const float4*>(sX + qc * 4);
+    c = __int_as_float(__builtin_amdgcn_ds_bpermute(((qc * 4) / K) << 2, __float_as_int(cl)));
+  };
+  float4 v;
+  float c;
+  load(q0, v, c);
+  for (; q0 < nruns; q0 += 256) {
+    float4 vn = v;
+    float cn = c;
+    if (q0 + 256 < nruns) load(q0 + 256, vn, cn);
+    const int q = q0 + lane;
+    const bool valid = q < nruns;
+    const int e = (valid ? q : q0) * 4;
+    const int r = e / K;
+    float s;
+    const uint32_t packed = quantize4(v, c, qmaxf, rqmax, &s);
+    if (valid) store_run_f<FMT>(a, K, row0 + r, e - r * K, packed, s, (lane & 7) == 0, v);
+    v = vn;
+    c = cn;
+  }
+}
+
 // Transform + quantize, NRT = ceil(n1 / 16) row tiles.  N1, N2 > 0 fix the
 // factor sizes at compile time (the k-loops then unroll fully, which keeps the
 // fp64 accumulators in place); N1 = N2 = 0 takes them from the arguments.
@@ -334,7 +397,7 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
 // fp32 rows [R][K].
 //
 // Work item = (row r of the chunk, 16-column tile jt of the n1 x n2 grid);
-// item i belongs to wave i % 4.  Stage 1 computes T[:, jt] = X_r * P2[:, jt]
+// item_of gives each wave its items.  Stage 1 computes T[:, jt] = X_r * P2[:, jt]
 // as NRT independent 16x16 accumulators (the reduction over b runs in 4-deep
 // MFMA steps).  In the result, lane l holds T[16 rt + 4 e + l/16][16 jt +
 // l%16] in element e of tile rt, which is exactly the B operand stage 2 needs
@@ -359,6 +422,7 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const float qmaxf = (float)a.qmax;
   const float rqmax = 1.0f / qmaxf;
   const int njt = (n2 + 15) >> 4;
+  constexpr bool SR = N2 > 0 && ((N2 + 15) / 16) % NIM == 0;
 
   const int sp1 = N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1;
   const int sp2 = N2 > 0 ? XStrides<N1, N2>::sp2 : a.sp2;
@@ -430,6 +494,8 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   for (int chunk = slot; chunk < nchunks; chunk += G) {
     const int row0 = chunk * R;
     const int rows = min(R, a.rows - row0);
+    // clip of chunk row `lane`, loaded now and used after both stages
+    const float cl = a.clips.c[(row0 + min(lane, rows - 1)) / a.rows_per_clip];
     __syncthreads();  // previous chunk done with the x~ rows (and P staged on the first pass)
 
     // ---- X rows into LDS: from the prefetch registers, or loaded here
@@ -458,47 +524,38 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
     const int items = rows * njt;
     int nmine = 0;
 #pragma unroll
-    for (int ii = 0; ii < NIM; ++ii) nmine += (wave + 4 * ii < items) ? 1 : 0;
+    for (int ii = 0; ii < NIM; ++ii) nmine += (item_of<SR, NIM>(wave, ii) < items) ? 1 : 0;
     v4d T[NIM][NRT];
 #pragma unroll
     for (int ii = 0; ii < NIM; ++ii)
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) T[ii][rt] = v4d{0.0, 0.0, 0.0, 0.0};
     switch (nmine) {
-      case 4: if constexpr (NIM >= 4) stage1<NRT, N1, N2, 4, NIM>(a, sP2, sX, wave, njt, li, lk, T); break;
-      case 3: if constexpr (NIM >= 3) stage1<NRT, N1, N2, 3, NIM>(a, sP2, sX, wave, njt, li, lk, T); break;
-      case 2: if constexpr (NIM >= 2) stage1<NRT, N1, N2, 2, NIM>(a, sP2, sX, wave, njt, li, lk, T); break;
-      case 1: stage1<NRT, N1, N2, 1, NIM>(a, sP2, sX, wave, njt, li, lk, T); break;
+      case 4: if constexpr (NIM >= 4) stage1<NRT, N1, N2, 4, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+      case 3: if constexpr (NIM >= 3) stage1<NRT, N1, N2, 3, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+      case 2: if constexpr (NIM >= 2) stage1<NRT, N1, N2, 2, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+      case 1: stage1<NRT, N1, N2, 1, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
       default: break;
     }
     __syncthreads();  // every X read is done; x~ may now overwrite the region
 
     // ---- stage 2: x~[i][j] = sum_a P1[a][i] T[a][j], rounded once to fp32
     switch (nmine) {
-      case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM>(a, sP1, sX, wave, njt, li, lk, T); break;
-      case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM>(a, sP1, sX, wave, njt, li, lk, T); break;
-      case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM>(a, sP1, sX, wave, njt, li, lk, T); break;
-      case 1: stage2<NRT, N1, N2, 1, NIM>(a, sP1, sX, wave, njt, li, lk, T); break;
+      case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+      case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+      case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+      case 1: stage2<NRT, N1, N2, 1, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
       default: break;
     }
     __syncthreads();
 
     // ---- quantize groups of the flat transformed rows
-    const int nruns = rows * K / 4;  // multiple of 8
-    for (int q0 = wave * 64; q0 < nruns; q0 += 256) {
-      const int q = q0 + lane;
-      const bool valid = q < nruns;
-      const int qc = valid ? q : q0;
-      const int e = qc * 4;
-      const int r = e / K;
-      const int k0 = e - r * K;
-      const float4 v = *reinterpret_cast<const float4*>(sX + r * K + k0);
-      const int row = row0 + r;
-      const float clip = a.clips.c[row / a.rows_per_clip];
-      float s;
-      const uint32_t packed = quantize4(v, clip, qmaxf, rqmax, &s);
-      if (valid) store_run(a, row, k0, packed, s, (lane & 7) == 0, v);
-    }
+    if (a.codes_fmt == kCodesTiledF6)
+      quant_chunk<kCodesTiledF6>(a, sX, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
+    else if (a.codes_fmt == kCodesTiledI8)
+      quant_chunk<kCodesTiledI8>(a, sX, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
+    else
+      quant_chunk<kCodesCanonical>(a, sX, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
   }
 }
 
