@@ -15,8 +15,9 @@
 //   stage 2:  x~ = P1^T * T        (rows i, columns j, reduction over a)
 // both on V_MFMA_F64_16X16X4_F64 with operands staged in LDS (P1, P2 and X as
 // fp32, T as fp64).  x~ is rounded to fp32 into the buffer X occupied, and the
-// quantizer reads 32-element groups of the flat row from there: 8 lanes per
-// group, 4 elements per lane, absmax reduced across the 8 lanes.
+// quantizer reads 32-element groups of the flat row from there: for the fp6
+// GEMM layout one group per lane, for the other layouts 8 lanes per group, 4
+// elements per lane, absmax reduced across the 8 lanes.
 #include "loopq_internal.h"
 
 #include <type_traits>
@@ -25,6 +26,8 @@ namespace loopq {
 namespace {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v6i __attribute__((ext_vector_type(6)));
 
 // v if mask is all ones, +0 if it is zero (bitwise, so no branch is formed)
 __device__ __forceinline__ float masked(float v, uint32_t mask) {
@@ -96,6 +99,64 @@ __device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf,
     }
   }
   return packed;
+}
+
+// Position of flat element f of a chunk's transformed rows in LDS: the eight
+// 16-byte quarters of each 32-element group are rotated by the group index,
+// so that lanes reading one whole group each spread over all LDS banks.
+__device__ __forceinline__ int xt_pos(int f) {
+  return (f & ~31) | ((((f >> 2) + (f >> 5)) & 7) << 2) | (f & 3);
+}
+
+// quantize4 for a whole 32-element group held by one lane, in place: the
+// same absmax, step and code arithmetic (the max is order-free, and a group
+// redone by exact division gives the codes the fast path gives wherever that
+// is not flagged), with the near-tie test taken over the group on
+// |p - rint(p)| itself (if that is at most 0.5 - 2^-14, fl32(x/s) lies within
+// 0.5 - 2^-15 of rint(p)).  ev and od
+// hold the group's even and odd elements on entry and their clamped codes
+// (as floats) on return; reload(ev, od) brings the group back for the rare
+// exact path.  Returns the step.
+template <typename Reload>
+__device__ __forceinline__ float quantize32(v16f& ev, v16f& od, float clip, float qmaxf, float rq,
+                                            Reload reload) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(ev[i]), fabsf(od[i])));
+  const float q0 = amax * rq;
+  const float base = __builtin_fmaf(__builtin_fmaf(-q0, qmaxf, amax), rq, q0);  // = fl32(amax / qmax)
+  const float s = clip * base;
+  if (!(s > 0.0f)) {
+    ev = v16f{};
+    od = v16f{};
+    return s;
+  }
+  const float r = __builtin_amdgcn_rcpf(s);
+  bool exact = !(r > 1.0e-37f && r < 1.0e37f);
+  // in place: p = fl32(x * r), then its distance to rint(p) (exact in fp32)
+  // against the same margin, then the clamped code
+  float dmax = 0.0f;
+  auto code = [&](float x) {
+    const float p = x * r;
+    const float rq_ = __builtin_rintf(p);
+    dmax = fmaxf(dmax, fabsf(p - rq_));
+    return __builtin_amdgcn_fmed3f(rq_, -qmaxf, qmaxf);
+  };
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = code(ev[i]);
+    od[i] = code(od[i]);
+  }
+  exact |= dmax > 0.5f - 6.103515625e-05f;
+  if (exact) {  // rare: near a rounding boundary, or s extreme
+    reload(ev, od);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ev[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(ev[i] / s), -qmaxf, qmaxf);
+      od[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(od[i] / s), -qmaxf, qmaxf);
+    }
+  }
+  return s;
 }
 
 // Store the codes of one 4-element run in code format FMT and, for the first
@@ -337,22 +398,22 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
     const int r = item / njt;
     const int j = (item - r * njt) * 16 + li;
     if (j < n2) {
-      float* xr = sX + r * K + j;
 #pragma unroll
       for (int it = 0; it < NRT; ++it)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int io = it * 16 + 4 * e + lk;  // result element e of lane l: row 4e + l/16
-          if (io < n1) xr[io * n2] = (float)o[ii][it][e];  // one rounding to fp32 (RNE)
+          if (io < n1) sX[xt_pos(r * K + io * n2 + j)] = (float)o[ii][it][e];  // one rounding to fp32 (RNE)
         }
     }
   }
 }
 
 // Quantize the flat transformed rows [rows][K] of a chunk held in LDS at sX
-// (chunk row r is global row row0 + r).  Lane r of the wave holds the clip of
-// chunk row r in cl (rows <= 64); a run takes it with one LDS permute, read a
-// step ahead together with the run's four elements.
+// (chunk row r is global row row0 + r; elements placed by xt_pos), four
+// elements per lane.  Lane r of the wave holds the clip of chunk row r in cl
+// (rows <= 64); a run takes it with one LDS permute, read a step ahead
+// together with the run's four elements.
 template <int FMT>
 __device__ __forceinline__ void quant_chunk(const QuantArgs& a, const float* sX, int row0, int rows,
                                             int K, int wave, int lane, float cl, float qmaxf,
@@ -363,7 +424,7 @@ __device__ __forceinline__ void quant_chunk(const QuantArgs& a, const float* sX,
   auto load = [&](int qb, float4& v, float& c) {
     const int q = qb + lane;
     const int qc = q < nruns ? q : qb;
-    v = *reinterpret_cast<const float4*>(sX + qc * 4);
+    v = *reinterpret_cast<const float4*>(sX + xt_pos(qc * 4));
     c = __int_as_float(__builtin_amdgcn_ds_bpermute(((qc * 4) / K) << 2, __float_as_int(cl)));
   };
   float4 v;
@@ -382,6 +443,69 @@ __device__ __forceinline__ void quant_chunk(const QuantArgs& a, const float* sX,
     if (valid) store_run_f<FMT>(a, K, row0 + r, e - r * K, packed, s, (lane & 7) == 0, v);
     v = vn;
     c = cn;
+  }
+}
+
+// The same for the fp6 code layout, one 32-element group per lane: each
+// wave takes a contiguous quarter of the chunk's groups.  The clamped codes
+// go through V_CVT_SCALEF32_2XPK16_FP6_F32 (scale 1: integers -7..7 are exact
+// e2m3 values), which packs its two 16-element sources interleaved, source 0
+// into the even fields; fed the even and the odd elements it yields the
+// group's 24 bytes in field order, stored as they are.  A zero code may come
+// out as either e2m3 zero pattern.
+__device__ __forceinline__ void quant_groups_f6(const QuantArgs& a, const float* sX, int row0,
+                                                int rows, int K, int wave, int lane, float cl,
+                                                float qmaxf, float rqmax) {
+  const int Ga = K >> 5;
+  const int Gp = (Ga + 1) >> 1;
+  const int ng = rows * Ga;
+  const int per = (ng + 3) >> 2;
+  const int g0 = wave * per;
+  const int g1 = min(ng, g0 + per);
+  for (int gb = g0; gb < g1; gb += 64) {  // wave-uniform
+    const int g = gb + lane;
+    const bool valid = g < g1;
+    const int gc = valid ? g : gb;
+    // element i sits at gc * 32 + xt_pos quarter rotation; read each one
+    // straight into its even / odd source register of the packing instruction
+    auto load = [&](v16f& ev, v16f& od) {
+      const float* gp = sX + gc * 32;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        ev[i] = gp[((((2 * i) >> 2) + gc) & 7) << 2 | ((2 * i) & 3)];
+        od[i] = gp[((((2 * i + 1) >> 2) + gc) & 7) << 2 | ((2 * i + 1) & 3)];
+      }
+    };
+    v16f ev, od;
+    load(ev, od);
+    const int r = gc / Ga;
+    const int j = gc - r * Ga;
+    const float clip = __int_as_float(__builtin_amdgcn_ds_bpermute(r << 2, __float_as_int(cl)));
+    const float s = quantize32(ev, od, clip, qmaxf, rqmax, load);
+    if (!valid) continue;
+    const v6i bits = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+    // The instruction's result must not share registers with its sources
+    // (measured: a result placed inside the second source comes out wrong in
+    // one dword per lane), and the register allocator may place it there;
+    // holding both sources live past it rules that out.
+    asm volatile("" ::"v"(ev), "v"(od));
+    const int row = row0 + r;
+    uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<char*>(a.codes) +
+                                          ((int64_t)(row >> 5) * Gp + (j >> 1)) * kF6BlockBytes +
+                                          ((row & 31) + 32 * (j & 1)) * 24);
+    dst[0] = uint2{(uint32_t)bits[0], (uint32_t)bits[1]};
+    dst[1] = uint2{(uint32_t)bits[2], (uint32_t)bits[3]};
+    dst[2] = uint2{(uint32_t)bits[4], (uint32_t)bits[5]};
+    if (a.scales_gm)
+      a.scales[(int64_t)j * a.scales_ld + row] = s;
+    else
+      a.scales[(int64_t)row * Ga + j] = s;
+    if (a.xt_out) {
+      load(ev, od);
+      float4* xo = reinterpret_cast<float4*>(a.xt_out + (int64_t)row * K + j * 32);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) xo[c] = float4{ev[2 * c], od[2 * c], ev[2 * c + 1], od[2 * c + 1]};
+    }
   }
 }
 
@@ -551,7 +675,7 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
 
     // ---- quantize groups of the flat transformed rows
     if (a.codes_fmt == kCodesTiledF6)
-      quant_chunk<kCodesTiledF6>(a, sX, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
+      quant_groups_f6(a, sX, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
     else if (a.codes_fmt == kCodesTiledI8)
       quant_chunk<kCodesTiledI8>(a, sX, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
     else
