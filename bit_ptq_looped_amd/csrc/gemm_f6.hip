@@ -152,24 +152,36 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
     }
   };
   // one group q of the pair: weight operands keep the lanes of K-half q
+  // MFMA and VALU work of one SIMD do not overlap on this chip, and a fold
+  // issued right behind the MFMA that produces its operand stalls on it.
+  // Each group therefore runs as two blocks, fenced so the scheduler keeps
+  // them apart: one coefficient MFMA and the two result MFMAs that use it,
+  // then their two folds (the results are complete by the time the folds
+  // issue).
   auto group = [&](const F6Stage& s, const v8i (&x)[2], int q, int j) {
-    v32f cA = {}, cB = {};
-    if (MODE == 0) {
-      const v32f z = {};
-      const float swf = __half2float(__ushort_as_half((unsigned short)s.sw[q]));
-      cA = __builtin_amdgcn_mfma_f32_32x32x1f32(swf, s.sa[q][0], z, 0, 0, 0);  // (t0,u0) | (t1,u1)
-      cB = __builtin_amdgcn_mfma_f32_32x32x1f32(swf, s.sa[q][1], z, 0, 0, 0);  // (t1,u0) | (t0,u1)
-    }
+    const float swf = MODE == 0 ? __half2float(__ushort_as_half((unsigned short)s.sw[q])) : 0.0f;
     const v8i w0 = f6_operand(s.wa[0], s.wc[0]);
     const v8i w1 = f6_operand(s.wa[1], s.wc[1]);
+    auto coef = [&](float sa) -> v32f {
+      v32f cf = {};
+      if (MODE == 0) cf = __builtin_amdgcn_mfma_f32_32x32x1f32(swf, sa, v32f{}, 0, 0, 0);
+      return cf;
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    const v32f cA = coef(s.sa[q][0]);  // (t0,u0) | (t1,u1)
     const v16f d00 = mfma(w0, x[0], q);
-    const v16f d01 = mfma(w1, x[0], q);
-    fold(d00, cA, 0, 0, 0, j);
-    const v16f d10 = mfma(w0, x[1], q);
-    fold(d01, cB, 1, 0, 1, j);
     const v16f d11 = mfma(w1, x[1], q);
-    fold(d10, cB, 0, 1, 0, j);
+    __builtin_amdgcn_sched_barrier(0);
+    fold(d00, cA, 0, 0, 0, j);
     fold(d11, cA, 1, 1, 1, j);
+    __builtin_amdgcn_sched_barrier(0);
+    const v32f cB = coef(s.sa[q][1]);  // (t1,u0) | (t0,u1)
+    const v16f d01 = mfma(w1, x[0], q);
+    const v16f d10 = mfma(w0, x[1], q);
+    __builtin_amdgcn_sched_barrier(0);
+    fold(d01, cB, 1, 0, 1, j);
+    fold(d10, cB, 0, 1, 0, j);
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto compute = [&](const F6Stage& s, int p) {
     const v8i x[2] = {f6_operand(s.xa[0], s.xc[0]), f6_operand(s.xa[1], s.xc[1])};
