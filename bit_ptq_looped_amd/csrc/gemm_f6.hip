@@ -212,15 +212,19 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
 
 // One thread per (column n of the padded weight, group j): the 32 biased
 // nibbles of the packed layout -> 24 bytes of e2m3 codes in the fp6 layout.
+// Threads run over (column block, group, column): the 32 threads of a block
+// and group read 256 contiguous bytes per K-half and write 768 contiguous
+// bytes.
 __global__ __launch_bounds__(256) void expand_f6_kernel(const uint8_t* __restrict__ w, int K, int Npad,
                                                         char* __restrict__ out) {
   const int Ga = K >> 5;
   const int Gp = (Ga + 1) >> 1;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)Npad * Ga) return;
-  const int n = (int)(idx / Ga);
-  const int j = (int)(idx - (int64_t)n * Ga);
-  const int nb = n >> 5, cc = n & 31;
+  const int cc = (int)(idx & 31);
+  const int64_t bj = idx >> 5;  // nb * Ga + j
+  const int nb = (int)(bj / Ga);
+  const int j = (int)(bj - (int64_t)nb * Ga);
   const uint8_t* blk = w + ((int64_t)nb * Ga + j) * kBlockBytes;
   uint32_t piece[8];  // 24-bit e2m3 runs of codes 4r .. 4r + 3
 #pragma unroll
