@@ -4,8 +4,10 @@
 // Method: Eq.(4) of the LoopQ specification ("paper_specification.yaml",
 // lq1_quantization), the LAS clip per module and loop (loopq_components.las,
 // implementation_status lq2) and the shared Kronecker transform
-// (implementation_status lq3).  Readings: the transform is formed in fp64 and
-// rounded once to fp32; the step is fl32(c * fl32(absmax / qmax)); codes are
+// (implementation_status lq3).  Readings: the transform is formed with fp32
+// products and fp32 accumulation (an fp32-class result: each element within
+// a few (n1 + n2) ulps of sum |P1| |X| |P2|); the codes and steps are those of
+// Eq.(4) applied to that x~ exactly; the step is fl32(c * fl32(absmax / qmax)); codes are
 // clamp(rint(fl32(x / s)), -qmax, qmax) with correctly rounded division and
 // ties to even; a zero step gives zero codes.
 //
@@ -13,8 +15,8 @@
 // X = reshape(x, n1, n2) and
 //   stage 1:  T  = X * P2          (rows (r, a), columns j, reduction over b)
 //   stage 2:  x~ = P1^T * T        (rows i, columns j, reduction over a)
-// both on V_MFMA_F64_16X16X4_F64 with operands staged in LDS (P1, P2 and X as
-// fp32, T as fp64).  x~ is rounded to fp32 into the buffer X occupied, and the
+// both on V_MFMA_F32_16X16X4_F32 with operands staged in LDS (P1, P2 and X as
+// fp32; T stays in the stage-1 result registers).  x~ goes into the buffer X occupied, and the
 // quantizer reads 32-element groups of the flat row from there: for the fp6
 // GEMM layout one group per lane, for the other layouts 8 lanes per group, 4
 // elements per lane, absmax reduced across the 8 lanes.
@@ -25,7 +27,7 @@
 namespace loopq {
 namespace {
 
-typedef double v4d __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v6i __attribute__((ext_vector_type(6)));
 
@@ -265,7 +267,7 @@ __device__ __forceinline__ int item_of(int wave, int ii) {
 // accumulates X_r * P2 over the 4-deep steps of b.
 template <int NRT, int N1, int N2, int NI, int NIM, bool SR>
 __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, const float* sX,
-                                       int wave, int njt, int li, int lk, v4d (&T)[NIM][NRT]) {
+                                       int wave, int njt, int li, int lk, v4f (&T)[NIM][NRT]) {
   const int n1 = N1 > 0 ? N1 : a.n1;
   const int n2 = N2 > 0 ? N2 : a.n2;
   constexpr int NA = SR ? 1 : NI;  // distinct X rows among the items
@@ -307,19 +309,11 @@ __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, con
       for (int rt = 0; rt < NRT; ++rt) o.a[ia][rt] = masked(xa[ia][rt][b], mrow[rt]);
   };
   auto mma = [&](const Raw& o) {
-    double bv[NI];
-    double av[NA][NRT];
-#pragma unroll
-    for (int ii = 0; ii < NI; ++ii) bv[ii] = (double)o.b[ii];
-#pragma unroll
-    for (int ia = 0; ia < NA; ++ia)
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) av[ia][rt] = (double)o.a[ia][rt];
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
-        T[ii][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[SR ? 0 : ii][rt], bv[ii], T[ii][rt], 0, 0, 0);
+        T[ii][rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.a[SR ? 0 : ii][rt], o.b[ii], T[ii][rt], 0, 0, 0);
   };
   if constexpr (N2 > 0) {  // fully unrolled: the accumulators stay in place
     Raw buf[2];
@@ -344,52 +338,52 @@ __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, con
 // writes fp32 x~ into the flat rows of the X region.
 template <int NRT, int N1, int N2, int NI, int NIM, bool SR>
 __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, float* sX, int wave,
-                                       int njt, int li, int lk, const v4d (&T)[NIM][NRT]) {
+                                       int njt, int li, int lk, const v4f (&T)[NIM][NRT]) {
   const int n1 = N1 > 0 ? N1 : a.n1;
   const int n2 = N2 > 0 ? N2 : a.n2;
   const int K = n1 * n2;
-  v4d o[NI][NRT];
+  v4f o[NI][NRT];
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
-    for (int it = 0; it < NRT; ++it) o[ii][it] = v4d{0.0, 0.0, 0.0, 0.0};
-  // step s = 4 rt + e reduces over rows a = 4 s + l/16; as in stage 1 the
-  // compile-time form reads the next step's P1 operands before multiplying
+    for (int it = 0; it < NRT; ++it) o[ii][it] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  // step s = 4 rt + e reduces over rows a = 16 rt + 4 (l/16) + e (the rows
+  // lane l holds in element e of stage-1 tile rt), for all 4 NRT steps: with
+  // n1 % 16 != 0 the last tile's rows below n1 are spread over all four of
+  // its steps, and the P1 operand is zero for rows a >= n1 (whose T rows are
+  // zero too).  As in stage 1 the compile-time form reads the next step's P1
+  // operands before multiplying.
   auto fetch = [&](int s, float (&o2)[NRT]) {
-    const float* pa = sP1 + (4 * s + lk) * (N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1);
+    const int ar = 16 * (s >> 2) + 4 * lk + (s & 3);
+    const float* pa = sP1 + min(ar, n1 - 1) * (N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1);
 #pragma unroll
     for (int it = 0; it < NRT; ++it) {
       const int i = it * 16 + li;
-      o2[it] = masked(pa[min(i, n1 - 1)], i < n1 ? 0xffffffffu : 0u);
+      o2[it] = masked(pa[min(i, n1 - 1)], (i < n1 && ar < n1) ? 0xffffffffu : 0u);
     }
   };
   auto mma = [&](int s, const float (&raw)[NRT]) {
-    double av[NRT];
-#pragma unroll
-    for (int it = 0; it < NRT; ++it) av[it] = (double)raw[it];
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
       for (int it = 0; it < NRT; ++it)
-        o[ii][it] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[it], T[ii][s >> 2][s & 3], o[ii][it], 0, 0, 0);
+        o[ii][it] = __builtin_amdgcn_mfma_f32_16x16x4f32(raw[it], T[ii][s >> 2][s & 3], o[ii][it], 0, 0, 0);
   };
   if constexpr (N1 > 0) {
     float buf[2][NRT];
     fetch(0, buf[0]);
 #pragma unroll
-    for (int s = 0; s < N1 / 4; ++s) {
-      if (s + 1 < N1 / 4) fetch(s + 1, buf[(s + 1) & 1]);
+    for (int s = 0; s < 4 * NRT; ++s) {
+      if (s + 1 < 4 * NRT) fetch(s + 1, buf[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       mma(s, buf[s & 1]);
     }
   } else {
 #pragma unroll
     for (int s = 0; s < 4 * NRT; ++s) {
-      if (s < (n1 >> 2)) {
-        float raw[NRT];
-        fetch(s, raw);
-        mma(s, raw);
-      }
+      float raw[NRT];
+      fetch(s, raw);
+      mma(s, raw);
     }
   }
 #pragma unroll
@@ -402,8 +396,8 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
       for (int it = 0; it < NRT; ++it)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int io = it * 16 + 4 * e + lk;  // result element e of lane l: row 4e + l/16
-          if (io < n1) sX[xt_pos(r * K + io * n2 + j)] = (float)o[ii][it][e];  // one rounding to fp32 (RNE)
+          const int io = it * 16 + 4 * lk + e;  // result element e of lane l: row 4 (l/16) + e
+          if (io < n1) sX[xt_pos(r * K + io * n2 + j)] = o[ii][it][e];
         }
     }
   }
@@ -511,7 +505,7 @@ __device__ __forceinline__ void quant_groups_f6(const QuantArgs& a, const float*
 
 // Transform + quantize, NRT = ceil(n1 / 16) row tiles.  N1, N2 > 0 fix the
 // factor sizes at compile time (the k-loops then unroll fully, which keeps the
-// fp64 accumulators in place); N1 = N2 = 0 takes them from the arguments.
+// accumulators in place); N1 = N2 = 0 takes them from the arguments.
 // RS > 0 fixes the rows per chunk (the host plan uses the same value) and
 // enables the prefetch of the next chunk's X into registers; BF is the input
 // type when RS > 0 (1 bf16, 0 fp32).  NIM bounds the work items per wave.
@@ -523,9 +517,10 @@ __device__ __forceinline__ void quant_groups_f6(const QuantArgs& a, const float*
 // Work item = (row r of the chunk, 16-column tile jt of the n1 x n2 grid);
 // item_of gives each wave its items.  Stage 1 computes T[:, jt] = X_r * P2[:, jt]
 // as NRT independent 16x16 accumulators (the reduction over b runs in 4-deep
-// MFMA steps).  In the result, lane l holds T[16 rt + 4 e + l/16][16 jt +
+// MFMA steps).  In the result, lane l holds T[16 rt + 4 (l/16) + e][16 jt +
 // l%16] in element e of tile rt, which is exactly the B operand stage 2 needs
-// from lane l at step s = 4 rt + e (rows a = 4 s + l/16), so T stays in
+// from lane l at step s = 4 rt + e once stage 2 takes its reduction over a in
+// that order (rows a = 16 rt + 4 (l/16) + e at step s), so T stays in
 // registers.  Stage 2 then forms x~[:, jt] = P1^T * T with NRT accumulators
 // over the i tiles.
 template <int NRT, int N1, int N2, int RS, int NIM, int BF>
@@ -649,11 +644,11 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
     int nmine = 0;
 #pragma unroll
     for (int ii = 0; ii < NIM; ++ii) nmine += (item_of<SR, NIM>(wave, ii) < items) ? 1 : 0;
-    v4d T[NIM][NRT];
+    v4f T[NIM][NRT];
 #pragma unroll
     for (int ii = 0; ii < NIM; ++ii)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) T[ii][rt] = v4d{0.0, 0.0, 0.0, 0.0};
+      for (int rt = 0; rt < NRT; ++rt) T[ii][rt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     switch (nmine) {
       case 4: if constexpr (NIM >= 4) stage1<NRT, N1, N2, 4, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
       case 3: if constexpr (NIM >= 3) stage1<NRT, N1, N2, 3, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
@@ -663,7 +658,7 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
     }
     __syncthreads();  // every X read is done; x~ may now overwrite the region
 
-    // ---- stage 2: x~[i][j] = sum_a P1[a][i] T[a][j], rounded once to fp32
+    // ---- stage 2: x~[i][j] = sum_a P1[a][i] T[a][j]
     switch (nmine) {
       case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
       case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
@@ -691,7 +686,7 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
 // are those of the chunked kernel, so x~ is bitwise the same; it is written
 // rounded to fp32 to `xt` ([rows][K]) and quantized by a second launch.
 // LDS: P1 [n1][sp1] f32, the P2 columns of the tile [n2][16] f32, the row of
-// X [n1][sx] f32 and T [n1][16] f64.
+// X [n1][sx] f32 and T [n1][16] f32.
 template <int NRT, int N1, int N2>
 __global__ __launch_bounds__(256) void xform_items_kernel(QuantArgs a, float* __restrict__ xt) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -704,7 +699,7 @@ __global__ __launch_bounds__(256) void xform_items_kernel(QuantArgs a, float* __
   float* sP1 = reinterpret_cast<float*>(lds);
   float* sP2 = reinterpret_cast<float*>(lds + off_p2);
   float* sX = reinterpret_cast<float*>(lds + off_x);
-  double* sT = reinterpret_cast<double*>(lds + off_t);
+  float* sT = reinterpret_cast<float*>(lds + off_t);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -737,20 +732,20 @@ __global__ __launch_bounds__(256) void xform_items_kernel(QuantArgs a, float* __
 
   // stage 1: T[rt] = X_r * P2[:, tile], steps of b in order (as the chunked kernel)
   for (int rt = wave; rt < NRT; rt += 4) {
-    v4d T = {0.0, 0.0, 0.0, 0.0};
+    v4f T = {0.0f, 0.0f, 0.0f, 0.0f};
     const float* xa = sX + min(rt * 16 + li, n1 - 1) * sx;
     const uint32_t mrow = (rt * 16 + li < n1) ? 0xffffffffu : 0u;
 #pragma unroll
     for (int st = 0; st < N2 / 4; ++st) {
       const int b = 4 * st + lk;
-      const double av = (double)masked(xa[b], mrow);
-      const double bv = (double)sP2[b * 16 + li];  // zero past n2
-      T = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, T, 0, 0, 0);
+      const float av = masked(xa[b], mrow);
+      const float bv = sP2[b * 16 + li];  // zero past n2
+      T = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, T, 0, 0, 0);
     }
-    // result element e of lane l: row 16 rt + 4 e + l / 16, column l % 16
+    // result element e of lane l: row 16 rt + 4 (l / 16) + e, column l % 16
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = rt * 16 + 4 * e + lk;
+      const int row = rt * 16 + 4 * lk + e;
       if (row < n1) sT[row * 16 + li] = T[e];
     }
   }
@@ -758,21 +753,24 @@ __global__ __launch_bounds__(256) void xform_items_kernel(QuantArgs a, float* __
 
   // stage 2: x~[it][tile] = sum_a P1[a][it] T[a][tile], steps of a in order
   for (int it = wave; it < NRT; it += 4) {
-    v4d o = {0.0, 0.0, 0.0, 0.0};
+    v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
     const int i = it * 16 + li;
     const uint32_t mi = i < n1 ? 0xffffffffu : 0u;
 #pragma unroll
-    for (int st = 0; st < N1 / 4; ++st) {
-      const double av = (double)masked(sP1[(4 * st + lk) * sp1 + min(i, n1 - 1)], mi);
-      const double bv = sT[(4 * st + lk) * 16 + li];
-      o = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, o, 0, 0, 0);
+    for (int st = 0; st < 4 * NRT; ++st) {
+      // the chunked kernel's order over a, rows >= n1 masked as there
+      const int ar = 16 * (st >> 2) + 4 * lk + (st & 3);
+      const int ac = min(ar, n1 - 1);
+      const float av = masked(sP1[ac * sp1 + min(i, n1 - 1)], ar < n1 ? mi : 0u);
+      const float bv = sT[ac * 16 + li];
+      o = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, o, 0, 0, 0);
     }
     const int j = jt * 16 + li;
     if (j < n2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int io = it * 16 + 4 * e + lk;
-        if (io < n1) xt[(int64_t)r * K + io * n2 + j] = (float)o[e];  // one rounding to fp32
+        const int io = it * 16 + 4 * lk + e;
+        if (io < n1) xt[(int64_t)r * K + io * n2 + j] = o[e];
       }
     }
   }
@@ -890,7 +888,7 @@ hipError_t launch_quant_act_few(QuantArgs a, float* xt_buf, hipStream_t s) {
       fn = reinterpret_cast<const void*>(xform_items_kernel<(n1_ + 15) / 16, n1_, n2_>);           \
       constexpr int sp1 = XStrides<n1_, n2_>::sp1, sx = XStrides<n1_, n2_>::sx;                    \
       constexpr int off_x = (n1_ * sp1 * 4 + 15) / 16 * 16 + n2_ * 16 * 4;                         \
-      lds = (off_x + n1_ * sx * 4 + 15) / 16 * 16 + n1_ * 16 * 8;                                 \
+      lds = (off_x + n1_ * sx * 4 + 15) / 16 * 16 + n1_ * 16 * 4;                                 \
     }
     LOOPQ_SHAPES(LOOPQ_ITEM_KERNEL)
 #undef LOOPQ_ITEM_KERNEL

@@ -24,8 +24,9 @@
  * fl32(c * fl32(absmax / qmax)) (weights: fl16(fl32(absmax / 7)), codes use
  * the fp16 step); division is correctly rounded; an all-zero group has step 0
  * and codes 0; groups run along K over the flat row-major index; the
- * transform is x~ = x (P1 kron P2) = vec_r(P1^T X P2), formed in fp64 and
- * rounded once to fp32.
+ * transform is x~ = x (P1 kron P2) = vec_r(P1^T X P2), formed with fp32
+ * products and fp32 accumulation (within 8 (n1 + n2) 2^-24 |P1|^T |X| |P2| of
+ * the exact value per element); codes and steps are Eq.(4) of that x~ exactly.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless the name ends in _host.

@@ -5,13 +5,13 @@ computes row by row.
 
 * Packed weights: the exported codes and fp16 steps of the whole matrix are
   bit-exact against the oracle's weight quantization.
-* y: sampled (loop, row) pairs, all N columns, max|y - y_oracle| /
-  max|y_oracle| <= 1e-4 over the sampled rows.
 * Quantizer: loopq_quant_act over all T*M rows (clip of loop 0) with the x~
-  dump; on sampled rows the dump is within one fp32 ulp of the oracle's
-  fp64-then-rounded transform, and codes and steps are bit-exact against the
-  oracle applied to the dump (equal to the oracle's own x~ wherever no ulp
-  differs).
+  dump; on sampled rows the dump is within the fp32-class bound of the
+  oracle's fp64 transform (``xt_check``), and codes and steps are bit-exact
+  against the oracle applied to the dump.
+* y: sampled (loop, row) pairs, all N columns, against the oracle applied to
+  the same x~ with the loop's clip: max|y - y_oracle| / max|y_oracle| <= 1e-4
+  over the sampled rows.
 
 Inputs are the seeded generators' full tensors, except for the Huginn-like
 recurrence, whose host-side generation at 65,536 rows x K = 17,920 takes about
@@ -29,6 +29,7 @@ import torch
 
 import oracle
 from bit_ptq_looped_amd import synth
+from xt_check import check_xt
 
 pytestmark = pytest.mark.gpu
 
@@ -115,13 +116,6 @@ def run_case(lq, wl, act, tile_rows=None):
     idx_m = torch.tensor(ms, device="cuda")
     ys = y.index_select(0, idx_t).index_select(1, idx_m).cpu().numpy()  # [len(ts)][len(ms)][N]
     del y
-    ref = np.empty(ys.shape, dtype=np.float64)
-    for a, t in enumerate(ts):
-        xr = np.stack([src(t, m) for m in ms])
-        ref[a], _, _ = oracle.linear(xr, P1, P2, float(clips[t]), wl.bits_a, qw, sw, gw)
-    err = float(np.max(np.abs(ys - ref)) / np.max(np.abs(ref)))
-    say(f"  y: {len(ts)} loops x {len(ms)} rows x {N} columns, rel err {err:.3e}")
-    assert err <= Y_TOL
 
     # quantizer over all T*M rows (loop-0 clip) with the x~ dump, sampled
     rows_all = T * M
@@ -140,14 +134,21 @@ def run_case(lq, wl, act, tile_rows=None):
         dump = xr.astype(np.float32)
     else:
         dump = xt.index_select(0, fi).cpu().numpy()
-        want = oracle.transformed_f32(xr, P1, P2)
-        ulps = np.abs(dump.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
-        say(f"  x~: {ulps.size} elements, {np.count_nonzero(ulps)} differ by one ulp")
-        assert ulps.max() <= 1
-        assert np.count_nonzero(ulps) <= max(4, ulps.size // 100000)
+        ratio = check_xt(dump, xr, P1, P2)
+        say(f"  x~: {dump.size} sampled elements within the fp32-class bound (max error/bound {ratio:.3f})")
+    del qc, qs, xt
     qa, sa = oracle.quant_act(dump, float(clips[0]), wl.bits_a)
     np.testing.assert_array_equal(gcodes, qa)
     np.testing.assert_array_equal(gsteps.view(np.uint32), sa.view(np.uint32))
+
+    # y of the sampled rows against the oracle applied to the same x~
+    dump = dump.reshape(len(ts), len(ms), K)
+    ref = np.empty(ys.shape, dtype=np.float64)
+    for a, t in enumerate(ts):
+        ref[a], _, _ = oracle.linear(dump[a], None, None, float(clips[t]), wl.bits_a, qw, sw, gw)
+    err = float(np.max(np.abs(ys - ref)) / np.max(np.abs(ref)))
+    say(f"  y: {len(ts)} loops x {len(ms)} rows x {N} columns, rel err {err:.3e}")
+    assert err <= Y_TOL
 
 
 OURO_INPUTS = ["qkv_in", "o_in", "up_in", "down_in"]

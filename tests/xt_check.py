@@ -1,0 +1,64 @@
+"""Parity reading for the Kronecker transform, shared by the GPU tests.
+
+The pages fix no precision for the transform: "paper_specification.yaml" lists
+the Kronecker factorization details among its underspecified items, and its
+runs simulate quantization on a bf16 base model.  The kernels form
+x~ = vec_r(P1^T X P2) with fp32 products and fp32 accumulation, so parity has
+two parts:
+
+1. the kernel's x~ (the ``xt_out`` dump of ``loopq_quant_act``, the values it
+   quantized) lies element by element within the fp32-class bound
+       |x~_gpu - x~_64| <= 8 (n1 + n2) 2^-24 (|P1|^T |X| |P2|)
+   of the oracle's fp64 transform;
+2. codes and steps are bit-exact, and y within 1e-4, against the oracle
+   applied to that dump (no transform on the oracle side).
+
+A row's x~ depends only on the row and the fixed sequence of MFMA steps, so
+the dump of ``loopq_quant_act`` is bitwise the x~ every other entry point
+quantizes for the same rows and factors.
+"""
+
+import numpy as np
+import torch
+
+import oracle
+
+XT_BOUND_FACTOR = 8.0
+
+
+def xt_bound(x32, P1, P2):
+    """8 (n1 + n2) 2^-24 |P1|^T |X| |P2| per element, fp64, [rows][K]."""
+    n1, n2 = P1.shape[0], P2.shape[0]
+    ax = np.abs(np.asarray(x32, dtype=np.float64))
+    mag = oracle.kron_transform(ax, np.abs(P1), np.abs(P2))
+    return XT_BOUND_FACTOR * (n1 + n2) * 2.0 ** -24 * mag
+
+
+def check_xt(dump, x32, P1, P2):
+    """Assert part 1 for the rows of ``dump`` (fp32 [rows][K]) whose inputs are
+    ``x32``; returns the largest |error| / bound seen."""
+    want = oracle.kron_transform(x32, P1, P2)
+    err = np.abs(np.asarray(dump, dtype=np.float64) - want)
+    bound = xt_bound(x32, P1, P2)
+    ratio = float(np.max(err / np.maximum(bound, 1e-300)))
+    assert np.all(err <= bound), f"x~ outside the fp32-class bound (max error/bound {ratio:.3f})"
+    return ratio
+
+
+def gpu_xt(lq, xdev, x32, P1, P2):
+    """The kernel's x~ for the rows of ``xdev`` ([rows][K] on the device, fp32
+    or bf16; ``x32`` its fp32 values on the host), checked against the bound.
+    With no transform it is x itself."""
+    x32 = np.asarray(x32, dtype=np.float32).reshape(xdev.shape[0], -1)
+    if P1 is None:
+        return x32
+    rows, K = xdev.shape
+    codes = torch.empty((rows, K), dtype=torch.int8, device="cuda")
+    scales = torch.empty((rows, K // 32), dtype=torch.float32, device="cuda")
+    xt = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+    lq.loopq_quant_act(xdev, torch.from_numpy(np.ascontiguousarray(P1)).cuda(),
+                       torch.from_numpy(np.ascontiguousarray(P2)).cuda(), 1.0, 4, codes, scales, xt)
+    torch.cuda.synchronize()
+    dump = xt.cpu().numpy()
+    check_xt(dump, x32, P1, P2)
+    return dump
