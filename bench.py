@@ -213,14 +213,14 @@ def decode_bench(lq, synth, torch, M, T, steps):
         decode_loop_step(lq, mods, i % T)
     torch.cuda.synchronize()
     lq.loopq_timing_enable(False)
-    kern = lq.loopq_timing_read(3)
+    kern = lq.loopq_timing_read(4)
+    launches = sum(n for _, n in kern) / steps
     t0 = time.perf_counter()
     for i in range(steps):
         decode_loop_step(lq, mods, i % T)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    gemv_ms = kern[lq.LOOPQ_KERNEL_GEMM][0] / steps
-    quant_ms = kern[lq.LOOPQ_KERNEL_QUANT_TRANSFORM][0] / steps
+    fused_ms = kern[lq.LOOPQ_KERNEL_DECODE][0] / steps  # the few-row kernel (one launch per call where it can)
     # the same loop-steps replayed from a captured graph (launch gaps only):
     # loops 0..T-1 once each per replay; outputs checked against eager runs
     eager_ref = []
@@ -272,10 +272,10 @@ def decode_bench(lq, synth, torch, M, T, steps):
         "ms_per_loop_step": wall * 1e3,
         "gbps_per_loop_step": step_bytes / wall / 1e9,
         "frac_hbm_peak": step_bytes / wall / 1e9 / HBM_PEAK_GBS,
-        "kernel_ms_per_loop_step": {"quant_transform": quant_ms, "gemv": gemv_ms},
-        "gemv_gbps": DECODE_LAYERS * per_layer_bytes / (gemv_ms * 1e-3) / 1e9,
-        "gemv_frac_hbm_peak": DECODE_LAYERS * per_layer_bytes / (gemv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "launches_per_loop_step": 2 * DECODE_LAYERS * len(mods),
+        "kernel_ms_per_loop_step": {"decode": fused_ms,
+                                    "transform_items_and_quantizer": sum(kern[k][0] for k in (
+                                        lq.LOOPQ_KERNEL_QUANT_TRANSFORM, lq.LOOPQ_KERNEL_QUANT_PLAIN)) / steps},
+        "launches_per_loop_step": launches,
         "bytes_per_loop_step": step_bytes,
         "graph_ms_per_loop_step": graph_wall * 1e3,
         "graph_gbps_per_loop_step": step_bytes / graph_wall / 1e9,

@@ -93,7 +93,6 @@ int code_format(int bits_a) { return bits_a == 4 && !force_int8_gemm() ? kCodesT
 //   codes  : chunks * padded(rows) rows in the tiled layout, row_bytes(K)
 //            per row (enough for either tiled format)
 //   scales : fp32 group-major, chunks * padded(rows) columns
-//   xt     : fp32 x~ rows of the few-row transform (launches of <= 16 rows)
 //   wexp   : weights expanded to fp6 operands (W4A4 kernel only)
 // The same region also holds all chunks * rows rows as one contiguous tiled
 // matrix (padded(chunks * rows) <= chunks * padded(rows)).
@@ -101,7 +100,7 @@ struct ActBuffers {
   void* codes;
   float* scales;
   void* wexp;
-  float* xt;  // x~ rows of the few-row transform
+  float* xt;  // x~ rows of the few-row path
   int ld;
 };
 
@@ -118,10 +117,11 @@ size_t scales_region(int64_t chunks, int64_t rows, int64_t K) {
 size_t wexp_region(int64_t K, int64_t N, int fmt) {
   return fmt == kCodesTiledF6 ? align256((size_t)(padded_cols(N) / 32 * group_pairs(K) * kF6BlockBytes)) : 0;
 }
-// x~ rows of the few-row transform: a launch of at most kGemvMaxRows rows
+// x~ rows of the few-row (decode) path: one launch of all chunks * rows rows
+// when they are few enough, else launches of `rows` rows
 size_t xt_region(int64_t chunks, int64_t rows, int64_t K) {
-  if (rows > kGemvMaxRows) return 0;
-  const int64_t r = chunks * rows < kGemvMaxRows ? chunks * rows : kGemvMaxRows;
+  if (rows > kDecodeMaxRows) return 0;
+  const int64_t r = chunks * rows <= kDecodeMaxRows ? chunks * rows : rows;
   return align256((size_t)(r * K * 4));
 }
 size_t act_bytes(int64_t chunks, int64_t rows, int64_t K, int64_t N, int fmt) {
@@ -131,7 +131,8 @@ size_t act_bytes(int64_t chunks, int64_t rows, int64_t K, int64_t N, int fmt) {
 
 // buffers of chunk c (rows rows each), or with all_rows > 0 the whole
 // all_rows-row matrix starting at the region's base
-ActBuffers carve(void* ws, int64_t chunks, int64_t rows, int64_t K, int64_t c, int64_t all_rows) {
+ActBuffers carve(void* ws, int64_t chunks, int64_t rows, int64_t K, int64_t N, int64_t c,
+                 int64_t all_rows) {
   ActBuffers b;
   char* base = reinterpret_cast<char*>(ws);
   const int64_t mp = padded_rows(rows);
@@ -273,34 +274,92 @@ QuantArgs internal_quant_args(const void* x, int dtype, int rows, int K, const f
   return a;
 }
 
+// Few rows (decode): the few-row kernel, in one launch where it can.
+// x [rows][K] with row r taking clips.c[r / rows_per_clip].
+hipError_t run_decode(const void* x, int dtype, int rows, int K, int N, const float* P1, int n1,
+                      const float* P2, int n2, const ClipTable& clips, int rows_per_clip,
+                      int bits_a, const void* w_codes, const void* w_scales, int gw, float* y,
+                      const ActBuffers& b, hipStream_t s) {
+  DecodeCall c;
+  memset(&c, 0, sizeof(c));
+  c.R = rows;
+  c.K = K;
+  c.N = N;
+  c.clips = clips;
+  c.rows_per_clip = rows_per_clip;
+  c.qmax = bits_a == 4 ? 7 : 127;
+  c.w = reinterpret_cast<const uint8_t*>(w_codes);
+  c.sw = reinterpret_cast<const __half*>(w_scales);
+  c.gw = gw;
+  c.y = y;
+  c.mode = 0;
+  // one launch: a transform it repeats per work-group cheaply, or at most 4
+  // rows quantized in place; otherwise the activations are quantized once
+  // (transform items, then the plain quantizer, or the chunked quantizer for
+  // a factor shape without items) and the kernel copies canonical codes
+  const bool one = P1 != nullptr ? decode_transform_fused(rows, n1, n2) : rows <= 4;
+  if (!one) {
+    QuantArgs a = make_quant_args(x, dtype, rows, K, P1, n1, P2, n2, bits_a);
+    a.clips = clips;
+    a.rows_per_clip = rows_per_clip;
+    a.codes = reinterpret_cast<int8_t*>(b.codes);
+    a.codes_fmt = kCodesCanonical;
+    a.scales = b.scales;
+    a.scales_gm = 0;
+    hipError_t e = hipSuccess;
+    if (P1 != nullptr && decode_transform_items(n1, n2)) {
+      {
+        TimingScope ts(LOOPQ_KERNEL_QUANT_TRANSFORM, s);
+        e = launch_decode_items(x, dtype == LOOPQ_BF16, P1, n1, P2, n2, rows, b.xt, s);
+      }
+      if (e != hipSuccess) return e;
+      a.x = b.xt;
+      a.bf16 = 0;
+      a.P1 = a.P2 = nullptr;
+      a.n1 = a.n2 = 0;
+    }
+    {
+      TimingScope ts(a.P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, s);
+      e = launch_quant_act(a, s);
+    }
+    if (e != hipSuccess) return e;
+    c.a_codes = reinterpret_cast<const int8_t*>(b.codes);
+    c.a_steps = b.scales;
+  } else {
+    c.x = x;
+    c.bf16 = dtype == LOOPQ_BF16;
+    c.P1 = P1;
+    c.P2 = P2;
+    c.n1 = n1;
+    c.n2 = n2;
+  }
+  TimingScope ts(LOOPQ_KERNEL_DECODE, s);
+  return launch_decode(c, s);
+}
+
 // weight-stationary: quantize all `rows` rows, then one GEMM pass over the
-// weights for all of them
+// weights for all of them (few rows: the fused decode kernel)
 int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const float* P1, int n1,
                     const float* P2, int n2, const ClipTable& clips, int rows_per_clip, int bits_a,
                     const void* w_codes, const void* w_scales, int gw, float* y, void* ws,
                     int64_t ws_chunks, int64_t ws_rows, hipStream_t s) {
-  ActBuffers b = carve(ws, ws_chunks, ws_rows, K, 0, rows);
+  ActBuffers b = carve(ws, ws_chunks, ws_rows, K, N, 0, rows);
+  if (rows <= kDecodeMaxRows)
+    return hip_status(run_decode(x, dtype, rows, K, N, P1, n1, P2, n2, clips, rows_per_clip, bits_a,
+                                 w_codes, w_scales, gw, y, b, s));
   QuantArgs a = internal_quant_args(x, dtype, rows, K, P1, n1, P2, n2, clips, rows_per_clip,
                                     bits_a, b);
-  const bool small = rows <= kGemvMaxRows;  // decode: the small-row kernel on canonical codes
-  if (small) {
-    a.codes_fmt = kCodesCanonical;
-    a.scales_gm = 0;
-  }
   const int fmt = code_format(bits_a);
-  hipError_t e = small ? hipSuccess : prepare_weights(b, fmt, w_codes, K, N, s);
+  hipError_t e = prepare_weights(b, fmt, w_codes, K, N, s);
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   {
     TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, s);
-    e = small ? launch_quant_act_few(a, b.xt, s) : launch_quant_act(a, s);
+    e = launch_quant_act(a, s);
   }
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   {
     TimingScope ts(LOOPQ_KERNEL_GEMM, s);
-    e = small ? launch_gemv(reinterpret_cast<const int8_t*>(b.codes), b.scales, rows, K, N,
-                            reinterpret_cast<const uint8_t*>(w_codes),
-                            reinterpret_cast<const __half*>(w_scales), gw, y, nullptr, 0, s)
-              : run_gemm(b, fmt, rows, K, N, w_codes, w_scales, gw, y, nullptr, 0, s);
+    e = run_gemm(b, fmt, rows, K, N, w_codes, w_scales, gw, y, nullptr, 0, s);
   }
   return hip_status(e);
 }
@@ -312,14 +371,25 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
                          int n1, const float* P2, int n2, const ClipTable& clips, int bits_a,
                          const void* w_codes, const void* w_scales, int gw, float* y, void* ws,
                          hipStream_t s) {
+  const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
+  if (M <= kDecodeMaxRows) {  // decode: one fused launch per loop, in loop order on `stream`
+    for (int t = 0; t < T; ++t) {
+      ClipTable one;
+      memset(&one, 0, sizeof(one));
+      one.c[0] = clips.c[t];
+      const void* xt = reinterpret_cast<const char*>(x) + (size_t)t * M * K * esz;
+      hipError_t e = run_decode(xt, dtype, M, K, N, P1, n1, P2, n2, one, M, bits_a, w_codes, w_scales,
+                                gw, y + (size_t)t * M * N, carve(ws, T, M, K, N, 0, 0), s);
+      if (e != hipSuccess) return LOOPQ_ERR_HIP;
+    }
+    return LOOPQ_OK;
+  }
   std::lock_guard<std::mutex> lk(g_pipe_mu);
   DevicePipe* p = nullptr;
   if (device_pipe(&p, T + 1) != hipSuccess) return LOOPQ_ERR_HIP;
   const int fmt = code_format(bits_a);
-  const bool small = M <= kGemvMaxRows;  // decode: the small-row kernel on canonical codes
-  if (!small && prepare_weights(carve(ws, T, M, K, 0, 0), fmt, w_codes, K, N, s) != hipSuccess)
+  if (prepare_weights(carve(ws, T, M, K, N, 0, 0), fmt, w_codes, K, N, s) != hipSuccess)
     return LOOPQ_ERR_HIP;
-  const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
   hipEvent_t start = p->events[T];
   if (hipEventRecord(start, s) != hipSuccess) return LOOPQ_ERR_HIP;
   if (hipStreamWaitEvent(p->aux, start, 0) != hipSuccess) return LOOPQ_ERR_HIP;
@@ -327,32 +397,24 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
     ClipTable one;
     memset(&one, 0, sizeof(one));
     one.c[0] = clips.c[t];
-    ActBuffers b = carve(ws, T, M, K, t, 0);
+    ActBuffers b = carve(ws, T, M, K, N, t, 0);
     const void* xt = reinterpret_cast<const char*>(x) + (size_t)t * M * K * esz;
     QuantArgs a = internal_quant_args(xt, dtype, M, K, P1, n1, P2, n2, one, M, bits_a, b);
-    if (small) {
-      a.codes_fmt = kCodesCanonical;
-      a.scales_gm = 0;
-    }
     hipError_t e;
     {
       TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, p->aux);
-      e = small ? launch_quant_act_few(a, b.xt, p->aux) : launch_quant_act(a, p->aux);
+      e = launch_quant_act(a, p->aux);
     }
     if (e != hipSuccess) return LOOPQ_ERR_HIP;
     if (hipEventRecord(p->events[t], p->aux) != hipSuccess) return LOOPQ_ERR_HIP;
   }
   for (int t = 0; t < T; ++t) {
     if (hipStreamWaitEvent(s, p->events[t], 0) != hipSuccess) return LOOPQ_ERR_HIP;
-    ActBuffers b = carve(ws, T, M, K, t, 0);
+    ActBuffers b = carve(ws, T, M, K, N, t, 0);
     hipError_t e;
     {
       TimingScope ts(LOOPQ_KERNEL_GEMM, s);
-      float* yt = y + (size_t)t * M * N;
-      e = small ? launch_gemv(reinterpret_cast<const int8_t*>(b.codes), b.scales, M, K, N,
-                              reinterpret_cast<const uint8_t*>(w_codes),
-                              reinterpret_cast<const __half*>(w_scales), gw, yt, nullptr, 0, s)
-                : run_gemm(b, fmt, M, K, N, w_codes, w_scales, gw, yt, nullptr, 0, s);
+      e = run_gemm(b, fmt, M, K, N, w_codes, w_scales, gw, y + (size_t)t * M * N, nullptr, 0, s);
     }
     if (e != hipSuccess) return LOOPQ_ERR_HIP;
   }
@@ -545,10 +607,23 @@ int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
-  if (M <= kGemvMaxRows)  // decode: the small-row kernel reads the canonical codes directly
-    return hip_status(launch_gemv(a_codes, a_scales, M, K, N, reinterpret_cast<const uint8_t*>(w_codes),
-                                  reinterpret_cast<const __half*>(w_scales), group_w, y, nullptr, 0, s));
-  ActBuffers b = carve(workspace, 1, M, K, 0, M);
+  ActBuffers b = carve(workspace, 1, M, K, N, 0, M);
+  if (M <= kDecodeMaxRows) {  // decode: the fused kernel reads the canonical codes directly
+    DecodeCall c;
+    memset(&c, 0, sizeof(c));
+    c.a_codes = a_codes;
+    c.a_steps = a_scales;
+    c.R = M;
+    c.K = K;
+    c.N = N;
+    c.qmax = bits_a == 4 ? 7 : 127;
+    c.w = reinterpret_cast<const uint8_t*>(w_codes);
+    c.sw = reinterpret_cast<const __half*>(w_scales);
+    c.gw = group_w;
+    c.y = y;
+    c.mode = 0;
+    return hip_status(launch_decode(c, s));
+  }
   hipError_t e = launch_tile_codes(a_codes, a_scales, M, K, b.codes, fmt, b.scales, b.ld, s);
   if (e == hipSuccess) e = prepare_weights(b, fmt, w_codes, K, N, s);
   if (e == hipSuccess) e = run_gemm(b, fmt, M, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s);
@@ -583,10 +658,21 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
-  if (M <= kGemvMaxRows)  // the kernel the forward uses for this many rows
-    return hip_status(launch_gemv(a_codes, nullptr, M, K, N, reinterpret_cast<const uint8_t*>(w_codes),
-                                  nullptr, 32, nullptr, dots, 1, s));
-  ActBuffers b = carve(workspace, 1, M, K, 0, M);
+  ActBuffers b = carve(workspace, 1, M, K, N, 0, M);
+  if (M <= kDecodeMaxRows) {  // the kernel the forward uses for this many rows
+    DecodeCall c;
+    memset(&c, 0, sizeof(c));
+    c.a_codes = a_codes;
+    c.R = M;
+    c.K = K;
+    c.N = N;
+    c.qmax = bits_a == 4 ? 7 : 127;
+    c.w = reinterpret_cast<const uint8_t*>(w_codes);
+    c.gw = 32;
+    c.dots = dots;
+    c.mode = 1;
+    return hip_status(launch_decode(c, s));
+  }
   hipError_t e = launch_tile_codes(a_codes, nullptr, M, K, b.codes, fmt, nullptr, b.ld, s);
   if (e == hipSuccess) e = prepare_weights(b, fmt, w_codes, K, N, s);
   if (e == hipSuccess) e = run_gemm(b, fmt, M, K, N, w_codes, nullptr, 32, nullptr, dots, 1, s);

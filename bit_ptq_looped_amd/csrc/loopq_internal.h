@@ -128,12 +128,6 @@ struct QuantArgs {
 hipError_t launch_quant_act(QuantArgs a, hipStream_t s);
 // true if the fused transform kernel's LDS plan fits one work-group
 bool quant_plan_fits(int K, int n1, int n2);
-// Few rows (decode): with a transform of one of the compile-time factor
-// shapes, one work-group per (row, 16-column tile) forms x~ into xt_buf
-// ([rows][K] fp32, bitwise the chunked kernel's x~) and a second launch
-// quantizes it; otherwise the same as launch_quant_act.
-hipError_t launch_quant_act_few(QuantArgs a, float* xt_buf, hipStream_t s);
-
 hipError_t launch_pack_weights(const float* w, int K, int N, int gw, uint8_t* codes,
                                __half* scales, hipStream_t s);
 hipError_t launch_export_weights(const uint8_t* codes, const __half* scales, int K, int N, int gw,
@@ -160,13 +154,41 @@ hipError_t launch_gemm(const int8_t* a_tiled, const float* a_scales_gm, int ld_s
                        int N, const uint8_t* w_codes, const __half* w_scales, int gw, float* y,
                        int32_t* dots, int mode, hipStream_t s);
 
-// Small-row (decode) GEMM: rows <= kGemvMaxRows token rows, canonical int8
-// codes [R][K] with row-major steps [R][K/32], packed weights read directly.
-// mode 0: y [R][N]; mode 1: int32 group dots [R][N][K/32].
-constexpr int kGemvMaxRows = 16;
-hipError_t launch_gemv(const int8_t* a_canon, const float* a_scales, int R, int K, int N,
-                       const uint8_t* w_codes, const __half* w_scales, int gw, float* y,
-                       int32_t* dots, int mode, hipStream_t s);
+// Few-row (decode) linear in one launch: at most kDecodeMaxRows token rows
+// of x (quantized in the launch, after an optional transform of one of the
+// compiled-in factor shapes) or of canonical codes and steps, times the
+// packed weights.  mode 0: y [R][N]; mode 1 (codes only): int32 group dots
+// [R][N][K/32].  No workspace.
+constexpr int kDecodeMaxRows = 16;
+struct DecodeCall {
+  const void* x;          // [R][K] fp32 or bf16, or null with codes
+  int bf16;
+  const int8_t* a_codes;  // canonical codes [R][K] (instead of x)
+  const float* a_steps;   // row-major steps [R][K/32]
+  const float* P1;        // factors or null
+  const float* P2;
+  int n1, n2;
+  int R, K, N;
+  ClipTable clips;        // row r uses clips.c[r / rows_per_clip]
+  int rows_per_clip;
+  int qmax;
+  const uint8_t* w;       // packed weights
+  const __half* sw;
+  int gw;
+  float* y;
+  int32_t* dots;
+  int mode;
+};
+// true if one launch takes this transform for R rows (a compiled-in factor
+// shape, and the transform repeated per work-group cheap enough)
+bool decode_transform_fused(int R, int n1, int n2);
+// true if the factor shape is compiled in; then launch_decode_items writes x~
+// of R rows ([R][K] fp32, bitwise the chunked kernel's) with one work-group
+// per (row, 16-column tile of the n1 x n2 grid)
+bool decode_transform_items(int n1, int n2);
+hipError_t launch_decode_items(const void* x, int bf16, const float* P1, int n1, const float* P2, int n2,
+                               int R, float* xt, hipStream_t s);
+hipError_t launch_decode(const DecodeCall& c, hipStream_t s);
 
 // status word shared by the synchronizing offline calls
 hipError_t reset_status(hipStream_t s);

@@ -21,87 +21,15 @@
 // GEMM layout one group per lane, for the other layouts 8 lanes per group, 4
 // elements per lane, absmax reduced across the 8 lanes.
 #include "loopq_internal.h"
+#include "quant_core.h"
 
 #include <type_traits>
 
 namespace loopq {
 namespace {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v6i __attribute__((ext_vector_type(6)));
-
-// v if mask is all ones, +0 if it is zero (bitwise, so no branch is formed)
-__device__ __forceinline__ float masked(float v, uint32_t mask) {
-  return __uint_as_float(__float_as_uint(v) & mask);
-}
-
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
-}
-
-// max over the 8 consecutive lanes of a group: quad swaps 1 and 2, then the
-// half-row mirror pairs each lane with one of the other quad (DPP, no LDS)
-__device__ __forceinline__ float group8_max(float v) {
-  int b = __float_as_int(v);
-  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false))));
-  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false))));
-  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x141, 0xF, 0xF, false))));
-  return __int_as_float(b);
-}
-
-// Quantize 4 consecutive elements of one 32-group whose 8 lanes are
-// consecutive in the wave (lane % 8 = position of the 4-element run).
-// Returns the 4 codes packed as int8 bytes; writes the step to *step.
-//
-// The step: base = fl32(absmax / qmax) is formed as q0 = fl32(absmax * rq)
-// with rq = fl32(1 / qmax), then one FMA correction q0 + (absmax - q0 qmax) rq;
-// for qmax = 7 and 127 this equals the correctly rounded quotient for every
-// finite non-negative fp32 absmax (checked exhaustively over all of them).
-// s = fl32(c * base).
-//
-// The codes: clamp(rint(fl32(x / s)), -qmax, qmax).  The quotient is formed
-// as p = fl32(x * r) with r the hardware reciprocal of s (within 1 ulp):
-// |p - x/s| < 3 * 2^-24 |x/s| and |fl32(x/s) - x/s| <= 2^-24 |x/s|, so below
-// the clamp (|x/s| < 128) p and fl32(x/s) differ by less than 2^-15.  The
-// distance d = |x * r - rint(p)| is taken with one FMA (within 2^-17 of
-// |p - rint(p)|); if d <= 0.5 - 2^-14 then fl32(x/s) lies within
-// 0.5 - 3 * 2^-17 of rint(p) and rounds to the same integer.  Runs with a
-// larger d, and any run whose r is not a positive finite normal-range value
-// (s outside about [2^-126, 2^126]), are redone with the correctly rounded
-// division.  Above the clamp both sides saturate alike.
-__device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf, float rq, float* step) {
-  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  amax = group8_max(amax);
-  const float q0 = amax * rq;
-  const float base = __builtin_fmaf(__builtin_fmaf(-q0, qmaxf, amax), rq, q0);  // = fl32(amax / qmax)
-  const float s = clip * base;      // one fp32 product
-  *step = s;
-  if (!(s > 0.0f)) return 0u;
-  const float r = __builtin_amdgcn_rcpf(s);
-  const float e[4] = {v.x, v.y, v.z, v.w};
-  uint32_t packed = 0u;
-  bool exact = !(r > 1.0e-37f && r < 1.0e37f);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = e[i] * r;
-    const float rq_ = __builtin_rintf(p);
-    // runs above the clamp may take the exact path too; both sides clamp
-    exact |= fabsf(__builtin_fmaf(e[i], r, -rq_)) > 0.5f - 6.103515625e-05f;
-    const float q = __builtin_amdgcn_fmed3f(rq_, -qmaxf, qmaxf);
-    packed |= (uint32_t)((int)q & 0xff) << (8 * i);
-  }
-  if (exact) {  // rare: near a rounding boundary, or s extreme
-    packed = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float q = __builtin_rintf(e[i] / s);  // ties to even
-      q = fminf(fmaxf(q, -qmaxf), qmaxf);
-      packed |= (uint32_t)((int)q & 0xff) << (8 * i);
-    }
-  }
-  return packed;
-}
 
 // Position of flat element f of a chunk's transformed rows in LDS: the eight
 // 16-byte quarters of each 32-element group are rotated by the group index,
@@ -238,21 +166,6 @@ __global__ __launch_bounds__(256) void quant_plain_kernel(QuantArgs a) {
     if (valid) store_run(a, row, k0, packed, s, (lane & 7) == 0, v);
   }
 }
-
-// LDS strides (elements) of P1, P2 and the X rows: P rows padded to 16 mod
-// 32 and X rows to 2 mod 32 so the 16 lanes of an MFMA operand read fall on
-// distinct banks.  For compile-time factor shapes the kernel uses these
-// constants (every LDS offset then folds into the instruction); the host plan
-// uses the same values for those shapes.
-constexpr int stride_to(int n, int rem) { return n + ((rem - n) % 32 + 32) % 32; }
-constexpr int p_stride(int n) { return n <= 16 ? 16 : stride_to(n, 16); }
-constexpr int x_stride(int n2) { return stride_to(n2, 2); }
-template <int N1, int N2>
-struct XStrides {
-  static constexpr int sp1 = N1 > 0 ? p_stride(N1) : 0;
-  static constexpr int sp2 = N2 > 0 ? p_stride(N2) : 0;
-  static constexpr int sx = N2 > 0 ? x_stride(N2) : 0;
-};
 
 // Work item of slot ii of a wave.  SR (shared row): a wave's NIM slots are
 // consecutive items, all in one row of the chunk (the row's column-tile count
@@ -678,104 +591,6 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   }
 }
 
-// Few-row form of the transform (decode: a handful of rows).  One
-// work-group per work item (row r, 16-column tile jt): wave w computes the
-// stage-1 tile T[16w .. 16w + 15][tile jt] with the full reduction over b,
-// stores it in LDS, and after a barrier computes the stage-2 tile x~[16w ..
-// 16w + 15][tile jt] with the full reduction over a.  Operands and MFMA order
-// are those of the chunked kernel, so x~ is bitwise the same; it is written
-// rounded to fp32 to `xt` ([rows][K]) and quantized by a second launch.
-// LDS: P1 [n1][sp1] f32, the P2 columns of the tile [n2][16] f32, the row of
-// X [n1][sx] f32 and T [n1][16] f32.
-template <int NRT, int N1, int N2>
-__global__ __launch_bounds__(256) void xform_items_kernel(QuantArgs a, float* __restrict__ xt) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  constexpr int n1 = N1, n2 = N2, K = N1 * N2;
-  constexpr int sp1 = XStrides<N1, N2>::sp1, sx = XStrides<N1, N2>::sx;
-  constexpr int njt = (N2 + 15) / 16;
-  constexpr int off_p2 = (n1 * sp1 * 4 + 15) / 16 * 16;
-  constexpr int off_x = off_p2 + n2 * 16 * 4;
-  constexpr int off_t = (off_x + n1 * sx * 4 + 15) / 16 * 16;
-  float* sP1 = reinterpret_cast<float*>(lds);
-  float* sP2 = reinterpret_cast<float*>(lds + off_p2);
-  float* sX = reinterpret_cast<float*>(lds + off_x);
-  float* sT = reinterpret_cast<float*>(lds + off_t);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int li = lane & 15;
-  const int lk = lane >> 4;
-  const int r = blockIdx.x / njt;
-  const int jt = blockIdx.x - r * njt;
-
-  for (int idx = tid; idx < n1 * n1; idx += 256) sP1[(idx / n1) * sp1 + idx % n1] = a.P1[idx];
-  for (int idx = tid; idx < n2 * 16; idx += 256) {
-    const int b = idx >> 4, j = jt * 16 + (idx & 15);
-    sP2[idx] = j < n2 ? a.P2[b * n2 + j] : 0.0f;
-  }
-  for (int q = tid; q < K / 4; q += 256) {
-    const int k = q * 4;
-    const int64_t gi = (int64_t)r * K + k;
-    float4 v;
-    if (a.bf16) {
-      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + gi);
-      v = float4{bf16_bits_to_float(u.x & 0xffffu), bf16_bits_to_float(u.x >> 16),
-                 bf16_bits_to_float(u.y & 0xffffu), bf16_bits_to_float(u.y >> 16)};
-    } else {
-      v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + gi);
-    }
-    float* dst = sX + (k / n2) * sx + k % n2;
-    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
-  }
-  __syncthreads();
-
-  // stage 1: T[rt] = X_r * P2[:, tile], steps of b in order (as the chunked kernel)
-  for (int rt = wave; rt < NRT; rt += 4) {
-    v4f T = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float* xa = sX + min(rt * 16 + li, n1 - 1) * sx;
-    const uint32_t mrow = (rt * 16 + li < n1) ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int st = 0; st < N2 / 4; ++st) {
-      const int b = 4 * st + lk;
-      const float av = masked(xa[b], mrow);
-      const float bv = sP2[b * 16 + li];  // zero past n2
-      T = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, T, 0, 0, 0);
-    }
-    // result element e of lane l: row 16 rt + 4 (l / 16) + e, column l % 16
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = rt * 16 + 4 * lk + e;
-      if (row < n1) sT[row * 16 + li] = T[e];
-    }
-  }
-  __syncthreads();
-
-  // stage 2: x~[it][tile] = sum_a P1[a][it] T[a][tile], steps of a in order
-  for (int it = wave; it < NRT; it += 4) {
-    v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int i = it * 16 + li;
-    const uint32_t mi = i < n1 ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int st = 0; st < 4 * NRT; ++st) {
-      // the chunked kernel's order over a, rows >= n1 masked as there
-      const int ar = 16 * (st >> 2) + 4 * lk + (st & 3);
-      const int ac = min(ar, n1 - 1);
-      const float av = masked(sP1[ac * sp1 + min(i, n1 - 1)], ar < n1 ? mi : 0u);
-      const float bv = sT[ac * 16 + li];
-      o = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, o, 0, 0, 0);
-    }
-    const int j = jt * 16 + li;
-    if (j < n2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int io = it * 16 + 4 * lk + e;
-        if (io < n1) xt[(int64_t)r * K + io * n2 + j] = o[e];
-      }
-    }
-  }
-}
-
 }  // namespace
 
 namespace {
@@ -786,18 +601,6 @@ int x_bytes_for(int R, int n1, int sx, int K) {
   return (xb + 15) / 16 * 16;
 }
 
-// Factor shapes of the Kronecker transforms in use (K = 256, 2048, 5632,
-// 2560, 6912, and a 32-wide test shape), each with its rows per chunk and the
-// most work items a wave then takes.  Chunk sizes make rows * ceil(n2 / 16)
-// items a multiple of the 4 waves where that fits (3 items per wave for
-// (64, 88) at 2 rows; (64, 108) has 7 per row and stays at one row).
-#define LOOPQ_SHAPES(X) \
-  X(16, 16, 16, 4)      \
-  X(32, 64, 4, 4)       \
-  X(64, 88, 2, 3)       \
-  X(40, 64, 3, 3)       \
-  X(64, 108, 1, 2)      \
-  X(4, 8, 16, 4)
 
 // LDS plan of the fused transform kernel: P1 and P2 with strides that put the
 // 16 lanes of an MFMA operand read on distinct banks, and R rows of X with a
@@ -868,45 +671,6 @@ bool quant_plan_fits(int K, int n1, int n2) {
   a.n1 = n1;
   a.n2 = n2;
   return plan_quant(a);
-}
-
-bool xform_items_supported(int n1, int n2) {
-#define LOOPQ_ITEM_SHAPE(n1_, n2_, rs_, nim_) \
-  if (n1 == n1_ && n2 == n2_) return true;
-  LOOPQ_SHAPES(LOOPQ_ITEM_SHAPE)
-#undef LOOPQ_ITEM_SHAPE
-  return false;
-}
-
-hipError_t launch_quant_act_few(QuantArgs a, float* xt_buf, hipStream_t s) {
-  if (a.rows <= 0) return hipSuccess;
-  if (a.P1 != nullptr && xform_items_supported(a.n1, a.n2)) {
-    const void* fn = nullptr;
-    int lds = 0;
-#define LOOPQ_ITEM_KERNEL(n1_, n2_, rs_, nim_)                                                      \
-    if (a.n1 == n1_ && a.n2 == n2_) {                                                               \
-      fn = reinterpret_cast<const void*>(xform_items_kernel<(n1_ + 15) / 16, n1_, n2_>);           \
-      constexpr int sp1 = XStrides<n1_, n2_>::sp1, sx = XStrides<n1_, n2_>::sx;                    \
-      constexpr int off_x = (n1_ * sp1 * 4 + 15) / 16 * 16 + n2_ * 16 * 4;                         \
-      lds = (off_x + n1_ * sx * 4 + 15) / 16 * 16 + n1_ * 16 * 4;                                 \
-    }
-    LOOPQ_SHAPES(LOOPQ_ITEM_KERNEL)
-#undef LOOPQ_ITEM_KERNEL
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    const int items = a.rows * ((a.n2 + 15) / 16);
-    void* args[] = {&a, &xt_buf};
-    e = hipLaunchKernel(fn, dim3(items), dim3(256), args, lds, s);
-    if (e != hipSuccess) return e;
-    // then quantize the transformed rows as plain fp32 input
-    QuantArgs q = a;
-    q.x = xt_buf;
-    q.bf16 = 0;
-    q.P1 = q.P2 = nullptr;
-    q.n1 = q.n2 = 0;
-    return launch_quant_act(q, s);
-  }
-  return launch_quant_act(a, s);
 }
 
 hipError_t launch_quant_act(QuantArgs a, hipStream_t s) {

@@ -29,7 +29,7 @@ LOOPQ_ERR_SINGULAR = -7
 LOOPQ_F32, LOOPQ_BF16 = 0, 1
 LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
 LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD = 1, 2, 3
-LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM = 0, 1, 2
+LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM, LOOPQ_KERNEL_DECODE = 0, 1, 2, 3
 
 # every entry point of include/loopq.h with its ctypes signature
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -219,7 +219,7 @@ def loopq_timing_reset() -> None:
     _check(load().loopq_timing_reset(), "loopq_timing_reset")
 
 
-def loopq_timing_read(n: int = 3):
+def loopq_timing_read(n: int = 4):
     """Per kernel id: (total milliseconds, launches) since the last read."""
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_int64 * n)()

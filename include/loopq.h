@@ -217,7 +217,8 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
 typedef enum {
   LOOPQ_KERNEL_QUANT_TRANSFORM = 0, /* fused transform + quantizer */
   LOOPQ_KERNEL_QUANT_PLAIN = 1,     /* quantizer without transform */
-  LOOPQ_KERNEL_GEMM = 2             /* integer GEMM + rescale */
+  LOOPQ_KERNEL_GEMM = 2,            /* integer GEMM + rescale */
+  LOOPQ_KERNEL_DECODE = 3           /* few-row linear: transform, quantizer and product in one launch */
 } loopq_kernel_id;
 
 /* Turn the hooks on (1) or off (0).  Host only; cheap. */

@@ -352,3 +352,50 @@ def test_decode_shapes(lq, act, K, N, M, bits, schedule):
     xt = gpu_xt(lq, bf16_dev(bits16).view(T * M, K), x32.reshape(T * M, K), P1, P2).reshape(T, M, K)
     ref = oracle.looped_forward(xt, None, None, clips, bits, qw, sw, 32)
     assert rel_err(y.cpu().numpy(), ref) <= Y_TOL
+
+
+def test_decode_graph_replays_match_eager(lq):
+    """The fused few-row kernel keeps its synchronization words in static
+    device memory and clears them at the end of every launch, so calls can be
+    captured into a graph: every replay (with eager work between replays)
+    equals the eager result bit for bit, and the eager result equals the
+    oracle on the kernel's x~."""
+    K, N, M, T = 2048, 200, 1, 4
+    wl = synth.ouro_block_workload(bits_a=4, M=M, T=T)
+    P1, P2 = synth.factors_for(wl, "up_in", K)
+    clips = synth.clips_for(wl, "up_in")
+    bits16, x32 = synth.activations_for(wl, "up_in", K)
+    w = synth.gaussian((N, K), 160, K, N, scale=0.02)
+    codes, scales = pack(lq, w, 32)
+    x = bf16_dev(bits16)
+    tP1, tP2 = dev(P1), dev(P2)
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, 4)
+    y = torch.zeros((T, M, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        for schedule in (1, 2):
+            lq.loopq_looped_forward(x, tP1, tP2, clips, 4, codes, scales, 32, N, y, schedule, ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = y.clone()
+    qw, sw = oracle.quant_weights(w, 32)
+    xt = gpu_xt(lq, x.view(T * M, K), x32.reshape(T * M, K), P1, P2).reshape(T, M, K)
+    ref = oracle.looped_forward(xt, None, None, clips, 4, qw, sw, 32)
+    assert rel_err(eager.cpu().numpy(), ref) <= Y_TOL
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {rep}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)
