@@ -29,7 +29,7 @@ import torch
 
 import oracle
 from bit_ptq_looped_amd import synth
-from xt_check import check_xt
+from xt_check import check_xt, gpu_xt
 
 pytestmark = pytest.mark.gpu
 
@@ -168,3 +168,37 @@ def test_fullsize_huginn(lq, act):
 @pytest.mark.parametrize("act", OURO_INPUTS)
 def test_fullsize_large_prefill(lq, act):
     run_case(lq, synth.large_prefill_workload(T=4), act)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("act", OURO_INPUTS)
+def test_fullsize_decode(lq, act, M):
+    """Decode calls at the block's full N and K (the bench's decode stack), both
+    schedules: loop by loop (M rows per launch) and weight-stationary (T*M
+    rows per launch, where they fit the few-row kernel).  Every row and column
+    against the oracle applied to the kernel's x~."""
+    wl = synth.ouro_block_workload(bits_a=4, M=M, T=4)
+    lins = groups_by_input(wl)[act]
+    K = lins[0].K
+    W = np.concatenate([synth.weights_for(wl, lin) for lin in lins], axis=0)
+    N = W.shape[0]
+    P1, P2 = synth.factors_for(wl, act, K)
+    clips = synth.clips_for(wl, act)
+    T = wl.T
+    say(f"decode {act} K={K} N={N} M={M} T={T}")
+    codes, scales = lq.empty_packed_weights(K, N, 32)
+    lq.loopq_pack_weights(dev(W), 32, codes, scales)
+    qw, sw = oracle.quant_weights(W, 32)
+    bits, x32 = synth.activations_for(wl, act, K)
+    x = bf16_dev(bits)
+    xt = gpu_xt(lq, x.view(T * M, K), x32.reshape(T * M, K), P1, P2).reshape(T, M, K)
+    ref = oracle.looped_forward(xt, None, None, clips, 4, qw, sw, 32)
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, 4)
+    for schedule in (1, 2):
+        y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+        lq.loopq_looped_forward(x, dev(P1), dev(P2), clips, 4, codes, scales, 32, N, y, schedule, ws)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        say(f"  schedule {schedule}: rel err {err:.3e}")
+        assert err <= Y_TOL
