@@ -38,6 +38,18 @@ def haar_orthogonal(n: int, rng: np.random.Generator) -> np.ndarray:
     return q.astype(np.float32)
 
 
+def hadamard(n: int) -> np.ndarray:
+    """Normalized Sylvester-Hadamard matrix of order n (a power of two), entries
+    +-1/sqrt(n), as fp32: the Hadamard choice of a Kronecker factor ("Quantizing
+    Looped Transformers", rotation ablation, Table 14).  H_a kron H_b is H_ab."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return (h / np.sqrt(n)).astype(np.float32)
+
+
 def round_to_bf16(x: np.ndarray):
     """Round fp32 values to bf16 (nearest, ties to even).
 

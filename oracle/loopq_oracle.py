@@ -286,3 +286,27 @@ def looped_forward(xs, P1, P2, clips, bits: int, qw, sw16, group_w: int) -> np.n
         raise ValueError("one clip per loop")
     return np.stack([linear(xs[t], P1, P2, float(clips[t]), bits, qw, sw16, group_w)[0]
                      for t in range(T)])
+
+
+def looped_forward_sets(xs, factor_sets, clips, bits, weight_sets, group_w: int, sets) -> np.ndarray:
+    """The loop with loop-dependent pieces: loop t uses transform and weights of
+    set ``sets[t]`` and activation bit width ``bits[t]``.
+
+    SLT ("paper_specification.yaml", ``loopq_components.slt``): selected groups
+    receive loop-dependent transforms and weights, the others keep the shared
+    ones.  A per-loop activation bit width is the output of a loop-wise
+    precision allocation ("Quantisation errors can keep returning inside a
+    looped model", "Three components address three sources of mismatch").
+    ``factor_sets`` is a list of ``(P1, P2)`` (or ``(None, None)``),
+    ``weight_sets`` a list of ``(qw, sw16)``; returns fp64 ``[T][M][N]``."""
+    xs = np.asarray(xs)
+    T = xs.shape[0]
+    if not (len(clips) == len(bits) == len(sets) == T):
+        raise ValueError("one clip, bit width and set per loop")
+    out = []
+    for t in range(T):
+        P1, P2 = factor_sets[sets[t]]
+        qw, sw = weight_sets[sets[t]]
+        out.append(linear(xs[t], P1, P2, float(clips[t]), int(bits[t]), qw, sw, group_w)[0])
+    return np.stack(out)
+

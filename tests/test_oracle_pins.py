@@ -350,3 +350,61 @@ def test_bf16_inputs_round_to_nearest_even():
     bits, wide = synth.round_to_bf16(x)
     np.testing.assert_array_equal(wide, np.array([1.0, 1.0, 1.0 + 2 ** -6, -2.5, 1.0], dtype=np.float32))
     np.testing.assert_array_equal(bits, (wide.view(np.uint32) >> 16).astype(np.uint16))
+
+
+# ---------------------------------------------------------------- Hadamard factors
+
+def _fwht(x):
+    """Walsh-Hadamard transform of each row by butterflies (natural order),
+    unnormalized: x . H_K with H_K the Sylvester matrix of +-1."""
+    y = np.array(x, dtype=np.float64)
+    h = 1
+    K = y.shape[1]
+    while h < K:
+        for i in range(0, K, 2 * h):
+            a = y[:, i:i + h].copy()
+            b = y[:, i + h:i + 2 * h].copy()
+            y[:, i:i + h] = a + b
+            y[:, i + h:i + 2 * h] = a - b
+        h *= 2
+    return y
+
+
+@pytest.mark.parametrize("n1,n2", [(16, 16), (32, 64), (4, 8)])
+def test_hadamard_factors_give_the_walsh_hadamard_transform(n1, n2):
+    H1, H2 = synth.hadamard(n1), synth.hadamard(n2)
+    np.testing.assert_allclose(H1.astype(np.float64) @ H1.T.astype(np.float64), np.eye(n1), atol=1e-6)
+    x = synth.gaussian((5, n1 * n2), 170, n1, n2)
+    got = oracle.kron_transform(x, H1, H2)
+    # fp32 entries +-1/sqrt(n) carry the rounding of 1/sqrt(n) (exact for even log2 n)
+    want = _fwht(x) / np.sqrt(n1 * n2)
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-6 * np.abs(want).max())
+
+
+# ---------------------------------------------------------------- loop-dependent sets
+
+def test_looped_forward_sets_reduces_to_shared_and_to_single_linears():
+    wl = synth.tiny_workload()
+    lin = wl.linears[0]
+    xs, _ = synth.activations_for(wl, "x", lin.K)
+    clips = synth.clips_for(wl, "x")
+    P1, P2 = synth.factors_for(wl, "x", lin.K)
+    Q1, Q2 = synth.hadamard(16), synth.hadamard(16)
+    qw0, sw0 = oracle.quant_weights(synth.gaussian((lin.N, lin.K), 171, scale=0.02), 32)
+    qw1, sw1 = oracle.quant_weights(synth.gaussian((lin.N, lin.K), 172, scale=0.02), 32)
+    T = wl.T
+    # one set for every loop and one bit width: the shared looped forward
+    ys = oracle.looped_forward_sets(xs, [(P1, P2)], clips, [4] * T, [(qw0, sw0)], 32, [0] * T)
+    np.testing.assert_array_equal(ys, oracle.looped_forward(xs, P1, P2, clips, 4, qw0, sw0, 32))
+    # loop t on its own set and width: the single linear of that set
+    sets, bits = [0, 1, 1, 0], [4, 8, 4, 8]
+    ys = oracle.looped_forward_sets(xs, [(P1, P2), (Q1, Q2)], clips, bits, [(qw0, sw0), (qw1, sw1)], 32, sets)
+    for t in range(T):
+        F = [(P1, P2), (Q1, Q2)][sets[t]]
+        W = [(qw0, sw0), (qw1, sw1)][sets[t]]
+        y1, _, _ = oracle.linear(xs[t], F[0], F[1], float(clips[t]), bits[t], W[0], W[1], 32)
+        np.testing.assert_array_equal(ys[t], y1)
+    # the two sets differ, so the loops do too
+    assert not np.array_equal(ys[0], oracle.looped_forward_sets(xs[:1], [(Q1, Q2)], clips[:1], [4], [(qw1, sw1)], 32, [0])[0])
+    with pytest.raises(ValueError):
+        oracle.looped_forward_sets(xs, [(P1, P2)], clips, [4] * T, [(qw0, sw0)], 32, [0] * (T - 1))
