@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--profile-schedule", type=int, default=0,
                    help="schedule used by --profile-steps (0 auto, 1 loop-sequential, 2 weight-stationary)")
     p.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    p.add_argument("--no-loop-dependent", action="store_true",
+                   help="skip the loop-dependent (per-loop weight sets / bit widths) measurement")
     p.add_argument("--decode-steps", type=int, default=20)
     p.add_argument("--profile-decode", type=int, default=0,
                    help="only run this many decode loop-steps at M=1 (for rocprofv3), no JSON")
@@ -286,6 +288,51 @@ def decode_bench(lq, synth, torch, M, T, steps):
     }
 
 
+def loop_dependent_bench(lq, synth, torch, wl, mods, steps, warmup):
+    """The block with loop-dependent pieces (loopq_looped_forward_ex): every
+    loop with its own packed weights and factors (SLT selecting every module:
+    no weight sharing), and a per-loop activation width table (A8 for loop 0,
+    A4 after) on the shared weights.  Same step, inputs and algorithmic ops."""
+    import numpy as np
+    T, M = wl.T, wl.M
+    for m in mods:
+        own = []
+        for t in range(T):
+            W = np.concatenate([synth.weights_for(wl, lin, layer=1 + t) for lin in
+                                [l for l in wl.linears if l.act == m.act]], axis=0)
+            codes, scales = lq.empty_packed_weights(m.K, m.N, wl.group_w)
+            lq.loopq_pack_weights(torch.from_numpy(W).cuda(), wl.group_w, codes, scales)
+            own.append((codes, scales))
+        m.own_weights = own
+        m.own_factors = [(m.P1, m.P2)] + [tuple(torch.from_numpy(f).cuda() for f in
+                                                synth.factors_for(wl, m.act, m.K, layer=1 + t)) for t in range(1, T)]
+        m.ws_ex = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_EX, T, M, m.K, m.N, 0)
+
+    def run(kind, n):
+        for _ in range(n):
+            for m in mods:
+                if kind == "slt":
+                    lq.loopq_looped_forward_ex(m.x, m.own_factors, m.clips, [4] * T, m.own_weights, 32, m.N,
+                                               m.y, list(range(T)), m.ws_ex)
+                else:
+                    lq.loopq_looped_forward_ex(m.x, [(m.P1, m.P2)], m.clips, [8] + [4] * (T - 1),
+                                               [(m.codes, m.scales)], 32, m.N, m.y, [0] * T, m.ws_ex)
+
+    out = {}
+    ops = alg_ops(mods, T, M)
+    for kind in ("slt", "bits_8444"):
+        run(kind, warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(kind, steps)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        out[kind] = {"ms_per_step": dt * 1e3, "value": ops / dt / 1e12}
+    out["slt"]["what"] = "every loop with its own packed weights and factors (no sharing): T launches per input"
+    out["bits_8444"]["what"] = "loop 0 at A8, loops 1-3 at A4, shared weights: two weight-stationary runs per input"
+    return out
+
+
 def cpu_baseline(wl, mods_meta, rows_hint):
     """The oracle, untuned, on a bounded sample: `rows` token rows of loop 0
     of every quantized input (transform + Eq.(4) RTN + integer group dots +
@@ -425,6 +472,8 @@ def main():
                  "gemm_ms_per_step": kern_a8[lq.LOOPQ_KERNEL_GEMM][0] / args.steps},
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.no_loop_dependent:
+        out["loop_dependent"] = loop_dependent_bench(lq, synth, torch, wl, mods, max(5, args.steps // 2), 2)
     if not args.no_decode:
         del mods
         torch.cuda.empty_cache()

@@ -468,6 +468,14 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
       *bytes = act_bytes(T, M, K, N, code_format(bits_a));
       return LOOPQ_OK;
+    case LOOPQ_OP_LOOPED_FORWARD_EX: {
+      if (T <= 0 || M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (T > LOOPQ_MAX_LOOPS || K % 32) return LOOPQ_ERR_UNSUPPORTED;
+      if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
+      const size_t a4 = act_bytes(T, M, K, N, code_format(4)), a8 = act_bytes(T, M, K, N, code_format(8));
+      *bytes = a4 > a8 ? a4 : a8;
+      return LOOPQ_OK;
+    }
     case LOOPQ_OP_FOLD:
       if (M <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (M > 128 || N > 128) return LOOPQ_ERR_UNSUPPORTED;
@@ -575,6 +583,66 @@ int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
                             group_w, y, workspace, s);
   return linear_core(x, dtype, T * M, K, N, P1, n1, P2, n2, clips, M, bits_a, w_codes, w_scales,
                      group_w, y, workspace, T, M, s);
+}
+
+int32_t loopq_looped_forward_ex(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
+                                int32_t N, int32_t nsets, const float* const* P1_sets, int32_t n1,
+                                const float* const* P2_sets, int32_t n2, const void* const* w_codes_sets,
+                                const void* const* w_scales_sets, int32_t group_w,
+                                const int32_t* sets_host, const int32_t* bits_host,
+                                const float* clips_host, float* y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (T <= 0 || nsets <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (T > LOOPQ_MAX_LOOPS) return LOOPQ_ERR_UNSUPPORTED;
+  if ((int64_t)T * M > (int64_t)1 << 30) return LOOPQ_ERR_UNSUPPORTED;
+  int32_t st = check_act(x, dtype, M, K, 4);
+  if (st != LOOPQ_OK) return st;
+  st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  st = check_gemm_extent((int64_t)T * padded_rows(M), K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  if (!sets_host || !bits_host || !clips_host || !w_codes_sets || !w_scales_sets) return LOOPQ_ERR_INVALID_ARG;
+  if ((P1_sets == nullptr) != (P2_sets == nullptr)) return LOOPQ_ERR_INVALID_ARG;
+  for (int s = 0; s < nsets; ++s) {
+    const float* p1 = P1_sets ? P1_sets[s] : nullptr;
+    const float* p2 = P2_sets ? P2_sets[s] : nullptr;
+    if (P1_sets && (!p1 || !p2)) return LOOPQ_ERR_INVALID_ARG;
+    st = check_transform(K, p1, n1, p2, n2);
+    if (st != LOOPQ_OK) return st;
+    if (!w_codes_sets[s] || !w_scales_sets[s]) return LOOPQ_ERR_INVALID_ARG;
+    if (!aligned(w_codes_sets[s], 16) || !aligned(w_scales_sets[s], 16)) return LOOPQ_ERR_ALIGNMENT;
+  }
+  for (int t = 0; t < T; ++t) {
+    if (sets_host[t] < 0 || sets_host[t] >= nsets) return LOOPQ_ERR_INVALID_ARG;
+    if (bits_host[t] != 4 && bits_host[t] != 8) return LOOPQ_ERR_UNSUPPORTED;
+    if (!clip_ok(clips_host[t])) return LOOPQ_ERR_INVALID_ARG;
+  }
+  if (M == 0) return LOOPQ_OK;
+  if (!y) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(y, 4)) return LOOPQ_ERR_ALIGNMENT;
+  size_t need = 0;
+  loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_EX, T, M, K, N, 0, &need);
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
+  // maximal runs of consecutive loops with the same set and bit width, each
+  // weight-stationary over its rows
+  for (int t0 = 0; t0 < T;) {
+    int t1 = t0 + 1;
+    while (t1 < T && sets_host[t1] == sets_host[t0] && bits_host[t1] == bits_host[t0]) ++t1;
+    const int set = sets_host[t0];
+    ClipTable ct;
+    memset(&ct, 0, sizeof(ct));
+    for (int t = t0; t < t1; ++t) ct.c[t - t0] = clips_host[t];
+    st = linear_core(reinterpret_cast<const char*>(x) + (size_t)t0 * M * K * esz, dtype, (t1 - t0) * M, K, N,
+                     P1_sets ? P1_sets[set] : nullptr, n1, P2_sets ? P2_sets[set] : nullptr, n2, ct, M,
+                     bits_host[t0], w_codes_sets[set], w_scales_sets[set], group_w, y + (size_t)t0 * M * N,
+                     workspace, T, M, s);
+    if (st != LOOPQ_OK) return st;
+    t0 = t1;
+  }
+  return LOOPQ_OK;
 }
 
 int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,

@@ -28,7 +28,7 @@ LOOPQ_ERR_SINGULAR = -7
 
 LOOPQ_F32, LOOPQ_BF16 = 0, 1
 LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
-LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD = 1, 2, 3
+LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD, LOOPQ_OP_LOOPED_FORWARD_EX = 1, 2, 3, 4
 LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM, LOOPQ_KERNEL_DECODE = 0, 1, 2, 3
 
 # every entry point of include/loopq.h with its ctypes signature
@@ -45,6 +45,8 @@ SIGNATURES = {
     "loopq_w4a4_linear": ([_P, _I, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
     "loopq_looped_forward": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _I,
                               _P, _Z, _P], _I),
+    "loopq_looped_forward_ex": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _I, _P, _P, _P,
+                                 _P, _P, _Z, _P], _I),
     "loopq_gemm_codes": ([_P, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _Z, _P], _I),
     "loopq_export_weights": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "loopq_group_dots": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
@@ -188,6 +190,35 @@ def loopq_looped_forward(x, P1, P2, clips: Sequence[float], bits_a: int, w_codes
                                        _ptr(w_scales), group_w, _ptr(y), schedule, _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
            "loopq_looped_forward")
+
+
+def loopq_looped_forward_ex(x, factor_sets, clips: Sequence[float], bits: Sequence[int], weight_sets,
+                            group_w: int, N: int, y, sets: Sequence[int], workspace, stream=None):
+    """factor_sets: a list of (P1, P2) device tensors per set, or None (no
+    transform); weight_sets: a list of (w_codes, w_scales) per set; sets, bits
+    and clips: one entry per loop."""
+    T, M, K = x.shape
+    nsets = len(weight_sets)
+    VP = ctypes.c_void_p * nsets
+    if factor_sets is None:
+        p1 = p2 = None
+        n1 = n2 = 0
+    else:
+        if len(factor_sets) != nsets:
+            raise ValueError("one factor pair per weight set")
+        p1 = VP(*[_ptr(f[0]) for f in factor_sets])
+        p2 = VP(*[_ptr(f[1]) for f in factor_sets])
+        n1, n2 = int(factor_sets[0][0].shape[0]), int(factor_sets[0][1].shape[0])
+    wc = VP(*[_ptr(w[0]) for w in weight_sets])
+    wsc = VP(*[_ptr(w[1]) for w in weight_sets])
+    c = (ctypes.c_float * T)(*[float(v) for v in clips])
+    st = (ctypes.c_int32 * T)(*[int(v) for v in sets])
+    bt = (ctypes.c_int32 * T)(*[int(v) for v in bits])
+    as_p = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
+    _check(load().loopq_looped_forward_ex(_ptr(x), _dtype_code(x), T, M, K, N, nsets, as_p(p1), n1, as_p(p2),
+                                          n2, as_p(wc), as_p(wsc), group_w, as_p(st), as_p(bt), as_p(c),
+                                          _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(stream)), "loopq_looped_forward_ex")
 
 
 def loopq_gemm_codes(a_codes, a_scales, w_codes, w_scales, group_w: int, N: int, y, workspace,

@@ -88,7 +88,8 @@ typedef enum {
 typedef enum {
   LOOPQ_OP_LINEAR = 1,
   LOOPQ_OP_LOOPED_FORWARD = 2,
-  LOOPQ_OP_FOLD = 3
+  LOOPQ_OP_FOLD = 3,
+  LOOPQ_OP_LOOPED_FORWARD_EX = 4 /* bits_a ignored: enough for 4- and 8-bit loops */
 } loopq_op;
 
 /* ABI version of the loaded library (LOOPQ_ABI_VERSION it was built with). */
@@ -184,6 +185,34 @@ int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
                              const void* w_codes, const void* w_scales, int32_t group_w,
                              float* y, int32_t schedule,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* a6 with loop-dependent pieces.  Loop t uses weight/transform set
+ * sets_host[t] (0 <= set < nsets) and activation bit width bits_host[t] (4 or 8).
+ * Pages: SLT ("paper_specification.yaml", loopq_components.slt: selected groups
+ * receive loop-dependent transforms and weights; the others keep the shared
+ * ones, i.e. one set for every loop) and a loop-wise activation precision
+ * allocation ("Quantisation errors can keep returning inside a looped model",
+ * "Three components address three sources of mismatch").  x, y, clips_host and
+ * the other arguments as for loopq_looped_forward.  Set s has factors
+ * P1_sets_host[s] (n1 x n1) and P2_sets_host[s] (n2 x n2), device pointers held
+ * in host arrays of nsets entries (both arrays NULL: no transform for any set),
+ * and packed weights w_codes_sets_host[s] / w_scales_sets_host[s] from
+ * loopq_pack_weights with the same K, N, group_w.  Each maximal run of
+ * consecutive loops with the same set and bit width runs weight-stationary
+ * (one pass over that set's weights for all of the run's rows), so one set for
+ * every loop is exactly loopq_looped_forward's weight-stationary schedule.
+ * Workspace: loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_EX, T, M, K, N, 0, ...).
+ * Errors: a set index outside [0, nsets), a bit width other than 4 or 8, or a
+ * NULL set entry return LOOPQ_ERR_INVALID_ARG / LOOPQ_ERR_UNSUPPORTED before
+ * any launch; the shape and transform checks are those of loopq_looped_forward. */
+int32_t loopq_looped_forward_ex(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
+                                int32_t N, int32_t nsets, const float* const* P1_sets_host, int32_t n1,
+                                const float* const* P2_sets_host, int32_t n2,
+                                const void* const* w_codes_sets_host,
+                                const void* const* w_scales_sets_host, int32_t group_w,
+                                const int32_t* sets_host, const int32_t* bits_host,
+                                const float* clips_host, float* y, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* a5 alone -- the GEMM on activation codes and steps already formed.
  * a_codes int8 [M][K], a_scales fp32 [M][K/32] (the layouts loopq_quant_act

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
         assert n in loopq.SIGNATURES, n
@@ -135,3 +135,25 @@ def test_pack_and_fold_reject_on_host(lib):
                 None) == loopq.LOOPQ_ERR_UNSUPPORTED
     assert _raw(lib, "loopq_fold_weights", FAKE, 256, 8, FAKE, 16, FAKE, 16, FAKE, FAKE, 16,
                 None) == loopq.LOOPQ_ERR_WORKSPACE
+
+
+def test_looped_forward_ex_rejects_on_host(lib):
+    T = 3
+    VP = ctypes.c_void_p * 2
+    wc, wsc = VP(FAKE, FAKE), VP(FAKE, FAKE)
+    arr = lambda ct, vals: ctypes.cast((ct * len(vals))(*vals), ctypes.c_void_p)
+    def call(sets, bits, clips=(1.0, 0.9, 0.8), nsets=2, codes=wc, ws=1 << 30):
+        return _raw(lib, "loopq_looped_forward_ex", FAKE, 0, T, 4, 256, 128, nsets, None, 0, None, 0,
+                    ctypes.cast(codes, ctypes.c_void_p), ctypes.cast(wsc, ctypes.c_void_p), 32,
+                    arr(ctypes.c_int32, sets), arr(ctypes.c_int32, bits), arr(ctypes.c_float, clips),
+                    FAKE, FAKE, ws, None)
+    assert call([0, 1, 2], [4, 4, 4]) == loopq.LOOPQ_ERR_INVALID_ARG   # set index past nsets
+    assert call([0, -1, 0], [4, 4, 4]) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call([0, 1, 1], [4, 6, 4]) == loopq.LOOPQ_ERR_UNSUPPORTED   # bit width
+    assert call([0, 1, 1], [4, 8, 4], clips=(1.0, 0.0, 1.0)) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call([0, 0, 0], [4, 4, 4], nsets=0) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call([0, 1, 1], [4, 8, 4], codes=VP(FAKE, None)) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call([0, 1, 1], [4, 8, 4], ws=16) == loopq.LOOPQ_ERR_WORKSPACE
+    # enough for both bit widths
+    need = loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LOOPED_FORWARD_EX, 4, 64, 2048, 512, 0)
+    assert need >= max(loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LOOPED_FORWARD, 4, 64, 2048, 512, b) for b in (4, 8))

@@ -399,3 +399,55 @@ def test_decode_graph_replays_match_eager(lq):
         step()  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(y, eager)
+
+
+# ------------------------------------------------------------------------ loop-dependent sets
+
+@pytest.mark.parametrize("M", [4, 16, 100])
+def test_looped_forward_ex_matches_oracle(lq, M):
+    """SLT-style loop-dependent weights and transforms and a per-loop activation
+    bit width: loops [0, 1, 1, 0] use two sets (Haar factors; Hadamard factors,
+    which make the transform the Walsh-Hadamard transform of order 2048) and
+    widths [4, 8, 8, 4], against the oracle on each loop's kernel x~."""
+    K, N, T = 2048, 160, 4
+    say(f"looped_forward_ex M={M}")
+    rng = synth.seeded_rng(synth.TEST, 180, M)
+    F = [(synth.haar_orthogonal(32, rng), synth.haar_orthogonal(64, rng)),
+         (synth.hadamard(32), synth.hadamard(64))]
+    W = [synth.gaussian((N, K), 181, s, scale=0.02) for s in range(2)]
+    packed = [pack(lq, w, 32) for w in W]
+    qws = [oracle.quant_weights(w, 32) for w in W]
+    sets, bits = [0, 1, 1, 0], [4, 8, 8, 4]
+    clips = [0.9, 0.8, 0.7, 0.95]
+    x = synth.with_outliers(synth.gaussian((T, M, K), 182, M), 8, 20.0, 183, M)
+    bits16, x32 = synth.round_to_bf16(x)
+    xd = bf16_dev(bits16)
+    y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_EX, T, M, K, N, 0)
+    fd = [(dev(a), dev(b)) for a, b in F]
+    lq.loopq_looped_forward_ex(xd, fd, clips, bits, packed, 32, N, y, sets, ws)
+    torch.cuda.synchronize()
+    # the oracle on each loop's x~ (the kernel's own, per set)
+    xt = np.stack([gpu_xt(lq, xd[t], x32[t], *F[sets[t]]) for t in range(T)])
+    ref = oracle.looped_forward_sets(xt, [(None, None)] * 2, clips, bits, qws, 32, sets)
+    got = y.cpu().numpy()
+    for t in range(T):
+        assert rel_err(got[t], ref[t]) <= Y_TOL, t
+
+
+def test_looped_forward_ex_with_one_set_is_the_shared_loop(lq):
+    K, N, M, T = 512, 96, 40, 4
+    P1, P2 = synth.hadamard(16), synth.hadamard(32)
+    w = synth.gaussian((N, K), 184, scale=0.02)
+    codes, scales = pack(lq, w, 32)
+    x = dev(synth.gaussian((T, M, K), 185))
+    clips = [0.9, 0.8, 0.7, 0.6]
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_EX, T, M, K, N, 0)
+    y1 = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y1)
+    lq.loopq_looped_forward_ex(x, [(dev(P1), dev(P2))], clips, [4] * T, [(codes, scales)], 32, N, y1,
+                               [0] * T, ws)
+    lq.loopq_looped_forward(x, dev(P1), dev(P2), clips, 4, codes, scales, 32, N, y2,
+                            lq.LOOPQ_SCHED_WEIGHT_STATIONARY, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
