@@ -2,4 +2,5 @@
 from .loopq_oracle import (  # noqa: F401
     GROUP_A, qmax_for_bits, kron_transform, fold_weights, quant_weights, quant_act,
     group_dots, rescale_dots, qdq_linear, transformed_f32, linear, looped_forward, looped_forward_sets,
+    trajectory_hessian, thresholded_rank,
 )

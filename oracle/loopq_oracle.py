@@ -310,3 +310,33 @@ def looped_forward_sets(xs, factor_sets, clips, bits, weight_sets, group_w: int,
         out.append(linear(xs[t], P1, P2, float(clips[t]), int(bits[t]), qw, sw, group_w)[0])
     return np.stack(out)
 
+
+
+# --------------------------------------------------------------------------
+# next: trajectory Hessian ("Quantizing Looped Transformers": the GPTQ
+#       Hessian accumulated across recurrence steps; Table 1, thresholded rank
+#       at 1e-3 lambda_max)
+# --------------------------------------------------------------------------
+
+def trajectory_hessian(xts) -> np.ndarray:
+    """``H = sum_t X_t^T X_t`` in fp64 over the steps' (transformed) activations
+    ``xts`` ``[T][M][K]`` (or one ``[M][K]`` step): the Hessian a GPTQ step uses,
+    built from every recurrence step instead of step 0 only."""
+    xts = np.asarray(xts, dtype=np.float64)
+    if xts.ndim == 2:
+        xts = xts[None]
+    K = xts.shape[2]
+    H = np.zeros((K, K))
+    for x in xts:
+        H += x.T @ x
+    return H
+
+
+def thresholded_rank(H, rel: float = 1e-3) -> int:
+    """Number of eigenvalues of the symmetric PSD ``H`` above ``rel * lambda_max``
+    (Table 1's rank measure)."""
+    ev = np.linalg.eigvalsh(np.asarray(H, dtype=np.float64))
+    lmax = ev[-1]
+    if lmax <= 0:
+        return 0
+    return int(np.count_nonzero(ev > rel * lmax))

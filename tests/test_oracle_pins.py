@@ -408,3 +408,38 @@ def test_looped_forward_sets_reduces_to_shared_and_to_single_linears():
     assert not np.array_equal(ys[0], oracle.looped_forward_sets(xs[:1], [(Q1, Q2)], clips[:1], [4], [(qw1, sw1)], 32, [0])[0])
     with pytest.raises(ValueError):
         oracle.looped_forward_sets(xs, [(P1, P2)], clips, [4] * T, [(qw0, sw0)], 32, [0] * (T - 1))
+
+
+# ---------------------------------------------------------------- trajectory Hessian
+
+def test_trajectory_hessian_brute_force_and_symmetry():
+    xs = synth.gaussian((3, 5, 6), 190)
+    H = oracle.trajectory_hessian(xs)
+    B = np.zeros((6, 6))
+    for t in range(3):                 # every outer product written out
+        for m in range(5):
+            for i in range(6):
+                for j in range(6):
+                    B[i, j] += float(xs[t, m, i]) * float(xs[t, m, j])
+    np.testing.assert_allclose(H, B, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(H, H.T)
+    assert np.linalg.eigvalsh(H)[0] > -1e-9           # positive semi-definite
+    np.testing.assert_array_equal(oracle.trajectory_hessian(xs[0]), oracle.trajectory_hessian(xs[:1]))
+
+
+def test_thresholded_rank_of_constructed_subspaces():
+    # rows confined to an r-dimensional subspace give a rank-r Hessian; steps on
+    # orthogonal subspaces add their ranks (the accumulated trajectory sees more)
+    rng = synth.seeded_rng(synth.TEST, 191)
+    K = 64
+    Q, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    def step(cols, rows=40):
+        Z = rng.standard_normal((rows, len(cols)))
+        return Z @ Q[:, cols].T
+    s0, s1 = step(list(range(0, 5))), step(list(range(5, 12)))
+    assert oracle.thresholded_rank(oracle.trajectory_hessian(s0)) == 5
+    assert oracle.thresholded_rank(oracle.trajectory_hessian(np.stack([s0, s1]))) == 12
+    # directions below 1e-3 lambda_max do not count
+    weak = s0 + 1e-3 * step(list(range(20, 30)))
+    assert oracle.thresholded_rank(oracle.trajectory_hessian(weak)) == 5
+    assert oracle.thresholded_rank(np.zeros((4, 4))) == 0
