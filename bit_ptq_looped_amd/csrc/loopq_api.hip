@@ -476,6 +476,11 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       *bytes = a4 > a8 ? a4 : a8;
       return LOOPQ_OK;
     }
+    case LOOPQ_OP_HESSIAN:
+      if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (K % 32 || K > kHessianMaxK || M > kHessianMaxRows) return LOOPQ_ERR_UNSUPPORTED;
+      *bytes = align256(hessian_workspace_bytes(K));
+      return LOOPQ_OK;
     case LOOPQ_OP_FOLD:
       if (M <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (M > 128 || N > 128) return LOOPQ_ERR_UNSUPPORTED;
@@ -745,6 +750,21 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
   if (e == hipSuccess) e = prepare_weights(b, fmt, w_codes, K, N, s);
   if (e == hipSuccess) e = run_gemm(b, fmt, M, K, N, w_codes, nullptr, 32, nullptr, dots, 1, s);
   return hip_status(e);
+}
+
+int32_t loopq_hessian_accumulate(const float* xt, int32_t rows, int32_t K, float* H, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (rows < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (K % 32 || K > kHessianMaxK || rows > kHessianMaxRows) return LOOPQ_ERR_UNSUPPORTED;
+  if (rows == 0) return LOOPQ_OK;  // nothing to read or add
+  if (!xt || !H) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(xt, 8) || !aligned(H, 4)) return LOOPQ_ERR_ALIGNMENT;
+  const size_t need = hessian_workspace_bytes(K);
+  if (need && (!workspace || workspace_bytes < need)) return LOOPQ_ERR_WORKSPACE;
+  if (need && !aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  TimingScope ts(LOOPQ_KERNEL_HESSIAN, s);
+  return hip_status(launch_hessian(xt, rows, K, H, reinterpret_cast<float*>(workspace), s));
 }
 
 int32_t loopq_timing_enable(int32_t on) {

@@ -191,6 +191,13 @@ hipError_t launch_decode_items(const void* x, int bf16, const float* P1, int n1,
 hipError_t launch_decode(const DecodeCall& c, hipStream_t s);
 
 // status word shared by the synchronizing offline calls
+// Trajectory Hessian: H [K][K] += x^T x over `rows` rows of x [rows][K] fp32
+// (K % 32 == 0, rows >= 1); `part` holds hessian_workspace_bytes(K) bytes.
+constexpr int kHessianMaxK = 65536;
+constexpr int kHessianMaxRows = 1 << 30;
+size_t hessian_workspace_bytes(int K);
+hipError_t launch_hessian(const float* x, int rows, int K, float* H, float* part, hipStream_t s);
+
 hipError_t reset_status(hipStream_t s);
 hipError_t read_status(int* host_status, hipStream_t s);
 

@@ -29,7 +29,9 @@ LOOPQ_ERR_SINGULAR = -7
 LOOPQ_F32, LOOPQ_BF16 = 0, 1
 LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
 LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD, LOOPQ_OP_LOOPED_FORWARD_EX = 1, 2, 3, 4
+LOOPQ_OP_HESSIAN = 5
 LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM, LOOPQ_KERNEL_DECODE = 0, 1, 2, 3
+LOOPQ_KERNEL_HESSIAN = 4
 
 # every entry point of include/loopq.h with its ctypes signature
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -50,6 +52,7 @@ SIGNATURES = {
     "loopq_gemm_codes": ([_P, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _Z, _P], _I),
     "loopq_export_weights": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "loopq_group_dots": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "loopq_hessian_accumulate": ([_P, _I, _I, _P, _P, _Z, _P], _I),
     "loopq_timing_enable": ([_I], _I),
     "loopq_timing_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
     "loopq_timing_reset": ([], _I),
@@ -242,6 +245,14 @@ def loopq_group_dots(a_codes, w_codes, N: int, dots, workspace, bits_a: int = 4,
            "loopq_group_dots")
 
 
+def loopq_hessian_accumulate(xt, H, workspace=None, stream=None):
+    """H += xt^T xt; xt fp32 [rows][K], H fp32 [K][K], both on the device."""
+    rows, K = xt.shape
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().loopq_hessian_accumulate(_ptr(xt), rows, K, _ptr(H), _ptr(workspace), nbytes,
+                                           _stream(stream)), "loopq_hessian_accumulate")
+
+
 def loopq_timing_enable(on: bool) -> None:
     _check(load().loopq_timing_enable(1 if on else 0), "loopq_timing_enable")
 
@@ -250,7 +261,7 @@ def loopq_timing_reset() -> None:
     _check(load().loopq_timing_reset(), "loopq_timing_reset")
 
 
-def loopq_timing_read(n: int = 4):
+def loopq_timing_read(n: int = 5):
     """Per kernel id: (total milliseconds, launches) since the last read."""
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_int64 * n)()

@@ -89,7 +89,8 @@ typedef enum {
   LOOPQ_OP_LINEAR = 1,
   LOOPQ_OP_LOOPED_FORWARD = 2,
   LOOPQ_OP_FOLD = 3,
-  LOOPQ_OP_LOOPED_FORWARD_EX = 4 /* bits_a ignored: enough for 4- and 8-bit loops */
+  LOOPQ_OP_LOOPED_FORWARD_EX = 4, /* bits_a ignored: enough for 4- and 8-bit loops */
+  LOOPQ_OP_HESSIAN = 5            /* rows as M; T, N and bits_a ignored */
 } loopq_op;
 
 /* ABI version of the loaded library (LOOPQ_ABI_VERSION it was built with). */
@@ -225,6 +226,28 @@ int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M
                          int32_t bits_a, float* y, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Trajectory Hessian accumulation: H += xt^T xt.
+ * Page: "Quantizing Looped Transformers: Feedback Exposure and Calibration
+ * Blindness" -- N-step GPTQ calibration accumulates the input Hessian over the
+ * recurrence steps, H = sum_t X_t^T X_t (Tables 19 and 25; Table 1 reports the
+ * rank of such Hessians at a 1e-3 lambda_max threshold); the GPTQ memory note
+ * of the same page set keeps one fp32 [in][in] Hessian per linear.  Passing
+ * the x~ rows of every loop t (the values the forward quantizes, e.g. the
+ * xt_out of loopq_quant_act) in one or several calls accumulates that sum for
+ * the transformed linear.
+ * xt fp32 [rows][K] (8-byte aligned); H fp32 [K][K] (4-byte aligned), read and
+ * written in place: H[i][j] += sum_r xt[r][i] * xt[r][j] for all i, j.  Each
+ * value is formed once for i <= j (fp32 products, fp32 accumulation) and
+ * stored at both (i, j) and (j, i), so a symmetric H stays exactly symmetric.
+ * The summation order depends only on (rows, K): results are deterministic.
+ * rows == 0 returns LOOPQ_OK at once (any pointers).  K % 32 == 0, K <= 65536,
+ * rows <= 2^30.
+ * Workspace: loopq_workspace_bytes(LOOPQ_OP_HESSIAN, 0, rows, K, 0, 0, ...)
+ * (0 bytes for some K, then workspace may be NULL).  Two calls on H must not
+ * overlap; xt must not alias H. */
+int32_t loopq_hessian_accumulate(const float* xt, int32_t rows, int32_t K, float* H, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Test export: canonical weight codes int8 [N][K] and steps fp16 [N][ceil(K/group_w)]
  * (raw binary16 bits) from the packed layout. */
 int32_t loopq_export_weights(const void* w_codes, const void* w_scales, int32_t K, int32_t N,
@@ -247,7 +270,8 @@ typedef enum {
   LOOPQ_KERNEL_QUANT_TRANSFORM = 0, /* fused transform + quantizer */
   LOOPQ_KERNEL_QUANT_PLAIN = 1,     /* quantizer without transform */
   LOOPQ_KERNEL_GEMM = 2,            /* integer GEMM + rescale */
-  LOOPQ_KERNEL_DECODE = 3           /* few-row linear: transform, quantizer and product in one launch */
+  LOOPQ_KERNEL_DECODE = 3,          /* few-row linear: transform, quantizer and product in one launch */
+  LOOPQ_KERNEL_HESSIAN = 4          /* trajectory Hessian accumulation (one record per call) */
 } loopq_kernel_id;
 
 /* Turn the hooks on (1) or off (0).  Host only; cheap. */

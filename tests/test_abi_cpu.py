@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
         assert n in loopq.SIGNATURES, n
@@ -157,3 +157,34 @@ def test_looped_forward_ex_rejects_on_host(lib):
     # enough for both bit widths
     need = loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LOOPED_FORWARD_EX, 4, 64, 2048, 512, 0)
     assert need >= max(loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LOOPED_FORWARD, 4, 64, 2048, 512, b) for b in (4, 8))
+
+
+def test_hessian_workspace_and_host_rejections(lib):
+    op = loopq.LOOPQ_OP_HESSIAN
+    # K = 2048: 528 tiles of 64 on or above the diagonal, 16 left over after 512
+    # whole ones -> room for two 64 x 64 pieces per work group
+    assert loopq.loopq_workspace_bytes(op, 0, 4096, 2048, 0, 0) == 512 * 2 * 64 * 64 * 4
+    # K = 65536: 1024 * 1025 / 2 tiles, a multiple of 512 -> nothing left over
+    assert loopq.loopq_workspace_bytes(op, 0, 16, 65536, 0, 0) == 0
+    for K, want in ((48, loopq.LOOPQ_ERR_UNSUPPORTED), (65536 + 32, loopq.LOOPQ_ERR_UNSUPPORTED),
+                    (0, loopq.LOOPQ_ERR_INVALID_ARG)):
+        with pytest.raises(loopq.LoopQError) as e:
+            loopq.loopq_workspace_bytes(op, 0, 16, K, 0, 0)
+        assert e.value.status == want
+    ws = 512 * 2 * 64 * 64 * 4
+    call = lambda x, rows, K, H, w=FAKE, nb=ws: _raw(lib, "loopq_hessian_accumulate", x, rows, K, H, w, nb, None)
+    assert call(FAKE, -1, 256, FAKE) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call(FAKE, 8, 0, FAKE) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call(FAKE, 8, 48, FAKE) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert call(FAKE, 8, 65536 + 32, FAKE) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert call(FAKE, (1 << 30) + 1, 256, FAKE) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert call(None, 8, 256, FAKE) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call(FAKE, 8, 256, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call(FAKE + 4, 8, 256, FAKE) == loopq.LOOPQ_ERR_ALIGNMENT   # xt needs 8 bytes
+    assert call(FAKE, 8, 256, FAKE + 2) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert call(FAKE, 8, 2048, FAKE, nb=ws - 1) == loopq.LOOPQ_ERR_WORKSPACE
+    assert call(FAKE, 8, 2048, FAKE, w=None) == loopq.LOOPQ_ERR_WORKSPACE
+    assert call(FAKE, 8, 2048, FAKE, w=FAKE + 16) == loopq.LOOPQ_ERR_ALIGNMENT
+    # no rows: nothing to add, nothing enqueued, whatever the pointers
+    assert call(FAKE, 0, 2048, FAKE) == loopq.LOOPQ_OK
+    assert call(None, 0, 2048, None, w=None) == loopq.LOOPQ_OK

@@ -1,0 +1,150 @@
+"""GPU parity of the trajectory Hessian accumulation (``loopq_hessian_accumulate``)
+against the CPU oracle, through the C ABI.
+
+Bar, derived from the arithmetic: each element of H0 + X^T X is a sum of
+rows + 1 terms (rows fp32 products and H0) that the kernel forms with fp32
+products and fp32 additions in some fixed order, so it lies within
+gamma_(rows+1) = (rows + 1) u / (1 - (rows + 1) u), u = 2^-24, times
+(|X|^T |X| + |H0|) of the exact value, which the fp64 oracle gives (its own
+error is far below that).  Several calls chain: the bound adds up over them.
+H is exactly symmetric (one value stored at (i, j) and (j, i)) and the call
+is deterministic.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_ptq_looped_amd import synth
+from xt_check import check_xt
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gamma(n):
+    return n * U / (1.0 - n * U)
+
+
+def workspace(lq, rows, K):
+    n = lq.loopq_workspace_bytes(lq.LOOPQ_OP_HESSIAN, 0, rows, K, 0, 0)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+
+
+def accumulate(lq, xs, H0):
+    """H0 + sum over the row blocks xs (one call each) on the GPU, fp32."""
+    K = H0.shape[0]
+    H = dev(H0.astype(np.float32))
+    ws = workspace(lq, max(x.shape[0] for x in xs), K)
+    for x in xs:
+        lq.loopq_hessian_accumulate(dev(x.astype(np.float32)), H, ws)
+    torch.cuda.synchronize()
+    return H.cpu().numpy()
+
+
+def check_bound(got, xs, H0):
+    """Element-wise bound of the module docstring over a chain of calls."""
+    want = np.asarray(H0, dtype=np.float64) + sum(oracle.trajectory_hessian(x) for x in xs)
+    mag = np.abs(np.asarray(H0, dtype=np.float64)) + sum(oracle.trajectory_hessian(np.abs(x)) for x in xs)
+    bound = gamma(sum(x.shape[0] for x in xs) + len(xs)) * mag
+    err = np.abs(got.astype(np.float64) - want)
+    ratio = float(np.max(err / np.maximum(bound, 1e-300)))
+    assert np.all(err <= bound), f"H outside the fp32 accumulation bound (max error/bound {ratio:.3g})"
+    return ratio
+
+
+def random_symmetric(K, *key):
+    a = synth.gaussian((K, K), *key)
+    return ((a + a.T) * np.float32(0.5)).astype(np.float32)
+
+
+# (rows, K): one tile and one row; a ragged 64-column edge and ragged rows;
+# fewer tiles than work groups with each tile split across many of them; whole
+# tiles plus split leftovers (K = 2048: 512 whole, 16 split; K = 5632: 7 whole
+# per work group, 332 split)
+@pytest.mark.parametrize("rows,K", [(1, 32), (63, 96), (130, 256), (4096, 256), (333, 2048), (70, 5632)])
+def test_hessian_matches_oracle(lq, rows, K):
+    say(f"hessian rows={rows} K={K}")
+    x = synth.with_outliers(synth.gaussian((rows, K), 71, rows, K), max(1, K // 100), 20.0, 72, K)
+    H0 = random_symmetric(K, 73, K) if rows > 1 else np.zeros((K, K), np.float32)
+    got = accumulate(lq, [x], H0)
+    ratio = check_bound(got, [x], H0)
+    say(f"  max error / bound {ratio:.3g}")
+    assert np.array_equal(got, got.T)
+    again = accumulate(lq, [x], H0)
+    assert np.array_equal(got, again)
+
+
+def test_hessian_without_rows_is_a_no_op(lq):
+    K = 256
+    H0 = random_symmetric(K, 74)
+    H = dev(H0)
+    lq.loopq_hessian_accumulate(torch.empty((0, K), dtype=torch.float32, device="cuda"), H, workspace(lq, 0, K))
+    torch.cuda.synchronize()
+    assert np.array_equal(H.cpu().numpy(), H0)
+
+
+def test_hessian_of_loop_trajectory_from_quantizer_dumps(lq):
+    """The side output of a looped forward: the x~ rows every loop quantizes
+    (the quantizer's dump), accumulated one loop per call, against the oracle's
+    trajectory Hessian of those rows (Ouro-like qkv input, K = 2048 = 32 x 64)."""
+    wl = synth.ouro_block_workload(M=96)
+    K = 2048
+    P1, P2 = synth.factors_for(wl, "qkv_in", K)
+    bits, x32 = synth.activations_for(wl, "qkv_in", K)
+    T, M = x32.shape[0], x32.shape[1]
+    p1, p2 = dev(P1), dev(P2)
+    H = torch.zeros((K, K), dtype=torch.float32, device="cuda")
+    ws = workspace(lq, M, K)
+    dumps = []
+    for t in range(T):
+        say(f"loop {t}")
+        xt = torch.from_numpy(np.ascontiguousarray(bits[t]).view(np.int16)).cuda().view(torch.bfloat16)
+        codes = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        steps = torch.empty((M, K // 32), dtype=torch.float32, device="cuda")
+        dump = torch.empty((M, K), dtype=torch.float32, device="cuda")
+        lq.loopq_quant_act(xt, p1, p2, 1.0, 4, codes, steps, dump)
+        lq.loopq_hessian_accumulate(dump, H, ws)
+        torch.cuda.synchronize()
+        d = dump.cpu().numpy()
+        check_xt(d, x32[t], P1, P2)
+        dumps.append(d)
+    got = H.cpu().numpy()
+    ratio = check_bound(got, dumps, np.zeros((K, K)))
+    say(f"  max error / bound {ratio:.3g}")
+    assert np.array_equal(got, got.T)
+
+
+def test_hessian_rank_grows_along_a_drifting_trajectory(lq):
+    """Thresholded rank (1e-3 lambda_max, "Quantizing Looped Transformers",
+    Table 1) of the accumulated Hessian after each loop: loop t's rows span
+    43 + 8 t fixed directions, so the rank after loop t is 43 + 8 t for the
+    GPU's fp32 H and for the oracle's fp64 H alike.  Orthonormal directions
+    and 512 rows per loop keep the smallest nonzero eigenvalue above 1/20 of
+    the largest, far from the threshold."""
+    K, M, T, d0, dd = 512, 512, 4, 43, 8
+    basis = synth.haar_orthogonal(K, synth.seeded_rng(synth.TEST, 75))[: d0 + dd * (T - 1)]
+    H = torch.zeros((K, K), dtype=torch.float32, device="cuda")
+    ws = workspace(lq, M, K)
+    xs = []
+    for t in range(T):
+        d = d0 + dd * t
+        z = synth.gaussian((M, d), 76, t)
+        x = (z.astype(np.float64) @ basis[:d].astype(np.float64)).astype(np.float32)
+        xs.append(x)
+        lq.loopq_hessian_accumulate(dev(x), H, ws)
+        torch.cuda.synchronize()
+        got = H.cpu().numpy()
+        want_rank = oracle.thresholded_rank(oracle.trajectory_hessian(xs))
+        assert want_rank == d
+        assert oracle.thresholded_rank(got) == d
