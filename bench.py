@@ -24,6 +24,7 @@ import time
 
 METRIC = "looped W4A4 linear TOPS & GB/s per loop-step, % of INT8-MFMA/HBM roofline"
 INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 
 
@@ -43,6 +44,9 @@ def parse():
     p.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     p.add_argument("--no-loop-dependent", action="store_true",
                    help="skip the loop-dependent (per-loop weight sets / bit widths) measurement")
+    p.add_argument("--no-hessian", action="store_true", help="skip the trajectory Hessian measurement")
+    p.add_argument("--profile-hessian", type=int, default=0,
+                   help="only run this many trajectory Hessian steps (for a profiler) and exit")
     p.add_argument("--decode-steps", type=int, default=20)
     p.add_argument("--profile-decode", type=int, default=0,
                    help="only run this many decode loop-steps at M=1 (for rocprofv3), no JSON")
@@ -333,6 +337,74 @@ def loop_dependent_bench(lq, synth, torch, wl, mods, steps, warmup):
     return out
 
 
+def hessian_setup(lq, torch, mods, T, M):
+    """x~ of every loop of each quantized input (the quantizer's dump, formed
+    once, untimed), a zeroed fp32 [K][K] Hessian and the workspace per input."""
+    for m in mods:
+        rows = T * M
+        x2 = m.x.reshape(rows, m.K)
+        codes = torch.empty((rows, m.K), dtype=torch.int8, device="cuda")
+        steps = torch.empty((rows, m.K // 32), dtype=torch.float32, device="cuda")
+        m.xt = torch.empty((rows, m.K), dtype=torch.float32, device="cuda")
+        lq.loopq_quant_act(x2, m.P1, m.P2, 1.0, 4, codes, steps, m.xt)
+        m.H = torch.zeros((m.K, m.K), dtype=torch.float32, device="cuda")
+        m.ws_h = lq.empty_workspace(lq.LOOPQ_OP_HESSIAN, 0, rows, m.K, 0, 0)
+        del codes, steps
+    torch.cuda.synchronize()
+
+
+def hessian_step(lq, mods):
+    for m in mods:
+        lq.loopq_hessian_accumulate(m.xt, m.H, m.ws_h)
+
+
+def hessian_bench(lq, torch, mods, T, M, steps, warmup):
+    """Trajectory Hessian H += x~^T x~ over the x~ rows of all T loops, one
+    accumulation per quantized input of the block (K = 2048 three times,
+    K = 5632 once).  Algorithmic flops: rows * K * (K + 1) per input (the
+    multiply-adds of the upper triangle with the diagonal)."""
+    hessian_setup(lq, torch, mods, T, M)
+    for _ in range(warmup):
+        hessian_step(lq, mods)
+    torch.cuda.synchronize()
+    lq.loopq_timing_enable(True)
+    lq.loopq_timing_read(5)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        hessian_step(lq, mods)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    kms, kn = lq.loopq_timing_read(5)[lq.LOOPQ_KERNEL_HESSIAN]
+    lq.loopq_timing_enable(False)
+    per_k = {}
+    for m in mods:  # per input shape, timed alone with the hooks
+        lq.loopq_timing_read(5)
+        lq.loopq_timing_enable(True)
+        for _ in range(steps):
+            lq.loopq_hessian_accumulate(m.xt, m.H, m.ws_h)
+        torch.cuda.synchronize()
+        ms, n = lq.loopq_timing_read(5)[lq.LOOPQ_KERNEL_HESSIAN]
+        lq.loopq_timing_enable(False)
+        fl = T * M * m.K * (m.K + 1.0)
+        per_k[m.act] = {"K": m.K, "rows": T * M, "ms": ms / n, "tflops": fl / (ms / n * 1e-3) / 1e12,
+                        "frac": fl / (ms / n * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS}
+    flops = sum(T * M * m.K * (m.K + 1.0) for m in mods)
+    achieved = flops / (kms / steps * 1e-3) / 1e12
+    for m in mods:
+        del m.xt, m.H, m.ws_h
+    torch.cuda.empty_cache()
+    return {
+        "what": "H += x~^T x~ over the x~ of all T loops, one call per quantized input (fp32 MFMA SYRK)",
+        "ms_per_step": dt * 1e3,
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "kernel_ms_per_step": kms / steps,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS},
+        "per_input": per_k,
+    }
+
+
 def cpu_baseline(wl, mods_meta, rows_hint):
     """The oracle, untuned, on a bounded sample: `rows` token rows of loop 0
     of every quantized input (transform + Eq.(4) RTN + integer group dots +
@@ -400,6 +472,13 @@ def main():
             decode_loop_step(lq, dmods, i % 4)
         torch.cuda.synchronize()
         print(f"profiled {args.profile_decode} decode loop-steps", flush=True)
+        return
+    if args.profile_hessian:
+        hessian_setup(lq, torch, mods, T, M)
+        for _ in range(args.profile_hessian):
+            hessian_step(lq, mods)
+        torch.cuda.synchronize()
+        print(f"profiled {args.profile_hessian} trajectory Hessian steps", flush=True)
         return
     if args.profile_steps:
         if args.copy_mib:
@@ -474,6 +553,8 @@ def main():
     }
     if not args.no_loop_dependent:
         out["loop_dependent"] = loop_dependent_bench(lq, synth, torch, wl, mods, max(5, args.steps // 2), 2)
+    if not args.no_hessian:
+        out["trajectory_hessian"] = hessian_bench(lq, torch, mods, T, M, max(5, args.steps // 5), 2)
     if not args.no_decode:
         del mods
         torch.cuda.empty_cache()

@@ -758,7 +758,7 @@ int32_t loopq_hessian_accumulate(const float* xt, int32_t rows, int32_t K, float
   if (K % 32 || K > kHessianMaxK || rows > kHessianMaxRows) return LOOPQ_ERR_UNSUPPORTED;
   if (rows == 0) return LOOPQ_OK;  // nothing to read or add
   if (!xt || !H) return LOOPQ_ERR_INVALID_ARG;
-  if (!aligned(xt, 8) || !aligned(H, 4)) return LOOPQ_ERR_ALIGNMENT;
+  if (!aligned(xt, 16) || !aligned(H, 4)) return LOOPQ_ERR_ALIGNMENT;
   const size_t need = hessian_workspace_bytes(K);
   if (need && (!workspace || workspace_bytes < need)) return LOOPQ_ERR_WORKSPACE;
   if (need && !aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;

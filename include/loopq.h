@@ -235,7 +235,7 @@ int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M
  * the x~ rows of every loop t (the values the forward quantizes, e.g. the
  * xt_out of loopq_quant_act) in one or several calls accumulates that sum for
  * the transformed linear.
- * xt fp32 [rows][K] (8-byte aligned); H fp32 [K][K] (4-byte aligned), read and
+ * xt fp32 [rows][K] (16-byte aligned); H fp32 [K][K] (4-byte aligned), read and
  * written in place: H[i][j] += sum_r xt[r][i] * xt[r][j] for all i, j.  Each
  * value is formed once for i <= j (fp32 products, fp32 accumulation) and
  * stored at both (i, j) and (j, i), so a symmetric H stays exactly symmetric.
@@ -243,8 +243,9 @@ int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M
  * rows == 0 returns LOOPQ_OK at once (any pointers).  K % 32 == 0, K <= 65536,
  * rows <= 2^30.
  * Workspace: loopq_workspace_bytes(LOOPQ_OP_HESSIAN, 0, rows, K, 0, 0, ...)
- * (0 bytes for some K, then workspace may be NULL).  Two calls on H must not
- * overlap; xt must not alias H. */
+ * (16 MiB below K = 4000, 64 MiB from there on; the size depends on K only).
+ * Two calls on one H must not overlap, nor two calls sharing a workspace;
+ * xt must not alias H. */
 int32_t loopq_hessian_accumulate(const float* xt, int32_t rows, int32_t K, float* H, void* workspace,
                                  size_t workspace_bytes, void* stream);
 

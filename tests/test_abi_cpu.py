@@ -164,8 +164,10 @@ def test_hessian_workspace_and_host_rejections(lib):
     # K = 2048: 528 tiles of 64 on or above the diagonal, 16 left over after 512
     # whole ones -> room for two 64 x 64 pieces per work group
     assert loopq.loopq_workspace_bytes(op, 0, 4096, 2048, 0, 0) == 512 * 2 * 64 * 64 * 4
-    # K = 65536: 1024 * 1025 / 2 tiles, a multiple of 512 -> nothing left over
-    assert loopq.loopq_workspace_bytes(op, 0, 16, 65536, 0, 0) == 0
+    # K >= 4000 takes 128-wide tiles (K = 4096: 528 of them): 128 x 128 pieces
+    assert loopq.loopq_workspace_bytes(op, 0, 16, 4096, 0, 0) == 512 * 2 * 128 * 128 * 4
+    assert loopq.loopq_workspace_bytes(op, 0, 16, 65536, 0, 0) == 512 * 2 * 128 * 128 * 4
+    assert loopq.loopq_workspace_bytes(op, 0, 16, 3968, 0, 0) == 512 * 2 * 64 * 64 * 4
     for K, want in ((48, loopq.LOOPQ_ERR_UNSUPPORTED), (65536 + 32, loopq.LOOPQ_ERR_UNSUPPORTED),
                     (0, loopq.LOOPQ_ERR_INVALID_ARG)):
         with pytest.raises(loopq.LoopQError) as e:
@@ -180,7 +182,7 @@ def test_hessian_workspace_and_host_rejections(lib):
     assert call(FAKE, (1 << 30) + 1, 256, FAKE) == loopq.LOOPQ_ERR_UNSUPPORTED
     assert call(None, 8, 256, FAKE) == loopq.LOOPQ_ERR_INVALID_ARG
     assert call(FAKE, 8, 256, None) == loopq.LOOPQ_ERR_INVALID_ARG
-    assert call(FAKE + 4, 8, 256, FAKE) == loopq.LOOPQ_ERR_ALIGNMENT   # xt needs 8 bytes
+    assert call(FAKE + 8, 8, 256, FAKE) == loopq.LOOPQ_ERR_ALIGNMENT   # xt needs 16 bytes
     assert call(FAKE, 8, 256, FAKE + 2) == loopq.LOOPQ_ERR_ALIGNMENT
     assert call(FAKE, 8, 2048, FAKE, nb=ws - 1) == loopq.LOOPQ_ERR_WORKSPACE
     assert call(FAKE, 8, 2048, FAKE, w=None) == loopq.LOOPQ_ERR_WORKSPACE

@@ -70,9 +70,11 @@ def random_symmetric(K, *key):
 
 # (rows, K): one tile and one row; a ragged 64-column edge and ragged rows;
 # fewer tiles than work groups with each tile split across many of them; whole
-# tiles plus split leftovers (K = 2048: 512 whole, 16 split; K = 5632: 7 whole
-# per work group, 332 split)
-@pytest.mark.parametrize("rows,K", [(1, 32), (63, 96), (130, 256), (4096, 256), (333, 2048), (70, 5632)])
+# tiles plus split leftovers (K = 2048: 512 whole 64-wide tiles, 16 split).
+# From K = 4000 on the tiles are 128 wide (LDS-staged): K = 4160 and 4128 end
+# in a half and a quarter strip, K = 5632 has 512 whole tiles and 478 split.
+@pytest.mark.parametrize("rows,K", [(1, 32), (63, 96), (130, 256), (4096, 256), (333, 2048),
+                                    (1000, 4160), (77, 4128), (70, 5632)])
 def test_hessian_matches_oracle(lq, rows, K):
     say(f"hessian rows={rows} K={K}")
     x = synth.with_outliers(synth.gaussian((rows, K), 71, rows, K), max(1, K // 100), 20.0, 72, K)
