@@ -243,7 +243,7 @@ int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M
  * rows == 0 returns LOOPQ_OK at once (any pointers).  K % 32 == 0, K <= 65536,
  * rows <= 2^30.
  * Workspace: loopq_workspace_bytes(LOOPQ_OP_HESSIAN, 0, rows, K, 0, 0, ...)
- * (16 MiB below K = 4000, 64 MiB from there on; the size depends on K only).
+ * (64 MiB; the size depends on K only).
  * Two calls on one H must not overlap, nor two calls sharing a workspace;
  * xt must not alias H. */
 int32_t loopq_hessian_accumulate(const float* xt, int32_t rows, int32_t K, float* H, void* workspace,

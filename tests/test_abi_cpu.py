@@ -161,19 +161,17 @@ def test_looped_forward_ex_rejects_on_host(lib):
 
 def test_hessian_workspace_and_host_rejections(lib):
     op = loopq.LOOPQ_OP_HESSIAN
-    # K = 2048: 528 tiles of 64 on or above the diagonal, 16 left over after 512
-    # whole ones -> room for two 64 x 64 pieces per work group
-    assert loopq.loopq_workspace_bytes(op, 0, 4096, 2048, 0, 0) == 512 * 2 * 64 * 64 * 4
-    # K >= 4000 takes 128-wide tiles (K = 4096: 528 of them): 128 x 128 pieces
-    assert loopq.loopq_workspace_bytes(op, 0, 16, 4096, 0, 0) == 512 * 2 * 128 * 128 * 4
-    assert loopq.loopq_workspace_bytes(op, 0, 16, 65536, 0, 0) == 512 * 2 * 128 * 128 * 4
-    assert loopq.loopq_workspace_bytes(op, 0, 16, 3968, 0, 0) == 512 * 2 * 64 * 64 * 4
+    # room for two 128 x 128 fp32 pieces per work group (512 of them) whenever
+    # the tiles on or above the diagonal are not a multiple of 512: K = 2048
+    # has 136, K = 4096 has 528, K = 65536 has 131328
+    for K in (32, 2048, 4096, 65536):
+        assert loopq.loopq_workspace_bytes(op, 0, 16, K, 0, 0) == 512 * 2 * 128 * 128 * 4
     for K, want in ((48, loopq.LOOPQ_ERR_UNSUPPORTED), (65536 + 32, loopq.LOOPQ_ERR_UNSUPPORTED),
                     (0, loopq.LOOPQ_ERR_INVALID_ARG)):
         with pytest.raises(loopq.LoopQError) as e:
             loopq.loopq_workspace_bytes(op, 0, 16, K, 0, 0)
         assert e.value.status == want
-    ws = 512 * 2 * 64 * 64 * 4
+    ws = 512 * 2 * 128 * 128 * 4
     call = lambda x, rows, K, H, w=FAKE, nb=ws: _raw(lib, "loopq_hessian_accumulate", x, rows, K, H, w, nb, None)
     assert call(FAKE, -1, 256, FAKE) == loopq.LOOPQ_ERR_INVALID_ARG
     assert call(FAKE, 8, 0, FAKE) == loopq.LOOPQ_ERR_INVALID_ARG

@@ -68,11 +68,10 @@ def random_symmetric(K, *key):
     return ((a + a.T) * np.float32(0.5)).astype(np.float32)
 
 
-# (rows, K): one tile and one row; a ragged 64-column edge and ragged rows;
-# fewer tiles than work groups with each tile split across many of them; whole
-# tiles plus split leftovers (K = 2048: 512 whole 64-wide tiles, 16 split).
-# From K = 4000 on the tiles are 128 wide (LDS-staged): K = 4160 and 4128 end
-# in a half and a quarter strip, K = 5632 has 512 whole tiles and 478 split.
+# (rows, K), tiles of 128: one tile and one row; a ragged column edge (K % 128
+# of 96, 64, 32) and ragged rows; fewer tiles than work groups with each tile
+# split across many of them (K = 256: 3 tiles; K = 2048: 136); whole tiles plus
+# split leftovers (K = 4160: 561 tiles, K = 5632: 990).
 @pytest.mark.parametrize("rows,K", [(1, 32), (63, 96), (130, 256), (4096, 256), (333, 2048),
                                     (1000, 4160), (77, 4128), (70, 5632)])
 def test_hessian_matches_oracle(lq, rows, K):
