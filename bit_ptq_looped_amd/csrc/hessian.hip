@@ -40,7 +40,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kGroups = 512;     // work groups of the tile kernel (fixed: the partition sets the summation order)
 constexpr int kTile = 128;       // H tile edge
 constexpr int kUnitRows = 64;    // rows per work unit
-constexpr int kStep = 16;        // rows per LDS stage
+constexpr int kStep = 32;        // rows per LDS stage
 constexpr int kStrip = kStep * kTile;  // floats of one staged strip
 constexpr int kStage = 2 * kStrip;     // A and B strips of one stage
 constexpr int kLds = 65;         // LDS row stride of a 64 x 64 quadrant (conflict-free column reads)
@@ -74,12 +74,14 @@ __device__ __forceinline__ int unit_owner(long long v, long long wr) {
   return (int)(((v + 1) * kGroups + wr - 1) / wr) - 1;
 }
 
-// Rows [row0, row0 + 16) of the 128-column strips at i0 (A) and j0 (B) into
-// registers, two float4 per thread and strip.  Columns past K are clamped to
+// Rows [row0, row0 + kStep) of the 128-column strips at i0 (A) and j0 (B)
+// into registers, kLoads float4 per thread and strip.  Columns past K are clamped to
 // K - 4 (their outputs are never stored); RAGGED clamps rows past the end to
 // the last row and zeroes their A side, so they add nothing.
+constexpr int kLoads = kStrip / (4 * kThreads);  // float4 per thread and strip
+
 struct StageRegs {
-  float4 a0, a1, b0, b1;
+  float4 a[kLoads], b[kLoads];
 };
 
 template <bool RAGGED, bool DIAG>
@@ -97,26 +99,27 @@ __device__ __forceinline__ float4 stage_elem(const HPlan& p, int row0, int i0, i
 template <bool RAGGED, bool DIAG>
 __device__ __forceinline__ StageRegs stage_load(const HPlan& p, int row0, int i0, int j0) {
   StageRegs r;
-  r.b0 = r.b1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  r.a0 = stage_elem<RAGGED, DIAG>(p, row0, i0, j0, threadIdx.x, &r.b0);
-  r.a1 = stage_elem<RAGGED, DIAG>(p, row0, i0, j0, threadIdx.x + kThreads, &r.b1);
+#pragma unroll
+  for (int h = 0; h < kLoads; ++h) {
+    r.b[h] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    r.a[h] = stage_elem<RAGGED, DIAG>(p, row0, i0, j0, threadIdx.x + kThreads * h, &r.b[h]);
+  }
   return r;
 }
 
-// registers -> one LDS stage ([16][128] A, then [16][128] B; a diagonal tile
-// keeps only A)
+// registers -> one LDS stage ([kStep][128] A, then [kStep][128] B; a
+// diagonal tile keeps only A)
 template <bool DIAG>
 __device__ __forceinline__ void stage_store(float* stage, const StageRegs& r) {
-  const int e = threadIdx.x;
-  *reinterpret_cast<float4*>(stage + 4 * e) = r.a0;
-  *reinterpret_cast<float4*>(stage + 4 * (e + kThreads)) = r.a1;
-  if (!DIAG) {
-    *reinterpret_cast<float4*>(stage + kStrip + 4 * e) = r.b0;
-    *reinterpret_cast<float4*>(stage + kStrip + 4 * (e + kThreads)) = r.b1;
+#pragma unroll
+  for (int h = 0; h < kLoads; ++h) {
+    const int e = threadIdx.x + kThreads * h;
+    *reinterpret_cast<float4*>(stage + 4 * e) = r.a[h];
+    if (!DIAG) *reinterpret_cast<float4*>(stage + kStrip + 4 * e) = r.b[h];
   }
 }
 
-// this wave's quadrant (qa, qb) over the 16 staged rows
+// this wave's quadrant (qa, qb) over the staged rows
 template <bool DIAG>
 __device__ __forceinline__ void stage_mfma(v16f acc[4], const float* stage, int qa, int qb, int lane) {
   const int lo = (lane >> 5) * kTile + 2 * (lane & 31);
