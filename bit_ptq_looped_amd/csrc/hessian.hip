@@ -181,20 +181,9 @@ __device__ __forceinline__ void run_units(v16f acc[4], float* lds, const HPlan& 
     run_units_t<false>(acc, lds, p, ti, tj, c0, c1, wave, lane);
 }
 
-// Tile element (a, b) of MFMA block (pa, pb), element e, lane l of the wave
-// owning quadrant (qa, qb): a = 64 qa + 2 i + pa, b = 64 qb + 2 j + pb with
-// i = 8 (e / 4) + 4 (l / 32) + e % 4 and j = l % 32.
-__device__ __forceinline__ int elem_a(int qa, int pa, int e, int lane) {
-  return 64 * qa + 2 * (8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) + pa;
-}
-__device__ __forceinline__ int elem_b(int qb, int pb, int lane) { return 64 * qb + 2 * (lane & 31) + pb; }
-
-// S(a, b) of a tile held in LDS as four 64 x 65 quadrants
-__device__ __forceinline__ float tile_at(const float* S, int a, int b) {
-  return S[((a >> 6) * 2 + (b >> 6)) * kQuadLds + (a & 63) * kLds + (b & 63)];
-}
-
-// this wave's accumulator -> its quadrant of S
+// This wave's accumulator -> its quadrant of S (four 64 x 65 quadrants in
+// LDS).  Element e of MFMA block (pa, pb) in lane l is quadrant element
+// (2 i + pa, 2 j + pb) with i = 8 (e / 4) + 4 (l / 32) + e % 4, j = l % 32.
 __device__ void write_quadrant(const v16f acc[4], float* S, int wave, int lane) {
   float* Q = S + wave * kQuadLds;
 #pragma unroll
@@ -209,24 +198,28 @@ __device__ void write_quadrant(const v16f acc[4], float* S, int wave, int lane) 
   }
 }
 
-// H[i0 + a][j0 + b] += S(a, b) (mirror = false) or H[j0 + b][i0 + a] += S(a, b)
-// (mirror = true).  A diagonal tile takes a <= b for the upper half and a < b
-// for the lower, so both halves come from the same values.  Each thread takes
-// 64 elements, with 128 consecutive lanes along the contiguous index of H;
-// the H values of a batch of 8 are all loaded before any is stored.
-__device__ void add_tile_pass(const HPlan& p, const float* S, int ti, int tj, bool mirror) {
-  const bool diag = ti == tj;
-  const int i0 = ti * kTile, j0 = tj * kTile, K = p.K, t = threadIdx.x;
-  const int lo = t & 127, hi = t >> 7;
+// Quadrant w = (qa, qb) of tile (ti, tj), held in LDS as Q[64][65], added
+// to H: H[i0 + a][j0 + b] += Q[a][b] (mirror = false) or H[j0 + b][i0 + a]
+// += Q[a][b] (mirror = true), (i0, j0) the quadrant's origin.  On the
+// diagonal of H (ti == tj and qa == qb) the upper half takes a <= b and the
+// mirror a < b, so both halves come from the same values; quadrant (1, 0) of
+// a diagonal tile is the mirror of (0, 1) and is skipped.  Each thread takes
+// 16 elements, with 64 consecutive lanes along the contiguous index of H; the
+// H values of a batch of 8 are all loaded before any is stored.
+__device__ void add_quadrant_pass(const HPlan& p, const float* Q, int ti, int tj, int w, bool mirror) {
+  const int qa = w >> 1, qb = w & 1;
+  const bool dq = ti == tj && qa == qb;
+  const int i0 = ti * kTile + 64 * qa, j0 = tj * kTile + 64 * qb, K = p.K, t = threadIdx.x;
+  const int lo = t & 63, hi = t >> 6;
   auto elem = [&](int k, int* a, int* b, size_t* off) {
-    *a = mirror ? lo : hi + 2 * k;
-    *b = mirror ? hi + 2 * k : lo;
+    *a = mirror ? lo : hi + 4 * k;
+    *b = mirror ? hi + 4 * k : lo;
     const int i = i0 + *a, j = j0 + *b;
     *off = mirror ? (size_t)j * K + i : (size_t)i * K + j;
-    return i < K && j < K && (!diag || (mirror ? *a < *b : *a <= *b));
+    return i < K && j < K && (!dq || (mirror ? *a < *b : *a <= *b));
   };
-#pragma unroll 1
-  for (int k0 = 0; k0 < 64; k0 += 8) {
+#pragma unroll
+  for (int k0 = 0; k0 < 16; k0 += 8) {
     float h[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -238,9 +231,15 @@ __device__ void add_tile_pass(const HPlan& p, const float* S, int ti, int tj, bo
     for (int k = 0; k < 8; ++k) {
       int a, b;
       size_t off;
-      if (elem(k0 + k, &a, &b, &off)) p.H[off] = h[k] + tile_at(S, a, b);
+      if (elem(k0 + k, &a, &b, &off)) p.H[off] = h[k] + Q[a * kLds + b];
     }
   }
+}
+
+__device__ void add_quadrant(const HPlan& p, const float* Q, int ti, int tj, int w) {
+  if (ti == tj && w == 2) return;
+  add_quadrant_pass(p, Q, ti, tj, w, false);
+  add_quadrant_pass(p, Q, ti, tj, w, true);
 }
 
 // Units [c0, c1) of tile u.  A whole tile is added to H here; a piece of a
@@ -254,8 +253,8 @@ __device__ void run_segment(v16f acc[4], float* lds, const HPlan& p, int u, int 
   if (c0 == 0 && c1 == p.nc) {  // the last stage's barrier has retired every staging read
     write_quadrant(acc, lds, wave, lane);
     __syncthreads();
-    add_tile_pass(p, lds, ti, tj, false);
-    add_tile_pass(p, lds, ti, tj, true);
+#pragma unroll 1
+    for (int w = 0; w < 4; ++w) add_quadrant(p, lds + w * kQuadLds, ti, tj, w);
   } else {
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk)
@@ -299,46 +298,40 @@ __global__ __launch_bounds__(kThreads) void hessian_tiles_kernel(HPlan p) {
 }
 
 // Adds up the pieces of each leftover tile that was split across work
-// groups, in work-group order, and adds the sum to H.  Block (t, y) takes 256
-// elements of leftover tile t (in the piece layout), one per thread, with up
-// to 8 piece loads in flight.
+// groups, in work-group order, and adds the sum to H.  Block (t, w) takes
+// quadrant w of leftover tile t: in the piece layout [wave][block][element]
+// [lane] that is the contiguous block of wave w, 16 elements per thread.
 __global__ __launch_bounds__(kThreads) void hessian_pieces_kernel(HPlan p) {
-  const int t = blockIdx.x;
-  const int e = blockIdx.y * kThreads + threadIdx.x;
+  __shared__ float Q[kQuadLds];
+  const int t = blockIdx.x, w = blockIdx.y;
   const long long v0 = (long long)t * p.nc, v1 = v0 + p.nc;
   const int gf = unit_owner(v0, p.wr), gl = unit_owner(v1 - 1, p.wr);
   if (gf == gl) return;  // covered by one work group, added there
-  float sum = 0.0f;
-  bool have = false;
-  for (int g0 = gf; g0 <= gl; g0 += 8) {
-    float v[8];
-    bool use[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int g = g0 + k;
-      const long long st = unit_start(g, p.wr);
-      use[k] = g <= gl && st < unit_start(g + 1, p.wr);  // empty ranges hold no piece
-      const float* src = p.part + ((size_t)g * 2 + (st >= v0 ? 0 : 1)) * (kTile * kTile);
-      v[k] = use[k] ? src[e] : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (use[k]) {
-        sum = have ? sum + v[k] : v[k];
-        have = true;
-      }
-    }
-  }
-  // e = ((wave * 4 + block) * 16 + element) * 64 + lane
-  const int lane = e & 63, el = (e >> 6) & 15, blk = (e >> 10) & 3, w = e >> 12;
-  const int a = elem_a(w >> 1, blk >> 1, el, lane), b = elem_b(w & 1, blk & 1, lane);
   int ti, tj;
   tile_of(p.q * kGroups + t, &ti, &tj);
-  const bool diag = ti == tj;
-  const int i = ti * kTile + a, j = tj * kTile + b, K = p.K;
-  if (i >= K || j >= K) return;
-  if (!diag || a <= b) p.H[(size_t)i * K + j] += sum;
-  if (!diag || a < b) p.H[(size_t)j * K + i] += sum;
+  if (ti == tj && w == 2) return;  // the mirror of quadrant (0, 1)
+  float sum[16];
+  bool have = false;
+  for (int g = gf; g <= gl; ++g) {
+    const long long st = unit_start(g, p.wr);
+    if (st == unit_start(g + 1, p.wr)) continue;  // empty ranges hold no piece
+    const float* src = p.part + ((size_t)g * 2 + (st >= v0 ? 0 : 1)) * (kTile * kTile) + w * 4096;
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = src[threadIdx.x + kThreads * k];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sum[k] = have ? sum[k] + v[k] : v[k];
+    have = true;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {  // element ((block * 16) + el) * 64 + lane of the quadrant
+    const int e = threadIdx.x + kThreads * k;
+    const int lane = e & 63, el = (e >> 6) & 15, blk = e >> 10;
+    const int i = 8 * (el >> 2) + 4 * (lane >> 5) + (el & 3);
+    Q[(2 * i + (blk >> 1)) * kLds + 2 * (lane & 31) + (blk & 1)] = sum[k];
+  }
+  __syncthreads();
+  add_quadrant(p, Q, ti, tj, w);
 }
 
 int tiles_of(int K) {
@@ -377,7 +370,7 @@ hipError_t launch_hessian(const float* x, int rows, int K, float* H, float* part
   hipLaunchKernelGGL(hessian_tiles_kernel, dim3(kGroups), dim3(kThreads), kLdsBytes, s, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.r == 0) return e;
-  hipLaunchKernelGGL(hessian_pieces_kernel, dim3(p.r, kTile * kTile / kThreads), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(hessian_pieces_kernel, dim3(p.r, 4), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
