@@ -115,6 +115,27 @@ def measured_traffic():
     return float(fields["gemm_traffic_bytes_per_launch"])
 
 
+HESSIAN_TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                    "hbm_traffic_trajectory_hessian_ouro_block_M1024_T4.md")
+
+
+def hessian_traffic():
+    """Counter bytes per trajectory Hessian step from the committed summary,
+    or None when hessian.hip changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        fields = dict(line.split(": ", 1) for line in open(HESSIAN_TRAFFIC_FILE).read().splitlines()
+                      if line.startswith("hessian_"))
+        with open(os.path.join(root, "bit_ptq_looped_amd/csrc/hessian.hip"), "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("hessian_source_sha256") != sha:
+        return None
+    return float(fields["hessian_traffic_bytes_per_step"])
+
+
 def alg_ops(mods, T, M):
     return sum(2.0 * T * M * m.N * m.K for m in mods)
 
@@ -400,7 +421,11 @@ def hessian_bench(lq, torch, mods, T, M, steps, warmup):
         "unit": "TFLOP/s",
         "kernel_ms_per_step": kms / steps,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS},
+                     "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS,
+                     "traffic": hessian_traffic(),
+                     "traffic_unit": "fabric bytes per step (FETCH_SIZE + WRITE_SIZE, copy-calibrated, "
+                                     "both kernels, all 4 inputs)",
+                     "alg_bytes_per_step": sum(4.0 * T * M * m.K + 8.0 * m.K * m.K for m in mods)},
         "per_input": per_k,
     }
 
@@ -441,6 +466,20 @@ def cpu_baseline(wl, mods_meta, rows_hint):
             "seconds": dt}
 
 
+def calibration_copy(args, torch):
+    """One plain device copy of --copy-mib MiB: the reference kernel that
+    scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    if not args.copy_mib:
+        return
+    src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {args.copy_mib} MiB", flush=True)
+    del src, dst
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -474,6 +513,7 @@ def main():
         print(f"profiled {args.profile_decode} decode loop-steps", flush=True)
         return
     if args.profile_hessian:
+        calibration_copy(args, torch)
         hessian_setup(lq, torch, mods, T, M)
         for _ in range(args.profile_hessian):
             hessian_step(lq, mods)
@@ -481,14 +521,7 @@ def main():
         print(f"profiled {args.profile_hessian} trajectory Hessian steps", flush=True)
         return
     if args.profile_steps:
-        if args.copy_mib:
-            src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
-            dst = torch.empty_like(src)
-            torch.cuda.synchronize()
-            dst.copy_(src)
-            torch.cuda.synchronize()
-            print(f"copied {args.copy_mib} MiB", flush=True)
-            del src, dst
+        calibration_copy(args, torch)
         run_steps(lq, mods, 4, args.profile_schedule, args.profile_steps)
         torch.cuda.synchronize()
         print(f"profiled {args.profile_steps} steps", flush=True)
