@@ -136,6 +136,23 @@ def hessian_traffic():
     return float(fields["hessian_traffic_bytes_per_step"])
 
 
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9  # fp32 lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+
+
+def fold_inclusive(mods, T, M, gemm_ms):
+    """The GEMM against a bound that counts the per-group fold: M*N*K/32
+    element-groups per loop, each an fp32 product of the two steps and an FMA
+    into the accumulator (2 VALU lane operations, no packed math), plus the
+    MFMA time of the integer ops.  On gfx950 MFMA and VALU issue cycles add,
+    so the bound is the sum."""
+    groups = sum(T * M * m.N * m.K / 32.0 for m in mods)
+    t_fold = 2.0 * groups / VALU_LANE_OPS
+    t_mfma = alg_ops(mods, T, M) / (INT8_PEAK_TOPS * 1e12)
+    return {"element_groups_per_step": groups, "t_fold_ms": t_fold * 1e3, "t_mfma_ms": t_mfma * 1e3,
+            "bound_ms": (t_fold + t_mfma) * 1e3, "gemm_ms": gemm_ms,
+            "frac": (t_fold + t_mfma) * 1e3 / gemm_ms}
+
+
 def alg_ops(mods, T, M):
     return sum(2.0 * T * M * m.N * m.K for m in mods)
 
@@ -578,6 +595,7 @@ def main():
         "frac_int8_peak": ops / s_ws_nohook / 1e12 / INT8_PEAK_TOPS,
         "frac_hbm_peak": bytes_ls / (s_ws_nohook / T) / 1e9 / HBM_PEAK_GBS,
         "kernels_ms_per_step": {"quant_transform": quant_ms / args.steps, "gemm": gemm_ms / args.steps},
+        "fold_inclusive": fold_inclusive(mods, T, M, gemm_ms / args.steps),
         "ms_per_step_with_timing_hooks": s_ws * 1e3,
         "loop_sequential_pipelined": {"ms_per_step": s_seq * 1e3, "value": ops / s_seq / 1e12},
         "w4a8": {"ms_per_step": s_a8 * 1e3, "value": ops / s_a8 / 1e12,
