@@ -276,6 +276,19 @@ def linear(x, P1, P2, clip: float, bits: int, qw, sw16, group_w: int):
     return y, qa, sa
 
 
+def linear_per_token(x, P1, P2, clip: float, bits: int, qw, sw16, group_w: int):
+    """The per-token arm: the same RTN with one activation step per token
+    ("LoopQ 4-bit quantization of Ouro-1.4B -- raw artifacts", "The arms":
+    ``rtn_w4a4_per_token``).  Eq.(4) over the whole row (one group of K),
+    weights as for :func:`linear` (group-wise), and the dequantized product.
+    Returns ``(y fp64 [M][N], codes, steps [M][1])``."""
+    xt32 = transformed_f32(x, P1, P2)
+    K = xt32.shape[1]
+    qa, sa = quant_act(xt32, clip, bits, group=K)
+    y = qdq_linear(qa, sa, qw, sw16, group_w, group_a=K)
+    return y, qa, sa
+
+
 def looped_forward(xs, P1, P2, clips, bits: int, qw, sw16, group_w: int) -> np.ndarray:
     """The same quantized weights applied at every loop t with the loop's own
     LAS clip ``clips[t]`` (spec ``las``: one clip per module and loop).

@@ -443,3 +443,56 @@ def test_thresholded_rank_of_constructed_subspaces():
     weak = s0 + 1e-3 * step(list(range(20, 30)))
     assert oracle.thresholded_rank(oracle.trajectory_hessian(weak)) == 5
     assert oracle.thresholded_rank(np.zeros((4, 4))) == 0
+
+
+def test_per_token_hand_example():
+    """One step per row ("The arms": rtn_w4a4_per_token), worked by hand.
+    Row 0: absmax 7 over the whole row, so s = fl32(c * 7/7) = c.  Its second
+    half only reaches 0.7, which a group of 32 would quantize on its own step
+    0.1; per token it shares the row's step."""
+    K = 64
+    x = np.zeros((1, K), dtype=np.float32)
+    x[0, :8] = [7.0, -3.5, 1.75, 0.0, 0.5, -0.25, 2.6, -7.0]
+    x[0, 32:36] = [0.7, -0.5, 0.25, 0.6]
+    qw = np.zeros((2, K), dtype=np.int8)
+    qw[0, :8] = [1, 1, 1, 1, 1, 1, 1, 1]
+    qw[1, 32:36] = [1, 2, -3, 7]
+    sw = np.full((2, 2), np.float16(0.5))
+    y, qa, sa = oracle.linear_per_token(x, None, None, 1.0, 4, qw, sw, 32)
+    assert sa.shape == (1, 1) and sa[0, 0] == np.float32(1.0)
+    # rint(x / 1), ties to even: -3.5 -> -4, 0.5 -> 0, -0.25 -> 0, 2.6 -> 3
+    assert list(qa[0, :8]) == [7, -4, 2, 0, 0, 0, 3, -7]
+    assert list(qa[0, 32:36]) == [1, 0, 0, 1]            # 0.7 -> 1, -0.5 -> 0, 0.25 -> 0, 0.6 -> 1
+    # y = s_a * s_w * dot: row 0 of W: 0.5 * (7 - 4 + 2 + 3 - 7) = 0.5; row 1: 0.5 * (1 + 0 + 0 + 7) = 4
+    np.testing.assert_array_equal(y, [[0.5, 4.0]])
+    # clip 0.5: s = 0.5; x / s = 14, -7, 3.5, 0, 1, -0.5, 5.2, -14 -> 7, -7, 4, 0, 1, 0, 5, -7
+    _, qa2, sa2 = oracle.linear_per_token(x, None, None, 0.5, 4, qw, sw, 32)
+    assert sa2[0, 0] == np.float32(0.5)
+    assert list(qa2[0, :8]) == [7, -7, 4, 0, 1, 0, 5, -7]
+    # group-32 quantizes the second half on its own step 0.1 instead
+    _, qg, sg = oracle.linear(x, None, None, 1.0, 4, qw, sw, 32)
+    assert sg[0, 1] == np.float32(np.float32(0.7) / np.float32(7.0))
+    assert list(qg[0, 32:36]) != list(qa[0, 32:36])
+
+
+def test_per_token_equals_groups_when_group_maxima_agree_and_the_fold_form():
+    """Rows whose 32-groups all have the same absmax give identical codes and
+    steps per token and per group; and the per-token y equals the group fold
+    with the row's step repeated in every group slot (the layout the GPU GEMM
+    consumes), up to fp64 summation order."""
+    rng = synth.seeded_rng(synth.TEST, 192)
+    M, K, N = 5, 128, 7
+    x = rng.uniform(-1, 1, size=(M, K)).astype(np.float32)
+    x[:, ::32] = np.float32(3.0)                  # every group's absmax is 3
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sw = rng.uniform(0.01, 0.1, size=(N, K // 32)).astype(np.float16)
+    yt, qt, st = oracle.linear_per_token(x, None, None, 0.8, 4, qw, sw, 32)
+    yg, qg, sg = oracle.linear(x, None, None, 0.8, 4, qw, sw, 32)
+    np.testing.assert_array_equal(qt, qg)
+    np.testing.assert_array_equal(np.repeat(st, K // 32, axis=1), sg)
+    np.testing.assert_allclose(yt, yg, rtol=1e-12, atol=1e-12)
+    # general rows: the fold with repeated steps
+    x = synth.with_outliers(synth.gaussian((M, K), 193), 3, 20.0, 194)
+    yt, qt, st = oracle.linear_per_token(x, None, None, 0.9, 8, qw, sw, 128)
+    folded = oracle.rescale_dots(np.repeat(st, K // 32, axis=1), oracle.group_dots(qt, qw), sw, 128)
+    np.testing.assert_allclose(yt, folded, rtol=1e-12, atol=1e-9)
