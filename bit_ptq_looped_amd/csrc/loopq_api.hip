@@ -421,6 +421,29 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
   return LOOPQ_OK;
 }
 
+// The per-token quantizer on x (or, with a transform, on x~ written to xt
+// first by the group kernel, whose codes and steps the per-token pass then
+// overwrites).  `a` carries the outputs; returns the first HIP error.
+hipError_t per_token_quant(QuantArgs a, float* xt, hipStream_t s) {
+  if (a.P1 != nullptr) {
+    QuantArgs t = a;
+    t.xt_out = xt;
+    hipError_t e;
+    {
+      TimingScope ts(LOOPQ_KERNEL_QUANT_TRANSFORM, s);
+      e = launch_quant_act(t, s);
+    }
+    if (e != hipSuccess) return e;
+    a.x = xt;
+    a.bf16 = 0;
+    a.P1 = a.P2 = nullptr;
+    a.n1 = a.n2 = 0;
+    a.xt_out = nullptr;  // already written by the transform pass
+  }
+  TimingScope ts(LOOPQ_KERNEL_QUANT_TOKEN, s);
+  return launch_quant_token(a, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -476,6 +499,18 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       *bytes = a4 > a8 ? a4 : a8;
       return LOOPQ_OK;
     }
+    case LOOPQ_OP_QUANT_PER_TOKEN:
+      if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (K % 32) return LOOPQ_ERR_UNSUPPORTED;
+      *bytes = align256((size_t)M * K * 4);
+      return LOOPQ_OK;
+    case LOOPQ_OP_LINEAR_PER_TOKEN:
+      if (bits_a != 4 && bits_a != 8) return LOOPQ_ERR_UNSUPPORTED;
+      if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (K % 32) return LOOPQ_ERR_UNSUPPORTED;
+      if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
+      *bytes = act_bytes(1, M, K, N, code_format(bits_a)) + align256((size_t)M * K * 4);
+      return LOOPQ_OK;
     case LOOPQ_OP_HESSIAN:
       if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (K % 32 || K > kHessianMaxK || M > kHessianMaxRows) return LOOPQ_ERR_UNSUPPORTED;
@@ -750,6 +785,93 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
   if (e == hipSuccess) e = prepare_weights(b, fmt, w_codes, K, N, s);
   if (e == hipSuccess) e = run_gemm(b, fmt, M, K, N, w_codes, nullptr, 32, nullptr, dots, 1, s);
   return hip_status(e);
+}
+
+int32_t loopq_quant_act_per_token(const void* x, int32_t dtype, int32_t M, int32_t K, const float* P1,
+                                  int32_t n1, const float* P2, int32_t n2, float clip, int32_t bits_a,
+                                  int8_t* codes, float* scales, float* xt_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  int32_t st = check_act(x, dtype, M, K, bits_a);
+  if (st != LOOPQ_OK) return st;
+  if ((int64_t)M * K > ((int64_t)1 << 40)) return LOOPQ_ERR_UNSUPPORTED;
+  st = check_transform(K, P1, n1, P2, n2);
+  if (st != LOOPQ_OK) return st;
+  if (!clip_ok(clip)) return LOOPQ_ERR_INVALID_ARG;
+  if (M == 0) return LOOPQ_OK;
+  if (!codes || !scales) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(xt_out, 16)) return LOOPQ_ERR_ALIGNMENT;
+  float* xt = xt_out;
+  if (P1 && !xt) {  // x~ staged in the workspace
+    if (!workspace || workspace_bytes < align256((size_t)M * K * 4)) return LOOPQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+    xt = reinterpret_cast<float*>(workspace);
+  }
+  QuantArgs a = make_quant_args(x, dtype, M, K, P1, n1, P2, n2, bits_a);
+  a.clips.c[0] = clip;
+  a.codes = codes;
+  a.scales = scales;
+  a.xt_out = xt_out;
+  return hip_status(per_token_quant(a, xt, as_stream(stream)));
+}
+
+int32_t loopq_linear_per_token(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,
+                               const float* P1, int32_t n1, const float* P2, int32_t n2, float clip,
+                               int32_t bits_a, const void* w_codes, const void* w_scales,
+                               int32_t group_w, float* y, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (M > (1 << 30)) return LOOPQ_ERR_UNSUPPORTED;
+  int32_t st = check_act(x, dtype, M, K, bits_a);
+  if (st != LOOPQ_OK) return st;
+  st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  st = check_gemm_extent(padded_rows(M), K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  st = check_transform(K, P1, n1, P2, n2);
+  if (st != LOOPQ_OK) return st;
+  if (!clip_ok(clip)) return LOOPQ_ERR_INVALID_ARG;
+  if (M == 0) return LOOPQ_OK;
+  if (!w_codes || !w_scales || !y) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(y, 4)) return LOOPQ_ERR_ALIGNMENT;
+  size_t need = 0;
+  loopq_workspace_bytes(LOOPQ_OP_LINEAR_PER_TOKEN, 1, M, K, N, bits_a, &need);
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  const int fmt = code_format(bits_a);
+  ActBuffers b = carve(workspace, 1, M, K, N, 0, M);
+  float* xt = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + act_bytes(1, M, K, N, fmt));
+  ClipTable clips;
+  memset(&clips, 0, sizeof(clips));
+  clips.c[0] = clip;
+  QuantArgs a = internal_quant_args(x, dtype, M, K, P1, n1, P2, n2, clips, M, bits_a, b);
+  const bool few = M <= kDecodeMaxRows;
+  if (few) {  // canonical codes and row-major steps for the few-row kernel
+    a.codes_fmt = kCodesCanonical;
+    a.scales_gm = 0;
+  }
+  hipError_t e = per_token_quant(a, xt, s);
+  if (e != hipSuccess) return LOOPQ_ERR_HIP;
+  if (few) {
+    DecodeCall c;
+    memset(&c, 0, sizeof(c));
+    c.a_codes = reinterpret_cast<const int8_t*>(b.codes);
+    c.a_steps = b.scales;
+    c.R = M;
+    c.K = K;
+    c.N = N;
+    c.qmax = bits_a == 4 ? 7 : 127;
+    c.w = reinterpret_cast<const uint8_t*>(w_codes);
+    c.sw = reinterpret_cast<const __half*>(w_scales);
+    c.gw = group_w;
+    c.y = y;
+    c.mode = 0;
+    TimingScope ts(LOOPQ_KERNEL_DECODE, s);
+    return hip_status(launch_decode(c, s));
+  }
+  e = prepare_weights(b, fmt, w_codes, K, N, s);
+  if (e != hipSuccess) return LOOPQ_ERR_HIP;
+  TimingScope ts(LOOPQ_KERNEL_GEMM, s);
+  return hip_status(run_gemm(b, fmt, M, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s));
 }
 
 int32_t loopq_hessian_accumulate(const float* xt, int32_t rows, int32_t K, float* H, void* workspace,

@@ -126,6 +126,9 @@ struct QuantArgs {
 
 // host launchers -------------------------------------------------------------
 hipError_t launch_quant_act(QuantArgs a, hipStream_t s);
+// one step per row (no transform: a.P1 must be null); the step fills every
+// group slot of the row in a.scales
+hipError_t launch_quant_token(QuantArgs a, hipStream_t s);
 // true if the fused transform kernel's LDS plan fits one work-group
 bool quant_plan_fits(int K, int n1, int n2);
 hipError_t launch_pack_weights(const float* w, int K, int N, int gw, uint8_t* codes,

@@ -167,6 +167,47 @@ __global__ __launch_bounds__(256) void quant_plain_kernel(QuantArgs a) {
   }
 }
 
+// One activation step per token ("LoopQ 4-bit quantization of Ouro-1.4B --
+// raw artifacts", "The arms": rtn_w4a4_per_token): Eq.(4) over the whole row.
+// One work group per row of x (fp32 or bf16; no transform here): the row's
+// absolute maximum, then its step (step_of) and codes (codes4), the same
+// arithmetic as the group quantizer.  The step is written to each of the
+// row's K/32 group slots, so the group-wise GEMM consumes it unchanged.
+// Lane l of each 1024-element window takes elements 4l..4l+3, as in the
+// group kernels (whole quads and 8-lane groups for the tiled stores).
+__device__ __forceinline__ float4 load_row4(const QuantArgs& a, int row, int k) {
+  const int64_t e = (int64_t)row * a.K + k;
+  if (a.bf16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + e);
+    return make_float4(bf16_bits_to_float(u.x & 0xffffu), bf16_bits_to_float(u.x >> 16),
+                       bf16_bits_to_float(u.y & 0xffffu), bf16_bits_to_float(u.y >> 16));
+  }
+  return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + e);
+}
+
+__global__ __launch_bounds__(256) void quant_token_kernel(QuantArgs a) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const int n4 = a.K >> 2;
+  const float qmaxf = (float)a.qmax;
+  const float rq = 1.0f / qmaxf;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const float4 v = load_row4(a, row, 4 * i);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = step_of(amax, a.clips.c[row / a.rows_per_clip], qmaxf, rq);
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const float4 v = load_row4(a, row, 4 * i);
+    store_run(a, row, 4 * i, codes4(v, s, qmaxf), s, ((4 * i) & 31) == 0, v);
+  }
+}
+
 // Work item of slot ii of a wave.  SR (shared row): a wave's NIM slots are
 // consecutive items, all in one row of the chunk (the row's column-tile count
 // is a multiple of NIM), so the stage-1 X operand is read once for all of
@@ -671,6 +712,13 @@ bool quant_plan_fits(int K, int n1, int n2) {
   a.n1 = n1;
   a.n2 = n2;
   return plan_quant(a);
+}
+
+hipError_t launch_quant_token(QuantArgs a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.P1 != nullptr) return hipErrorInvalidValue;  // transform first, then quantize x~
+  hipLaunchKernelGGL(quant_token_kernel, dim3((unsigned)a.rows), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_act(QuantArgs a, hipStream_t s) {

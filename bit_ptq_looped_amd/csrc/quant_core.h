@@ -30,33 +30,30 @@ __device__ __forceinline__ float group8_max(float v) {
   return __int_as_float(b);
 }
 
-// Quantize 4 consecutive elements of one 32-group whose 8 lanes are
-// consecutive in the wave (lane % 8 = position of the 4-element run).
-// Returns the 4 codes packed as int8 bytes; writes the step to *step.
-//
-// The step: base = fl32(absmax / qmax) is formed as q0 = fl32(absmax * rq)
-// with rq = fl32(1 / qmax), then one FMA correction q0 + (absmax - q0 qmax) rq;
-// for qmax = 7 and 127 this equals the correctly rounded quotient for every
-// finite non-negative fp32 absmax (checked exhaustively over all of them).
+// The Eq.(4) step of a group with absolute maximum amax, clip c and
+// rq = fl32(1 / qmax): base = fl32(amax / qmax) is formed as
+// q0 = fl32(amax * rq), then one FMA correction q0 + (amax - q0 qmax) rq; for
+// qmax = 7 and 127 this equals the correctly rounded quotient for every
+// finite non-negative fp32 amax (checked exhaustively over all of them).
 // s = fl32(c * base).
-//
-// The codes: clamp(rint(fl32(x / s)), -qmax, qmax).  The quotient is formed
-// as p = fl32(x * r) with r the hardware reciprocal of s (within 1 ulp):
-// |p - x/s| < 3 * 2^-24 |x/s| and |fl32(x/s) - x/s| <= 2^-24 |x/s|, so below
-// the clamp (|x/s| < 128) p and fl32(x/s) differ by less than 2^-15.  The
-// distance d = |x * r - rint(p)| is taken with one FMA (within 2^-17 of
-// |p - rint(p)|); if d <= 0.5 - 2^-14 then fl32(x/s) lies within
+__device__ __forceinline__ float step_of(float amax, float clip, float qmaxf, float rq) {
+  const float q0 = amax * rq;
+  const float base = __builtin_fmaf(__builtin_fmaf(-q0, qmaxf, amax), rq, q0);  // = fl32(amax / qmax)
+  return clip * base;  // one fp32 product
+}
+
+// The codes of 4 elements on step s, packed as int8 bytes:
+// clamp(rint(fl32(x / s)), -qmax, qmax), 0 when s == 0.  The quotient is
+// formed as p = fl32(x * r) with r the hardware reciprocal of s (within
+// 1 ulp): |p - x/s| < 3 * 2^-24 |x/s| and |fl32(x/s) - x/s| <= 2^-24 |x/s|,
+// so below the clamp (|x/s| < 128) p and fl32(x/s) differ by less than
+// 2^-15.  The distance d = |x * r - rint(p)| is taken with one FMA (within
+// 2^-17 of |p - rint(p)|); if d <= 0.5 - 2^-14 then fl32(x/s) lies within
 // 0.5 - 3 * 2^-17 of rint(p) and rounds to the same integer.  Runs with a
 // larger d, and any run whose r is not a positive finite normal-range value
 // (s outside about [2^-126, 2^126]), are redone with the correctly rounded
 // division.  Above the clamp both sides saturate alike.
-__device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf, float rq, float* step) {
-  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  amax = group8_max(amax);
-  const float q0 = amax * rq;
-  const float base = __builtin_fmaf(__builtin_fmaf(-q0, qmaxf, amax), rq, q0);  // = fl32(amax / qmax)
-  const float s = clip * base;      // one fp32 product
-  *step = s;
+__device__ __forceinline__ uint32_t codes4(float4 v, float s, float qmaxf) {
   if (!(s > 0.0f)) return 0u;
   const float r = __builtin_amdgcn_rcpf(s);
   const float e[4] = {v.x, v.y, v.z, v.w};
@@ -81,6 +78,17 @@ __device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf,
     }
   }
   return packed;
+}
+
+// Quantize 4 consecutive elements of one 32-group whose 8 lanes are
+// consecutive in the wave (lane % 8 = position of the 4-element run).
+// Returns the 4 codes packed as int8 bytes; writes the step to *step.
+__device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf, float rq, float* step) {
+  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  amax = group8_max(amax);
+  const float s = step_of(amax, clip, qmaxf, rq);
+  *step = s;
+  return codes4(v, s, qmaxf);
 }
 
 // LDS strides (elements) of P1, P2 and the X rows: P rows padded to 16 mod

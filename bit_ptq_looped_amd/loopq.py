@@ -29,9 +29,9 @@ LOOPQ_ERR_SINGULAR = -7
 LOOPQ_F32, LOOPQ_BF16 = 0, 1
 LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
 LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD, LOOPQ_OP_LOOPED_FORWARD_EX = 1, 2, 3, 4
-LOOPQ_OP_HESSIAN = 5
+LOOPQ_OP_HESSIAN, LOOPQ_OP_QUANT_PER_TOKEN, LOOPQ_OP_LINEAR_PER_TOKEN = 5, 6, 7
 LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM, LOOPQ_KERNEL_DECODE = 0, 1, 2, 3
-LOOPQ_KERNEL_HESSIAN = 4
+LOOPQ_KERNEL_HESSIAN, LOOPQ_KERNEL_QUANT_TOKEN = 4, 5
 
 # every entry point of include/loopq.h with its ctypes signature
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -53,6 +53,8 @@ SIGNATURES = {
     "loopq_export_weights": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "loopq_group_dots": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "loopq_hessian_accumulate": ([_P, _I, _I, _P, _P, _Z, _P], _I),
+    "loopq_quant_act_per_token": ([_P, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _P, _P, _Z, _P], _I),
+    "loopq_linear_per_token": ([_P, _I, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
     "loopq_timing_enable": ([_I], _I),
     "loopq_timing_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
     "loopq_timing_reset": ([], _I),
@@ -245,6 +247,26 @@ def loopq_group_dots(a_codes, w_codes, N: int, dots, workspace, bits_a: int = 4,
            "loopq_group_dots")
 
 
+def loopq_quant_act_per_token(x, P1, P2, clip: float, bits_a: int, codes, scales, xt_out=None,
+                              workspace=None, stream=None):
+    M, K = x.shape
+    p1, n1, p2, n2 = _factor_args(P1, P2)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().loopq_quant_act_per_token(_ptr(x), _dtype_code(x), M, K, p1, n1, p2, n2, float(clip), bits_a,
+                                            _ptr(codes), _ptr(scales), _ptr(xt_out), _ptr(workspace), nbytes,
+                                            _stream(stream)), "loopq_quant_act_per_token")
+
+
+def loopq_linear_per_token(x, P1, P2, clip: float, bits_a: int, w_codes, w_scales, group_w: int, N: int,
+                           y, workspace, stream=None):
+    M, K = x.shape
+    p1, n1, p2, n2 = _factor_args(P1, P2)
+    _check(load().loopq_linear_per_token(_ptr(x), _dtype_code(x), M, K, N, p1, n1, p2, n2, float(clip), bits_a,
+                                         _ptr(w_codes), _ptr(w_scales), group_w, _ptr(y), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)),
+           "loopq_linear_per_token")
+
+
 def loopq_hessian_accumulate(xt, H, workspace=None, stream=None):
     """H += xt^T xt; xt fp32 [rows][K], H fp32 [K][K], both on the device."""
     rows, K = xt.shape
@@ -261,7 +283,7 @@ def loopq_timing_reset() -> None:
     _check(load().loopq_timing_reset(), "loopq_timing_reset")
 
 
-def loopq_timing_read(n: int = 5):
+def loopq_timing_read(n: int = 6):
     """Per kernel id: (total milliseconds, launches) since the last read."""
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_int64 * n)()

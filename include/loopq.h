@@ -90,7 +90,9 @@ typedef enum {
   LOOPQ_OP_LOOPED_FORWARD = 2,
   LOOPQ_OP_FOLD = 3,
   LOOPQ_OP_LOOPED_FORWARD_EX = 4, /* bits_a ignored: enough for 4- and 8-bit loops */
-  LOOPQ_OP_HESSIAN = 5            /* rows as M; T, N and bits_a ignored */
+  LOOPQ_OP_HESSIAN = 5,           /* rows as M; T, N and bits_a ignored */
+  LOOPQ_OP_QUANT_PER_TOKEN = 6,   /* M, K; T, N and bits_a ignored */
+  LOOPQ_OP_LINEAR_PER_TOKEN = 7   /* M, K, N, bits_a; T ignored */
 } loopq_op;
 
 /* ABI version of the loaded library (LOOPQ_ABI_VERSION it was built with). */
@@ -161,6 +163,35 @@ int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, in
                           float clip, int32_t bits_a,
                           const void* w_codes, const void* w_scales, int32_t group_w,
                           float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-token activation steps: the same RTN with one step per token.
+ * Page: "LoopQ 4-bit quantization of Ouro-1.4B -- raw artifacts", "The arms"
+ * (rtn_w4a4_per_token, the field-standard W4A4 baseline setting).  Eq.(4)
+ * over the whole row of x~ (x with no transform): for row m,
+ * s = fl32(clip * fl32(absmax_m / qmax)), codes[m][k] = clamp(rint(fl32(x~ / s)),
+ * -qmax, qmax) (0 when s == 0), with the arithmetic of loopq_quant_act.
+ * codes int8 [M][K]; scales fp32 [M][K/32]: the row's one step written to each
+ * of its K/32 group slots, so loopq_gemm_codes consumes the pair unchanged.
+ * xt_out (nullable) receives x~.  Arguments and errors as loopq_quant_act.
+ * Workspace: with a transform and xt_out NULL, x~ is staged in `workspace`
+ * (loopq_workspace_bytes(LOOPQ_OP_QUANT_PER_TOKEN, 0, M, K, 0, 0, ...)
+ * bytes, 256-byte aligned); otherwise workspace may be NULL. */
+int32_t loopq_quant_act_per_token(const void* x, int32_t dtype, int32_t M, int32_t K,
+                                  const float* P1, int32_t n1, const float* P2, int32_t n2,
+                                  float clip, int32_t bits_a, int8_t* codes, float* scales,
+                                  float* xt_out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* One linear with per-token activation steps: loopq_quant_act_per_token, then
+ * the GEMM of loopq_gemm_codes, y = sum_j s_a[m] * s_w[n][32j/group_w] * d[m][n][j]
+ * (= s_a[m] * sum_j s_w * d up to fp32 rounding order).  Page as above.
+ * Arguments as loopq_w4a4_linear.  Workspace:
+ * loopq_workspace_bytes(LOOPQ_OP_LINEAR_PER_TOKEN, 0, M, K, N, bits_a, ...). */
+int32_t loopq_linear_per_token(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,
+                               const float* P1, int32_t n1, const float* P2, int32_t n2,
+                               float clip, int32_t bits_a, const void* w_codes,
+                               const void* w_scales, int32_t group_w, float* y, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* a6 -- the loop: the same packed weights applied at every loop t with the
  * loop's own clip.  Page: "LoopQ 4-bit quantization of Ouro-1.4B" (24 layers
@@ -272,7 +303,8 @@ typedef enum {
   LOOPQ_KERNEL_QUANT_PLAIN = 1,     /* quantizer without transform */
   LOOPQ_KERNEL_GEMM = 2,            /* integer GEMM + rescale */
   LOOPQ_KERNEL_DECODE = 3,          /* few-row linear: transform, quantizer and product in one launch */
-  LOOPQ_KERNEL_HESSIAN = 4          /* trajectory Hessian accumulation (one record per call) */
+  LOOPQ_KERNEL_HESSIAN = 4,         /* trajectory Hessian accumulation (one record per call) */
+  LOOPQ_KERNEL_QUANT_TOKEN = 5      /* per-token quantizer */
 } loopq_kernel_id;
 
 /* Turn the hooks on (1) or off (0).  Host only; cheap. */

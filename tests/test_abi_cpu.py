@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
         assert n in loopq.SIGNATURES, n
@@ -188,3 +188,37 @@ def test_hessian_workspace_and_host_rejections(lib):
     # no rows: nothing to add, nothing enqueued, whatever the pointers
     assert call(FAKE, 0, 2048, FAKE) == loopq.LOOPQ_OK
     assert call(None, 0, 2048, None, w=None) == loopq.LOOPQ_OK
+
+
+def test_per_token_entries_reject_on_host(lib):
+    qop, lop = loopq.LOOPQ_OP_QUANT_PER_TOKEN, loopq.LOOPQ_OP_LINEAR_PER_TOKEN
+    assert loopq.loopq_workspace_bytes(qop, 0, 100, 2048, 0, 0) == 100 * 2048 * 4
+    # the linear: the group path's activation buffers plus the x~ staging
+    assert loopq.loopq_workspace_bytes(lop, 0, 100, 2048, 512, 4) == \
+        loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LINEAR, 1, 100, 2048, 512, 4) + 100 * 2048 * 4
+    with pytest.raises(loopq.LoopQError) as e:
+        loopq.loopq_workspace_bytes(lop, 0, 100, 2048, 512, 5)
+    assert e.value.status == loopq.LOOPQ_ERR_UNSUPPORTED
+    q = lambda *a: _raw(lib, "loopq_quant_act_per_token", *a)
+    # x, dtype, M, K, P1, n1, P2, n2, clip, bits, codes, scales, xt_out, ws, ws_bytes, stream
+    assert q(FAKE, 0, 4, 48, None, 0, None, 0, 1.0, 4, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert q(FAKE, 0, 4, 256, None, 0, None, 0, 0.0, 4, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert q(FAKE, 0, 4, 256, None, 0, None, 0, 1.0, 6, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert q(FAKE, 0, 4, 256, None, 0, None, 0, 1.0, 4, None, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert q(FAKE, 0, 4, 256, None, 0, None, 0, 1.0, 4, FAKE + 2, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_ALIGNMENT
+    # a transform with no x~ output needs the staging workspace
+    assert q(FAKE, 0, 4, 256, FAKE, 16, FAKE, 16, 1.0, 4, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_WORKSPACE
+    assert q(FAKE, 0, 4, 256, FAKE, 16, FAKE, 16, 1.0, 4, FAKE, FAKE, None, FAKE, 4 * 256 * 4 - 1, None) == \
+        loopq.LOOPQ_ERR_WORKSPACE
+    assert q(FAKE, 0, 4, 256, FAKE, 16, FAKE, 8, 1.0, 4, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert q(FAKE, 0, 0, 256, None, 0, None, 0, 1.0, 4, None, None, None, None, 0, None) == loopq.LOOPQ_OK
+    lin = lambda *a: _raw(lib, "loopq_linear_per_token", *a)
+    # x, dtype, M, K, N, P1, n1, P2, n2, clip, bits, w_codes, w_scales, gw, y, ws, ws_bytes, stream
+    assert lin(FAKE, 0, 4, 256, 128, None, 0, None, 0, 1.0, 4, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
+        loopq.LOOPQ_ERR_UNSUPPORTED                                    # group_w
+    assert lin(FAKE, 0, 4, 256, 128, None, 0, None, 0, 1.0, 4, FAKE, FAKE, 32, FAKE, FAKE, 16, None) == \
+        loopq.LOOPQ_ERR_WORKSPACE
+    assert lin(FAKE, 0, 4, 256, 128, None, 0, None, 0, 1.0, 4, None, FAKE, 32, FAKE, FAKE, 1 << 30, None) == \
+        loopq.LOOPQ_ERR_INVALID_ARG
+    assert lin(FAKE, 0, 4, 256, 128, None, 0, None, 0, float("nan"), 4, FAKE, FAKE, 32, FAKE, FAKE, 1 << 30, None) == \
+        loopq.LOOPQ_ERR_INVALID_ARG
