@@ -375,6 +375,33 @@ def loop_dependent_bench(lq, synth, torch, wl, mods, steps, warmup):
     return out
 
 
+def per_token_bench(lq, torch, mods, T, M, steps, warmup):
+    """The block's step with one activation step per token (the
+    rtn_w4a4_per_token arm) on the same transforms and packed weights: per
+    quantized input one loopq_looped_forward_per_token over all T loops
+    (transform pass, per-token quantizer, one weight-stationary GEMM).  Same
+    algorithmic ops."""
+    for m in mods:
+        m.ws_tok = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN, T, M, m.K, m.N, 4)
+
+    def run(n):
+        for _ in range(n):
+            for m in mods:
+                lq.loopq_looped_forward_per_token(m.x, m.P1, m.P2, m.clips, 4, m.codes, m.scales, 32, m.N, m.y,
+                                                  m.ws_tok)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    for m in mods:
+        del m.ws_tok
+    return {"what": "per-token activation steps, W4A4, all T loops of an input in one weight-stationary call",
+            "ms_per_step": dt * 1e3, "value": alg_ops(mods, T, M) / dt / 1e12, "unit": "TOPS"}
+
+
 def hessian_setup(lq, torch, mods, T, M):
     """x~ of every loop of each quantized input (the quantizer's dump, formed
     once, untimed), a zeroed fp32 [K][K] Hessian and the workspace per input."""
@@ -604,6 +631,7 @@ def main():
     }
     if not args.no_loop_dependent:
         out["loop_dependent"] = loop_dependent_bench(lq, synth, torch, wl, mods, max(5, args.steps // 2), 2)
+    out["per_token"] = per_token_bench(lq, torch, mods, T, M, max(5, args.steps // 2), 2)
     if not args.no_hessian:
         out["trajectory_hessian"] = hessian_bench(lq, torch, mods, T, M, max(5, args.steps // 5), 2)
     if not args.no_decode:

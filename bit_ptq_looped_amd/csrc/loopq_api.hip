@@ -504,13 +504,15 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       if (K % 32) return LOOPQ_ERR_UNSUPPORTED;
       *bytes = align256((size_t)M * K * 4);
       return LOOPQ_OK;
-    case LOOPQ_OP_LINEAR_PER_TOKEN:
+    case LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN: {
       if (bits_a != 4 && bits_a != 8) return LOOPQ_ERR_UNSUPPORTED;
-      if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
-      if (K % 32) return LOOPQ_ERR_UNSUPPORTED;
+      if (T <= 0 || M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (T > LOOPQ_MAX_LOOPS || K % 32) return LOOPQ_ERR_UNSUPPORTED;
       if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
-      *bytes = act_bytes(1, M, K, N, code_format(bits_a)) + align256((size_t)M * K * 4);
+      const int64_t rows = (int64_t)T * M;
+      *bytes = act_bytes(1, rows, K, N, code_format(bits_a)) + align256((size_t)rows * K * 4);
       return LOOPQ_OK;
+    }
     case LOOPQ_OP_HESSIAN:
       if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (K % 32 || K > kHessianMaxK || M > kHessianMaxRows) return LOOPQ_ERR_UNSUPPORTED;
@@ -814,37 +816,43 @@ int32_t loopq_quant_act_per_token(const void* x, int32_t dtype, int32_t M, int32
   return hip_status(per_token_quant(a, xt, as_stream(stream)));
 }
 
-int32_t loopq_linear_per_token(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,
-                               const float* P1, int32_t n1, const float* P2, int32_t n2, float clip,
-                               int32_t bits_a, const void* w_codes, const void* w_scales,
-                               int32_t group_w, float* y, void* workspace, size_t workspace_bytes,
-                               void* stream) {
-  if (M > (1 << 30)) return LOOPQ_ERR_UNSUPPORTED;
+int32_t loopq_looped_forward_per_token(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
+                                       int32_t N, const float* P1, int32_t n1, const float* P2, int32_t n2,
+                                       const float* clips_host, int32_t bits_a, const void* w_codes,
+                                       const void* w_scales, int32_t group_w, float* y, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (T <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (T > LOOPQ_MAX_LOOPS) return LOOPQ_ERR_UNSUPPORTED;
+  if ((int64_t)T * M > (int64_t)1 << 30) return LOOPQ_ERR_UNSUPPORTED;
   int32_t st = check_act(x, dtype, M, K, bits_a);
   if (st != LOOPQ_OK) return st;
   st = check_weights(K, N, group_w);
   if (st != LOOPQ_OK) return st;
-  st = check_gemm_extent(padded_rows(M), K, N, group_w);
+  st = check_gemm_extent(padded_rows((int64_t)T * M), K, N, group_w);
   if (st != LOOPQ_OK) return st;
   st = check_transform(K, P1, n1, P2, n2);
   if (st != LOOPQ_OK) return st;
-  if (!clip_ok(clip)) return LOOPQ_ERR_INVALID_ARG;
+  if (!clips_host) return LOOPQ_ERR_INVALID_ARG;
+  ClipTable clips;
+  memset(&clips, 0, sizeof(clips));
+  for (int t = 0; t < T; ++t) {
+    if (!clip_ok(clips_host[t])) return LOOPQ_ERR_INVALID_ARG;
+    clips.c[t] = clips_host[t];
+  }
   if (M == 0) return LOOPQ_OK;
   if (!w_codes || !w_scales || !y) return LOOPQ_ERR_INVALID_ARG;
   if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(y, 4)) return LOOPQ_ERR_ALIGNMENT;
   size_t need = 0;
-  loopq_workspace_bytes(LOOPQ_OP_LINEAR_PER_TOKEN, 1, M, K, N, bits_a, &need);
+  loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN, T, M, K, N, bits_a, &need);
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  const int rows = T * M;
   hipStream_t s = as_stream(stream);
   const int fmt = code_format(bits_a);
-  ActBuffers b = carve(workspace, 1, M, K, N, 0, M);
-  float* xt = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + act_bytes(1, M, K, N, fmt));
-  ClipTable clips;
-  memset(&clips, 0, sizeof(clips));
-  clips.c[0] = clip;
-  QuantArgs a = internal_quant_args(x, dtype, M, K, P1, n1, P2, n2, clips, M, bits_a, b);
-  const bool few = M <= kDecodeMaxRows;
+  ActBuffers b = carve(workspace, 1, rows, K, N, 0, rows);
+  float* xt = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + act_bytes(1, rows, K, N, fmt));
+  QuantArgs a = internal_quant_args(x, dtype, rows, K, P1, n1, P2, n2, clips, M, bits_a, b);
+  const bool few = rows <= kDecodeMaxRows;
   if (few) {  // canonical codes and row-major steps for the few-row kernel
     a.codes_fmt = kCodesCanonical;
     a.scales_gm = 0;
@@ -856,7 +864,7 @@ int32_t loopq_linear_per_token(const void* x, int32_t dtype, int32_t M, int32_t 
     memset(&c, 0, sizeof(c));
     c.a_codes = reinterpret_cast<const int8_t*>(b.codes);
     c.a_steps = b.scales;
-    c.R = M;
+    c.R = rows;
     c.K = K;
     c.N = N;
     c.qmax = bits_a == 4 ? 7 : 127;
@@ -871,7 +879,7 @@ int32_t loopq_linear_per_token(const void* x, int32_t dtype, int32_t M, int32_t 
   e = prepare_weights(b, fmt, w_codes, K, N, s);
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   TimingScope ts(LOOPQ_KERNEL_GEMM, s);
-  return hip_status(run_gemm(b, fmt, M, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s));
+  return hip_status(run_gemm(b, fmt, rows, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s));
 }
 
 int32_t loopq_hessian_accumulate(const float* xt, int32_t rows, int32_t K, float* H, void* workspace,

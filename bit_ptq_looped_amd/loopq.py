@@ -29,7 +29,7 @@ LOOPQ_ERR_SINGULAR = -7
 LOOPQ_F32, LOOPQ_BF16 = 0, 1
 LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
 LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD, LOOPQ_OP_LOOPED_FORWARD_EX = 1, 2, 3, 4
-LOOPQ_OP_HESSIAN, LOOPQ_OP_QUANT_PER_TOKEN, LOOPQ_OP_LINEAR_PER_TOKEN = 5, 6, 7
+LOOPQ_OP_HESSIAN, LOOPQ_OP_QUANT_PER_TOKEN, LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 5, 6, 7
 LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM, LOOPQ_KERNEL_DECODE = 0, 1, 2, 3
 LOOPQ_KERNEL_HESSIAN, LOOPQ_KERNEL_QUANT_TOKEN = 4, 5
 
@@ -54,7 +54,8 @@ SIGNATURES = {
     "loopq_group_dots": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "loopq_hessian_accumulate": ([_P, _I, _I, _P, _P, _Z, _P], _I),
     "loopq_quant_act_per_token": ([_P, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _P, _P, _Z, _P], _I),
-    "loopq_linear_per_token": ([_P, _I, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
+    "loopq_looped_forward_per_token": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _P, _Z,
+                                        _P], _I),
     "loopq_timing_enable": ([_I], _I),
     "loopq_timing_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
     "loopq_timing_reset": ([], _I),
@@ -257,14 +258,19 @@ def loopq_quant_act_per_token(x, P1, P2, clip: float, bits_a: int, codes, scales
                                             _stream(stream)), "loopq_quant_act_per_token")
 
 
-def loopq_linear_per_token(x, P1, P2, clip: float, bits_a: int, w_codes, w_scales, group_w: int, N: int,
-                           y, workspace, stream=None):
-    M, K = x.shape
+def loopq_looped_forward_per_token(x, P1, P2, clips: Sequence[float], bits_a: int, w_codes, w_scales,
+                                   group_w: int, N: int, y, workspace, stream=None):
+    """x [T][M][K] (or [M][K] for one loop), one clip per loop."""
+    if x.dim() == 2:
+        x = x.unsqueeze(0)
+    T, M, K = x.shape
     p1, n1, p2, n2 = _factor_args(P1, P2)
-    _check(load().loopq_linear_per_token(_ptr(x), _dtype_code(x), M, K, N, p1, n1, p2, n2, float(clip), bits_a,
-                                         _ptr(w_codes), _ptr(w_scales), group_w, _ptr(y), _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(stream)),
-           "loopq_linear_per_token")
+    c = (ctypes.c_float * T)(*[float(v) for v in clips])
+    _check(load().loopq_looped_forward_per_token(_ptr(x), _dtype_code(x), T, M, K, N, p1, n1, p2, n2,
+                                                 ctypes.cast(c, ctypes.c_void_p), bits_a, _ptr(w_codes),
+                                                 _ptr(w_scales), group_w, _ptr(y), _ptr(workspace),
+                                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "loopq_looped_forward_per_token")
 
 
 def loopq_hessian_accumulate(xt, H, workspace=None, stream=None):

@@ -92,7 +92,7 @@ typedef enum {
   LOOPQ_OP_LOOPED_FORWARD_EX = 4, /* bits_a ignored: enough for 4- and 8-bit loops */
   LOOPQ_OP_HESSIAN = 5,           /* rows as M; T, N and bits_a ignored */
   LOOPQ_OP_QUANT_PER_TOKEN = 6,   /* M, K; T, N and bits_a ignored */
-  LOOPQ_OP_LINEAR_PER_TOKEN = 7   /* M, K, N, bits_a; T ignored */
+  LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 7 /* T, M, K, N, bits_a */
 } loopq_op;
 
 /* ABI version of the loaded library (LOOPQ_ABI_VERSION it was built with). */
@@ -182,16 +182,21 @@ int32_t loopq_quant_act_per_token(const void* x, int32_t dtype, int32_t M, int32
                                   float* xt_out, void* workspace, size_t workspace_bytes,
                                   void* stream);
 
-/* One linear with per-token activation steps: loopq_quant_act_per_token, then
- * the GEMM of loopq_gemm_codes, y = sum_j s_a[m] * s_w[n][32j/group_w] * d[m][n][j]
- * (= s_a[m] * sum_j s_w * d up to fp32 rounding order).  Page as above.
- * Arguments as loopq_w4a4_linear.  Workspace:
- * loopq_workspace_bytes(LOOPQ_OP_LINEAR_PER_TOKEN, 0, M, K, N, bits_a, ...). */
-int32_t loopq_linear_per_token(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,
-                               const float* P1, int32_t n1, const float* P2, int32_t n2,
-                               float clip, int32_t bits_a, const void* w_codes,
-                               const void* w_scales, int32_t group_w, float* y, void* workspace,
-                               size_t workspace_bytes, void* stream);
+/* The loop with per-token activation steps: for each loop t,
+ * loopq_quant_act_per_token of x_t with the loop's clip clips_host[t], then
+ * the GEMM of loopq_gemm_codes against the same packed weights,
+ * y_t = sum_j s_a[m] * s_w[n][32j/group_w] * d[m][n][j] (= s_a[m] * sum_j s_w * d
+ * up to fp32 rounding order).  Page as above; the loop as for
+ * loopq_looped_forward.  All T*M rows run weight-stationary (one pass over
+ * the weights); T = 1 is one linear.  x [T][M][K], y [T][M][N]; other
+ * arguments and errors as loopq_looped_forward.  Workspace:
+ * loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN, T, M, K, N, bits_a, ...). */
+int32_t loopq_looped_forward_per_token(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
+                                       int32_t N, const float* P1, int32_t n1, const float* P2,
+                                       int32_t n2, const float* clips_host, int32_t bits_a,
+                                       const void* w_codes, const void* w_scales, int32_t group_w,
+                                       float* y, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /* a6 -- the loop: the same packed weights applied at every loop t with the
  * loop's own clip.  Page: "LoopQ 4-bit quantization of Ouro-1.4B" (24 layers

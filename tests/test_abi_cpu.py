@@ -191,14 +191,17 @@ def test_hessian_workspace_and_host_rejections(lib):
 
 
 def test_per_token_entries_reject_on_host(lib):
-    qop, lop = loopq.LOOPQ_OP_QUANT_PER_TOKEN, loopq.LOOPQ_OP_LINEAR_PER_TOKEN
+    qop, lop = loopq.LOOPQ_OP_QUANT_PER_TOKEN, loopq.LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN
     assert loopq.loopq_workspace_bytes(qop, 0, 100, 2048, 0, 0) == 100 * 2048 * 4
-    # the linear: the group path's activation buffers plus the x~ staging
-    assert loopq.loopq_workspace_bytes(lop, 0, 100, 2048, 512, 4) == \
-        loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LINEAR, 1, 100, 2048, 512, 4) + 100 * 2048 * 4
-    with pytest.raises(loopq.LoopQError) as e:
-        loopq.loopq_workspace_bytes(lop, 0, 100, 2048, 512, 5)
-    assert e.value.status == loopq.LOOPQ_ERR_UNSUPPORTED
+    # the loop: the group path's activation buffers for T*M rows plus their x~ staging
+    assert loopq.loopq_workspace_bytes(lop, 3, 100, 2048, 512, 4) == \
+        loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LINEAR, 1, 300, 2048, 512, 4) + 300 * 2048 * 4
+    for args, want in (((lop, 3, 100, 2048, 512, 5), loopq.LOOPQ_ERR_UNSUPPORTED),
+                       ((lop, 65, 1, 2048, 512, 4), loopq.LOOPQ_ERR_UNSUPPORTED),
+                       ((lop, 0, 1, 2048, 512, 4), loopq.LOOPQ_ERR_INVALID_ARG)):
+        with pytest.raises(loopq.LoopQError) as e:
+            loopq.loopq_workspace_bytes(*args)
+        assert e.value.status == want
     q = lambda *a: _raw(lib, "loopq_quant_act_per_token", *a)
     # x, dtype, M, K, P1, n1, P2, n2, clip, bits, codes, scales, xt_out, ws, ws_bytes, stream
     assert q(FAKE, 0, 4, 48, None, 0, None, 0, 1.0, 4, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_UNSUPPORTED
@@ -212,13 +215,13 @@ def test_per_token_entries_reject_on_host(lib):
         loopq.LOOPQ_ERR_WORKSPACE
     assert q(FAKE, 0, 4, 256, FAKE, 16, FAKE, 8, 1.0, 4, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_UNSUPPORTED
     assert q(FAKE, 0, 0, 256, None, 0, None, 0, 1.0, 4, None, None, None, None, 0, None) == loopq.LOOPQ_OK
-    lin = lambda *a: _raw(lib, "loopq_linear_per_token", *a)
-    # x, dtype, M, K, N, P1, n1, P2, n2, clip, bits, w_codes, w_scales, gw, y, ws, ws_bytes, stream
-    assert lin(FAKE, 0, 4, 256, 128, None, 0, None, 0, 1.0, 4, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
-        loopq.LOOPQ_ERR_UNSUPPORTED                                    # group_w
-    assert lin(FAKE, 0, 4, 256, 128, None, 0, None, 0, 1.0, 4, FAKE, FAKE, 32, FAKE, FAKE, 16, None) == \
-        loopq.LOOPQ_ERR_WORKSPACE
-    assert lin(FAKE, 0, 4, 256, 128, None, 0, None, 0, 1.0, 4, None, FAKE, 32, FAKE, FAKE, 1 << 30, None) == \
-        loopq.LOOPQ_ERR_INVALID_ARG
-    assert lin(FAKE, 0, 4, 256, 128, None, 0, None, 0, float("nan"), 4, FAKE, FAKE, 32, FAKE, FAKE, 1 << 30, None) == \
-        loopq.LOOPQ_ERR_INVALID_ARG
+    arr = lambda vals: ctypes.cast((ctypes.c_float * len(vals))(*vals), ctypes.c_void_p)
+    lp = lambda T, clips, gw=32, ws=1 << 30, wc=FAKE: _raw(
+        lib, "loopq_looped_forward_per_token", FAKE, 0, T, 4, 256, 128, None, 0, None, 0, arr(clips), 4, wc, FAKE,
+        gw, FAKE, FAKE, ws, None)
+    assert lp(2, [1.0, 0.9], gw=64) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert lp(2, [1.0, 0.9], ws=16) == loopq.LOOPQ_ERR_WORKSPACE
+    assert lp(2, [1.0, 0.9], wc=None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert lp(2, [1.0, float("nan")]) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert lp(0, [1.0]) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert lp(65, [1.0] * 65) == loopq.LOOPQ_ERR_UNSUPPORTED

@@ -106,42 +106,47 @@ def test_quant_per_token_zero_row_and_saturation(lq):
     assert codes[2, 7] == 7             # clip 0.5 saturates the maximum at qmax
 
 
-# (M, K, N, gw, transform): few-row kernel (M <= 16) and the MFMA GEMM, both
-# code formats (A4 fp6 operands, A8 INT8), weight groups of 32 and 128
+# (T, M, K, N, gw, factors): the few-row kernel (T*M <= 16) and the MFMA GEMM,
+# both code formats (A4 fp6 operands, A8 INT8), weight groups of 32 and 128;
+# every loop with its own clip
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("M,K,N,gw,factors", [(3, 512, 96, 32, (16, 32)), (16, 2048, 200, 32, (32, 64)),
-                                              (100, 2048, 160, 32, (32, 64)), (70, 640, 64, 128, None)])
-def test_linear_per_token_matches_oracle(lq, bits, M, K, N, gw, factors):
-    say(f"per-token linear A{bits} M={M} K={K} N={N} gw={gw} factors={factors}")
+@pytest.mark.parametrize("T,M,K,N,gw,factors", [(1, 3, 512, 96, 32, (16, 32)), (4, 4, 2048, 200, 32, (32, 64)),
+                                                (3, 100, 2048, 160, 32, (32, 64)), (1, 70, 640, 64, 128, None),
+                                                (2, 40, 5632, 72, 32, (64, 88))])
+def test_looped_per_token_matches_oracle(lq, bits, T, M, K, N, gw, factors):
+    say(f"per-token loop A{bits} T={T} M={M} K={K} N={N} gw={gw} factors={factors}")
     P1 = P2 = None
     if factors:
         rng = synth.seeded_rng(synth.TEST, 204, *factors)
         P1, P2 = synth.haar_orthogonal(factors[0], rng), synth.haar_orthogonal(factors[1], rng)
-    xdev, x32 = x_dev_and_f32(M, K, "bf16", 3)
+    xdev, x32 = x_dev_and_f32(T * M, K, "bf16", 3)
+    clips = [0.95 - 0.1 * t for t in range(T)]
     w = synth.gaussian((N, K), 205, N, K, scale=0.02)
     codes, scales = pack(lq, w, gw)
-    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR_PER_TOKEN, 1, M, K, N, bits)
-    lq.loopq_linear_per_token(xdev, None if P1 is None else dev(P1), None if P2 is None else dev(P2),
-                              0.9, bits, codes, scales, gw, N, y, ws)
+    y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN, T, M, K, N, bits)
+    lq.loopq_looped_forward_per_token(xdev.view(T, M, K), None if P1 is None else dev(P1),
+                                      None if P2 is None else dev(P2), clips, bits, codes, scales, gw, N, y, ws)
     torch.cuda.synchronize()
     qw, sw = oracle.quant_weights(w, gw)
-    xt = gpu_xt(lq, xdev, x32, P1, P2)
-    ref, _, _ = oracle.linear_per_token(xt, None, None, 0.9, bits, qw, sw, gw)
-    err = rel_err(y.cpu().numpy(), ref)
-    say(f"  rel err {err:.2e}")
-    assert err <= Y_TOL
-    # per token differs from the group-32 arm on these outlier rows
-    ref_g, _, _ = oracle.linear(xt, None, None, 0.9, bits, qw, sw, gw)
-    assert rel_err(ref, ref_g) > 1e-3
+    xt = gpu_xt(lq, xdev, x32, P1, P2).reshape(T, M, K)
+    got = y.cpu().numpy()
+    for t in range(T):
+        ref, _, _ = oracle.linear_per_token(xt[t], None, None, clips[t], bits, qw, sw, gw)
+        err = rel_err(got[t], ref)
+        say(f"  loop {t}: rel err {err:.2e}")
+        assert err <= Y_TOL
+        # per token differs from the group-32 arm on these outlier rows
+        ref_g, _, _ = oracle.linear(xt[t], None, None, clips[t], bits, qw, sw, gw)
+        assert rel_err(ref, ref_g) > 1e-3
 
 
-def test_linear_per_token_empty_is_a_no_op(lq):
+def test_looped_per_token_empty_is_a_no_op(lq):
     K, N = 256, 64
     codes, scales = pack(lq, synth.gaussian((N, K), 206, scale=0.02), 32)
-    y = torch.full((1, N), 5.0, device="cuda")
-    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR_PER_TOKEN, 1, 1, K, N, 4)
-    lq.loopq_linear_per_token(torch.empty((0, K), dtype=torch.float32, device="cuda"), None, None, 1.0, 4,
-                              codes, scales, 32, N, y, ws)
+    y = torch.full((1, 1, N), 5.0, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN, 1, 1, K, N, 4)
+    lq.loopq_looped_forward_per_token(torch.empty((1, 0, K), dtype=torch.float32, device="cuda"), None, None, [1.0],
+                                      4, codes, scales, 32, N, y, ws)
     torch.cuda.synchronize()
     assert torch.all(y == 5.0)
