@@ -289,6 +289,26 @@ def linear_per_token(x, P1, P2, clip: float, bits: int, qw, sw16, group_w: int):
     return y, qa, sa
 
 
+def recurrent_adapter(s0, e, P1, P2, clips, bits: int, qw, sw16, group_w: int) -> np.ndarray:
+    """A dependent recurrence through one quantized linear: the adapter of a
+    depth-recurrent model maps ``cat(s_t, e)`` back to the model width with no
+    residual path ("Quantizing Looped Transformers", Figure 4, the Huginn
+    recurrence loop), here with the recurrent blocks between two adapter calls
+    left out: ``s_{t+1} = fl32(linear(cat(s_t, e)))`` with loop t's clip.
+    ``s0`` and ``e`` are ``[M][N]``, the weight ``[N][2N]``; returns the states
+    ``s_1 .. s_T`` as fp32 ``[T][M][N]`` (the state is kept in fp32 between
+    loops, as a device would store it)."""
+    s = np.asarray(s0, dtype=np.float32)
+    e = np.asarray(e, dtype=np.float32)
+    out = []
+    for c in clips:
+        x = np.concatenate([s, e], axis=1)
+        y, _, _ = linear(x, P1, P2, float(c), bits, qw, sw16, group_w)
+        s = y.astype(np.float32)
+        out.append(s)
+    return np.stack(out)
+
+
 def looped_forward(xs, P1, P2, clips, bits: int, qw, sw16, group_w: int) -> np.ndarray:
     """The same quantized weights applied at every loop t with the loop's own
     LAS clip ``clips[t]`` (spec ``las``: one clip per module and loop).

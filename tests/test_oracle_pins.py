@@ -496,3 +496,38 @@ def test_per_token_equals_groups_when_group_maxima_agree_and_the_fold_form():
     yt, qt, st = oracle.linear_per_token(x, None, None, 0.9, 8, qw, sw, 128)
     folded = oracle.rescale_dots(np.repeat(st, K // 32, axis=1), oracle.group_dots(qt, qw), sw, 128)
     np.testing.assert_allclose(yt, folded, rtol=1e-12, atol=1e-9)
+
+
+def test_recurrent_adapter_with_a_scaled_identity_weight():
+    """W = [7 I | 0]: the weight group holding the diagonal has step
+    fl16(7/7) = 1 and code 7, every other group is zero, so the linear returns
+    7 times the dequantized state, and the
+    recurrence is s_{t+1} = 7 * s_t^ with s_t^ the Eq.(4) group RTN of s_t (the
+    e half meets zero weights).  Written out per element with plain numpy:
+    step per 32-group fl32(c * fl32(absmax / 7)), code rint(fl32(s / step))."""
+    M, N = 3, 64
+    s0 = synth.gaussian((M, N), 195)
+    e = synth.gaussian((M, N), 196, scale=5.0)
+    W = np.zeros((N, 2 * N), dtype=np.float32)
+    W[:, :N] = 7.0 * np.eye(N, dtype=np.float32)
+    qw, sw = oracle.quant_weights(W, 32)
+    want_sw = np.zeros((N, 2 * N // 32), dtype=np.float16)
+    want_sw[np.arange(N), np.arange(N) // 32] = 1.0   # the diagonal's group; all-zero groups have step 0
+    np.testing.assert_array_equal(sw, want_sw)
+    np.testing.assert_array_equal(qw[:, :N], 7 * np.eye(N))
+    clips = [1.0, 0.8, 0.9]
+    got = oracle.recurrent_adapter(s0, e, None, None, clips, 4, qw, sw, 32)
+    s = s0.astype(np.float32)
+    for t, c in enumerate(clips):
+        nxt = np.empty_like(s)
+        for m in range(M):
+            for g in range(N // 32):
+                blk = s[m, 32 * g:32 * g + 32]
+                step = np.float32(np.float32(c) * np.float32(np.float32(np.max(np.abs(blk))) / np.float32(7)))
+                q = np.clip(np.rint(np.float32(blk / step)), -7, 7)
+                nxt[m, 32 * g:32 * g + 32] = 7.0 * (q * np.float64(step))
+        s = nxt.astype(np.float32)
+        np.testing.assert_array_equal(got[t], s)
+    # T = 1 is one linear on cat(s_0, e)
+    y1, _, _ = oracle.linear(np.concatenate([s0, e], axis=1), None, None, 1.0, 4, qw, sw, 32)
+    np.testing.assert_array_equal(got[0], y1.astype(np.float32))
