@@ -513,6 +513,12 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       *bytes = act_bytes(1, rows, K, N, code_format(bits_a)) + align256((size_t)rows * K * 4);
       return LOOPQ_OK;
     }
+    case LOOPQ_OP_RECURRENT_ADAPTER:  // K = 2N is implied; the K argument is ignored
+      if (bits_a != 4 && bits_a != 8) return LOOPQ_ERR_UNSUPPORTED;
+      if (M < 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (N % 16) return LOOPQ_ERR_UNSUPPORTED;
+      *bytes = align256((size_t)M * 2 * N * 4) + act_bytes(1, M, 2 * (int64_t)N, N, code_format(bits_a));
+      return LOOPQ_OK;
     case LOOPQ_OP_HESSIAN:
       if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (K % 32 || K > kHessianMaxK || M > kHessianMaxRows) return LOOPQ_ERR_UNSUPPORTED;
@@ -880,6 +886,49 @@ int32_t loopq_looped_forward_per_token(const void* x, int32_t dtype, int32_t T, 
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   TimingScope ts(LOOPQ_KERNEL_GEMM, s);
   return hip_status(run_gemm(b, fmt, rows, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s));
+}
+
+int32_t loopq_recurrent_adapter(const float* s0, const float* e, int32_t T, int32_t M, int32_t N,
+                                const float* P1, int32_t n1, const float* P2, int32_t n2,
+                                const float* clips_host, int32_t bits_a, const void* w_codes,
+                                const void* w_scales, int32_t group_w, float* y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (T <= 0 || M < 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (T > LOOPQ_MAX_LOOPS || N % 16 || M > (1 << 30) / 2) return LOOPQ_ERR_UNSUPPORTED;
+  const int K = 2 * N;
+  int32_t st = check_act(s0, LOOPQ_F32, M, K, bits_a);
+  if (st != LOOPQ_OK) return st;
+  st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  st = check_gemm_extent(padded_rows(M), K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  st = check_transform(K, P1, n1, P2, n2);
+  if (st != LOOPQ_OK) return st;
+  if (!clips_host) return LOOPQ_ERR_INVALID_ARG;
+  for (int t = 0; t < T; ++t)
+    if (!clip_ok(clips_host[t])) return LOOPQ_ERR_INVALID_ARG;
+  if (M == 0) return LOOPQ_OK;
+  if (!e || !w_codes || !w_scales || !y) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(e, 16) || !aligned(y, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 16))
+    return LOOPQ_ERR_ALIGNMENT;
+  size_t need = 0;
+  loopq_workspace_bytes(LOOPQ_OP_RECURRENT_ADAPTER, T, M, K, N, bits_a, &need);
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  float* x = reinterpret_cast<float*>(workspace);
+  void* ws = reinterpret_cast<char*>(workspace) + align256((size_t)M * K * 4);
+  for (int t = 0; t < T; ++t) {
+    const float* state = t == 0 ? s0 : y + (size_t)(t - 1) * M * N;
+    if (launch_concat_state(state, e, x, M, N, s) != hipSuccess) return LOOPQ_ERR_HIP;
+    ClipTable clips;
+    memset(&clips, 0, sizeof(clips));
+    clips.c[0] = clips_host[t];
+    st = linear_core(x, LOOPQ_F32, M, K, N, P1, n1, P2, n2, clips, M, bits_a, w_codes, w_scales, group_w,
+                     y + (size_t)t * M * N, ws, 1, M, s);
+    if (st != LOOPQ_OK) return st;
+  }
+  return LOOPQ_OK;
 }
 
 int32_t loopq_hessian_accumulate(const float* xt, int32_t rows, int32_t K, float* H, void* workspace,

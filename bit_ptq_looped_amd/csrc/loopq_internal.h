@@ -201,6 +201,9 @@ constexpr int kHessianMaxRows = 1 << 30;
 size_t hessian_workspace_bytes(int K);
 hipError_t launch_hessian(const float* x, int rows, int K, float* H, float* part, hipStream_t s);
 
+// x [M][2N] = cat(s [M][N], e [M][N]) per row (fp32, N % 4 == 0, 16-byte aligned)
+hipError_t launch_concat_state(const float* s, const float* e, float* x, int M, int N, hipStream_t st);
+
 hipError_t reset_status(hipStream_t s);
 hipError_t read_status(int* host_status, hipStream_t s);
 

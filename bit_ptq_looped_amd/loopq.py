@@ -30,6 +30,7 @@ LOOPQ_F32, LOOPQ_BF16 = 0, 1
 LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
 LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD, LOOPQ_OP_LOOPED_FORWARD_EX = 1, 2, 3, 4
 LOOPQ_OP_HESSIAN, LOOPQ_OP_QUANT_PER_TOKEN, LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 5, 6, 7
+LOOPQ_OP_RECURRENT_ADAPTER = 8
 LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM, LOOPQ_KERNEL_DECODE = 0, 1, 2, 3
 LOOPQ_KERNEL_HESSIAN, LOOPQ_KERNEL_QUANT_TOKEN = 4, 5
 
@@ -53,6 +54,7 @@ SIGNATURES = {
     "loopq_export_weights": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "loopq_group_dots": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "loopq_hessian_accumulate": ([_P, _I, _I, _P, _P, _Z, _P], _I),
+    "loopq_recurrent_adapter": ([_P, _P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
     "loopq_quant_act_per_token": ([_P, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _P, _P, _Z, _P], _I),
     "loopq_looped_forward_per_token": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _P, _Z,
                                         _P], _I),
@@ -271,6 +273,20 @@ def loopq_looped_forward_per_token(x, P1, P2, clips: Sequence[float], bits_a: in
                                                  _ptr(w_scales), group_w, _ptr(y), _ptr(workspace),
                                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "loopq_looped_forward_per_token")
+
+
+def loopq_recurrent_adapter(s0, e, P1, P2, clips: Sequence[float], bits_a: int, w_codes, w_scales,
+                            group_w: int, y, workspace, stream=None):
+    """s0, e fp32 [M][N]; y fp32 [T][M][N] receives s_1 .. s_T."""
+    M, N = s0.shape
+    T = len(clips)
+    p1, n1, p2, n2 = _factor_args(P1, P2)
+    c = (ctypes.c_float * T)(*[float(v) for v in clips])
+    _check(load().loopq_recurrent_adapter(_ptr(s0), _ptr(e), T, M, N, p1, n1, p2, n2,
+                                          ctypes.cast(c, ctypes.c_void_p), bits_a, _ptr(w_codes), _ptr(w_scales),
+                                          group_w, _ptr(y), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream)),
+           "loopq_recurrent_adapter")
 
 
 def loopq_hessian_accumulate(xt, H, workspace=None, stream=None):

@@ -92,7 +92,8 @@ typedef enum {
   LOOPQ_OP_LOOPED_FORWARD_EX = 4, /* bits_a ignored: enough for 4- and 8-bit loops */
   LOOPQ_OP_HESSIAN = 5,           /* rows as M; T, N and bits_a ignored */
   LOOPQ_OP_QUANT_PER_TOKEN = 6,   /* M, K; T, N and bits_a ignored */
-  LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 7 /* T, M, K, N, bits_a */
+  LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 7, /* T, M, K, N, bits_a */
+  LOOPQ_OP_RECURRENT_ADAPTER = 8  /* M, N, bits_a (K = 2N implied); T and K ignored */
 } loopq_op;
 
 /* ABI version of the loaded library (LOOPQ_ABI_VERSION it was built with). */
@@ -249,6 +250,27 @@ int32_t loopq_looped_forward_ex(const void* x, int32_t dtype, int32_t T, int32_t
                                 const void* const* w_scales_sets_host, int32_t group_w,
                                 const int32_t* sets_host, const int32_t* bits_host,
                                 const float* clips_host, float* y, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* A dependent recurrence through one quantized linear (the adapter loop).
+ * Page: "Quantizing Looped Transformers: Feedback Exposure and Calibration
+ * Blindness", Figure 4 (the Huginn recurrence loop): the adapter maps
+ * cat(s_t, e) back to the model width with no residual path.  With the
+ * recurrent blocks between two adapter calls left out, loop t computes
+ * s_{t+1} = y_t = the quantized linear (loopq_w4a4_linear, clip clips_host[t])
+ * of x_t = cat(s_t, e), so every loop's input is the previous loop's output.
+ * s0, e [M][N] fp32 (16-byte aligned), N % 16 == 0; the weight is [N][2N]
+ * (K = 2N), packed by loopq_pack_weights; y [T][M][N] fp32 receives
+ * s_1 .. s_T (loop t + 1 reads y[t] after loop t wrote it, in stream order).
+ * Each loop is one call of the single-linear path (the few-row kernel up to
+ * 16 rows, else quantizer and GEMM) after a device-side concatenation; no
+ * host synchronization between loops, so the sequence can be captured into a
+ * HIP graph.  Workspace: loopq_workspace_bytes(LOOPQ_OP_RECURRENT_ADAPTER, 0,
+ * M, 0, N, bits_a, ...).  Errors as loopq_looped_forward. */
+int32_t loopq_recurrent_adapter(const float* s0, const float* e, int32_t T, int32_t M, int32_t N,
+                                const float* P1, int32_t n1, const float* P2, int32_t n2,
+                                const float* clips_host, int32_t bits_a, const void* w_codes,
+                                const void* w_scales, int32_t group_w, float* y, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
 /* a5 alone -- the GEMM on activation codes and steps already formed.

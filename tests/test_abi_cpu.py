@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
         assert n in loopq.SIGNATURES, n
@@ -225,3 +225,28 @@ def test_per_token_entries_reject_on_host(lib):
     assert lp(2, [1.0, float("nan")]) == loopq.LOOPQ_ERR_INVALID_ARG
     assert lp(0, [1.0]) == loopq.LOOPQ_ERR_INVALID_ARG
     assert lp(65, [1.0] * 65) == loopq.LOOPQ_ERR_UNSUPPORTED
+
+
+def test_recurrent_adapter_rejects_on_host(lib):
+    op = loopq.LOOPQ_OP_RECURRENT_ADAPTER
+    # x = cat(s, e) staging plus the linear's buffers for K = 2N
+    assert loopq.loopq_workspace_bytes(op, 0, 16, 0, 5280, 8) == \
+        16 * 10560 * 4 + loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LINEAR, 1, 16, 10560, 5280, 8)
+    with pytest.raises(loopq.LoopQError) as e:
+        loopq.loopq_workspace_bytes(op, 0, 16, 0, 72, 8)     # N % 16
+    assert e.value.status == loopq.LOOPQ_ERR_UNSUPPORTED
+    arr = lambda vals: ctypes.cast((ctypes.c_float * len(vals))(*vals), ctypes.c_void_p)
+    def call(T=2, M=4, N=64, clips=(1.0, 0.9), gw=32, ws=1 << 30, e=FAKE, s0=FAKE, bits=4):
+        return _raw(lib, "loopq_recurrent_adapter", s0, e, T, M, N, None, 0, None, 0, arr(list(clips)), bits, FAKE,
+                    FAKE, gw, FAKE, FAKE, ws, None)
+    assert call(N=72) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert call(T=0, clips=(1.0,)) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call(T=65, clips=(1.0,) * 65) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert call(clips=(1.0, -1.0)) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call(gw=64) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert call(bits=6) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert call(e=None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert call(e=FAKE + 8) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert call(s0=FAKE + 4) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert call(ws=16) == loopq.LOOPQ_ERR_WORKSPACE
+    assert call(M=0, e=None, s0=None) == loopq.LOOPQ_OK
