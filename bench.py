@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--no-loop-dependent", action="store_true",
                    help="skip the loop-dependent (per-loop weight sets / bit widths) measurement")
     p.add_argument("--no-hessian", action="store_true", help="skip the trajectory Hessian measurement")
+    p.add_argument("--no-recurrence", action="store_true", help="skip the adapter recurrence measurement")
     p.add_argument("--profile-hessian", type=int, default=0,
                    help="only run this many trajectory Hessian steps (for a profiler) and exit")
     p.add_argument("--decode-steps", type=int, default=20)
@@ -402,6 +403,42 @@ def per_token_bench(lq, torch, mods, T, M, steps, warmup):
             "ms_per_step": dt * 1e3, "value": alg_ops(mods, T, M) / dt / 1e12, "unit": "TOPS"}
 
 
+def recurrence_bench(lq, synth, torch, M, T, steps):
+    """The Huginn-like adapter loop (adapter 10560 -> 5280, weight groups of
+    128, A8, no transform): T dependent loops s_{t+1} = adapter(cat(s_t, e))
+    in one loopq_recurrent_adapter call.  The weight is drawn N(0, (0.5 /
+    sqrt(K))^2) so the state keeps its scale over 32 loops (timing does not
+    depend on the values).  Per loop: 2 M N K ops; bytes = packed weight and
+    steps + the fp32 x read + the fp32 y written."""
+    import numpy as np
+    N, K, gw, bits = 5280, 10560, 128, 8
+    rng = synth.seeded_rng(synth.HUGINN, synth.T_W, 99)
+    w = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.5 / np.sqrt(K)))
+    codes, scales = lq.empty_packed_weights(K, N, gw)
+    lq.loopq_pack_weights(torch.from_numpy(w).cuda(), gw, codes, scales)
+    del w
+    s0 = torch.from_numpy(synth.seeded_rng(synth.HUGINN, synth.T_X, 99).standard_normal((M, N), dtype=np.float32)).cuda()
+    e = torch.from_numpy(synth.seeded_rng(synth.HUGINN, synth.T_AUX, 99).standard_normal((M, N), dtype=np.float32)).cuda()
+    y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lq.loopq_workspace_bytes(lq.LOOPQ_OP_RECURRENT_ADAPTER, 0, M, 0, N, bits), dtype=torch.uint8,
+                     device="cuda")
+    clips = [1.0] * T
+    lq.loopq_recurrent_adapter(s0, e, None, None, clips, bits, codes, scales, gw, y, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lq.loopq_recurrent_adapter(s0, e, None, None, clips, bits, codes, scales, gw, y, ws)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps / T
+    wbytes = codes.numel() + scales.numel()
+    loop_bytes = wbytes + 4.0 * M * K + 4.0 * M * N
+    finite = bool(torch.isfinite(y).all().item())
+    return {"M": M, "T": T, "N": N, "K": K, "group_w": gw, "bits": "W4A8", "ms_per_loop": dt * 1e3,
+            "tops": 2.0 * M * N * K / dt / 1e12, "gbps": loop_bytes / dt / 1e9,
+            "frac_hbm_peak": loop_bytes / dt / 1e9 / HBM_PEAK_GBS, "weight_bytes": wbytes,
+            "states_finite": finite}
+
+
 def hessian_setup(lq, torch, mods, T, M):
     """x~ of every loop of each quantized input (the quantizer's dump, formed
     once, untimed), a zeroed fp32 [K][K] Hessian and the workspace per input."""
@@ -634,6 +671,9 @@ def main():
     out["per_token"] = per_token_bench(lq, torch, mods, T, M, max(5, args.steps // 2), 2)
     if not args.no_hessian:
         out["trajectory_hessian"] = hessian_bench(lq, torch, mods, T, M, max(5, args.steps // 5), 2)
+    if not args.no_recurrence:
+        out["recurrence"] = [recurrence_bench(lq, synth, torch, 1, 32, 20),
+                             recurrence_bench(lq, synth, torch, 2048, 32, 2)]
     if not args.no_decode:
         del mods
         torch.cuda.empty_cache()
