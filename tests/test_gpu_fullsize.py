@@ -202,3 +202,116 @@ def test_fullsize_decode(lq, act, M):
         err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
         say(f"  schedule {schedule}: rel err {err:.3e}")
         assert err <= Y_TOL
+
+
+# ---------------------------------------------------------------------------
+# the NEXT rows at the bench's sizes
+# ---------------------------------------------------------------------------
+
+def sample_pairs(K, n, key):
+    """n (i, j) pairs of H: the corners and diagonal, tile edges, and seeded
+    random pairs (both triangles)."""
+    rng = synth.seeded_rng(synth.TEST, 220, K, key)
+    fixed = [(0, 0), (K - 1, K - 1), (0, K - 1), (K - 1, 0), (127, 128), (128, 127), (K // 2, K // 2 + 1)]
+    return fixed + [tuple(int(v) for v in rng.integers(0, K, size=2)) for _ in range(n)]
+
+
+@pytest.mark.parametrize("act", ["qkv_in", "down_in"])
+def test_fullsize_trajectory_hessian(lq, act):
+    """The bench's trajectory Hessian: the x~ of all T*M = 4096 rows of one
+    block input (the quantizer's dump) accumulated in one call; sampled
+    elements against the fp64 sum over the rows, computed one by one, within
+    the fp32 accumulation bound (rows + 1) u (|x|^T |x|)_ij; exact symmetry."""
+    wl = synth.ouro_block_workload()
+    K = groups_by_input(wl)[act][0].K
+    P1, P2 = synth.factors_for(wl, act, K)
+    bits, x32 = synth.activations_for(wl, act, K)
+    rows = wl.T * wl.M
+    say(f"hessian {act} rows={rows} K={K}")
+    xdev = bf16_dev(bits.reshape(rows, K))
+    codes = torch.empty((rows, K), dtype=torch.int8, device="cuda")
+    steps = torch.empty((rows, K // 32), dtype=torch.float32, device="cuda")
+    xt = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+    lq.loopq_quant_act(xdev, dev(P1), dev(P2), 1.0, 4, codes, steps, xt)
+    H = torch.zeros((K, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lq.loopq_workspace_bytes(lq.LOOPQ_OP_HESSIAN, 0, rows, K, 0, 0), dtype=torch.uint8,
+                     device="cuda")
+    lq.loopq_hessian_accumulate(xt, H, ws)
+    torch.cuda.synchronize()
+    X = xt.cpu().numpy().astype(np.float64)
+    check_xt(X[sample_rows(rows)].astype(np.float32), x32.reshape(rows, K)[sample_rows(rows)], P1, P2)
+    Hc = H.cpu().numpy()
+    assert np.array_equal(Hc, Hc.T)
+    u = 2.0 ** -24
+    worst = 0.0
+    for i, j in sample_pairs(K, 400, 1):
+        want = float(X[:, i] @ X[:, j])
+        mag = float(np.abs(X[:, i]) @ np.abs(X[:, j]))
+        bound = (rows + 1) * u / (1 - (rows + 1) * u) * mag
+        err = abs(float(Hc[i, j]) - want)
+        assert err <= bound, (i, j, err, bound)
+        worst = max(worst, err / max(bound, 1e-300))
+    say(f"  max error / bound {worst:.3g}")
+
+
+def test_fullsize_per_token_loop(lq):
+    """The bench's per-token step for the up input (K = 2048, N = 5632, T = 4,
+    M = 1024) in one loopq_looped_forward_per_token call; sampled (loop, row)
+    pairs against the oracle's per-token linear on the kernel's x~."""
+    wl = synth.ouro_block_workload()
+    act = "up_in"
+    lins = groups_by_input(wl)[act]
+    K, N = lins[0].K, sum(l.N for l in lins)
+    T, M = wl.T, wl.M
+    P1, P2 = synth.factors_for(wl, act, K)
+    bits, x32 = synth.activations_for(wl, act, K)
+    clips = [float(c) for c in synth.clips_for(wl, act)]
+    W = np.concatenate([synth.weights_for(wl, l) for l in lins], axis=0)
+    codes, scales = lq.empty_packed_weights(K, N, wl.group_w)
+    lq.loopq_pack_weights(dev(W), wl.group_w, codes, scales)
+    xdev = bf16_dev(bits)
+    y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lq.loopq_workspace_bytes(lq.LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN, T, M, K, N, 4),
+                     dtype=torch.uint8, device="cuda")
+    say(f"per-token loop {act} T={T} M={M} K={K} N={N}")
+    lq.loopq_looped_forward_per_token(xdev, dev(P1), dev(P2), clips, 4, codes, scales, wl.group_w, N, y, ws)
+    torch.cuda.synchronize()
+    qw, sw = oracle.quant_weights(W, wl.group_w)
+    got = y.cpu().numpy()
+    rows = sample_rows(M)
+    for t in sample_loops(T):
+        xt = gpu_xt(lq, bf16_dev(bits[t][rows]), x32[t][rows], P1, P2)
+        ref, _, _ = oracle.linear_per_token(xt, None, None, clips[t], 4, qw, sw, wl.group_w)
+        err = float(np.max(np.abs(got[t][rows] - ref)) / np.max(np.abs(ref)))
+        say(f"  loop {t}: rel err {err:.2e}")
+        assert err <= Y_TOL
+
+
+def test_fullsize_adapter_recurrence_decode(lq):
+    """The bench's Huginn-like adapter loop at M = 1: adapter 10560 -> 5280,
+    weight groups of 128, A8, T = 32 dependent loops in one call; every loop
+    against the oracle's linear on cat(s_t, e) with the GPU's own state."""
+    N, K, gw, T = 5280, 10560, 128, 32
+    rng = synth.seeded_rng(synth.HUGINN, synth.T_W, 99)
+    w = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.5 / np.sqrt(K))
+    s0 = synth.seeded_rng(synth.HUGINN, synth.T_X, 99).standard_normal((1, N), dtype=np.float32)
+    e = synth.seeded_rng(synth.HUGINN, synth.T_AUX, 99).standard_normal((1, N), dtype=np.float32)
+    codes, scales = lq.empty_packed_weights(K, N, gw)
+    lq.loopq_pack_weights(dev(w), gw, codes, scales)
+    y = torch.empty((T, 1, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lq.loopq_workspace_bytes(lq.LOOPQ_OP_RECURRENT_ADAPTER, 0, 1, 0, N, 8), dtype=torch.uint8,
+                     device="cuda")
+    say(f"adapter recurrence M=1 T={T} N={N} K={K}")
+    lq.loopq_recurrent_adapter(dev(s0), dev(e), None, None, [1.0] * T, 8, codes, scales, gw, y, ws)
+    torch.cuda.synchronize()
+    qw, sw = oracle.quant_weights(w, gw)
+    got = y.cpu().numpy()
+    worst = 0.0
+    for t in range(T):
+        state = s0 if t == 0 else got[t - 1]
+        x = np.concatenate([state, e], axis=1).astype(np.float32)
+        ref, _, _ = oracle.linear(x, None, None, 1.0, 8, qw, sw, gw)
+        err = float(np.max(np.abs(got[t] - ref)) / np.max(np.abs(ref)))
+        worst = max(worst, err)
+        assert err <= Y_TOL, (t, err)
+    say(f"  worst loop rel err {worst:.2e}, final max|s| {np.max(np.abs(got[-1])):.3g}")
