@@ -533,18 +533,41 @@ def cpu_baseline(wl, mods_meta, rows_hint):
         clip = float(synth.clips_for(wl, act)[0])
         prepared.append((x32[0], P1, P2, clip, qw, sw))
     import contextlib
-    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
-    with ctx:
-        t0 = time.perf_counter()
-        for x, P1, P2, clip, qw, sw in prepared:
-            oracle.linear(x, P1, P2, clip, wl.bits_a, qw, sw, wl.group_w)
-        dt = time.perf_counter() - t0
+    import os as _os
+    import platform
+
+    def timed_run(threads):
+        ctx = threadpool_limits(limits=threads) if threadpool_limits else contextlib.nullcontext()
+        with ctx:
+            t0 = time.perf_counter()
+            for x, P1, P2, clip, qw, sw in prepared:
+                oracle.linear(x, P1, P2, clip, wl.bits_a, qw, sw, wl.group_w)
+            return time.perf_counter() - t0
+
     ops = sum(2.0 * rows * x.shape[1] * qw.shape[0] for x, _, _, _, qw, _ in prepared)
+    dt = timed_run(1)
+    ncpu = len(_os.sched_getaffinity(0)) if hasattr(_os, "sched_getaffinity") else (_os.cpu_count() or 1)
+    dt_all = timed_run(ncpu)
+    cpu = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = ""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()}))
+    except Exception:  # pragma: no cover
+        pass
+    sample = (f"{rows} token rows of loop 0 of each quantized input (qkv, o, up, down) at full K and N; "
+              f"weight quantization and input drawing not timed; host {cpu}, numpy {np.__version__}, BLAS {blas}")
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} token rows of loop 0 of each quantized input (qkv, o, up, down) at full "
-                      f"K and N; {dt:.1f} s on the host, BLAS limited to 1 thread; weight "
-                      f"quantization and input drawing not timed",
-            "seconds": dt}
+            "sample": f"{sample}; {dt:.1f} s with BLAS limited to 1 thread", "seconds": dt,
+            "all_cores": {"value": ops / dt_all / 1e12, "unit": "TOPS", "cores": ncpu, "kind": "oracle",
+                          "sample": f"the same sample, BLAS on {ncpu} threads: {dt_all:.1f} s", "seconds": dt_all}}
 
 
 def calibration_copy(args, torch):
@@ -685,6 +708,7 @@ def main():
         meta = [(act, lins[0].K, lins) for act, lins in groups.items()]
         cb = cpu_baseline(wl, meta, args.cpu_rows)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        out["cpu_baseline_all_cores"] = {k: cb["all_cores"][k] for k in ("value", "unit", "cores", "kind", "sample")}
     print(json.dumps(out), flush=True)
 
 
