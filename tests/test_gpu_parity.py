@@ -355,11 +355,10 @@ def test_decode_shapes(lq, act, K, N, M, bits, schedule):
 
 
 def test_decode_graph_replays_match_eager(lq):
-    """The fused few-row kernel keeps its synchronization words in static
-    device memory and clears them at the end of every launch, so calls can be
-    captured into a graph: every replay (with eager work between replays)
-    equals the eager result bit for bit, and the eager result equals the
-    oracle on the kernel's x~."""
+    """The few-row kernel keeps no state between launches (no work-group waits
+    for another), so calls can be captured into a graph: every replay (with
+    eager work between replays) equals the eager result bit for bit, and the
+    eager result equals the oracle on the kernel's x~."""
     K, N, M, T = 2048, 200, 1, 4
     wl = synth.ouro_block_workload(bits_a=4, M=M, T=T)
     P1, P2 = synth.factors_for(wl, "up_in", K)
