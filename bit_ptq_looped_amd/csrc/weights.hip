@@ -1,8 +1,8 @@
 // Offline weight-side kernels: transform fold (fp64), INT4 packing, export.
 //
 // Fold: "paper_specification.yaml", loopq_components.shared_transformed_backbone
-// and implementation_status lq3 (exact no-quant inverse-transpose weight
-// folding).  Row n of the [N][K] weight storage is output column n, and
+// and implementation_status lq3 (the weights absorb the exact inverse
+// transpose of the transform, before any quantization).  Row n of the [N][K] weight storage is output column n, and
 //   w~[n] = vec_r(P1^-1 * reshape(w[n], n1, n2) * P2^-T),
 // accumulated in fp64 and rounded once to fp32.  The factors are inverted on
 // the GPU by Gauss-Jordan elimination with partial pivoting in fp64.

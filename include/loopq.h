@@ -11,8 +11,8 @@
  *     invertible transform folded into the activation and weight sides; LAS
  *     replaces the shared activation clip with one clip per module and loop.
  *   - implementation_status lq2 (clips multiply dynamic token/group absmax
- *     steps) and lq3 (a shared Kronecker transform, exact no-quant
- *     inverse-transpose weight folding).
+ *     steps) and lq3 (one Kronecker transform shared by all loops, folded
+ *     into the weights through its exact inverse transpose, unquantized).
  *   - "LoopQ 4-bit quantization of Ouro-1.4B -- raw artifacts", "The arms":
  *     random orthogonal Kronecker transforms; Ouro-1.4B runs 24 layers 4 times
  *     per token with the same weights.
@@ -116,8 +116,8 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
 
 /* a0 -- fold the transform into the weights (offline).
  * Page: paper_specification.yaml, loopq_components.shared_transformed_backbone
- * and implementation_status lq3 ("exact no-quant inverse-transpose weight
- * folding").  w [N][K] fp32 holds one output column per row; for each row
+ * and implementation_status lq3 (the weights absorb the exact inverse
+ * transpose of the transform, before any quantization).  w [N][K] fp32 holds one output column per row; for each row
  * w_folded[n] = vec_r(P1^-1 * reshape(w[n], n1, n2) * P2^-T), computed in
  * fp64 with the factors inverted on the GPU (Gauss-Jordan, partial pivoting)
  * and rounded once to fp32.  P1 is n1 x n1 and P2 is n2 x n2 fp32, n1*n2 = K,
@@ -167,7 +167,7 @@ int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, in
 
 /* Per-token activation steps: the same RTN with one step per token.
  * Page: "LoopQ 4-bit quantization of Ouro-1.4B -- raw artifacts", "The arms"
- * (rtn_w4a4_per_token, the field-standard W4A4 baseline setting).  Eq.(4)
+ * (rtn_w4a4_per_token: plain RTN, one step per token, a common W4A4 reference).  Eq.(4)
  * over the whole row of x~ (x with no transform): for row m,
  * s = fl32(clip * fl32(absmax_m / qmax)), codes[m][k] = clamp(rint(fl32(x~ / s)),
  * -qmax, qmax) (0 when s == 0), with the arithmetic of loopq_quant_act.
@@ -254,8 +254,9 @@ int32_t loopq_looped_forward_ex(const void* x, int32_t dtype, int32_t T, int32_t
 
 /* A dependent recurrence through one quantized linear (the adapter loop).
  * Page: "Quantizing Looped Transformers: Feedback Exposure and Calibration
- * Blindness", Figure 4 (the Huginn recurrence loop): the adapter maps
- * cat(s_t, e) back to the model width with no residual path.  With the
+ * Blindness", Figure 4 (the Huginn recurrence loop): the adapter reads the
+ * state concatenated with the embedding, cat(s_t, e), and its output enters the
+ * recurrence directly, with no skip connection around it.  With the
  * recurrent blocks between two adapter calls left out, loop t computes
  * s_{t+1} = y_t = the quantized linear (loopq_w4a4_linear, clip clips_host[t])
  * of x_t = cat(s_t, e), so every loop's input is the previous loop's output.

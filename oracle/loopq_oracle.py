@@ -20,7 +20,8 @@ the pages the method is described on):
   backbone with an invertible transform folded into both sides; LAS: one
   clipping scalar per module and loop), ``implementation_status`` lq2 (clips
   multiply dynamic token/group absmax scales) and lq3 (shared Kronecker
-  transform, exact no-quant inverse-transpose weight folding), and the list of
+  transform folded into the weights by its exact inverse transpose before
+  quantization), and the list of
   ``paper_underspecified_items``.
 * "Quantizing Looped Transformers: Feedback Exposure and Calibration
   Blindness": Figure 3 and Tables 2 and 6 -- grouped INT4 weights with g=128.
@@ -73,8 +74,8 @@ def _group_bounds(K: int, g: int):
 
 # --------------------------------------------------------------------------
 # a0 -- transform and weight fold (spec: "shared_transformed_backbone";
-#        implementation_status lq3: Kronecker transform, exact no-quant
-#        inverse-transpose weight folding)
+#        implementation_status lq3: a Kronecker transform whose exact
+#        inverse transpose is folded into the unquantized weights)
 # --------------------------------------------------------------------------
 
 def kron_transform(x: np.ndarray, P1: np.ndarray, P2: np.ndarray) -> np.ndarray:
@@ -290,11 +291,12 @@ def linear_per_token(x, P1, P2, clip: float, bits: int, qw, sw16, group_w: int):
 
 
 def recurrent_adapter(s0, e, P1, P2, clips, bits: int, qw, sw16, group_w: int) -> np.ndarray:
-    """A dependent recurrence through one quantized linear: the adapter of a
-    depth-recurrent model maps ``cat(s_t, e)`` back to the model width with no
-    residual path ("Quantizing Looped Transformers", Figure 4, the Huginn
-    recurrence loop), here with the recurrent blocks between two adapter calls
-    left out: ``s_{t+1} = fl32(linear(cat(s_t, e)))`` with loop t's clip.
+    """A dependent recurrence through one quantized linear.  In the Huginn
+    recurrence loop ("Quantizing Looped Transformers", Figure 4) the adapter
+    reads the state concatenated with the embedding, ``cat(s_t, e)``, and its
+    output feeds the recurrence directly, with no skip connection around it.
+    Leaving out the recurrent blocks between two adapter calls gives
+    ``s_{t+1} = fl32(linear(cat(s_t, e)))`` with loop t's clip.
     ``s0`` and ``e`` are ``[M][N]``, the weight ``[N][2N]``; returns the states
     ``s_1 .. s_T`` as fp32 ``[T][M][N]`` (the state is kept in fp32 between
     loops, as a device would store it)."""
