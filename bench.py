@@ -371,7 +371,8 @@ def loop_dependent_bench(lq, synth, torch, wl, mods, steps, warmup):
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / steps
         out[kind] = {"ms_per_step": dt * 1e3, "value": ops / dt / 1e12}
-    out["slt"]["what"] = "every loop with its own packed weights and factors (no sharing): T launches per input"
+    out["slt"]["what"] = ("every loop with its own packed weights and factors (no sharing): per input, one "
+                          "quantizer launch per loop and one grouped GEMM over all T*M rows")
     out["bits_8444"]["what"] = "loop 0 at A8, loops 1-3 at A4, shared weights: two weight-stationary runs per input"
     return out
 

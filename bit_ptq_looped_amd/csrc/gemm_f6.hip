@@ -77,6 +77,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
 
   // buffer loads: wave-uniform resource per tile, fixed per-lane offset, the
   // pair offset as scalar offset (tiles past the edge re-read the last block)
+  const void* wp;
+  const __half* swp;
+  tile_weights(g, m_base, &wp, &swp);  // the grouped form's weight set of these rows
   __amdgpu_buffer_rsrc_t x_rs[2], w_rs[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -84,13 +87,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
     const int nb = min((n_base >> 5) + t, nlast);
     x_rs[t] = make_rsrc(reinterpret_cast<const char*>(g.a) + (int64_t)mb * Gp * kF6BlockBytes,
                         (uint32_t)Gp * kF6BlockBytes);
-    w_rs[t] = make_rsrc(reinterpret_cast<const char*>(g.w) + (int64_t)nb * Gp * kF6BlockBytes,
+    w_rs[t] = make_rsrc(reinterpret_cast<const char*>(wp) + (int64_t)nb * Gp * kF6BlockBytes,
                         (uint32_t)Gp * kF6BlockBytes);
   }
   const int op_off = lane * 24;
   // step resources exist only in the rescale mode (the dots mode passes null)
   const __amdgpu_buffer_rsrc_t sa_rs = make_rsrc(g.sa, MODE == 0 ? (uint32_t)g.ld_sa * (uint32_t)Ga * 4u : 0u);
-  const __amdgpu_buffer_rsrc_t sw_rs = make_rsrc(g.sw, MODE == 0 ? (uint32_t)(nlast + 1) * (uint32_t)Gw * 64u : 0u);
+  const __amdgpu_buffer_rsrc_t sw_rs = make_rsrc(swp, MODE == 0 ? (uint32_t)(nlast + 1) * (uint32_t)Gw * 64u : 0u);
   const int sa_off0 = (min((m_base >> 5) + h, mlast) * 32 + c) * 4;
   const int sa_off1 = (min((m_base >> 5) + 1 - h, mlast) * 32 + c) * 4;
   const int sw_off = (min((n_base >> 5) + h, nlast) * Gw * 32 + step_slot(coef_row(c))) * 2;
@@ -265,9 +268,19 @@ hipError_t launch_expand_weights_f6(const uint8_t* w_codes, int K, int N, void* 
 
 hipError_t launch_gemm_f6(const void* a_tiled, const float* a_scales_gm, int ld_sa, int M, int K,
                           int N, const void* w_f6, const __half* w_scales, int gw, float* y,
-                          int32_t* dots, int mode, hipStream_t s) {
+                          int32_t* dots, int mode, hipStream_t s, const GemmSets* sets) {
   if (M <= 0) return hipSuccess;
-  GemmArgs g;
+  GemmArgs g{};
+  if (sets && sets->rows_per_set > 0) {
+    if (sets->rows_per_set % 64 || sets->n < 1 || sets->n > kGemmMaxSets ||
+        (int64_t)sets->n * sets->rows_per_set != M)
+      return hipErrorInvalidValue;
+    g.rows_per_set = sets->rows_per_set;
+    for (int i = 0; i < sets->n; ++i) {
+      g.w_set[i] = sets->w[i];
+      g.sw_set[i] = sets->sw[i];
+    }
+  }
   g.a = a_tiled;
   g.sa = a_scales_gm;
   g.ld_sa = ld_sa;

@@ -15,6 +15,8 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 
+constexpr int kGemmMaxSets = 64;
+
 struct GemmArgs {
   const void* a;     // tiled activation codes (int8 or fp6 layout)
   const float* sa;   // group-major activation steps [Ga][ld_sa]
@@ -25,7 +27,24 @@ struct GemmArgs {
   int gshift;        // log2(group_w / 32)
   float* y;          // [M][N]
   int32_t* dots;     // [M][N][Ga] (mode 1)
+  // grouped form: with rows_per_set > 0 (a multiple of 64), rows
+  // [s * rows_per_set, (s + 1) * rows_per_set) take weights w_set[s], sw_set[s]
+  int rows_per_set;
+  const void* w_set[kGemmMaxSets];
+  const __half* sw_set[kGemmMaxSets];
 };
+
+// The weights of the wave whose 64 rows start at m_base (wave-uniform).
+__device__ __forceinline__ void tile_weights(const GemmArgs& g, int m_base, const void** w, const __half** sw) {
+  if (g.rows_per_set > 0) {
+    const int set = m_base / g.rows_per_set;
+    *w = g.w_set[set];
+    *sw = g.sw_set[set];
+  } else {
+    *w = g.w;
+    *sw = g.sw;
+  }
+}
 
 // raw buffer resource over [p, p + bytes): stride 0, gfx9 data format word;
 // loads at or past `bytes` return 0

@@ -67,13 +67,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   // offset as the scalar offset, so the K loop does no vector address
   // arithmetic.  Tiles past the matrix edge re-read the last valid block
   // (always in bounds); their results are dropped at the store.
+  const void* wp;
+  const __half* swp;
+  tile_weights(g, m_base, &wp, &swp);  // the grouped form's weight set of these rows
   __amdgpu_buffer_rsrc_t x_rs[2], w_rs[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int mb = min((m_base >> 5) + t, mlast);
     const int nb = min((n_base >> 5) + t, nlast);
     x_rs[t] = make_rsrc(reinterpret_cast<const char*>(g.a) + (int64_t)mb * Ga * 1024, (uint32_t)Ga * 1024u);
-    w_rs[t] = make_rsrc(reinterpret_cast<const uint8_t*>(g.w) + (int64_t)nb * Ga * kBlockBytes,
+    w_rs[t] = make_rsrc(reinterpret_cast<const uint8_t*>(wp) + (int64_t)nb * Ga * kBlockBytes,
                         (uint32_t)Ga * kBlockBytes);
   }
   const int x_off = lane * 16;
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   // column l % 32 of column tile h, and the activation steps of row l % 32 of
   // row tiles h and 1 - h
   const __amdgpu_buffer_rsrc_t sa_rs = make_rsrc(g.sa, (uint32_t)g.ld_sa * (uint32_t)Ga * 4u);
-  const __amdgpu_buffer_rsrc_t sw_rs = make_rsrc(g.sw, (uint32_t)(nlast + 1) * (uint32_t)Gw * 64u);
+  const __amdgpu_buffer_rsrc_t sw_rs = make_rsrc(swp, (uint32_t)(nlast + 1) * (uint32_t)Gw * 64u);
   const int sa_off0 = (min((m_base >> 5) + h, mlast) * 32 + c) * 4;
   const int sa_off1 = (min((m_base >> 5) + 1 - h, mlast) * 32 + c) * 4;
   const int sw_off = (min((n_base >> 5) + h, nlast) * Gw * 32 + step_slot(c)) * 2;
@@ -214,9 +217,19 @@ __global__ __launch_bounds__(256) void tile_codes_kernel(const int8_t* __restric
 
 hipError_t launch_gemm(const int8_t* a_tiled, const float* a_scales_gm, int ld_sa, int M, int K,
                        int N, const uint8_t* w_codes, const __half* w_scales, int gw, float* y,
-                       int32_t* dots, int mode, hipStream_t s) {
+                       int32_t* dots, int mode, hipStream_t s, const GemmSets* sets) {
   if (M <= 0) return hipSuccess;
-  GemmArgs g;
+  GemmArgs g{};
+  if (sets && sets->rows_per_set > 0) {
+    if (sets->rows_per_set % 64 || sets->n < 1 || sets->n > kGemmMaxSets ||
+        (int64_t)sets->n * sets->rows_per_set != M)
+      return hipErrorInvalidValue;
+    g.rows_per_set = sets->rows_per_set;
+    for (int i = 0; i < sets->n; ++i) {
+      g.w_set[i] = sets->w[i];
+      g.sw_set[i] = sets->sw[i];
+    }
+  }
   g.a = a_tiled;
   g.sa = a_scales_gm;
   g.ld_sa = ld_sa;

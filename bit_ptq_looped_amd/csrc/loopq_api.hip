@@ -161,12 +161,13 @@ hipError_t prepare_weights(const ActBuffers& b, int fmt, const void* w_codes, in
 
 // GEMM stage on codes already in the internal layout `fmt`
 hipError_t run_gemm(const ActBuffers& b, int fmt, int rows, int K, int N, const void* w_codes,
-                    const void* w_scales, int gw, float* y, int32_t* dots, int mode, hipStream_t s) {
+                    const void* w_scales, int gw, float* y, int32_t* dots, int mode, hipStream_t s,
+                    const GemmSets* sets = nullptr) {
   const __half* wsc = reinterpret_cast<const __half*>(w_scales);
   if (fmt == kCodesTiledF6)
-    return launch_gemm_f6(b.codes, b.scales, b.ld, rows, K, N, b.wexp, wsc, gw, y, dots, mode, s);
+    return launch_gemm_f6(b.codes, b.scales, b.ld, rows, K, N, b.wexp, wsc, gw, y, dots, mode, s, sets);
   return launch_gemm(reinterpret_cast<const int8_t*>(b.codes), b.scales, b.ld, rows, K, N,
-                     reinterpret_cast<const uint8_t*>(w_codes), wsc, gw, y, dots, mode, s);
+                     reinterpret_cast<const uint8_t*>(w_codes), wsc, gw, y, dots, mode, s, sets);
 }
 
 // ---------------------------------------------------------------------------
@@ -421,6 +422,73 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
   return LOOPQ_OK;
 }
 
+// Loop-dependent weight sets in one grouped GEMM (all loops at one bit width,
+// M % 64 == 0): each maximal run of loops with one set is quantized with that
+// set's transform into rows [t0 * M, t1 * M) of one activation buffer, every
+// set in use has its W4A4 operands expanded once, and a single GEMM over all
+// T * M rows takes loop t's weights for loop t's rows.  The workspace holds
+// the activation buffers of T * M rows and one expansion region per set used.
+hipError_t looped_grouped(const void* x, int dtype, int T, int M, int K, int N, const float* const* P1_sets,
+                          int n1, const float* const* P2_sets, int n2, const void* const* w_codes_sets,
+                          const void* const* w_scales_sets, int gw, const int32_t* sets, int bits_a,
+                          const float* clips_host, float* y, void* ws, hipStream_t s) {
+  const int fmt = code_format(bits_a);
+  const int rows = T * M;
+  const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
+  ActBuffers b = carve(ws, T, M, K, N, 0, rows);
+  const int64_t block_bytes = fmt == kCodesTiledF6 ? group_pairs(K) * kF6BlockBytes : (int64_t)(K / 32) * 1024;
+  hipError_t e = hipSuccess;
+  for (int t0 = 0; t0 < T;) {
+    int t1 = t0 + 1;
+    while (t1 < T && sets[t1] == sets[t0]) ++t1;
+    const int set = sets[t0];
+    ClipTable ct;
+    memset(&ct, 0, sizeof(ct));
+    for (int t = t0; t < t1; ++t) ct.c[t - t0] = clips_host[t];
+    QuantArgs a = internal_quant_args(reinterpret_cast<const char*>(x) + (size_t)t0 * M * K * esz, dtype,
+                                      (t1 - t0) * M, K, P1_sets ? P1_sets[set] : nullptr, n1,
+                                      P2_sets ? P2_sets[set] : nullptr, n2, ct, M, bits_a, b);
+    // rows t0 * M.. of the tiled codes (32-row blocks) and of the group-major steps
+    a.codes = reinterpret_cast<int8_t*>(b.codes) + (int64_t)t0 * M / 32 * block_bytes;
+    a.scales = b.scales + (int64_t)t0 * M;
+    {
+      TimingScope ts(a.P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, s);
+      e = launch_quant_act(a, s);
+    }
+    if (e != hipSuccess) return e;
+    t0 = t1;
+  }
+  GemmSets gs;
+  gs.rows_per_set = M;
+  gs.n = T;
+  int slot_of[LOOPQ_MAX_LOOPS];
+  int nslots = 0;
+  for (int t = 0; t < T; ++t) {
+    int slot = -1;
+    for (int u = 0; u < t; ++u)
+      if (sets[u] == sets[t]) slot = slot_of[u];
+    if (slot < 0) {  // first loop of this set: expand its weights into a fresh region
+      slot = nslots++;
+      if (fmt == kCodesTiledF6) {
+        ActBuffers bs = b;
+        if (slot > 0)
+          bs.wexp = reinterpret_cast<char*>(ws) + act_bytes(T, M, K, N, fmt) + (size_t)(slot - 1) * wexp_region(K, N, fmt);
+        e = prepare_weights(bs, fmt, w_codes_sets[sets[t]], K, N, s);
+        if (e != hipSuccess) return e;
+      }
+    }
+    slot_of[t] = slot;
+    gs.w[t] = fmt == kCodesTiledF6
+                  ? (slot == 0 ? b.wexp
+                               : reinterpret_cast<char*>(ws) + act_bytes(T, M, K, N, fmt) +
+                                     (size_t)(slot - 1) * wexp_region(K, N, fmt))
+                  : w_codes_sets[sets[t]];
+    gs.sw[t] = reinterpret_cast<const __half*>(w_scales_sets[sets[t]]);
+  }
+  TimingScope ts(LOOPQ_KERNEL_GEMM, s);
+  return run_gemm(b, fmt, rows, K, N, gs.w[0], gs.sw[0], gw, y, nullptr, 0, s, &gs);
+}
+
 // The per-token quantizer on x (or, with a transform, on x~ written to xt
 // first by the group kernel, whose codes and steps the per-token pass then
 // overwrites).  `a` carries the outputs; returns the first HIP error.
@@ -495,7 +563,9 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       if (T <= 0 || M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (T > LOOPQ_MAX_LOOPS || K % 32) return LOOPQ_ERR_UNSUPPORTED;
       if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
-      const size_t a4 = act_bytes(T, M, K, N, code_format(4)), a8 = act_bytes(T, M, K, N, code_format(8));
+      // W4A4 with a weight set per loop: one fp6 expansion region per set
+      const size_t a4 = act_bytes(T, M, K, N, code_format(4)) + (size_t)(T - 1) * wexp_region(K, N, code_format(4));
+      const size_t a8 = act_bytes(T, M, K, N, code_format(8));
       *bytes = a4 > a8 ? a4 : a8;
       return LOOPQ_OK;
     }
@@ -674,6 +744,15 @@ int32_t loopq_looped_forward_ex(const void* x, int32_t dtype, int32_t T, int32_t
   if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
   hipStream_t s = as_stream(stream);
   const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
+  bool same_bits = true, one_run = true;
+  for (int t = 1; t < T; ++t) {
+    same_bits = same_bits && bits_host[t] == bits_host[0];
+    one_run = one_run && sets_host[t] == sets_host[0] && bits_host[t] == bits_host[0];
+  }
+  if (!one_run && same_bits && M % 64 == 0 && (int64_t)T * M > kDecodeMaxRows)
+    return hip_status(looped_grouped(x, dtype, T, M, K, N, P1_sets, n1, P2_sets, n2, w_codes_sets,
+                                     w_scales_sets, group_w, sets_host, bits_host[0], clips_host, y,
+                                     workspace, s));
   // maximal runs of consecutive loops with the same set and bit width, each
   // weight-stationary over its rows
   for (int t0 = 0; t0 < T;) {

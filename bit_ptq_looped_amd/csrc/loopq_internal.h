@@ -147,15 +147,24 @@ hipError_t launch_expand_weights_f6(const uint8_t* w_codes, int K, int N, void* 
 
 // fp6-operand GEMM (W4A4: codes and expanded weights in the fp6 tiled
 // layout); same modes as launch_gemm
+// Grouped GEMM: rows [s * rows_per_set, (s + 1) * rows_per_set) take weight
+// set s (rows_per_set a multiple of 64, at most 64 sets).
+struct GemmSets {
+  int rows_per_set = 0;
+  int n = 0;
+  const void* w[64];
+  const __half* sw[64];
+};
+
 hipError_t launch_gemm_f6(const void* a_tiled, const float* a_scales_gm, int ld_sa, int M, int K,
                           int N, const void* w_f6, const __half* w_scales, int gw, float* y,
-                          int32_t* dots, int mode, hipStream_t s);
+                          int32_t* dots, int mode, hipStream_t s, const GemmSets* sets = nullptr);
 
 // GEMM over the internal activation layout.  mode 0: y = rescaled sum;
 // mode 1: write int32 per-group dots [M][N][K/32].
 hipError_t launch_gemm(const int8_t* a_tiled, const float* a_scales_gm, int ld_sa, int M, int K,
                        int N, const uint8_t* w_codes, const __half* w_scales, int gw, float* y,
-                       int32_t* dots, int mode, hipStream_t s);
+                       int32_t* dots, int mode, hipStream_t s, const GemmSets* sets = nullptr);
 
 // Few-row (decode) linear in one launch: at most kDecodeMaxRows token rows
 // of x (quantized in the launch, after an optional transform of one of the

@@ -434,6 +434,48 @@ def test_looped_forward_ex_matches_oracle(lq, M):
         assert rel_err(got[t], ref[t]) <= Y_TOL, t
 
 
+@pytest.mark.parametrize("bits_a", [4, 8])
+@pytest.mark.parametrize("M,sets", [(64, [0, 1, 2, 3]), (128, [0, 1, 1, 0]), (64, [2, 0, 0, 1, 2, 1])])
+def test_looped_forward_ex_grouped_gemm(lq, M, sets, bits_a):
+    """Loop-dependent weight sets at one bit width with M % 64 == 0 run as one
+    grouped GEMM over all T * M rows (each loop's rows take its set's weights;
+    each set's transform quantizes its loops' rows): against the oracle on
+    each loop's kernel x~, and bitwise equal to running the loops one call
+    each (the same kernels per tile)."""
+    K, N = 2048, 160
+    T = len(sets)
+    say(f"grouped looped_forward_ex M={M} sets={sets} A{bits_a}")
+    rng = synth.seeded_rng(synth.TEST, 185, M, T)
+    nsets = max(sets) + 1
+    F = [(synth.haar_orthogonal(32, rng), synth.haar_orthogonal(64, rng)) for _ in range(nsets)]
+    W = [synth.gaussian((N, K), 186, si, scale=0.02) for si in range(nsets)]
+    packed = [pack(lq, w, 32) for w in W]
+    qws = [oracle.quant_weights(w, 32) for w in W]
+    bits = [bits_a] * T
+    clips = [0.95 - 0.05 * t for t in range(T)]
+    x = synth.with_outliers(synth.gaussian((T, M, K), 187, M, T), 8, 20.0, 188, M)
+    bits16, x32 = synth.round_to_bf16(x)
+    xd = bf16_dev(bits16)
+    y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_EX, T, M, K, N, 0)
+    fd = [(dev(a), dev(b)) for a, b in F]
+    lq.loopq_looped_forward_ex(xd, fd, clips, bits, packed, 32, N, y, sets, ws)
+    torch.cuda.synchronize()
+    xt = np.stack([gpu_xt(lq, xd[t], x32[t], *F[sets[t]]) for t in range(T)])
+    ref = oracle.looped_forward_sets(xt, [(None, None)] * nsets, clips, bits, qws, 32, sets)
+    got = y.cpu().numpy()
+    for t in range(T):
+        assert rel_err(got[t], ref[t]) <= Y_TOL, t
+    # loop by loop (one set per call: the ungrouped path) gives the same bits
+    for t in range(T):
+        y1 = torch.empty((1, M, N), dtype=torch.float32, device="cuda")
+        ws1 = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_EX, 1, M, K, N, 0)
+        lq.loopq_looped_forward_ex(xd[t:t + 1], [fd[sets[t]]], [clips[t]], [bits_a], [packed[sets[t]]], 32, N,
+                                   y1, [0], ws1)
+        torch.cuda.synchronize()
+        assert torch.equal(y1[0], y[t]), t
+
+
 def test_looped_forward_ex_with_one_set_is_the_shared_loop(lq):
     K, N, M, T = 512, 96, 40, 4
     P1, P2 = synth.hadamard(16), synth.hadamard(32)
