@@ -239,7 +239,11 @@ int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
  * consecutive loops with the same set and bit width runs weight-stationary
  * (one pass over that set's weights for all of the run's rows), so one set for
  * every loop is exactly loopq_looped_forward's weight-stationary schedule.
- * Workspace: loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_EX, T, M, K, N, 0, ...).
+ * When every loop has the same bit width, M % 64 == 0 and T * M > 16, the
+ * runs share one grouped GEMM launch over all T * M rows instead, each loop's
+ * rows multiplied by its own set's weights (the same bits as separate calls).
+ * Workspace: loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_EX, T, M, K, N, 0, ...)
+ * (room for the W4A4 operands of up to T weight sets).
  * Errors: a set index outside [0, nsets), a bit width other than 4 or 8, or a
  * NULL set entry return LOOPQ_ERR_INVALID_ARG / LOOPQ_ERR_UNSUPPORTED before
  * any launch; the shape and transform checks are those of loopq_looped_forward. */
