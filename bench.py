@@ -46,6 +46,7 @@ def parse():
                    help="skip the loop-dependent (per-loop weight sets / bit widths) measurement")
     p.add_argument("--no-hessian", action="store_true", help="skip the trajectory Hessian measurement")
     p.add_argument("--no-recurrence", action="store_true", help="skip the adapter recurrence measurement")
+    p.add_argument("--no-per-token", action="store_true", help="skip the per-token measurement")
     p.add_argument("--profile-hessian", type=int, default=0,
                    help="only run this many trajectory Hessian steps (for a profiler) and exit")
     p.add_argument("--decode-steps", type=int, default=20)
@@ -692,7 +693,8 @@ def main():
     }
     if not args.no_loop_dependent:
         out["loop_dependent"] = loop_dependent_bench(lq, synth, torch, wl, mods, max(5, args.steps // 2), 2)
-    out["per_token"] = per_token_bench(lq, torch, mods, T, M, max(5, args.steps // 2), 2)
+    if not args.no_per_token:
+        out["per_token"] = per_token_bench(lq, torch, mods, T, M, max(5, args.steps // 2), 2)
     if not args.no_hessian:
         out["trajectory_hessian"] = hessian_bench(lq, torch, mods, T, M, max(5, args.steps // 5), 2)
     if not args.no_recurrence:
