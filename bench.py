@@ -675,6 +675,10 @@ def main():
             "traffic": measured_traffic(),
             "traffic_unit": "HBM bytes per GEMM launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": "gemm_f6_kernel<0> (W4A4 GEMM on e2m3 MFMA operands + per-group rescale)",
+            "frac_fold_inclusive": fold_inclusive(mods, T, M, gemm_ms / args.steps)["frac"],
+            "frac_fold_inclusive_note": ("the GEMM kernel time against MFMA time at 5 POPS plus the per-group fold "
+                                         "(2 fp32 VALU lane operations per element-group at 39.3 T/s); see "
+                                         "fold_inclusive"),
             "launches": gemm_n,
             "avg_launch_ms": gemm_ms / max(gemm_n, 1),
         },
