@@ -435,25 +435,27 @@ def test_looped_forward_ex_matches_oracle(lq, M):
 
 
 @pytest.mark.parametrize("bits_a", [4, 8])
-@pytest.mark.parametrize("M,sets", [(64, [0, 1, 2, 3]), (128, [0, 1, 1, 0]), (64, [2, 0, 0, 1, 2, 1])])
-def test_looped_forward_ex_grouped_gemm(lq, M, sets, bits_a):
+@pytest.mark.parametrize("M,sets,K,N,factors", [(64, [0, 1, 2, 3], 2048, 160, (32, 64)),
+                                                (128, [0, 1, 1, 0], 2048, 160, (32, 64)),
+                                                (64, [2, 0, 0, 1, 2, 1], 2048, 160, (32, 64)),
+                                                (64, [1, 0, 1], 96, 40, (8, 12))])
+def test_looped_forward_ex_grouped_gemm(lq, M, sets, K, N, factors, bits_a):
     """Loop-dependent weight sets at one bit width with M % 64 == 0 run as one
     grouped GEMM over all T * M rows (each loop's rows take its set's weights;
     each set's transform quantizes its loops' rows): against the oracle on
     each loop's kernel x~, and bitwise equal to running the loops one call
     each (the same kernels per tile)."""
-    K, N = 2048, 160
     T = len(sets)
-    say(f"grouped looped_forward_ex M={M} sets={sets} A{bits_a}")
-    rng = synth.seeded_rng(synth.TEST, 185, M, T)
+    say(f"grouped looped_forward_ex M={M} sets={sets} K={K} N={N} A{bits_a}")
+    rng = synth.seeded_rng(synth.TEST, 185, M, T, K)
     nsets = max(sets) + 1
-    F = [(synth.haar_orthogonal(32, rng), synth.haar_orthogonal(64, rng)) for _ in range(nsets)]
-    W = [synth.gaussian((N, K), 186, si, scale=0.02) for si in range(nsets)]
+    F = [(synth.haar_orthogonal(factors[0], rng), synth.haar_orthogonal(factors[1], rng)) for _ in range(nsets)]
+    W = [synth.gaussian((N, K), 186, si, K, scale=0.02) for si in range(nsets)]
     packed = [pack(lq, w, 32) for w in W]
     qws = [oracle.quant_weights(w, 32) for w in W]
     bits = [bits_a] * T
     clips = [0.95 - 0.05 * t for t in range(T)]
-    x = synth.with_outliers(synth.gaussian((T, M, K), 187, M, T), 8, 20.0, 188, M)
+    x = synth.with_outliers(synth.gaussian((T, M, K), 187, M, T, K), min(8, K // 8), 20.0, 188, M)
     bits16, x32 = synth.round_to_bf16(x)
     xd = bf16_dev(bits16)
     y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
