@@ -457,6 +457,27 @@ __device__ __forceinline__ void quant_groups_f6(const QuantArgs& a, const float*
   }
 }
 
+// Copy an n x n factor into LDS rows of stride sp.  Each thread issues a
+// batch of loads before its first LDS write, so the copy takes a few memory
+// round trips rather than one per element it moves.
+__device__ __forceinline__ void stage_factor(float* dst, const float* src, int n, int sp, int tid) {
+  constexpr int kBatch = 16;
+  const int nn = n * n;
+  for (int base = tid; base < nn; base += 256 * kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int idx = base + 256 * i;
+      v[i] = idx < nn ? src[idx] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int idx = base + 256 * i;
+      if (idx < nn) dst[(idx / n) * sp + idx % n] = v[i];
+    }
+  }
+}
+
 // Transform + quantize, NRT = ceil(n1 / 16) row tiles.  N1, N2 > 0 fix the
 // factor sizes at compile time (the k-loops then unroll fully, which keeps the
 // accumulators in place); N1 = N2 = 0 takes them from the arguments.
@@ -500,9 +521,6 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const int sp1 = N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1;
   const int sp2 = N2 > 0 ? XStrides<N1, N2>::sp2 : a.sp2;
   const int sx = N2 > 0 ? XStrides<N1, N2>::sx : a.sx;
-  for (int idx = tid; idx < n1 * n1; idx += 256) sP1[(idx / n1) * sp1 + idx % n1] = a.P1[idx];
-  for (int idx = tid; idx < n2 * n2; idx += 256) sP2[(idx / n2) * sp2 + idx % n2] = a.P2[idx];
-
   const int li = lane & 15;  // row of A / column of B and of the result
   const int lk = lane >> 4;  // k within a 4-deep step; result rows lk + 4 e
   const int nchunks = (a.rows + R - 1) / R;
@@ -563,7 +581,10 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int slot = xcd * (G >> 3) + min(xcd, G & 7) + (int)(blockIdx.x >> 3);
+  // the first chunk's X is in flight while the factors are staged
   if (RS > 0 && slot < nchunks) fetch(slot);
+  stage_factor(sP1, a.P1, n1, sp1, tid);
+  stage_factor(sP2, a.P2, n2, sp2, tid);
   for (int chunk = slot; chunk < nchunks; chunk += G) {
     const int row0 = chunk * R;
     const int rows = min(R, a.rows - row0);
