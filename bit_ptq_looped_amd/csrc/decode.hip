@@ -892,7 +892,7 @@ hipError_t launch_decode(const DecodeCall& c, hipStream_t s) {
     lds = g.whole ? whole_lds(c.R, c.K, RM) : slice_lds(RM);
   }
   if (fn == nullptr || lds > kLdsBudget) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipError_t e = prepare_launch(fn, lds, 256);
   if (e != hipSuccess) return e;
   void* args[] = {&g};
   e = hipLaunchKernel(fn, dim3((unsigned)(padded_cols(c.N) / 32)), dim3(256), args, lds, s);
@@ -920,7 +920,7 @@ hipError_t launch_decode_items(const void* x, int bf16, const float* P1, int n1,
   }
   LOOPQ_SHAPES(LOOPQ_ITEM_KERNEL)
 #undef LOOPQ_ITEM_KERNEL
-  hipError_t e = hipFuncSetAttribute(fi, hipFuncAttributeMaxDynamicSharedMemorySize, ilds);
+  hipError_t e = prepare_launch(fi, ilds, 256);
   if (e != hipSuccess) return e;
   void* iargs[] = {&ga, &xt};
   e = hipLaunchKernel(fi, dim3((unsigned)items), dim3(256), iargs, ilds, s);

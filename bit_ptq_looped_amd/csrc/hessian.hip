@@ -364,8 +364,7 @@ size_t hessian_workspace_bytes(int K) {
 
 hipError_t launch_hessian(const float* x, int rows, int K, float* H, float* part, hipStream_t s) {
   const HPlan p = make_plan(x, rows, K, H, part);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(hessian_tiles_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  hipError_t e = prepare_launch(reinterpret_cast<const void*>(hessian_tiles_kernel), (int)kLdsBytes, kThreads);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(hessian_tiles_kernel, dim3(kGroups), dim3(kThreads), kLdsBytes, s, p);
   e = hipGetLastError();

@@ -177,6 +177,16 @@ hipError_t run_gemm(const ActBuffers& b, int fmt, int rows, int K, int N, const 
 // Enqueueing is serialized by a mutex; the caller's stream waits for every
 // auxiliary launch it depends on, so stream order is preserved for the caller.
 // ---------------------------------------------------------------------------
+std::mutex g_launch_mu;
+struct KernelState {
+  int dev;
+  const void* fn;
+  int lds_set;
+  std::vector<int> occ;  // (lds bytes, block, work-groups per CU) triples
+};
+std::vector<KernelState> g_kernels;
+int g_ncu[64];
+
 std::mutex g_pipe_mu;
 struct DevicePipe {
   hipStream_t aux = nullptr;
@@ -1061,3 +1071,46 @@ int32_t loopq_timing_read(int32_t n, double* ms_host, int64_t* launches_host) {
 }
 
 }  // extern "C"
+
+namespace loopq {
+
+hipError_t prepare_launch(const void* fn, int lds_bytes, int block, int* per_cu, int* ncu) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_launch_mu);
+  KernelState* st = nullptr;
+  for (KernelState& k : g_kernels)
+    if (k.dev == dev && k.fn == fn) st = &k;
+  if (!st) {
+    g_kernels.push_back(KernelState{dev, fn, 0, {}});
+    st = &g_kernels.back();
+  }
+  if (lds_bytes > st->lds_set) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    st->lds_set = lds_bytes;
+  }
+  if (ncu) {
+    if (g_ncu[dev] <= 0) {
+      int n = 0;
+      g_ncu[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+    }
+    *ncu = g_ncu[dev];
+  }
+  if (per_cu) {
+    int found = -1;
+    for (size_t i = 0; i + 2 < st->occ.size(); i += 3)
+      if (st->occ[i] == lds_bytes && st->occ[i + 1] == block) found = st->occ[i + 2];
+    if (found < 0) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&found, fn, block, lds_bytes) != hipSuccess || found < 1)
+        found = 1;
+      st->occ.insert(st->occ.end(), {lds_bytes, block, found});
+    }
+    *per_cu = found;
+  }
+  return hipSuccess;
+}
+
+}  // namespace loopq

@@ -208,6 +208,14 @@ hipError_t launch_decode(const DecodeCall& c, hipStream_t s);
 constexpr int kHessianMaxK = 65536;
 constexpr int kHessianMaxRows = 1 << 30;
 size_t hessian_workspace_bytes(int K);
+// Raises fn's dynamic-LDS limit on the current device to lds_bytes if it is
+// below (never lowers it, so every earlier launch size stays valid) and, if
+// asked, reports the device's CU count and fn's resident work-groups per CU
+// for blocks of `block` threads at that LDS size (256 CUs and 1 if a query
+// fails).  Kept per device and kernel, so only a kernel's first launch at a
+// given size pays for the runtime queries.
+hipError_t prepare_launch(const void* fn, int lds_bytes, int block, int* per_cu = nullptr, int* ncu = nullptr);
+
 hipError_t launch_hessian(const float* x, int rows, int K, float* H, float* part, hipStream_t s);
 
 // x [M][2N] = cat(s [M][N], e [M][N]) per row (fp32, N % 4 == 0, 16-byte aligned)

@@ -185,26 +185,47 @@ __device__ __forceinline__ float4 load_row4(const QuantArgs& a, int row, int k) 
   return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + e);
 }
 
+// NC > 0: the row is held in NC float4 registers per thread (K <= 1024 NC),
+// all of its loads issued before the first is used; NC = 0 reads the row
+// twice, one quad at a time, for any K.
+template <int NC>
 __global__ __launch_bounds__(256) void quant_token_kernel(QuantArgs a) {
   __shared__ float red[4];
   const int row = blockIdx.x;
   const int n4 = a.K >> 2;
   const float qmaxf = (float)a.qmax;
   const float rq = 1.0f / qmaxf;
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    const float4 v = load_row4(a, row, 4 * i);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-  }
+  auto amax4 = [](const float4& v) { return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))); };
+  auto row_max = [&](float m) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = step_of(amax, a.clips.c[row / a.rows_per_clip], qmaxf, rq);
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    const float4 v = load_row4(a, row, 4 * i);
-    store_run(a, row, 4 * i, codes4(v, s, qmaxf), s, ((4 * i) & 31) == 0, v);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  };
+  float m = 0.0f;
+  if constexpr (NC > 0) {
+    float4 v[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int i = threadIdx.x + 256 * c;
+      v[c] = i < n4 ? load_row4(a, row, 4 * i) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) m = fmaxf(m, amax4(v[c]));
+    const float s = step_of(row_max(m), a.clips.c[row / a.rows_per_clip], qmaxf, rq);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int i = threadIdx.x + 256 * c;
+      if (i < n4) store_run(a, row, 4 * i, codes4(v[c], s, qmaxf), s, ((4 * i) & 31) == 0, v[c]);
+    }
+  } else {
+    for (int i = threadIdx.x; i < n4; i += 256) m = fmaxf(m, amax4(load_row4(a, row, 4 * i)));
+    const float s = step_of(row_max(m), a.clips.c[row / a.rows_per_clip], qmaxf, rq);
+    for (int i = threadIdx.x; i < n4; i += 256) {
+      const float4 v = load_row4(a, row, 4 * i);
+      store_run(a, row, 4 * i, codes4(v, s, qmaxf), s, ((4 * i) & 31) == 0, v);
+    }
   }
 }
 
@@ -738,7 +759,14 @@ bool quant_plan_fits(int K, int n1, int n2) {
 hipError_t launch_quant_token(QuantArgs a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (a.P1 != nullptr) return hipErrorInvalidValue;  // transform first, then quantize x~
-  hipLaunchKernelGGL(quant_token_kernel, dim3((unsigned)a.rows), dim3(256), 0, s, a);
+  const int n4 = a.K / 4;
+  void (*fn)(QuantArgs) = n4 <= 256    ? quant_token_kernel<1>
+                          : n4 <= 512  ? quant_token_kernel<2>
+                          : n4 <= 1024 ? quant_token_kernel<4>
+                          : n4 <= 1536 ? quant_token_kernel<6>
+                          : n4 <= 2048 ? quant_token_kernel<8>
+                                       : quant_token_kernel<0>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)a.rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -772,17 +800,10 @@ hipError_t launch_quant_act(QuantArgs a, hipStream_t s) {
       default: return hipErrorInvalidConfiguration;
     }
   }
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, a.lds_bytes);
+  int per_cu = 1, ncu = 256;
+  hipError_t e = prepare_launch(fn, a.lds_bytes, 256, &per_cu, &ncu);
   if (e != hipSuccess) return e;
   const int nchunks = (a.rows + a.R - 1) / a.R;
-  int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    ncu = 256;
-  int per_cu = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, a.lds_bytes) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
   int blocks = ncu * per_cu;
   if (blocks > nchunks) blocks = nchunks;
   void* args[] = {&a};
