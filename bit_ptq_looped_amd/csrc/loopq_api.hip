@@ -499,24 +499,16 @@ hipError_t looped_grouped(const void* x, int dtype, int T, int M, int K, int N, 
   return run_gemm(b, fmt, rows, K, N, gs.w[0], gs.sw[0], gw, y, nullptr, 0, s, &gs);
 }
 
-// The per-token quantizer on x (or, with a transform, on x~ written to xt
-// first by the group kernel, whose codes and steps the per-token pass then
-// overwrites).  `a` carries the outputs; returns the first HIP error.
-hipError_t per_token_quant(QuantArgs a, float* xt, hipStream_t s) {
+// The per-token quantizer.  With a transform it runs inside the transform
+// kernel, which holds whole x~ rows in LDS and takes each row's absmax there
+// (one launch, no x~ round trip; x~ goes to a.xt_out only if the caller asked
+// for it); without one, the row kernel quantizes x.  `a` carries the
+// outputs; returns the first HIP error.
+hipError_t per_token_quant(QuantArgs a, hipStream_t s) {
   if (a.P1 != nullptr) {
-    QuantArgs t = a;
-    t.xt_out = xt;
-    hipError_t e;
-    {
-      TimingScope ts(LOOPQ_KERNEL_QUANT_TRANSFORM, s);
-      e = launch_quant_act(t, s);
-    }
-    if (e != hipSuccess) return e;
-    a.x = xt;
-    a.bf16 = 0;
-    a.P1 = a.P2 = nullptr;
-    a.n1 = a.n2 = 0;
-    a.xt_out = nullptr;  // already written by the transform pass
+    a.per_token = 1;
+    TimingScope ts(LOOPQ_KERNEL_QUANT_TRANSFORM, s);
+    return launch_quant_act(a, s);
   }
   TimingScope ts(LOOPQ_KERNEL_QUANT_TOKEN, s);
   return launch_quant_token(a, s);
@@ -897,18 +889,16 @@ int32_t loopq_quant_act_per_token(const void* x, int32_t dtype, int32_t M, int32
   if (M == 0) return LOOPQ_OK;
   if (!codes || !scales) return LOOPQ_ERR_INVALID_ARG;
   if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(xt_out, 16)) return LOOPQ_ERR_ALIGNMENT;
-  float* xt = xt_out;
-  if (P1 && !xt) {  // x~ staged in the workspace
+  if (P1 && !xt_out) {  // the documented workspace contract (x~ staging region)
     if (!workspace || workspace_bytes < align256((size_t)M * K * 4)) return LOOPQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
-    xt = reinterpret_cast<float*>(workspace);
   }
   QuantArgs a = make_quant_args(x, dtype, M, K, P1, n1, P2, n2, bits_a);
   a.clips.c[0] = clip;
   a.codes = codes;
   a.scales = scales;
   a.xt_out = xt_out;
-  return hip_status(per_token_quant(a, xt, as_stream(stream)));
+  return hip_status(per_token_quant(a, as_stream(stream)));
 }
 
 int32_t loopq_looped_forward_per_token(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
@@ -945,14 +935,13 @@ int32_t loopq_looped_forward_per_token(const void* x, int32_t dtype, int32_t T, 
   hipStream_t s = as_stream(stream);
   const int fmt = code_format(bits_a);
   ActBuffers b = carve(workspace, 1, rows, K, N, 0, rows);
-  float* xt = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + act_bytes(1, rows, K, N, fmt));
   QuantArgs a = internal_quant_args(x, dtype, rows, K, P1, n1, P2, n2, clips, M, bits_a, b);
   const bool few = rows <= kDecodeMaxRows;
   if (few) {  // canonical codes and row-major steps for the few-row kernel
     a.codes_fmt = kCodesCanonical;
     a.scales_gm = 0;
   }
-  hipError_t e = per_token_quant(a, xt, s);
+  hipError_t e = per_token_quant(a, s);
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   if (few) {
     DecodeCall c;

@@ -117,10 +117,12 @@ struct QuantArgs {
   int scales_gm;
   int scales_ld;
   float* xt_out;     // nullable, [rows][K]
+  int per_token;     // 1: one step per row from the row's absmax, written to every group slot
   // transform kernel LDS plan (set by the host launcher)
   int R;             // rows per work chunk
   int sp1, sp2, sx, st;  // LDS strides (elements) of P1, P2, X, T
   int off_p2, off_x, off_t;  // byte offsets in dynamic LDS
+  int off_rmax;      // byte offset of the per-row, per-wave absmax partials (per_token)
   int lds_bytes;
 };
 

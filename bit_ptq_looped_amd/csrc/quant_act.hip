@@ -46,13 +46,15 @@ __device__ __forceinline__ int xt_pos(int f) {
 // 0.5 - 2^-15 of rint(p)).  ev and od
 // hold the group's even and odd elements on entry and their clamped codes
 // (as floats) on return; reload(ev, od) brings the group back for the rare
-// exact path.  Returns the step.
+// exact path.  A row_amax >= 0 replaces the group's absmax (one step per
+// row).  Returns the step.
 template <typename Reload>
 __device__ __forceinline__ float quantize32(v16f& ev, v16f& od, float clip, float qmaxf, float rq,
-                                            Reload reload) {
+                                            Reload reload, float row_amax) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(ev[i]), fabsf(od[i])));
+  if (row_amax >= 0.0f) amax = row_amax;  // one step for the whole row
   const float q0 = amax * rq;
   const float base = __builtin_fmaf(__builtin_fmaf(-q0, qmaxf, amax), rq, q0);  // = fl32(amax / qmax)
   const float s = clip * base;
@@ -378,15 +380,20 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
   }
 }
 
+// Absmax of chunk row r from its four per-wave partials (per-token steps).
+__device__ __forceinline__ float row_amax_of(const float* sR, int r) {
+  return fmaxf(fmaxf(sR[4 * r], sR[4 * r + 1]), fmaxf(sR[4 * r + 2], sR[4 * r + 3]));
+}
+
 // Quantize the flat transformed rows [rows][K] of a chunk held in LDS at sX
 // (chunk row r is global row row0 + r; elements placed by xt_pos), four
 // elements per lane.  Lane r of the wave holds the clip of chunk row r in cl
 // (rows <= 64); a run takes it with one LDS permute, read a step ahead
 // together with the run's four elements.
 template <int FMT>
-__device__ __forceinline__ void quant_chunk(const QuantArgs& a, const float* sX, int row0, int rows,
-                                            int K, int wave, int lane, float cl, float qmaxf,
-                                            float rqmax) {
+__device__ __forceinline__ void quant_chunk(const QuantArgs& a, const float* sX, const float* sR,
+                                            int row0, int rows, int K, int wave, int lane, float cl,
+                                            float qmaxf, float rqmax) {
   const int nruns = rows * K / 4;  // multiple of 8
   int q0 = wave * 64;
   if (q0 >= nruns) return;
@@ -408,7 +415,13 @@ __device__ __forceinline__ void quant_chunk(const QuantArgs& a, const float* sX,
     const int e = (valid ? q : q0) * 4;
     const int r = e / K;
     float s;
-    const uint32_t packed = quantize4(v, c, qmaxf, rqmax, &s);
+    uint32_t packed;
+    if (a.per_token) {
+      s = step_of(row_amax_of(sR, r), c, qmaxf, rqmax);
+      packed = codes4(v, s, qmaxf);
+    } else {
+      packed = quantize4(v, c, qmaxf, rqmax, &s);
+    }
     if (valid) store_run_f<FMT>(a, K, row0 + r, e - r * K, packed, s, (lane & 7) == 0, v);
     v = vn;
     c = cn;
@@ -422,8 +435,8 @@ __device__ __forceinline__ void quant_chunk(const QuantArgs& a, const float* sX,
 // into the even fields; fed the even and the odd elements it yields the
 // group's 24 bytes in field order, stored as they are.  A zero code may come
 // out as either e2m3 zero pattern.
-__device__ __forceinline__ void quant_groups_f6(const QuantArgs& a, const float* sX, int row0,
-                                                int rows, int K, int wave, int lane, float cl,
+__device__ __forceinline__ void quant_groups_f6(const QuantArgs& a, const float* sX, const float* sR,
+                                                int row0, int rows, int K, int wave, int lane, float cl,
                                                 float qmaxf, float rqmax) {
   const int Ga = K >> 5;
   const int Gp = (Ga + 1) >> 1;
@@ -450,7 +463,7 @@ __device__ __forceinline__ void quant_groups_f6(const QuantArgs& a, const float*
     const int r = gc / Ga;
     const int j = gc - r * Ga;
     const float clip = __int_as_float(__builtin_amdgcn_ds_bpermute(r << 2, __float_as_int(cl)));
-    const float s = quantize32(ev, od, clip, qmaxf, rqmax, load);
+    const float s = quantize32(ev, od, clip, qmaxf, rqmax, load, a.per_token ? row_amax_of(sR, r) : -1.0f);
     if (!valid) continue;
     const v6i bits = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
     // The instruction's result must not share registers with its sources
@@ -525,6 +538,7 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   float* sP1 = reinterpret_cast<float*>(lds);
   float* sP2 = reinterpret_cast<float*>(lds + a.off_p2);
   float* sX = reinterpret_cast<float*>(lds + a.off_x);
+  float* sR = reinterpret_cast<float*>(lds + a.off_rmax);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -664,19 +678,37 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
     }
     __syncthreads();
 
+    // ---- per-token steps: each row's absmax over its whole x~ row (the
+    // max is order-free), one partial per wave, combined when used
+    if (a.per_token) {
+      for (int r = 0; r < rows; ++r) {
+        float m = 0.0f;
+        for (int q = tid; q < (K >> 2); q += 256) {
+          const float4 v = *reinterpret_cast<const float4*>(sX + xt_pos(r * K + 4 * q));
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if (lane == 0) sR[4 * r + wave] = m;
+      }
+      __syncthreads();
+    }
+
     // ---- quantize groups of the flat transformed rows
     if (a.codes_fmt == kCodesTiledF6)
-      quant_groups_f6(a, sX, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
+      quant_groups_f6(a, sX, sR, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
     else if (a.codes_fmt == kCodesTiledI8)
-      quant_chunk<kCodesTiledI8>(a, sX, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
+      quant_chunk<kCodesTiledI8>(a, sX, sR, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
     else
-      quant_chunk<kCodesCanonical>(a, sX, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
+      quant_chunk<kCodesCanonical>(a, sX, sR, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
   }
 }
 
 }  // namespace
 
 namespace {
+
+constexpr int kRowMaxBytes = 16 * 4 * 4;
 
 int x_bytes_for(int R, int n1, int sx, int K) {
   int xb = R * n1 * sx * 4;
@@ -710,10 +742,11 @@ bool plan_quant(QuantArgs& a) {
     if (R > 16) R = 16;
   }
   if (R * njt > 4 * nim) return false;  // every work item must have a wave slot
+  // + 256 bytes of per-row absmax partials (16 rows x 4 waves) after X
   auto lds_for = [&](int sp1, int sp2, int sx, int r) {
     const int p2 = (a.n1 * sp1 * 4 + 15) / 16 * 16;
     const int px = (p2 + a.n2 * sp2 * 4 + 15) / 16 * 16;
-    return px + x_bytes_for(r, a.n1, sx, a.K);
+    return px + x_bytes_for(r, a.n1, sx, a.K) + kRowMaxBytes;
   };
   int sp1 = p_stride(a.n1);
   int sp2 = p_stride(a.n2);
@@ -742,7 +775,8 @@ bool plan_quant(QuantArgs& a) {
   a.off_p2 = (a.n1 * sp1 * 4 + 15) / 16 * 16;
   a.off_x = (a.off_p2 + a.n2 * sp2 * 4 + 15) / 16 * 16;
   a.off_t = 0;
-  a.lds_bytes = a.off_x + x_bytes_for(R, a.n1, sx, a.K);
+  a.off_rmax = a.off_x + x_bytes_for(R, a.n1, sx, a.K);
+  a.lds_bytes = a.off_rmax + kRowMaxBytes;
   return true;
 }
 

@@ -174,9 +174,12 @@ int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, in
  * codes int8 [M][K]; scales fp32 [M][K/32]: the row's one step written to each
  * of its K/32 group slots, so loopq_gemm_codes consumes the pair unchanged.
  * xt_out (nullable) receives x~.  Arguments and errors as loopq_quant_act.
- * Workspace: with a transform and xt_out NULL, x~ is staged in `workspace`
- * (loopq_workspace_bytes(LOOPQ_OP_QUANT_PER_TOKEN, 0, M, K, 0, 0, ...)
- * bytes, 256-byte aligned); otherwise workspace may be NULL. */
+ * With a transform, each row's absmax is taken over the x~ row the transform
+ * kernel holds on chip (one launch; x~ reaches memory only through xt_out).
+ * Workspace: with a transform and xt_out NULL, a workspace of
+ * loopq_workspace_bytes(LOOPQ_OP_QUANT_PER_TOKEN, 0, M, K, 0, 0, ...) bytes,
+ * 256-byte aligned, is still required (reserved: this version writes none of
+ * it); otherwise workspace may be NULL. */
 int32_t loopq_quant_act_per_token(const void* x, int32_t dtype, int32_t M, int32_t K,
                                   const float* P1, int32_t n1, const float* P2, int32_t n2,
                                   float clip, int32_t bits_a, int8_t* codes, float* scales,

@@ -1,7 +1,7 @@
 """HIP graph capture of the entry points added for the loop's neighbours: the
 adapter recurrence (device-side concatenation and one linear per loop), the
 trajectory Hessian (tile and piece kernels) and the per-token loop (transform
-pass, per-token quantizer, weight expansion, GEMM).  None records a memset.
+kernel with per-row steps, weight expansion, GEMM).  None records a memset.
 Each graph is replayed several times with eager work between replays; every
 replay must equal the eager result bit for bit.
 """
