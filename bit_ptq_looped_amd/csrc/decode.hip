@@ -65,7 +65,29 @@ struct DecodeArgs {
   int32_t* dots;          // [R][N][K/32] (mode 1)
   int whole;              // non-transform instances: all codes fit LDS at once
   int wide_codes;         // canonical codes 16-byte aligned (copied 16 at a time)
+  int8_t* codes_out;      // nullable: the codes formed from x, canonical [R][K]
+  float* steps_out;       // with codes_out: their steps, row-major [R][K/32]
 };
+
+// The codes and steps of groups [j0, j0 + G) of every row, held in LDS (codes
+// of group j0 + gi of row m at sA + m * a_ld + gi * 32, its step at
+// sS[m * s_ld + gi]), written to the canonical output.  Every work-group holds
+// the same codes, so the work-groups share the writes out between them.
+__device__ __forceinline__ void dump_codes(const DecodeArgs& g, int j0, int G, const int8_t* sA, int a_ld,
+                                           const float* sS, int s_ld) {
+  const int K = g.K, Ga = K >> 5;
+  const int stride = (int)gridDim.x * 256;
+  const int n16 = g.R * G * 2;  // 16-code pieces
+  for (int q = (int)blockIdx.x * 256 + (int)threadIdx.x; q < n16; q += stride) {
+    const int m = q / (2 * G), rem = q - m * 2 * G;
+    *reinterpret_cast<uint4*>(g.codes_out + (int64_t)m * K + (j0 + (rem >> 1)) * 32 + (rem & 1) * 16) =
+        *reinterpret_cast<const uint4*>(sA + m * a_ld + (rem >> 1) * 32 + (rem & 1) * 16);
+  }
+  for (int q = (int)blockIdx.x * 256 + (int)threadIdx.x; q < g.R * G; q += stride) {
+    const int m = q / G;
+    g.steps_out[(int64_t)m * Ga + j0 + (q - m * G)] = sS[m * s_ld + q - m * G];
+  }
+}
 
 // 8 biased nibbles (q + 8) per dword -> 16 int8 codes, in K order
 __device__ __forceinline__ v4i unpack16(uint2 p) {
@@ -736,6 +758,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
     stage_matrix<N2, P::sp2>(g.P2, sP2);
     // (transform_row's barrier after the X staging orders these stores too)
     for (int r = 0; r < R; ++r) transform_row<NRT, N1, N2>(g, r, lds, sC, sS);
+    if (g.codes_out) dump_codes(g, 0, Ga, sC, K, sS, Ga);
     if (nsl > 1) load(1, wb);
     sweep([&](int sl, const Slice& buf) { dots(sl, buf, 0, Ga, sC, K, 0, sS, Ga); });
   } else if (g.whole) {
@@ -749,6 +772,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
     else
       make_codes<MODE>(g, 0, Ga, sA, K, sSt, Ga);
     __syncthreads();
+    if (g.codes_out && !g.in_codes) dump_codes(g, 0, Ga, sA, K, sSt, Ga);
     sweep([&](int sl, const Slice& buf) { dots(sl, buf, 0, Ga, sA, K, 0, sSt, Ga); });
   } else {
     // too many codes for LDS: one weight slice of codes at a time
@@ -765,6 +789,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
       else
         make_codes<MODE>(g, j0, GS, sA, kSlice * 32, sSt, kSlice);
       __syncthreads();
+      if (g.codes_out && !g.in_codes) dump_codes(g, j0, GS, sA, kSlice * 32, sSt, kSlice);
       dots(sl, buf, j0, j0 + GS, sA, kSlice * 32, j0, sSt, kSlice);
     });
   }
@@ -871,6 +896,11 @@ hipError_t launch_decode(const DecodeCall& c, hipStream_t s) {
   g.y = c.y;
   g.dots = c.dots;
   g.wide_codes = c.a_codes != nullptr && (reinterpret_cast<uintptr_t>(c.a_codes) & 15) == 0 && (c.K & 15) == 0;
+  if (c.codes_out != nullptr && c.a_codes == nullptr && c.mode == 0) {
+    if ((reinterpret_cast<uintptr_t>(c.codes_out) & 15) != 0 || c.steps_out == nullptr) return hipErrorInvalidValue;
+    g.codes_out = c.codes_out;
+    g.steps_out = c.steps_out;
+  }
   const void* fn = nullptr;
   int lds = 0;
   const bool small = c.R <= 4;

@@ -75,18 +75,9 @@ void recycle_locked() {
   g_timing_recs.clear();
 }
 
-// Which GEMM the hot path uses: W4A4 runs on the fp6-operand kernel and W4A8
-// on the INT8 kernel.  LOOPQ_GEMM=int8 sends W4A4 to the INT8 kernel too
-// (same results; kept for comparison).
-bool force_int8_gemm() {
-  static const bool v = [] {
-    const char* e = getenv("LOOPQ_GEMM");
-    return e != nullptr && strcmp(e, "int8") == 0;
-  }();
-  return v;
-}
-
-int code_format(int bits_a) { return bits_a == 4 && !force_int8_gemm() ? kCodesTiledF6 : kCodesTiledI8; }
+// The GEMM each activation width runs on: W4A4 on the fp6-operand kernel
+// (e2m3 holds the codes -7..7 exactly), W4A8 on the INT8 kernel.
+int code_format(int bits_a) { return bits_a == 4 ? kCodesTiledF6 : kCodesTiledI8; }
 
 // Internal buffers of the quantize -> GEMM path, carved from the caller's
 // workspace for `chunks` chunks of `rows` rows each:
@@ -343,6 +334,10 @@ hipError_t run_decode(const void* x, int dtype, int rows, int K, int N, const fl
     c.P2 = P2;
     c.n1 = n1;
     c.n2 = n2;
+    // the codes the launch forms go to the workspace too (canonical), where
+    // the other few-row form leaves them, for loopq_export_act_codes
+    c.codes_out = reinterpret_cast<int8_t*>(b.codes);
+    c.steps_out = b.scales;
   }
   TimingScope ts(LOOPQ_KERNEL_DECODE, s);
   return launch_decode(c, s);
@@ -390,7 +385,7 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
       one.c[0] = clips.c[t];
       const void* xt = reinterpret_cast<const char*>(x) + (size_t)t * M * K * esz;
       hipError_t e = run_decode(xt, dtype, M, K, N, P1, n1, P2, n2, one, M, bits_a, w_codes, w_scales,
-                                gw, y + (size_t)t * M * N, carve(ws, T, M, K, N, 0, 0), s);
+                                gw, y + (size_t)t * M * N, carve(ws, T, M, K, N, t, 0), s);
       if (e != hipSuccess) return LOOPQ_ERR_HIP;
     }
     return LOOPQ_OK;
@@ -571,10 +566,10 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       *bytes = a4 > a8 ? a4 : a8;
       return LOOPQ_OK;
     }
-    case LOOPQ_OP_QUANT_PER_TOKEN:
+    case LOOPQ_OP_QUANT_PER_TOKEN:  // the call needs no workspace
       if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (K % 32) return LOOPQ_ERR_UNSUPPORTED;
-      *bytes = align256((size_t)M * K * 4);
+      *bytes = 0;
       return LOOPQ_OK;
     case LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN: {
       if (bits_a != 4 && bits_a != 8) return LOOPQ_ERR_UNSUPPORTED;
@@ -582,7 +577,7 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       if (T > LOOPQ_MAX_LOOPS || K % 32) return LOOPQ_ERR_UNSUPPORTED;
       if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
       const int64_t rows = (int64_t)T * M;
-      *bytes = act_bytes(1, rows, K, N, code_format(bits_a)) + align256((size_t)rows * K * 4);
+      *bytes = act_bytes(1, rows, K, N, code_format(bits_a));
       return LOOPQ_OK;
     }
     case LOOPQ_OP_RECURRENT_ADAPTER:  // K = 2N is implied; the K argument is ignored
@@ -876,6 +871,69 @@ int32_t loopq_group_dots(const int8_t* a_codes, int32_t M, int32_t K, int32_t N,
   return hip_status(e);
 }
 
+int32_t loopq_export_weight_codes(const void* w_codes, int32_t K, int32_t N, int32_t group_w, int8_t* codes,
+                                  void* stream) {
+  int32_t st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  if (!w_codes || !codes) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(w_codes, 16)) return LOOPQ_ERR_ALIGNMENT;
+  return hip_status(launch_export_weights(reinterpret_cast<const uint8_t*>(w_codes), nullptr, K, N, group_w,
+                                          codes, nullptr, as_stream(stream)));
+}
+
+int32_t loopq_export_act_codes(const void* workspace, size_t workspace_bytes, int32_t op, int32_t T, int32_t M,
+                               int32_t K, int32_t N, int32_t bits_a, int32_t schedule, int8_t* codes,
+                               float* scales, void* stream) {
+  if (op == LOOPQ_OP_LINEAR) {
+    if (T != 1) return LOOPQ_ERR_INVALID_ARG;
+  } else if (op != LOOPQ_OP_LOOPED_FORWARD && op != LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN &&
+             op != LOOPQ_OP_RECURRENT_ADAPTER) {
+    return LOOPQ_ERR_INVALID_ARG;
+  }
+  if (op == LOOPQ_OP_RECURRENT_ADAPTER) {
+    if (T != 1) return LOOPQ_ERR_INVALID_ARG;
+    if (N <= 0 || N % 16) return N <= 0 ? LOOPQ_ERR_INVALID_ARG : LOOPQ_ERR_UNSUPPORTED;
+    K = 2 * N;
+  }
+  if (T <= 0 || M < 0 || K <= 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (T > LOOPQ_MAX_LOOPS || K % 32) return LOOPQ_ERR_UNSUPPORTED;
+  if (bits_a != 4 && bits_a != 8) return LOOPQ_ERR_UNSUPPORTED;
+  if (schedule < LOOPQ_SCHED_AUTO || schedule > LOOPQ_SCHED_WEIGHT_STATIONARY) return LOOPQ_ERR_INVALID_ARG;
+  if ((int64_t)T * M > (int64_t)1 << 30) return LOOPQ_ERR_UNSUPPORTED;
+  size_t need = 0;
+  int32_t st = loopq_workspace_bytes(op, T, M, K, N, bits_a, &need);
+  if (st != LOOPQ_OK) return st;
+  if (M == 0) return LOOPQ_OK;
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  if (!codes || !scales) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(scales, 4)) return LOOPQ_ERR_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  const int64_t rows = (int64_t)T * M;
+  const int Ga = K / 32;
+  void* wsp = const_cast<void*>(workspace);  // carve() only computes addresses; nothing is written
+  // where each forward form leaves its codes (carve() as the call used it)
+  auto one = [&](const ActBuffers& b, int64_t r, int64_t row0) -> hipError_t {
+    const bool few = r <= kDecodeMaxRows;  // few-row path: canonical codes, row-major steps
+    return launch_export_act(b.codes, b.scales, (int)r, K, few ? kCodesCanonical : code_format(bits_a), b.ld,
+                             few ? 0 : 1, codes + row0 * K, scales + row0 * Ga, s);
+  };
+  if (op == LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN)
+    return hip_status(one(carve(wsp, 1, rows, K, N, 0, rows), rows, 0));
+  if (op == LOOPQ_OP_RECURRENT_ADAPTER) {
+    void* ws = reinterpret_cast<char*>(wsp) + align256((size_t)M * K * 4);
+    return hip_status(one(carve(ws, 1, M, K, N, 0, M), M, 0));
+  }
+  if (schedule == LOOPQ_SCHED_LOOP_SEQUENTIAL && T > 1) {
+    for (int t = 0; t < T; ++t) {
+      hipError_t e = one(carve(wsp, T, M, K, N, t, 0), M, (int64_t)t * M);
+      if (e != hipSuccess) return LOOPQ_ERR_HIP;
+    }
+    return LOOPQ_OK;
+  }
+  return hip_status(one(carve(wsp, T, M, K, N, 0, rows), rows, 0));
+}
+
 int32_t loopq_quant_act_per_token(const void* x, int32_t dtype, int32_t M, int32_t K, const float* P1,
                                   int32_t n1, const float* P2, int32_t n2, float clip, int32_t bits_a,
                                   int8_t* codes, float* scales, float* xt_out, void* workspace,
@@ -889,10 +947,8 @@ int32_t loopq_quant_act_per_token(const void* x, int32_t dtype, int32_t M, int32
   if (M == 0) return LOOPQ_OK;
   if (!codes || !scales) return LOOPQ_ERR_INVALID_ARG;
   if (!aligned(codes, 4) || !aligned(scales, 4) || !aligned(xt_out, 16)) return LOOPQ_ERR_ALIGNMENT;
-  if (P1 && !xt_out) {  // the documented workspace contract (x~ staging region)
-    if (!workspace || workspace_bytes < align256((size_t)M * K * 4)) return LOOPQ_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
-  }
+  (void)workspace;  // accepted for compatibility; this call needs none
+  (void)workspace_bytes;
   QuantArgs a = make_quant_args(x, dtype, M, K, P1, n1, P2, n2, bits_a);
   a.clips.c[0] = clip;
   a.codes = codes;

@@ -143,6 +143,13 @@ hipError_t launch_fold(const float* w, int K, int N, const float* P1, int n1, co
 hipError_t launch_tile_codes(const int8_t* canon_codes, const float* canon_scales, int M, int K,
                              void* tiled_codes, int fmt, float* gm_scales, int ld, hipStream_t s);
 
+// Codes in layout `fmt` (ld: padded rows of the tiled layouts) and steps
+// (group-major [K/32][ld] if steps_gm, else row-major [rows][K/32]) back to
+// canonical int8 [rows][K] and row-major fp32 steps.  fp6 fields that are not
+// a code -7..7 come back as -128.
+hipError_t launch_export_act(const void* codes, const float* steps, int rows, int K, int fmt, int ld,
+                             int steps_gm, int8_t* out_codes, float* out_steps, hipStream_t s);
+
 // packed nibbles -> fp6 weight operands in the fp6 tiled layout
 // (padded_cols(N) / 32 * group_pairs(K) blocks of kF6BlockBytes)
 hipError_t launch_expand_weights_f6(const uint8_t* w_codes, int K, int N, void* out, hipStream_t s);
@@ -192,6 +199,10 @@ struct DecodeCall {
   float* y;
   int32_t* dots;
   int mode;
+  // nullable: when the launch forms the codes itself (from x), it also
+  // writes them here, canonical [R][K], with row-major steps [R][K/32]
+  int8_t* codes_out;
+  float* steps_out;
 };
 // true if one launch takes this transform for R rows (a compiled-in factor
 // shape, and the transform repeated per work-group cheap enough)

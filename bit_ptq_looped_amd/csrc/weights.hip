@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void export_kernel(const uint8_t* __restrict__
       const int nib = ((i & 7) < 4) ? (byte & 15) : (byte >> 4);
       out_codes[(int64_t)n * K + kc * 32 + h * 16 + i] = (int8_t)(nib - 8);
     }
-  if ((kc * 32) % gw == 0) {
+  if (out_scales != nullptr && (kc * 32) % gw == 0) {
     const int jw = kc * 32 / gw;
     out_scales[(int64_t)n * Gw + jw] =
         __half_as_ushort(scales[((int64_t)nb * Gw + jw) * 32 + step_slot(c)]);

@@ -53,6 +53,8 @@ SIGNATURES = {
     "loopq_gemm_codes": ([_P, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _Z, _P], _I),
     "loopq_export_weights": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "loopq_group_dots": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+    "loopq_export_weight_codes": ([_P, _I, _I, _I, _P, _P], _I),
+    "loopq_export_act_codes": ([_P, _Z, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "loopq_hessian_accumulate": ([_P, _I, _I, _P, _P, _Z, _P], _I),
     "loopq_recurrent_adapter": ([_P, _P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _P, _Z, _P], _I),
     "loopq_quant_act_per_token": ([_P, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _P, _P, _Z, _P], _I),
@@ -241,6 +243,20 @@ def loopq_gemm_codes(a_codes, a_scales, w_codes, w_scales, group_w: int, N: int,
 def loopq_export_weights(w_codes, w_scales, K: int, N: int, group_w: int, codes, scales, stream=None):
     _check(load().loopq_export_weights(_ptr(w_codes), _ptr(w_scales), K, N, group_w, _ptr(codes),
                                        _ptr(scales), _stream(stream)), "loopq_export_weights")
+
+
+def loopq_export_weight_codes(w_codes, K: int, N: int, group_w: int, codes, stream=None):
+    _check(load().loopq_export_weight_codes(_ptr(w_codes), K, N, group_w, _ptr(codes), _stream(stream)),
+           "loopq_export_weight_codes")
+
+
+def loopq_export_act_codes(workspace, op: int, T: int, M: int, K: int, N: int, bits_a: int, schedule: int,
+                           codes, scales, stream=None):
+    """The codes [T*M][K] int8 and steps [T*M][K/32] fp32 the last forward call
+    of this op and shape left in ``workspace``."""
+    _check(load().loopq_export_act_codes(_ptr(workspace), workspace.numel() * workspace.element_size(), op, T,
+                                         M, K, N, bits_a, schedule, _ptr(codes), _ptr(scales), _stream(stream)),
+           "loopq_export_act_codes")
 
 
 def loopq_group_dots(a_codes, w_codes, N: int, dots, workspace, bits_a: int = 4, stream=None):

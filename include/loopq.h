@@ -14,8 +14,8 @@
  *     steps) and lq3 (one Kronecker transform shared by all loops, folded
  *     into the weights through its exact inverse transpose, unquantized).
  *   - "LoopQ 4-bit quantization of Ouro-1.4B -- raw artifacts", "The arms":
- *     random orthogonal Kronecker transforms; Ouro-1.4B runs 24 layers 4 times
- *     per token with the same weights.
+ *     random orthogonal Kronecker transforms; Ouro-1.4B applies one set of 24
+ *     layers four times to every token.
  *   - "Quantizing Looped Transformers: Feedback Exposure and Calibration
  *     Blindness", Figure 3 and Table 6: grouped INT4 weights with g = 128.
  *
@@ -176,10 +176,8 @@ int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, in
  * xt_out (nullable) receives x~.  Arguments and errors as loopq_quant_act.
  * With a transform, each row's absmax is taken over the x~ row the transform
  * kernel holds on chip (one launch; x~ reaches memory only through xt_out).
- * Workspace: with a transform and xt_out NULL, a workspace of
- * loopq_workspace_bytes(LOOPQ_OP_QUANT_PER_TOKEN, 0, M, K, 0, 0, ...) bytes,
- * 256-byte aligned, is still required (reserved: this version writes none of
- * it); otherwise workspace may be NULL. */
+ * The call needs no workspace: workspace and workspace_bytes are accepted and
+ * ignored (loopq_workspace_bytes(LOOPQ_OP_QUANT_PER_TOKEN, ...) returns 0). */
 int32_t loopq_quant_act_per_token(const void* x, int32_t dtype, int32_t M, int32_t K,
                                   const float* P1, int32_t n1, const float* P2, int32_t n2,
                                   float clip, int32_t bits_a, int8_t* codes, float* scales,
@@ -203,8 +201,9 @@ int32_t loopq_looped_forward_per_token(const void* x, int32_t dtype, int32_t T, 
                                        void* stream);
 
 /* a6 -- the loop: the same packed weights applied at every loop t with the
- * loop's own clip.  Page: "LoopQ 4-bit quantization of Ouro-1.4B" (24 layers
- * run 4 times per token); LAS, one clip per module and loop.
+ * loop's own clip.  Page: "LoopQ 4-bit quantization of Ouro-1.4B -- raw
+ * artifacts" (each token passes through the same 24 layers four times); LAS,
+ * one clip per module and loop.
  * x [T][M][K], y [T][M][N]; clips_host [T] (host memory, read before return).
  * schedule: a loopq_schedule.  LOOP_SEQUENTIAL quantizes and multiplies loop
  * by loop, pipelined: the quantizer of loop t + 1 runs on an auxiliary stream
@@ -229,9 +228,10 @@ int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
 
 /* a6 with loop-dependent pieces.  Loop t uses weight/transform set
  * sets_host[t] (0 <= set < nsets) and activation bit width bits_host[t] (4 or 8).
- * Pages: SLT ("paper_specification.yaml", loopq_components.slt: selected groups
- * receive loop-dependent transforms and weights; the others keep the shared
- * ones, i.e. one set for every loop) and a loop-wise activation precision
+ * Pages: SLT ("paper_specification.yaml", loopq_components.slt, Section 4.2,
+ * Eqs. (5)-(6): the transform and weight groups that SLT picks vary with the
+ * loop, the rest stay shared, i.e. one set for every loop) and a loop-wise
+ * activation precision
  * allocation ("Quantisation errors can keep returning inside a looped model",
  * "Three components address three sources of mismatch").  x, y, clips_host and
  * the other arguments as for loopq_looped_forward.  Set s has factors
@@ -319,6 +319,30 @@ int32_t loopq_hessian_accumulate(const float* xt, int32_t rows, int32_t K, float
  * (raw binary16 bits) from the packed layout. */
 int32_t loopq_export_weights(const void* w_codes, const void* w_scales, int32_t K, int32_t N,
                              int32_t group_w, int8_t* codes, uint16_t* scales, void* stream);
+
+/* Test export: canonical weight codes int8 [N][K] from the packed layout
+ * (loopq_export_weights without the steps). */
+int32_t loopq_export_weight_codes(const void* w_codes, int32_t K, int32_t N, int32_t group_w, int8_t* codes,
+                                  void* stream);
+
+/* Test export: the activation codes and steps that the last forward call on
+ * `workspace` (the same op, T, M, K, N, bits_a and schedule) left there and its
+ * product consumed, in canonical form: codes int8 [T*M][K], steps fp32
+ * [T*M][K/32] (16-byte aligned codes, 4-byte aligned steps).  Page: Eq.(4)
+ * (lq1_quantization) -- these are the codes and steps to compare with it.
+ *   op LOOPQ_OP_LOOPED_FORWARD (loopq_looped_forward, either schedule),
+ *      LOOPQ_OP_LINEAR (loopq_w4a4_linear, T = 1),
+ *      LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN (loopq_looped_forward_per_token),
+ *      LOOPQ_OP_RECURRENT_ADAPTER (loopq_recurrent_adapter, T = 1 here: the
+ *      last loop's codes; K is ignored, 2N is used).
+ * The GEMM paths keep W4A4 codes as e2m3 fp6 MFMA operands and W4A8 codes as
+ * int8 tiles; both are decoded here (an fp6 field that is not a code -7..7
+ * comes back as -128).  The few-row path (at most 16 rows per launch) writes
+ * the codes it formed on chip to the workspace in canonical form.
+ * Workspace as the forward call sized it (loopq_workspace_bytes of the op). */
+int32_t loopq_export_act_codes(const void* workspace, size_t workspace_bytes, int32_t op, int32_t T, int32_t M,
+                               int32_t K, int32_t N, int32_t bits_a, int32_t schedule, int8_t* codes,
+                               float* scales, void* stream);
 
 /* Test export: the exact int32 per-group dots d[m][n][j] = sum_{k in group j}
  * a_codes[m][k] * w[n][k], computed by the MFMA path of the bits_a kernel

@@ -12,8 +12,8 @@ the pages the method is described on):
 * "LoopQ 4-bit quantization of Ouro-1.4B -- raw artifacts" (README of a LoopQ
   reproduction): sections "The arms" and "Protocol" -- RTN with activations in
   groups of 32, random orthogonal Kronecker transforms with LAS clip 1.0 for
-  the untrained LoopQ arm, 24 layers run 4 times per token, quantization
-  simulated as quantize-dequantize.
+  the untrained LoopQ arm, one set of 24 layers applied four times to every
+  token, quantization simulated as quantize-dequantize.
 * "paper_specification.yaml" of the same reproduction: ``lq1_quantization``
   (Eq.(4) ``Q_a(x; c) = c * clip(round(x / c), q_min, q_max)``, RTN, W4 with A4
   or A8, group-wise, group size 32), ``loopq_components`` (shared transformed
@@ -327,9 +327,9 @@ def looped_forward_sets(xs, factor_sets, clips, bits, weight_sets, group_w: int,
     """The loop with loop-dependent pieces: loop t uses transform and weights of
     set ``sets[t]`` and activation bit width ``bits[t]``.
 
-    SLT ("paper_specification.yaml", ``loopq_components.slt``): selected groups
-    receive loop-dependent transforms and weights, the others keep the shared
-    ones.  A per-loop activation bit width is the output of a loop-wise
+    SLT ("paper_specification.yaml", ``loopq_components.slt``, Section 4.2,
+    Eqs. (5)-(6)): the transform and weight groups SLT picks vary with the loop,
+    the rest stay shared.  A per-loop activation bit width is the output of a loop-wise
     precision allocation ("Quantisation errors can keep returning inside a
     looped model", "Three components address three sources of mismatch").
     ``factor_sets`` is a list of ``(P1, P2)`` (or ``(None, None)``),

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
         assert n in loopq.SIGNATURES, n
@@ -192,10 +192,10 @@ def test_hessian_workspace_and_host_rejections(lib):
 
 def test_per_token_entries_reject_on_host(lib):
     qop, lop = loopq.LOOPQ_OP_QUANT_PER_TOKEN, loopq.LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN
-    assert loopq.loopq_workspace_bytes(qop, 0, 100, 2048, 0, 0) == 100 * 2048 * 4
-    # the loop: the group path's activation buffers for T*M rows plus their x~ staging
+    assert loopq.loopq_workspace_bytes(qop, 0, 100, 2048, 0, 0) == 0  # the call needs none
+    # the loop: the group path's activation buffers for T*M rows
     assert loopq.loopq_workspace_bytes(lop, 3, 100, 2048, 512, 4) == \
-        loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LINEAR, 1, 300, 2048, 512, 4) + 300 * 2048 * 4
+        loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LINEAR, 1, 300, 2048, 512, 4)
     for args, want in (((lop, 3, 100, 2048, 512, 5), loopq.LOOPQ_ERR_UNSUPPORTED),
                        ((lop, 65, 1, 2048, 512, 4), loopq.LOOPQ_ERR_UNSUPPORTED),
                        ((lop, 0, 1, 2048, 512, 4), loopq.LOOPQ_ERR_INVALID_ARG)):
@@ -209,10 +209,10 @@ def test_per_token_entries_reject_on_host(lib):
     assert q(FAKE, 0, 4, 256, None, 0, None, 0, 1.0, 6, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_UNSUPPORTED
     assert q(FAKE, 0, 4, 256, None, 0, None, 0, 1.0, 4, None, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_INVALID_ARG
     assert q(FAKE, 0, 4, 256, None, 0, None, 0, 1.0, 4, FAKE + 2, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_ALIGNMENT
-    # a transform with no x~ output needs the staging workspace
-    assert q(FAKE, 0, 4, 256, FAKE, 16, FAKE, 16, 1.0, 4, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_WORKSPACE
-    assert q(FAKE, 0, 4, 256, FAKE, 16, FAKE, 16, 1.0, 4, FAKE, FAKE, None, FAKE, 4 * 256 * 4 - 1, None) == \
-        loopq.LOOPQ_ERR_WORKSPACE
+    # a transform with no x~ output needs no workspace either: only the
+    # factor checks run (n1 * n2 != K is rejected before any launch)
+    assert q(FAKE, 0, 4, 256, FAKE, 16, FAKE, 8, 1.0, 4, FAKE, FAKE, None, None, 0, None) == \
+        loopq.LOOPQ_ERR_UNSUPPORTED
     assert q(FAKE, 0, 4, 256, FAKE, 16, FAKE, 8, 1.0, 4, FAKE, FAKE, None, None, 0, None) == loopq.LOOPQ_ERR_UNSUPPORTED
     assert q(FAKE, 0, 0, 256, None, 0, None, 0, 1.0, 4, None, None, None, None, 0, None) == loopq.LOOPQ_OK
     arr = lambda vals: ctypes.cast((ctypes.c_float * len(vals))(*vals), ctypes.c_void_p)
@@ -250,3 +250,26 @@ def test_recurrent_adapter_rejects_on_host(lib):
     assert call(s0=FAKE + 4) == loopq.LOOPQ_ERR_ALIGNMENT
     assert call(ws=16) == loopq.LOOPQ_ERR_WORKSPACE
     assert call(M=0, e=None, s0=None) == loopq.LOOPQ_OK
+
+
+def test_export_act_codes_rejects_on_host(lib):
+    x = lambda *a: _raw(lib, "loopq_export_act_codes", *a)
+    op = loopq.LOOPQ_OP_LOOPED_FORWARD
+    ws = loopq.loopq_workspace_bytes(op, 4, 64, 2048, 512, 4)
+    # workspace, bytes, op, T, M, K, N, bits, schedule, codes, scales, stream
+    assert x(FAKE, ws, 99, 4, 64, 2048, 512, 4, 0, FAKE, FAKE, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert x(FAKE, ws, loopq.LOOPQ_OP_LINEAR, 2, 64, 2048, 512, 4, 0, FAKE, FAKE, None) == \
+        loopq.LOOPQ_ERR_INVALID_ARG
+    assert x(FAKE, ws, op, 4, 64, 2048, 512, 6, 0, FAKE, FAKE, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert x(FAKE, ws, op, 4, 64, 2040, 512, 4, 0, FAKE, FAKE, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert x(FAKE, ws, op, 4, 64, 2048, 512, 4, 3, FAKE, FAKE, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert x(FAKE, ws - 1, op, 4, 64, 2048, 512, 4, 0, FAKE, FAKE, None) == loopq.LOOPQ_ERR_WORKSPACE
+    assert x(FAKE + 16, ws, op, 4, 64, 2048, 512, 4, 0, FAKE, FAKE, None) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert x(FAKE, ws, op, 4, 64, 2048, 512, 4, 0, None, FAKE, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert x(FAKE, ws, op, 4, 64, 2048, 512, 4, 0, FAKE, FAKE + 2, None) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert x(None, 0, op, 4, 0, 2048, 512, 4, 0, None, None, None) == loopq.LOOPQ_OK  # no rows
+    w = lambda *a: _raw(lib, "loopq_export_weight_codes", *a)
+    assert w(FAKE, 2040, 64, 32, FAKE, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert w(FAKE, 2048, 64, 64, FAKE, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert w(None, 2048, 64, 32, FAKE, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert w(FAKE + 8, 2048, 64, 32, FAKE, None) == loopq.LOOPQ_ERR_ALIGNMENT

@@ -45,12 +45,8 @@ def quant_token_gpu(lq, xdev, P1, P2, clip, bits, with_xt):
     codes = torch.empty((M, K), dtype=torch.int8, device="cuda")
     scales = torch.empty((M, K // 32), dtype=torch.float32, device="cuda")
     xt = torch.empty((M, K), dtype=torch.float32, device="cuda") if with_xt else None
-    ws = None
-    if P1 is not None and not with_xt:
-        ws = torch.empty(lq.loopq_workspace_bytes(lq.LOOPQ_OP_QUANT_PER_TOKEN, 0, M, K, 0, 0),
-                         dtype=torch.uint8, device="cuda")
     lq.loopq_quant_act_per_token(xdev, None if P1 is None else dev(P1), None if P2 is None else dev(P2),
-                                 clip, bits, codes, scales, xt, ws)
+                                 clip, bits, codes, scales, xt)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), scales.cpu().numpy(), (xt.cpu().numpy() if with_xt else None)
 
@@ -87,7 +83,7 @@ def test_quant_per_token_transformed(lq, n1, n2):
     qa, sa = oracle.quant_act(xt, 0.7, 4, group=K)
     np.testing.assert_array_equal(codes, qa.astype(np.int8))
     np.testing.assert_array_equal(scales, np.repeat(sa, K // 32, axis=1))
-    # x~ staged in the workspace instead of xt_out: the same codes and steps
+    # without the x~ output (x~ then stays on chip): the same codes and steps
     codes2, scales2, _ = quant_token_gpu(lq, xdev, P1, P2, 0.7, 4, False)
     np.testing.assert_array_equal(codes2, codes)
     np.testing.assert_array_equal(scales2, scales)
