@@ -45,10 +45,10 @@ def inputs(T, M, K, dtype, key, zero_rows=(), hot=None):
     """[T][M][K] activations (device tensor, fp32 host copy) with outlier
     channels, some all-zero rows and optionally one huge element per row."""
     x = synth.with_outliers(synth.gaussian((T, M, K), 300, key, T, M, K), max(1, K // 100), 20.0, 301, key)
-    for t, m in zero_rows:
-        x[t, m] = 0.0
     if hot is not None:
         x[:, :, hot] = 500.0
+    for t, m in zero_rows:
+        x[t, m] = 0.0
     if dtype == "bf16":
         bits16, x32 = synth.round_to_bf16(x)
         return torch.from_numpy(bits16.view(np.int16)).cuda().view(torch.bfloat16), x32
