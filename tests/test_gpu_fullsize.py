@@ -67,7 +67,10 @@ def sample_loops(T):
     return sorted({0, 1, T // 2, T - 1})
 
 
-def run_case(lq, wl, act, tile_rows=None):
+def run_case(lq, wl, act, tile_rows=None, per_loop_calls=False):
+    """per_loop_calls: one loopq_looped_forward call of M rows per loop (the
+    launch configuration of the headline stack), else one weight-stationary
+    call over all T * M rows."""
     lins = groups_by_input(wl)[act]
     K = lins[0].K
     gw = wl.group_w
@@ -102,11 +105,17 @@ def run_case(lq, wl, act, tile_rows=None):
     del bits
 
     y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
-    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, wl.bits_a)
     tP1 = dev(P1) if P1 is not None else None
     tP2 = dev(P2) if P2 is not None else None
-    lq.loopq_looped_forward(x, tP1, tP2, clips, wl.bits_a, codes, scales, gw, N, y,
-                            lq.LOOPQ_SCHED_AUTO, ws)
+    if per_loop_calls:
+        ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, 1, M, K, N, wl.bits_a)
+        for t in range(T):
+            lq.loopq_looped_forward(x[t:t + 1], tP1, tP2, [clips[t]], wl.bits_a, codes, scales, gw, N, y[t:t + 1],
+                                    lq.LOOPQ_SCHED_WEIGHT_STATIONARY, ws)
+    else:
+        ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, wl.bits_a)
+        lq.loopq_looped_forward(x, tP1, tP2, clips, wl.bits_a, codes, scales, gw, N, y,
+                                lq.LOOPQ_SCHED_AUTO, ws)
     torch.cuda.synchronize()
     del ws
 
@@ -168,6 +177,19 @@ def test_fullsize_huginn(lq, act):
 @pytest.mark.parametrize("act", OURO_INPUTS)
 def test_fullsize_large_prefill(lq, act):
     run_case(lq, synth.large_prefill_workload(T=4), act)
+
+
+@pytest.mark.parametrize("act", OURO_INPUTS)
+def test_fullsize_large_prefill_per_loop_calls(lq, act):
+    """The headline stack's launch configuration: one call of M = 8192 rows
+    per loop (transform + quantizer launch, GEMM launch)."""
+    run_case(lq, synth.large_prefill_workload(T=4), act, per_loop_calls=True)
+
+
+@pytest.mark.parametrize("act", ["qkv_in", "down_in"])
+def test_fullsize_large_prefill_T8(lq, act):
+    """T = 8: all 65,536 rows of an input in one weight-stationary launch."""
+    run_case(lq, synth.large_prefill_workload(T=8), act)
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
