@@ -509,6 +509,41 @@ hipError_t per_token_quant(QuantArgs a, hipStream_t s) {
   return launch_quant_token(a, s);
 }
 
+// Host-side checks of loopq_looped_forward, before any HIP call.  Fills the
+// clip table; *empty is set (with LOOPQ_OK) when there are no rows to run.
+int32_t check_forward(const void* x, int dtype, int T, int M, int K, int N, const float* P1, int n1,
+                      const float* P2, int n2, const float* clips_host, int bits_a, const void* w_codes,
+                      const void* w_scales, int group_w, const float* y, int schedule, ClipTable* clips,
+                      bool* empty) {
+  *empty = false;
+  if (T <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (T > LOOPQ_MAX_LOOPS) return LOOPQ_ERR_UNSUPPORTED;
+  if ((int64_t)T * M > (int64_t)1 << 30) return LOOPQ_ERR_UNSUPPORTED;
+  int32_t st = check_act(x, dtype, M, K, bits_a);
+  if (st != LOOPQ_OK) return st;
+  st = check_weights(K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  st = check_gemm_extent((int64_t)T * padded_rows(M), K, N, group_w);
+  if (st != LOOPQ_OK) return st;
+  st = check_transform(K, P1, n1, P2, n2);
+  if (st != LOOPQ_OK) return st;
+  if (!clips_host) return LOOPQ_ERR_INVALID_ARG;
+  memset(clips, 0, sizeof(*clips));
+  for (int t = 0; t < T; ++t) {
+    if (!clip_ok(clips_host[t])) return LOOPQ_ERR_INVALID_ARG;
+    clips->c[t] = clips_host[t];
+  }
+  if (schedule < LOOPQ_SCHED_AUTO || schedule > LOOPQ_SCHED_WEIGHT_STATIONARY)
+    return LOOPQ_ERR_INVALID_ARG;
+  if (M == 0) {
+    *empty = true;
+    return LOOPQ_OK;
+  }
+  if (!w_codes || !w_scales || !y) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(y, 4)) return LOOPQ_ERR_ALIGNMENT;
+  return LOOPQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -665,29 +700,11 @@ int32_t loopq_looped_forward(const void* x, int32_t dtype, int32_t T, int32_t M,
                              const float* clips_host, int32_t bits_a, const void* w_codes,
                              const void* w_scales, int32_t group_w, float* y, int32_t schedule,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (T <= 0) return LOOPQ_ERR_INVALID_ARG;
-  if (T > LOOPQ_MAX_LOOPS) return LOOPQ_ERR_UNSUPPORTED;
-  if ((int64_t)T * M > (int64_t)1 << 30) return LOOPQ_ERR_UNSUPPORTED;
-  int32_t st = check_act(x, dtype, M, K, bits_a);
-  if (st != LOOPQ_OK) return st;
-  st = check_weights(K, N, group_w);
-  if (st != LOOPQ_OK) return st;
-  st = check_gemm_extent((int64_t)T * padded_rows(M), K, N, group_w);
-  if (st != LOOPQ_OK) return st;
-  st = check_transform(K, P1, n1, P2, n2);
-  if (st != LOOPQ_OK) return st;
-  if (!clips_host) return LOOPQ_ERR_INVALID_ARG;
   ClipTable clips;
-  memset(&clips, 0, sizeof(clips));
-  for (int t = 0; t < T; ++t) {
-    if (!clip_ok(clips_host[t])) return LOOPQ_ERR_INVALID_ARG;
-    clips.c[t] = clips_host[t];
-  }
-  if (schedule < LOOPQ_SCHED_AUTO || schedule > LOOPQ_SCHED_WEIGHT_STATIONARY)
-    return LOOPQ_ERR_INVALID_ARG;
-  if (M == 0) return LOOPQ_OK;
-  if (!w_codes || !w_scales || !y) return LOOPQ_ERR_INVALID_ARG;
-  if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(y, 4)) return LOOPQ_ERR_ALIGNMENT;
+  bool empty = false;
+  int32_t st = check_forward(x, dtype, T, M, K, N, P1, n1, P2, n2, clips_host, bits_a, w_codes, w_scales,
+                             group_w, y, schedule, &clips, &empty);
+  if (st != LOOPQ_OK || empty) return st;
   size_t need = 0;
   loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, bits_a, &need);
   if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
