@@ -47,11 +47,16 @@ hipEvent_t pooled_event() {
   return e;
 }
 
+// Set while loopq_w4a4_linear_noalloc runs on this thread: its launches take
+// no timing records (a record may create HIP events, which allocate).
+thread_local bool t_no_alloc = false;
+
 struct TimingScope {
   bool on = false;
   TimingRec rec{};
   hipStream_t s;
   TimingScope(int kid, hipStream_t stream) : s(stream) {
+    if (t_no_alloc) return;
     std::lock_guard<std::mutex> lk(g_timing_mu);
     if (!g_timing_on) return;
     rec.kid = kid;
@@ -509,6 +514,35 @@ hipError_t per_token_quant(QuantArgs a, hipStream_t s) {
   return launch_quant_token(a, s);
 }
 
+// ---------------------------------------------------------------------------
+// Fixed scratch memory of loopq_w4a4_linear_noalloc, for callers that cannot
+// allocate.  Every device the library runs on holds its own copy of the
+// array until the process ends.  In host code the array's name is not a
+// device address: the address is taken once per device with
+// hipGetSymbolAddress (that device current) and only that address is used.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // Host-side checks of loopq_looped_forward, before any HIP call.  Fills the
 // clip table; *empty is set (with LOOPQ_OK) when there are no rows to run.
 int32_t check_forward(const void* x, int dtype, int T, int M, int K, int N, const float* P1, int n1,
@@ -795,6 +829,31 @@ int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, in
                               w_scales, group_w, y, LOOPQ_SCHED_WEIGHT_STATIONARY, workspace,
                               workspace_bytes, stream);
 }
+
+int32_t loopq_w4a4_linear_noalloc(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,
+                                  const float* P1, int32_t n1, const float* P2, int32_t n2, float clip,
+                                  int32_t bits_a, const void* w_codes, const void* w_scales, int32_t group_w,
+                                  float* y, void* stream) {
+  ClipTable clips;
+  bool empty = false;
+  int32_t st = check_forward(x, dtype, 1, M, K, N, P1, n1, P2, n2, &clip, bits_a, w_codes, w_scales, group_w, y,
+                             LOOPQ_SCHED_WEIGHT_STATIONARY, &clips, &empty);
+  if (st != LOOPQ_OK || empty) return st;
+  size_t need = 0;
+  st = loopq_workspace_bytes(LOOPQ_OP_LINEAR, 1, M, K, N, bits_a, &need);
+  if (st != LOOPQ_OK) return st;
+  if (need > kScratchBytes) return LOOPQ_ERR_WORKSPACE;  // the call needs more than the fixed scratch
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return LOOPQ_ERR_HIP;
+  t_no_alloc = true;
+  // the kernels and workspace layout of loopq_w4a4_linear, on the scratch
+  st = linear_core(x, dtype, M, K, N, P1, n1, P2, n2, clips, M, bits_a, w_codes, w_scales, group_w, y, ws, 1, M,
+                   as_stream(stream));
+  t_no_alloc = false;
+  return st;
+}
+
+size_t loopq_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int32_t loopq_gemm_codes(const int8_t* a_codes, const float* a_scales, int32_t M, int32_t K,
                          int32_t N, const void* w_codes, const void* w_scales, int32_t group_w,

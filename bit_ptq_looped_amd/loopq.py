@@ -51,6 +51,8 @@ SIGNATURES = {
     "loopq_looped_forward_ex": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _I, _P, _P, _P,
                                  _P, _P, _Z, _P], _I),
     "loopq_gemm_codes": ([_P, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _Z, _P], _I),
+    "loopq_w4a4_linear_noalloc": ([_P, _I, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _I, _P, _P], _I),
+    "loopq_noalloc_scratch_bytes": ([], _Z),
     "loopq_export_weights": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "loopq_group_dots": ([_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
     "loopq_export_weight_codes": ([_P, _I, _I, _I, _P, _P], _I),
@@ -188,6 +190,20 @@ def loopq_w4a4_linear(x, P1, P2, clip: float, bits_a: int, w_codes, w_scales, gr
                                     bits_a, _ptr(w_codes), _ptr(w_scales), group_w, _ptr(y),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "loopq_w4a4_linear")
+
+
+def loopq_w4a4_linear_noalloc(x, P1, P2, clip: float, bits_a: int, w_codes, w_scales, group_w: int, N: int,
+                              y, stream=None):
+    """loopq_w4a4_linear on the library's fixed scratch (no workspace)."""
+    M, K = x.shape
+    p1, n1, p2, n2 = _factor_args(P1, P2)
+    _check(load().loopq_w4a4_linear_noalloc(_ptr(x), _dtype_code(x), M, K, N, p1, n1, p2, n2, float(clip), bits_a,
+                                            _ptr(w_codes), _ptr(w_scales), group_w, _ptr(y), _stream(stream)),
+           "loopq_w4a4_linear_noalloc")
+
+
+def loopq_noalloc_scratch_bytes() -> int:
+    return int(load().loopq_noalloc_scratch_bytes())
 
 
 def loopq_looped_forward(x, P1, P2, clips: Sequence[float], bits_a: int, w_codes, w_scales,

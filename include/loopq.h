@@ -165,6 +165,28 @@ int32_t loopq_w4a4_linear(const void* x, int32_t dtype, int32_t M, int32_t K, in
                           const void* w_codes, const void* w_scales, int32_t group_w,
                           float* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* loopq_w4a4_linear without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It runs the kernels of
+ * loopq_w4a4_linear on a fixed scratch array the library holds on each
+ * device it runs on (loopq_noalloc_scratch_bytes() bytes, 64 MiB, kept
+ * until the process ends) and calls no allocating routine; the timing
+ * hooks record nothing for it.  The same arguments, errors and results as
+ * loopq_w4a4_linear (bitwise: same kernels, same layout); a call whose
+ * loopq_workspace_bytes(LOOPQ_OP_LINEAR, 1, M, K, N, bits_a) exceeds the
+ * scratch returns LOOPQ_ERR_WORKSPACE before any launch (e.g. M * K above
+ * roughly 40 M elements at N = K).  Every call on one device shares that
+ * device's scratch and leaves the last call's contents there: calls that
+ * overlap on one device (different streams or threads) race and must be
+ * ordered by the caller. */
+int32_t loopq_w4a4_linear_noalloc(const void* x, int32_t dtype, int32_t M, int32_t K, int32_t N,
+                                  const float* P1, int32_t n1, const float* P2, int32_t n2, float clip,
+                                  int32_t bits_a, const void* w_codes, const void* w_scales, int32_t group_w,
+                                  float* y, void* stream);
+
+/* Bytes of the fixed scratch of loopq_w4a4_linear_noalloc (host only). */
+size_t loopq_noalloc_scratch_bytes(void);
+
 /* Per-token activation steps: the same RTN with one step per token.
  * Page: "LoopQ 4-bit quantization of Ouro-1.4B -- raw artifacts", "The arms"
  * (rtn_w4a4_per_token: plain RTN, one step per token, a common W4A4 reference).  Eq.(4)

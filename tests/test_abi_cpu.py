@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "loopq.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int32_t|const char\*)\s+(loopq_\w+)\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:int32_t|size_t|const char\*)\s+(loopq_\w+)\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
         assert n in loopq.SIGNATURES, n
@@ -273,3 +273,23 @@ def test_export_act_codes_rejects_on_host(lib):
     assert w(FAKE, 2048, 64, 64, FAKE, None) == loopq.LOOPQ_ERR_UNSUPPORTED
     assert w(None, 2048, 64, 32, FAKE, None) == loopq.LOOPQ_ERR_INVALID_ARG
     assert w(FAKE + 8, 2048, 64, 32, FAKE, None) == loopq.LOOPQ_ERR_ALIGNMENT
+
+
+def test_noalloc_linear_rejects_on_host(lib):
+    """Argument errors and a call larger than the fixed scratch return before
+    any HIP call (this runs without a GPU)."""
+    f = lambda *a: _raw(lib, "loopq_w4a4_linear_noalloc", *a)
+    assert loopq.loopq_noalloc_scratch_bytes() == 64 << 20
+    # x, dtype, M, K, N, P1, n1, P2, n2, clip, bits, w_codes, w_scales, group_w, y, stream
+    assert f(FAKE, 0, 4, 48, 64, None, 0, None, 0, 1.0, 4, FAKE, FAKE, 32, FAKE, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert f(FAKE, 0, 4, 256, 64, None, 0, None, 0, 0.0, 4, FAKE, FAKE, 32, FAKE, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, 4, 256, 64, None, 0, None, 0, 1.0, 6, FAKE, FAKE, 32, FAKE, None) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert f(FAKE, 0, 4, 256, 64, None, 0, None, 0, 1.0, 4, None, FAKE, 32, FAKE, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, 4, 256, 64, None, 0, None, 0, 1.0, 4, FAKE + 8, FAKE, 32, FAKE, None) == \
+        loopq.LOOPQ_ERR_ALIGNMENT
+    assert f(None, 0, 0, 256, 64, None, 0, None, 0, 1.0, 4, None, None, 32, None, None) == loopq.LOOPQ_OK  # no rows
+    # 32768 rows at K = N = 2048 need more than 64 MiB of scratch
+    need = loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LINEAR, 1, 32768, 2048, 2048, 4)
+    assert need > 64 << 20
+    assert f(FAKE, 0, 32768, 2048, 2048, None, 0, None, 0, 1.0, 4, FAKE, FAKE, 32, FAKE, None) == \
+        loopq.LOOPQ_ERR_WORKSPACE
