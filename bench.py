@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--sweep-steps", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="token rows in the oracle sample")
+    p.add_argument("--no-stack", action="store_true",
+                   help="skip the headline stack (development runs of the secondary lines; value is then null)")
     p.add_argument("--no-block", action="store_true", help="skip the Ouro-1.4B-like block lines")
     p.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     p.add_argument("--no-loop-dependent", action="store_true",
@@ -967,6 +969,11 @@ def main():
             print(f"profiled {args.profile_steps} steps", flush=True)
         return
 
+    if args.no_stack:
+        out = {"metric": METRIC, "value": None, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "note": "headline stack skipped (--no-stack)"}
+        secondary(lq, synth, torch, args, out, synth.large_prefill_workload(T=1, M=args.M, layers=args.layers))
+        return
     print(f"bench: headline stack M={args.M} layers={args.layers} T={args.T}", file=sys.stderr, flush=True)
     st = stack_bench(lq, synth, torch, args)
     T, M, L = args.T, args.M, args.layers
@@ -1012,6 +1019,10 @@ def main():
     stack_wl = st["wl"]
     del st
     torch.cuda.empty_cache()
+    secondary(lq, synth, torch, args, out, stack_wl)
+
+
+def secondary(lq, synth, torch, args, out, stack_wl):
     print("bench: secondary lines", file=sys.stderr, flush=True)
 
     if not args.no_block:

@@ -42,8 +42,20 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kSlice = 64;        // groups per weight slice
-constexpr int kPer = kSlice / 8;  // groups of a slice per thread
+// A work-group owns CPW consecutive output columns (8, 16 or 32, so that a
+// call has about as many work-groups as the chip has CUs) over all of K.
+// Each thread holds 128 bytes of packed weights per slice in flight: in the
+// VALU form thread (column c, lane group gq) takes groups gq + GL i (i < 8)
+// of a slice; in the MFMA form a wave takes groups wave + 4 i of a slice for
+// all 16-column halves of the work-group's columns.
+constexpr int kPer = 8;  // groups of a slice per thread (VALU form)
+template <int CPW>
+struct Cols {
+  static constexpr int GL = 256 / CPW;             // lane groups per column (VALU form)
+  static constexpr int kSlice = 2048 / CPW;        // groups per weight slice
+  static constexpr int NH = CPW >= 16 ? CPW / 16 : 1;  // 16-column halves (MFMA form)
+  static constexpr int kMPer = kSlice / 4;         // groups per wave and slice (MFMA form)
+};
 constexpr int kLdsBudget = 160 * 1024;
 
 struct DecodeArgs {
@@ -99,7 +111,7 @@ __device__ __forceinline__ v4i unpack16(uint2 p) {
   return r;
 }
 
-// The weights of one slice held by one thread: groups sl * kSlice + gq + 8 i.
+// The weights of one slice held by one thread: groups sl * kSlice + gq + GL i.
 struct WSlice {
   uint2 lo[kPer], hi[kPer];
   float s[kPer];
@@ -107,34 +119,38 @@ struct WSlice {
 
 // Load a thread's part of slice `sl`; groups past Ga re-read group Ga - 1
 // and are not used.
-template <int MODE>
+template <int CPW, int MODE>
 __device__ __forceinline__ void load_slice(const DecodeArgs& g, int cb, int sl, int c, int gq,
                                            WSlice& ws) {
+  using C = Cols<CPW>;
   const int Ga = g.K >> 5;
   const int Gw = (Ga + (1 << g.gshift) - 1) >> g.gshift;
+  const int n = cb * CPW + c;  // padded column: block n / 32, column n % 32 of it
+  const int nb = n >> 5, cc = n & 31;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int j = min(sl * kSlice + gq + 8 * i, Ga - 1);
-    const uint8_t* blk = g.w + ((int64_t)cb * Ga + j) * kBlockBytes + c * 8;
+    const int j = min(sl * C::kSlice + gq + C::GL * i, Ga - 1);
+    const uint8_t* blk = g.w + ((int64_t)nb * Ga + j) * kBlockBytes + cc * 8;
     ws.lo[i] = *reinterpret_cast<const uint2*>(blk);        // K 32 j + 0..15
     ws.hi[i] = *reinterpret_cast<const uint2*>(blk + 256);  // K 32 j + 16..31
-    ws.s[i] = MODE == 0 ? __half2float(g.sw[((int64_t)cb * Gw + (j >> g.gshift)) * 32 + step_slot(c)]) : 0.0f;
+    ws.s[i] = MODE == 0 ? __half2float(g.sw[((int64_t)nb * Gw + (j >> g.gshift)) * 32 + step_slot(cc)]) : 0.0f;
   }
 }
 
 // Dots of the thread's groups of slice `sl` that lie in [jlo, jhi) with every
 // row's codes: codes of group j of row m at sA + m * a_ld + (j - a_j0) * 32
 // (bytes), its step at sS[m * s_ld + j - a_j0].
-template <int RM, int MODE>
+template <int CPW, int RM, int MODE>
 __device__ __forceinline__ void dot_slice(const DecodeArgs& g, int cb, int sl, int c, int gq,
                                           const WSlice& ws, int jlo, int jhi, const int8_t* sA,
                                           int a_ld, int a_j0, const float* sS, int s_ld,
                                           float (&acc)[RM]) {
+  using C = Cols<CPW>;
   const int Ga = g.K >> 5;
-  const int n = cb * 32 + c;
+  const int n = cb * CPW + c;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int j = sl * kSlice + gq + 8 * i;
+    const int j = sl * C::kSlice + gq + C::GL * i;
     if (j >= jlo && j < jhi && j < Ga) {
       const v4i w0 = unpack16(ws.lo[i]);
       const v4i w1 = unpack16(ws.hi[i]);
@@ -169,28 +185,31 @@ __device__ __forceinline__ void dot_slice(const DecodeArgs& g, int cb, int sl, i
 // the block; its nibbles for one (half, group) are one dword of the packed
 // layout (K-half (l / 16) / 2, run (l / 16) % 2).
 
-// The weights of one slice held by one lane: groups sl * kSlice + wave + 4 i.
-constexpr int kMPer = kSlice / 4;
+// The weights of one slice held by one lane: groups sl * kSlice + wave + 4 i,
+// for each 16-column half of the work-group's columns.
+template <int CPW>
 struct MSlice {
-  uint32_t w[kMPer][2];  // packed nibbles, [group][column half]
-  float s[kMPer][2];     // fp16 steps of the lane's column
+  uint32_t w[Cols<CPW>::kMPer][Cols<CPW>::NH];  // packed nibbles, [group][column half]
+  float s[Cols<CPW>::kMPer][Cols<CPW>::NH];     // fp16 steps of the lane's column
 };
 
-template <int MODE>
-__device__ __forceinline__ void load_mslice(const DecodeArgs& g, int cb, int sl, MSlice& ms) {
+template <int CPW, int MODE>
+__device__ __forceinline__ void load_mslice(const DecodeArgs& g, int cb, int sl, MSlice<CPW>& ms) {
+  using C = Cols<CPW>;
   const int Ga = g.K >> 5;
   const int Gw = (Ga + (1 << g.gshift) - 1) >> g.gshift;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < kMPer; ++i) {
-    const int j = min(sl * kSlice + wave + 4 * i, Ga - 1);  // past Ga: re-read, unused
+  for (int i = 0; i < C::kMPer; ++i) {
+    const int j = min(sl * C::kSlice + wave + 4 * i, Ga - 1);  // past Ga: re-read, unused
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int c = tt * 16 + (lane & 15);
-      ms.w[i][tt] = *reinterpret_cast<const uint32_t*>(g.w + ((int64_t)cb * Ga + j) * kBlockBytes + (q >> 1) * 256 +
-                                                        c * 8 + (q & 1) * 4);
-      ms.s[i][tt] = MODE == 0 ? __half2float(g.sw[((int64_t)cb * Gw + (j >> g.gshift)) * 32 + step_slot(c)]) : 0.0f;
+    for (int tt = 0; tt < C::NH; ++tt) {
+      const int n = cb * CPW + tt * 16 + (lane & 15);
+      const int nb = n >> 5, cc = n & 31;
+      ms.w[i][tt] = *reinterpret_cast<const uint32_t*>(g.w + ((int64_t)nb * Ga + j) * kBlockBytes + (q >> 1) * 256 +
+                                                        cc * 8 + (q & 1) * 4);
+      ms.s[i][tt] = MODE == 0 ? __half2float(g.sw[((int64_t)nb * Gw + (j >> g.gshift)) * 32 + step_slot(cc)]) : 0.0f;
     }
   }
 }
@@ -206,10 +225,11 @@ __device__ __forceinline__ long unpack8(uint32_t p) {
 // Dots of the wave's groups of slice `sl` lying in [jlo, jhi), codes and
 // steps addressed as in dot_slice; acc[half][e] is row 4 (l / 16) + e of
 // column half * 16 + l % 16.
-template <int MODE>
-__device__ __forceinline__ void mfma_slice(const DecodeArgs& g, int cb, int sl, const MSlice& ms, int jlo,
+template <int CPW, int MODE>
+__device__ __forceinline__ void mfma_slice(const DecodeArgs& g, int cb, int sl, const MSlice<CPW>& ms, int jlo,
                                            int jhi, const int8_t* sA, int a_ld, int a_j0, const float* sS,
-                                           int s_ld, float (&acc)[2][4]) {
+                                           int s_ld, float (&acc)[Cols<CPW>::NH][4]) {
+  using C = Cols<CPW>;
   typedef int v4i_t __attribute__((ext_vector_type(4)));
   const int Ga = g.K >> 5;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -217,8 +237,8 @@ __device__ __forceinline__ void mfma_slice(const DecodeArgs& g, int cb, int sl, 
   const int ra = lane & 15;           // A row of the lane
   const int rac = min(ra, g.R - 1);   // rows past R read row R - 1, then zeroed
 #pragma unroll
-  for (int i = 0; i < kMPer; ++i) {
-    const int j = sl * kSlice + wave + 4 * i;
+  for (int i = 0; i < C::kMPer; ++i) {
+    const int j = sl * C::kSlice + wave + 4 * i;
     if (j >= jlo && j < jhi && j < Ga) {  // wave-uniform
       long a = *reinterpret_cast<const long*>(sA + rac * a_ld + (j - a_j0) * 32 + q * 8);
       if (ra >= g.R) a = 0;
@@ -228,14 +248,14 @@ __device__ __forceinline__ void mfma_slice(const DecodeArgs& g, int cb, int sl, 
         for (int e = 0; e < 4; ++e) sa[e] = sS[min(4 * q + e, g.R - 1) * s_ld + j - a_j0];
       }
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < C::NH; ++tt) {
         const v4i_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, unpack8(ms.w[i][tt]), v4i_t{0, 0, 0, 0}, 0, 0, 0);
         if (MODE == 0) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             acc[tt][e] = __builtin_fmaf((float)d[e], ms.s[i][tt] * sa[e], acc[tt][e]);  // coef fl32(s_w * s_a)
         } else {
-          const int n = cb * 32 + tt * 16 + (lane & 15);
+          const int n = cb * CPW + tt * 16 + (lane & 15);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int m = 4 * q + e;
@@ -250,19 +270,77 @@ __device__ __forceinline__ void mfma_slice(const DecodeArgs& g, int cb, int sl, 
 // Copy an NN x NN fp32 matrix into LDS rows of stride SP.  All of a
 // thread's loads are issued before any store, so the copy costs one memory
 // round trip rather than one per element.
+template <int NN>
+struct MatRegs {
+  static constexpr int T = (NN * NN + 255) / 256;
+  float v[T];
+};
+template <int NN>
+__device__ __forceinline__ void stage_matrix_issue(const float* __restrict__ src, MatRegs<NN>& m) {
+#pragma unroll
+  for (int i = 0; i < MatRegs<NN>::T; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    m.v[i] = idx < NN * NN ? src[idx] : 0.0f;
+  }
+}
+template <int NN, int SP>
+__device__ __forceinline__ void stage_matrix_commit(const MatRegs<NN>& m, float* dst) {
+#pragma unroll
+  for (int i = 0; i < MatRegs<NN>::T; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    if (idx < NN * NN) dst[(idx / NN) * SP + idx % NN] = m.v[i];
+  }
+}
 template <int NN, int SP>
 __device__ __forceinline__ void stage_matrix(const float* __restrict__ src, float* dst) {
-  constexpr int T = (NN * NN + 255) / 256;
-  float v[T];
+  MatRegs<NN> m;
+  stage_matrix_issue<NN>(src, m);
+  stage_matrix_commit<NN, SP>(m, dst);
+}
+
+// Row r of x (K elements, bf16 or fp32) held in registers between the issue
+// of its loads and their commit to LDS: bf16 in .x .y of each entry, fp32 in
+// all four.
+template <int K>
+struct RowRegs {
+  static constexpr int T = (K / 4 + 255) / 256;
+  uint4 v[T];
+};
+template <int K>
+__device__ __forceinline__ void x_row_issue(const DecodeArgs& g, int r, RowRegs<K>& x) {
 #pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    v[i] = idx < NN * NN ? src[idx] : 0.0f;
+  for (int i = 0; i < RowRegs<K>::T; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    if (q < K / 4) {
+      if (g.bf16) {
+        const uint2 u = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.x) + (int64_t)r * K)[q];
+        x.v[i] = uint4{u.x, u.y, 0u, 0u};
+      } else {
+        x.v[i] = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(g.x) + (int64_t)r * K)[q];
+      }
+    }
   }
+}
+template <int K, int N2, int SX>
+__device__ __forceinline__ void x_row_commit(const DecodeArgs& g, const RowRegs<K>& x, float* sX) {
 #pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    if (idx < NN * NN) dst[(idx / NN) * SP + idx % NN] = v[i];
+  for (int i = 0; i < RowRegs<K>::T; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    if (q < K / 4) {
+      const int k = q * 4;
+      float* dst = sX + (k / N2) * SX + k % N2;
+      if (g.bf16) {
+        dst[0] = bf16_bits_to_float(x.v[i].x & 0xffffu);
+        dst[1] = bf16_bits_to_float(x.v[i].x >> 16);
+        dst[2] = bf16_bits_to_float(x.v[i].y & 0xffffu);
+        dst[3] = bf16_bits_to_float(x.v[i].y >> 16);
+      } else {
+        dst[0] = __uint_as_float(x.v[i].x);
+        dst[1] = __uint_as_float(x.v[i].y);
+        dst[2] = __uint_as_float(x.v[i].z);
+        dst[3] = __uint_as_float(x.v[i].w);
+      }
+    }
   }
 }
 
@@ -316,9 +394,14 @@ struct XPlan {
   static constexpr int sp1 = XStrides<N1, N2>::sp1, sp2 = XStrides<N1, N2>::sp2, sx = XStrides<N1, N2>::sx;
   static constexpr int njt = (N2 + 15) / 16;
   static constexpr int st = njt * 16;  // T row stride
+  // P2 as fp32 (fp32 input) or as the bf16 planes (bf16 input); the X region
+  // holds the fp32 or bf16 X grid and later the fp32 x~ row
+  using BL = BfLayout<N2>;
+  static constexpr int p2_bytes = N2 * sp2 * 4 > BL::p2_bytes ? N2 * sp2 * 4 : BL::p2_bytes;
   static constexpr int off_p2 = (N1 * sp1 * 4 + 15) / 16 * 16;
-  static constexpr int off_x = off_p2 + (N2 * sp2 * 4 + 15) / 16 * 16;
-  static constexpr int x_bytes = N1 * sx * 4 > K * 4 ? N1 * sx * 4 : K * 4;
+  static constexpr int off_x = off_p2 + (p2_bytes + 15) / 16 * 16;
+  static constexpr int x_f32 = N1 * sx * 4 > K * 4 ? N1 * sx * 4 : K * 4;
+  static constexpr int x_bytes = x_f32 > N1 * BL::sb * 2 ? x_f32 : N1 * BL::sb * 2;
   static constexpr int off_t = off_x + (x_bytes + 15) / 16 * 16;
   static constexpr int off_codes = off_t + N1 * st * 4;
   static constexpr int codes_bytes(int R) { return (R * K + 15) / 16 * 16; }
@@ -334,12 +417,90 @@ struct XPlan {
 // kernel, so x~ is bitwise the same.
 template <int N1, int N2>
 struct ItemPlan {
+  using BL = BfLayout<N2>;
   static constexpr int sp1 = XStrides<N1, N2>::sp1, sx = XStrides<N1, N2>::sx;
+  static constexpr int p2_f32 = N2 * 16 * 4;          // the tile's fp32 columns [n2][16]
+  static constexpr int p2_bf = 3 * 16 * BL::sb * 2;   // or its bf16 planes (16 columns)
   static constexpr int off_p2 = (N1 * sp1 * 4 + 15) / 16 * 16;
-  static constexpr int off_x = off_p2 + N2 * 16 * 4;
-  static constexpr int off_t = (off_x + N1 * sx * 4 + 15) / 16 * 16;
+  static constexpr int off_x = off_p2 + ((p2_f32 > p2_bf ? p2_f32 : p2_bf) + 15) / 16 * 16;
+  static constexpr int x_bytes = N1 * sx * 4 > N1 * BL::sb * 2 ? N1 * sx * 4 : N1 * BL::sb * 2;
+  static constexpr int off_t = (off_x + x_bytes + 15) / 16 * 16;
   static constexpr int lds = off_t + N1 * 16 * 4;
 };
+
+// The P2 registers of stage_matrix_issue committed as the three bf16 planes
+// (transposed, zeros outside the factor), and the bf16 X row registers of
+// x_row_issue as the bf16 grid (K columns n2 .. kb - 1 zeroed).
+template <int N2>
+__device__ __forceinline__ void p2_planes_commit(const MatRegs<N2>& m, uint16_t* dst) {
+  using L = BfLayout<N2>;
+#pragma unroll
+  for (int i = 0; i < MatRegs<N2>::T; ++i) {
+    const int idx = threadIdx.x + 256 * i;  // element b * N2 + j of P2
+    if (idx < N2 * N2) {
+      const int b = idx / N2, j = idx - b * N2;
+      uint32_t h, mm, l;
+      split3_bf16(m.v[i], &h, &mm, &l);
+      dst[j * L::sb + b] = (uint16_t)h;
+      dst[L::plane + j * L::sb + b] = (uint16_t)mm;
+      dst[2 * L::plane + j * L::sb + b] = (uint16_t)l;
+    }
+  }
+  // zeros: columns j >= N2 (all b < kb) and K indices b >= N2 of columns j < N2
+  constexpr int padj = (L::jp - N2) * L::kb, padb = N2 * (L::kb - N2);
+  for (int idx = threadIdx.x; idx < padj + padb; idx += 256) {
+    int j, b;
+    if (idx < padj) {
+      j = N2 + idx / L::kb;
+      b = idx % L::kb;
+    } else {
+      constexpr int w = L::kb - N2 > 0 ? L::kb - N2 : 1;  // (no such entries when N2 % 32 == 0)
+      j = (idx - padj) / w;
+      b = N2 + (idx - padj) % w;
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) dst[p * L::plane + j * L::sb + b] = 0;
+  }
+}
+template <int N1, int N2>
+__device__ __forceinline__ void x_row_commit_bf(const RowRegs<N1 * N2>& x, uint16_t* sXb) {
+  using L = BfLayout<N2>;
+  constexpr int K = N1 * N2;
+#pragma unroll
+  for (int i = 0; i < RowRegs<K>::T; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    if (q < K / 4) *reinterpret_cast<uint2*>(sXb + (4 * q / N2) * L::sb + (4 * q) % N2) = uint2{x.v[i].x, x.v[i].y};
+  }
+  if constexpr (L::kb > N2) {
+    constexpr int pad = L::kb - N2;
+    for (int idx = threadIdx.x; idx < N1 * pad; idx += 256) sXb[(idx / pad) * L::sb + N2 + idx % pad] = 0;
+  }
+}
+
+// Row r of bf16 x as the n1 x n2 grid of bf16 rows with stride sb (the bf16
+// stage-1 layout), K columns n2 .. kb - 1 zeroed; loads first.
+template <int N1, int N2>
+__device__ __forceinline__ void stage_x_row_bf(const DecodeArgs& g, int r, uint16_t* sXb) {
+  using L = BfLayout<N2>;
+  constexpr int K = N1 * N2;
+  constexpr int T = (K / 4 + 255) / 256;
+  const uint2* src = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.x) + (int64_t)r * K);
+  uint2 u[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    u[i] = q < K / 4 ? src[q] : uint2{0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    if (q < K / 4) *reinterpret_cast<uint2*>(sXb + (4 * q / N2) * L::sb + (4 * q) % N2) = u[i];
+  }
+  if constexpr (L::kb > N2) {
+    constexpr int pad = L::kb - N2;
+    for (int idx = threadIdx.x; idx < N1 * pad; idx += 256) sXb[(idx / pad) * L::sb + N2 + idx % pad] = 0;
+  }
+}
 
 template <int NRT, int N1, int N2>
 __global__ __launch_bounds__(256) void xform_items_kernel(DecodeArgs g, float* __restrict__ xt) {
@@ -360,6 +521,27 @@ __global__ __launch_bounds__(256) void xform_items_kernel(DecodeArgs g, float* _
   const int jt = blockIdx.x - r * njt;
 
   stage_matrix<N1, P::sp1>(g.P1, sP1);
+  if (g.bf16) {  // bf16 stage 1: the tile's P2 planes and the bf16 X grid
+    using BL = BfLayout<N2>;
+    uint16_t* sP2b = reinterpret_cast<uint16_t*>(lds + P::off_p2);
+    uint16_t* sXb = reinterpret_cast<uint16_t*>(lds + P::off_x);
+    stage_p2_planes<N2>(g.P2, sP2b, jt * 16, 16, tid, 256);
+    stage_x_row_bf<N1, N2>(g, r, sXb);
+    __syncthreads();
+    for (int rt = wave; rt < NRT; rt += 4) {
+      const uint16_t* xg[1] = {sXb};
+      const uint16_t* pc[1] = {sP2b};
+      const int rt0[1] = {rt};
+      v4f T[1][1] = {{v4f{0.0f, 0.0f, 0.0f, 0.0f}}};
+      stage1_bf16<N1, N2, 1, 1>(xg, rt0, pc, 16 * BL::sb, li, lk, T);
+      mfma_settle_before_join();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // element e of lane l: row 16 rt + 4 (l / 16) + e
+        const int row = rt * 16 + 4 * lk + e;
+        if (row < n1) sT[row * 16 + li] = T[0][0][e];
+      }
+    }
+  } else {
   {  // the tile's P2 columns [n2][16] (zero past n2), loads first
     constexpr int T = (N2 * 16 + 255) / 256;
     float v[T];
@@ -388,11 +570,13 @@ __global__ __launch_bounds__(256) void xform_items_kernel(DecodeArgs g, float* _
       const int b = 4 * st + lk;
       T = __builtin_amdgcn_mfma_f32_16x16x4f32(masked(xa[b], mrow), sP2[b * 16 + li], T, 0, 0, 0);
     }
+    mfma_settle_before_join();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {  // element e of lane l: row 16 rt + 4 (l / 16) + e
       const int row = rt * 16 + 4 * lk + e;
       if (row < n1) sT[row * 16 + li] = T[e];
     }
+  }
   }
   __syncthreads();
 
@@ -423,7 +607,7 @@ __global__ __launch_bounds__(256) void xform_items_kernel(DecodeArgs g, float* _
 // and steps into sC / sS.  Ends with a barrier.
 template <int NRT, int N1, int N2>
 __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsigned char* lds,
-                                              int8_t* sC, float* sS) {
+                                              int8_t* sC, float* sS, bool staged) {
   using P = XPlan<N1, N2>;
   constexpr int n1 = N1, n2 = N2, K = P::K, Ga = K / 32;
   const float* sP1 = reinterpret_cast<const float*>(lds);
@@ -436,7 +620,15 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
   const int li = lane & 15;
   const int lk = lane >> 4;
 
-  stage_x_row<K, N2, P::sx>(g, r, sX);
+  using BL = BfLayout<N2>;
+  const uint16_t* sP2b = reinterpret_cast<const uint16_t*>(lds + P::off_p2);
+  uint16_t* sXb = reinterpret_cast<uint16_t*>(lds + P::off_x);
+  if (!staged) {  // (row 0 is staged with the factors)
+    if (g.bf16)
+      stage_x_row_bf<N1, N2>(g, r, sXb);
+    else
+      stage_x_row<K, N2, P::sx>(g, r, sX);
+  }
   __syncthreads();
 
   // stage 1: tile (rt, jt) of T = X[16 rt .., :] * P2[:, 16 jt ..], steps of b
@@ -458,7 +650,33 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
     mrow[u] = rt[u] * 16 + li < n1 ? 0xffffffffu : 0u;
     mj[u] = jc[u] < n2 ? 0xffffffffu : 0u;
   }
-  {
+  if (g.bf16) {
+    // bf16 input: the bf16 MFMA on the X grid and the P2 planes (the tile
+    // sequence of every other kernel, so x~ is bitwise the same)
+    const uint16_t* xg[NT];
+    const uint16_t* pc[NT];
+    int rt0[NT];
+    v4f acc[NT][1];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      xg[u] = sXb;
+      pc[u] = sP2b + (jc[u] - li) * BL::sb;
+      rt0[u] = rt[u];
+      acc[u][0] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    stage1_bf16<N1, N2, NT, 1>(xg, rt0, pc, BL::plane, li, lk, acc);
+    mfma_settle_before_join();
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      if (has[u]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = rt[u] * 16 + 4 * lk + e;
+          if (row < n1) sT[row * P::st + jc[u]] = acc[u][0][e];
+        }
+      }
+    }
+  } else {
     v4f acc[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -480,6 +698,7 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
       for (int u = 0; u < NT; ++u)
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s & 1][u], bv[s & 1][u], acc[u], 0, 0, 0);
     }
+    mfma_settle_before_join();
     // element e of lane l: row 16 rt + 4 (l / 16) + e, column jc
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
@@ -559,9 +778,12 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
 // Canonical codes (16-byte aligned rows) and steps of every row for groups
 // [j0, j0 + G) into LDS as make_codes lays them out, 16 codes per load, all
 // of a round's loads (8 per thread) issued before its stores.
-template <int MODE>
+// kick() runs once, right after the first round of loads is issued (the
+// caller issues its weight loads there, behind the activation loads, so that
+// waiting for these does not wait for the weights).
+template <int MODE, typename Kick>
 __device__ __forceinline__ void copy_codes(const DecodeArgs& g, int j0, int G, int8_t* sA, int a_ld,
-                                           float* sS, int s_ld) {
+                                           float* sS, int s_ld, Kick kick) {
   const int K = g.K, Ga = K >> 5;
   const int nch = g.R * G * 2;  // 16-code chunks
   for (int base = 0; base < nch; base += 256 * 8) {
@@ -569,11 +791,13 @@ __device__ __forceinline__ void copy_codes(const DecodeArgs& g, int j0, int G, i
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = base + (int)threadIdx.x + 256 * i;
+      v[i] = uint4{0u, 0u, 0u, 0u};
       if (t < nch) {
         const int m = t / (2 * G), rem = t - m * 2 * G;
         v[i] = *reinterpret_cast<const uint4*>(g.a_codes + (int64_t)m * K + (j0 + (rem >> 1)) * 32 + (rem & 1) * 16);
       }
     }
+    if (base == 0) kick();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = base + (int)threadIdx.x + 256 * i;
@@ -619,9 +843,9 @@ constexpr int kU = 4;
 struct CodeRaw {
   uint4 v[kU];  // fp32: 4 elements; bf16: 4 elements in .x .y; codes: .x codes, .y step bits
 };
-template <int MODE>
+template <int MODE, typename Kick>
 __device__ __forceinline__ void make_codes(const DecodeArgs& g, int j0, int G, int8_t* sA, int a_ld,
-                                           float* sS, int s_ld) {
+                                           float* sS, int s_ld, Kick kick) {
   const int K = g.K, Ga = K >> 5;
   const int ntask = g.R * G * 8;
   const int per_round = 256 * kU;
@@ -686,6 +910,7 @@ __device__ __forceinline__ void make_codes(const DecodeArgs& g, int j0, int G, i
   };
   CodeRaw ra, rb;
   issue(0, ra);
+  kick();
   for (int q = 0; q < nround; q += 2) {  // two register buffers, unrolled by two
     if (q + 1 < nround) issue(q + 1, rb);
     process(q, ra);
@@ -697,14 +922,18 @@ __device__ __forceinline__ void make_codes(const DecodeArgs& g, int j0, int G, i
 }
 
 // N1 = N2 = 0: no transform (x quantized as it is, or codes given).
-// RM: rows bound (4 or 16).  MODE 0: y; MODE 1: int32 group dots.
-template <int NRT, int N1, int N2, int RM, int MODE>
+// RM: rows bound (4 or 16).  MODE 0: y; MODE 1: int32 group dots.  CPW:
+// output columns per work-group (8, 16 or 32; 16 or 32 for RM = 16).
+template <int NRT, int N1, int N2, int RM, int MODE, int CPW>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
   extern __shared__ __align__(16) unsigned char lds[];
+  using C = Cols<CPW>;
+  constexpr int kSlice = C::kSlice;
+  constexpr int NH = C::NH;
   const int tid = threadIdx.x;
-  const int cb = blockIdx.x;  // column block
-  const int c = tid & 31;     // column of the block
-  const int gq = tid >> 5;    // lane group: groups gq + 8 i of each slice
+  const int cb = blockIdx.x;       // columns cb * CPW .. + CPW - 1
+  const int c = tid & (CPW - 1);   // column of the work-group
+  const int gq = tid / CPW;        // lane group: groups gq + GL i of each slice
   const int K = g.K;
   const int Ga = K >> 5;
   const int R = g.R;
@@ -713,24 +942,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
   // the first weight slice is in flight while the codes are formed (the
   // second follows once they are: both would crowd the transform's registers)
   constexpr bool kMfma = RM > 4;  // up to 16 rows: MFMA dots; up to 4: VALU dots
-  typedef typename std::conditional<kMfma, MSlice, WSlice>::type Slice;
+  static_assert(!kMfma || CPW >= 16, "the MFMA form takes 16 columns per instruction");
+  typedef typename std::conditional<kMfma, MSlice<CPW>, WSlice>::type Slice;
   Slice wa, wb;
   auto load = [&](int sl, Slice& buf) {
-    if constexpr (kMfma) load_mslice<MODE>(g, cb, sl, buf);
-    else load_slice<MODE>(g, cb, sl, c, gq, buf);
+    if constexpr (kMfma) load_mslice<CPW, MODE>(g, cb, sl, buf);
+    else load_slice<CPW, MODE>(g, cb, sl, c, gq, buf);
   };
   float acc[RM];
-  float accm[2][4];
+  float accm[NH][4];
 #pragma unroll
   for (int m = 0; m < RM; ++m) acc[m] = 0.0f;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int tt = 0; tt < NH; ++tt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) accm[tt][e] = 0.0f;
   auto dots = [&](int sl, const Slice& buf, int jlo, int jhi, const int8_t* sA, int a_ld, int a_j0,
                   const float* sS, int s_ld) {
-    if constexpr (kMfma) mfma_slice<MODE>(g, cb, sl, buf, jlo, jhi, sA, a_ld, a_j0, sS, s_ld, accm);
-    else dot_slice<RM, MODE>(g, cb, sl, c, gq, buf, jlo, jhi, sA, a_ld, a_j0, sS, s_ld, acc);
+    if constexpr (kMfma) mfma_slice<CPW, MODE>(g, cb, sl, buf, jlo, jhi, sA, a_ld, a_j0, sS, s_ld, accm);
+    else dot_slice<CPW, RM, MODE>(g, cb, sl, c, gq, buf, jlo, jhi, sA, a_ld, a_j0, sS, s_ld, acc);
   };
   // slices alternate between the two register buffers (unrolled by two so
   // each buffer stays in registers); `body(sl, buf)` consumes slice sl
@@ -744,7 +974,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
       }
     }
   };
-  load(0, wa);
+  // The activation-side loads (factors and the first row, or the first round
+  // of x / codes) are issued before the weight loads: a wait for them then
+  // leaves the weights in flight, so the weight fetch overlaps the transform
+  // or the quantizer instead of preceding it.
   float* red;
 
   if constexpr (N1 > 0) {
@@ -754,10 +987,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
     int8_t* sC = reinterpret_cast<int8_t*>(lds + P::off_codes);
     float* sS = reinterpret_cast<float*>(lds + P::off_codes + P::codes_bytes(R));
     red = sS + R * (P::K / 32);
-    stage_matrix<N1, P::sp1>(g.P1, sP1);
-    stage_matrix<N2, P::sp2>(g.P2, sP2);
-    // (transform_row's barrier after the X staging orders these stores too)
-    for (int r = 0; r < R; ++r) transform_row<NRT, N1, N2>(g, r, lds, sC, sS);
+    {
+      MatRegs<N1> m1;
+      MatRegs<N2> m2;
+      RowRegs<P::K> x0;
+      stage_matrix_issue<N1>(g.P1, m1);
+      stage_matrix_issue<N2>(g.P2, m2);
+      x_row_issue<P::K>(g, 0, x0);
+      load(0, wa);
+      stage_matrix_commit<N1, P::sp1>(m1, sP1);
+      if (g.bf16) {
+        p2_planes_commit<N2>(m2, reinterpret_cast<uint16_t*>(lds + P::off_p2));
+        x_row_commit_bf<N1, N2>(x0, reinterpret_cast<uint16_t*>(lds + P::off_x));
+      } else {
+        stage_matrix_commit<N2, P::sp2>(m2, sP2);
+        x_row_commit<P::K, N2, P::sx>(g, x0, reinterpret_cast<float*>(lds + P::off_x));
+      }
+    }
+    // (transform_row's first barrier orders these stores)
+    for (int r = 0; r < R; ++r) transform_row<NRT, N1, N2>(g, r, lds, sC, sS, r == 0);
     if (g.codes_out) dump_codes(g, 0, Ga, sC, K, sS, Ga);
     if (nsl > 1) load(1, wb);
     sweep([&](int sl, const Slice& buf) { dots(sl, buf, 0, Ga, sC, K, 0, sS, Ga); });
@@ -766,11 +1014,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
     int8_t* sA = reinterpret_cast<int8_t*>(lds);                                    // [R][K]
     float* sSt = reinterpret_cast<float*>(lds + ((R * K + 15) & ~15));            // [R][Ga]
     red = sSt + R * Ga;
-    if (nsl > 1) load(1, wb);
+    auto kick = [&]() {
+      load(0, wa);
+      if (nsl > 1) load(1, wb);
+    };
     if (g.in_codes && g.wide_codes)
-      copy_codes<MODE>(g, 0, Ga, sA, K, sSt, Ga);
+      copy_codes<MODE>(g, 0, Ga, sA, K, sSt, Ga, kick);
     else
-      make_codes<MODE>(g, 0, Ga, sA, K, sSt, Ga);
+      make_codes<MODE>(g, 0, Ga, sA, K, sSt, Ga, kick);
     __syncthreads();
     if (g.codes_out && !g.in_codes) dump_codes(g, 0, Ga, sA, K, sSt, Ga);
     sweep([&](int sl, const Slice& buf) { dots(sl, buf, 0, Ga, sA, K, 0, sSt, Ga); });
@@ -779,15 +1030,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
     int8_t* sA = reinterpret_cast<int8_t*>(lds);                          // [RM][kSlice * 32]
     float* sSt = reinterpret_cast<float*>(lds + RM * kSlice * 32);       // [RM][kSlice]
     red = sSt + RM * kSlice;
+    load(0, wa);
     if (nsl > 1) load(1, wb);
+    auto none = [] {};
     sweep([&](int sl, const Slice& buf) {
       const int j0 = sl * kSlice;
       const int GS = min(kSlice, Ga - j0);
       __syncthreads();  // the previous slice's codes are no longer read
       if (g.in_codes && g.wide_codes)
-        copy_codes<MODE>(g, j0, GS, sA, kSlice * 32, sSt, kSlice);
+        copy_codes<MODE>(g, j0, GS, sA, kSlice * 32, sSt, kSlice, none);
       else
-        make_codes<MODE>(g, j0, GS, sA, kSlice * 32, sSt, kSlice);
+        make_codes<MODE>(g, j0, GS, sA, kSlice * 32, sSt, kSlice, none);
       __syncthreads();
       if (g.codes_out && !g.in_codes) dump_codes(g, j0, GS, sA, kSlice * 32, sSt, kSlice);
       dots(sl, buf, j0, j0 + GS, sA, kSlice * 32, j0, sSt, kSlice);
@@ -797,54 +1050,70 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
 
   // partial sums of each (row, column) added in a fixed order through LDS
   if constexpr (kMfma) {
-    // the four waves' sums: red[((wave * 2 + half) * 4 + e) * 64 + lane]
+    // the four waves' sums: red[((wave * NH + half) * 4 + e) * 64 + lane]
     const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < NH; ++tt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[((wave * 2 + tt) * 4 + e) * 64 + lane] = accm[tt][e];
+      for (int e = 0; e < 4; ++e) red[((wave * NH + tt) * 4 + e) * 64 + lane] = accm[tt][e];
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int o = tid + 256 * i;  // row o / 32, column o % 32
-      const int m = o >> 5, col = o & 31;
-      const int n = cb * 32 + col;
-      if (m < R && n < g.N) {
+    for (int o = tid; o < R * CPW; o += 256) {  // row o / CPW, column o % CPW
+      const int m = o / CPW, col = o - m * CPW;
+      const int n = cb * CPW + col;
+      if (n < g.N) {
         const int ln = (m >> 2) * 16 + (col & 15);
         float tot = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) tot += red[((w * 2 + (col >> 4)) * 4 + (m & 3)) * 64 + ln];
+        for (int w = 0; w < 4; ++w) tot += red[((w * NH + (col >> 4)) * 4 + (m & 3)) * 64 + ln];
         g.y[(int64_t)m * g.N + n] = tot;
       }
     }
   } else {
-    // the eight lane groups' sums
+    // the GL lane groups' sums
 #pragma unroll
-    for (int m = 0; m < RM; ++m) red[(gq * RM + m) * 32 + c] = acc[m];
+    for (int m = 0; m < RM; ++m) red[(gq * RM + m) * CPW + c] = acc[m];
     __syncthreads();
-    const int n = cb * 32 + c;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int o = tid + 256 * i;  // row o / 32, column c
-      if (o < R * 32 && n < g.N) {
+    for (int o = tid; o < R * CPW; o += 256) {  // row o / CPW, column o % CPW
+      const int m = o / CPW, col = o - m * CPW;
+      const int n = cb * CPW + col;
+      if (n < g.N) {
         float tot = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) tot += red[(q * RM + (o >> 5)) * 32 + c];
-        g.y[(int64_t)(o >> 5) * g.N + n] = tot;
+        for (int q = 0; q < C::GL; ++q) tot += red[(q * RM + m) * CPW + col];
+        g.y[(int64_t)m * g.N + n] = tot;
       }
     }
   }
 }
 
-template <int RM, int MODE>
-const void* plain_kernel() {
-  return reinterpret_cast<const void*>(decode_kernel<1, 0, 0, RM, MODE>);
+// the kernel of a factor shape (N1 = N2 = 0: none) for CPW columns per work-group
+template <int NRT, int N1, int N2, int RM, int MODE>
+const void* decode_fn(int cpw) {
+  if (cpw == 8) {
+    if constexpr (RM <= 4) return reinterpret_cast<const void*>(decode_kernel<NRT, N1, N2, RM, MODE, 8>);
+    return nullptr;
+  }
+  if (cpw == 16) return reinterpret_cast<const void*>(decode_kernel<NRT, N1, N2, RM, MODE, 16>);
+  return reinterpret_cast<const void*>(decode_kernel<NRT, N1, N2, RM, MODE, 32>);
 }
 
 // LDS of the non-transform instances: all rows' codes and steps, or one
-// weight slice of them; then the partial sums
+// weight slice of them; then the partial sums (RM * 1 KiB: 256 threads x RM
+// floats in the VALU form, at most 8 KiB in the MFMA form)
 int whole_lds(int R, int K, int RM) { return ((R * K + 15) & ~15) + R * (K / 32) * 4 + 8 * RM * 32 * 4; }
-int slice_lds(int RM) { return RM * kSlice * 32 + RM * kSlice * 4 + 8 * RM * 32 * 4; }
+int slice_lds(int RM, int cpw) {
+  const int ks = 2048 / cpw;
+  return RM * ks * 32 + RM * ks * 4 + 8 * RM * 32 * 4;
+}
+
+// Columns per work-group: the largest of 32, 16, 8 that still gives every CU
+// a work-group (16 at least for the MFMA form), else the smallest allowed.
+int pick_cpw(int64_t n_padded, int R, int ncu) {
+  const int lo = R > 4 ? 16 : 8;
+  for (int cpw = 32; cpw >= lo; cpw >>= 1)
+    if (n_padded / cpw >= ncu) return cpw;
+  return lo;
+}
 
 }  // namespace
 
@@ -905,27 +1174,28 @@ hipError_t launch_decode(const DecodeCall& c, hipStream_t s) {
   int lds = 0;
   const bool small = c.R <= 4;
   const int RM = small ? 4 : kDecodeMaxRows;
+  const int cpw = pick_cpw(padded_cols(c.N), c.R, device_cu_count());
   if (xform) {
 #define LOOPQ_DECODE_KERNEL(n1_, n2_, rs_, nim_)                                                   \
     if (c.n1 == n1_ && c.n2 == n2_) {                                                              \
       constexpr int nrt = (n1_ + 15) / 16;                                                         \
-      fn = small ? reinterpret_cast<const void*>(decode_kernel<nrt, n1_, n2_, 4, 0>)               \
-                 : reinterpret_cast<const void*>(decode_kernel<nrt, n1_, n2_, kDecodeMaxRows, 0>); \
+      fn = small ? decode_fn<nrt, n1_, n2_, 4, 0>(cpw) : decode_fn<nrt, n1_, n2_, kDecodeMaxRows, 0>(cpw); \
       lds = XPlan<n1_, n2_>::lds(c.R, RM);                                                         \
     }
     LOOPQ_SHAPES(LOOPQ_DECODE_KERNEL)
 #undef LOOPQ_DECODE_KERNEL
   } else {
-    fn = small ? (c.mode == 0 ? plain_kernel<4, 0>() : plain_kernel<4, 1>())
-               : (c.mode == 0 ? plain_kernel<kDecodeMaxRows, 0>() : plain_kernel<kDecodeMaxRows, 1>());
+    fn = small ? (c.mode == 0 ? decode_fn<1, 0, 0, 4, 0>(cpw) : decode_fn<1, 0, 0, 4, 1>(cpw))
+               : (c.mode == 0 ? decode_fn<1, 0, 0, kDecodeMaxRows, 0>(cpw)
+                              : decode_fn<1, 0, 0, kDecodeMaxRows, 1>(cpw));
     g.whole = whole_lds(c.R, c.K, RM) <= kLdsBudget;
-    lds = g.whole ? whole_lds(c.R, c.K, RM) : slice_lds(RM);
+    lds = g.whole ? whole_lds(c.R, c.K, RM) : slice_lds(RM, cpw);
   }
   if (fn == nullptr || lds > kLdsBudget) return hipErrorInvalidValue;
   hipError_t e = prepare_launch(fn, lds, 256);
   if (e != hipSuccess) return e;
   void* args[] = {&g};
-  e = hipLaunchKernel(fn, dim3((unsigned)(padded_cols(c.N) / 32)), dim3(256), args, lds, s);
+  e = hipLaunchKernel(fn, dim3((unsigned)(padded_cols(c.N) / cpw)), dim3(256), args, lds, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

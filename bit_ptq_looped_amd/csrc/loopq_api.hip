@@ -1195,6 +1195,17 @@ int32_t loopq_timing_read(int32_t n, double* ms_host, int64_t* launches_host) {
 
 namespace loopq {
 
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(g_launch_mu);
+  if (g_ncu[dev] <= 0) {
+    int n = 0;
+    g_ncu[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return g_ncu[dev];
+}
+
 hipError_t prepare_launch(const void* fn, int lds_bytes, int block, int* per_cu, int* ncu) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

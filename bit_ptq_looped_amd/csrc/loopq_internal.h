@@ -228,6 +228,8 @@ size_t hessian_workspace_bytes(int K);
 // fails).  Kept per device and kernel, so only a kernel's first launch at a
 // given size pays for the runtime queries.
 hipError_t prepare_launch(const void* fn, int lds_bytes, int block, int* per_cu = nullptr, int* ncu = nullptr);
+// CU count of the current device (queried once per device; 256 if the query fails)
+int device_cu_count();
 
 hipError_t launch_hessian(const float* x, int rows, int K, float* H, float* part, hipStream_t s);
 

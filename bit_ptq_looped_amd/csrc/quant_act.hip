@@ -23,6 +23,8 @@
 #include "loopq_internal.h"
 #include "quant_core.h"
 
+#include <string.h>
+
 #include <type_traits>
 
 namespace loopq {
@@ -310,6 +312,35 @@ __device__ __forceinline__ void stage1(const QuantArgs& a, const float* sP2, con
   }
 }
 
+// Stage 1 on the bf16 MFMA for the wave's NI items (bf16 input, compile-time
+// factor shape): item (row r, column tile jt) covers all NRT row tiles of the
+// row's X grid (bf16 rows of stride sb at sXb) against the P2 planes.
+template <int NRT, int N1, int N2, int NI, int NIM, bool SR>
+__device__ __forceinline__ void stage1_bf(const uint16_t* sXb, const uint16_t* sP2b, int wave, int njt, int li,
+                                          int lk, v4f (&T)[NIM][NRT]) {
+  using L = BfLayout<N2>;
+  const uint16_t* xg[NI];
+  const uint16_t* pc[NI];
+  int rt0[NI];
+  v4f acc[NI][NRT];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int item = item_of<SR, NIM>(wave, ii);
+    const int r = item / njt;
+    const int jt = item - r * njt;
+    xg[ii] = sXb + r * N1 * L::sb;
+    pc[ii] = sP2b + jt * 16 * L::sb;
+    rt0[ii] = 0;
+#pragma unroll
+    for (int q = 0; q < NRT; ++q) acc[ii][q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  stage1_bf16<N1, N2, NI, NRT>(xg, rt0, pc, L::plane, li, lk, acc);
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+    for (int q = 0; q < NRT; ++q) T[ii][q] = acc[ii][q];
+}
+
 // Stage 2 for the same items: x~[:, tile] = P1^T * T, B operands straight
 // from the stage-1 results (element e of tile rt is step s = 4 rt + e);
 // writes fp32 x~ into the flat rows of the X region.
@@ -556,6 +587,12 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const int sp1 = N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1;
   const int sp2 = N2 > 0 ? XStrides<N1, N2>::sp2 : a.sp2;
   const int sx = N2 > 0 ? XStrides<N1, N2>::sx : a.sx;
+  // bf16 input of a compile-time shape: stage 1 on the bf16 MFMA (X rows and
+  // the P2 planes as bf16 in LDS); otherwise fp32 operands on the fp32 MFMA
+  constexpr bool BFS = BF == 1 && N2 > 0 && RS > 0;
+  using BL = BfLayout<(N2 > 0 ? N2 : 16)>;
+  uint16_t* sP2b = reinterpret_cast<uint16_t*>(lds + a.off_p2);
+  uint16_t* sXb = reinterpret_cast<uint16_t*>(lds + a.off_x);
   const int li = lane & 15;  // row of A / column of B and of the result
   const int lk = lane >> 4;  // k within a 4-deep step; result rows lk + 4 e
   const int nchunks = (a.rows + R - 1) / R;
@@ -601,10 +638,24 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
     for (int i = 0; i < PF; ++i) {
       const int q = tid + 256 * i;
       if (q < nq) {
-        if constexpr (BF == 1)
+        if constexpr (BFS) {
+          // four bf16 values as they are, into the bf16 X grid
+          const int e = q * 4;
+          const int r = e / K;
+          const int k = e - r * K;
+          *reinterpret_cast<uint2*>(sXb + (r * n1 + k / n2) * BL::sb + k % n2) = pre[i];
+        } else if constexpr (BF == 1) {
           put(x_dst(q), widen(pre[i]));
-        else
+        } else {
           put(x_dst(q), pre[i]);
+        }
+      }
+    }
+    if constexpr (BFS && BL::kb > (N2 > 0 ? N2 : 16)) {  // zero K columns n2 .. kb - 1 of every X row
+      constexpr int pad = BL::kb - N2;
+      for (int idx = tid; idx < R * N1 * pad; idx += 256) {
+        const int row = idx / pad;
+        sXb[row * BL::sb + N2 + (idx - row * pad)] = 0;
       }
     }
   };
@@ -619,7 +670,10 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   // the first chunk's X is in flight while the factors are staged
   if (RS > 0 && slot < nchunks) fetch(slot);
   stage_factor(sP1, a.P1, n1, sp1, tid);
-  stage_factor(sP2, a.P2, n2, sp2, tid);
+  if constexpr (BFS)
+    stage_p2_planes<(N2 > 0 ? N2 : 16)>(a.P2, sP2b, 0, BL::jp, tid, 256);
+  else
+    stage_factor(sP2, a.P2, n2, sp2, tid);
   for (int chunk = slot; chunk < nchunks; chunk += G) {
     const int row0 = chunk * R;
     const int rows = min(R, a.rows - row0);
@@ -659,12 +713,22 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
     for (int ii = 0; ii < NIM; ++ii)
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) T[ii][rt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    switch (nmine) {
-      case 4: if constexpr (NIM >= 4) stage1<NRT, N1, N2, 4, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
-      case 3: if constexpr (NIM >= 3) stage1<NRT, N1, N2, 3, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
-      case 2: if constexpr (NIM >= 2) stage1<NRT, N1, N2, 2, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
-      case 1: stage1<NRT, N1, N2, 1, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
-      default: break;
+    if constexpr (BFS) {
+      switch (nmine) {
+        case 4: if constexpr (NIM >= 4) stage1_bf<NRT, N1, N2, 4, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+        case 3: if constexpr (NIM >= 3) stage1_bf<NRT, N1, N2, 3, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+        case 2: if constexpr (NIM >= 2) stage1_bf<NRT, N1, N2, 2, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+        case 1: stage1_bf<NRT, N1, N2, 1, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+        default: break;
+      }
+    } else {
+      switch (nmine) {
+        case 4: if constexpr (NIM >= 4) stage1<NRT, N1, N2, 4, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+        case 3: if constexpr (NIM >= 3) stage1<NRT, N1, N2, 3, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+        case 2: if constexpr (NIM >= 2) stage1<NRT, N1, N2, 2, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+        case 1: stage1<NRT, N1, N2, 1, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+        default: break;
+      }
     }
     __syncthreads();  // every X read is done; x~ may now overwrite the region
 
@@ -716,6 +780,10 @@ int x_bytes_for(int R, int n1, int sx, int K) {
   return (xb + 15) / 16 * 16;
 }
 
+// host copies of BfLayout<n2> (the bf16 stage-1 layouts)
+int bf_sb(int n2) { return (n2 + 31) / 32 * 32 + 8; }
+int bf_p2_bytes(int n2) { return 3 * ((n2 + 15) / 16 * 16) * bf_sb(n2) * 2; }
+
 
 // LDS plan of the fused transform kernel: P1 and P2 with strides that put the
 // 16 lanes of an MFMA operand read on distinct banks, and R rows of X with a
@@ -742,11 +810,20 @@ bool plan_quant(QuantArgs& a) {
     if (R > 16) R = 16;
   }
   if (R * njt > 4 * nim) return false;  // every work item must have a wave slot
+  // bf16 input of a compile-time shape: P2 as bf16 planes, X rows as bf16
+  // (the X region must also hold the fp32 x~ rows)
+  const bool bfs = fixed && a.bf16;
+  auto p2_bytes = [&](int sp2) { return bfs ? bf_p2_bytes(a.n2) : a.n2 * sp2 * 4; };
+  auto xb_for = [&](int sx, int r) {
+    int xb = x_bytes_for(r, a.n1, sx, a.K);
+    const int xbb = (r * a.n1 * bf_sb(a.n2) * 2 + 15) / 16 * 16;
+    return bfs && xbb > xb ? xbb : xb;
+  };
   // + 256 bytes of per-row absmax partials (16 rows x 4 waves) after X
   auto lds_for = [&](int sp1, int sp2, int sx, int r) {
     const int p2 = (a.n1 * sp1 * 4 + 15) / 16 * 16;
-    const int px = (p2 + a.n2 * sp2 * 4 + 15) / 16 * 16;
-    return px + x_bytes_for(r, a.n1, sx, a.K) + kRowMaxBytes;
+    const int px = (p2 + p2_bytes(sp2) + 15) / 16 * 16;
+    return px + xb_for(sx, r) + kRowMaxBytes;
   };
   int sp1 = p_stride(a.n1);
   int sp2 = p_stride(a.n2);
@@ -773,9 +850,9 @@ bool plan_quant(QuantArgs& a) {
   a.st = 0;
   a.R = R;
   a.off_p2 = (a.n1 * sp1 * 4 + 15) / 16 * 16;
-  a.off_x = (a.off_p2 + a.n2 * sp2 * 4 + 15) / 16 * 16;
+  a.off_x = (a.off_p2 + p2_bytes(sp2) + 15) / 16 * 16;
   a.off_t = 0;
-  a.off_rmax = a.off_x + x_bytes_for(R, a.n1, sx, a.K);
+  a.off_rmax = a.off_x + xb_for(sx, R);
   a.lds_bytes = a.off_rmax + kRowMaxBytes;
   return true;
 }
@@ -783,11 +860,18 @@ bool plan_quant(QuantArgs& a) {
 }  // namespace
 
 bool quant_plan_fits(int K, int n1, int n2) {
-  QuantArgs a;
-  a.K = K;
-  a.n1 = n1;
-  a.n2 = n2;
-  return plan_quant(a);
+  // the plan must fit for either input type (bf16 inputs of compile-time
+  // shapes use the bf16 stage-1 layouts)
+  for (int bf = 0; bf < 2; ++bf) {
+    QuantArgs a;
+    memset(&a, 0, sizeof(a));
+    a.K = K;
+    a.n1 = n1;
+    a.n2 = n2;
+    a.bf16 = bf;
+    if (!plan_quant(a)) return false;
+  }
+  return true;
 }
 
 hipError_t launch_quant_token(QuantArgs a, hipStream_t s) {

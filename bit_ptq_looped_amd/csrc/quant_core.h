@@ -106,6 +106,128 @@ struct XStrides {
   static constexpr int sx = N2 > 0 ? x_stride(N2) : 0;
 };
 
+// Ends a branch whose MFMA accumulators are read only after the branch has
+// joined another one.  The compiler's hazard count across such a join has
+// come out short on gfx950 (the last element of a 16x16x4 f32 accumulator
+// read 8 wait states after its MFMA, where straight-line code gets 10, and
+// seen without that MFMA's contribution); 16 wait states of the branch's own
+// make the read safe whatever the count.
+__device__ __forceinline__ void mfma_settle_before_join() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1 of the transform on the bf16 MFMA, for bf16 inputs: T = X * P2 with
+// X exactly bf16 and P2 split into three bf16 planes whose sum is P2 exactly
+// (hi = P2 truncated to bf16, mid = the remainder truncated, lo = what is
+// left, which has at most 8 significant bits).  Every product of an X value
+// and a plane value is exact in fp32; only the fp32 accumulation rounds, as
+// on the fp32 MFMA, so x~ keeps the fp32-class bound.
+//
+// LDS layouts (bf16 elements): P2 planes transposed, plane p, column j, K
+// index b at p * plane + j * sb + b; X rows i of the n1 x n2 grid at i * sb,
+// K index b.  Entries outside the n2 x n2 factor and the n2 columns of X are
+// zero.  The row stride sb = kb + 8 puts the 16 rows one 16-byte read per
+// lane touches on distinct LDS banks.
+// ---------------------------------------------------------------------------
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+template <int N2>
+struct BfLayout {
+  static constexpr int kb = (N2 + 31) / 32 * 32;  // K extent, in steps of 32
+  static constexpr int jp = (N2 + 15) / 16 * 16;  // column extent, in tiles of 16
+  static constexpr int sb = kb + 8;               // row stride (elements)
+  static constexpr int plane = jp * sb;           // elements per plane (all columns)
+  static constexpr int p2_bytes = 3 * plane * 2;
+};
+
+// v = hi + mid + lo exactly, each the bits of a bf16 (truncations)
+__device__ __forceinline__ void split3_bf16(float v, uint32_t* h, uint32_t* m, uint32_t* l) {
+  const uint32_t hu = __float_as_uint(v) & 0xFFFF0000u;
+  const float r1 = v - __uint_as_float(hu);  // exact: the low 16 mantissa bits of v
+  const uint32_t mu = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(mu);  // exact, at most 8 significant bits
+  *h = hu >> 16;
+  *m = mu >> 16;
+  *l = __float_as_uint(r2) >> 16;
+}
+
+// NI items of T = X * P2, each one 16-column tile of T over NRT consecutive
+// 16-row tiles starting at tile rt0[ii].  Item ii reads the X grid whose row
+// i is at xgrid[ii] + i * sb (rows >= N1 read as zero) and the planes of its
+// columns starting at pcol[ii] (plane p at + p * plane, column li of the tile
+// at + li * sb).  Lane l takes A row l % 16, B column l % 16 and K slots
+// 8 (l / 16) .. + 7 of each step of 32; result element e of lane l is T row
+// 16 (rt0 + q) + 4 (l / 16) + e, column l % 16 (the fp32 MFMA's layout).
+// Every tile accumulates in the same order (K steps, then planes hi, mid,
+// lo), so a tile's value does not depend on which kernel or wave forms it.
+template <int N1, int N2, int NI, int NRT>
+__device__ __forceinline__ void stage1_bf16(const uint16_t* const (&xgrid)[NI], const int (&rt0)[NI],
+                                            const uint16_t* const (&pcol)[NI], int plane, int li, int lk,
+                                            v4f (&T)[NI][NRT]) {
+  using L = BfLayout<N2>;
+#pragma unroll
+  for (int ks = 0; ks < L::kb / 32; ++ks) {
+    v4u a[NI][NRT], b[NI][3];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        b[ii][p] = *reinterpret_cast<const v4u*>(pcol[ii] + p * plane + li * L::sb + 32 * ks + 8 * lk);
+#pragma unroll
+      for (int q = 0; q < NRT; ++q) {
+        const int i = (rt0[ii] + q) * 16 + li;
+        a[ii][q] = *reinterpret_cast<const v4u*>(xgrid[ii] + (i < N1 ? i : N1 - 1) * L::sb + 32 * ks + 8 * lk);
+        if (i >= N1) a[ii][q] = v4u{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+        for (int q = 0; q < NRT; ++q)
+          T[ii][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[ii][q]),
+                                                           __builtin_bit_cast(v8bf, b[ii][p]), T[ii][q], 0, 0, 0);
+  }
+}
+
+// Stage the planes of columns j0 .. j0 + nj - 1 of P2 (fp32 [N2][N2] in
+// global memory) into dst (plane stride nj * sb, local column j - j0), zeros
+// outside the factor; threads tid, tid + nthr, ...  Loads are issued in
+// batches of 8 before their stores (coalesced along j).
+template <int N2>
+__device__ __forceinline__ void stage_p2_planes(const float* __restrict__ P2, uint16_t* dst, int j0, int nj, int tid,
+                                                int nthr) {
+  using L = BfLayout<N2>;
+  const int n = nj * L::kb;
+  const int pl = nj * L::sb;
+  for (int base = tid; base < n; base += 8 * nthr) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * nthr;
+      const int b = idx / nj, j = j0 + (idx - (idx / nj) * nj);
+      v[u] = (idx < n && b < N2 && j < N2) ? P2[b * N2 + j] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * nthr;
+      if (idx < n) {
+        const int b = idx / nj, jj = idx - b * nj;
+        uint32_t h, m, l;
+        split3_bf16(v[u], &h, &m, &l);
+        dst[jj * L::sb + b] = (uint16_t)h;
+        dst[pl + jj * L::sb + b] = (uint16_t)m;
+        dst[2 * pl + jj * L::sb + b] = (uint16_t)l;
+      }
+    }
+  }
+}
+
 // Factor shapes of the Kronecker transforms in use (K = 256, 2048, 5632,
 // 2560, 6912, and a 32-wide test shape), each with its rows per chunk and the
 // most work items a wave then takes.  Chunk sizes make rows * ceil(n2 / 16)

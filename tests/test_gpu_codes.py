@@ -124,6 +124,11 @@ CASES = [
     ("few-row three-launch form (16 rows)", 1, 16, 2048, (32, 64), 4, 2, "bf16", 64, 1.0, [(0, 3)], None),
     ("few-row MFMA form, 12 rows", 3, 4, 2048, (32, 64), 8, 2, "bf16", 64, 1.0, [], None),
     ("few-row, no transform, K = 10560, A8", 2, 2, 10560, None, 8, 2, "f32", 64, 1.0, [(1, 1)], None),
+    # fp32 inputs of the few-row kernel (the fp32 transform path)
+    ("few-row fp32, (16, 16), 16 rows", 1, 16, 256, (16, 16), 4, 2, "f32", 128, 1.0, [(0, 2)], None),
+    ("few-row fp32, (16, 16), 4 rows", 1, 4, 256, (16, 16), 4, 2, "f32", 128, 1.0, [], None),
+    ("few-row fp32, (32, 64), 2 rows", 2, 1, 2048, (32, 64), 4, 2, "f32", 64, 1.0, [], None),
+    ("few-row fp32 loop-sequential (16, 16)", 4, 16, 256, (16, 16), 4, 1, "f32", 128, 1.0, [], None),
 ]
 
 
