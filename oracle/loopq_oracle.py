@@ -46,6 +46,15 @@ design notes):
   output column per row, ``[N][K]``) ``w~_n = vec_r(P1^-1 W_n P2^-T)``;
 * the transformed activation is formed in fp64 and rounded once to fp32
   before it is quantized.
+* CTA ("paper_specification.yaml", ``loopq_components.cta``, Section 4.3,
+  Eq.(7), which the pages do not print; ``experiment_hyperparameters``
+  ``cta_rank: 8``; "The arms": CTA at exact identity in the untrained arm): at
+  the transition into loop t (t >= 1) a row h of the state becomes
+  ``a_{t-1} * h + b_{t-1} + eta_{t-1} * U (V^T h)`` -- an elementwise affine
+  map plus a scalar-gated low-rank term, U and V (``[K][r]``) shared by every
+  transition, a, b (``[K]``) and eta per transition; identity is a = 1, b = 0,
+  eta = 0.  It is formed in fp64 and stored in the state's type (bf16: round
+  to nearest, ties to even; fp32: one fp32 rounding) before loop t reads it.
 
 Functions with no pin against anything but themselves: none -- every function
 here is pinned by ``tests/test_oracle_pins.py``.
@@ -345,6 +354,58 @@ def looped_forward_sets(xs, factor_sets, clips, bits, weight_sets, group_w: int,
         out.append(linear(xs[t], P1, P2, float(clips[t]), int(bits[t]), qw, sw, group_w)[0])
     return np.stack(out)
 
+
+
+# --------------------------------------------------------------------------
+# CTA: the loop-transition adapter ("paper_specification.yaml",
+#      loopq_components.cta, Section 4.3, Eq.(7); cta_rank 8)
+# --------------------------------------------------------------------------
+
+def round_bf16(v) -> np.ndarray:
+    """``v`` (fp64) rounded to the nearest bfloat16 value (8 significant bits,
+    fp32's exponent range), ties to even; returned as fp64.  Values past the
+    largest finite bf16 are not handled (the adapted states stay far below)."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)                      # v = m 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                 # below 2^-126 the spacing stays 2^-133
+    ulp = np.ldexp(1.0, e - 8)
+    return np.rint(v / ulp) * ulp           # v / ulp is exact (power of two)
+
+
+def cta_transition(h, U, V, a, b, eta) -> np.ndarray:
+    """One loop transition of CTA on the rows of ``h`` ``[M][K]``:
+    ``a * h + b + eta * U (V^T h)`` per row, in fp64.  ``U`` and ``V`` are
+    ``[K][r]`` (the shared low-rank pair), ``a`` and ``b`` ``[K]`` and ``eta`` a
+    scalar (this transition's parameters)."""
+    h = np.asarray(h, dtype=np.float64)
+    U = np.asarray(U, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    z = h @ V                               # [M][r]: V^T h of every row
+    return np.asarray(a, dtype=np.float64) * h + np.asarray(b, dtype=np.float64) + float(eta) * (z @ U.T)
+
+
+def cta_loop_inputs(xs, U, V, a_sets, b_sets, etas, state: str) -> np.ndarray:
+    """The inputs the loops read with CTA at every transition: loop 0 reads
+    ``xs[0]``; loop t >= 1 reads transition t-1 applied to ``xs[t]``, stored
+    as ``state`` ("bf16" or "fp32").  ``a_sets``/``b_sets`` are ``[T-1][K]``,
+    ``etas`` ``[T-1]``; returns fp64 ``[T][M][K]``."""
+    xs = np.asarray(xs, dtype=np.float64)
+    T = xs.shape[0]
+    if not (len(a_sets) >= T - 1 and len(b_sets) >= T - 1 and len(etas) >= T - 1):
+        raise ValueError("one set of transition parameters per transition")
+    store = {"bf16": round_bf16, "fp32": lambda v: v.astype(np.float32).astype(np.float64)}[state]
+    out = [xs[0]]
+    for t in range(1, T):
+        out.append(store(cta_transition(xs[t], U, V, a_sets[t - 1], b_sets[t - 1], etas[t - 1])))
+    return np.stack(out)
+
+
+def looped_forward_cta(xs, P1, P2, clips, bits: int, qw, sw16, group_w: int, U, V, a_sets, b_sets, etas,
+                       state: str) -> np.ndarray:
+    """:func:`looped_forward` with CTA at the loop transitions: loop t >= 1
+    quantizes the adapted state of :func:`cta_loop_inputs`."""
+    return looped_forward(cta_loop_inputs(xs, U, V, a_sets, b_sets, etas, state), P1, P2, clips, bits, qw,
+                          sw16, group_w)
 
 
 # --------------------------------------------------------------------------
