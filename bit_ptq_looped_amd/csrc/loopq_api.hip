@@ -655,6 +655,12 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       if (N % 16) return LOOPQ_ERR_UNSUPPORTED;
       *bytes = align256((size_t)M * 2 * N * 4) + act_bytes(1, M, 2 * (int64_t)N, N, code_format(bits_a));
       return LOOPQ_OK;
+    case LOOPQ_OP_LOOPED_FORWARD_CTA:  // the looped forward's region, then the adapted loop inputs
+      if (T <= 0 || M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (T > LOOPQ_MAX_LOOPS || K % 32) return LOOPQ_ERR_UNSUPPORTED;
+      if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
+      *bytes = align256(act_bytes(T, M, K, N, code_format(bits_a))) + align256((size_t)T * M * K * 4);
+      return LOOPQ_OK;
     case LOOPQ_OP_HESSIAN:
       if (M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (K % 32 || K > kHessianMaxK || M > kHessianMaxRows) return LOOPQ_ERR_UNSUPPORTED;
@@ -1096,6 +1102,63 @@ int32_t loopq_looped_forward_per_token(const void* x, int32_t dtype, int32_t T, 
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   TimingScope ts(LOOPQ_KERNEL_GEMM, s);
   return hip_status(run_gemm(b, fmt, rows, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s));
+}
+
+int32_t loopq_cta_apply(const void* h, int32_t dtype, int32_t M, int32_t K, const float* U,
+                        const float* V, int32_t rank, const float* a, const float* b, float eta,
+                        void* out, void* stream) {
+  if (dtype != LOOPQ_F32 && dtype != LOOPQ_BF16) return LOOPQ_ERR_INVALID_ARG;
+  if (M < 0 || K <= 0 || rank <= 0) return LOOPQ_ERR_INVALID_ARG;
+  if (K % 32 || rank > cta_max_rank()) return LOOPQ_ERR_UNSUPPORTED;
+  if (!isfinite(eta)) return LOOPQ_ERR_INVALID_ARG;
+  if (M == 0) return LOOPQ_OK;
+  if (!h || !out || !U || !V || !a || !b) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(h, 16) || !aligned(out, 16) || !aligned(U, 4) || !aligned(V, 4) || !aligned(a, 4) ||
+      !aligned(b, 4))
+    return LOOPQ_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)M * K * (dtype == LOOPQ_BF16 ? 2 : 4);
+  const uintptr_t hi = reinterpret_cast<uintptr_t>(h), oi = reinterpret_cast<uintptr_t>(out);
+  if (hi != oi && hi < oi + bytes && oi < hi + bytes) return LOOPQ_ERR_INVALID_ARG;  // partial overlap
+  return hip_status(launch_cta(h, dtype == LOOPQ_BF16, M, K, U, V, rank, a, b, &eta, 1, M, 0, out,
+                               as_stream(stream)));
+}
+
+int32_t loopq_looped_forward_cta(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
+                                 int32_t N, const float* P1, int32_t n1, const float* P2, int32_t n2,
+                                 const float* clips_host, int32_t bits_a, const void* w_codes,
+                                 const void* w_scales, int32_t group_w, float* y, int32_t schedule,
+                                 const float* U, const float* V, int32_t rank, const float* a_sets,
+                                 const float* b_sets, const float* eta_host, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  ClipTable clips;
+  bool empty = false;
+  int32_t st = check_forward(x, dtype, T, M, K, N, P1, n1, P2, n2, clips_host, bits_a, w_codes, w_scales,
+                             group_w, y, schedule, &clips, &empty);
+  if (st != LOOPQ_OK) return st;
+  if (T > 1) {
+    if (rank <= 0) return LOOPQ_ERR_INVALID_ARG;
+    if (rank > cta_max_rank()) return LOOPQ_ERR_UNSUPPORTED;
+    if (!U || !V || !a_sets || !b_sets || !eta_host) return LOOPQ_ERR_INVALID_ARG;
+    if (!aligned(U, 4) || !aligned(V, 4) || !aligned(a_sets, 4) || !aligned(b_sets, 4)) return LOOPQ_ERR_ALIGNMENT;
+    for (int t = 0; t + 1 < T; ++t)
+      if (!isfinite(eta_host[t])) return LOOPQ_ERR_INVALID_ARG;
+  }
+  if (empty) return LOOPQ_OK;
+  size_t need = 0, base = 0;
+  loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_CTA, T, M, K, N, bits_a, &need);
+  loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, bits_a, &base);
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  if (T == 1)  // no transition
+    return loopq_looped_forward(x, dtype, T, M, K, N, P1, n1, P2, n2, clips_host, bits_a, w_codes, w_scales,
+                                group_w, y, schedule, workspace, base, stream);
+  void* xa = static_cast<unsigned char*>(workspace) + align256(base);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = launch_cta(x, dtype == LOOPQ_BF16, (int64_t)T * M, K, U, V, rank, a_sets, b_sets, eta_host,
+                            T - 1, M, -1, xa, s);
+  if (e != hipSuccess) return LOOPQ_ERR_HIP;
+  return loopq_looped_forward(xa, dtype, T, M, K, N, P1, n1, P2, n2, clips_host, bits_a, w_codes, w_scales,
+                              group_w, y, schedule, workspace, base, stream);
 }
 
 int32_t loopq_recurrent_adapter(const float* s0, const float* e, int32_t T, int32_t M, int32_t N,

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
+#include <string.h>
 
 namespace loopq {
 
@@ -235,6 +236,14 @@ hipError_t launch_hessian(const float* x, int rows, int K, float* H, float* part
 
 // x [M][2N] = cat(s [M][N], e [M][N]) per row (fp32, N % 4 == 0, 16-byte aligned)
 hipError_t launch_concat_state(const float* s, const float* e, float* x, int M, int N, hipStream_t st);
+
+// CTA over `rows` rows of K: row i takes transition i / rows_per_tr + first
+// (a negative transition copies the row unchanged); a, b [ntr][K], eta [ntr]
+// (host), U, V [K][r], 1 <= r <= cta_max_rank(), K % 32 == 0
+hipError_t launch_cta(const void* h, int bf16, int64_t rows, int K, const float* U, const float* V, int r,
+                      const float* a, const float* b, const float* eta, int ntr, int64_t rows_per_tr, int first,
+                      void* out, hipStream_t s);
+int cta_max_rank();
 
 hipError_t reset_status(hipStream_t s);
 hipError_t read_status(int* host_status, hipStream_t s);

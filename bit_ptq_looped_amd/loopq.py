@@ -30,7 +30,7 @@ LOOPQ_F32, LOOPQ_BF16 = 0, 1
 LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
 LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD, LOOPQ_OP_LOOPED_FORWARD_EX = 1, 2, 3, 4
 LOOPQ_OP_HESSIAN, LOOPQ_OP_QUANT_PER_TOKEN, LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 5, 6, 7
-LOOPQ_OP_RECURRENT_ADAPTER = 8
+LOOPQ_OP_RECURRENT_ADAPTER, LOOPQ_OP_LOOPED_FORWARD_CTA = 8, 9
 LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM, LOOPQ_KERNEL_DECODE = 0, 1, 2, 3
 LOOPQ_KERNEL_HESSIAN, LOOPQ_KERNEL_QUANT_TOKEN = 4, 5
 
@@ -62,6 +62,9 @@ SIGNATURES = {
     "loopq_quant_act_per_token": ([_P, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _P, _P, _Z, _P], _I),
     "loopq_looped_forward_per_token": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _P, _Z,
                                         _P], _I),
+    "loopq_cta_apply": ([_P, _I, _I, _I, _P, _P, _I, _P, _P, _F, _P, _P], _I),
+    "loopq_looped_forward_cta": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _I,
+                                  _P, _P, _I, _P, _P, _P, _P, _Z, _P], _I),
     "loopq_timing_enable": ([_I], _I),
     "loopq_timing_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)], _I),
     "loopq_timing_reset": ([], _I),
@@ -216,6 +219,33 @@ def loopq_looped_forward(x, P1, P2, clips: Sequence[float], bits_a: int, w_codes
                                        _ptr(w_scales), group_w, _ptr(y), schedule, _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
            "loopq_looped_forward")
+
+
+def loopq_cta_apply(h, U, V, a, b, eta: float, out, stream=None):
+    """One CTA transition on the rows of h [M][K] into out (may be h)."""
+    M, K = h.shape
+    _check(load().loopq_cta_apply(_ptr(h), _dtype_code(h), M, K, _ptr(U), _ptr(V), int(U.shape[1]), _ptr(a),
+                                  _ptr(b), float(eta), _ptr(out), _stream(stream)),
+           "loopq_cta_apply")
+
+
+def loopq_looped_forward_cta(x, P1, P2, clips: Sequence[float], bits_a: int, w_codes, w_scales,
+                             group_w: int, N: int, y, schedule: int, U, V, a_sets, b_sets,
+                             etas: Sequence[float], workspace, stream=None):
+    """loopq_looped_forward with CTA transition t - 1 applied to loop t >= 1."""
+    T, M, K = x.shape
+    p1, n1, p2, n2 = _factor_args(P1, P2)
+    c = (ctypes.c_float * T)(*[float(v) for v in clips])
+    ev = [float(v) for v in etas][: max(T - 1, 0)]
+    e = (ctypes.c_float * max(len(ev), 1))(*ev)
+    rank = int(U.shape[1]) if U is not None else 0
+    _check(load().loopq_looped_forward_cta(_ptr(x), _dtype_code(x), T, M, K, N, p1, n1, p2, n2,
+                                           ctypes.cast(c, ctypes.c_void_p), bits_a, _ptr(w_codes),
+                                           _ptr(w_scales), group_w, _ptr(y), schedule, _ptr(U), _ptr(V), rank,
+                                           _ptr(a_sets), _ptr(b_sets), ctypes.cast(e, ctypes.c_void_p),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _stream(stream)),
+           "loopq_looped_forward_cta")
 
 
 def loopq_looped_forward_ex(x, factor_sets, clips: Sequence[float], bits: Sequence[int], weight_sets,

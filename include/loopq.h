@@ -93,7 +93,8 @@ typedef enum {
   LOOPQ_OP_HESSIAN = 5,           /* rows as M; T, N and bits_a ignored */
   LOOPQ_OP_QUANT_PER_TOKEN = 6,   /* M, K; T, N and bits_a ignored */
   LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 7, /* T, M, K, N, bits_a */
-  LOOPQ_OP_RECURRENT_ADAPTER = 8  /* M, N, bits_a (K = 2N implied); T and K ignored */
+  LOOPQ_OP_RECURRENT_ADAPTER = 8, /* M, N, bits_a (K = 2N implied); T and K ignored */
+  LOOPQ_OP_LOOPED_FORWARD_CTA = 9  /* T, M, K, N, bits_a; dtype bytes taken as 4 */
 } loopq_op;
 
 /* ABI version of the loaded library (LOOPQ_ABI_VERSION it was built with). */
@@ -280,6 +281,44 @@ int32_t loopq_looped_forward_ex(const void* x, int32_t dtype, int32_t T, int32_t
                                 const int32_t* sets_host, const int32_t* bits_host,
                                 const float* clips_host, float* y, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* CTA, one loop transition on M rows: out = a * h + b + eta * U (V^T h) per
+ * row.  Page: "paper_specification.yaml", loopq_components.cta (Section 4.3,
+ * Eq.(7), not printed there: an affine plus gated low-rank adapter applied
+ * only at loop transitions, U and V shared, a_t, b_t and eta_t per
+ * transition), experiment_hyperparameters cta_rank 8; identity (a = 1,
+ * b = 0, eta = 0) is the untrained arm's CTA ("LoopQ 4-bit quantization of
+ * Ouro-1.4B -- raw artifacts", "The arms").
+ * h, out [M][K] in `dtype` (16-byte aligned; out may be h itself, any other
+ * overlap is an error); U, V [K][rank] fp32 row-major, a, b [K] fp32 (device
+ * memory, 4-byte aligned); eta a host scalar.  V^T h is accumulated in fp32
+ * in a fixed order (deterministic); the result is formed as
+ * fma(eta, sum_j U[k][j] z_j, fma(a_k, h_k, b_k)) and stored in `dtype`
+ * (bf16: round to nearest, ties to even).  K % 32 == 0 and 1 <= rank <= 16,
+ * else LOOPQ_ERR_UNSUPPORTED; M == 0 is a no-op. */
+int32_t loopq_cta_apply(const void* h, int32_t dtype, int32_t M, int32_t K, const float* U,
+                        const float* V, int32_t rank, const float* a, const float* b, float eta,
+                        void* out, void* stream);
+
+/* a6 with CTA at the loop transitions: loop 0 reads x_0; loop t >= 1 reads
+ * transition t - 1 of loopq_cta_apply applied to x_t (a_sets + (t-1) K,
+ * b_sets + (t-1) K, eta_host[t-1]), stored in the input's type.  Pages as
+ * for loopq_cta_apply and loopq_looped_forward.  The adapted loop inputs
+ * (and a copy of loop 0) are written to the workspace after the region
+ * loopq_looped_forward uses, then that path runs on them with the same
+ * schedule; a_sets, b_sets [T-1][K] and U, V as for loopq_cta_apply (unused
+ * when T == 1), eta_host [T-1] host memory.  Other arguments and errors as
+ * loopq_looped_forward.  Workspace:
+ * loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_CTA, T, M, K, N, bits_a, ...),
+ * whose first loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD, ...) bytes are
+ * laid out as loopq_looped_forward's (loopq_export_act_codes reads them). */
+int32_t loopq_looped_forward_cta(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
+                                 int32_t N, const float* P1, int32_t n1, const float* P2, int32_t n2,
+                                 const float* clips_host, int32_t bits_a, const void* w_codes,
+                                 const void* w_scales, int32_t group_w, float* y, int32_t schedule,
+                                 const float* U, const float* V, int32_t rank, const float* a_sets,
+                                 const float* b_sets, const float* eta_host, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* A dependent recurrence through one quantized linear (the adapter loop).
  * Page: "Quantizing Looped Transformers: Feedback Exposure and Calibration

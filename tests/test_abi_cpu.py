@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 24
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), n
         assert n in loopq.SIGNATURES, n
@@ -293,3 +293,52 @@ def test_noalloc_linear_rejects_on_host(lib):
     assert need > 64 << 20
     assert f(FAKE, 0, 32768, 2048, 2048, None, 0, None, 0, 1.0, 4, FAKE, FAKE, 32, FAKE, None) == \
         loopq.LOOPQ_ERR_WORKSPACE
+
+
+def test_cta_entries_reject_on_host(lib):
+    """Argument errors of the CTA calls return before any HIP call."""
+    f = lambda *a: _raw(lib, "loopq_cta_apply", *a)
+    # h, dtype, M, K, U, V, rank, a, b, eta, out, stream
+    ok = (FAKE, 1, 4, 256, FAKE, FAKE, 8, FAKE, FAKE, 0.5, FAKE + (1 << 20), None)
+
+    def vary(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert vary(1, 2) == loopq.LOOPQ_ERR_INVALID_ARG           # dtype
+    assert vary(3, 250) == loopq.LOOPQ_ERR_UNSUPPORTED          # K % 32
+    assert vary(6, 0) == loopq.LOOPQ_ERR_INVALID_ARG            # rank
+    assert vary(6, 17) == loopq.LOOPQ_ERR_UNSUPPORTED           # rank above 16
+    assert vary(9, float("nan")) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert vary(4, None) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert vary(0, FAKE + 8) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert vary(7, FAKE + 2) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert vary(10, FAKE + 16) == loopq.LOOPQ_ERR_INVALID_ARG   # out overlaps h, not in place
+    assert vary(2, 0) == loopq.LOOPQ_OK                         # no rows
+    g = lambda *a: _raw(lib, "loopq_looped_forward_cta", *a)
+    op = loopq.LOOPQ_OP_LOOPED_FORWARD_CTA
+    ws = loopq.loopq_workspace_bytes(op, 4, 64, 2048, 512, 4)
+    base = loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LOOPED_FORWARD, 4, 64, 2048, 512, 4)
+    assert ws >= base + 4 * 64 * 2048 * 4
+    clips = (ctypes.c_float * 4)(1.0, 1.0, 1.0, 1.0)
+    etas = (ctypes.c_float * 3)(0.1, 0.2, 0.3)
+    bad_etas = (ctypes.c_float * 3)(0.1, float("inf"), 0.3)
+    # x, dtype, T, M, K, N, P1, n1, P2, n2, clips, bits, w_codes, w_scales, group_w, y, schedule,
+    # U, V, rank, a_sets, b_sets, etas, workspace, bytes, stream
+    base_args = [FAKE, 1, 4, 64, 2048, 512, None, 0, None, 0, ctypes.cast(clips, ctypes.c_void_p), 4, FAKE, FAKE,
+                 32, FAKE, 0, FAKE, FAKE, 8, FAKE, FAKE, ctypes.cast(etas, ctypes.c_void_p), FAKE, ws, None]
+
+    def gv(**kw):
+        a = list(base_args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return g(*a)
+    assert gv(i19=0) == loopq.LOOPQ_ERR_INVALID_ARG                 # rank
+    assert gv(i19=17) == loopq.LOOPQ_ERR_UNSUPPORTED
+    assert gv(i17=None) == loopq.LOOPQ_ERR_INVALID_ARG              # U
+    assert gv(i22=ctypes.cast(bad_etas, ctypes.c_void_p)) == loopq.LOOPQ_ERR_INVALID_ARG
+    assert gv(i20=FAKE + 2) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert gv(i24=ws - 1) == loopq.LOOPQ_ERR_WORKSPACE
+    assert gv(i23=FAKE + 16) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert gv(i4=2040) == loopq.LOOPQ_ERR_UNSUPPORTED              # K % 32
+    assert gv(i3=0, i0=None, i23=None, i24=0) == loopq.LOOPQ_OK     # no rows
