@@ -64,6 +64,7 @@ def parse():
     p.add_argument("--no-hessian", action="store_true", help="skip the trajectory Hessian measurement")
     p.add_argument("--no-recurrence", action="store_true", help="skip the adapter recurrence measurement")
     p.add_argument("--no-per-token", action="store_true", help="skip the per-token measurement")
+    p.add_argument("--no-cta", action="store_true", help="skip the CTA adapter measurement")
     p.add_argument("--no-huginn-core", action="store_true", help="skip the Huginn-like core linears")
     p.add_argument("--profile-stack", type=int, default=0,
                    help="only run this many headline steps (for rocprofv3), no JSON")
@@ -122,7 +123,7 @@ def fold_inclusive(ops, element_groups, gemm_ms):
             "bound_tops": ops / bound / 1e12, "frac": bound * 1e3 / gemm_ms if gemm_ms > 0 else None}
 
 
-def timing_read(lq, n=6):
+def timing_read(lq, n=7):
     return lq.loopq_timing_read(n)
 
 
@@ -612,6 +613,69 @@ def hessian_bench(lq, torch, mods, T, M, steps, warmup):
 HUGINN_BLOCK_ROWS = 256
 
 
+def cta_bench(lq, synth, torch, steps):
+    """CTA at the loop transitions of the 2.6B-like stack's q|k|v input:
+    M = 8192 rows, K = 2560, N = 7680, T = 4 loops, bf16 state, rank 8.  The
+    adapter kernel runs over all T*M rows of one loopq_looped_forward_cta call
+    (loop 0 copied, loops 1..3 adapted); the call is timed against the plain
+    loopq_looped_forward (weight-stationary) on the same inputs."""
+    M, K, N, T, r = 8192, 2560, 7680, 4, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7007)
+    rng = synth.seeded_rng(synth.TEST, 7007)
+    x = torch.randn((T, M, K), generator=gen, device="cuda").to(torch.bfloat16)
+    U = torch.randn((K, r), generator=gen, device="cuda") / K ** 0.5
+    V = torch.randn((K, r), generator=gen, device="cuda") / K ** 0.5
+    a = 1.0 + 0.1 * torch.randn((T - 1, K), generator=gen, device="cuda")
+    b = 0.05 * torch.randn((T - 1, K), generator=gen, device="cuda")
+    eta = [0.3, -0.2, 0.5]
+    P1 = torch.from_numpy(synth.haar_orthogonal(40, rng)).cuda()
+    P2 = torch.from_numpy(synth.haar_orthogonal(64, rng)).cuda()
+    codes, scales = lq.empty_packed_weights(K, N, 32)
+    codes.copy_(torch.randint(0, 256, codes.shape, dtype=torch.uint8, device="cuda", generator=gen))
+    st = torch.rand(scales.numel() // 2, device="cuda", generator=gen) * 0.004 + 0.001
+    scales.copy_(st.to(torch.float16).view(torch.uint8))
+    y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_CTA, T, M, K, N, 4)
+    clips = [1.0] * T
+    WS = lq.LOOPQ_SCHED_WEIGHT_STATIONARY
+
+    def plain(n):
+        for _ in range(n):
+            lq.loopq_looped_forward(x, P1, P2, clips, 4, codes, scales, 32, N, y, WS, ws)
+
+    def with_cta(n):
+        for _ in range(n):
+            lq.loopq_looped_forward_cta(x, P1, P2, clips, 4, codes, scales, 32, N, y, WS, U, V, a, b, eta, ws)
+
+    plain(1)
+    with_cta(1)
+    t_plain, walls_p, kern_p = median_blocks(torch, lq, plain, steps)
+    t_cta, walls_c, kern_c = median_blocks(torch, lq, with_cta, steps)
+    lq.loopq_timing_reset()
+    lq.loopq_timing_enable(True)
+    with_cta(steps)
+    torch.cuda.synchronize()
+    lq.loopq_timing_enable(False)
+    cms, cn = timing_read(lq)[lq.LOOPQ_KERNEL_CTA]
+    cta_ms = cms / max(cn, 1)
+    # algorithmic bytes of one adapter launch: read and write every row once,
+    # plus a, b of each transition and U, V
+    alg = 2.0 * T * M * K * 2 + (T - 1) * K * 4 * 2 + 2 * K * r * 4
+    out = {"workload": "CTA at the transitions of the 2.6B-like stack's q|k|v input, M=8192, K=2560, N=7680, T=4, "
+                       "bf16 state, rank 8, weight-stationary",
+           "forward_ms": t_plain * 1e3, "forward_cta_ms": t_cta * 1e3,
+           "overhead_frac": (t_cta - t_plain) / t_plain,
+           "cta_kernel_ms": cta_ms, "cta_kernel_launches": cn // max(steps, 1),
+           "cta_alg_bytes": alg, "cta_gbps": alg / (cta_ms * 1e-3) / 1e9,
+           "cta_frac_hbm_peak": alg / (cta_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "blocks_ms": {"forward": walls_p, "forward_cta": walls_c},
+           "blocks_kernel_ms": {"forward": kern_p, "forward_cta": kern_c}}
+    del x, y, ws, codes, scales
+    torch.cuda.empty_cache()
+    return out
+
+
 def huginn_core_bench(lq, synth, torch, steps):
     """The Huginn-like core linears at M = 2048 token rows: Wqkv 5280 -> 15840
     and mlp.proj 17920 -> 5280, weight groups of 128, A8 activations in groups
@@ -1039,6 +1103,9 @@ def secondary(lq, synth, torch, args, out, stack_wl):
         torch.cuda.empty_cache()
     if not args.no_huginn_core:
         out["huginn_core"] = huginn_core_bench(lq, synth, torch, 2)
+    if not args.no_cta:
+        print("bench: cta", file=sys.stderr, flush=True)
+        out["cta"] = cta_bench(lq, synth, torch, 4)
     if not args.no_recurrence:
         out["recurrence"] = [recurrence_bench(lq, synth, torch, 1, 32, 20),
                              recurrence_bench(lq, synth, torch, 2048, 32, 2)]

@@ -9,21 +9,25 @@
 // eta = 0, and stores the result in the state's type (bf16 rounded to nearest
 // even, or fp32).
 //
-// One work-group takes kRows consecutive rows.  Pass 1 forms z = V^T h of
-// each row (each thread runs over its k in order, then a butterfly within the
-// wave and the four waves in order: a fixed reduction order, so the result
-// does not depend on timing); pass 2 re-reads the rows (from L2) and writes
+// A work-group takes up to 16 consecutive rows of one transition block (4
+// per wave) and runs over K in tiles of 512 (8 consecutive elements per
+// lane).  Pass 1 forms z = V^T h of each row: the tile of V is staged in LDS
+// (element k of column j at [j][k % 8][lane], conflict-free reads), every
+// lane accumulates its elements in order and the wave sums its lanes by a
+// butterfly -- a fixed order, so the result does not depend on timing.  Pass 2
+// re-reads the rows (from L2) with the tiles of U, a and b in LDS and writes
 // fma(eta, sum_j U[k][j] z_j, fma(a_k, h_k, b_k)).  Rows whose transition
-// index is negative are copied unchanged (loop 0 of a looped forward).  A row
-// is read completely before any of its elements is written, so the output
-// may be the input itself.
+// index is negative are copied unchanged (loop 0 of a looped forward).  A
+// work-group reads all of its rows before it writes any of them and rows of
+// different work-groups are disjoint, so the output may be the input itself.
 #include "loopq_internal.h"
 #include "quant_core.h"
 
 namespace loopq {
 namespace {
 
-constexpr int kRows = 4;      // rows per work-group
+constexpr int kRows = 16;     // rows per work-group (4 per wave)
+constexpr int kTile = 512;    // elements of K per tile (8 per lane)
 constexpr int kMaxRank = 16;  // largest r
 
 struct CtaArgs {
@@ -36,8 +40,8 @@ struct CtaArgs {
   ClipTable eta;     // eta of each transition
   int64_t rows;
   int K, r, bf16;
-  int64_t rows_per_tr;  // rows of one transition block
-  int first;            // transition of the first block (-1: copy it)
+  int64_t rows_per_tr;  // rows of one transition block (blockIdx.y)
+  int first;            // transition of block 0 (-1: copy it)
 };
 
 // 8 consecutive elements of row m from k (k % 8 == 0)
@@ -79,80 +83,106 @@ __device__ __forceinline__ void store8(const CtaArgs& g, int64_t m, int k, const
   }
 }
 
+template <int R>  // R >= r: columns of U and V (those past r are zero)
 __global__ __launch_bounds__(256) void cta_kernel(CtaArgs g) {
-  __shared__ float red[4][kRows][kMaxRank];
+  __shared__ float sW[R * kTile];  // V, then U: column j, element k0 + 8 l + e at [j][e][l]
+  __shared__ float sA[kTile], sB[kTile];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row0 = (int64_t)blockIdx.x * kRows;
   const int K = g.K, r = g.r;
-  int tr[kRows];
-#pragma unroll
-  for (int i = 0; i < kRows; ++i)
-    tr[i] = row0 + i < g.rows ? (int)((row0 + i) / g.rows_per_tr) + g.first : -2;  // -2: past the end
+  const int tr = (int)blockIdx.y + g.first;  // uniform over the work-group
+  const int64_t rb0 = (int64_t)blockIdx.y * g.rows_per_tr;
+  const int64_t rb1 = min(rb0 + g.rows_per_tr, g.rows);
+  const int64_t r0 = rb0 + (int64_t)blockIdx.x * kRows + wave * 4;  // this wave's first row
+  const int nr = (int)max((int64_t)0, min((int64_t)4, rb1 - r0));    // its rows (0..4)
 
-  // pass 1: z = V^T h of every adapted row
-  float acc[kRows][kMaxRank];
-#pragma unroll
-  for (int i = 0; i < kRows; ++i)
-#pragma unroll
-    for (int j = 0; j < kMaxRank; ++j) acc[i][j] = 0.0f;
-  for (int k = tid * 8; k < K; k += 256 * 8) {
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-      if (tr[i] < 0) continue;  // uniform over the work-group
-      float hv[8];
-      load8(g, row0 + i, k, hv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float* vk = g.V + (int64_t)(k + e) * r;
-#pragma unroll
-        for (int j = 0; j < kMaxRank; ++j)
-          if (j < r) acc[i][j] = fmaf(vk[j], hv[e], acc[i][j]);
-      }
+  // stage elements [k0, k0 + kn) of the columns of W ([K][r]) into sW
+  auto stage = [&](const float* __restrict__ W, int k0, int kn) {
+    for (int q = tid; q < kn * R; q += 256) {
+      const int kk = q / R, j = q - kk * R;
+      sW[j * kTile + (kk & 7) * 64 + (kk >> 3)] = j < r ? W[(int64_t)(k0 + kk) * r + j] : 0.0f;
     }
-  }
-#pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    if (tr[i] < 0) continue;
-#pragma unroll
-    for (int j = 0; j < kMaxRank; ++j) {
-      if (j >= r) continue;
-      float v = acc[i][j];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      if (lane == 0) red[wave][i][j] = v;
-    }
-  }
-  __syncthreads();
-  float z[kRows][kMaxRank];
-#pragma unroll
-  for (int i = 0; i < kRows; ++i)
-#pragma unroll
-    for (int j = 0; j < kMaxRank; ++j)
-      z[i][j] = (tr[i] >= 0 && j < r) ? ((red[0][i][j] + red[1][i][j]) + red[2][i][j]) + red[3][i][j] : 0.0f;
+  };
 
-  // pass 2: the adapted rows (copied rows unchanged)
-  for (int k = tid * 8; k < K; k += 256 * 8) {
+  float z[4][R];
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-      if (tr[i] == -2) continue;
-      float hv[8];
-      load8(g, row0 + i, k, hv);
-      if (tr[i] >= 0) {
-        const float* ak = g.a + (int64_t)tr[i] * K + k;
-        const float* bk = g.b + (int64_t)tr[i] * K + k;
-        const float eta = g.eta.c[tr[i]];
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < R; ++j) z[i][j] = 0.0f;
+
+  if (tr >= 0) {  // pass 1: z = V^T h
+    for (int k0 = 0; k0 < K; k0 += kTile) {
+      const int kn = min(kTile, K - k0);
+      __syncthreads();  // the previous tile is no longer read
+      stage(g.V, k0, kn);
+      __syncthreads();
+      const int k = k0 + 8 * lane;
+      if (k < k0 + kn) {
+        float hv[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nr) load8(g, r0 + i, k, hv[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float* uk = g.U + (int64_t)(k + e) * r;
-          float s = 0.0f;
+          float v[R];
 #pragma unroll
-          for (int j = 0; j < kMaxRank; ++j)
-            if (j < r) s = fmaf(uk[j], z[i][j], s);
-          hv[e] = fmaf(eta, s, fmaf(ak[e], hv[e], bk[e]));
+          for (int j = 0; j < R; ++j) v[j] = sW[j * kTile + e * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < nr)
+#pragma unroll
+              for (int j = 0; j < R; ++j) z[i][j] = fmaf(v[j], hv[i][e], z[i][j]);
         }
       }
-      store8(g, row0 + i, k, hv);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        float v = z[i][j];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        z[i][j] = v;
+      }
+  }
+
+  // pass 2: the adapted rows (copied rows unchanged)
+  const float eta = tr >= 0 ? g.eta.c[tr] : 0.0f;
+  for (int k0 = 0; k0 < K; k0 += kTile) {
+    const int kn = min(kTile, K - k0);
+    if (tr >= 0) {
+      __syncthreads();
+      stage(g.U, k0, kn);
+      for (int q = tid; q < kn; q += 256) {
+        sA[(q & 7) * 64 + (q >> 3)] = g.a[(int64_t)tr * K + k0 + q];
+        sB[(q & 7) * 64 + (q >> 3)] = g.b[(int64_t)tr * K + k0 + q];
+      }
+      __syncthreads();
+    }
+    const int k = k0 + 8 * lane;
+    if (k >= k0 + kn || nr == 0) continue;
+    float hv[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < nr) load8(g, r0 + i, k, hv[i]);
+    if (tr >= 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float u[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) u[j] = sW[j * kTile + e * 64 + lane];
+        const float ak = sA[e * 64 + lane], bk = sB[e * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = 0.0f;
+#pragma unroll
+          for (int j = 0; j < R; ++j) s = fmaf(u[j], z[i][j], s);
+          hv[i][e] = fmaf(eta, s, fmaf(ak, hv[i][e], bk));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < nr) store8(g, r0 + i, k, hv[i]);
   }
 }
 
@@ -180,11 +210,16 @@ hipError_t launch_cta(const void* h, int bf16, int64_t rows, int K, const float*
   g.rows_per_tr = rows_per_tr;
   g.first = first;
   // every row's transition must have parameters
-  const int64_t last_tr = (rows - 1) / rows_per_tr + first;
-  if (last_tr >= ntr) return hipErrorInvalidValue;
-  const int64_t blocks = (rows + kRows - 1) / kRows;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(cta_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g);
+  const int64_t nblk = (rows + rows_per_tr - 1) / rows_per_tr;
+  if (nblk - 1 + first >= ntr || nblk > 65535) return hipErrorInvalidValue;
+  const int64_t per_blk = min(rows_per_tr, rows);
+  const int64_t gx = (per_blk + kRows - 1) / kRows;
+  if (gx > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)gx, (unsigned)nblk);
+  if (r <= 8)
+    hipLaunchKernelGGL(cta_kernel<8>, grid, dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL(cta_kernel<16>, grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 

@@ -1119,8 +1119,9 @@ int32_t loopq_cta_apply(const void* h, int32_t dtype, int32_t M, int32_t K, cons
   const size_t bytes = (size_t)M * K * (dtype == LOOPQ_BF16 ? 2 : 4);
   const uintptr_t hi = reinterpret_cast<uintptr_t>(h), oi = reinterpret_cast<uintptr_t>(out);
   if (hi != oi && hi < oi + bytes && oi < hi + bytes) return LOOPQ_ERR_INVALID_ARG;  // partial overlap
-  return hip_status(launch_cta(h, dtype == LOOPQ_BF16, M, K, U, V, rank, a, b, &eta, 1, M, 0, out,
-                               as_stream(stream)));
+  hipStream_t s = as_stream(stream);
+  TimingScope ts(LOOPQ_KERNEL_CTA, s);
+  return hip_status(launch_cta(h, dtype == LOOPQ_BF16, M, K, U, V, rank, a, b, &eta, 1, M, 0, out, s));
 }
 
 int32_t loopq_looped_forward_cta(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
@@ -1154,9 +1155,12 @@ int32_t loopq_looped_forward_cta(const void* x, int32_t dtype, int32_t T, int32_
                                 group_w, y, schedule, workspace, base, stream);
   void* xa = static_cast<unsigned char*>(workspace) + align256(base);
   hipStream_t s = as_stream(stream);
-  hipError_t e = launch_cta(x, dtype == LOOPQ_BF16, (int64_t)T * M, K, U, V, rank, a_sets, b_sets, eta_host,
-                            T - 1, M, -1, xa, s);
-  if (e != hipSuccess) return LOOPQ_ERR_HIP;
+  {
+    TimingScope ts(LOOPQ_KERNEL_CTA, s);
+    if (launch_cta(x, dtype == LOOPQ_BF16, (int64_t)T * M, K, U, V, rank, a_sets, b_sets, eta_host, T - 1, M, -1,
+                   xa, s) != hipSuccess)
+      return LOOPQ_ERR_HIP;
+  }
   return loopq_looped_forward(xa, dtype, T, M, K, N, P1, n1, P2, n2, clips_host, bits_a, w_codes, w_scales,
                               group_w, y, schedule, workspace, base, stream);
 }

@@ -32,7 +32,7 @@ LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD, LOOPQ_OP_LOOPED_FORWARD
 LOOPQ_OP_HESSIAN, LOOPQ_OP_QUANT_PER_TOKEN, LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 5, 6, 7
 LOOPQ_OP_RECURRENT_ADAPTER, LOOPQ_OP_LOOPED_FORWARD_CTA = 8, 9
 LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM, LOOPQ_KERNEL_DECODE = 0, 1, 2, 3
-LOOPQ_KERNEL_HESSIAN, LOOPQ_KERNEL_QUANT_TOKEN = 4, 5
+LOOPQ_KERNEL_HESSIAN, LOOPQ_KERNEL_QUANT_TOKEN, LOOPQ_KERNEL_CTA = 4, 5, 6
 
 # every entry point of include/loopq.h with its ctypes signature
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -367,7 +367,7 @@ def loopq_timing_reset() -> None:
     _check(load().loopq_timing_reset(), "loopq_timing_reset")
 
 
-def loopq_timing_read(n: int = 6):
+def loopq_timing_read(n: int = 7):
     """Per kernel id: (total milliseconds, launches) since the last read."""
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_int64 * n)()

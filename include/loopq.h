@@ -424,7 +424,8 @@ typedef enum {
   LOOPQ_KERNEL_GEMM = 2,            /* integer GEMM + rescale */
   LOOPQ_KERNEL_DECODE = 3,          /* few-row linear: transform, quantizer and product in one launch */
   LOOPQ_KERNEL_HESSIAN = 4,         /* trajectory Hessian accumulation (one record per call) */
-  LOOPQ_KERNEL_QUANT_TOKEN = 5      /* per-token quantizer */
+  LOOPQ_KERNEL_QUANT_TOKEN = 5,     /* per-token quantizer */
+  LOOPQ_KERNEL_CTA = 6              /* CTA loop-transition adapter */
 } loopq_kernel_id;
 
 /* Turn the hooks on (1) or off (0).  Host only; cheap. */
