@@ -555,6 +555,54 @@ def hessian_step(lq, mods):
         lq.loopq_hessian_accumulate(m.xt, m.H, m.ws_h)
 
 
+def hessian_side_bench(lq, torch, mods, T, M, steps):
+    """The looped forward with the trajectory Hessian as its side output
+    (loopq_looped_forward_hessian: the forward's quantizer writes x~, then the
+    SYRK) against the separate path: loopq_quant_act for the x~ dump, the
+    forward, then loopq_hessian_accumulate.  Weight-stationary, every
+    quantized input of the block, T*M rows each."""
+    WS = lq.LOOPQ_SCHED_WEIGHT_STATIONARY
+    bufs = []
+    for m in mods:
+        rows = T * m.x.shape[1]
+        b = {"ws": lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_HESSIAN, T, M, m.K, m.N, 4),
+             "ws_f": lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, m.K, m.N, 4),
+             "ws_h": lq.empty_workspace(lq.LOOPQ_OP_HESSIAN, 0, rows, m.K, 0, 0),
+             "H": torch.zeros((m.K, m.K), dtype=torch.float32, device="cuda"),
+             "y": torch.empty((T, M, m.N), dtype=torch.float32, device="cuda"),
+             "codes": torch.empty((rows, m.K), dtype=torch.int8, device="cuda"),
+             "steps": torch.empty((rows, m.K // 32), dtype=torch.float32, device="cuda"),
+             "xt": torch.empty((rows, m.K), dtype=torch.float32, device="cuda")}
+        bufs.append(b)
+
+    def side(n):
+        for _ in range(n):
+            for m, b in zip(mods, bufs):
+                lq.loopq_looped_forward_hessian(m.x, m.P1, m.P2, m.clips[:T], 4, m.codes, m.scales, 32, m.N, b["y"],
+                                                WS, b["H"], b["ws"])
+
+    def separate(n):
+        for _ in range(n):
+            for m, b in zip(mods, bufs):
+                lq.loopq_quant_act(m.x.reshape(T * M, m.K), m.P1, m.P2, 1.0, 4, b["codes"], b["steps"], b["xt"])
+                lq.loopq_looped_forward(m.x, m.P1, m.P2, m.clips[:T], 4, m.codes, m.scales, 32, m.N, b["y"], WS,
+                                        b["ws_f"])
+                lq.loopq_hessian_accumulate(b["xt"], b["H"], b["ws_h"])
+
+    side(1)
+    separate(1)
+    t_side, walls_s, kern_s = median_blocks(torch, lq, side, steps)
+    t_sep, walls_p, kern_p = median_blocks(torch, lq, separate, steps)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"what": "looped forward + trajectory Hessian per step (all 4 quantized inputs, weight-stationary): "
+                    "one loopq_looped_forward_hessian call per input vs quantizer dump + forward + accumulation",
+            "side_output_ms_per_step": t_side * 1e3, "separate_ms_per_step": t_sep * 1e3,
+            "saving_frac": (t_sep - t_side) / t_sep,
+            "blocks_ms": {"side_output": walls_s, "separate": walls_p},
+            "blocks_kernel_ms": {"side_output": kern_s, "separate": kern_p}}
+
+
 def hessian_bench(lq, torch, mods, T, M, steps, warmup):
     """Trajectory Hessian H += x~^T x~ over the x~ rows of all T loops, one
     accumulation per quantized input of the block (K = 2048 three times,
@@ -1099,6 +1147,7 @@ def secondary(lq, synth, torch, args, out, stack_wl):
             out["ouro_block"]["per_token"] = per_token_bench(lq, torch, mods, T2, M2, 5, 2)
         if not args.no_hessian:
             out["ouro_block"]["trajectory_hessian"] = hessian_bench(lq, torch, mods, T2, M2, 4, 2)
+            out["ouro_block"]["trajectory_hessian"]["side_output"] = hessian_side_bench(lq, torch, mods, T2, M2, 4)
         del mods
         torch.cuda.empty_cache()
     if not args.no_huginn_core:

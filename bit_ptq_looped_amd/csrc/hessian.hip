@@ -265,7 +265,12 @@ __device__ void run_segment(v16f acc[4], float* lds, const HPlan& p, int u, int 
 
 __global__ __launch_bounds__(kThreads) void hessian_tiles_kernel(HPlan p) {
   extern __shared__ float lds[];  // max(2 stages, 4 quadrants) floats
-  const int g = blockIdx.x;
+  // Logical work group g: the hardware dispatches consecutive work groups to
+  // the 8 XCDs in turn, so g = 64 * (XCD) + (slot) gives each XCD a run of
+  // 64 consecutive logical groups -- neighbouring tiles, which share column
+  // strips of the same rows, then read them through one L2.  The partition
+  // (and so the summation order) is that of g alone.
+  const int g = (int)(blockIdx.x & 7) * (kGroups / 8) + (int)(blockIdx.x >> 3);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   v16f acc[4];
   // whole tiles round robin (k < q), then this work group's contiguous range

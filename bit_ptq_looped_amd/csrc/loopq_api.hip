@@ -353,13 +353,14 @@ hipError_t run_decode(const void* x, int dtype, int rows, int K, int N, const fl
 int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const float* P1, int n1,
                     const float* P2, int n2, const ClipTable& clips, int rows_per_clip, int bits_a,
                     const void* w_codes, const void* w_scales, int gw, float* y, void* ws,
-                    int64_t ws_chunks, int64_t ws_rows, hipStream_t s) {
+                    int64_t ws_chunks, int64_t ws_rows, hipStream_t s, float* xt_out = nullptr) {
   ActBuffers b = carve(ws, ws_chunks, ws_rows, K, N, 0, rows);
-  if (rows <= kDecodeMaxRows)
+  if (rows <= kDecodeMaxRows && !xt_out)
     return hip_status(run_decode(x, dtype, rows, K, N, P1, n1, P2, n2, clips, rows_per_clip, bits_a,
                                  w_codes, w_scales, gw, y, b, s));
   QuantArgs a = internal_quant_args(x, dtype, rows, K, P1, n1, P2, n2, clips, rows_per_clip,
                                     bits_a, b);
+  a.xt_out = xt_out;
   const int fmt = code_format(bits_a);
   hipError_t e = prepare_weights(b, fmt, w_codes, K, N, s);
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
@@ -381,9 +382,9 @@ int32_t linear_core(const void* x, int dtype, int rows, int K, int N, const floa
 int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, const float* P1,
                          int n1, const float* P2, int n2, const ClipTable& clips, int bits_a,
                          const void* w_codes, const void* w_scales, int gw, float* y, void* ws,
-                         hipStream_t s) {
+                         hipStream_t s, float* xt_out = nullptr) {
   const size_t esz = dtype == LOOPQ_F32 ? 4 : 2;
-  if (M <= kDecodeMaxRows) {  // decode: one fused launch per loop, in loop order on `stream`
+  if (M <= kDecodeMaxRows && !xt_out) {  // decode: one fused launch per loop, in loop order on `stream`
     for (int t = 0; t < T; ++t) {
       ClipTable one;
       memset(&one, 0, sizeof(one));
@@ -411,6 +412,7 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
     ActBuffers b = carve(ws, T, M, K, N, t, 0);
     const void* xt = reinterpret_cast<const char*>(x) + (size_t)t * M * K * esz;
     QuantArgs a = internal_quant_args(xt, dtype, M, K, P1, n1, P2, n2, one, M, bits_a, b);
+    if (xt_out) a.xt_out = xt_out + (size_t)t * M * K;
     hipError_t e;
     {
       TimingScope ts(P1 ? LOOPQ_KERNEL_QUANT_TRANSFORM : LOOPQ_KERNEL_QUANT_PLAIN, p->aux);
@@ -654,6 +656,14 @@ int32_t loopq_workspace_bytes(int32_t op, int32_t T, int32_t M, int32_t K, int32
       if (M < 0 || N <= 0) return LOOPQ_ERR_INVALID_ARG;
       if (N % 16) return LOOPQ_ERR_UNSUPPORTED;
       *bytes = align256((size_t)M * 2 * N * 4) + act_bytes(1, M, 2 * (int64_t)N, N, code_format(bits_a));
+      return LOOPQ_OK;
+    case LOOPQ_OP_LOOPED_FORWARD_HESSIAN:  // the looped forward's region, x~ of all rows, the Hessian's
+      if (T <= 0 || M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
+      if (T > LOOPQ_MAX_LOOPS || K % 32 || K > kHessianMaxK || (int64_t)T * M > kHessianMaxRows)
+        return LOOPQ_ERR_UNSUPPORTED;
+      if (N <= 0) return LOOPQ_ERR_INVALID_ARG;
+      *bytes = align256(act_bytes(T, M, K, N, code_format(bits_a))) + align256((size_t)T * M * K * 4) +
+               align256(hessian_workspace_bytes(K));
       return LOOPQ_OK;
     case LOOPQ_OP_LOOPED_FORWARD_CTA:  // the looped forward's region, then the adapted loop inputs
       if (T <= 0 || M < 0 || K <= 0) return LOOPQ_ERR_INVALID_ARG;
@@ -1102,6 +1112,40 @@ int32_t loopq_looped_forward_per_token(const void* x, int32_t dtype, int32_t T, 
   if (e != hipSuccess) return LOOPQ_ERR_HIP;
   TimingScope ts(LOOPQ_KERNEL_GEMM, s);
   return hip_status(run_gemm(b, fmt, rows, K, N, w_codes, w_scales, group_w, y, nullptr, 0, s));
+}
+
+int32_t loopq_looped_forward_hessian(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
+                                     int32_t N, const float* P1, int32_t n1, const float* P2, int32_t n2,
+                                     const float* clips_host, int32_t bits_a, const void* w_codes,
+                                     const void* w_scales, int32_t group_w, float* y, int32_t schedule,
+                                     float* H, void* workspace, size_t workspace_bytes, void* stream) {
+  ClipTable clips;
+  bool empty = false;
+  int32_t st = check_forward(x, dtype, T, M, K, N, P1, n1, P2, n2, clips_host, bits_a, w_codes, w_scales,
+                             group_w, y, schedule, &clips, &empty);
+  if (st != LOOPQ_OK) return st;
+  if (K > kHessianMaxK || (int64_t)T * M > kHessianMaxRows) return LOOPQ_ERR_UNSUPPORTED;
+  if (empty) return LOOPQ_OK;
+  if (!H) return LOOPQ_ERR_INVALID_ARG;
+  if (!aligned(H, 4)) return LOOPQ_ERR_ALIGNMENT;
+  size_t need = 0, base = 0;
+  loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_HESSIAN, T, M, K, N, bits_a, &need);
+  loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, bits_a, &base);
+  if (!workspace || workspace_bytes < need) return LOOPQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOOPQ_ERR_ALIGNMENT;
+  unsigned char* w8 = static_cast<unsigned char*>(workspace);
+  float* xt = reinterpret_cast<float*>(w8 + align256(base));
+  float* part = reinterpret_cast<float*>(w8 + align256(base) + align256((size_t)T * M * K * 4));
+  hipStream_t s = as_stream(stream);
+  if (schedule == LOOPQ_SCHED_LOOP_SEQUENTIAL && T > 1)
+    st = looped_pipelined(x, dtype, T, M, K, N, P1, n1, P2, n2, clips, bits_a, w_codes, w_scales, group_w, y,
+                          workspace, s, xt);
+  else
+    st = linear_core(x, dtype, T * M, K, N, P1, n1, P2, n2, clips, M, bits_a, w_codes, w_scales, group_w, y,
+                     workspace, T, M, s, xt);
+  if (st != LOOPQ_OK) return st;
+  TimingScope ts(LOOPQ_KERNEL_HESSIAN, s);
+  return hip_status(launch_hessian(xt, T * M, K, H, part, s));
 }
 
 int32_t loopq_cta_apply(const void* h, int32_t dtype, int32_t M, int32_t K, const float* U,

@@ -30,7 +30,7 @@ LOOPQ_F32, LOOPQ_BF16 = 0, 1
 LOOPQ_SCHED_AUTO, LOOPQ_SCHED_LOOP_SEQUENTIAL, LOOPQ_SCHED_WEIGHT_STATIONARY = 0, 1, 2
 LOOPQ_OP_LINEAR, LOOPQ_OP_LOOPED_FORWARD, LOOPQ_OP_FOLD, LOOPQ_OP_LOOPED_FORWARD_EX = 1, 2, 3, 4
 LOOPQ_OP_HESSIAN, LOOPQ_OP_QUANT_PER_TOKEN, LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 5, 6, 7
-LOOPQ_OP_RECURRENT_ADAPTER, LOOPQ_OP_LOOPED_FORWARD_CTA = 8, 9
+LOOPQ_OP_RECURRENT_ADAPTER, LOOPQ_OP_LOOPED_FORWARD_CTA, LOOPQ_OP_LOOPED_FORWARD_HESSIAN = 8, 9, 10
 LOOPQ_KERNEL_QUANT_TRANSFORM, LOOPQ_KERNEL_QUANT_PLAIN, LOOPQ_KERNEL_GEMM, LOOPQ_KERNEL_DECODE = 0, 1, 2, 3
 LOOPQ_KERNEL_HESSIAN, LOOPQ_KERNEL_QUANT_TOKEN, LOOPQ_KERNEL_CTA = 4, 5, 6
 
@@ -62,6 +62,8 @@ SIGNATURES = {
     "loopq_quant_act_per_token": ([_P, _I, _I, _I, _P, _I, _P, _I, _F, _I, _P, _P, _P, _P, _Z, _P], _I),
     "loopq_looped_forward_per_token": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _P, _Z,
                                         _P], _I),
+    "loopq_looped_forward_hessian": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _I,
+                                      _P, _P, _Z, _P], _I),
     "loopq_cta_apply": ([_P, _I, _I, _I, _P, _P, _I, _P, _P, _F, _P, _P], _I),
     "loopq_looped_forward_cta": ([_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _I,
                                   _P, _P, _I, _P, _P, _P, _P, _Z, _P], _I),
@@ -219,6 +221,19 @@ def loopq_looped_forward(x, P1, P2, clips: Sequence[float], bits_a: int, w_codes
                                        _ptr(w_scales), group_w, _ptr(y), schedule, _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
            "loopq_looped_forward")
+
+
+def loopq_looped_forward_hessian(x, P1, P2, clips: Sequence[float], bits_a: int, w_codes, w_scales,
+                                 group_w: int, N: int, y, schedule: int, H, workspace, stream=None):
+    """loopq_looped_forward that also accumulates H += x~^T x~ over all loops."""
+    T, M, K = x.shape
+    p1, n1, p2, n2 = _factor_args(P1, P2)
+    c = (ctypes.c_float * T)(*[float(v) for v in clips])
+    _check(load().loopq_looped_forward_hessian(_ptr(x), _dtype_code(x), T, M, K, N, p1, n1, p2, n2,
+                                               ctypes.cast(c, ctypes.c_void_p), bits_a, _ptr(w_codes),
+                                               _ptr(w_scales), group_w, _ptr(y), schedule, _ptr(H), _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "loopq_looped_forward_hessian")
 
 
 def loopq_cta_apply(h, U, V, a, b, eta: float, out, stream=None):

@@ -94,7 +94,8 @@ typedef enum {
   LOOPQ_OP_QUANT_PER_TOKEN = 6,   /* M, K; T, N and bits_a ignored */
   LOOPQ_OP_LOOPED_FORWARD_PER_TOKEN = 7, /* T, M, K, N, bits_a */
   LOOPQ_OP_RECURRENT_ADAPTER = 8, /* M, N, bits_a (K = 2N implied); T and K ignored */
-  LOOPQ_OP_LOOPED_FORWARD_CTA = 9  /* T, M, K, N, bits_a; dtype bytes taken as 4 */
+  LOOPQ_OP_LOOPED_FORWARD_CTA = 9, /* T, M, K, N, bits_a; dtype bytes taken as 4 */
+  LOOPQ_OP_LOOPED_FORWARD_HESSIAN = 10 /* T, M, K, N, bits_a */
 } loopq_op;
 
 /* ABI version of the loaded library (LOOPQ_ABI_VERSION it was built with). */
@@ -281,6 +282,27 @@ int32_t loopq_looped_forward_ex(const void* x, int32_t dtype, int32_t T, int32_t
                                 const int32_t* sets_host, const int32_t* bits_host,
                                 const float* clips_host, float* y, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* a6 with the trajectory Hessian as a side output: the looped forward of
+ * loopq_looped_forward (same arguments, schedules and results: y is bitwise
+ * that call's whenever that call takes the quantizer and the GEMM, i.e. for
+ * more than 16 rows per launch; here the few-row kernel is never used) whose
+ * quantizer also writes the x~ it quantizes, fp32 [T][M][K], into the
+ * workspace, followed by H += x~^T x~ over all T*M rows as
+ * loopq_hessian_accumulate computes it (bitwise the same H), so no second
+ * transform pass is made.  Page as for loopq_hessian_accumulate: the N-step
+ * calibration Hessian summed over the recurrence steps.  After the call the
+ * x~ rows stay in the workspace at byte offset
+ * loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, bits_a) rounded
+ * up to a multiple of 256.  H fp32 [K][K] (4-byte aligned), accumulated in
+ * place; K <= 65536 and T*M <= 2^30 as for loopq_hessian_accumulate.
+ * Workspace: loopq_workspace_bytes(LOOPQ_OP_LOOPED_FORWARD_HESSIAN, T, M, K, N,
+ * bits_a, ...).  Other errors as loopq_looped_forward. */
+int32_t loopq_looped_forward_hessian(const void* x, int32_t dtype, int32_t T, int32_t M, int32_t K,
+                                     int32_t N, const float* P1, int32_t n1, const float* P2, int32_t n2,
+                                     const float* clips_host, int32_t bits_a, const void* w_codes,
+                                     const void* w_scales, int32_t group_w, float* y, int32_t schedule,
+                                     float* H, void* workspace, size_t workspace_bytes, void* stream);
 
 /* CTA, one loop transition on M rows: out = a * h + b + eta * U (V^T h) per
  * row.  Page: "paper_specification.yaml", loopq_components.cta (Section 4.3,

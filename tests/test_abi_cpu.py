@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 26
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
         assert n in loopq.SIGNATURES, n
@@ -342,3 +342,32 @@ def test_cta_entries_reject_on_host(lib):
     assert gv(i23=FAKE + 16) == loopq.LOOPQ_ERR_ALIGNMENT
     assert gv(i4=2040) == loopq.LOOPQ_ERR_UNSUPPORTED              # K % 32
     assert gv(i3=0, i0=None, i23=None, i24=0) == loopq.LOOPQ_OK     # no rows
+
+
+def test_forward_hessian_rejects_on_host(lib):
+    f = lambda *a: _raw(lib, "loopq_looped_forward_hessian", *a)
+    op = loopq.LOOPQ_OP_LOOPED_FORWARD_HESSIAN
+    ws = loopq.loopq_workspace_bytes(op, 4, 64, 2048, 512, 4)
+    base = loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_LOOPED_FORWARD, 4, 64, 2048, 512, 4)
+    hw = loopq.loopq_workspace_bytes(loopq.LOOPQ_OP_HESSIAN, 0, 256, 2048, 0, 0)
+    assert ws >= base + 4 * 64 * 2048 * 4 + hw
+    clips = (ctypes.c_float * 4)(1.0, 1.0, 1.0, 1.0)
+    c = ctypes.cast(clips, ctypes.c_void_p)
+    # x, dtype, T, M, K, N, P1, n1, P2, n2, clips, bits, w_codes, w_scales, group_w, y, schedule, H, ws, bytes, stream
+    args = [FAKE, 1, 4, 64, 2048, 512, None, 0, None, 0, c, 4, FAKE, FAKE, 32, FAKE, 0, FAKE, FAKE, ws, None]
+
+    def v(i, x):
+        a = list(args)
+        a[i] = x
+        return f(*a)
+    assert v(17, None) == loopq.LOOPQ_ERR_INVALID_ARG        # H
+    assert v(17, FAKE + 2) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert v(19, ws - 1) == loopq.LOOPQ_ERR_WORKSPACE
+    assert v(18, FAKE + 16) == loopq.LOOPQ_ERR_ALIGNMENT
+    assert v(4, 2040) == loopq.LOOPQ_ERR_UNSUPPORTED          # K % 32
+    assert v(16, 7) == loopq.LOOPQ_ERR_INVALID_ARG            # schedule
+    with pytest.raises(loopq.LoopQError):
+        loopq.loopq_workspace_bytes(op, 4, 64, 65568, 512, 4)  # K above the Hessian's limit
+    a = list(args)
+    a[3], a[0], a[17], a[18], a[19] = 0, None, None, None, 0
+    assert f(*a) == loopq.LOOPQ_OK                             # no rows

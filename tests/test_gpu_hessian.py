@@ -149,3 +149,59 @@ def test_hessian_rank_grows_along_a_drifting_trajectory(lq):
         want_rank = oracle.thresholded_rank(oracle.trajectory_hessian(xs))
         assert want_rank == d
         assert oracle.thresholded_rank(got) == d
+
+
+@pytest.mark.parametrize("schedule,M", [(2, 96), (1, 96), (2, 3), (1, 3)])
+def test_looped_forward_hessian_side_output(lq, schedule, M):
+    """loopq_looped_forward_hessian: the forward's own quantizer writes the x~
+    it quantizes (bitwise loopq_quant_act's dump of the same rows) and H0 +
+    x~^T x~ over all loops is bitwise one loopq_hessian_accumulate call on
+    those rows; y is bitwise the plain looped forward's where that call also
+    takes the quantizer and the GEMM, and matches the oracle on x~ (1e-4)."""
+    wl = synth.ouro_block_workload(M=M)
+    K, N = 2048, 256
+    P1, P2 = synth.factors_for(wl, "qkv_in", K)
+    bits, x32 = synth.activations_for(wl, "qkv_in", K)
+    T = x32.shape[0]
+    clips = [1.0, 0.9, 0.95, 0.85][:T]
+    say(f"forward + hessian schedule={schedule} T={T} M={M}")
+    W = synth.gaussian((N, K), 950, M, scale=0.02)
+    wt = oracle.fold_weights(W, P1, P2).astype(np.float32)
+    qw, sw = oracle.quant_weights(wt, 32)
+    codes, scales = lq.empty_packed_weights(K, N, 32)
+    lq.loopq_pack_weights(dev(wt), 32, codes, scales)
+    x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    p1, p2 = dev(P1), dev(P2)
+    H0 = random_symmetric(K, 951)
+    H = dev(H0.astype(np.float32))
+    y = torch.empty((T, M, N), dtype=torch.float32, device="cuda")
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD_HESSIAN, T, M, K, N, 4)
+    lq.loopq_looped_forward_hessian(x, p1, p2, clips, 4, codes, scales, 32, N, y, schedule, H, ws)
+    torch.cuda.synchronize()
+    base = lq.loopq_workspace_bytes(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, 4)
+    off = (base + 255) // 256 * 256
+    xt_ws = ws[off:off + T * M * K * 4].view(torch.float32).view(T * M, K).clone()
+    # the same rows through loopq_quant_act (one call per loop: its own clip)
+    dump = torch.empty((T * M, K), dtype=torch.float32, device="cuda")
+    for t in range(T):
+        codes_t = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        steps_t = torch.empty((M, K // 32), dtype=torch.float32, device="cuda")
+        lq.loopq_quant_act(x[t], p1, p2, clips[t], 4, codes_t, steps_t, dump[t * M:(t + 1) * M])
+    H2 = dev(H0.astype(np.float32))
+    lq.loopq_hessian_accumulate(dump, H2, workspace(lq, T * M, K))
+    y2 = torch.empty_like(y)
+    lq.loopq_looped_forward(x, p1, p2, clips, 4, codes, scales, 32, N, y2, schedule,
+                            lq.empty_workspace(lq.LOOPQ_OP_LOOPED_FORWARD, T, M, K, N, 4))
+    torch.cuda.synchronize()
+    assert torch.equal(xt_ws, dump)
+    assert torch.equal(H, H2)
+    d = dump.cpu().numpy()
+    check_xt(d, x32.reshape(T * M, K), P1, P2)
+    ratio = check_bound(H.cpu().numpy(), [d], H0)
+    say(f"  H max error / bound {ratio:.3g}")
+    rows_per_launch = T * M if schedule == 2 else M
+    if rows_per_launch > 16:
+        assert torch.equal(y, y2)
+    ref = oracle.looped_forward(d.reshape(T, M, K), None, None, clips, 4, qw, sw, 32)
+    got = y.cpu().numpy().astype(np.float64)
+    assert float(np.max(np.abs(got - ref)) / np.max(np.abs(ref))) <= 1e-4
