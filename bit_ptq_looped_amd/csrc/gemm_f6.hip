@@ -60,15 +60,24 @@ __device__ __forceinline__ int coef_row(int i) {
   return (i & 3) < 3 ? i + 1 : ((((i >> 3) + 1) & 3) << 3) | (i & 4);
 }
 
-template <int MODE>
+// SPLIT (rescale mode only): the split-K form of map_tile_split; the two
+// halves of each quadrant's sum are added through LDS, the first half's wave
+// adding the second's (a fixed order), and only the first half's wave
+// stores.  Every wave of that form reaches the barrier, so none returns early.
+template <int MODE, int SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
+  __shared__ float red[SPLIT ? 2 * 64 * 64 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int c = lane & 31;
-  int m_base, n_base;
-  map_tile(g, wave, &m_base, &n_base);
-  if (m_base >= g.M || n_base >= g.N) return;
+  int m_base, n_base, kh = 0;
+  if (SPLIT)
+    map_tile_split(g, wave, &m_base, &n_base, &kh);
+  else
+    map_tile(g, wave, &m_base, &n_base);
+  const bool active = m_base < g.M && n_base < g.N;
+  if (!SPLIT && !active) return;
   const int Ga = g.K >> 5;
   const int Gp = (Ga + 1) >> 1;
   const int Gw = (Ga + (1 << g.gshift) - 1) >> g.gshift;
@@ -79,7 +88,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
   // pair offset as scalar offset (tiles past the edge re-read the last block)
   const void* wp;
   const __half* swp;
-  tile_weights(g, m_base, &wp, &swp);  // the grouped form's weight set of these rows
+  tile_weights(g, active ? m_base : 0, &wp, &swp);  // the grouped form's weight set of these rows
   __amdgpu_buffer_rsrc_t x_rs[2], w_rs[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -192,24 +201,49 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
     if (2 * p + 1 < Ga) group(s, x, 1, 2 * p + 1);  // wave-uniform
   };
 
+  // this wave's group pairs [p0, p1)
+  const int half = (Gp + 1) >> 1;
+  const int p0 = SPLIT && kh ? half : 0;
+  const int p1 = SPLIT && !kh ? half : Gp;
   // Loads past the last pair re-read it (in bounds, unused), so the loop
   // body is one basic block the barriers can order.
-  F6Stage s0, s1;
-  load(0, s0);
-  load(min(1, Gp - 1), s1);
-  int p = 0;
-  for (; p + 1 < Gp; p += 2) {
-    compute(s0, p);
-    __builtin_amdgcn_sched_barrier(0);
-    load(min(p + 2, Gp - 1), s0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s1, p + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load(min(p + 3, Gp - 1), s1);
-    __builtin_amdgcn_sched_barrier(0);
+  if (active && p0 < p1) {
+    F6Stage s0, s1;
+    load(p0, s0);
+    load(min(p0 + 1, p1 - 1), s1);
+    int p = p0;
+    for (; p + 1 < p1; p += 2) {
+      compute(s0, p);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(p + 2, p1 - 1), s0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s1, p + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(p + 3, p1 - 1), s1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (p < p1) compute(s0, p);
   }
-  if (p < Gp) compute(s0, p);
 
+  if (SPLIT) {
+    float* r = red + (wave & 1) * 64 * 64;
+    if (kh == 1 && active) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) r[((t * 2 + u) * 16 + e) * 64 + lane] = acc[t][u][e];
+    }
+    __syncthreads();
+    if (kh == 1 || !active) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][u][e] += r[((t * 2 + u) * 16 + e) * 64 + lane];
+  }
   if (MODE == 0) store_y(g, acc, m_base, n_base, h, c);
 }
 
@@ -266,6 +300,19 @@ hipError_t launch_expand_weights_f6(const uint8_t* w_codes, int K, int N, void* 
   return hipGetLastError();
 }
 
+// Whether the split-K form spreads the work better: every wave of a 128x128
+// tile runs over all of K, every wave of the split form over half of it, and
+// the waves of a launch land about evenly on the chip's SIMDs (four per CU),
+// so a launch takes about ceil(waves / SIMDs) wave times.  The split form is
+// taken when that estimate is at least 5% lower (it also pays an exchange
+// through LDS).
+bool split_k_pays(int64_t tiles, int64_t tiles_split) {
+  const int64_t simds = 4 * (int64_t)device_cu_count();
+  const double whole = (double)((4 * tiles + simds - 1) / simds);
+  const double split = 0.5 * (double)((4 * tiles_split + simds - 1) / simds);
+  return split < 0.95 * whole;
+}
+
 hipError_t launch_gemm_f6(const void* a_tiled, const float* a_scales_gm, int ld_sa, int M, int K,
                           int N, const void* w_f6, const __half* w_scales, int gw, float* y,
                           int32_t* dots, int mode, hipStream_t s, const GemmSets* sets) {
@@ -292,11 +339,18 @@ hipError_t launch_gemm_f6(const void* a_tiled, const float* a_scales_gm, int ld_
   g.gshift = gw == 128 ? 2 : 0;
   g.y = y;
   g.dots = dots;
-  dim3 grid(((N + 127) / 128) * ((M + 127) / 128));
-  if (mode == 0)
-    hipLaunchKernelGGL(gemm_f6_kernel<0>, grid, dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL(gemm_f6_kernel<1>, grid, dim3(256), 0, s, g);
+  const int64_t tiles = (int64_t)((N + 127) / 128) * ((M + 127) / 128);
+  const int64_t tiles_split = (int64_t)((N + 127) / 128) * ((M + 63) / 64);
+  if (mode == 0 && split_k_pays(tiles, tiles_split)) {
+    dim3 grid((unsigned)tiles_split);
+    hipLaunchKernelGGL((gemm_f6_kernel<0, 1>), grid, dim3(256), 0, s, g);
+  } else {
+    dim3 grid((unsigned)tiles);
+    if (mode == 0)
+      hipLaunchKernelGGL((gemm_f6_kernel<0, 0>), grid, dim3(256), 0, s, g);
+    else
+      hipLaunchKernelGGL((gemm_f6_kernel<1, 0>), grid, dim3(256), 0, s, g);
+  }
   return hipGetLastError();
 }
 

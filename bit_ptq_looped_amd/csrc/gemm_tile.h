@@ -71,6 +71,24 @@ __device__ __forceinline__ void map_tile(const GemmArgs& g, int wave, int* m_bas
   *n_base = (r / gm) * 128 + (wave & 1) * 64;
 }
 
+// Split-K form for launches with fewer 128x128 tiles than CUs: 64x128
+// tiles, the same XCD-aware walk over 64-row panels; waves 0 and 1 take the
+// first half of the group pairs of their 64x64 quadrant, waves 2 and 3 (kh =
+// 1) the second half of the same quadrants.
+__device__ __forceinline__ void map_tile_split(const GemmArgs& g, int wave, int* m_base, int* n_base, int* kh) {
+  const int Mp = (g.M + 63) >> 6;
+  const int Np = (g.N + 127) >> 7;
+  const int total = Mp * Np;
+  const int xcd = blockIdx.x & 7;
+  const int q = xcd * (total >> 3) + min(xcd, total & 7) + (int)(blockIdx.x >> 3);
+  const int grp = q / (8 * Np);
+  const int gm = min(Mp - grp * 8, 8);
+  const int r = q - grp * 8 * Np;
+  *m_base = (grp * 8 + r % gm) * 64;
+  *n_base = (r / gm) * 128 + (wave & 1) * 64;
+  *kh = wave >> 1;
+}
+
 // Result element e of lane l of tile (t, u) is row m = m_base + 32 t + l % 32
 // and column n = n_base + 32 u + 8 (e / 4) + 4 (l / 32) + e % 4.
 __device__ __forceinline__ void store_y(const GemmArgs& g, const float (&acc)[2][2][16], int m_base,
