@@ -825,7 +825,7 @@ bool plan_quant(QuantArgs& a) {
     const int px = (p2 + p2_bytes(sp2) + 15) / 16 * 16;
     return px + xb_for(sx, r) + kRowMaxBytes;
   };
-  int sp1 = p_stride(a.n1);
+  int sp1 = p1_stride(a.n1);
   int sp2 = p_stride(a.n2);
   int sx = x_stride(a.n2);
   if (fixed) {

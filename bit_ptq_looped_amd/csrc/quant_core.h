@@ -91,17 +91,21 @@ __device__ __forceinline__ uint32_t quantize4(float4 v, float clip, float qmaxf,
   return codes4(v, s, qmaxf);
 }
 
-// LDS strides (elements) of P1, P2 and the X rows: P rows padded to 16 mod
-// 32 and X rows to 2 mod 32 so the 16 lanes of an MFMA operand read fall on
-// distinct banks.  For compile-time factor shapes the kernel uses these
-// constants (every LDS offset then folds into the instruction); the host plan
-// uses the same values for those shapes.
+// LDS strides (elements) of P1, P2 and the X rows, so the lanes of an MFMA
+// operand read fall on distinct banks: stage 1 reads P2 rows b, b + 1, b + 2,
+// b + 3 (one per 16-lane group), so P2 rows are padded to 16 mod 32; stage 2
+// reads P1 rows a, a + 4, a + 8, a + 12 (the rows the stage-1 result holds
+// per lane group), so P1 rows are padded to 4 mod 16 (4 rows = 16 banks
+// apart); X rows to 2 mod 32.  For compile-time factor shapes the kernel uses
+// these constants (every LDS offset then folds into the instruction); the
+// host plan uses the same values for those shapes.
 constexpr int stride_to(int n, int rem) { return n + ((rem - n) % 32 + 32) % 32; }
 constexpr int p_stride(int n) { return n <= 16 ? 16 : stride_to(n, 16); }
+constexpr int p1_stride(int n) { return n + ((4 - n) % 16 + 16) % 16; }
 constexpr int x_stride(int n2) { return stride_to(n2, 2); }
 template <int N1, int N2>
 struct XStrides {
-  static constexpr int sp1 = N1 > 0 ? p_stride(N1) : 0;
+  static constexpr int sp1 = N1 > 0 ? p1_stride(N1) : 0;
   static constexpr int sp2 = N2 > 0 ? p_stride(N2) : 0;
   static constexpr int sx = N2 > 0 ? x_stride(N2) : 0;
 };
