@@ -77,6 +77,10 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=20)
     p.add_argument("--profile-decode", type=int, default=0,
                    help="only run this many decode loop-steps at M=1 (for rocprofv3), no JSON")
+    p.add_argument("--profile-reuse", type=int, default=0,
+                   help="only run this many rounds of the decode weight-reuse call (layer 0, all T = 4 loops "
+                        "of M = 1 in one weight-stationary call per input, the L2 flushed by a 128 MiB copy "
+                        "before each), for rocprofv3 FETCH_SIZE; no JSON")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="with a --profile-* run: first run one device-to-device copy of this many MiB "
                         "(a plain copy kernel of known size that calibrates HBM byte counters)")
@@ -1057,6 +1061,20 @@ def main():
             decode_loop_step(lq, dmods, i % 4)
         torch.cuda.synchronize()
         print(f"profiled {args.profile_decode} decode loop-steps", flush=True)
+        return
+    if args.profile_reuse:
+        _, dmods = build_decode(lq, synth, torch, 1, 4)
+        calibration_copy(args, torch)
+        src = torch.ones(32 << 20, dtype=torch.float32, device="cuda")  # 128 MiB: more than the L2s hold
+        dst = torch.empty_like(src)
+        for _ in range(args.profile_reuse):
+            for m in dmods:
+                dst.copy_(src)
+                codes, scales = m.weights[0]
+                lq.loopq_looped_forward(m.x, m.P1, m.P2, m.clips, 4, codes, scales, 32, m.N, m.yT,
+                                        lq.LOOPQ_SCHED_WEIGHT_STATIONARY, m.wsT)
+        torch.cuda.synchronize()
+        print(f"profiled {args.profile_reuse} rounds of the decode reuse call", flush=True)
         return
     if args.profile_stack:
         _, smods = build_stack(lq, synth, torch, args.M, args.layers)

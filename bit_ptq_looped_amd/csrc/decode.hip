@@ -931,7 +931,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
   constexpr int kSlice = C::kSlice;
   constexpr int NH = C::NH;
   const int tid = threadIdx.x;
-  const int cb = blockIdx.x;       // columns cb * CPW .. + CPW - 1
+  // columns cb * CPW .. + CPW - 1.  Consecutive work-groups land on the 8
+  // XCDs in turn; each XCD takes a contiguous range of column blocks instead,
+  // so the 128-byte lines of packed weights (16 columns) and of their steps,
+  // which neighbouring blocks of 8 columns share, are fetched through one L2.
+  const int G = (int)gridDim.x;
+  const int xcd = (int)(blockIdx.x & 7);
+  const int cb = xcd * (G >> 3) + min(xcd, G & 7) + (int)(blockIdx.x >> 3);
   const int c = tid & (CPW - 1);   // column of the work-group
   const int gq = tid / CPW;        // lane group: groups gq + GL i of each slice
   const int K = g.K;
