@@ -1129,7 +1129,7 @@ bool decode_transform_fused(int R, int n1, int n2) {
   if (R <= 0 || R > kDecodeMaxRows) return false;
   if ((int64_t)R * n1 * n2 * (n1 + n2) > 1250000) return false;
   const int RM = R <= 4 ? 4 : kDecodeMaxRows;
-#define LOOPQ_DECODE_FITS(n1_, n2_, rs_, nim_) \
+#define LOOPQ_DECODE_FITS(n1_, n2_, rs_, nim_, ws_) \
   if (n1 == n1_ && n2 == n2_) return XPlan<n1_, n2_>::lds(R, RM) <= kLdsBudget;
   LOOPQ_SHAPES(LOOPQ_DECODE_FITS)
 #undef LOOPQ_DECODE_FITS
@@ -1137,7 +1137,7 @@ bool decode_transform_fused(int R, int n1, int n2) {
 }
 
 bool decode_transform_items(int n1, int n2) {
-#define LOOPQ_ITEM_SHAPE(n1_, n2_, rs_, nim_) \
+#define LOOPQ_ITEM_SHAPE(n1_, n2_, rs_, nim_, ws_) \
   if (n1 == n1_ && n2 == n2_) return true;
   LOOPQ_SHAPES(LOOPQ_ITEM_SHAPE)
 #undef LOOPQ_ITEM_SHAPE
@@ -1182,7 +1182,7 @@ hipError_t launch_decode(const DecodeCall& c, hipStream_t s) {
   const int RM = small ? 4 : kDecodeMaxRows;
   const int cpw = pick_cpw(padded_cols(c.N), c.R, device_cu_count());
   if (xform) {
-#define LOOPQ_DECODE_KERNEL(n1_, n2_, rs_, nim_)                                                   \
+#define LOOPQ_DECODE_KERNEL(n1_, n2_, rs_, nim_, ws_)                                                   \
     if (c.n1 == n1_ && c.n2 == n2_) {                                                              \
       constexpr int nrt = (n1_ + 15) / 16;                                                         \
       fn = small ? decode_fn<nrt, n1_, n2_, 4, 0>(cpw) : decode_fn<nrt, n1_, n2_, kDecodeMaxRows, 0>(cpw); \
@@ -1218,7 +1218,7 @@ hipError_t launch_decode_items(const void* x, int bf16, const float* P1, int n1,
   ga.P2 = P2;
   const void* fi = nullptr;
   int ilds = 0, items = 0;
-#define LOOPQ_ITEM_KERNEL(n1_, n2_, rs_, nim_)                                                \
+#define LOOPQ_ITEM_KERNEL(n1_, n2_, rs_, nim_, ws_)                                                \
   if (n1 == n1_ && n2 == n2_) {                                                               \
     fi = reinterpret_cast<const void*>(xform_items_kernel<(n1_ + 15) / 16, n1_, n2_>);       \
     ilds = ItemPlan<n1_, n2_>::lds;                                                           \

@@ -125,6 +125,7 @@ struct QuantArgs {
   int off_p2, off_x, off_t;  // byte offsets in dynamic LDS
   int off_rmax;      // byte offset of the per-row, per-wave absmax partials (per_token)
   int lds_bytes;
+  int ws;            // 1: the two-role kernel form (512 threads)
 };
 
 // host launchers -------------------------------------------------------------

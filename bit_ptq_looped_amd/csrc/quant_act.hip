@@ -235,8 +235,9 @@ __global__ __launch_bounds__(256) void quant_token_kernel(QuantArgs a) {
 
 // Work item of slot ii of a wave.  SR (shared row): a wave's NIM slots are
 // consecutive items, all in one row of the chunk (the row's column-tile count
-// is a multiple of NIM), so the stage-1 X operand is read once for all of
-// them; otherwise the items are dealt to the 4 waves in turn.
+// is a multiple of NIM, or the chunk is one row), so the stage-1 X operand is
+// read once for all of them; otherwise the items are dealt to the 4 waves in
+// turn.
 template <bool SR, int NIM>
 __device__ __forceinline__ int item_of(int wave, int ii) {
   return SR ? wave * NIM + ii : wave + 4 * ii;
@@ -334,7 +335,7 @@ __device__ __forceinline__ void stage1_bf(const uint16_t* sXb, const uint16_t* s
 #pragma unroll
     for (int q = 0; q < NRT; ++q) acc[ii][q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  stage1_bf16<N1, N2, NI, NRT>(xg, rt0, pc, L::plane, li, lk, acc);
+  stage1_bf16<N1, N2, NI, NRT, SR>(xg, rt0, pc, L::plane, li, lk, acc);
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
@@ -466,16 +467,54 @@ __device__ __forceinline__ void quant_chunk(const QuantArgs& a, const float* sX,
 // into the even fields; fed the even and the odd elements it yields the
 // group's 24 bytes in field order, stored as they are.  A zero code may come
 // out as either e2m3 zero pattern.
+//
+// MAXT > 0 (at most MAXT groups per lane): the codes and steps are kept in
+// `out` and stored later by f6_store_deferred; the x~ side output, if any,
+// is still written here.
+struct F6Group {
+  v6i bits;
+  float s;
+  int row, j, ok;
+};
+
+__device__ __forceinline__ void f6_store(const QuantArgs& a, int Gp, int Ga, int row, int j, const v6i& bits,
+                                         float s) {
+  uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<char*>(a.codes) +
+                                        ((int64_t)(row >> 5) * Gp + (j >> 1)) * kF6BlockBytes +
+                                        ((row & 31) + 32 * (j & 1)) * 24);
+  dst[0] = uint2{(uint32_t)bits[0], (uint32_t)bits[1]};
+  dst[1] = uint2{(uint32_t)bits[2], (uint32_t)bits[3]};
+  dst[2] = uint2{(uint32_t)bits[4], (uint32_t)bits[5]};
+  if (a.scales_gm)
+    a.scales[(int64_t)j * a.scales_ld + row] = s;
+  else
+    a.scales[(int64_t)row * Ga + j] = s;
+}
+
+template <int MAXT>
+__device__ __forceinline__ void f6_store_deferred(const QuantArgs& a, int K, const F6Group (&out)[MAXT]) {
+  const int Ga = K >> 5;
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t)
+    if (out[t].ok) f6_store(a, (Ga + 1) >> 1, Ga, out[t].row, out[t].j, out[t].bits, out[t].s);
+}
+
+template <int MAXT>
 __device__ __forceinline__ void quant_groups_f6(const QuantArgs& a, const float* sX, const float* sR,
                                                 int row0, int rows, int K, int wave, int lane, float cl,
-                                                float qmaxf, float rqmax) {
+                                                float qmaxf, float rqmax, F6Group (&out)[MAXT > 0 ? MAXT : 1]) {
   const int Ga = K >> 5;
   const int Gp = (Ga + 1) >> 1;
   const int ng = rows * Ga;
   const int per = (ng + 3) >> 2;
   const int g0 = wave * per;
   const int g1 = min(ng, g0 + per);
-  for (int gb = g0; gb < g1; gb += 64) {  // wave-uniform
+  if constexpr (MAXT > 0) {
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) out[t].ok = 0;
+  }
+  int trip = 0;
+  for (int gb = g0; gb < g1; gb += 64, ++trip) {  // wave-uniform
     const int g = gb + lane;
     const bool valid = g < g1;
     const int gc = valid ? g : gb;
@@ -496,23 +535,22 @@ __device__ __forceinline__ void quant_groups_f6(const QuantArgs& a, const float*
     const float clip = __int_as_float(__builtin_amdgcn_ds_bpermute(r << 2, __float_as_int(cl)));
     const float s = quantize32(ev, od, clip, qmaxf, rqmax, load, a.per_token ? row_amax_of(sR, r) : -1.0f);
     if (!valid) continue;
-    const v6i bits = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
     // The instruction's result must not share registers with its sources
     // (measured: a result placed inside the second source comes out wrong in
-    // one dword per lane), and the register allocator may place it there;
-    // holding both sources live past it rules that out.
-    asm volatile("" ::"v"(ev), "v"(od));
+    // one dword per lane).  The register allocator may place it there, and a
+    // fence that only keeps the sources live can be scheduled ahead of the
+    // instruction, so it is issued here with an early-clobber result, which
+    // no input may overlap.
+    v6i bits;
+    asm volatile("s_nop 1\n\tv_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, 1.0" : "=&v"(bits) : "v"(ev), "v"(od));
     const int row = row0 + r;
-    uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<char*>(a.codes) +
-                                          ((int64_t)(row >> 5) * Gp + (j >> 1)) * kF6BlockBytes +
-                                          ((row & 31) + 32 * (j & 1)) * 24);
-    dst[0] = uint2{(uint32_t)bits[0], (uint32_t)bits[1]};
-    dst[1] = uint2{(uint32_t)bits[2], (uint32_t)bits[3]};
-    dst[2] = uint2{(uint32_t)bits[4], (uint32_t)bits[5]};
-    if (a.scales_gm)
-      a.scales[(int64_t)j * a.scales_ld + row] = s;
-    else
-      a.scales[(int64_t)row * Ga + j] = s;
+    if constexpr (MAXT > 0) {
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t)
+        if (t == trip) out[t] = F6Group{bits, s, row, j, 1};
+    } else {
+      f6_store(a, Gp, Ga, row, j, bits, s);
+    }
     if (a.xt_out) {
       load(ev, od);
       float4* xo = reinterpret_cast<float4*>(a.xt_out + (int64_t)row * K + j * 32);
@@ -543,6 +581,82 @@ __device__ __forceinline__ void stage_factor(float* dst, const float* src, int n
   }
 }
 
+// P1 (fp32 rows of stride sp1) and P2 (its three bf16 planes when BFS, else
+// fp32 rows of stride sp2) into LDS for a compile-time factor shape, with
+// every global load issued before the first LDS write, so that the staging
+// takes one memory round trip.  NT threads take part; thread t is t.  The
+// planes are written two K rows at a time (one 32-bit store per plane).
+template <int N1, int N2, bool BFS, int NT>
+__device__ __forceinline__ void stage_factors_once(const float* __restrict__ P1, const float* __restrict__ P2,
+                                                   float* sP1, unsigned char* p2, int t) {
+  using S = XStrides<N1, N2>;
+  constexpr int U1 = (N1 * N1 + NT - 1) / NT;
+  float v1[U1];
+#pragma unroll
+  for (int u = 0; u < U1; ++u) {
+    const int idx = t + u * NT;
+    v1[u] = idx < N1 * N1 ? P1[idx] : 0.0f;
+  }
+  if constexpr (BFS) {
+    using L = BfLayout<N2>;
+    constexpr int NP = L::jp * (L::kb / 2);  // (pair of K rows b, b + 1; column j)
+    constexpr int U2 = (NP + NT - 1) / NT;
+    float v2[U2][2];
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      const int idx = t + u * NT;
+      const int b = 2 * (idx / L::jp), j = idx % L::jp;
+      v2[u][0] = (idx < NP && b < N2 && j < N2) ? P2[b * N2 + j] : 0.0f;
+      v2[u][1] = (idx < NP && b + 1 < N2 && j < N2) ? P2[(b + 1) * N2 + j] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U1; ++u) {
+      const int idx = t + u * NT;
+      if (idx < N1 * N1) sP1[(idx / N1) * S::sp1 + idx % N1] = v1[u];
+    }
+    uint32_t* d = reinterpret_cast<uint32_t*>(p2);
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      const int idx = t + u * NT;
+      if (idx < NP) {
+        const int b = 2 * (idx / L::jp), j = idx % L::jp;
+        uint32_t h0, m0, l0, h1, m1, l1;
+        split3_bf16(v2[u][0], &h0, &m0, &l0);
+        split3_bf16(v2[u][1], &h1, &m1, &l1);
+        const int o = (j * L::sb + b) >> 1;  // sb and b are even
+        d[o] = h0 | (h1 << 16);
+        d[o + L::plane / 2] = m0 | (m1 << 16);
+        d[o + L::plane] = l0 | (l1 << 16);
+      }
+    }
+  } else {
+    constexpr int U2 = (N2 * N2 + NT - 1) / NT;
+    float v2[U2];
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      const int idx = t + u * NT;
+      v2[u] = idx < N2 * N2 ? P2[idx] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U1; ++u) {
+      const int idx = t + u * NT;
+      if (idx < N1 * N1) sP1[(idx / N1) * S::sp1 + idx % N1] = v1[u];
+    }
+    float* d = reinterpret_cast<float*>(p2);
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      const int idx = t + u * NT;
+      if (idx < N2 * N2) d[(idx / N2) * S::sp2 + idx % N2] = v2[u];
+    }
+  }
+}
+
+// Work-groups per CU the register allocation is held to: two (at most 256
+// registers a lane, two waves a SIMD) where the instance fits in them without
+// spilling, which hides one wave's LDS and MFMA latency behind the other's;
+// one for the fp32-input instances with four row tiles and the generic ones.
+constexpr int xform_min_blocks(int nrt, int n1, int bf) { return n1 > 0 && (bf || nrt < 4) ? 2 : 1; }
+
 // Transform + quantize, NRT = ceil(n1 / 16) row tiles.  N1, N2 > 0 fix the
 // factor sizes at compile time (the k-loops then unroll fully, which keeps the
 // accumulators in place); N1 = N2 = 0 takes them from the arguments.
@@ -552,7 +666,16 @@ __device__ __forceinline__ void stage_factor(float* dst, const float* src, int n
 //
 // Dynamic LDS: P1 [n1][sp1] f32 at 0, P2 [n2][sp2] f32 at off_p2, and
 // X [R*n1][sx] f32 at off_x; after stage 1 the same region holds x~ as flat
-// fp32 rows [R][K].
+// fp32 rows [R][K] (WS: x~ has a region of its own at off_t).
+//
+// WS (compile-time shapes): 512 threads in two roles, so that each SIMD runs
+// one wave of MFMA stages beside one wave of quantizing.  Waves 0-3 run both
+// stages of chunk c; waves 4-7 meanwhile quantize chunk c - G (the previous
+// chunk of this work-group) from the x~ region, then copy the next chunk's X
+// into the X region and prefetch the one after.  Each step has two phases,
+// (stage 1 | quantize) and (stage 2 | next X), with a barrier after each:
+// stage 2 writes x~ only after the quantizer has read the previous chunk's,
+// and the next X lands only after stage 1 has read the current one.
 //
 // Work item = (row r of the chunk, 16-column tile jt of the n1 x n2 grid);
 // item_of gives each wave its items.  Stage 1 computes T[:, jt] = X_r * P2[:, jt]
@@ -563,17 +686,22 @@ __device__ __forceinline__ void stage_factor(float* dst, const float* src, int n
 // that order (rows a = 16 rt + 4 (l/16) + e at step s), so T stays in
 // registers.  Stage 2 then forms x~[:, jt] = P1^T * T with NRT accumulators
 // over the i tiles.
-template <int NRT, int N1, int N2, int RS, int NIM, int BF>
-__global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
+template <int NRT, int N1, int N2, int RS, int NIM, int BF, int WS>
+__global__ __launch_bounds__(WS ? 512 : 256, WS ? 1 : xform_min_blocks(NRT, N1, BF)) void quant_xform_kernel(
+    QuantArgs a) {
+  static_assert(!WS || RS > 0, "the two-role form needs a compile-time shape");
   extern __shared__ __align__(16) unsigned char lds[];
   float* sP1 = reinterpret_cast<float*>(lds);
   float* sP2 = reinterpret_cast<float*>(lds + a.off_p2);
   float* sX = reinterpret_cast<float*>(lds + a.off_x);
+  float* sXt = WS ? reinterpret_cast<float*>(lds + a.off_t) : sX;  // the x~ rows
   float* sR = reinterpret_cast<float*>(lds + a.off_rmax);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int ltid = tid & 255;  // thread within its role (WS), else tid
+  const int qwave = wave & 3;  // wave within its role
   const int n1 = N1 > 0 ? N1 : a.n1;
   const int n2 = N2 > 0 ? N2 : a.n2;
   const int K = n1 * n2;
@@ -582,7 +710,7 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const float qmaxf = (float)a.qmax;
   const float rqmax = 1.0f / qmaxf;
   const int njt = (n2 + 15) >> 4;
-  constexpr bool SR = N2 > 0 && ((N2 + 15) / 16) % NIM == 0;
+  constexpr bool SR = N2 > 0 && (((N2 + 15) / 16) % NIM == 0 || RS == 1);  // a wave's items share one row
 
   const int sp1 = N1 > 0 ? XStrides<N1, N2>::sp1 : a.sp1;
   const int sp2 = N2 > 0 ? XStrides<N1, N2>::sp2 : a.sp2;
@@ -617,26 +745,27 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   constexpr int PF = RS > 0 ? (RS * N1 * N2 / 4 + 255) / 256 : 1;
   typedef typename std::conditional<BF == 1, uint2, float4>::type raw_t;
   raw_t pre[PF];
+  // Every lane issues all PF loads (past the chunk's end it re-reads its last
+  // run), so the loads are counted in program order and the stash waits for
+  // them alone, not for the code stores issued after them.
   auto fetch = [&](int chunk) {
     const int row0 = chunk * R;
     const int nq = min(R, a.rows - row0) * K / 4;
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      const int q = tid + 256 * i;
-      if (q < nq) {
-        if constexpr (BF == 1)
-          pre[i] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + x_src(row0, q));
-        else
-          pre[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + x_src(row0, q));
-      }
+      const int q = min(ltid + 256 * i, nq - 1);
+      if constexpr (BF == 1)
+        pre[i] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + x_src(row0, q));
+      else
+        pre[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + x_src(row0, q));
     }
   };
-  auto stash = [&](int chunk) {
+  auto stash = [&](int chunk, bool pad_k) {
     const int row0 = chunk * R;
     const int nq = min(R, a.rows - row0) * K / 4;
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      const int q = tid + 256 * i;
+      const int q = ltid + 256 * i;
       if (q < nq) {
         if constexpr (BFS) {
           // four bf16 values as they are, into the bf16 X grid
@@ -653,11 +782,32 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
     }
     if constexpr (BFS && BL::kb > (N2 > 0 ? N2 : 16)) {  // zero K columns n2 .. kb - 1 of every X row
       constexpr int pad = BL::kb - N2;
-      for (int idx = tid; idx < R * N1 * pad; idx += 256) {
+      if (!pad_k) return;
+      for (int idx = ltid; idx < R * N1 * pad; idx += 256) {
         const int row = idx / pad;
         sXb[row * BL::sb + N2 + (idx - row * pad)] = 0;
       }
     }
+  };
+
+  // The clip of each chunk row, kept by lane r for row r (rows <= 16): the
+  // table indices are wave-uniform, so these are scalar loads, whose wait
+  // does not hold up the vector-memory traffic in flight.
+  auto clip_lanes = [&](int row0, int rows) {
+    float cl = 0.0f;
+    int idx = row0 / a.rows_per_clip, pos = row0 - idx * a.rows_per_clip;
+#pragma unroll
+    for (int r = 0; r < (RS > 0 ? RS : 16); ++r) {
+      if (r < rows) {
+        const float c = a.clips.c[idx];
+        cl = (lane == r || (r == rows - 1 && lane > r)) ? c : cl;  // lanes past the rows: the last row's
+        if (++pos == a.rows_per_clip) {
+          pos = 0;
+          ++idx;
+        }
+      }
+    }
+    return cl;
   };
 
   // Each pass of the grid covers gridDim.x consecutive chunks.  Work-groups
@@ -668,103 +818,189 @@ __global__ __launch_bounds__(256) void quant_xform_kernel(QuantArgs a) {
   const int xcd = blockIdx.x & 7;
   const int slot = xcd * (G >> 3) + min(xcd, G & 7) + (int)(blockIdx.x >> 3);
   // the first chunk's X is in flight while the factors are staged
-  if (RS > 0 && slot < nchunks) fetch(slot);
-  stage_factor(sP1, a.P1, n1, sp1, tid);
-  if constexpr (BFS)
-    stage_p2_planes<(N2 > 0 ? N2 : 16)>(a.P2, sP2b, 0, BL::jp, tid, 256);
-  else
+  const bool xrole = !WS || wave >= 4;  // this wave moves X and quantizes
+  if (RS > 0 && xrole && slot < nchunks) fetch(slot);
+  if constexpr (RS > 0) {
+    stage_factors_once<N1, N2, BFS, WS ? 512 : 256>(a.P1, a.P2, sP1, lds + a.off_p2, tid);
+  } else {
+    stage_factor(sP1, a.P1, n1, sp1, tid);
     stage_factor(sP2, a.P2, n2, sp2, tid);
-  for (int chunk = slot; chunk < nchunks; chunk += G) {
-    const int row0 = chunk * R;
-    const int rows = min(R, a.rows - row0);
-    // clip of chunk row `lane`, loaded now and used after both stages
-    const float cl = a.clips.c[(row0 + min(lane, rows - 1)) / a.rows_per_clip];
-    __syncthreads();  // previous chunk done with the x~ rows (and P staged on the first pass)
-
-    // ---- X rows into LDS: from the prefetch registers, or loaded here
-    if constexpr (RS > 0) {
-      stash(chunk);
-    } else {
-      const int nq = rows * K / 4;
-      for (int q = tid; q < nq; q += 256) {
-        const int64_t g = x_src(row0, q);
-        float4 v;
-        if (bf16)
-          v = widen(*reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + g));
-        else
-          v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + g);
-        put(x_dst(q), v);
-      }
+  }
+  if constexpr (WS) {
+    // the two-role pipeline (see above); x~ of chunk cq waits in its region
+    // for the quantizer while the stages run on chunk c
+    if (xrole && slot < nchunks) {
+      stash(slot, true);
+      if (slot + G < nchunks) fetch(slot + G);
     }
     __syncthreads();
-    // the next chunk's X is in flight during both MFMA stages
-    if constexpr (RS > 0) {
-      if (chunk + G < nchunks) fetch(chunk + G);
-    }
-
-    // ---- stage 1 for the wave's items; all of them run in one loop so
-    // NI * NRT accumulator chains interleave
-    const int items = rows * njt;
-    int nmine = 0;
+    // steps of this work-group: one per chunk, and one more that quantizes
+    // the last; each role runs its own loop (so that neither keeps the
+    // other's registers live), both meeting the same two barriers a step
+    const int nsteps = slot < nchunks ? (nchunks - 1 - slot) / G + 2 : 0;
+    if (!xrole) {
+      v4f T[NIM][NRT];
+      for (int i = 0, c = slot; i < nsteps; ++i, c += G) {
+        const bool st = c < nchunks;
+        int nmine = 0;
+        if (st) {
+          const int items = min(R, a.rows - c * R) * njt;
 #pragma unroll
-    for (int ii = 0; ii < NIM; ++ii) nmine += (item_of<SR, NIM>(wave, ii) < items) ? 1 : 0;
-    v4f T[NIM][NRT];
+          for (int ii = 0; ii < NIM; ++ii) nmine += (item_of<SR, NIM>(wave, ii) < items) ? 1 : 0;
 #pragma unroll
-    for (int ii = 0; ii < NIM; ++ii)
+          for (int ii = 0; ii < NIM; ++ii)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) T[ii][rt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (BFS) {
-      switch (nmine) {
-        case 4: if constexpr (NIM >= 4) stage1_bf<NRT, N1, N2, 4, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
-        case 3: if constexpr (NIM >= 3) stage1_bf<NRT, N1, N2, 3, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
-        case 2: if constexpr (NIM >= 2) stage1_bf<NRT, N1, N2, 2, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
-        case 1: stage1_bf<NRT, N1, N2, 1, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
-        default: break;
-      }
-    } else {
-      switch (nmine) {
-        case 4: if constexpr (NIM >= 4) stage1<NRT, N1, N2, 4, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
-        case 3: if constexpr (NIM >= 3) stage1<NRT, N1, N2, 3, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
-        case 2: if constexpr (NIM >= 2) stage1<NRT, N1, N2, 2, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
-        case 1: stage1<NRT, N1, N2, 1, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
-        default: break;
-      }
-    }
-    __syncthreads();  // every X read is done; x~ may now overwrite the region
-
-    // ---- stage 2: x~[i][j] = sum_a P1[a][i] T[a][j]
-    switch (nmine) {
-      case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
-      case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
-      case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
-      case 1: stage2<NRT, N1, N2, 1, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
-      default: break;
-    }
-    __syncthreads();
-
-    // ---- per-token steps: each row's absmax over its whole x~ row (the
-    // max is order-free), one partial per wave, combined when used
-    if (a.per_token) {
-      for (int r = 0; r < rows; ++r) {
-        float m = 0.0f;
-        for (int q = tid; q < (K >> 2); q += 256) {
-          const float4 v = *reinterpret_cast<const float4*>(sX + xt_pos(r * K + 4 * q));
-          m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            for (int rt = 0; rt < NRT; ++rt) T[ii][rt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (BFS) {
+            switch (nmine) {
+              case 4: if constexpr (NIM >= 4) stage1_bf<NRT, N1, N2, 4, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+              case 3: if constexpr (NIM >= 3) stage1_bf<NRT, N1, N2, 3, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+              case 2: if constexpr (NIM >= 2) stage1_bf<NRT, N1, N2, 2, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+              case 1: stage1_bf<NRT, N1, N2, 1, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+              default: break;
+            }
+          } else {
+            switch (nmine) {
+              case 4: if constexpr (NIM >= 4) stage1<NRT, N1, N2, 4, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+              case 3: if constexpr (NIM >= 3) stage1<NRT, N1, N2, 3, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+              case 2: if constexpr (NIM >= 2) stage1<NRT, N1, N2, 2, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+              case 1: stage1<NRT, N1, N2, 1, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+              default: break;
+            }
+          }
         }
+        __syncthreads();  // stage 1 done with X; the quantizer done with the x~ rows
+        switch (nmine) {
+          case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
+          case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
+          case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
+          case 1: stage2<NRT, N1, N2, 1, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
+          default: break;
+        }
+        __syncthreads();  // x~ of chunk c and X of chunk c + G are in place
+      }
+    } else {
+      // fp6 codes of the chunk being quantized, stored in phase B after the
+      // next X is copied in (the prefetch loads are then the newest memory
+      // operations, so copying X waits for them alone)
+      constexpr int MAXT = (((RS * (N1 * N2 / 32) + 3) / 4) + 63) / 64;
+      F6Group fout[MAXT];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-        if (lane == 0) sR[4 * r + wave] = m;
+      for (int t = 0; t < MAXT; ++t) fout[t].ok = 0;
+      for (int i = 0, c = slot; i < nsteps; ++i, c += G) {
+        const bool st = c < nchunks;
+        if (i > 0) {  // chunk c - G, whose x~ stage 2 wrote in the previous step
+          const int row0 = (c - G) * R;
+          const int qrows = min(R, a.rows - row0);
+          const float cl = clip_lanes(row0, qrows);
+          if (a.codes_fmt == kCodesTiledF6)
+            quant_groups_f6<MAXT>(a, sXt, sR, row0, qrows, K, qwave, lane, cl, qmaxf, rqmax, fout);
+          else if (a.codes_fmt == kCodesTiledI8)
+            quant_chunk<kCodesTiledI8>(a, sXt, sR, row0, qrows, K, qwave, lane, cl, qmaxf, rqmax);
+          else
+            quant_chunk<kCodesCanonical>(a, sXt, sR, row0, qrows, K, qwave, lane, cl, qmaxf, rqmax);
+        }
+        __syncthreads();  // stage 1 done with X; the quantizer done with the x~ rows
+        if (st && c + G < nchunks) stash(c + G, false);
+        if (i > 0 && a.codes_fmt == kCodesTiledF6) f6_store_deferred<MAXT>(a, K, fout);
+        if (st && c + 2 * G < nchunks) fetch(c + 2 * G);
+        __syncthreads();  // x~ of chunk c and X of chunk c + G are in place
+      }
+    }
+  } else {
+    for (int chunk = slot; chunk < nchunks; chunk += G) {
+      const int row0 = chunk * R;
+      const int rows = min(R, a.rows - row0);
+      // clip of chunk row `lane`, loaded now and used after both stages
+      const float cl = clip_lanes(row0, rows);
+      __syncthreads();  // previous chunk done with the x~ rows (and P staged on the first pass)
+
+      // ---- X rows into LDS: from the prefetch registers, or loaded here
+      if constexpr (RS > 0) {
+        stash(chunk, true);
+      } else {
+        const int nq = rows * K / 4;
+        for (int q = tid; q < nq; q += 256) {
+          const int64_t g = x_src(row0, q);
+          float4 v;
+          if (bf16)
+            v = widen(*reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + g));
+          else
+            v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + g);
+          put(x_dst(q), v);
+        }
       }
       __syncthreads();
-    }
+      // the next chunk's X is in flight during both MFMA stages
+      if constexpr (RS > 0) {
+        if (chunk + G < nchunks) fetch(chunk + G);
+      }
 
-    // ---- quantize groups of the flat transformed rows
-    if (a.codes_fmt == kCodesTiledF6)
-      quant_groups_f6(a, sX, sR, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
-    else if (a.codes_fmt == kCodesTiledI8)
-      quant_chunk<kCodesTiledI8>(a, sX, sR, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
-    else
-      quant_chunk<kCodesCanonical>(a, sX, sR, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
+      // ---- stage 1 for the wave's items; all of them run in one loop so
+      // NI * NRT accumulator chains interleave
+      const int items = rows * njt;
+      int nmine = 0;
+  #pragma unroll
+      for (int ii = 0; ii < NIM; ++ii) nmine += (item_of<SR, NIM>(wave, ii) < items) ? 1 : 0;
+      v4f T[NIM][NRT];
+  #pragma unroll
+      for (int ii = 0; ii < NIM; ++ii)
+  #pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) T[ii][rt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (BFS) {
+        switch (nmine) {
+          case 4: if constexpr (NIM >= 4) stage1_bf<NRT, N1, N2, 4, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+          case 3: if constexpr (NIM >= 3) stage1_bf<NRT, N1, N2, 3, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+          case 2: if constexpr (NIM >= 2) stage1_bf<NRT, N1, N2, 2, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+          case 1: stage1_bf<NRT, N1, N2, 1, NIM, SR>(sXb, sP2b, wave, njt, li, lk, T); break;
+          default: break;
+        }
+      } else {
+        switch (nmine) {
+          case 4: if constexpr (NIM >= 4) stage1<NRT, N1, N2, 4, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+          case 3: if constexpr (NIM >= 3) stage1<NRT, N1, N2, 3, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+          case 2: if constexpr (NIM >= 2) stage1<NRT, N1, N2, 2, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+          case 1: stage1<NRT, N1, N2, 1, NIM, SR>(a, sP2, sX, wave, njt, li, lk, T); break;
+          default: break;
+        }
+      }
+      __syncthreads();  // every X read is done; x~ may now overwrite the region
+
+      // ---- stage 2: x~[i][j] = sum_a P1[a][i] T[a][j]
+      switch (nmine) {
+        case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+        case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+        case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+        case 1: stage2<NRT, N1, N2, 1, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+        default: break;
+      }
+      __syncthreads();
+
+      // ---- per-token steps: each row's absmax over its whole x~ row (the
+      // max is order-free), one partial per wave, combined when used
+      if (a.per_token) {
+        for (int r = 0; r < rows; ++r) {
+          float m = 0.0f;
+          for (int q = tid; q < (K >> 2); q += 256) {
+            const float4 v = *reinterpret_cast<const float4*>(sX + xt_pos(r * K + 4 * q));
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+          }
+  #pragma unroll
+          for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+          if (lane == 0) sR[4 * r + wave] = m;
+        }
+        __syncthreads();
+      }
+
+      // ---- quantize groups of the flat transformed rows
+      F6Group none[1];
+      if (a.codes_fmt == kCodesTiledF6)
+        quant_groups_f6<0>(a, sX, sR, row0, rows, K, wave, lane, cl, qmaxf, rqmax, none);
+      else if (a.codes_fmt == kCodesTiledI8)
+        quant_chunk<kCodesTiledI8>(a, sX, sR, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
+      else
+        quant_chunk<kCodesCanonical>(a, sX, sR, row0, rows, K, wave, lane, cl, qmaxf, rqmax);
+    }
   }
 }
 
@@ -795,11 +1031,12 @@ int bf_p2_bytes(int n2) { return 3 * ((n2 + 15) / 16 * 16) * bf_sb(n2) * 2; }
 bool plan_quant(QuantArgs& a) {
   const int budget = 160 * 1024;
   const int njt = (a.n2 + 15) / 16;
-  int R = 0, nim = 2;
-#define LOOPQ_PLAN_SHAPE(n1_, n2_, rs_, nim_) \
-  if (a.n1 == n1_ && a.n2 == n2_) {           \
-    R = rs_;                                  \
-    nim = nim_;                               \
+  int R = 0, nim = 2, ws = 0;
+#define LOOPQ_PLAN_SHAPE(n1_, n2_, rs_, nim_, ws_) \
+  if (a.n1 == n1_ && a.n2 == n2_) {                \
+    R = rs_;                                       \
+    nim = nim_;                                    \
+    ws = (ws_) & (a.bf16 ? 1 : 2);                 \
   }
   LOOPQ_SHAPES(LOOPQ_PLAN_SHAPE)
 #undef LOOPQ_PLAN_SHAPE
@@ -854,6 +1091,21 @@ bool plan_quant(QuantArgs& a) {
   a.off_t = 0;
   a.off_rmax = a.off_x + xb_for(sx, R);
   a.lds_bytes = a.off_rmax + kRowMaxBytes;
+  a.ws = 0;
+  // the two-role form (compile-time shapes; per-token steps need a barrier
+  // among the quantizing waves alone, so they keep the one-phase form): X
+  // and the x~ rows in regions of their own
+  if (fixed && ws && !a.per_token) {
+    const int xg = bfs ? R * a.n1 * bf_sb(a.n2) * 2 : R * a.n1 * sx * 4;
+    const int off_t = a.off_x + (xg + 15) / 16 * 16;
+    const int off_rmax = off_t + (R * a.K * 4 + 15) / 16 * 16;
+    if (off_rmax + kRowMaxBytes <= budget) {
+      a.ws = 1;
+      a.off_t = off_t;
+      a.off_rmax = off_rmax;
+      a.lds_bytes = off_rmax + kRowMaxBytes;
+    }
+  }
   return true;
 }
 
@@ -899,33 +1151,38 @@ hipError_t launch_quant_act(QuantArgs a, hipStream_t s) {
   }
   if (!plan_quant(a)) return hipErrorInvalidConfiguration;
   const void* fn = nullptr;
-#define LOOPQ_KERNEL_SHAPE(n1_, n2_, rs_, nim_)                                                     \
-  if (a.n1 == n1_ && a.n2 == n2_)                                                                   \
-    fn = a.bf16 ? reinterpret_cast<const void*>(quant_xform_kernel<(n1_ + 15) / 16, n1_, n2_, rs_, nim_, 1>) \
-                : reinterpret_cast<const void*>(quant_xform_kernel<(n1_ + 15) / 16, n1_, n2_, rs_, nim_, 0>);
+#define LOOPQ_KERNEL_FORM(n1_, n2_, rs_, nim_, bf_, ws_)                                                  \
+  (a.ws ? reinterpret_cast<const void*>(quant_xform_kernel<(n1_ + 15) / 16, n1_, n2_, rs_, nim_, bf_, ws_>) \
+        : reinterpret_cast<const void*>(quant_xform_kernel<(n1_ + 15) / 16, n1_, n2_, rs_, nim_, bf_, 0>))
+#define LOOPQ_KERNEL_SHAPE(n1_, n2_, rs_, nim_, ws_)                                     \
+  if (a.n1 == n1_ && a.n2 == n2_)                                                        \
+    fn = a.bf16 ? LOOPQ_KERNEL_FORM(n1_, n2_, rs_, nim_, 1, ((ws_) & 1) ? 1 : 0)         \
+                : LOOPQ_KERNEL_FORM(n1_, n2_, rs_, nim_, 0, ((ws_) & 2) ? 1 : 0);
   LOOPQ_SHAPES(LOOPQ_KERNEL_SHAPE)
 #undef LOOPQ_KERNEL_SHAPE
+#undef LOOPQ_KERNEL_FORM
   if (fn == nullptr) {
     switch ((a.n1 + 15) / 16) {
-      case 1: fn = reinterpret_cast<const void*>(quant_xform_kernel<1, 0, 0, 0, 2, 0>); break;
-      case 2: fn = reinterpret_cast<const void*>(quant_xform_kernel<2, 0, 0, 0, 2, 0>); break;
-      case 3: fn = reinterpret_cast<const void*>(quant_xform_kernel<3, 0, 0, 0, 2, 0>); break;
-      case 4: fn = reinterpret_cast<const void*>(quant_xform_kernel<4, 0, 0, 0, 2, 0>); break;
-      case 5: fn = reinterpret_cast<const void*>(quant_xform_kernel<5, 0, 0, 0, 2, 0>); break;
-      case 6: fn = reinterpret_cast<const void*>(quant_xform_kernel<6, 0, 0, 0, 2, 0>); break;
-      case 7: fn = reinterpret_cast<const void*>(quant_xform_kernel<7, 0, 0, 0, 2, 0>); break;
-      case 8: fn = reinterpret_cast<const void*>(quant_xform_kernel<8, 0, 0, 0, 2, 0>); break;
+      case 1: fn = reinterpret_cast<const void*>(quant_xform_kernel<1, 0, 0, 0, 2, 0, 0>); break;
+      case 2: fn = reinterpret_cast<const void*>(quant_xform_kernel<2, 0, 0, 0, 2, 0, 0>); break;
+      case 3: fn = reinterpret_cast<const void*>(quant_xform_kernel<3, 0, 0, 0, 2, 0, 0>); break;
+      case 4: fn = reinterpret_cast<const void*>(quant_xform_kernel<4, 0, 0, 0, 2, 0, 0>); break;
+      case 5: fn = reinterpret_cast<const void*>(quant_xform_kernel<5, 0, 0, 0, 2, 0, 0>); break;
+      case 6: fn = reinterpret_cast<const void*>(quant_xform_kernel<6, 0, 0, 0, 2, 0, 0>); break;
+      case 7: fn = reinterpret_cast<const void*>(quant_xform_kernel<7, 0, 0, 0, 2, 0, 0>); break;
+      case 8: fn = reinterpret_cast<const void*>(quant_xform_kernel<8, 0, 0, 0, 2, 0, 0>); break;
       default: return hipErrorInvalidConfiguration;
     }
   }
+  const int threads = a.ws ? 512 : 256;
   int per_cu = 1, ncu = 256;
-  hipError_t e = prepare_launch(fn, a.lds_bytes, 256, &per_cu, &ncu);
+  hipError_t e = prepare_launch(fn, a.lds_bytes, threads, &per_cu, &ncu);
   if (e != hipSuccess) return e;
   const int nchunks = (a.rows + a.R - 1) / a.R;
   int blocks = ncu * per_cu;
   if (blocks > nchunks) blocks = nchunks;
   void* args[] = {&a};
-  e = hipLaunchKernel(fn, dim3(blocks), dim3(256), args, a.lds_bytes, s);
+  e = hipLaunchKernel(fn, dim3(blocks), dim3(threads), args, a.lds_bytes, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

@@ -168,24 +168,30 @@ __device__ __forceinline__ void split3_bf16(float v, uint32_t* h, uint32_t* m, u
 // 16 (rt0 + q) + 4 (l / 16) + e, column l % 16 (the fp32 MFMA's layout).
 // Every tile accumulates in the same order (K steps, then planes hi, mid,
 // lo), so a tile's value does not depend on which kernel or wave forms it.
-template <int N1, int N2, int NI, int NRT>
+// SA: all items share item 0's X grid and row tiles, whose A operands are
+// then read once per step for all of them.
+template <int N1, int N2, int NI, int NRT, bool SA = false>
 __device__ __forceinline__ void stage1_bf16(const uint16_t* const (&xgrid)[NI], const int (&rt0)[NI],
                                             const uint16_t* const (&pcol)[NI], int plane, int li, int lk,
                                             v4f (&T)[NI][NRT]) {
   using L = BfLayout<N2>;
+  constexpr int NA = SA ? 1 : NI;
 #pragma unroll
   for (int ks = 0; ks < L::kb / 32; ++ks) {
-    v4u a[NI][NRT], b[NI][3];
+    v4u a[NA][NRT], b[NI][3];
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
 #pragma unroll
       for (int p = 0; p < 3; ++p)
         b[ii][p] = *reinterpret_cast<const v4u*>(pcol[ii] + p * plane + li * L::sb + 32 * ks + 8 * lk);
+    }
+#pragma unroll
+    for (int ia = 0; ia < NA; ++ia) {
 #pragma unroll
       for (int q = 0; q < NRT; ++q) {
-        const int i = (rt0[ii] + q) * 16 + li;
-        a[ii][q] = *reinterpret_cast<const v4u*>(xgrid[ii] + (i < N1 ? i : N1 - 1) * L::sb + 32 * ks + 8 * lk);
-        if (i >= N1) a[ii][q] = v4u{0u, 0u, 0u, 0u};
+        const int i = (rt0[ia] + q) * 16 + li;
+        a[ia][q] = *reinterpret_cast<const v4u*>(xgrid[ia] + (i < N1 ? i : N1 - 1) * L::sb + 32 * ks + 8 * lk);
+        if (i >= N1) a[ia][q] = v4u{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -194,7 +200,7 @@ __device__ __forceinline__ void stage1_bf16(const uint16_t* const (&xgrid)[NI], 
       for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
         for (int q = 0; q < NRT; ++q)
-          T[ii][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[ii][q]),
+          T[ii][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[SA ? 0 : ii][q]),
                                                            __builtin_bit_cast(v8bf, b[ii][p]), T[ii][q], 0, 0, 0);
   }
 }
@@ -233,16 +239,23 @@ __device__ __forceinline__ void stage_p2_planes(const float* __restrict__ P2, ui
 }
 
 // Factor shapes of the Kronecker transforms in use (K = 256, 2048, 5632,
-// 2560, 6912, and a 32-wide test shape), each with its rows per chunk and the
-// most work items a wave then takes.  Chunk sizes make rows * ceil(n2 / 16)
-// items a multiple of the 4 waves where that fits (3 items per wave for
-// (64, 88) at 2 rows; (64, 108) has 7 per row and stays at one row).
+// 2560, 6912, and a 32-wide test shape), each with its rows per chunk, the
+// most work items a wave then takes, and the inputs for which the transform
+// kernel runs them in its two-role form (512 threads, MFMA stages beside the
+// quantizer) rather than as 256 threads doing one phase at a time: bit 0 for
+// bf16 input, bit 1 for fp32 input (set where it measured faster: the shapes
+// whose one-phase form fits one work-group per CU, and the small ones; (32,
+// 64) and (40, 64) run two one-phase work-groups per CU, which overlap their
+// phases as well).  Chunk sizes
+// make rows * ceil(n2 / 16) items a multiple of the 4 stage waves where that
+// fits (3 items per wave for (64, 88) at 2 rows; (64, 108) has 7 per row and
+// stays at one row).
 #define LOOPQ_SHAPES(X) \
-  X(16, 16, 16, 4)      \
-  X(32, 64, 4, 4)       \
-  X(64, 88, 2, 3)       \
-  X(40, 64, 3, 3)       \
-  X(64, 108, 1, 2)      \
-  X(4, 8, 16, 4)
+  X(16, 16, 16, 4, 3)   \
+  X(32, 64, 4, 4, 0)    \
+  X(64, 88, 2, 3, 3)    \
+  X(40, 64, 3, 3, 0)    \
+  X(64, 108, 1, 2, 3)   \
+  X(4, 8, 16, 4, 3)
 
 }  // namespace loopq
