@@ -28,6 +28,8 @@
 // register pipeline, and is not used.
 #include "gemm_tile.h"
 
+#include <cmath>
+
 namespace loopq {
 namespace {
 
@@ -60,19 +62,24 @@ __device__ __forceinline__ int coef_row(int i) {
   return (i & 3) < 3 ? i + 1 : ((((i >> 3) + 1) & 3) << 3) | (i & 4);
 }
 
-// SPLIT (rescale mode only): the split-K form of map_tile_split; the two
+// SPLIT (rescale mode only): 1, the split-K form of map_tile_split; the two
 // halves of each quadrant's sum are added through LDS, the first half's wave
 // adding the second's (a fixed order), and only the first half's wave
-// stores.  Every wave of that form reaches the barrier, so none returns early.
+// stores.  2, the four-way form of map_tile_split4: the four waves of a
+// work-group take the four quarters of one quadrant's K pairs, and wave 0
+// adds waves 1, 2, 3 in that order and stores.  Every wave of a split form
+// reaches the barrier, so none returns early.
 template <int MODE, int SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
-  __shared__ float red[SPLIT ? 2 * 64 * 64 : 1];
+  __shared__ float red[SPLIT == 2 ? 3 * 64 * 64 : SPLIT ? 2 * 64 * 64 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int c = lane & 31;
   int m_base, n_base, kh = 0;
-  if (SPLIT)
+  if (SPLIT == 2)
+    map_tile_split4(g, wave, &m_base, &n_base, &kh);
+  else if (SPLIT)
     map_tile_split(g, wave, &m_base, &n_base, &kh);
   else
     map_tile(g, wave, &m_base, &n_base);
@@ -203,8 +210,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
 
   // this wave's group pairs [p0, p1)
   const int half = (Gp + 1) >> 1;
-  const int p0 = SPLIT && kh ? half : 0;
-  const int p1 = SPLIT && !kh ? half : Gp;
+  const int quarter = (Gp + 3) >> 2;
+  const int p0 = SPLIT == 2 ? min(Gp, kh * quarter) : SPLIT && kh ? half : 0;
+  const int p1 = SPLIT == 2 ? min(Gp, p0 + quarter) : SPLIT && !kh ? half : Gp;
   // Loads past the last pair re-read it (in bounds, unused), so the loop
   // body is one basic block the barriers can order.
   if (active && p0 < p1) {
@@ -225,7 +233,27 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_kernel(GemmArgs g) {
     if (p < p1) compute(s0, p);
   }
 
-  if (SPLIT) {
+  if (SPLIT == 2) {
+    if (kh > 0 && active) {
+      float* r = red + (kh - 1) * 64 * 64;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) r[((t * 2 + u) * 16 + e) * 64 + lane] = acc[t][u][e];
+    }
+    __syncthreads();
+    if (kh > 0 || !active) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[t][u][e] += red[w * 64 * 64 + ((t * 2 + u) * 16 + e) * 64 + lane];
+  } else if (SPLIT) {
     float* r = red + (wave & 1) * 64 * 64;
     if (kh == 1 && active) {
 #pragma unroll
@@ -300,17 +328,29 @@ hipError_t launch_expand_weights_f6(const uint8_t* w_codes, int K, int N, void* 
   return hipGetLastError();
 }
 
-// Whether the split-K form spreads the work better: every wave of a 128x128
-// tile runs over all of K, every wave of the split form over half of it, and
-// the waves of a launch land about evenly on the chip's SIMDs (four per CU),
-// so a launch takes about ceil(waves / SIMDs) wave times.  The split form is
-// taken when that estimate is at least 5% lower (it also pays an exchange
-// through LDS).
-bool split_k_pays(int64_t tiles, int64_t tiles_split) {
-  const int64_t simds = 4 * (int64_t)device_cu_count();
-  const double whole = (double)((4 * tiles + simds - 1) / simds);
-  const double split = 0.5 * (double)((4 * tiles_split + simds - 1) / simds);
-  return split < 0.95 * whole;
+// Which tile form spreads a launch best over the chip's SIMDs (four per CU):
+// 0 the 128x128 form (every wave over all of K), 1 the two-way split-K form
+// (64x128 tiles, half of K per wave), 2 the four-way form (64x64 tiles, a
+// quarter of K per wave).  The waves of a launch land about evenly on the
+// SIMDs, so it takes about ceil(waves / SIMDs) wave times of its K fraction;
+// a launch that leaves at most one wave on each SIMD hides none of a wave's
+// latencies behind another's (measured about 25% slower per wave), and each
+// split pays an exchange through LDS (5%).  The four-way form needs 32 group
+// pairs of K (8 per wave).
+int gemm_form(int M, int N, int K) {
+  const double simds = 4.0 * device_cu_count();
+  auto cost = [&](int64_t tiles, double kfrac) {
+    const double waves = 4.0 * (double)tiles;
+    return kfrac * std::ceil(waves / simds) * (waves <= simds ? 1.25 : 1.0);
+  };
+  const int64_t t0 = (int64_t)((N + 127) / 128) * ((M + 127) / 128);
+  const int64_t t1 = (int64_t)((N + 127) / 128) * ((M + 63) / 64);
+  const int64_t t2 = (int64_t)((N + 63) / 64) * ((M + 63) / 64);
+  const double c0 = cost(t0, 1.0);
+  const double c1 = cost(t1, 0.5) / 0.95;
+  const double c2 = ((((K >> 5) + 1) >> 1) >= 32) ? cost(t2, 0.25) / (0.95 * 0.95) : 1e30;
+  if (c2 < c1 && c2 < c0) return 2;
+  return c1 < c0 ? 1 : 0;
 }
 
 hipError_t launch_gemm_f6(const void* a_tiled, const float* a_scales_gm, int ld_sa, int M, int K,
@@ -341,7 +381,11 @@ hipError_t launch_gemm_f6(const void* a_tiled, const float* a_scales_gm, int ld_
   g.dots = dots;
   const int64_t tiles = (int64_t)((N + 127) / 128) * ((M + 127) / 128);
   const int64_t tiles_split = (int64_t)((N + 127) / 128) * ((M + 63) / 64);
-  if (mode == 0 && split_k_pays(tiles, tiles_split)) {
+  const int form = mode == 0 ? gemm_form(M, N, K) : 0;
+  if (form == 2) {
+    dim3 grid((unsigned)((int64_t)((N + 63) / 64) * ((M + 63) / 64)));
+    hipLaunchKernelGGL((gemm_f6_kernel<0, 2>), grid, dim3(256), 0, s, g);
+  } else if (form == 1) {
     dim3 grid((unsigned)tiles_split);
     hipLaunchKernelGGL((gemm_f6_kernel<0, 1>), grid, dim3(256), 0, s, g);
   } else {

@@ -89,6 +89,23 @@ __device__ __forceinline__ void map_tile_split(const GemmArgs& g, int wave, int*
   *kh = wave >> 1;
 }
 
+// Four-way split-K form: one 64x64 quadrant per work-group, wave w takes the
+// w-th quarter of the K pairs (kq = w).  Tile numbering and XCD placement as
+// map_tile_split, over 64x64 tiles.
+__device__ __forceinline__ void map_tile_split4(const GemmArgs& g, int wave, int* m_base, int* n_base, int* kq) {
+  const int Mp = (g.M + 63) >> 6;
+  const int Np = (g.N + 63) >> 6;
+  const int total = Mp * Np;
+  const int xcd = blockIdx.x & 7;
+  const int q = xcd * (total >> 3) + min(xcd, total & 7) + (int)(blockIdx.x >> 3);
+  const int grp = q / (8 * Np);
+  const int gm = min(Mp - grp * 8, 8);
+  const int r = q - grp * 8 * Np;
+  *m_base = (grp * 8 + r % gm) * 64;
+  *n_base = (r / gm) * 64;
+  *kq = wave;
+}
+
 // Result element e of lane l of tile (t, u) is row m = m_base + 32 t + l % 32
 // and column n = n_base + 32 u + 8 (e / 4) + 4 (l / 32) + e % 4.
 __device__ __forceinline__ void store_y(const GemmArgs& g, const float (&acc)[2][2][16], int m_base,
