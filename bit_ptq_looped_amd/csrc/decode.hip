@@ -398,7 +398,9 @@ struct XPlan {
   // holds the fp32 or bf16 X grid and later the fp32 x~ row
   using BL = BfLayout<N2>;
   static constexpr int p2_bytes = N2 * sp2 * 4 > BL::p2_bytes ? N2 * sp2 * 4 : BL::p2_bytes;
-  static constexpr int off_p2 = (N1 * sp1 * 4 + 15) / 16 * 16;
+  // P1 as fp32 rows (fp32 input) or as its bf16 stage-2 planes (bf16 input)
+  static constexpr int p1_bytes = N1 * sp1 * 4 > P1Layout<N1>::bytes ? N1 * sp1 * 4 : P1Layout<N1>::bytes;
+  static constexpr int off_p2 = (p1_bytes + 15) / 16 * 16;
   static constexpr int off_x = off_p2 + (p2_bytes + 15) / 16 * 16;
   static constexpr int x_f32 = N1 * sx * 4 > K * 4 ? N1 * sx * 4 : K * 4;
   static constexpr int x_bytes = x_f32 > N1 * BL::sb * 2 ? x_f32 : N1 * BL::sb * 2;
@@ -421,7 +423,8 @@ struct ItemPlan {
   static constexpr int sp1 = XStrides<N1, N2>::sp1, sx = XStrides<N1, N2>::sx;
   static constexpr int p2_f32 = N2 * 16 * 4;          // the tile's fp32 columns [n2][16]
   static constexpr int p2_bf = 3 * 16 * BL::sb * 2;   // or its bf16 planes (16 columns)
-  static constexpr int off_p2 = (N1 * sp1 * 4 + 15) / 16 * 16;
+  static constexpr int p1_bytes = N1 * sp1 * 4 > P1Layout<N1>::bytes ? N1 * sp1 * 4 : P1Layout<N1>::bytes;
+  static constexpr int off_p2 = (p1_bytes + 15) / 16 * 16;
   static constexpr int off_x = off_p2 + ((p2_f32 > p2_bf ? p2_f32 : p2_bf) + 15) / 16 * 16;
   static constexpr int x_bytes = N1 * sx * 4 > N1 * BL::sb * 2 ? N1 * sx * 4 : N1 * BL::sb * 2;
   static constexpr int off_t = (off_x + x_bytes + 15) / 16 * 16;
@@ -446,22 +449,43 @@ __device__ __forceinline__ void p2_planes_commit(const MatRegs<N2>& m, uint16_t*
       dst[2 * L::plane + j * L::sb + b] = (uint16_t)l;
     }
   }
-  // zeros: columns j >= N2 (all b < kb) and K indices b >= N2 of columns j < N2
-  constexpr int padj = (L::jp - N2) * L::kb, padb = N2 * (L::kb - N2);
-  for (int idx = threadIdx.x; idx < padj + padb; idx += 256) {
-    int j, b;
-    if (idx < padj) {
-      j = N2 + idx / L::kb;
-      b = idx % L::kb;
-    } else {
-      constexpr int w = L::kb - N2 > 0 ? L::kb - N2 : 1;  // (no such entries when N2 % 32 == 0)
-      j = (idx - padj) / w;
-      b = N2 + (idx - padj) % w;
-    }
+  // zeros: K indices b >= N2 of every column (none when N2 % 32 == 0)
+  constexpr int w = L::kb - N2 > 0 ? L::kb - N2 : 1;
+  constexpr int padb = N2 * (L::kb - N2);
+  for (int idx = threadIdx.x; idx < padb; idx += 256) {
+    const int j = idx / w, b = N2 + idx % w;
 #pragma unroll
     for (int p = 0; p < 3; ++p) dst[p * L::plane + j * L::sb + b] = 0;
   }
 }
+// The P1 registers of stage_matrix_issue committed as the bf16 stage-2 planes
+// (P1Layout): element (a, i) to row i, slot p1_slot(a); zeros at the rows i
+// and slots of reduction rows a past n1 (positions no element writes).
+template <int N1>
+__device__ __forceinline__ void p1_planes_commit(const MatRegs<N1>& m, uint16_t* dst) {
+  using L = P1Layout<N1>;
+#pragma unroll
+  for (int u = 0; u < MatRegs<N1>::T; ++u) {
+    const int idx = threadIdx.x + 256 * u;  // element a * N1 + i of P1
+    if (idx < N1 * N1) {
+      const int a = idx / N1, i = idx - a * N1;
+      uint32_t h, mm, l;
+      split3_bf16(m.v[u], &h, &mm, &l);
+      const int o = i * L::sb + p1_slot(a);
+      dst[o] = (uint16_t)h;
+      dst[L::plane + o] = (uint16_t)mm;
+      dst[2 * L::plane + o] = (uint16_t)l;
+    }
+  }
+  for (int idx = threadIdx.x; idx < L::rows * L::ka; idx += 256) {
+    const int i = idx / L::ka, sl = idx - i * L::ka;
+    if (i >= N1 || p1_row_of_slot(sl) >= N1) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p) dst[p * L::plane + i * L::sb + sl] = 0;
+    }
+  }
+}
+
 template <int N1, int N2>
 __device__ __forceinline__ void x_row_commit_bf(const RowRegs<N1 * N2>& x, uint16_t* sXb) {
   using L = BfLayout<N2>;
@@ -520,7 +544,10 @@ __global__ __launch_bounds__(256) void xform_items_kernel(DecodeArgs g, float* _
   const int r = blockIdx.x / njt;
   const int jt = blockIdx.x - r * njt;
 
-  stage_matrix<N1, P::sp1>(g.P1, sP1);
+  if (g.bf16)
+    stage_p1_planes<N1, 256>(g.P1, reinterpret_cast<uint16_t*>(lds), tid);
+  else
+    stage_matrix<N1, P::sp1>(g.P1, sP1);
   if (g.bf16) {  // bf16 stage 1: the tile's P2 planes and the bf16 X grid
     using BL = BfLayout<N2>;
     uint16_t* sP2b = reinterpret_cast<uint16_t*>(lds + P::off_p2);
@@ -530,7 +557,7 @@ __global__ __launch_bounds__(256) void xform_items_kernel(DecodeArgs g, float* _
     __syncthreads();
     for (int rt = wave; rt < NRT; rt += 4) {
       const uint16_t* xg[1] = {sXb};
-      const uint16_t* pc[1] = {sP2b};
+      const uint16_t* pc[1] = {sP2b + li * BL::sb};
       const int rt0[1] = {rt};
       v4f T[1][1] = {{v4f{0.0f, 0.0f, 0.0f, 0.0f}}};
       stage1_bf16<N1, N2, 1, 1>(xg, rt0, pc, 16 * BL::sb, li, lk, T);
@@ -581,6 +608,36 @@ __global__ __launch_bounds__(256) void xform_items_kernel(DecodeArgs g, float* _
   __syncthreads();
 
   // stage 2: x~[it][tile] = sum_a P1[a][it] T[a][tile], a in the chunked kernel's order
+  if (g.bf16) {  // bf16 input: the six plane products per step (quant_core.h)
+    const uint16_t* sP1b = reinterpret_cast<const uint16_t*>(lds);
+    for (int it = wave; it < NRT; it += 4) {
+      v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < P1Layout<N1>::ka / 32; ++q) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {  // slot 8 lk + u: T row 32 q + 16 (u / 4) + 4 lk + u % 4
+          const int a = 32 * q + 16 * (u >> 2) + 4 * lk + (u & 3);
+          v[u] = a < n1 ? sT[a * 16 + li] : 0.0f;
+        }
+        v4u b[3], ap[3];
+        planes8(v, b);
+        p1_planes_at<N1>(sP1b, it, q, li, lk, ap);
+#pragma unroll
+        for (int k = 0; k < 6; ++k) o = s2_mm(ap[s2_pa(k)], b[s2_pb(k)], o);
+      }
+      mfma_settle_before_join();
+      const int j = jt * 16 + li;
+      if (j < n2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int io = it * 16 + 4 * lk + e;
+          if (io < n1) xt[(int64_t)r * K + io * n2 + j] = o[e];
+        }
+      }
+    }
+    return;
+  }
   for (int it = wave; it < NRT; it += 4) {
     v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
     const int i = it * 16 + li;
@@ -592,6 +649,7 @@ __global__ __launch_bounds__(256) void xform_items_kernel(DecodeArgs g, float* _
       o = __builtin_amdgcn_mfma_f32_16x16x4f32(masked(sP1[ac * P::sp1 + min(i, n1 - 1)], ar < n1 ? mi : 0u),
                                                sT[ac * 16 + li], o, 0, 0, 0);
     }
+    mfma_settle_before_join();
     const int j = jt * 16 + li;
     if (j < n2) {
 #pragma unroll
@@ -660,7 +718,7 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
       xg[u] = sXb;
-      pc[u] = sP2b + (jc[u] - li) * BL::sb;
+      pc[u] = sP2b + min(jc[u], N2 - 1) * BL::sb;  // columns past n2 read n2 - 1
       rt0[u] = rt[u];
       acc[u][0] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -718,7 +776,50 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
   // + 4 (l / 16) + s % 4, rows >= n1 masked), into the flat x~ row in the X
   // region (no longer read)
   float* sXt = sX;
-  {
+  if (g.bf16) {
+    // bf16 input: the six plane products per step (quant_core.h), the B
+    // planes split from T (rows past n1 as zero), tasks interleaved per product
+    const uint16_t* sP1b = reinterpret_cast<const uint16_t*>(lds);
+    constexpr int GT = NT < 2 ? NT : 2;  // tasks interleaved at a time (registers)
+#pragma unroll
+    for (int u0 = 0; u0 < NT; u0 += GT) {
+      v4f acc[GT];
+#pragma unroll
+      for (int g2 = 0; g2 < GT; ++g2) acc[g2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < P1Layout<N1>::ka / 32; ++q) {
+        v4u b[GT][3], ap[GT][3];
+#pragma unroll
+        for (int g2 = 0; g2 < GT; ++g2) {
+          const int u = u0 + g2 < NT ? u0 + g2 : NT - 1;
+          float v[8];
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {  // slot 8 lk + w: T row 32 q + 16 (w / 4) + 4 lk + w % 4
+            const int a = 32 * q + 16 * (w >> 2) + 4 * lk + (w & 3);
+            v[w] = a < n1 ? sT[a * P::st + jc[u]] : 0.0f;
+          }
+          planes8(v, b[g2]);
+          p1_planes_at<N1>(sP1b, rt[u], q, li, lk, ap[g2]);
+        }
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+#pragma unroll
+          for (int g2 = 0; g2 < GT; ++g2) acc[g2] = s2_mm(ap[g2][s2_pa(k)], b[g2][s2_pb(k)], acc[g2]);
+      }
+      mfma_settle_before_join();
+#pragma unroll
+      for (int g2 = 0; g2 < GT; ++g2) {
+        const int u = u0 + g2;
+        if (u < NT && has[u] && jc[u] < n2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int io = rt[u] * 16 + 4 * lk + e;
+            if (io < n1) sXt[io * n2 + jc[u]] = acc[g2][e];
+          }
+        }
+      }
+    }
+  } else {
     v4f acc[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -742,6 +843,7 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
       for (int u = 0; u < NT; ++u)
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s & 1][u], bv[s & 1][u], acc[u], 0, 0, 0);
     }
+    mfma_settle_before_join();  // (this branch of the input type joins the bf16 one)
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
       if (has[u] && jc[u] < n2) {
@@ -1001,7 +1103,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
       stage_matrix_issue<N2>(g.P2, m2);
       x_row_issue<P::K>(g, 0, x0);
       load(0, wa);
-      stage_matrix_commit<N1, P::sp1>(m1, sP1);
+      if (g.bf16)
+        p1_planes_commit<N1>(m1, reinterpret_cast<uint16_t*>(lds));
+      else
+        stage_matrix_commit<N1, P::sp1>(m1, sP1);
       if (g.bf16) {
         p2_planes_commit<N2>(m2, reinterpret_cast<uint16_t*>(lds + P::off_p2));
         x_row_commit_bf<N1, N2>(x0, reinterpret_cast<uint16_t*>(lds + P::off_x));

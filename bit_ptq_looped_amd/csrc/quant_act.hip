@@ -330,7 +330,7 @@ __device__ __forceinline__ void stage1_bf(const uint16_t* sXb, const uint16_t* s
     const int r = item / njt;
     const int jt = item - r * njt;
     xg[ii] = sXb + r * N1 * L::sb;
-    pc[ii] = sP2b + jt * 16 * L::sb;
+    pc[ii] = sP2b + min(jt * 16 + li, N2 - 1) * L::sb;  // columns past n2 read n2 - 1
     rt0[ii] = 0;
 #pragma unroll
     for (int q = 0; q < NRT; ++q) acc[ii][q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -407,6 +407,61 @@ __device__ __forceinline__ void stage2(const QuantArgs& a, const float* sP1, flo
         for (int e = 0; e < 4; ++e) {
           const int io = it * 16 + 4 * lk + e;  // result element e of lane l: row 4 (l/16) + e
           if (io < n1) sX[xt_pos(r * K + io * n2 + j)] = o[ii][it][e];
+        }
+    }
+  }
+}
+
+// Stage 2 on the bf16 MFMA for the same items (bf16 input, compile-time
+// shape): the six plane products of each 16x16 tile of x~ and step of 32
+// reduction indices (quant_core.h), the B planes split from the stage-1
+// result registers (step q takes tiles 2q and 2q + 1), the A planes read from
+// the P1 planes in LDS.  Product k runs across all of the wave's tiles before
+// product k + 1, so the six products of a tile do not wait on each other.
+template <int NRT, int N1, int N2, int NI, int NIM, bool SR>
+__device__ __forceinline__ void stage2_bf(const uint16_t* sP1b, float* sX, int wave, int njt, int li, int lk,
+                                          const v4f (&T)[NIM][NRT]) {
+  constexpr int K = N1 * N2;
+  constexpr int NQ = P1Layout<N1>::ka / 32;
+  v4f o[NI][NRT];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) o[ii][it] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    v4u b[NI][3], a[NRT][3];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = T[ii][2 * q][e];
+        v[4 + e] = 2 * q + 1 < NRT ? T[ii][2 * q + 1 < NRT ? 2 * q + 1 : 0][e] : 0.0f;
+      }
+      planes8(v, b[ii]);
+    }
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) p1_planes_at<N1>(sP1b, it, q, li, lk, a[it]);
+#pragma unroll
+    for (int k = 0; k < 6; ++k)
+#pragma unroll
+      for (int it = 0; it < NRT; ++it)
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) o[ii][it] = s2_mm(a[it][s2_pa(k)], b[ii][s2_pb(k)], o[ii][it]);
+  }
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int item = item_of<SR, NIM>(wave, ii);
+    const int r = item / njt;
+    const int j = (item - r * njt) * 16 + li;
+    if (j < N2) {
+#pragma unroll
+      for (int it = 0; it < NRT; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int io = it * 16 + 4 * lk + e;  // result element e of lane l: row 4 (l/16) + e
+          if (io < N1) sX[xt_pos(r * K + io * N2 + j)] = o[ii][it][e];
         }
     }
   }
@@ -590,36 +645,35 @@ template <int N1, int N2, bool BFS, int NT>
 __device__ __forceinline__ void stage_factors_once(const float* __restrict__ P1, const float* __restrict__ P2,
                                                    float* sP1, unsigned char* p2, int t) {
   using S = XStrides<N1, N2>;
-  constexpr int U1 = (N1 * N1 + NT - 1) / NT;
+  constexpr int U1 = BFS ? 1 : (N1 * N1 + NT - 1) / NT;
   float v1[U1];
+  if constexpr (!BFS) {
 #pragma unroll
-  for (int u = 0; u < U1; ++u) {
-    const int idx = t + u * NT;
-    v1[u] = idx < N1 * N1 ? P1[idx] : 0.0f;
+    for (int u = 0; u < U1; ++u) {
+      const int idx = t + u * NT;
+      v1[u] = idx < N1 * N1 ? P1[idx] : 0.0f;
+    }
   }
   if constexpr (BFS) {
     using L = BfLayout<N2>;
-    constexpr int NP = L::jp * (L::kb / 2);  // (pair of K rows b, b + 1; column j)
+    constexpr int NP = N2 * (L::kb / 2);  // (pair of K rows b, b + 1; column j < n2)
     constexpr int U2 = (NP + NT - 1) / NT;
     float v2[U2][2];
 #pragma unroll
     for (int u = 0; u < U2; ++u) {
       const int idx = t + u * NT;
-      const int b = 2 * (idx / L::jp), j = idx % L::jp;
-      v2[u][0] = (idx < NP && b < N2 && j < N2) ? P2[b * N2 + j] : 0.0f;
-      v2[u][1] = (idx < NP && b + 1 < N2 && j < N2) ? P2[(b + 1) * N2 + j] : 0.0f;
+      const int b = 2 * (idx / N2), j = idx % N2;
+      v2[u][0] = (idx < NP && b < N2) ? P2[b * N2 + j] : 0.0f;
+      v2[u][1] = (idx < NP && b + 1 < N2) ? P2[(b + 1) * N2 + j] : 0.0f;
     }
-#pragma unroll
-    for (int u = 0; u < U1; ++u) {
-      const int idx = t + u * NT;
-      if (idx < N1 * N1) sP1[(idx / N1) * S::sp1 + idx % N1] = v1[u];
-    }
+    // P1 as its bf16 planes (loads issued behind P2's, one round trip for both)
+    stage_p1_planes<N1, NT>(P1, reinterpret_cast<uint16_t*>(sP1), t);
     uint32_t* d = reinterpret_cast<uint32_t*>(p2);
 #pragma unroll
     for (int u = 0; u < U2; ++u) {
       const int idx = t + u * NT;
       if (idx < NP) {
-        const int b = 2 * (idx / L::jp), j = idx % L::jp;
+        const int b = 2 * (idx / N2), j = idx % N2;
         uint32_t h0, m0, l0, h1, m1, l1;
         split3_bf16(v2[u][0], &h0, &m0, &l0);
         split3_bf16(v2[u][1], &h1, &m1, &l1);
@@ -870,12 +924,23 @@ __global__ __launch_bounds__(WS ? 512 : 256, WS ? 1 : xform_min_blocks(NRT, N1, 
           }
         }
         __syncthreads();  // stage 1 done with X; the quantizer done with the x~ rows
-        switch (nmine) {
-          case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
-          case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
-          case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
-          case 1: stage2<NRT, N1, N2, 1, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
-          default: break;
+        if constexpr (BFS) {
+          const uint16_t* sP1b = reinterpret_cast<const uint16_t*>(lds);
+          switch (nmine) {
+            case 4: if constexpr (NIM >= 4) stage2_bf<NRT, N1, N2, 4, NIM, SR>(sP1b, sXt, wave, njt, li, lk, T); break;
+            case 3: if constexpr (NIM >= 3) stage2_bf<NRT, N1, N2, 3, NIM, SR>(sP1b, sXt, wave, njt, li, lk, T); break;
+            case 2: if constexpr (NIM >= 2) stage2_bf<NRT, N1, N2, 2, NIM, SR>(sP1b, sXt, wave, njt, li, lk, T); break;
+            case 1: stage2_bf<NRT, N1, N2, 1, NIM, SR>(sP1b, sXt, wave, njt, li, lk, T); break;
+            default: break;
+          }
+        } else {
+          switch (nmine) {
+            case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
+            case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
+            case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
+            case 1: stage2<NRT, N1, N2, 1, NIM, SR>(a, sP1, sXt, wave, njt, li, lk, T); break;
+            default: break;
+          }
         }
         __syncthreads();  // x~ of chunk c and X of chunk c + G are in place
       }
@@ -967,12 +1032,23 @@ __global__ __launch_bounds__(WS ? 512 : 256, WS ? 1 : xform_min_blocks(NRT, N1, 
       __syncthreads();  // every X read is done; x~ may now overwrite the region
 
       // ---- stage 2: x~[i][j] = sum_a P1[a][i] T[a][j]
-      switch (nmine) {
-        case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
-        case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
-        case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
-        case 1: stage2<NRT, N1, N2, 1, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
-        default: break;
+      if constexpr (BFS) {
+        const uint16_t* sP1b = reinterpret_cast<const uint16_t*>(lds);
+        switch (nmine) {
+          case 4: if constexpr (NIM >= 4) stage2_bf<NRT, N1, N2, 4, NIM, SR>(sP1b, sX, wave, njt, li, lk, T); break;
+          case 3: if constexpr (NIM >= 3) stage2_bf<NRT, N1, N2, 3, NIM, SR>(sP1b, sX, wave, njt, li, lk, T); break;
+          case 2: if constexpr (NIM >= 2) stage2_bf<NRT, N1, N2, 2, NIM, SR>(sP1b, sX, wave, njt, li, lk, T); break;
+          case 1: stage2_bf<NRT, N1, N2, 1, NIM, SR>(sP1b, sX, wave, njt, li, lk, T); break;
+          default: break;
+        }
+      } else {
+        switch (nmine) {
+          case 4: if constexpr (NIM >= 4) stage2<NRT, N1, N2, 4, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+          case 3: if constexpr (NIM >= 3) stage2<NRT, N1, N2, 3, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+          case 2: if constexpr (NIM >= 2) stage2<NRT, N1, N2, 2, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+          case 1: stage2<NRT, N1, N2, 1, NIM, SR>(a, sP1, sX, wave, njt, li, lk, T); break;
+          default: break;
+        }
       }
       __syncthreads();
 
@@ -1018,7 +1094,9 @@ int x_bytes_for(int R, int n1, int sx, int K) {
 
 // host copies of BfLayout<n2> (the bf16 stage-1 layouts)
 int bf_sb(int n2) { return (n2 + 31) / 32 * 32 + 8; }
-int bf_p2_bytes(int n2) { return 3 * ((n2 + 15) / 16 * 16) * bf_sb(n2) * 2; }
+int bf_p2_bytes(int n2) { return 3 * n2 * bf_sb(n2) * 2; }
+// host copy of P1Layout<n1>::bytes (the bf16 stage-2 planes of P1)
+int bf_p1_bytes(int n1) { return 3 * ((n1 + 15) / 16 * 16) * ((n1 + 31) / 32 * 32 + 8) * 2; }
 
 
 // LDS plan of the fused transform kernel: P1 and P2 with strides that put the
@@ -1057,8 +1135,9 @@ bool plan_quant(QuantArgs& a) {
     return bfs && xbb > xb ? xbb : xb;
   };
   // + 256 bytes of per-row absmax partials (16 rows x 4 waves) after X
+  auto p1_bytes = [&](int sp1) { return bfs ? bf_p1_bytes(a.n1) : a.n1 * sp1 * 4; };
   auto lds_for = [&](int sp1, int sp2, int sx, int r) {
-    const int p2 = (a.n1 * sp1 * 4 + 15) / 16 * 16;
+    const int p2 = (p1_bytes(sp1) + 15) / 16 * 16;
     const int px = (p2 + p2_bytes(sp2) + 15) / 16 * 16;
     return px + xb_for(sx, r) + kRowMaxBytes;
   };
@@ -1086,7 +1165,7 @@ bool plan_quant(QuantArgs& a) {
   a.sx = sx;
   a.st = 0;
   a.R = R;
-  a.off_p2 = (a.n1 * sp1 * 4 + 15) / 16 * 16;
+  a.off_p2 = (p1_bytes(sp1) + 15) / 16 * 16;
   a.off_x = (a.off_p2 + p2_bytes(sp2) + 15) / 16 * 16;
   a.off_t = 0;
   a.off_rmax = a.off_x + xb_for(sx, R);

@@ -130,11 +130,12 @@ __device__ __forceinline__ void mfma_settle_before_join() {
 // and a plane value is exact in fp32; only the fp32 accumulation rounds, as
 // on the fp32 MFMA, so x~ keeps the fp32-class bound.
 //
-// LDS layouts (bf16 elements): P2 planes transposed, plane p, column j, K
-// index b at p * plane + j * sb + b; X rows i of the n1 x n2 grid at i * sb,
-// K index b.  Entries outside the n2 x n2 factor and the n2 columns of X are
-// zero.  The row stride sb = kb + 8 puts the 16 rows one 16-byte read per
-// lane touches on distinct LDS banks.
+// LDS layouts (bf16 elements): P2 planes transposed, plane p, column j < n2,
+// K index b at p * plane + j * sb + b; X rows i of the n1 x n2 grid at i * sb,
+// K index b.  K indices b >= n2 of P2 and of X are zero.  A column tile that
+// runs past n2 reads column n2 - 1 in place of the missing ones (those
+// columns of T are never used).  The row stride sb = kb + 8 puts the 16 rows
+// one 16-byte read per lane touches on distinct LDS banks.
 // ---------------------------------------------------------------------------
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -144,7 +145,7 @@ struct BfLayout {
   static constexpr int kb = (N2 + 31) / 32 * 32;  // K extent, in steps of 32
   static constexpr int jp = (N2 + 15) / 16 * 16;  // column extent, in tiles of 16
   static constexpr int sb = kb + 8;               // row stride (elements)
-  static constexpr int plane = jp * sb;           // elements per plane (all columns)
+  static constexpr int plane = N2 * sb;           // elements per plane (columns j < n2)
   static constexpr int p2_bytes = 3 * plane * 2;
 };
 
@@ -161,9 +162,9 @@ __device__ __forceinline__ void split3_bf16(float v, uint32_t* h, uint32_t* m, u
 
 // NI items of T = X * P2, each one 16-column tile of T over NRT consecutive
 // 16-row tiles starting at tile rt0[ii].  Item ii reads the X grid whose row
-// i is at xgrid[ii] + i * sb (rows >= N1 read as zero) and the planes of its
-// columns starting at pcol[ii] (plane p at + p * plane, column li of the tile
-// at + li * sb).  Lane l takes A row l % 16, B column l % 16 and K slots
+// i is at xgrid[ii] + i * sb (rows >= N1 read as zero) and the planes of the
+// lane's column at pcol[ii] (plane p at + p * plane; the caller points lanes
+// past n2 at column n2 - 1).  Lane l takes A row l % 16, B column l % 16 and K slots
 // 8 (l / 16) .. + 7 of each step of 32; result element e of lane l is T row
 // 16 (rt0 + q) + 4 (l / 16) + e, column l % 16 (the fp32 MFMA's layout).
 // Every tile accumulates in the same order (K steps, then planes hi, mid,
@@ -183,7 +184,7 @@ __device__ __forceinline__ void stage1_bf16(const uint16_t* const (&xgrid)[NI], 
     for (int ii = 0; ii < NI; ++ii) {
 #pragma unroll
       for (int p = 0; p < 3; ++p)
-        b[ii][p] = *reinterpret_cast<const v4u*>(pcol[ii] + p * plane + li * L::sb + 32 * ks + 8 * lk);
+        b[ii][p] = *reinterpret_cast<const v4u*>(pcol[ii] + p * plane + 32 * ks + 8 * lk);
     }
 #pragma unroll
     for (int ia = 0; ia < NA; ++ia) {
@@ -202,6 +203,107 @@ __device__ __forceinline__ void stage1_bf16(const uint16_t* const (&xgrid)[NI], 
         for (int q = 0; q < NRT; ++q)
           T[ii][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[SA ? 0 : ii][q]),
                                                            __builtin_bit_cast(v8bf, b[ii][p]), T[ii][q], 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2 of the transform on the bf16 MFMA, for bf16 inputs: x~ = P1^T * T,
+// with T (the fp32 stage-1 result) and P1 each split into three exact bf16
+// planes (split3_bf16), and the six plane products of order <= 2 taken (hi,
+// mid, lo = 0, 1, 2; the three dropped ones are below 2^-20 of |P1| |T|).
+// Per 16x16 tile of x~ and step q of 32 reduction indices the six MFMAs run
+// in one fixed order, smallest first: (P1 lo, T hi), (mid, mid), (hi, lo),
+// (mid, hi), (hi, mid), (hi, hi); every kernel takes the steps in order, so a
+// tile's value does not depend on which kernel or wave forms it.
+//
+// Reduction order.  The fp32 stage-1 result gives lane l the T rows
+// 16 rt + 4 (l / 16) + e in element e of tile rt; step q of the bf16 MFMA
+// wants 8 consecutive K slots 8 (l / 16) .. + 7 per lane.  Slot 8 g + 4 h + e
+// of step q takes T row a = 32 q + 16 h + 4 g + e, so a lane's slots are
+// tile 2q's elements then tile 2q + 1's, straight from its registers; the P1
+// planes are stored with their reduction index in the same order.
+//
+// P1 plane layout (bf16): plane p, output row i < 16 NRT, slot a' at
+// p * plane + i * sb + a' (a' = slot of row a; zeros for a, i >= n1).
+// ---------------------------------------------------------------------------
+template <int N1>
+struct P1Layout {
+  static constexpr int rows = (N1 + 15) / 16 * 16;  // output rows, in tiles of 16
+  static constexpr int ka = (N1 + 31) / 32 * 32;    // reduction extent, in steps of 32
+  static constexpr int sb = ka + 8;                 // row stride (elements): spreads the banks
+  static constexpr int plane = rows * sb;
+  static constexpr int bytes = 3 * plane * 2;
+};
+// slot of reduction index a, and back
+__host__ __device__ constexpr int p1_slot(int a) {
+  return (a & ~31) | (((a >> 2) & 3) << 3) | (((a >> 4) & 1) << 2) | (a & 3);
+}
+__host__ __device__ constexpr int p1_row_of_slot(int s) {
+  return (s & ~31) | (((s >> 2) & 1) << 4) | (((s >> 3) & 3) << 2) | (s & 3);
+}
+
+// the three bf16 planes of 8 fp32 values, packed two per register
+__device__ __forceinline__ void planes8(const float (&v)[8], v4u (&b)[3]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3_bf16(v[2 * k], &h0, &m0, &l0);
+    split3_bf16(v[2 * k + 1], &h1, &m1, &l1);
+    b[0][k] = h0 | (h1 << 16);
+    b[1][k] = m0 | (m1 << 16);
+    b[2][k] = l0 | (l1 << 16);
+  }
+}
+
+// A operands of tile it, step q (lane's row 16 it + li, slots 32 q + 8 lk ..)
+template <int N1>
+__device__ __forceinline__ void p1_planes_at(const uint16_t* sP1b, int it, int q, int li, int lk, v4u (&a)[3]) {
+  using L = P1Layout<N1>;
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    a[p] = *reinterpret_cast<const v4u*>(sP1b + p * L::plane + (it * 16 + li) * L::sb + 32 * q + 8 * lk);
+}
+
+// Product k = 0..5 of a tile and step multiplies P1 plane s2_pa(k) by T plane
+// s2_pb(k): (2,0), (1,1), (0,2), (1,0), (0,1), (0,0).  Callers run k outermost
+// across their independent tiles, so every tile takes the same sequence.
+__host__ __device__ constexpr int s2_pa(int k) { return k == 0 ? 2 : (k == 1 || k == 3) ? 1 : 0; }
+__host__ __device__ constexpr int s2_pb(int k) { return k == 0 ? 0 : (k == 1 || k == 4) ? 1 : k == 2 ? 2 : 0; }
+__device__ __forceinline__ v4f s2_mm(const v4u& a, const v4u& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// The P1 planes from fp32 P1 ([n1][n1], row a, column i) in global memory,
+// threads t, t + NT, ...: two slots (a pair of consecutive reduction rows)
+// per 32-bit store and plane; loads first.
+template <int N1, int NT>
+__device__ __forceinline__ void stage_p1_planes(const float* __restrict__ P1, uint16_t* dst, int t) {
+  using L = P1Layout<N1>;
+  constexpr int NP = L::rows * (L::ka / 2);
+  constexpr int U = (NP + NT - 1) / NT;
+  float v[U][2];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int idx = t + u * NT;
+    const int i = idx / (L::ka / 2), s = 2 * (idx - i * (L::ka / 2));
+    const int a = p1_row_of_slot(s);
+    v[u][0] = (idx < NP && i < N1 && a < N1) ? P1[a * N1 + i] : 0.0f;
+    v[u][1] = (idx < NP && i < N1 && a + 1 < N1) ? P1[(a + 1) * N1 + i] : 0.0f;
+  }
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int idx = t + u * NT;
+    if (idx < NP) {
+      const int i = idx / (L::ka / 2), s = 2 * (idx - i * (L::ka / 2));
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3_bf16(v[u][0], &h0, &m0, &l0);
+      split3_bf16(v[u][1], &h1, &m1, &l1);
+      const int o = (i * L::sb + s) >> 1;  // sb and s are even
+      d[o] = h0 | (h1 << 16);
+      d[o + L::plane / 2] = m0 | (m1 << 16);
+      d[o + L::plane] = l0 | (l1 << 16);
+    }
   }
 }
 
