@@ -12,25 +12,27 @@
 // "Protocol").
 //
 // With a handful of rows the call is bound by streaming the packed INT4
-// weights once and by latency.  Each work-group owns one block of 32 output
+// weights once and by latency.  Each work-group owns one block of CPW output
 // columns over all of K and needs no other work-group: it issues the loads of
-// its first weight slice (64 groups) into registers, forms the rows' codes
-// while they arrive, then dots, with the next slice's loads in flight.
+// its first weight slice into registers, forms the rows' codes while they
+// arrive, then dots, with the next slice's loads in flight.
 //   * Transform instances compute x~ of every row themselves (the same
 //     operands and MFMA order as the chunked transform kernel, so the same x~
 //     bit for bit), quantize each row into LDS with the quantizer the other
 //     kernels use, and keep all rows' codes in LDS.  Every work-group repeats
-//     the transform; the host takes this form only while that costs about as
-//     much as the weight fetch it overlaps.
+//     the transform, so its latency is the call's: these instances run 8
+//     waves (4 for K = 6912), which split the factor staging, the MFMA tiles
+//     and the quantizer between them; the host takes this form only while the
+//     transform costs about as much as the weight fetch it overlaps.
 //   * Other instances quantize x (no transform) or copy canonical codes for
 //     all rows and all of K into LDS (one weight slice at a time if that does
 //     not fit), with every thread's loads of the next round in flight while
 //     it quantizes the current one.
-// Group dots: thread (column c, lane group gq) takes groups gq, gq + 8, ...
+// Group dots: thread (column c, lane group gq) takes groups gq, gq + GL, ...
 // of each slice, unpacks the column's 32 nibbles and dots them with every
-// row's codes on V_DOT4_I32_I8 (exact), folding with fl32(s_w * s_a); the
-// eight partial sums of a column are added in a fixed order through LDS, so y
-// is deterministic.
+// row's codes on V_DOT4_I32_I8 (exact), folding with fl32(s_w * s_a); a
+// column's partial sums are added by a butterfly across the lanes of each
+// wave that hold it, then in wave order through LDS, so y is deterministic.
 #include "loopq_internal.h"
 #include "quant_core.h"
 
@@ -42,20 +44,26 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// A work-group owns CPW consecutive output columns (8, 16 or 32, so that a
-// call has about as many work-groups as the chip has CUs) over all of K.
-// Each thread holds 128 bytes of packed weights per slice in flight: in the
-// VALU form thread (column c, lane group gq) takes groups gq + GL i (i < 8)
-// of a slice; in the MFMA form a wave takes groups wave + 4 i of a slice for
-// all 16-column halves of the work-group's columns.
-constexpr int kPer = 8;  // groups of a slice per thread (VALU form)
-template <int CPW>
+// A work-group of NTH threads (NW = NTH / 64 waves) owns CPW consecutive
+// output columns (8, 16 or 32, so that a call has about as many work-groups
+// as the chip has CUs) over all of K.  Each thread holds KP groups of packed
+// weights per slice in flight (at most 8, 128 bytes): in the VALU form thread
+// (column c, lane group gq) takes groups gq + GL i (i < KP) of a slice; in the
+// MFMA form a wave takes groups wave + NW i of a slice for all 16-column
+// halves of the work-group's columns.  Where K is compiled in, KP is the
+// fewest slots that cover K in one slice.
+constexpr int kPer = 8;  // most groups of a slice per thread (VALU form)
+template <int CPW, int NTH = 256, int KP = kPer>
 struct Cols {
-  static constexpr int GL = 256 / CPW;             // lane groups per column (VALU form)
-  static constexpr int kSlice = 2048 / CPW;        // groups per weight slice
+  static constexpr int NW = NTH / 64;                  // waves
+  static constexpr int GL = NTH / CPW;                 // lane groups per column (VALU form)
+  static constexpr int kSlice = KP * GL;               // groups per weight slice
   static constexpr int NH = CPW >= 16 ? CPW / 16 : 1;  // 16-column halves (MFMA form)
-  static constexpr int kMPer = kSlice / 4;         // groups per wave and slice (MFMA form)
+  static constexpr int kMPer = kSlice / NW;            // groups per wave and slice (MFMA form)
+  static_assert(kSlice % NW == 0, "a slice splits evenly over the waves");
 };
+// slots per thread for a compiled-in K of ga groups
+constexpr int slots_for(int ga, int gl) { return (ga + gl - 1) / gl < kPer ? (ga + gl - 1) / gl : kPer; }
 constexpr int kLdsBudget = 160 * 1024;
 
 struct DecodeArgs {
@@ -85,17 +93,18 @@ struct DecodeArgs {
 // of group j0 + gi of row m at sA + m * a_ld + gi * 32, its step at
 // sS[m * s_ld + gi]), written to the canonical output.  Every work-group holds
 // the same codes, so the work-groups share the writes out between them.
+template <int NTH>
 __device__ __forceinline__ void dump_codes(const DecodeArgs& g, int j0, int G, const int8_t* sA, int a_ld,
                                            const float* sS, int s_ld) {
   const int K = g.K, Ga = K >> 5;
-  const int stride = (int)gridDim.x * 256;
+  const int stride = (int)gridDim.x * NTH;
   const int n16 = g.R * G * 2;  // 16-code pieces
-  for (int q = (int)blockIdx.x * 256 + (int)threadIdx.x; q < n16; q += stride) {
+  for (int q = (int)blockIdx.x * NTH + (int)threadIdx.x; q < n16; q += stride) {
     const int m = q / (2 * G), rem = q - m * 2 * G;
     *reinterpret_cast<uint4*>(g.codes_out + (int64_t)m * K + (j0 + (rem >> 1)) * 32 + (rem & 1) * 16) =
         *reinterpret_cast<const uint4*>(sA + m * a_ld + (rem >> 1) * 32 + (rem & 1) * 16);
   }
-  for (int q = (int)blockIdx.x * 256 + (int)threadIdx.x; q < g.R * G; q += stride) {
+  for (int q = (int)blockIdx.x * NTH + (int)threadIdx.x; q < g.R * G; q += stride) {
     const int m = q / G;
     g.steps_out[(int64_t)m * Ga + j0 + (q - m * G)] = sS[m * s_ld + q - m * G];
   }
@@ -112,23 +121,24 @@ __device__ __forceinline__ v4i unpack16(uint2 p) {
 }
 
 // The weights of one slice held by one thread: groups sl * kSlice + gq + GL i.
+template <int KP>
 struct WSlice {
-  uint2 lo[kPer], hi[kPer];
-  float s[kPer];
+  uint2 lo[KP], hi[KP];
+  float s[KP];
 };
 
 // Load a thread's part of slice `sl`; groups past Ga re-read group Ga - 1
 // and are not used.
-template <int CPW, int MODE>
+template <int CPW, int MODE, int NTH, int KP>
 __device__ __forceinline__ void load_slice(const DecodeArgs& g, int cb, int sl, int c, int gq,
-                                           WSlice& ws) {
-  using C = Cols<CPW>;
+                                           WSlice<KP>& ws) {
+  using C = Cols<CPW, NTH, KP>;
   const int Ga = g.K >> 5;
   const int Gw = (Ga + (1 << g.gshift) - 1) >> g.gshift;
   const int n = cb * CPW + c;  // padded column: block n / 32, column n % 32 of it
   const int nb = n >> 5, cc = n & 31;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < KP; ++i) {
     const int j = min(sl * C::kSlice + gq + C::GL * i, Ga - 1);
     const uint8_t* blk = g.w + ((int64_t)nb * Ga + j) * kBlockBytes + cc * 8;
     ws.lo[i] = *reinterpret_cast<const uint2*>(blk);        // K 32 j + 0..15
@@ -140,16 +150,16 @@ __device__ __forceinline__ void load_slice(const DecodeArgs& g, int cb, int sl, 
 // Dots of the thread's groups of slice `sl` that lie in [jlo, jhi) with every
 // row's codes: codes of group j of row m at sA + m * a_ld + (j - a_j0) * 32
 // (bytes), its step at sS[m * s_ld + j - a_j0].
-template <int CPW, int RM, int MODE>
+template <int CPW, int RM, int MODE, int NTH, int KP>
 __device__ __forceinline__ void dot_slice(const DecodeArgs& g, int cb, int sl, int c, int gq,
-                                          const WSlice& ws, int jlo, int jhi, const int8_t* sA,
+                                          const WSlice<KP>& ws, int jlo, int jhi, const int8_t* sA,
                                           int a_ld, int a_j0, const float* sS, int s_ld,
                                           float (&acc)[RM]) {
-  using C = Cols<CPW>;
+  using C = Cols<CPW, NTH, KP>;
   const int Ga = g.K >> 5;
   const int n = cb * CPW + c;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < KP; ++i) {
     const int j = sl * C::kSlice + gq + C::GL * i;
     if (j >= jlo && j < jhi && j < Ga) {
       const v4i w0 = unpack16(ws.lo[i]);
@@ -185,24 +195,25 @@ __device__ __forceinline__ void dot_slice(const DecodeArgs& g, int cb, int sl, i
 // the block; its nibbles for one (half, group) are one dword of the packed
 // layout (K-half (l / 16) / 2, run (l / 16) % 2).
 
-// The weights of one slice held by one lane: groups sl * kSlice + wave + 4 i,
+// The weights of one slice held by one lane: groups sl * kSlice + wave + NW i,
 // for each 16-column half of the work-group's columns.
-template <int CPW>
+template <int CPW, int NTH, int KP>
 struct MSlice {
-  uint32_t w[Cols<CPW>::kMPer][Cols<CPW>::NH];  // packed nibbles, [group][column half]
-  float s[Cols<CPW>::kMPer][Cols<CPW>::NH];     // fp16 steps of the lane's column
+  using C = Cols<CPW, NTH, KP>;
+  uint32_t w[C::kMPer][C::NH];  // packed nibbles, [group][column half]
+  float s[C::kMPer][C::NH];     // fp16 steps of the lane's column
 };
 
-template <int CPW, int MODE>
-__device__ __forceinline__ void load_mslice(const DecodeArgs& g, int cb, int sl, MSlice<CPW>& ms) {
-  using C = Cols<CPW>;
+template <int CPW, int MODE, int NTH, int KP>
+__device__ __forceinline__ void load_mslice(const DecodeArgs& g, int cb, int sl, MSlice<CPW, NTH, KP>& ms) {
+  using C = Cols<CPW, NTH, KP>;
   const int Ga = g.K >> 5;
   const int Gw = (Ga + (1 << g.gshift) - 1) >> g.gshift;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4;
 #pragma unroll
   for (int i = 0; i < C::kMPer; ++i) {
-    const int j = min(sl * C::kSlice + wave + 4 * i, Ga - 1);  // past Ga: re-read, unused
+    const int j = min(sl * C::kSlice + wave + C::NW * i, Ga - 1);  // past Ga: re-read, unused
 #pragma unroll
     for (int tt = 0; tt < C::NH; ++tt) {
       const int n = cb * CPW + tt * 16 + (lane & 15);
@@ -225,11 +236,11 @@ __device__ __forceinline__ long unpack8(uint32_t p) {
 // Dots of the wave's groups of slice `sl` lying in [jlo, jhi), codes and
 // steps addressed as in dot_slice; acc[half][e] is row 4 (l / 16) + e of
 // column half * 16 + l % 16.
-template <int CPW, int MODE>
-__device__ __forceinline__ void mfma_slice(const DecodeArgs& g, int cb, int sl, const MSlice<CPW>& ms, int jlo,
-                                           int jhi, const int8_t* sA, int a_ld, int a_j0, const float* sS,
-                                           int s_ld, float (&acc)[Cols<CPW>::NH][4]) {
-  using C = Cols<CPW>;
+template <int CPW, int MODE, int NTH, int KP>
+__device__ __forceinline__ void mfma_slice(const DecodeArgs& g, int cb, int sl, const MSlice<CPW, NTH, KP>& ms,
+                                           int jlo, int jhi, const int8_t* sA, int a_ld, int a_j0,
+                                           const float* sS, int s_ld, float (&acc)[Cols<CPW>::NH][4]) {
+  using C = Cols<CPW, NTH, KP>;
   typedef int v4i_t __attribute__((ext_vector_type(4)));
   const int Ga = g.K >> 5;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -238,7 +249,7 @@ __device__ __forceinline__ void mfma_slice(const DecodeArgs& g, int cb, int sl, 
   const int rac = min(ra, g.R - 1);   // rows past R read row R - 1, then zeroed
 #pragma unroll
   for (int i = 0; i < C::kMPer; ++i) {
-    const int j = sl * C::kSlice + wave + 4 * i;
+    const int j = sl * C::kSlice + wave + C::NW * i;
     if (j >= jlo && j < jhi && j < Ga) {  // wave-uniform
       long a = *reinterpret_cast<const long*>(sA + rac * a_ld + (j - a_j0) * 32 + q * 8);
       if (ra >= g.R) a = 0;
@@ -270,24 +281,24 @@ __device__ __forceinline__ void mfma_slice(const DecodeArgs& g, int cb, int sl, 
 // Copy an NN x NN fp32 matrix into LDS rows of stride SP.  All of a
 // thread's loads are issued before any store, so the copy costs one memory
 // round trip rather than one per element.
-template <int NN>
+template <int NN, int NTH = 256>
 struct MatRegs {
-  static constexpr int T = (NN * NN + 255) / 256;
+  static constexpr int T = (NN * NN + NTH - 1) / NTH;
   float v[T];
 };
-template <int NN>
-__device__ __forceinline__ void stage_matrix_issue(const float* __restrict__ src, MatRegs<NN>& m) {
+template <int NN, int NTH>
+__device__ __forceinline__ void stage_matrix_issue(const float* __restrict__ src, MatRegs<NN, NTH>& m) {
 #pragma unroll
-  for (int i = 0; i < MatRegs<NN>::T; ++i) {
-    const int idx = threadIdx.x + 256 * i;
+  for (int i = 0; i < MatRegs<NN, NTH>::T; ++i) {
+    const int idx = threadIdx.x + NTH * i;
     m.v[i] = idx < NN * NN ? src[idx] : 0.0f;
   }
 }
-template <int NN, int SP>
-__device__ __forceinline__ void stage_matrix_commit(const MatRegs<NN>& m, float* dst) {
+template <int NN, int SP, int NTH>
+__device__ __forceinline__ void stage_matrix_commit(const MatRegs<NN, NTH>& m, float* dst) {
 #pragma unroll
-  for (int i = 0; i < MatRegs<NN>::T; ++i) {
-    const int idx = threadIdx.x + 256 * i;
+  for (int i = 0; i < MatRegs<NN, NTH>::T; ++i) {
+    const int idx = threadIdx.x + NTH * i;
     if (idx < NN * NN) dst[(idx / NN) * SP + idx % NN] = m.v[i];
   }
 }
@@ -301,16 +312,16 @@ __device__ __forceinline__ void stage_matrix(const float* __restrict__ src, floa
 // Row r of x (K elements, bf16 or fp32) held in registers between the issue
 // of its loads and their commit to LDS: bf16 in .x .y of each entry, fp32 in
 // all four.
-template <int K>
+template <int K, int NTH = 256>
 struct RowRegs {
-  static constexpr int T = (K / 4 + 255) / 256;
+  static constexpr int T = (K / 4 + NTH - 1) / NTH;
   uint4 v[T];
 };
-template <int K>
-__device__ __forceinline__ void x_row_issue(const DecodeArgs& g, int r, RowRegs<K>& x) {
+template <int K, int NTH>
+__device__ __forceinline__ void x_row_issue(const DecodeArgs& g, int r, RowRegs<K, NTH>& x) {
 #pragma unroll
-  for (int i = 0; i < RowRegs<K>::T; ++i) {
-    const int q = threadIdx.x + 256 * i;
+  for (int i = 0; i < RowRegs<K, NTH>::T; ++i) {
+    const int q = threadIdx.x + NTH * i;
     if (q < K / 4) {
       if (g.bf16) {
         const uint2 u = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.x) + (int64_t)r * K)[q];
@@ -321,11 +332,11 @@ __device__ __forceinline__ void x_row_issue(const DecodeArgs& g, int r, RowRegs<
     }
   }
 }
-template <int K, int N2, int SX>
-__device__ __forceinline__ void x_row_commit(const DecodeArgs& g, const RowRegs<K>& x, float* sX) {
+template <int K, int N2, int SX, int NTH>
+__device__ __forceinline__ void x_row_commit(const DecodeArgs& g, const RowRegs<K, NTH>& x, float* sX) {
 #pragma unroll
-  for (int i = 0; i < RowRegs<K>::T; ++i) {
-    const int q = threadIdx.x + 256 * i;
+  for (int i = 0; i < RowRegs<K, NTH>::T; ++i) {
+    const int q = threadIdx.x + NTH * i;
     if (q < K / 4) {
       const int k = q * 4;
       float* dst = sX + (k / N2) * SX + k % N2;
@@ -346,9 +357,9 @@ __device__ __forceinline__ void x_row_commit(const DecodeArgs& g, const RowRegs<
 
 // Row r of x (K elements, bf16 or fp32) into LDS as the n1 x n2 grid with
 // row stride SX, loads first as above.
-template <int K, int N2, int SX>
+template <int K, int N2, int SX, int NTH = 256>
 __device__ __forceinline__ void stage_x_row(const DecodeArgs& g, int r, float* sX) {
-  constexpr int T = (K / 4 + 255) / 256;
+  constexpr int T = (K / 4 + NTH - 1) / NTH;
   auto put = [&](int q, const float4& v) {
     const int k = q * 4;
     float* dst = sX + (k / N2) * SX + k % N2;
@@ -359,12 +370,12 @@ __device__ __forceinline__ void stage_x_row(const DecodeArgs& g, int r, float* s
     uint2 u[T];
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      const int q = threadIdx.x + 256 * i;
+      const int q = threadIdx.x + NTH * i;
       u[i] = q < K / 4 ? src[q] : uint2{0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      const int q = threadIdx.x + 256 * i;
+      const int q = threadIdx.x + NTH * i;
       if (q < K / 4)
         put(q, float4{bf16_bits_to_float(u[i].x & 0xffffu), bf16_bits_to_float(u[i].x >> 16),
                       bf16_bits_to_float(u[i].y & 0xffffu), bf16_bits_to_float(u[i].y >> 16)});
@@ -374,12 +385,12 @@ __device__ __forceinline__ void stage_x_row(const DecodeArgs& g, int r, float* s
     float4 v[T];
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      const int q = threadIdx.x + 256 * i;
+      const int q = threadIdx.x + NTH * i;
       v[i] = q < K / 4 ? src[q] : float4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      const int q = threadIdx.x + 256 * i;
+      const int q = threadIdx.x + NTH * i;
       if (q < K / 4) put(q, v[i]);
     }
   }
@@ -407,7 +418,7 @@ struct XPlan {
   static constexpr int off_t = off_x + (x_bytes + 15) / 16 * 16;
   static constexpr int off_codes = off_t + N1 * st * 4;
   static constexpr int codes_bytes(int R) { return (R * K + 15) / 16 * 16; }
-  static constexpr int lds(int R, int RM) { return off_codes + codes_bytes(R) + R * (K / 32) * 4 + 8 * RM * 32 * 4; }
+  static constexpr int lds(int R, int RM, int nth) { return off_codes + codes_bytes(R) + R * (K / 32) * 4 + nth * RM * 4; }
 };
 
 // ---- transform work items (rows the one-launch form does not take): one
@@ -434,12 +445,12 @@ struct ItemPlan {
 // The P2 registers of stage_matrix_issue committed as the three bf16 planes
 // (transposed, zeros outside the factor), and the bf16 X row registers of
 // x_row_issue as the bf16 grid (K columns n2 .. kb - 1 zeroed).
-template <int N2>
-__device__ __forceinline__ void p2_planes_commit(const MatRegs<N2>& m, uint16_t* dst) {
+template <int N2, int NTH>
+__device__ __forceinline__ void p2_planes_commit(const MatRegs<N2, NTH>& m, uint16_t* dst) {
   using L = BfLayout<N2>;
 #pragma unroll
-  for (int i = 0; i < MatRegs<N2>::T; ++i) {
-    const int idx = threadIdx.x + 256 * i;  // element b * N2 + j of P2
+  for (int i = 0; i < MatRegs<N2, NTH>::T; ++i) {
+    const int idx = threadIdx.x + NTH * i;  // element b * N2 + j of P2
     if (idx < N2 * N2) {
       const int b = idx / N2, j = idx - b * N2;
       uint32_t h, mm, l;
@@ -452,7 +463,7 @@ __device__ __forceinline__ void p2_planes_commit(const MatRegs<N2>& m, uint16_t*
   // zeros: K indices b >= N2 of every column (none when N2 % 32 == 0)
   constexpr int w = L::kb - N2 > 0 ? L::kb - N2 : 1;
   constexpr int padb = N2 * (L::kb - N2);
-  for (int idx = threadIdx.x; idx < padb; idx += 256) {
+  for (int idx = threadIdx.x; idx < padb; idx += NTH) {
     const int j = idx / w, b = N2 + idx % w;
 #pragma unroll
     for (int p = 0; p < 3; ++p) dst[p * L::plane + j * L::sb + b] = 0;
@@ -461,12 +472,12 @@ __device__ __forceinline__ void p2_planes_commit(const MatRegs<N2>& m, uint16_t*
 // The P1 registers of stage_matrix_issue committed as the bf16 stage-2 planes
 // (P1Layout): element (a, i) to row i, slot p1_slot(a); zeros at the rows i
 // and slots of reduction rows a past n1 (positions no element writes).
-template <int N1>
-__device__ __forceinline__ void p1_planes_commit(const MatRegs<N1>& m, uint16_t* dst) {
+template <int N1, int NTH>
+__device__ __forceinline__ void p1_planes_commit(const MatRegs<N1, NTH>& m, uint16_t* dst) {
   using L = P1Layout<N1>;
 #pragma unroll
-  for (int u = 0; u < MatRegs<N1>::T; ++u) {
-    const int idx = threadIdx.x + 256 * u;  // element a * N1 + i of P1
+  for (int u = 0; u < MatRegs<N1, NTH>::T; ++u) {
+    const int idx = threadIdx.x + NTH * u;  // element a * N1 + i of P1
     if (idx < N1 * N1) {
       const int a = idx / N1, i = idx - a * N1;
       uint32_t h, mm, l;
@@ -477,7 +488,7 @@ __device__ __forceinline__ void p1_planes_commit(const MatRegs<N1>& m, uint16_t*
       dst[2 * L::plane + o] = (uint16_t)l;
     }
   }
-  for (int idx = threadIdx.x; idx < L::rows * L::ka; idx += 256) {
+  for (int idx = threadIdx.x; idx < L::rows * L::ka; idx += NTH) {
     const int i = idx / L::ka, sl = idx - i * L::ka;
     if (i >= N1 || p1_row_of_slot(sl) >= N1) {
 #pragma unroll
@@ -486,43 +497,43 @@ __device__ __forceinline__ void p1_planes_commit(const MatRegs<N1>& m, uint16_t*
   }
 }
 
-template <int N1, int N2>
-__device__ __forceinline__ void x_row_commit_bf(const RowRegs<N1 * N2>& x, uint16_t* sXb) {
+template <int N1, int N2, int NTH>
+__device__ __forceinline__ void x_row_commit_bf(const RowRegs<N1 * N2, NTH>& x, uint16_t* sXb) {
   using L = BfLayout<N2>;
   constexpr int K = N1 * N2;
 #pragma unroll
-  for (int i = 0; i < RowRegs<K>::T; ++i) {
-    const int q = threadIdx.x + 256 * i;
+  for (int i = 0; i < RowRegs<K, NTH>::T; ++i) {
+    const int q = threadIdx.x + NTH * i;
     if (q < K / 4) *reinterpret_cast<uint2*>(sXb + (4 * q / N2) * L::sb + (4 * q) % N2) = uint2{x.v[i].x, x.v[i].y};
   }
   if constexpr (L::kb > N2) {
     constexpr int pad = L::kb - N2;
-    for (int idx = threadIdx.x; idx < N1 * pad; idx += 256) sXb[(idx / pad) * L::sb + N2 + idx % pad] = 0;
+    for (int idx = threadIdx.x; idx < N1 * pad; idx += NTH) sXb[(idx / pad) * L::sb + N2 + idx % pad] = 0;
   }
 }
 
 // Row r of bf16 x as the n1 x n2 grid of bf16 rows with stride sb (the bf16
 // stage-1 layout), K columns n2 .. kb - 1 zeroed; loads first.
-template <int N1, int N2>
+template <int N1, int N2, int NTH = 256>
 __device__ __forceinline__ void stage_x_row_bf(const DecodeArgs& g, int r, uint16_t* sXb) {
   using L = BfLayout<N2>;
   constexpr int K = N1 * N2;
-  constexpr int T = (K / 4 + 255) / 256;
+  constexpr int T = (K / 4 + NTH - 1) / NTH;
   const uint2* src = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.x) + (int64_t)r * K);
   uint2 u[T];
 #pragma unroll
   for (int i = 0; i < T; ++i) {
-    const int q = threadIdx.x + 256 * i;
+    const int q = threadIdx.x + NTH * i;
     u[i] = q < K / 4 ? src[q] : uint2{0u, 0u};
   }
 #pragma unroll
   for (int i = 0; i < T; ++i) {
-    const int q = threadIdx.x + 256 * i;
+    const int q = threadIdx.x + NTH * i;
     if (q < K / 4) *reinterpret_cast<uint2*>(sXb + (4 * q / N2) * L::sb + (4 * q) % N2) = u[i];
   }
   if constexpr (L::kb > N2) {
     constexpr int pad = L::kb - N2;
-    for (int idx = threadIdx.x; idx < N1 * pad; idx += 256) sXb[(idx / pad) * L::sb + N2 + idx % pad] = 0;
+    for (int idx = threadIdx.x; idx < N1 * pad; idx += NTH) sXb[(idx / pad) * L::sb + N2 + idx % pad] = 0;
   }
 }
 
@@ -663,7 +674,7 @@ __global__ __launch_bounds__(256) void xform_items_kernel(DecodeArgs g, float* _
 
 // x~ of row r (bitwise the chunked kernel's) into the X region, then its codes
 // and steps into sC / sS.  Ends with a barrier.
-template <int NRT, int N1, int N2>
+template <int NRT, int N1, int N2, int NTH>
 __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsigned char* lds,
                                               int8_t* sC, float* sS, bool staged) {
   using P = XPlan<N1, N2>;
@@ -683,24 +694,25 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
   uint16_t* sXb = reinterpret_cast<uint16_t*>(lds + P::off_x);
   if (!staged) {  // (row 0 is staged with the factors)
     if (g.bf16)
-      stage_x_row_bf<N1, N2>(g, r, sXb);
+      stage_x_row_bf<N1, N2, NTH>(g, r, sXb);
     else
-      stage_x_row<K, N2, P::sx>(g, r, sX);
+      stage_x_row<K, N2, P::sx, NTH>(g, r, sX);
   }
   __syncthreads();
 
   // stage 1: tile (rt, jt) of T = X[16 rt .., :] * P2[:, 16 jt ..], steps of b
-  // in order.  Wave w takes tiles w, w + 4, ... (task t: rt = t % NRT, jt =
+  // in order.  Wave w takes tiles w, w + NW, ... (task t: rt = t % NRT, jt =
   // t / NRT), all at once as independent accumulators; the operands of step
   // s + 1 are read before step s multiplies.
+  constexpr int NW = NTH / 64;
   constexpr int ntask = NRT * P::njt;
-  constexpr int NT = (ntask + 3) / 4;  // tiles per wave
+  constexpr int NT = (ntask + NW - 1) / NW;  // tiles per wave
   int rt[NT], jc[NT];
   bool has[NT];
   uint32_t mrow[NT], mj[NT];
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
-    const int t0 = wave + 4 * u;
+    const int t0 = wave + NW * u;
     has[u] = t0 < ntask;
     const int t = min(t0, ntask - 1);
     rt[u] = t % NRT;
@@ -861,7 +873,7 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
   const float qmaxf = (float)g.qmax;
   const float rq = 1.0f / qmaxf;
   const float clip = g.clips.c[r / g.rows_per_clip];
-  for (int base = 0; base < Ga * 8; base += 256) {
+  for (int base = 0; base < Ga * 8; base += NTH) {
     const int q = base + tid;
     const bool valid = q < Ga * 8;
     const int qc = valid ? q : base;  // keep the group's shuffle partners active
@@ -883,16 +895,16 @@ __device__ __forceinline__ void transform_row(const DecodeArgs& g, int r, unsign
 // kick() runs once, right after the first round of loads is issued (the
 // caller issues its weight loads there, behind the activation loads, so that
 // waiting for these does not wait for the weights).
-template <int MODE, typename Kick>
+template <int MODE, int NTH, typename Kick>
 __device__ __forceinline__ void copy_codes(const DecodeArgs& g, int j0, int G, int8_t* sA, int a_ld,
                                            float* sS, int s_ld, Kick kick) {
   const int K = g.K, Ga = K >> 5;
   const int nch = g.R * G * 2;  // 16-code chunks
-  for (int base = 0; base < nch; base += 256 * 8) {
+  for (int base = 0; base < nch; base += NTH * 8) {
     uint4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int t = base + (int)threadIdx.x + 256 * i;
+      const int t = base + (int)threadIdx.x + NTH * i;
       v[i] = uint4{0u, 0u, 0u, 0u};
       if (t < nch) {
         const int m = t / (2 * G), rem = t - m * 2 * G;
@@ -902,7 +914,7 @@ __device__ __forceinline__ void copy_codes(const DecodeArgs& g, int j0, int G, i
     if (base == 0) kick();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int t = base + (int)threadIdx.x + 256 * i;
+      const int t = base + (int)threadIdx.x + NTH * i;
       if (t < nch) {
         const int m = t / (2 * G), rem = t - m * 2 * G;
         *reinterpret_cast<uint4*>(sA + m * a_ld + (rem >> 1) * 32 + (rem & 1) * 16) = v[i];
@@ -911,11 +923,11 @@ __device__ __forceinline__ void copy_codes(const DecodeArgs& g, int j0, int G, i
   }
   if (MODE == 0) {
     const int ns = g.R * G;
-    for (int base = 0; base < ns; base += 256 * 8) {
+    for (int base = 0; base < ns; base += NTH * 8) {
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int t = base + (int)threadIdx.x + 256 * i;
+        const int t = base + (int)threadIdx.x + NTH * i;
         if (t < ns) {
           const int m = t / G;
           v[i] = g.a_steps[(int64_t)m * Ga + j0 + (t - m * G)];
@@ -923,7 +935,7 @@ __device__ __forceinline__ void copy_codes(const DecodeArgs& g, int j0, int G, i
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int t = base + (int)threadIdx.x + 256 * i;
+        const int t = base + (int)threadIdx.x + NTH * i;
         if (t < ns) {
           const int m = t / G;
           sS[m * s_ld + t - m * G] = v[i];
@@ -936,7 +948,7 @@ __device__ __forceinline__ void copy_codes(const DecodeArgs& g, int j0, int G, i
 // Codes and steps of every row for groups [j0, j0 + G) into LDS: codes of
 // group j0 + gi of row m at sA + m * a_ld + gi * 32, its step at
 // sS[m * s_ld + gi].  Task t = 8 (m G + gi) + l8 covers 4 elements; thread
-// tid takes tasks tid + 256 i, kU per round, and the loads of round q + 1
+// tid takes tasks tid + NTH i, kU per round, and the loads of round q + 1
 // are issued before round q is quantized.  A group's 8 lanes are consecutive
 // and aligned, and R G 8 is a multiple of 8, so a group is wholly valid or
 // wholly past the end (then it quantizes a copy of the round's first task
@@ -945,17 +957,17 @@ constexpr int kU = 4;
 struct CodeRaw {
   uint4 v[kU];  // fp32: 4 elements; bf16: 4 elements in .x .y; codes: .x codes, .y step bits
 };
-template <int MODE, typename Kick>
+template <int MODE, int NTH, typename Kick>
 __device__ __forceinline__ void make_codes(const DecodeArgs& g, int j0, int G, int8_t* sA, int a_ld,
                                            float* sS, int s_ld, Kick kick) {
   const int K = g.K, Ga = K >> 5;
   const int ntask = g.R * G * 8;
-  const int per_round = 256 * kU;
+  const int per_round = NTH * kU;
   const int nround = (ntask + per_round - 1) / per_round;
   const float qmaxf = (float)g.qmax;
   const float rq = 1.0f / qmaxf;
   auto task_of = [&](int q, int i, int* m, int* gi, int* l8) {
-    const int base = q * per_round + 256 * i;
+    const int base = q * per_round + NTH * i;
     const int t = base + (int)threadIdx.x < ntask ? base + (int)threadIdx.x : base;
     const int grp = t >> 3;
     *l8 = t & 7;
@@ -968,7 +980,7 @@ __device__ __forceinline__ void make_codes(const DecodeArgs& g, int j0, int G, i
       int m, gi, l8;
       task_of(q, i, &m, &gi, &l8);
       const int64_t e = (int64_t)m * K + (j0 + gi) * 32 + l8 * 4;
-      if (q * per_round + 256 * i >= ntask) {  // uniform: nothing of this pass exists
+      if (q * per_round + NTH * i >= ntask) {  // uniform: nothing of this pass exists
         raw.v[i] = uint4{0u, 0u, 0u, 0u};
       } else if (g.in_codes) {
         raw.v[i].x = *reinterpret_cast<const uint32_t*>(g.a_codes + e);
@@ -985,7 +997,7 @@ __device__ __forceinline__ void make_codes(const DecodeArgs& g, int j0, int G, i
   auto process = [&](int q, const CodeRaw& raw) {
 #pragma unroll
     for (int i = 0; i < kU; ++i) {
-      const int base = q * per_round + 256 * i;
+      const int base = q * per_round + NTH * i;
       if (base >= ntask) continue;  // uniform
       int m, gi, l8;
       task_of(q, i, &m, &gi, &l8);
@@ -1025,11 +1037,14 @@ __device__ __forceinline__ void make_codes(const DecodeArgs& g, int j0, int G, i
 
 // N1 = N2 = 0: no transform (x quantized as it is, or codes given).
 // RM: rows bound (4 or 16).  MODE 0: y; MODE 1: int32 group dots.  CPW:
-// output columns per work-group (8, 16 or 32; 16 or 32 for RM = 16).
-template <int NRT, int N1, int N2, int RM, int MODE, int CPW>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
+// output columns per work-group (8, 16 or 32; 16 or 32 for RM = 16).  NTH:
+// threads per work-group (256 or 512).
+template <int NRT, int N1, int N2, int RM, int MODE, int CPW, int NTH>
+__global__ __launch_bounds__(NTH) void decode_kernel(DecodeArgs g) {
   extern __shared__ __align__(16) unsigned char lds[];
-  using C = Cols<CPW>;
+  constexpr int KP = N1 > 0 ? slots_for(N1 * N2 / 32, NTH / CPW) : kPer;
+  using C = Cols<CPW, NTH, KP>;
+  constexpr int NW = C::NW;
   constexpr int kSlice = C::kSlice;
   constexpr int NH = C::NH;
   const int tid = threadIdx.x;
@@ -1051,11 +1066,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
   // second follows once they are: both would crowd the transform's registers)
   constexpr bool kMfma = RM > 4;  // up to 16 rows: MFMA dots; up to 4: VALU dots
   static_assert(!kMfma || CPW >= 16, "the MFMA form takes 16 columns per instruction");
-  typedef typename std::conditional<kMfma, MSlice<CPW>, WSlice>::type Slice;
+  typedef typename std::conditional<kMfma, MSlice<CPW, NTH, KP>, WSlice<KP>>::type Slice;
   Slice wa, wb;
   auto load = [&](int sl, Slice& buf) {
-    if constexpr (kMfma) load_mslice<CPW, MODE>(g, cb, sl, buf);
-    else load_slice<CPW, MODE>(g, cb, sl, c, gq, buf);
+    if constexpr (kMfma) load_mslice<CPW, MODE, NTH, KP>(g, cb, sl, buf);
+    else load_slice<CPW, MODE, NTH, KP>(g, cb, sl, c, gq, buf);
   };
   float acc[RM];
   float accm[NH][4];
@@ -1067,8 +1082,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
     for (int e = 0; e < 4; ++e) accm[tt][e] = 0.0f;
   auto dots = [&](int sl, const Slice& buf, int jlo, int jhi, const int8_t* sA, int a_ld, int a_j0,
                   const float* sS, int s_ld) {
-    if constexpr (kMfma) mfma_slice<CPW, MODE>(g, cb, sl, buf, jlo, jhi, sA, a_ld, a_j0, sS, s_ld, accm);
-    else dot_slice<CPW, RM, MODE>(g, cb, sl, c, gq, buf, jlo, jhi, sA, a_ld, a_j0, sS, s_ld, acc);
+    if constexpr (kMfma) mfma_slice<CPW, MODE, NTH, KP>(g, cb, sl, buf, jlo, jhi, sA, a_ld, a_j0, sS, s_ld, accm);
+    else dot_slice<CPW, RM, MODE, NTH, KP>(g, cb, sl, c, gq, buf, jlo, jhi, sA, a_ld, a_j0, sS, s_ld, acc);
   };
   // slices alternate between the two register buffers (unrolled by two so
   // each buffer stays in registers); `body(sl, buf)` consumes slice sl
@@ -1096,9 +1111,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
     float* sS = reinterpret_cast<float*>(lds + P::off_codes + P::codes_bytes(R));
     red = sS + R * (P::K / 32);
     {
-      MatRegs<N1> m1;
-      MatRegs<N2> m2;
-      RowRegs<P::K> x0;
+      MatRegs<N1, NTH> m1;
+      MatRegs<N2, NTH> m2;
+      RowRegs<P::K, NTH> x0;
       stage_matrix_issue<N1>(g.P1, m1);
       stage_matrix_issue<N2>(g.P2, m2);
       x_row_issue<P::K>(g, 0, x0);
@@ -1116,8 +1131,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
       }
     }
     // (transform_row's first barrier orders these stores)
-    for (int r = 0; r < R; ++r) transform_row<NRT, N1, N2>(g, r, lds, sC, sS, r == 0);
-    if (g.codes_out) dump_codes(g, 0, Ga, sC, K, sS, Ga);
+    for (int r = 0; r < R; ++r) transform_row<NRT, N1, N2, NTH>(g, r, lds, sC, sS, r == 0);
+    if (g.codes_out) dump_codes<NTH>(g, 0, Ga, sC, K, sS, Ga);
     if (nsl > 1) load(1, wb);
     sweep([&](int sl, const Slice& buf) { dots(sl, buf, 0, Ga, sC, K, 0, sS, Ga); });
   } else if (g.whole) {
@@ -1130,11 +1145,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
       if (nsl > 1) load(1, wb);
     };
     if (g.in_codes && g.wide_codes)
-      copy_codes<MODE>(g, 0, Ga, sA, K, sSt, Ga, kick);
+      copy_codes<MODE, NTH>(g, 0, Ga, sA, K, sSt, Ga, kick);
     else
-      make_codes<MODE>(g, 0, Ga, sA, K, sSt, Ga, kick);
+      make_codes<MODE, NTH>(g, 0, Ga, sA, K, sSt, Ga, kick);
     __syncthreads();
-    if (g.codes_out && !g.in_codes) dump_codes(g, 0, Ga, sA, K, sSt, Ga);
+    if (g.codes_out && !g.in_codes) dump_codes<NTH>(g, 0, Ga, sA, K, sSt, Ga);
     sweep([&](int sl, const Slice& buf) { dots(sl, buf, 0, Ga, sA, K, 0, sSt, Ga); });
   } else {
     // too many codes for LDS: one weight slice of codes at a time
@@ -1149,11 +1164,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
       const int GS = min(kSlice, Ga - j0);
       __syncthreads();  // the previous slice's codes are no longer read
       if (g.in_codes && g.wide_codes)
-        copy_codes<MODE>(g, j0, GS, sA, kSlice * 32, sSt, kSlice, none);
+        copy_codes<MODE, NTH>(g, j0, GS, sA, kSlice * 32, sSt, kSlice, none);
       else
-        make_codes<MODE>(g, j0, GS, sA, kSlice * 32, sSt, kSlice, none);
+        make_codes<MODE, NTH>(g, j0, GS, sA, kSlice * 32, sSt, kSlice, none);
       __syncthreads();
-      if (g.codes_out && !g.in_codes) dump_codes(g, j0, GS, sA, kSlice * 32, sSt, kSlice);
+      if (g.codes_out && !g.in_codes) dump_codes<NTH>(g, j0, GS, sA, kSlice * 32, sSt, kSlice);
       dots(sl, buf, j0, j0 + GS, sA, kSlice * 32, j0, sSt, kSlice);
     });
   }
@@ -1161,36 +1176,45 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
 
   // partial sums of each (row, column) added in a fixed order through LDS
   if constexpr (kMfma) {
-    // the four waves' sums: red[((wave * NH + half) * 4 + e) * 64 + lane]
+    // the NW waves' sums: red[((wave * NH + half) * 4 + e) * 64 + lane]
     const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
     for (int tt = 0; tt < NH; ++tt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[((wave * NH + tt) * 4 + e) * 64 + lane] = accm[tt][e];
     __syncthreads();
-    for (int o = tid; o < R * CPW; o += 256) {  // row o / CPW, column o % CPW
+    for (int o = tid; o < R * CPW; o += NTH) {  // row o / CPW, column o % CPW
       const int m = o / CPW, col = o - m * CPW;
       const int n = cb * CPW + col;
       if (n < g.N) {
         const int ln = (m >> 2) * 16 + (col & 15);
         float tot = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) tot += red[((w * NH + (col >> 4)) * 4 + (m & 3)) * 64 + ln];
+        for (int w = 0; w < NW; ++w) tot += red[((w * NH + (col >> 4)) * 4 + (m & 3)) * 64 + ln];
         g.y[(int64_t)m * g.N + n] = tot;
       }
     }
   } else {
-    // the GL lane groups' sums
+    // the GL lane groups' sums: the 64 / CPW lanes of a wave that hold one
+    // column (lanes c + CPW k) by an xor butterfly, then the NW waves'
+    // totals in wave order through LDS (a fixed order: y is deterministic)
+    const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int m = 0; m < RM; ++m) red[(gq * RM + m) * CPW + c] = acc[m];
+    for (int m = 0; m < RM; ++m)
+#pragma unroll
+      for (int o = CPW; o < 64; o <<= 1) acc[m] += __shfl_xor(acc[m], o);
+    if (lane < CPW) {
+#pragma unroll
+      for (int m = 0; m < RM; ++m) red[(wave * RM + m) * CPW + lane] = acc[m];
+    }
     __syncthreads();
-    for (int o = tid; o < R * CPW; o += 256) {  // row o / CPW, column o % CPW
+    for (int o = tid; o < R * CPW; o += NTH) {  // row o / CPW, column o % CPW
       const int m = o / CPW, col = o - m * CPW;
       const int n = cb * CPW + col;
       if (n < g.N) {
         float tot = 0.0f;
 #pragma unroll
-        for (int q = 0; q < C::GL; ++q) tot += red[(q * RM + m) * CPW + col];
+        for (int w = 0; w < NW; ++w) tot += red[(w * RM + m) * CPW + col];
         g.y[(int64_t)m * g.N + n] = tot;
       }
     }
@@ -1198,15 +1222,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs g) {
 }
 
 // the kernel of a factor shape (N1 = N2 = 0: none) for CPW columns per work-group
-template <int NRT, int N1, int N2, int RM, int MODE>
+template <int NRT, int N1, int N2, int RM, int MODE, int NTH>
 const void* decode_fn(int cpw) {
   if (cpw == 8) {
-    if constexpr (RM <= 4) return reinterpret_cast<const void*>(decode_kernel<NRT, N1, N2, RM, MODE, 8>);
+    if constexpr (RM <= 4) return reinterpret_cast<const void*>(decode_kernel<NRT, N1, N2, RM, MODE, 8, NTH>);
     return nullptr;
   }
-  if (cpw == 16) return reinterpret_cast<const void*>(decode_kernel<NRT, N1, N2, RM, MODE, 16>);
-  return reinterpret_cast<const void*>(decode_kernel<NRT, N1, N2, RM, MODE, 32>);
+  if (cpw == 16) return reinterpret_cast<const void*>(decode_kernel<NRT, N1, N2, RM, MODE, 16, NTH>);
+  return reinterpret_cast<const void*>(decode_kernel<NRT, N1, N2, RM, MODE, 32, NTH>);
 }
+
+// Threads per work-group of a transform instance: the factor staging, the
+// row transform and the quantizer, which every work-group repeats, split over
+// 8 waves; 4 for K = 6912, whose 8-wave form spills registers (2 waves per
+// SIMD leave 256 each).  The other instances take 4 waves.
+constexpr int xform_threads(int n1, int n2) { return n1 * n2 > 6000 ? 256 : 512; }
 
 // LDS of the non-transform instances: all rows' codes and steps, or one
 // weight slice of them; then the partial sums (RM * 1 KiB: 256 threads x RM
@@ -1235,7 +1265,7 @@ bool decode_transform_fused(int R, int n1, int n2) {
   if ((int64_t)R * n1 * n2 * (n1 + n2) > 1250000) return false;
   const int RM = R <= 4 ? 4 : kDecodeMaxRows;
 #define LOOPQ_DECODE_FITS(n1_, n2_, rs_, nim_, ws_) \
-  if (n1 == n1_ && n2 == n2_) return XPlan<n1_, n2_>::lds(R, RM) <= kLdsBudget;
+  if (n1 == n1_ && n2 == n2_) return XPlan<n1_, n2_>::lds(R, RM, xform_threads(n1_, n2_)) <= kLdsBudget;
   LOOPQ_SHAPES(LOOPQ_DECODE_FITS)
 #undef LOOPQ_DECODE_FITS
   return false;
@@ -1282,7 +1312,7 @@ hipError_t launch_decode(const DecodeCall& c, hipStream_t s) {
     g.steps_out = c.steps_out;
   }
   const void* fn = nullptr;
-  int lds = 0;
+  int lds = 0, threads = 256;
   const bool small = c.R <= 4;
   const int RM = small ? 4 : kDecodeMaxRows;
   const int cpw = pick_cpw(padded_cols(c.N), c.R, device_cu_count());
@@ -1290,23 +1320,25 @@ hipError_t launch_decode(const DecodeCall& c, hipStream_t s) {
 #define LOOPQ_DECODE_KERNEL(n1_, n2_, rs_, nim_, ws_)                                                   \
     if (c.n1 == n1_ && c.n2 == n2_) {                                                              \
       constexpr int nrt = (n1_ + 15) / 16;                                                         \
-      fn = small ? decode_fn<nrt, n1_, n2_, 4, 0>(cpw) : decode_fn<nrt, n1_, n2_, kDecodeMaxRows, 0>(cpw); \
-      lds = XPlan<n1_, n2_>::lds(c.R, RM);                                                         \
+      constexpr int nth = xform_threads(n1_, n2_);                                                 \
+      fn = small ? decode_fn<nrt, n1_, n2_, 4, 0, nth>(cpw) : decode_fn<nrt, n1_, n2_, kDecodeMaxRows, 0, nth>(cpw); \
+      lds = XPlan<n1_, n2_>::lds(c.R, RM, nth);                                                    \
+      threads = nth;                                                                               \
     }
     LOOPQ_SHAPES(LOOPQ_DECODE_KERNEL)
 #undef LOOPQ_DECODE_KERNEL
   } else {
-    fn = small ? (c.mode == 0 ? decode_fn<1, 0, 0, 4, 0>(cpw) : decode_fn<1, 0, 0, 4, 1>(cpw))
-               : (c.mode == 0 ? decode_fn<1, 0, 0, kDecodeMaxRows, 0>(cpw)
-                              : decode_fn<1, 0, 0, kDecodeMaxRows, 1>(cpw));
+    fn = small ? (c.mode == 0 ? decode_fn<1, 0, 0, 4, 0, 256>(cpw) : decode_fn<1, 0, 0, 4, 1, 256>(cpw))
+               : (c.mode == 0 ? decode_fn<1, 0, 0, kDecodeMaxRows, 0, 256>(cpw)
+                              : decode_fn<1, 0, 0, kDecodeMaxRows, 1, 256>(cpw));
     g.whole = whole_lds(c.R, c.K, RM) <= kLdsBudget;
     lds = g.whole ? whole_lds(c.R, c.K, RM) : slice_lds(RM, cpw);
   }
   if (fn == nullptr || lds > kLdsBudget) return hipErrorInvalidValue;
-  hipError_t e = prepare_launch(fn, lds, 256);
+  hipError_t e = prepare_launch(fn, lds, threads);
   if (e != hipSuccess) return e;
   void* args[] = {&g};
-  e = hipLaunchKernel(fn, dim3((unsigned)(padded_cols(c.N) / cpw)), dim3(256), args, lds, s);
+  e = hipLaunchKernel(fn, dim3((unsigned)(padded_cols(c.N) / cpw)), dim3((unsigned)threads), args, lds, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

@@ -116,9 +116,26 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+_torch = None
+_raw_stream = None
+
+
+def _torch_mod():
+    global _torch, _raw_stream
+    if _torch is None:
+        import torch
+        # the current stream's handle as an int: torch's raw getter costs a
+        # tenth of building a Stream object, which matters for few-row calls
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _torch = torch
+    return _torch
+
+
 def _stream(stream) -> Optional[int]:
-    import torch
     if stream is None:
+        torch = _torch_mod()
+        if _raw_stream is not None:
+            return _raw_stream(torch.cuda.current_device())
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
         return stream
@@ -126,7 +143,7 @@ def _stream(stream) -> Optional[int]:
 
 
 def _dtype_code(x) -> int:
-    import torch
+    torch = _torch_mod()
     if x.dtype == torch.float32:
         return LOOPQ_F32
     if x.dtype == torch.bfloat16:
