@@ -442,57 +442,146 @@ struct ItemPlan {
   static constexpr int lds = off_t + N1 * 16 * 4;
 };
 
-// The P2 registers of stage_matrix_issue committed as the three bf16 planes
-// (transposed, zeros outside the factor), and the bf16 X row registers of
-// x_row_issue as the bf16 grid (K columns n2 .. kb - 1 zeroed).
+// The factors staged in quads: four consecutive reduction indices of one
+// output column (P2: K indices b = 4 bq .. + 3 of column j; P1: reduction
+// indices a = 4 aq .. + 3 of output row i), loaded first and committed either
+// as the bf16 planes, one 8-byte store per plane and quad (the four indices
+// sit in consecutive slots of both plane layouts, at a row stride that spreads
+// the lanes of a store over the banks), or as the fp32 rows.  Quads of the
+// planes' padding are zeroed without loads.  The plane contents are those of
+// the chunked kernel's staging (split3_bf16 of each element), so x~ is the
+// same bit for bit.
+inline __device__ uint2 pack4_bf16(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return uint2{a | (b << 16), c | (d << 16)};
+}
+// the three planes of four values, as 8-byte words at dst + o (+ plane, + 2 plane)
+inline __device__ void planes_quad_store(const float4& v, uint16_t* dst, int o, int plane) {
+  uint32_t h[4], m[4], l[4];
+  split3_bf16(v.x, &h[0], &m[0], &l[0]);
+  split3_bf16(v.y, &h[1], &m[1], &l[1]);
+  split3_bf16(v.z, &h[2], &m[2], &l[2]);
+  split3_bf16(v.w, &h[3], &m[3], &l[3]);
+  *reinterpret_cast<uint2*>(dst + o) = pack4_bf16(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint2*>(dst + plane + o) = pack4_bf16(m[0], m[1], m[2], m[3]);
+  *reinterpret_cast<uint2*>(dst + 2 * plane + o) = pack4_bf16(l[0], l[1], l[2], l[3]);
+}
+
+// P2 (n2 x n2, row b, column j): quad q = bq * N2 + j
 template <int N2, int NTH>
-__device__ __forceinline__ void p2_planes_commit(const MatRegs<N2, NTH>& m, uint16_t* dst) {
-  using L = BfLayout<N2>;
+struct P2Quads {
+  static_assert(N2 % 4 == 0, "quads of K indices");
+  static constexpr int NQ = N2 * (N2 / 4);
+  static constexpr int T = (NQ + NTH - 1) / NTH;
+  float4 v[T];
+};
+template <int N2, int NTH>
+__device__ __forceinline__ void p2_quads_issue(const float* __restrict__ P2, P2Quads<N2, NTH>& m) {
 #pragma unroll
-  for (int i = 0; i < MatRegs<N2, NTH>::T; ++i) {
-    const int idx = threadIdx.x + NTH * i;  // element b * N2 + j of P2
-    if (idx < N2 * N2) {
-      const int b = idx / N2, j = idx - b * N2;
-      uint32_t h, mm, l;
-      split3_bf16(m.v[i], &h, &mm, &l);
-      dst[j * L::sb + b] = (uint16_t)h;
-      dst[L::plane + j * L::sb + b] = (uint16_t)mm;
-      dst[2 * L::plane + j * L::sb + b] = (uint16_t)l;
+  for (int i = 0; i < P2Quads<N2, NTH>::T; ++i) {
+    const int q = threadIdx.x + NTH * i;
+    if (q < P2Quads<N2, NTH>::NQ) {
+      const int bq = q / N2, j = q - bq * N2;
+      const float* src = P2 + 4 * bq * N2 + j;
+      m.v[i] = float4{src[0], src[N2], src[2 * N2], src[3 * N2]};
     }
-  }
-  // zeros: K indices b >= N2 of every column (none when N2 % 32 == 0)
-  constexpr int w = L::kb - N2 > 0 ? L::kb - N2 : 1;
-  constexpr int padb = N2 * (L::kb - N2);
-  for (int idx = threadIdx.x; idx < padb; idx += NTH) {
-    const int j = idx / w, b = N2 + idx % w;
-#pragma unroll
-    for (int p = 0; p < 3; ++p) dst[p * L::plane + j * L::sb + b] = 0;
   }
 }
-// The P1 registers of stage_matrix_issue committed as the bf16 stage-2 planes
-// (P1Layout): element (a, i) to row i, slot p1_slot(a); zeros at the rows i
-// and slots of reduction rows a past n1 (positions no element writes).
-template <int N1, int NTH>
-__device__ __forceinline__ void p1_planes_commit(const MatRegs<N1, NTH>& m, uint16_t* dst) {
-  using L = P1Layout<N1>;
+// as the bf16 planes (BfLayout: plane p, column j, K slot b at p * plane +
+// j * sb + b), K slots n2 .. kb - 1 zeroed
+template <int N2, int NTH>
+__device__ __forceinline__ void p2_quads_commit_bf(const P2Quads<N2, NTH>& m, uint16_t* dst) {
+  using L = BfLayout<N2>;
 #pragma unroll
-  for (int u = 0; u < MatRegs<N1, NTH>::T; ++u) {
-    const int idx = threadIdx.x + NTH * u;  // element a * N1 + i of P1
-    if (idx < N1 * N1) {
-      const int a = idx / N1, i = idx - a * N1;
-      uint32_t h, mm, l;
-      split3_bf16(m.v[u], &h, &mm, &l);
-      const int o = i * L::sb + p1_slot(a);
-      dst[o] = (uint16_t)h;
-      dst[L::plane + o] = (uint16_t)mm;
-      dst[2 * L::plane + o] = (uint16_t)l;
+  for (int i = 0; i < P2Quads<N2, NTH>::T; ++i) {
+    const int q = threadIdx.x + NTH * i;
+    if (q < P2Quads<N2, NTH>::NQ) {
+      const int bq = q / N2, j = q - bq * N2;
+      planes_quad_store(m.v[i], dst, j * L::sb + 4 * bq, L::plane);
     }
   }
-  for (int idx = threadIdx.x; idx < L::rows * L::ka; idx += NTH) {
-    const int i = idx / L::ka, sl = idx - i * L::ka;
-    if (i >= N1 || p1_row_of_slot(sl) >= N1) {
+  constexpr int NZ = N2 * ((L::kb - N2) / 4);  // padding quads
+  for (int z = threadIdx.x; z < NZ; z += NTH) {
+    const int zq = z / N2, j = z - zq * N2;
+    const int o = j * L::sb + N2 + 4 * zq;
 #pragma unroll
-      for (int p = 0; p < 3; ++p) dst[p * L::plane + i * L::sb + sl] = 0;
+    for (int p = 0; p < 3; ++p) *reinterpret_cast<uint2*>(dst + p * L::plane + o) = uint2{0u, 0u};
+  }
+}
+// as fp32 rows: element (b, j) at dst[b * SP + j]
+template <int N2, int SP, int NTH>
+__device__ __forceinline__ void p2_quads_commit_f32(const P2Quads<N2, NTH>& m, float* dst) {
+#pragma unroll
+  for (int i = 0; i < P2Quads<N2, NTH>::T; ++i) {
+    const int q = threadIdx.x + NTH * i;
+    if (q < P2Quads<N2, NTH>::NQ) {
+      const int bq = q / N2, j = q - bq * N2;
+      float* d = dst + 4 * bq * SP + j;
+      d[0] = m.v[i].x;
+      d[SP] = m.v[i].y;
+      d[2 * SP] = m.v[i].z;
+      d[3 * SP] = m.v[i].w;
+    }
+  }
+}
+
+// P1 (n1 x n1, row a, column i): quad q = aq * N1 + i
+template <int N1, int NTH>
+struct P1Quads {
+  static_assert(N1 % 4 == 0, "quads of reduction indices");
+  static constexpr int NQ = N1 * (N1 / 4);
+  static constexpr int T = (NQ + NTH - 1) / NTH;
+  float4 v[T];
+};
+template <int N1, int NTH>
+__device__ __forceinline__ void p1_quads_issue(const float* __restrict__ P1, P1Quads<N1, NTH>& m) {
+#pragma unroll
+  for (int u = 0; u < P1Quads<N1, NTH>::T; ++u) {
+    const int q = threadIdx.x + NTH * u;
+    if (q < P1Quads<N1, NTH>::NQ) {
+      const int aq = q / N1, i = q - aq * N1;
+      const float* src = P1 + 4 * aq * N1 + i;
+      m.v[u] = float4{src[0], src[N1], src[2 * N1], src[3 * N1]};
+    }
+  }
+}
+// as the bf16 stage-2 planes (P1Layout: element (a, i) at row i, slot
+// p1_slot(a); the slots of a quad are consecutive), with zeros at the rows i
+// and slots of reduction rows a past n1
+template <int N1, int NTH>
+__device__ __forceinline__ void p1_quads_commit_bf(const P1Quads<N1, NTH>& m, uint16_t* dst) {
+  using L = P1Layout<N1>;
+#pragma unroll
+  for (int u = 0; u < P1Quads<N1, NTH>::T; ++u) {
+    const int q = threadIdx.x + NTH * u;
+    if (q < P1Quads<N1, NTH>::NQ) {
+      const int aq = q / N1, i = q - aq * N1;
+      planes_quad_store(m.v[u], dst, i * L::sb + p1_slot(4 * aq), L::plane);
+    }
+  }
+  constexpr int NZ = L::rows * (L::ka / 4);  // every quad of the planes; the data ones are skipped
+  if constexpr (L::rows > N1 || L::ka > N1) {
+    for (int z = threadIdx.x; z < NZ; z += NTH) {
+      const int i = z / (L::ka / 4), sq = z - i * (L::ka / 4);
+      if (i >= N1 || p1_row_of_slot(4 * sq) >= N1) {
+#pragma unroll
+        for (int p = 0; p < 3; ++p) *reinterpret_cast<uint2*>(dst + p * L::plane + i * L::sb + 4 * sq) = uint2{0u, 0u};
+      }
+    }
+  }
+}
+// as fp32 rows: element (a, i) at dst[a * SP + i]
+template <int N1, int SP, int NTH>
+__device__ __forceinline__ void p1_quads_commit_f32(const P1Quads<N1, NTH>& m, float* dst) {
+#pragma unroll
+  for (int u = 0; u < P1Quads<N1, NTH>::T; ++u) {
+    const int q = threadIdx.x + NTH * u;
+    if (q < P1Quads<N1, NTH>::NQ) {
+      const int aq = q / N1, i = q - aq * N1;
+      float* d = dst + 4 * aq * SP + i;
+      d[0] = m.v[u].x;
+      d[SP] = m.v[u].y;
+      d[2 * SP] = m.v[u].z;
+      d[3 * SP] = m.v[u].w;
     }
   }
 }
@@ -1105,34 +1194,40 @@ __global__ __launch_bounds__(NTH) void decode_kernel(DecodeArgs g) {
 
   if constexpr (N1 > 0) {
     using P = XPlan<N1, N2>;
+    // the first weight slice is requested with the factors, except where its
+    // registers, live across the transform, would spill ((64, 88), (64, 108)):
+    // there it is requested once the codes are formed (measured faster than
+    // spilling, whose stores wait for every load in flight)
+    constexpr bool late = N1 * N2 > 4096;
     float* sP1 = reinterpret_cast<float*>(lds);
     float* sP2 = reinterpret_cast<float*>(lds + P::off_p2);
     int8_t* sC = reinterpret_cast<int8_t*>(lds + P::off_codes);
     float* sS = reinterpret_cast<float*>(lds + P::off_codes + P::codes_bytes(R));
     red = sS + R * (P::K / 32);
     {
-      MatRegs<N1, NTH> m1;
-      MatRegs<N2, NTH> m2;
+      P1Quads<N1, NTH> m1;
+      P2Quads<N2, NTH> m2;
       RowRegs<P::K, NTH> x0;
-      stage_matrix_issue<N1>(g.P1, m1);
-      stage_matrix_issue<N2>(g.P2, m2);
+      p1_quads_issue<N1>(g.P1, m1);
+      p2_quads_issue<N2>(g.P2, m2);
       x_row_issue<P::K>(g, 0, x0);
-      load(0, wa);
+      if constexpr (!late) load(0, wa);
       if (g.bf16)
-        p1_planes_commit<N1>(m1, reinterpret_cast<uint16_t*>(lds));
+        p1_quads_commit_bf<N1>(m1, reinterpret_cast<uint16_t*>(lds));
       else
-        stage_matrix_commit<N1, P::sp1>(m1, sP1);
+        p1_quads_commit_f32<N1, P::sp1>(m1, sP1);
       if (g.bf16) {
-        p2_planes_commit<N2>(m2, reinterpret_cast<uint16_t*>(lds + P::off_p2));
+        p2_quads_commit_bf<N2>(m2, reinterpret_cast<uint16_t*>(lds + P::off_p2));
         x_row_commit_bf<N1, N2>(x0, reinterpret_cast<uint16_t*>(lds + P::off_x));
       } else {
-        stage_matrix_commit<N2, P::sp2>(m2, sP2);
+        p2_quads_commit_f32<N2, P::sp2>(m2, sP2);
         x_row_commit<P::K, N2, P::sx>(g, x0, reinterpret_cast<float*>(lds + P::off_x));
       }
     }
     // (transform_row's first barrier orders these stores)
     for (int r = 0; r < R; ++r) transform_row<NRT, N1, N2, NTH>(g, r, lds, sC, sS, r == 0);
     if (g.codes_out) dump_codes<NTH>(g, 0, Ga, sC, K, sS, Ga);
+    if constexpr (late) load(0, wa);
     if (nsl > 1) load(1, wb);
     sweep([&](int sl, const Slice& buf) { dots(sl, buf, 0, Ga, sC, K, 0, sS, Ga); });
   } else if (g.whole) {
