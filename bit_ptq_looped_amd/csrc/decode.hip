@@ -1342,12 +1342,17 @@ int slice_lds(int RM, int cpw) {
   return RM * ks * 32 + RM * ks * 4 + 8 * RM * 32 * 4;
 }
 
-// Columns per work-group: the largest of 32, 16, 8 that still gives every CU
-// a work-group (16 at least for the MFMA form), else the smallest allowed.
+// Columns per work-group: the largest of 32, 16, 8 that still gives at least
+// 60% of the CUs a work-group (16 at least for the MFMA form), else the
+// smallest allowed.  More work-groups than CUs put two on some CUs, which then
+// finish about one row transform later than the rest; 32 columns per
+// work-group and 60-100% of the CUs busy cost only a longer weight sweep
+// (measured at N = 6144 and 5632, one row: 192 and 176 work-groups of 32
+// columns end 0.7 us sooner than 384 and 352 of 16).
 int pick_cpw(int64_t n_padded, int R, int ncu) {
   const int lo = R > 4 ? 16 : 8;
   for (int cpw = 32; cpw >= lo; cpw >>= 1)
-    if (n_padded / cpw >= ncu) return cpw;
+    if (n_padded / cpw * 5 >= (int64_t)ncu * 3) return cpw;
   return lo;
 }
 

@@ -400,11 +400,14 @@ int32_t looped_pipelined(const void* x, int dtype, int T, int M, int K, int N, c
   DevicePipe* p = nullptr;
   if (device_pipe(&p, T + 1) != hipSuccess) return LOOPQ_ERR_HIP;
   const int fmt = code_format(bits_a);
-  if (prepare_weights(carve(ws, T, M, K, N, 0, 0), fmt, w_codes, K, N, s) != hipSuccess)
-    return LOOPQ_ERR_HIP;
+  // the auxiliary stream starts quantizing loop 0 while the caller's stream
+  // expands the weights (separate workspace regions); the first GEMM waits
+  // for both
   hipEvent_t start = p->events[T];
   if (hipEventRecord(start, s) != hipSuccess) return LOOPQ_ERR_HIP;
   if (hipStreamWaitEvent(p->aux, start, 0) != hipSuccess) return LOOPQ_ERR_HIP;
+  if (prepare_weights(carve(ws, T, M, K, N, 0, 0), fmt, w_codes, K, N, s) != hipSuccess)
+    return LOOPQ_ERR_HIP;
   for (int t = 0; t < T; ++t) {
     ClipTable one;
     memset(&one, 0, sizeof(one));
