@@ -8,17 +8,25 @@
 // GPTQ memory note of the same page set).  Stacking the rows of every loop,
 // the sum is one symmetric rank-k update of H by all rows.
 //
-// The contraction runs on the fp32 matrix cores (V_MFMA_F32_32X32X2_F32):
+// The contraction runs on the bf16 matrix cores (V_MFMA_F32_32X32X16_BF16):
+// every fp32 x~ value is split into three bf16 planes whose sum is the value
+// exactly (hi = the value truncated to bf16, mid = the remainder truncated,
+// lo = the rest), and each product x~_ri x~_rj is taken as the six plane
+// products of order <= 2 (mid mid, lo hi, hi lo, mid hi, hi mid, hi hi per
+// step of 16 rows, in that order), each exact in fp32; the dropped mid lo,
+// lo mid and lo lo are below 2^-20 of |x~_ri x~_rj|.  Accumulation is fp32.
+// Six bf16 products take 6 x 32 cycles per 32 x 32 block and 16 rows against
+// 8 x 64 for the fp32 MFMA (V_MFMA_F32_32X32X2_F32).
 //   - H is cut into 128 x 128 tiles; only tiles on or above the diagonal are
 //     computed, and each tile's sum is added to H at its place and, mirrored,
 //     below the diagonal, so H stays exactly symmetric.
-//   - A work group (4 waves) owns one tile at a time and stages 16 rows of
+//   - A work group (4 waves) owns one tile at a time and stages 32 rows of
 //     both 128-column strips at a time in LDS (double buffered, float4 loads
 //     from global memory); each wave keeps a 64 x 64 quadrant of the tile in
 //     a fp32 accumulator (2 x 2 MFMA blocks) over all rows.
-//   - MFMA operands: lane l reads columns 2(l % 32) and 2(l % 32) + 1 of its
-//     64-column half strip and row l / 32 of a row pair, so MFMA block p
-//     (0, 1) holds the columns of parity p.
+//   - MFMA operands: lane l reads column 2(l % 32) + p of its 64-column half
+//     strip for rows 8 (l / 32) .. + 7 of a 16-row step and splits them into
+//     the planes, so MFMA block p (0, 1) holds the columns of parity p.
 //   - Work balance: the grid is a fixed number of work groups (kGroups, two
 //     per compute unit of a 256-CU part).  Whole tiles are dealt out round
 //     robin; the tiles left over (fewer than kGroups) are cut into 64-row
@@ -31,6 +39,7 @@
 #include <math.h>
 
 #include "loopq_internal.h"
+#include "quant_core.h"
 
 namespace loopq {
 namespace {
@@ -119,20 +128,51 @@ __device__ __forceinline__ void stage_store(float* stage, const StageRegs& r) {
   }
 }
 
-// this wave's quadrant (qa, qb) over the staged rows
+// The three bf16 planes (hi + mid + lo = v exactly, split3_bf16) of 8
+// consecutive staged rows of one column (P, row stride kTile): the MFMA
+// operand of that column with the 8 rows as its K slots, pl[plane].
+__device__ __forceinline__ void planes_rows8(const float* P, v4u (&pl)[3]) {
+  float v[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) v[t] = P[t * kTile];
+  planes8(v, pl);
+}
+
+__device__ __forceinline__ v16f mm16(const v4u& a, const v4u& b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// this wave's quadrant (qa, qb) over the staged rows, 16 rows per step on the
+// bf16 MFMA: both operands as three exact bf16 planes and the six plane
+// products of order <= 2, smallest first (mid mid, lo hi, hi lo, mid hi,
+// hi mid, hi hi), into one fp32 accumulator per block.  Lane l takes column
+// 2 (l % 32) + p of its half strip for MFMA operand parity p (block (pa, pb)
+// holds the columns of parities pa and pb) and rows 8 (l / 32) .. + 7 of the
+// step.
 template <bool DIAG>
 __device__ __forceinline__ void stage_mfma(v16f acc[4], const float* stage, int qa, int qb, int lane) {
-  const int lo = (lane >> 5) * kTile + 2 * (lane & 31);
+  const int lo = (lane >> 5) * 8 * kTile + 2 * (lane & 31);
   const float* A = stage + 64 * qa + lo;
   const float* B = stage + (DIAG ? 0 : kStrip) + 64 * qb + lo;
+  constexpr int pa_of[6] = {1, 2, 0, 1, 0, 0};
+  constexpr int pb_of[6] = {1, 0, 2, 0, 1, 0};
 #pragma unroll
-  for (int k = 0; k < kStep / 2; ++k) {
-    const float2 a = *reinterpret_cast<const float2*>(A + 2 * k * kTile);
-    const float2 b = *reinterpret_cast<const float2*>(B + 2 * k * kTile);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.y, acc[1], 0, 0, 0);
-    acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.x, acc[2], 0, 0, 0);
-    acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc[3], 0, 0, 0);
+  for (int k = 0; k < kStep / 16; ++k) {
+    v4u b[2][3];
+    planes_rows8(B + 16 * k * kTile, b[0]);
+    planes_rows8(B + 16 * k * kTile + 1, b[1]);
+#pragma unroll
+    for (int pa = 0; pa < 2; ++pa) {
+      v4u a[3];
+      planes_rows8(A + 16 * k * kTile + pa, a);
+#pragma unroll
+      for (int q = 0; q < 6; ++q)
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+          const int blk = 2 * pa + pb;
+          acc[blk] = mm16(a[pa_of[q]], b[pb][pb_of[q]], acc[blk]);
+        }
+    }
   }
 }
 
@@ -263,7 +303,7 @@ __device__ void run_segment(v16f acc[4], float* lds, const HPlan& p, int u, int 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void hessian_tiles_kernel(HPlan p) {
+__global__ __launch_bounds__(kThreads, 2) void hessian_tiles_kernel(HPlan p) {
   extern __shared__ float lds[];  // max(2 stages, 4 quadrants) floats
   // Logical work group g: the hardware dispatches consecutive work groups to
   // the 8 XCDs in turn, so g = 64 * (XCD) + (slot) gives each XCD a run of

@@ -29,7 +29,7 @@ import torch
 
 import oracle
 from bit_ptq_looped_amd import synth
-from xt_check import check_xt, gpu_xt
+from xt_check import check_xt, gpu_xt, hessian_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -243,7 +243,8 @@ def test_fullsize_trajectory_hessian(lq, act):
     """The bench's trajectory Hessian: the x~ of all T*M = 4096 rows of one
     block input (the quantizer's dump) accumulated in one call; sampled
     elements against the fp64 sum over the rows, computed one by one, within
-    the fp32 accumulation bound (rows + 1) u (|x|^T |x|)_ij; exact symmetry."""
+    the bound of the kernel's plane-product arithmetic (xt_check.hessian_bound);
+    exact symmetry."""
     wl = synth.ouro_block_workload()
     K = groups_by_input(wl)[act][0].K
     P1, P2 = synth.factors_for(wl, act, K)
@@ -264,12 +265,11 @@ def test_fullsize_trajectory_hessian(lq, act):
     check_xt(X[sample_rows(rows)].astype(np.float32), x32.reshape(rows, K)[sample_rows(rows)], P1, P2)
     Hc = H.cpu().numpy()
     assert np.array_equal(Hc, Hc.T)
-    u = 2.0 ** -24
     worst = 0.0
     for i, j in sample_pairs(K, 400, 1):
         want = float(X[:, i] @ X[:, j])
         mag = float(np.abs(X[:, i]) @ np.abs(X[:, j]))
-        bound = (rows + 1) * u / (1 - (rows + 1) * u) * mag
+        bound = hessian_bound(rows, mag)
         err = abs(float(Hc[i, j]) - want)
         assert err <= bound, (i, j, err, bound)
         worst = max(worst, err / max(bound, 1e-300))

@@ -1,14 +1,16 @@
 """GPU parity of the trajectory Hessian accumulation (``loopq_hessian_accumulate``)
 against the CPU oracle, through the C ABI.
 
-Bar, derived from the arithmetic: each element of H0 + X^T X is a sum of
-rows + 1 terms (rows fp32 products and H0) that the kernel forms with fp32
-products and fp32 additions in some fixed order, so it lies within
-gamma_(rows+1) = (rows + 1) u / (1 - (rows + 1) u), u = 2^-24, times
-(|X|^T |X| + |H0|) of the exact value, which the fp64 oracle gives (its own
-error is far below that).  Several calls chain: the bound adds up over them.
-H is exactly symmetric (one value stored at (i, j) and (j, i)) and the call
-is deterministic.
+Bar, derived from the arithmetic (``xt_check.hessian_bound``): the kernel takes
+each product x~_ri x~_rj as the six bf16-plane products of order <= 2 (each
+exact in fp32, the dropped rest below 2^-20 of |x~_ri x~_rj|) and adds them in
+fp32 (six additions per row, one per split-tile piece, one into H), so every
+element of H0 + X^T X lies within
+gamma(6 rows + ceil(rows / 64) + 2) ((1 + 2^-6) |X|^T |X| + |H0|) + 2^-20 |X|^T |X|
+of the exact value, which the fp64 oracle gives (its own error is far below
+that).  Several calls chain: the bound adds up over them.  H is exactly
+symmetric (one value stored at (i, j) and (j, i)) and the call is
+deterministic.
 """
 
 import numpy as np
@@ -17,12 +19,9 @@ import torch
 
 import oracle
 from bit_ptq_looped_amd import synth
-from xt_check import check_xt
+from xt_check import check_xt, hessian_bound
 
 pytestmark = pytest.mark.gpu
-
-U = 2.0 ** -24
-
 
 def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -30,10 +29,6 @@ def dev(a):
 
 def say(*a):
     print(*a, flush=True)
-
-
-def gamma(n):
-    return n * U / (1.0 - n * U)
 
 
 def workspace(lq, rows, K):
@@ -53,13 +48,18 @@ def accumulate(lq, xs, H0):
 
 
 def check_bound(got, xs, H0):
-    """Element-wise bound of the module docstring over a chain of calls."""
+    """Element-wise bound of the module docstring over a chain of calls: each
+    call's bound with the running |H| before it as its |H0|."""
     want = np.asarray(H0, dtype=np.float64) + sum(oracle.trajectory_hessian(x) for x in xs)
-    mag = np.abs(np.asarray(H0, dtype=np.float64)) + sum(oracle.trajectory_hessian(np.abs(x)) for x in xs)
-    bound = gamma(sum(x.shape[0] for x in xs) + len(xs)) * mag
+    run = np.abs(np.asarray(H0, dtype=np.float64))
+    bound = np.zeros_like(run)
+    for x in xs:
+        mag_x = oracle.trajectory_hessian(np.abs(x))
+        bound = bound + hessian_bound(x.shape[0], mag_x, run)
+        run = run + mag_x
     err = np.abs(got.astype(np.float64) - want)
     ratio = float(np.max(err / np.maximum(bound, 1e-300)))
-    assert np.all(err <= bound), f"H outside the fp32 accumulation bound (max error/bound {ratio:.3g})"
+    assert np.all(err <= bound), f"H outside the plane-product accumulation bound (max error/bound {ratio:.3g})"
     return ratio
 
 

@@ -62,3 +62,29 @@ def gpu_xt(lq, xdev, x32, P1, P2):
     dump = xt.cpu().numpy()
     check_xt(dump, x32, P1, P2)
     return dump
+
+
+# ---------------------------------------------------------------------------
+# Parity reading for the trajectory Hessian (H += x~^T x~).  The kernel
+# multiplies on the bf16 matrix cores: each fp32 x~ value is split into three
+# bf16 planes whose sum is the value exactly (hi = the value truncated to
+# bf16, mid = the remainder truncated, lo = the rest), and each product
+# x~_ri x~_rj is taken as the six plane products of order <= 2, each exact in
+# fp32; the three dropped ones (mid lo, lo mid, lo lo) are below
+# 2 * 2^-7 * 2^-14 + 2^-28 < 2^-20 of |x~_ri x~_rj|, and the kept ones sum to
+# at most (1 + 2^-6) |x~_ri x~_rj|.  They are added in fp32: six additions per
+# row, at most one per 64-row piece of a tile split across work groups, and
+# the final addition to H, so an element of H0 + sum_r x~_r^T x~_r lies within
+#   gamma(6 rows + ceil(rows / 64) + 2) ((1 + 2^-6) |x~|^T |x~| + |H0|) + 2^-20 |x~|^T |x~|
+# of the exact value, gamma(n) = n u / (1 - n u), u = 2^-24.  Chained calls
+# add their bounds.
+# ---------------------------------------------------------------------------
+HESS_U = 2.0 ** -24
+
+
+def hessian_bound(rows, mag_x, mag_h0=0.0):
+    """The element-wise bound above for one call over `rows` rows, with
+    mag_x = (|x~|^T |x~|)_ij and mag_h0 = |H0_ij| (scalars or arrays)."""
+    n = 6 * rows + -(-rows // 64) + 2
+    gamma = n * HESS_U / (1.0 - n * HESS_U)
+    return gamma * ((1.0 + 2.0 ** -6) * mag_x + mag_h0) + 2.0 ** -20 * mag_x
