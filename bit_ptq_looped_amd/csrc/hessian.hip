@@ -24,9 +24,10 @@
 //     both 128-column strips at a time in LDS (double buffered, float4 loads
 //     from global memory); each wave keeps a 64 x 64 quadrant of the tile in
 //     a fp32 accumulator (2 x 2 MFMA blocks) over all rows.
-//   - MFMA operands: lane l reads column 2(l % 32) + p of its 64-column half
-//     strip for rows 8 (l / 32) .. + 7 of a 16-row step and splits them into
-//     the planes, so MFMA block p (0, 1) holds the columns of parity p.
+//   - MFMA operands: lane l reads columns 2(l % 32) and 2(l % 32) + 1 of its
+//     64-column half strip for rows 8 (l / 32) .. + 7 of a 16-row step and
+//     splits them into the planes, so MFMA block p (0, 1) holds the columns
+//     of parity p.
 //   - Work balance: the grid is a fixed number of work groups (kGroups, two
 //     per compute unit of a 256-CU part).  Whole tiles are dealt out round
 //     robin; the tiles left over (fewer than kGroups) are cut into 64-row
@@ -129,13 +130,21 @@ __device__ __forceinline__ void stage_store(float* stage, const StageRegs& r) {
 }
 
 // The three bf16 planes (hi + mid + lo = v exactly, split3_bf16) of 8
-// consecutive staged rows of one column (P, row stride kTile): the MFMA
-// operand of that column with the 8 rows as its K slots, pl[plane].
-__device__ __forceinline__ void planes_rows8(const float* P, v4u (&pl)[3]) {
-  float v[8];
+// consecutive staged rows of two adjacent columns (P, row stride kTile): the
+// MFMA operand of the column of parity p with the 8 rows as its K slots,
+// pl[p][plane].
+__device__ __forceinline__ void planes_rows8(const float* P, v4u (&pl)[2][3]) {
+  float2 v[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) v[t] = P[t * kTile];
-  planes8(v, pl);
+  for (int t = 0; t < 8; ++t) v[t] = *reinterpret_cast<const float2*>(P + t * kTile);
+  float e[8], o[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    e[t] = v[t].x;
+    o[t] = v[t].y;
+  }
+  planes8(e, pl[0]);
+  planes8(o, pl[1]);
 }
 
 __device__ __forceinline__ v16f mm16(const v4u& a, const v4u& b, v16f c) {
@@ -145,10 +154,9 @@ __device__ __forceinline__ v16f mm16(const v4u& a, const v4u& b, v16f c) {
 // this wave's quadrant (qa, qb) over the staged rows, 16 rows per step on the
 // bf16 MFMA: both operands as three exact bf16 planes and the six plane
 // products of order <= 2, smallest first (mid mid, lo hi, hi lo, mid hi,
-// hi mid, hi hi), into one fp32 accumulator per block.  Lane l takes column
-// 2 (l % 32) + p of its half strip for MFMA operand parity p (block (pa, pb)
-// holds the columns of parities pa and pb) and rows 8 (l / 32) .. + 7 of the
-// step.
+// hi mid, hi hi), into one fp32 accumulator per block.  Lane l takes columns
+// 2 (l % 32) and 2 (l % 32) + 1 of its half strip (block (pa, pb) holds the
+// columns of parities pa and pb) and rows 8 (l / 32) .. + 7 of the step.
 template <bool DIAG>
 __device__ __forceinline__ void stage_mfma(v16f acc[4], const float* stage, int qa, int qb, int lane) {
   const int lo = (lane >> 5) * 8 * kTile + 2 * (lane & 31);
@@ -158,21 +166,14 @@ __device__ __forceinline__ void stage_mfma(v16f acc[4], const float* stage, int 
   constexpr int pb_of[6] = {1, 0, 2, 0, 1, 0};
 #pragma unroll
   for (int k = 0; k < kStep / 16; ++k) {
-    v4u b[2][3];
-    planes_rows8(B + 16 * k * kTile, b[0]);
-    planes_rows8(B + 16 * k * kTile + 1, b[1]);
+    v4u a[2][3], b[2][3];
+    planes_rows8(A + 16 * k * kTile, a);
+    planes_rows8(B + 16 * k * kTile, b);
 #pragma unroll
-    for (int pa = 0; pa < 2; ++pa) {
-      v4u a[3];
-      planes_rows8(A + 16 * k * kTile + pa, a);
+    for (int q = 0; q < 6; ++q)
 #pragma unroll
-      for (int q = 0; q < 6; ++q)
-#pragma unroll
-        for (int pb = 0; pb < 2; ++pb) {
-          const int blk = 2 * pa + pb;
-          acc[blk] = mm16(a[pa_of[q]], b[pb][pb_of[q]], acc[blk]);
-        }
-    }
+      for (int blk = 0; blk < 4; ++blk)
+        acc[blk] = mm16(a[blk >> 1][pa_of[q]], b[blk & 1][pb_of[q]], acc[blk]);
   }
 }
 
