@@ -332,23 +332,29 @@ hipError_t launch_expand_weights_f6(const uint8_t* w_codes, int K, int N, void* 
 // 0 the 128x128 form (every wave over all of K), 1 the two-way split-K form
 // (64x128 tiles, half of K per wave), 2 the four-way form (64x64 tiles, a
 // quarter of K per wave).  The waves of a launch land about evenly on the
-// SIMDs, so it takes about ceil(waves / SIMDs) wave times of its K fraction;
-// a launch that leaves at most one wave on each SIMD hides none of a wave's
-// latencies behind another's (measured about 25% slower per wave), and each
-// split pays an exchange through LDS (5%).  The four-way form needs 32 group
-// pairs of K (8 per wave).
+// SIMDs, two at a time (two work-groups per CU), so the busiest SIMD takes
+// ceil(waves / SIMDs) waves in rounds of two; a wave that runs alone in the
+// last round hides none of its latencies (measured about 25% slower), and a
+// split wave pays a fixed exchange through LDS (about one group pair of work
+// in the two-way form, one and a half in the four-way form).  Work is counted
+// in group pairs.  This picks the four-way form for the 1024-row launches at
+// N = 2048 and 2560, the two-way form for the other 1024-row launches, for
+// 4096 rows at N = 5632, and for the 8192-row K = 6912 projection (measured
+// 6% faster there than whole tiles), and whole tiles elsewhere.  The
+// four-way form needs 32 group pairs of K (8 per wave).
 int gemm_form(int M, int N, int K) {
-  const double simds = 4.0 * device_cu_count();
-  auto cost = [&](int64_t tiles, double kfrac) {
-    const double waves = 4.0 * (double)tiles;
-    return kfrac * std::ceil(waves / simds) * (waves <= simds ? 1.25 : 1.0);
+  const int64_t simds = 4 * (int64_t)device_cu_count();
+  const double pairs = (double)(((K >> 5) + 1) >> 1);
+  auto cost = [&](int64_t tiles, double work) {
+    const int64_t n = (4 * tiles + simds - 1) / simds;  // waves on the busiest SIMD
+    return (double)(n / 2) * 2.0 * work + ((n & 1) ? 1.25 * work : 0.0);
   };
   const int64_t t0 = (int64_t)((N + 127) / 128) * ((M + 127) / 128);
   const int64_t t1 = (int64_t)((N + 127) / 128) * ((M + 63) / 64);
   const int64_t t2 = (int64_t)((N + 63) / 64) * ((M + 63) / 64);
-  const double c0 = cost(t0, 1.0);
-  const double c1 = cost(t1, 0.5) / 0.95;
-  const double c2 = ((((K >> 5) + 1) >> 1) >= 32) ? cost(t2, 0.25) / (0.95 * 0.95) : 1e30;
+  const double c0 = cost(t0, pairs);
+  const double c1 = cost(t1, pairs / 2.0 + 1.0);
+  const double c2 = pairs >= 32 ? cost(t2, pairs / 4.0 + 1.5) : 1e30;
   if (c2 < c1 && c2 < c0) return 2;
   return c1 < c0 ? 1 : 0;
 }
