@@ -401,6 +401,45 @@ def timed(lq, torch, mods, bits, schedule, steps, warmup, hooks=False):
     return (t1 - t0) / steps, per_kernel
 
 
+def graph_step_ms(lq, torch, mods, bits, schedule, steps):
+    """One step of the block captured into a HIP graph (the pipelined schedule's
+    auxiliary stream and events become graph nodes), replayed three times with
+    eager work between the replays and every replay's outputs checked bitwise
+    against an eager step, then timed over `steps` replays.  Returns (ms per
+    step or None, replays match, error text or None)."""
+    run_steps(lq, mods, bits, schedule, 1)
+    torch.cuda.synchronize()
+    ref = [m.y.clone() for m in mods]
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    try:
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                run_steps(lq, mods, bits, schedule, 1)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+    except Exception as e:  # capture is a measurement option, not part of the path
+        torch.cuda.synchronize()
+        return None, False, str(e)[:200]
+    ok = True
+    for _ in range(3):
+        for m in mods:
+            m.y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        ok &= all(torch.equal(m.y, r) for m, r in zip(mods, ref))
+        run_steps(lq, mods, bits, schedule, 1)  # eager work between replays
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    del graph
+    return dt * 1e3, bool(ok), None
+
+
 def setup_block(lq, synth, torch, M=1024, T=4):
     wl = synth.ouro_block_workload(bits_a=4, M=M, T=T)
     mods = build_modules(lq, synth, wl, torch)
@@ -421,6 +460,8 @@ def block_bench(lq, torch, wl, mods, steps, warmup):
     s_seq, kern_seq = timed(lq, torch, mods, 4, lq.LOOPQ_SCHED_LOOP_SEQUENTIAL, steps, warmup, hooks=True)
     s_seq_nohook, _ = timed(lq, torch, mods, 4, lq.LOOPQ_SCHED_LOOP_SEQUENTIAL, steps, warmup)
     s_a8, kern_a8 = timed(lq, torch, mods, 8, lq.LOOPQ_SCHED_AUTO, steps, warmup, hooks=True)
+    g_ws = graph_step_ms(lq, torch, mods, 4, lq.LOOPQ_SCHED_AUTO, steps)
+    g_seq = graph_step_ms(lq, torch, mods, 4, lq.LOOPQ_SCHED_LOOP_SEQUENTIAL, steps)
     gemm_ms, gemm_n = kern[lq.LOOPQ_KERNEL_GEMM]
     quant_ms, _ = kern[lq.LOOPQ_KERNEL_QUANT_TRANSFORM]
     achieved = ops * steps / (gemm_ms * 1e-3) / 1e12
@@ -441,7 +482,9 @@ def block_bench(lq, torch, wl, mods, steps, warmup):
                  "launches": gemm_n, "traffic": measured_traffic(BLOCK_TRAFFIC_FILE)},
         "fold_inclusive": fold_inclusive(ops, groups, gemm_ms / steps),
         "ms_per_step_with_timing_hooks": s_ws * 1e3,
+        "graph_ms_per_step": g_ws[0], "graph_replays_match_eager": g_ws[1], "graph_error": g_ws[2],
         "loop_sequential_pipelined": {
+            "graph_ms_per_step": g_seq[0], "graph_replays_match_eager": g_seq[1], "graph_error": g_seq[2],
             "ms_per_step": s_seq_nohook * 1e3, "value": ops / s_seq_nohook / 1e12,
             "gemm_launches": seq_gemm_n,
             "gemm_avg_launch_ms": seq_gemm_ms / max(seq_gemm_n, 1),
