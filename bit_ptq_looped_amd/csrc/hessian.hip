@@ -129,22 +129,34 @@ __device__ __forceinline__ void stage_store(float* stage, const StageRegs& r) {
   }
 }
 
-// The three bf16 planes (hi + mid + lo = v exactly, split3_bf16) of 8
+// The three bf16 planes (hi + mid + lo = v exactly: hi = v truncated to
+// bf16, mid = the remainder truncated, lo = the rest, as split3_bf16) of 8
 // consecutive staged rows of two adjacent columns (P, row stride kTile): the
 // MFMA operand of the column of parity p with the 8 rows as its K slots,
-// pl[p][plane].
+// pl[p][plane].  A plane value is the upper half of an fp32 word (v, then
+// r1 = v - hi, then r2 = r1 - mid, each difference exact), so each pair of
+// K slots is one byte permute of two such words.
+__device__ __forceinline__ uint32_t hi_halves(float lo_slot, float hi_slot) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi_slot), __float_as_uint(lo_slot), 0x07060302u);
+}
+__device__ __forceinline__ float minus_top(float v) {
+  return v - __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+}
 __device__ __forceinline__ void planes_rows8(const float* P, v4u (&pl)[2][3]) {
   float2 v[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) v[t] = *reinterpret_cast<const float2*>(P + t * kTile);
-  float e[8], o[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    e[t] = v[t].x;
-    o[t] = v[t].y;
+  for (int k = 0; k < 4; ++k) {
+    const float e0 = v[2 * k].x, e1 = v[2 * k + 1].x, o0 = v[2 * k].y, o1 = v[2 * k + 1].y;
+    const float e0m = minus_top(e0), e1m = minus_top(e1), o0m = minus_top(o0), o1m = minus_top(o1);
+    pl[0][0][k] = hi_halves(e0, e1);
+    pl[0][1][k] = hi_halves(e0m, e1m);
+    pl[0][2][k] = hi_halves(minus_top(e0m), minus_top(e1m));
+    pl[1][0][k] = hi_halves(o0, o1);
+    pl[1][1][k] = hi_halves(o0m, o1m);
+    pl[1][2][k] = hi_halves(minus_top(o0m), minus_top(o1m));
   }
-  planes8(e, pl[0]);
-  planes8(o, pl[1]);
 }
 
 __device__ __forceinline__ v16f mm16(const v4u& a, const v4u& b, v16f c) {
