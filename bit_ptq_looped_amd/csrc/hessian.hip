@@ -135,13 +135,7 @@ __device__ __forceinline__ void stage_store(float* stage, const StageRegs& r) {
 // MFMA operand of the column of parity p with the 8 rows as its K slots,
 // pl[p][plane].  A plane value is the upper half of an fp32 word (v, then
 // r1 = v - hi, then r2 = r1 - mid, each difference exact), so each pair of
-// K slots is one byte permute of two such words.
-__device__ __forceinline__ uint32_t hi_halves(float lo_slot, float hi_slot) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi_slot), __float_as_uint(lo_slot), 0x07060302u);
-}
-__device__ __forceinline__ float minus_top(float v) {
-  return v - __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
-}
+// K slots is one byte permute of two such words (top_halves).
 __device__ __forceinline__ void planes_rows8(const float* P, v4u (&pl)[2][3]) {
   float2 v[8];
 #pragma unroll
@@ -150,12 +144,12 @@ __device__ __forceinline__ void planes_rows8(const float* P, v4u (&pl)[2][3]) {
   for (int k = 0; k < 4; ++k) {
     const float e0 = v[2 * k].x, e1 = v[2 * k + 1].x, o0 = v[2 * k].y, o1 = v[2 * k + 1].y;
     const float e0m = minus_top(e0), e1m = minus_top(e1), o0m = minus_top(o0), o1m = minus_top(o1);
-    pl[0][0][k] = hi_halves(e0, e1);
-    pl[0][1][k] = hi_halves(e0m, e1m);
-    pl[0][2][k] = hi_halves(minus_top(e0m), minus_top(e1m));
-    pl[1][0][k] = hi_halves(o0, o1);
-    pl[1][1][k] = hi_halves(o0m, o1m);
-    pl[1][2][k] = hi_halves(minus_top(o0m), minus_top(o1m));
+    pl[0][0][k] = top_halves(e0, e1);
+    pl[0][1][k] = top_halves(e0m, e1m);
+    pl[0][2][k] = top_halves(minus_top(e0m), minus_top(e1m));
+    pl[1][0][k] = top_halves(o0, o1);
+    pl[1][1][k] = top_halves(o0m, o1m);
+    pl[1][2][k] = top_halves(minus_top(o0m), minus_top(o1m));
   }
 }
 

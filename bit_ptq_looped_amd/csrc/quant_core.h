@@ -242,16 +242,28 @@ __host__ __device__ constexpr int p1_row_of_slot(int s) {
   return (s & ~31) | (((s >> 2) & 1) << 4) | (((s >> 3) & 3) << 2) | (s & 3);
 }
 
-// the three bf16 planes of 8 fp32 values, packed two per register
+// The planes of split3_bf16 are the upper halves of fp32 words: hi of v, mid
+// of r1 = v - hi, lo of r2 = r1 - mid (each difference exact).  top_halves
+// packs the upper halves of two words (the first in the low half) in one
+// byte permute; minus_top is the exact difference that uncovers the next
+// plane.
+__device__ __forceinline__ uint32_t top_halves(float lo_slot, float hi_slot) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi_slot), __float_as_uint(lo_slot), 0x07060302u);
+}
+__device__ __forceinline__ float minus_top(float v) {
+  return v - __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+}
+
+// the three bf16 planes of 8 fp32 values, packed two per register (element
+// 2k in the low half of register k): split3_bf16 of each value
 __device__ __forceinline__ void planes8(const float (&v)[8], v4u (&b)[3]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    uint32_t h0, m0, l0, h1, m1, l1;
-    split3_bf16(v[2 * k], &h0, &m0, &l0);
-    split3_bf16(v[2 * k + 1], &h1, &m1, &l1);
-    b[0][k] = h0 | (h1 << 16);
-    b[1][k] = m0 | (m1 << 16);
-    b[2][k] = l0 | (l1 << 16);
+    const float v0 = v[2 * k], v1 = v[2 * k + 1];
+    const float m0 = minus_top(v0), m1 = minus_top(v1);
+    b[0][k] = top_halves(v0, v1);
+    b[1][k] = top_halves(m0, m1);
+    b[2][k] = top_halves(minus_top(m0), minus_top(m1));
   }
 }
 
