@@ -18,7 +18,9 @@
 // W4A4 on request); gemm_f6.hip is the W4A4 kernel.
 //
 // Tiling: 256 threads = 4 waves in a 2x2 arrangement, 128x128 outputs per
-// work-group, 64x64 (2x2 MFMA tiles) per wave.  Operands stream from global
+// work-group, 64x64 (2x2 MFMA tiles) per wave; the two split-K forms of the
+// fp6 kernel (64x128 tiles over half of K per wave, 64x64 over a quarter)
+// where they spread a launch's waves over the SIMDs better (gemm_form).  Operands stream from global
 // memory in the tiled layouts of loopq_internal.h (each wave load is one
 // contiguous 1 KB / 512 B block); the loop is unrolled twice so the next
 // group's loads are in flight while the current one is multiplied and folded,
@@ -47,16 +49,30 @@ struct Stage {
   uint32_t sw;       // raw fp16 weight step of column l % 32 of column tile h
 };
 
-template <int MODE>
+// SPLIT (rescale mode only): 1, the two-way split-K form (64x128 tiles, waves
+// 0-1 over the first half of the groups of their 64x64 quadrants, waves 2-3
+// over the second half); 2, the four-way form (one 64x64 quadrant per
+// work-group, wave w over the w-th quarter of the groups).  The partial sums
+// are added through LDS in a fixed order (the first wave of a quadrant adds
+// the others' and stores), as in the fp6 kernel; every wave of a split form
+// reaches the barrier, so none returns early.
+template <int MODE, int SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
+  __shared__ float red[SPLIT == 2 ? 3 * 64 * 64 : SPLIT ? 2 * 64 * 64 : 1];
   const int lane = threadIdx.x & 63;
   // the wave index is uniform; say so, so that tile bases live in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int c = lane & 31;
-  int m_base, n_base;
-  map_tile(g, wave, &m_base, &n_base);
-  if (m_base >= g.M || n_base >= g.N) return;
+  int m_base, n_base, kh = 0;
+  if (SPLIT == 2)
+    map_tile_split4(g, wave, &m_base, &n_base, &kh);
+  else if (SPLIT)
+    map_tile_split(g, wave, &m_base, &n_base, &kh);
+  else
+    map_tile(g, wave, &m_base, &n_base);
+  const bool active = m_base < g.M && n_base < g.N;
+  if (!SPLIT && !active) return;
   const int Ga = g.K >> 5;
   const int Gw = ((g.K >> 5) + (1 << g.gshift) - 1) >> g.gshift;
   const int mlast = ((g.M + 31) >> 5) - 1;
@@ -69,7 +85,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   // (always in bounds); their results are dropped at the store.
   const void* wp;
   const __half* swp;
-  tile_weights(g, m_base, &wp, &swp);  // the grouped form's weight set of these rows
+  tile_weights(g, active ? m_base : 0, &wp, &swp);  // the grouped form's weight set of these rows
   __amdgpu_buffer_rsrc_t x_rs[2], w_rs[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -168,24 +184,70 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     fold(d11, cA, 1, 1, 1, j);
   };
 
-  // Loads past the last group re-read it (in bounds, unused), so the loop
-  // body is one basic block the barriers can order.
-  Stage s0, s1;
-  load(0, s0);
-  load(min(1, Ga - 1), s1);
-  int j = 0;
-  for (; j + 1 < Ga; j += 2) {
-    compute(s0, j);
-    __builtin_amdgcn_sched_barrier(0);
-    load(min(j + 2, Ga - 1), s0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s1, j + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load(min(j + 3, Ga - 1), s1);
-    __builtin_amdgcn_sched_barrier(0);
+  // this wave's groups [j0, j1).  Loads past the last group re-read it (in
+  // bounds, unused), so the loop body is one basic block the barriers can
+  // order.
+  const int half = (Ga + 1) >> 1;
+  const int quarter = (Ga + 3) >> 2;
+  const int j0 = SPLIT == 2 ? min(Ga, kh * quarter) : SPLIT && kh ? half : 0;
+  const int j1 = SPLIT == 2 ? min(Ga, j0 + quarter) : SPLIT && !kh ? half : Ga;
+  if (active && j0 < j1) {
+    Stage s0, s1;
+    load(j0, s0);
+    load(min(j0 + 1, j1 - 1), s1);
+    int j = j0;
+    for (; j + 1 < j1; j += 2) {
+      compute(s0, j);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(j + 2, j1 - 1), s0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s1, j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(j + 3, j1 - 1), s1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (j < j1) compute(s0, j);
   }
-  if (j < Ga) compute(s0, j);
 
+  if (SPLIT == 2) {
+    if (kh > 0 && active) {
+      float* r = red + (kh - 1) * 64 * 64;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) r[((t * 2 + u) * 16 + e) * 64 + lane] = acc[t][u][e];
+    }
+    __syncthreads();
+    if (kh > 0 || !active) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[t][u][e] += red[w * 64 * 64 + ((t * 2 + u) * 16 + e) * 64 + lane];
+  } else if (SPLIT) {
+    float* r = red + (wave & 1) * 64 * 64;
+    if (kh == 1 && active) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) r[((t * 2 + u) * 16 + e) * 64 + lane] = acc[t][u][e];
+    }
+    __syncthreads();
+    if (kh == 1 || !active) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][u][e] += r[((t * 2 + u) * 16 + e) * 64 + lane];
+  }
   if (MODE == 0) store_y(g, acc, m_base, n_base, h, c);
 }
 
@@ -241,11 +303,22 @@ hipError_t launch_gemm(const int8_t* a_tiled, const float* a_scales_gm, int ld_s
   g.gshift = gw == 128 ? 2 : 0;
   g.y = y;
   g.dots = dots;
-  dim3 grid(((N + 127) / 128) * ((M + 127) / 128));
-  if (mode == 0)
-    hipLaunchKernelGGL(gemm_kernel<0>, grid, dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL(gemm_kernel<1>, grid, dim3(256), 0, s, g);
+  // the tile form as for the fp6 kernel (gemm_form: the busiest SIMD's waves
+  // in rounds of two); the dots mode always takes whole tiles
+  const int form = mode == 0 ? gemm_form(M, N, K) : 0;
+  if (form == 2) {
+    dim3 grid((unsigned)((int64_t)((N + 63) / 64) * ((M + 63) / 64)));
+    hipLaunchKernelGGL((gemm_kernel<0, 2>), grid, dim3(256), 0, s, g);
+  } else if (form == 1) {
+    dim3 grid((unsigned)((int64_t)((N + 127) / 128) * ((M + 63) / 64)));
+    hipLaunchKernelGGL((gemm_kernel<0, 1>), grid, dim3(256), 0, s, g);
+  } else {
+    dim3 grid(((N + 127) / 128) * ((M + 127) / 128));
+    if (mode == 0)
+      hipLaunchKernelGGL((gemm_kernel<0, 0>), grid, dim3(256), 0, s, g);
+    else
+      hipLaunchKernelGGL((gemm_kernel<1, 0>), grid, dim3(256), 0, s, g);
+  }
   return hipGetLastError();
 }
 

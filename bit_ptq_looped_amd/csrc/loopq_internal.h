@@ -233,6 +233,10 @@ hipError_t prepare_launch(const void* fn, int lds_bytes, int block, int* per_cu 
 // CU count of the current device (queried once per device; 256 if the query fails)
 int device_cu_count();
 
+// Tile form of a rescale-mode GEMM launch (both kernels): 0 whole 128x128
+// tiles, 1 the two-way split-K form, 2 the four-way form (gemm_f6.hip).
+int gemm_form(int M, int N, int K);
+
 hipError_t launch_hessian(const float* x, int rows, int K, float* H, float* part, hipStream_t s);
 
 // x [M][2N] = cat(s [M][N], e [M][N]) per row (fp32, N % 4 == 0, 16-byte aligned)

@@ -196,29 +196,36 @@ def test_gemm_codes_matches_oracle(lq, bits, M, K, N, gw):
     assert rel_err(y.cpu().numpy(), ref) <= Y_TOL
 
 
-@pytest.mark.parametrize("M,K,N", [(1024, 2048, 2048), (1000, 2080, 2000), (1024, 2048, 6144), (1024, 5632, 2048)],
-                         ids=["four-way", "four-way ragged, odd groups", "two-way", "four-way long K"])
-def test_gemm_split_forms_match_oracle(lq, M, K, N):
-    """The launch sizes at which the W4A4 GEMM takes its split-K forms (two-way: 64x128 tiles over
+@pytest.mark.parametrize("M,K,N,bits,gw", [(1024, 2048, 2048, 4, 32), (1000, 2080, 2000, 4, 32), (1024, 2048, 6144, 4, 32),
+                                            (1024, 5632, 2048, 4, 32), (8192, 6912, 2560, 4, 32),
+                                            (1024, 2048, 2048, 8, 32), (1000, 2080, 2000, 8, 32), (4096, 2048, 5632, 8, 32),
+                                            (2048, 10560, 5280, 8, 128), (1000, 10528, 2000, 8, 128)],
+                         ids=["four-way", "four-way ragged, odd groups", "two-way", "four-way long K",
+                              "two-way, the stack's down projection",
+                              "A8 four-way", "A8 four-way ragged, odd groups", "A8 two-way",
+                              "A8 four-way g128, the adapter recurrence", "A8 four-way g128 ragged, short tail"])
+def test_gemm_split_forms_match_oracle(lq, M, K, N, bits, gw):
+    """The launch sizes at which the GEMMs take their split-K forms (two-way: 64x128 tiles over
     half of K per wave; four-way: 64x64 tiles over a quarter of K per wave, the partial sums added
-    through LDS), against the oracle's per-group rescale on sampled rows and columns that cover
-    the first, last and tile-boundary rows and columns (the oracle's dots for the whole output
-    would take minutes)."""
-    say(f"gemm split forms M={M} K={K} N={N}")
+    through LDS): the W4A4 kernel on fp6 operands and the W4A8 kernel on int8 operands, against
+    the oracle's per-group rescale on sampled rows and columns that cover the first, last and
+    tile-boundary rows and columns (the oracle's dots for the whole output would take minutes)."""
+    say(f"gemm split forms M={M} K={K} N={N} A{bits} g_w={gw}")
+    qmax = 7 if bits == 4 else 127
     rng = synth.seeded_rng(synth.TEST, 125, M, K, N)
-    qa = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    qa = rng.integers(-qmax, qmax + 1, size=(M, K)).astype(np.int8)
     sa = rng.uniform(0.01, 2.0, size=(M, K // 32)).astype(np.float32)
     w = synth.gaussian((N, K), 126, M, K, scale=0.02)
-    codes, scales = pack(lq, w, 32)
-    qw, sw = oracle.quant_weights(w, 32)
+    codes, scales = pack(lq, w, gw)
+    qw, sw = oracle.quant_weights(w, gw)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR, 1, M, K, N, 4)
-    lq.loopq_gemm_codes(dev(qa), dev(sa), codes, scales, 32, N, y, ws, bits_a=4)
+    ws = lq.empty_workspace(lq.LOOPQ_OP_LINEAR, 1, M, K, N, bits)
+    lq.loopq_gemm_codes(dev(qa), dev(sa), codes, scales, gw, N, y, ws, bits_a=bits)
     torch.cuda.synchronize()
     got = y.cpu().numpy()
     rows = sorted({0, 1, 31, 32, 63, 64, 127, 128, M // 2, M - 65, M - 64, M - 1} | set(rng.integers(0, M, 8).tolist()))
     cols = sorted({0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 65, N - 64, N - 1} | set(rng.integers(0, N, 8).tolist()))
-    ref = oracle.rescale_dots(sa[rows], oracle.group_dots(qa[rows], qw[cols]), sw[cols], 32)
+    ref = oracle.rescale_dots(sa[rows], oracle.group_dots(qa[rows], qw[cols]), sw[cols], gw)
     assert rel_err(got[np.ix_(rows, cols)], ref) <= Y_TOL
     assert np.all(np.isfinite(got))
 
