@@ -1342,17 +1342,23 @@ int slice_lds(int RM, int cpw) {
   return RM * ks * 32 + RM * ks * 4 + 8 * RM * 32 * 4;
 }
 
-// Columns per work-group: the largest of 32, 16, 8 that still gives at least
-// 60% of the CUs a work-group (16 at least for the MFMA form), else the
-// smallest allowed.  More work-groups than CUs put two on some CUs, which then
-// finish about one row transform later than the rest; 32 columns per
-// work-group and 60-100% of the CUs busy cost only a longer weight sweep
-// (measured at N = 6144 and 5632, one row: 192 and 176 work-groups of 32
-// columns end 0.7 us sooner than 384 and 352 of 16).
-int pick_cpw(int64_t n_padded, int R, int ncu) {
+// Columns per work-group.  Where every work-group repeats a fixed chain
+// before its weight sweep (the row transform of the fused instances, or the
+// codes of up to 16 rows over all of K in the MFMA form): the largest of 32,
+// 16, 8 that still gives at least 60% of the CUs a work-group (16 at least
+// for the MFMA form).  More work-groups than CUs put two on some CUs, which
+// then finish about one chain later than the rest; 32 columns per work-group
+// and 60-100% of the CUs busy cost only a longer weight sweep (measured at
+// N = 6144 and 5632, one row: 192 and 176 work-groups of 32 columns end
+// 0.7 us sooner than 384 and 352 of 16; 16 rows of codes: 1.94 against
+// 2.28 ms per decode loop-step).  Otherwise (at most 4 rows quantized in
+// place or copied, no transform) the sweep is the work, and every CU gets a
+// work-group (the adapter recurrence at one row, K = 10560: 19.9 against
+// 24.0 us per loop with 165 work-groups of 32 columns).
+int pick_cpw(int64_t n_padded, int R, int ncu, bool repeats) {
   const int lo = R > 4 ? 16 : 8;
   for (int cpw = 32; cpw >= lo; cpw >>= 1)
-    if (n_padded / cpw * 5 >= (int64_t)ncu * 3) return cpw;
+    if (repeats ? n_padded / cpw * 5 >= (int64_t)ncu * 3 : n_padded / cpw >= ncu) return cpw;
   return lo;
 }
 
@@ -1415,7 +1421,7 @@ hipError_t launch_decode(const DecodeCall& c, hipStream_t s) {
   int lds = 0, threads = 256;
   const bool small = c.R <= 4;
   const int RM = small ? 4 : kDecodeMaxRows;
-  const int cpw = pick_cpw(padded_cols(c.N), c.R, device_cu_count());
+  const int cpw = pick_cpw(padded_cols(c.N), c.R, device_cu_count(), xform || c.R > 4);
   if (xform) {
 #define LOOPQ_DECODE_KERNEL(n1_, n2_, rs_, nim_, ws_)                                                   \
     if (c.n1 == n1_ && c.n2 == n2_) {                                                              \
