@@ -9,10 +9,20 @@
 // eta = 0, and stores the result in the state's type (bf16 rounded to nearest
 // even, or fp32).
 //
-// A work-group takes up to 16 consecutive rows of one transition block (4
-// per wave) and runs over K in tiles of 512 (8 consecutive elements per
-// lane).  Pass 1 forms z = V^T h of each row: the tile of V is staged in LDS
-// (element k of column j at [j][k % 8][lane], conflict-free reads), every
+// Resident form (rank 8, K <= 2560: the hidden sizes of the block and the
+// stack):
+// each wave issues every load of its rows (4 bf16 rows or 2 fp32 rows, all
+// of K) at once and keeps them in registers through both passes, so each row
+// is read from HBM once and the wait for it is paid once; the tiles of V, and
+// then of U, a and b, are loaded into registers one tile ahead and staged in
+// LDS behind a barrier.  Its arithmetic is the general form's, in the same
+// order, so both give the same bits.
+//
+// General form (any K): a work-group takes up to 16 consecutive rows of one
+// transition block (4 per wave) and runs over K in tiles of 512 (8
+// consecutive elements per lane).  Pass 1 forms z = V^T h of each row: the
+// tile of V is staged in LDS (element k of column j at [j][k % 8][lane],
+// conflict-free reads), every
 // lane accumulates its elements in order and the wave sums its lanes by a
 // butterfly -- a fixed order, so the result does not depend on timing.  Pass 2
 // re-reads the rows (from L2) with the tiles of U, a and b in LDS and writes
@@ -42,6 +52,7 @@ struct CtaArgs {
   int K, r, bf16;
   int64_t rows_per_tr;  // rows of one transition block (blockIdx.y)
   int first;            // transition of block 0 (-1: copy it)
+  int vec;              // U and V 16-byte aligned with r equal to the kernel's R
 };
 
 // 8 consecutive elements of row m from k (k % 8 == 0)
@@ -186,6 +197,194 @@ __global__ __launch_bounds__(256) void cta_kernel(CtaArgs g) {
   }
 }
 
+constexpr int kResTiles = 5;  // the resident form's largest K: kResTiles * kTile
+
+// The resident form: RW rows per wave (4 bf16 or 2 fp32, 4 * RW per
+// work-group), NT tiles of K, every row element loaded once into hw.
+template <int R, int NT, bool BF16>
+__global__ __launch_bounds__(256) void cta_resident_kernel(CtaArgs g) {
+  constexpr int RW = BF16 ? 4 : 2;  // rows per wave
+  constexpr int NW = BF16 ? 4 : 8;  // 32-bit words of a lane's 8 elements
+  constexpr int NP = 2 * R;         // staged elements per thread and tile
+  __shared__ float sW[R * kTile];   // as in the general form
+  __shared__ float sA[kTile], sB[kTile];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = g.K;
+  const int tr = (int)blockIdx.y + g.first;
+  const int64_t rb0 = (int64_t)blockIdx.y * g.rows_per_tr;
+  const int64_t rb1 = min(rb0 + g.rows_per_tr, g.rows);
+  const int64_t r0 = rb0 + (int64_t)blockIdx.x * (4 * RW) + wave * RW;
+  const int nr = (int)max((int64_t)0, min((int64_t)RW, rb1 - r0));
+
+  uint32_t hw[NT][RW][NW];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int k = t * kTile + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      if (i < nr && k < K) {
+        const uint4* p = BF16 ? reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(g.h) + (r0 + i) * K + k)
+                              : reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(g.h) + (r0 + i) * K + k);
+#pragma unroll
+        for (int v = 0; v < NW / 4; ++v) {
+          const uint4 u = p[v];
+          hw[t][i][4 * v] = u.x; hw[t][i][4 * v + 1] = u.y; hw[t][i][4 * v + 2] = u.z; hw[t][i][4 * v + 3] = u.w;
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) hw[t][i][w] = 0u;
+      }
+    }
+  }
+  auto elems = [&](int t, int i, float (&v)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      v[q] = BF16 ? bf16_bits_to_float(q & 1 ? hw[t][i][q >> 1] >> 16 : hw[t][i][q >> 1] & 0xffffu)
+                  : __uint_as_float(hw[t][i][q]);
+  };
+
+  // the thread's share of tile t of W ([K][r]) into pre; element (kk, j) of
+  // the tile goes to sW[j][kk % 8][kk / 8]
+  auto fetch = [&](const float* __restrict__ W, int t, float (&pre)[NP]) {
+    const int k0 = t * kTile, kn = min(kTile, K - k0);
+    if (g.vec) {
+#pragma unroll
+      for (int s = 0; s < NP / 4; ++s) {
+        const int f = 4 * (tid + 256 * s), kk = f / R;
+        float4 u = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (kk < kn) u = *reinterpret_cast<const float4*>(W + (int64_t)k0 * R + f);
+        pre[4 * s] = u.x; pre[4 * s + 1] = u.y; pre[4 * s + 2] = u.z; pre[4 * s + 3] = u.w;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NP; ++s) {
+        const int q = tid + 256 * s, kk = q / R, j = q % R;
+        pre[s] = j < g.r && kk < kn ? W[(int64_t)(k0 + kk) * g.r + j] : 0.0f;
+      }
+    }
+  };
+  auto put = [&](const float (&pre)[NP]) {
+    if (g.vec) {
+#pragma unroll
+      for (int s = 0; s < NP / 4; ++s) {
+        const int f = 4 * (tid + 256 * s), kk = f / R, j = f % R;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sW[(j + c) * kTile + (kk & 7) * 64 + (kk >> 3)] = pre[4 * s + c];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NP; ++s) {
+        const int q = tid + 256 * s, kk = q / R, j = q % R;
+        sW[j * kTile + (kk & 7) * 64 + (kk >> 3)] = pre[s];
+      }
+    }
+  };
+
+  float z[RW][R];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int j = 0; j < R; ++j) z[i][j] = 0.0f;
+
+  float pre[NP];
+  if (tr >= 0) {  // pass 1: z = V^T h
+    fetch(g.V, 0, pre);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t * kTile >= K) break;
+      __syncthreads();  // the previous tile is no longer read
+      put(pre);
+      if (t + 1 < NT && (t + 1) * kTile < K) fetch(g.V, t + 1, pre);
+      __syncthreads();
+      if (t * kTile + 8 * lane < K) {
+        float hv[RW][8];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) elems(t, i, hv[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float v[R];
+#pragma unroll
+          for (int j = 0; j < R; ++j) v[j] = sW[j * kTile + e * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < RW; ++i)
+            if (i < nr)
+#pragma unroll
+              for (int j = 0; j < R; ++j) z[i][j] = fmaf(v[j], hv[i][e], z[i][j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        float v = z[i][j];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        z[i][j] = v;
+      }
+  }
+
+  // pass 2: the adapted rows (copied rows unchanged)
+  const float eta = tr >= 0 ? g.eta.c[tr] : 0.0f;
+  float pa[2], pb[2];
+  auto fetch_ab = [&](int t) {
+    const int k0 = t * kTile, kn = min(kTile, K - k0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int q = tid + 256 * s;
+      pa[s] = q < kn ? g.a[(int64_t)tr * K + k0 + q] : 0.0f;
+      pb[s] = q < kn ? g.b[(int64_t)tr * K + k0 + q] : 0.0f;
+    }
+  };
+  if (tr >= 0) {
+    fetch(g.U, 0, pre);
+    fetch_ab(0);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t * kTile >= K) break;
+    if (tr >= 0) {
+      __syncthreads();
+      put(pre);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int q = tid + 256 * s;
+        sA[(q & 7) * 64 + (q >> 3)] = pa[s];
+        sB[(q & 7) * 64 + (q >> 3)] = pb[s];
+      }
+      if (t + 1 < NT && (t + 1) * kTile < K) {
+        fetch(g.U, t + 1, pre);
+        fetch_ab(t + 1);
+      }
+      __syncthreads();
+    }
+    const int k = t * kTile + 8 * lane;
+    if (k >= K || nr == 0) continue;
+    float hv[RW][8];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) elems(t, i, hv[i]);
+    if (tr >= 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float u[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) u[j] = sW[j * kTile + e * 64 + lane];
+        const float ak = sA[e * 64 + lane], bk = sB[e * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+          float s = 0.0f;
+#pragma unroll
+          for (int j = 0; j < R; ++j) s = fmaf(u[j], z[i][j], s);
+          hv[i][e] = fmaf(eta, s, fmaf(ak, hv[i][e], bk));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      if (i < nr) store8(g, r0 + i, k, hv[i]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_cta(const void* h, int bf16, int64_t rows, int K, const float* U, const float* V, int r,
@@ -213,10 +412,28 @@ hipError_t launch_cta(const void* h, int bf16, int64_t rows, int K, const float*
   const int64_t nblk = (rows + rows_per_tr - 1) / rows_per_tr;
   if (nblk - 1 + first >= ntr || nblk > 65535) return hipErrorInvalidValue;
   const int64_t per_blk = min(rows_per_tr, rows);
+  const int R = r <= 8 ? 8 : 16;
+  const int nt = (K + kTile - 1) / kTile;
+  // the resident form for rank 8 up to 5 tiles of K, where it keeps two
+  // waves per SIMD; other shapes take the general form
+  if (R == 8 && nt <= kResTiles) {
+    using Fn = void (*)(CtaArgs);
+    static const Fn res[2][kResTiles] = {
+        {cta_resident_kernel<8, 1, false>, cta_resident_kernel<8, 2, false>, cta_resident_kernel<8, 3, false>,
+         cta_resident_kernel<8, 4, false>, cta_resident_kernel<8, 5, false>},
+        {cta_resident_kernel<8, 1, true>, cta_resident_kernel<8, 2, true>, cta_resident_kernel<8, 3, true>,
+         cta_resident_kernel<8, 4, true>, cta_resident_kernel<8, 5, true>}};
+    const int wg_rows = bf16 ? 16 : 8;  // 4 waves of 4 bf16 or 2 fp32 rows
+    const int64_t gx = (per_blk + wg_rows - 1) / wg_rows;
+    if (gx > 0x7fffffff) return hipErrorInvalidValue;
+    g.vec = r == R && (reinterpret_cast<uintptr_t>(U) & 15) == 0 && (reinterpret_cast<uintptr_t>(V) & 15) == 0;
+    hipLaunchKernelGGL(res[bf16 ? 1 : 0][nt - 1], dim3((unsigned)gx, (unsigned)nblk), dim3(256), 0, s, g);
+    return hipGetLastError();
+  }
   const int64_t gx = (per_blk + kRows - 1) / kRows;
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gx, (unsigned)nblk);
-  if (r <= 8)
+  if (R == 8)
     hipLaunchKernelGGL(cta_kernel<8>, grid, dim3(256), 0, s, g);
   else
     hipLaunchKernelGGL(cta_kernel<16>, grid, dim3(256), 0, s, g);

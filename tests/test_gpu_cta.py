@@ -74,7 +74,9 @@ def host(t):
 
 
 @pytest.mark.parametrize("state,M,K,r", [("bf16", 37, 2560, 8), ("fp32", 7, 256, 3), ("bf16", 1, 6912, 16),
-                                         ("fp32", 37, 6912, 8), ("bf16", 7, 256, 1), ("fp32", 5, 17920, 8)])
+                                         ("fp32", 37, 6912, 8), ("bf16", 7, 256, 1), ("fp32", 5, 17920, 8),
+                                         ("bf16", 45, 3072, 8), ("fp32", 19, 2080, 8), ("bf16", 16, 2080, 5),
+                                         ("fp32", 9, 3072, 8), ("bf16", 33, 3104, 8), ("bf16", 21, 2080, 8)])
 def test_cta_apply_within_bound_of_the_oracle(lq, state, M, K, r):
     say(f"cta apply {state} M={M} K={K} r={r}")
     U, V, a, b, eta = cta_params(K, r, 1, M)
@@ -87,9 +89,10 @@ def test_cta_apply_within_bound_of_the_oracle(lq, state, M, K, r):
     assert np.max(np.abs(exact - oracle.cta_transition(h, U, V, a[0], b[0], 0.0)) / bound) > 10
 
 
+@pytest.mark.parametrize("K", [512, 2080, 3584])
 @pytest.mark.parametrize("state", ["bf16", "fp32"])
-def test_cta_identity_zero_gate_and_in_place(lq, state):
-    M, K, r = 9, 512, 8
+def test_cta_identity_zero_gate_and_in_place(lq, state, K):
+    M, r = 9, 8
     U, V, a, b, eta = cta_params(K, r, 1, 77)
     h = state_values((M, K), 78, state)
     hd = to_dev(h, state)
