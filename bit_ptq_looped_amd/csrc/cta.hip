@@ -73,19 +73,20 @@ __device__ __forceinline__ void load8(const CtaArgs& g, int64_t m, int k, float 
   }
 }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (finite values; a NaN
-// stays a NaN)
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// two fp32 values -> their bf16 bits (low half the first), round to nearest,
+// ties to even, one V_CVT_PK_BF16_F32 (a NaN stays a NaN)
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ void store8(const CtaArgs& g, int64_t m, int k, const float (&v)[8]) {
   if (g.bf16) {
     uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = bf16_bits_rne(v[2 * q]) | (bf16_bits_rne(v[2 * q + 1]) << 16);
+    for (int q = 0; q < 4; ++q) w[q] = bf16x2_rne(v[2 * q], v[2 * q + 1]);
     *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.out) + m * g.K + k) = uint4{w[0], w[1], w[2], w[3]};
   } else {
     float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(g.out) + m * g.K + k);
